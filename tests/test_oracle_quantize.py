@@ -1,0 +1,211 @@
+"""Pins for the oracle's amax, scale, scaled cast, delayed history and MXFP8 quantizer.
+
+Each test checks the oracle against something other than itself: a Python
+loop, a closed form fixed by the scale relation scale = fp8_max / amax, an
+invariant of current scaling, the delayed-history closed forms (constant input,
+a spike, most_recent, a drifting input), or the per-element encoder (pinned in
+test_oracle_formats.py).
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import (E4M3, E5M2, DelayedScalingState, amax, current_scale, decode_table,
+                    delayed_update, encode, mxfp8_quantize, scale_inverse, scaled_cast,
+                    cast_transpose)
+
+FLT_MAX = np.float32(np.finfo(np.float32).max)
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "recipe_constants.json")
+
+
+def test_amax_python_loop_and_planted_max():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((37, 53)).astype(np.float32)
+    m = 0.0
+    for v in x.reshape(-1):
+        m = max(m, abs(float(v)))
+    assert amax(x) == np.float32(m)
+    x[5, 7] = -123.5
+    assert amax(x) == np.float32(123.5)
+    perm = rng.permutation(x.size)
+    assert amax(x.reshape(-1)[perm]) == amax(x)
+    assert amax(np.array([-0.0, 0.0], dtype=np.float32)) == 0.0
+    assert amax(np.zeros((0, 4), dtype=np.float32)) == 0.0
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2], ids=lambda f: f.name)
+def test_current_scale_closed_forms(fmt):
+    mx = np.float32(fmt.max)
+    assert current_scale(mx, fmt) == 1.0
+    for k in range(-20, 20):
+        # power-of-two amax: the division is exact
+        assert current_scale(np.float32(2.0 ** k), fmt) == np.float32(fmt.max * 2.0 ** -k)
+    assert current_scale(0.0, fmt) == 1.0
+    assert current_scale(np.inf, fmt) == 1.0
+    assert current_scale(np.nan, fmt) == 1.0
+    assert current_scale(np.finfo(np.float32).smallest_subnormal, fmt) == FLT_MAX
+    assert current_scale(np.float32(fmt.max), fmt, margin=2) == 0.25
+    assert scale_inverse(np.float32(4.0)) == 0.25
+    # margin halves the scale per unit
+    assert current_scale(np.float32(3.0), fmt, margin=1) == np.float32(np.float32(fmt.max / 3.0) / 2)
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2], ids=lambda f: f.name)
+@pytest.mark.parametrize("seed", range(6))
+def test_current_scaling_amax_element_hits_max_code(fmt, seed):
+    """Invariant: with scale = fp8_max/amax, the amax element encodes to +-max exactly,
+    and every other code stays within [-max, max]."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_t(3, (64, 96)) * 10.0 ** rng.uniform(-6, 3)).astype(np.float32)
+    a = amax(x)
+    s = current_scale(a, fmt)
+    q = scaled_cast(x, s, fmt)
+    i = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    assert (q[i] & 0x7F) == fmt.max_code
+    v = decode_table(fmt)[q]
+    assert np.all(np.abs(v) <= fmt.max)
+
+
+def test_scaled_cast_reduces_to_encode():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(4096).astype(np.float32) * 30
+    np.testing.assert_array_equal(scaled_cast(x, 1.0, E4M3), encode(x, E4M3))
+    # a power-of-two scale is exact in fp32, so the cast equals the encode of the exact product
+    np.testing.assert_array_equal(scaled_cast(x, 0.125, E5M2), encode(x / 8, E5M2))
+
+
+def test_cast_transpose_is_byte_transpose():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((48, 80)).astype(np.float32)
+    row, col = cast_transpose(x, np.float32(3.5), E4M3)
+    np.testing.assert_array_equal(row, scaled_cast(x, np.float32(3.5), E4M3))
+    assert col.shape == (80, 48)
+    for r in range(48):
+        for c in range(80):
+            assert col[c, r] == row[r, c]
+
+
+def test_recipe_constants_from_pages():
+    with open(GOLD) as f:
+        g = json.load(f)
+    st = DelayedScalingState(E4M3, g["example_amax_history_len"], g["example_amax_compute_algo"],
+                             g["nemo_fp8_margin"])
+    assert st.hist.shape == (16,) and st.scale == 1.0 and st.scale_inv == 1.0
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2], ids=lambda f: f.name)
+def test_delayed_constant_input(fmt):
+    """Constant input c: scale_0 = 1 (initial), scale_t = fp8_max / c for t >= 1."""
+    c = np.float32(0.37)
+    st = DelayedScalingState(fmt, 16, "max")
+    scales = []
+    for t in range(20):
+        scales.append(st.scale)
+        st.cast(np.full((4, 8), c, dtype=np.float32))
+        st.update()
+    assert scales[0] == 1.0
+    for t in range(1, 20):
+        assert scales[t] == np.float32(np.float32(fmt.max) / c)
+
+
+def test_delayed_spike_dominates_exactly_sixteen_steps():
+    base, spike, k = np.float32(1.0), np.float32(64.0), 3
+    st = DelayedScalingState(E4M3, 16, "max")
+    used = []
+    for t in range(40):
+        used.append(st.scale)
+        v = spike if t == k else base
+        st.cast(np.full((2, 2), v, dtype=np.float32))
+        st.update()
+    for t in range(1, 40):
+        expect = np.float32(448.0) / (spike if k + 1 <= t <= k + 16 else base)
+        assert used[t] == np.float32(expect), t
+
+
+def test_delayed_most_recent():
+    rng = np.random.default_rng(4)
+    st = DelayedScalingState(E5M2, 16, "most_recent")
+    prev = None
+    for t in range(12):
+        x = rng.standard_normal((8, 8)).astype(np.float32) * np.float32(2.0 ** rng.integers(-5, 5))
+        if prev is not None:
+            assert st.scale == np.float32(np.float32(57344.0) / prev)
+        st.cast(x)
+        st.update()
+        prev = np.float32(np.max(np.abs(x)))
+
+
+def test_delayed_keeps_scale_on_zero_history_and_rolls():
+    h = np.zeros(4, dtype=np.float32)
+    nh, s, si = delayed_update(h, np.float32(8.0), E4M3)
+    assert s == 8.0 and si == 0.125 and (nh == 0).all()
+    h = np.array([3.0, 5.0, 1.0, 2.0], dtype=np.float32)
+    nh, s, si = delayed_update(h, np.float32(1.0), E4M3)
+    np.testing.assert_array_equal(nh, [0.0, 3.0, 5.0, 1.0])
+    assert s == np.float32(448.0 / 5.0)
+    nh, s, _ = delayed_update(np.array([np.inf, 1, 1, 1], dtype=np.float32), np.float32(2.0), E4M3)
+    assert s == 2.0
+    nh, s, _ = delayed_update(np.array([1e-45, 0, 0, 0], dtype=np.float32), np.float32(2.0), E4M3)
+    assert s == FLT_MAX
+
+
+def test_delayed_drift_saturation_count():
+    """Input growing x1.05 per step: the scale for step t+1 is fp8_max/amax_t, so the
+    elements of x_{t+1} above amax_t saturate -- a count fixed by the data alone."""
+    rng = np.random.default_rng(5)
+    base = rng.standard_normal((64, 64)).astype(np.float32)
+    st = DelayedScalingState(E4M3, 16, "most_recent")
+    prev_amax = None
+    for t in range(6):
+        x = (base * np.float32(1.05 ** t)).astype(np.float32)
+        q, _ = st.cast(x)
+        if prev_amax is not None:
+            prod = np.abs(x * st.scale)
+            # the elements that grew past amax_t (by the factor 1.05) saturate
+            n_over = int(np.sum(np.abs(x) > prev_amax))
+            assert n_over >= 1
+            assert int(np.sum(prod > np.float32(448.0))) == n_over
+            # max code = saturated values plus those rounding to 448 from above the
+            # 416/448 midpoint (432, a tie that goes to the even mantissa of 448)
+            n_max = int(np.sum((q & 0x7F) == E4M3.max_code))
+            assert n_max == int(np.sum(prod >= np.float32(432.0)))
+        st.update()
+        prev_amax = np.max(np.abs(x))
+
+
+def test_mxfp8_closed_form_codes():
+    rng = np.random.default_rng(6)
+    R, C = 8, 128
+    x = rng.standard_normal((R, C)).astype(np.float32)
+    # plant a known block amax per block: 2^j * 1.5 -> floor(log2) = j -> code j - 8 + 127
+    js = rng.integers(-30, 30, (R, C // 32))
+    for r in range(R):
+        for b in range(C // 32):
+            blk = x[r, b * 32:(b + 1) * 32]
+            blk[:] = np.clip(blk, -1.0, 1.0) * np.float32(2.0 ** int(js[r, b]))
+            blk[int(rng.integers(0, 32))] = np.float32(1.5 * 2.0 ** int(js[r, b]))
+    q, e = mxfp8_quantize(x)
+    np.testing.assert_array_equal(e.astype(int), js - 8 + 127)
+    # elements are the per-element encode of x * 2^-(code-127)
+    for r in range(R):
+        for b in range(C // 32):
+            sc = np.float32(2.0 ** -(int(e[r, b]) - 127))
+            np.testing.assert_array_equal(q[r, b * 32:(b + 1) * 32],
+                                          encode(x[r, b * 32:(b + 1) * 32] * sc, E4M3))
+
+
+def test_mxfp8_zero_block_and_clamp():
+    x = np.zeros((2, 64), dtype=np.float32)
+    x[1, 32:] = np.float32(2.0 ** 120)
+    q, e = mxfp8_quantize(x)
+    assert e[0, 0] == 127 and e[0, 1] == 127 and e[1, 0] == 127
+    assert e[1, 1] == 120 - 8 + 127
+    # 2^120 / 2^112 = 2^8 = 256: E4M3 exponent field 8 + 7 = 15, mantissa 0 -> 0x78
+    assert (q[1, 32:] == 0x78).all()
+    # the shared exponent clamps at -127 (code 0) for a block of fp32 subnormals
+    y = np.full((1, 32), np.finfo(np.float32).smallest_subnormal, dtype=np.float32)
+    qy, ey = mxfp8_quantize(y)
+    assert ey[0, 0] == 0 and (qy == 0).all()
