@@ -1,0 +1,414 @@
+"""Benchmark: FP8 GEMM TFLOP/s and ms per layer, autocast and pre-quantize, on the
+CodonFM-5B-shaped layer ([LP-opt] = "How to Optimize Transformer-Based Models for
+Low-Precision Training", sections "モデル設定とトレーニング入力" and "autocast モード
+の使用と事前量子化の比較": hidden 4096, intermediate 16384, micro-batch 31 x seq 512
+-> M = 15,872; the 12 GEMMs Fprop/Dgrad/Wgrad of QKV, attention-out, MLP-up, MLP-down).
+
+One step = one pass of the whole path over the layer in every mode:
+  bf16                 BF16 GEMMs (comparison)
+  fp8_delayed_autocast quantize both operands before each GEMM (delayed scaling,
+                       history 16, max) + GEMM; one scale-update launch per format
+  fp8_current_autocast two-pass current scaling before each GEMM + GEMM
+  fp8_current_prequant operands quantized once before timing; GEMM kernels only
+  mxfp8_autocast       MXFP8 1x32 quantization before each GEMM + MX GEMM
+  mxfp8_prequant       MX GEMM kernels only
+Delayed scaling has no pre-quantize number of its own: it relies on the amax
+history, so the page keeps it in autocast mode even with --pre-quantize.
+
+``value`` is the FP8 delayed-scaling layer in autocast mode (quantization
+included) in TFLOP/s: 19.17 TFLOP per layer / its measured time.  Inputs are
+synthetic (seeded N(0,1) activations with 0.1% x50 outliers, N(0,0.02) weights,
+Student-t(3) x 1e-3 gradients, bf16) and resident in HBM before timing starts.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MI355X_FP8_PEAK_TFLOPS = 5000.0   # dense FP8 MFMA (published)
+MI355X_BF16_PEAK_TFLOPS = 2500.0  # dense BF16 MFMA (published)
+MI355X_HBM_GBS = 8000.0           # HBM3E (published)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--modes", default="all")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=48, help="sampled output rows per GEMM for the oracle")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU: the path runs on one device and "
+                          "--gpus above 1 is not supported"}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from fp8_precision_transformer_amd import binding as B
+    from fp8_precision_transformer_amd import synth
+    from fp8_precision_transformer_amd.shapes import CODONFM_5B, layer_flops, layer_gemms, layer_weights
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    cfg = CODONFM_5B
+    M = cfg.tokens
+    weights = layer_weights(cfg)
+    gemms = layer_gemms(cfg)
+    LAYER_FLOPS = layer_flops(cfg)
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ---------------- inputs (host-generated, seeded; copied to HBM once) ----------------
+    t_gen = time.time()
+
+    def to_dev_bf16(x32):
+        bits = synth.to_bf16_bits(x32)
+        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    CFGID = 3
+    X, W, DY = {}, {}, {}
+    for li, w in enumerate(weights):
+        X[w.name] = to_dev_bf16(synth.activations((M, w.in_features), CFGID, li, synth.T_X, 0))
+        W[w.name] = to_dev_bf16(synth.normal((w.out_features, w.in_features), 0.02, CFGID, li, synth.T_W, 0))
+        DY[w.name] = to_dev_bf16(synth.grads((M, w.out_features), CFGID, li, synth.T_DY, 0))
+        log(f"inputs for {w.name} ready ({time.time() - t_gen:.1f}s)")
+    torch.cuda.synchronize()
+
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=dev)  # noqa: E731
+    f32 = lambda *s: torch.zeros(s, dtype=torch.float32, device=dev)  # noqa: E731
+    bf = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=dev)  # noqa: E731
+
+    # FP8 operand buffers per weight: row copies and transposed copies
+    def fp8_buffers():
+        q = {}
+        for w in weights:
+            K, N = w.in_features, w.out_features
+            q[w.name] = dict(x=u8(M, K), xT=u8(K, M), w=u8(N, K), wT=u8(K, N), dy=u8(M, N), dyT=u8(N, M))
+        return q
+
+    Q = fp8_buffers()       # written every step by the autocast modes
+    # outputs
+    OUT = {}
+    for w in weights:
+        K, N = w.in_features, w.out_features
+        OUT[w.name] = dict(fprop=bf(M, N), dgrad=bf(M, K), wgrad=bf(N, K))
+    # scaling state: E4M3 group = X (0..3) and W (4..7); E5M2 group = dY (0..3)
+    L = 16
+    hist4, s4, si4 = f32(8, L), torch.ones(8, device=dev), torch.ones(8, device=dev)
+    hist5, s5, si5 = f32(4, L), torch.ones(4, device=dev), torch.ones(4, device=dev)
+    new_cur = lambda: {w.name: {t: (f32(1), f32(1), f32(1)) for t in ("x", "w", "dy")} for w in weights}  # noqa: E731
+    cur = new_cur()
+    # BF16 transposed operands (materialised once; the BF16 GEMM is TN)
+    BT = {}
+    # MX buffers
+    def mx_buffers():
+        mb = {}
+        for w in weights:
+            K, N = w.in_features, w.out_features
+            mb[w.name] = dict(
+                x=u8(M, K), xs=u8(M, K // 32), xT=u8(K, M), xTs=u8(K, M // 32),
+                w=u8(N, K), ws=u8(N, K // 32), wT=u8(K, N), wTs=u8(K, N // 32),
+                dy=u8(M, N), dys=u8(M, N // 32), dyT=u8(N, M), dyTs=u8(N, M // 32))
+        return mb
+
+    MXB = mx_buffers()
+
+    modes_all = ["bf16", "fp8_delayed_autocast", "fp8_current_autocast", "fp8_current_prequant",
+                 "mxfp8_autocast", "mxfp8_prequant"]
+    modes = modes_all if args.modes == "all" else args.modes.split(",")
+    if "bf16" in modes:
+        for w in weights:
+            BT[w.name] = dict(wT=W[w.name].t().contiguous(), xT=X[w.name].t().contiguous(),
+                              dyT=DY[w.name].t().contiguous())
+
+    E4, E5, DEL, CUR = "E4M3", "E5M2", B.TE_SCALE_DELAYED, B.TE_SCALE_CURRENT
+
+    def quant_fp8(w, li, stage, mode, qset=None, cset=None):
+        """Quantize the two operands one GEMM needs, from their natural bf16 layout."""
+        q = (qset or Q)[w.name]
+        if mode == DEL:
+            sx = (s4[li:li + 1], si4[li:li + 1], hist4[li, 0:1])
+            sw = (s4[4 + li:5 + li], si4[4 + li:5 + li], hist4[4 + li, 0:1])
+            sg = (s5[li:li + 1], si5[li:li + 1], hist5[li, 0:1])
+        else:
+            c = (cset or cur)[w.name]
+            sx, sw, sg = c["x"], c["w"], c["dy"]
+        if stage == "fprop":
+            B.te_amax_cast(X[w.name], E4, mode, 0, *sx, q["x"])
+            B.te_amax_cast(W[w.name], E4, mode, 0, *sw, q["w"])
+            return (q["x"], E4, sx[1], q["w"], E4, sw[1])
+        if stage == "dgrad":
+            B.te_amax_cast(DY[w.name], E5, mode, 0, *sg, q["dy"])
+            B.te_cast_transpose(W[w.name], E4, mode, 0, *sw, None, q["wT"])
+            return (q["dy"], E5, sg[1], q["wT"], E4, sw[1])
+        B.te_cast_transpose(DY[w.name], E5, mode, 0, *sg, None, q["dyT"])
+        B.te_cast_transpose(X[w.name], E4, mode, 0, *sx, None, q["xT"])
+        return (q["dyT"], E5, sg[1], q["xT"], E4, sx[1])
+
+    def quant_mx(w, stage, bset=None):
+        b = (bset or MXB)[w.name]
+        if stage == "fprop":
+            B.te_mxfp8_quantize(X[w.name], E4, b["x"], b["xs"])
+            B.te_mxfp8_quantize(W[w.name], E4, b["w"], b["ws"])
+            return (b["x"], b["xs"], b["w"], b["ws"])
+        if stage == "dgrad":
+            B.te_mxfp8_quantize(DY[w.name], E4, b["dy"], b["dys"])
+            B.te_mxfp8_quantize(W[w.name], E4, None, None, b["wT"], b["wTs"])
+            return (b["dy"], b["dys"], b["wT"], b["wTs"])
+        B.te_mxfp8_quantize(DY[w.name], E4, None, None, b["dyT"], b["dyTs"])
+        B.te_mxfp8_quantize(X[w.name], E4, None, None, b["xT"], b["xTs"])
+        return (b["dyT"], b["dyTs"], b["xT"], b["xTs"])
+
+    prequant_fp8, prequant_mx = {}, {}
+
+    def prepare_prequant():
+        q_pre = fp8_buffers() if "fp8_current_prequant" in modes else None
+        c_pre = new_cur()
+        mx_pre = mx_buffers() if "mxfp8_prequant" in modes else None
+        for li, w in enumerate(weights):
+            for stage in ("fprop", "dgrad", "wgrad"):
+                if q_pre is not None:
+                    prequant_fp8[(w.name, stage)] = quant_fp8(w, li, stage, CUR, q_pre, c_pre)
+                if mx_pre is not None:
+                    prequant_mx[(w.name, stage)] = quant_mx(w, stage, mx_pre)
+        torch.cuda.synchronize()
+
+    def gemm_fp8(ops, out):
+        a, fa, sa, b, fb, sb = ops
+        B.te_fp8_gemm(a, fa, sa, b, fb, sb, out)
+
+    def gemm_mx(ops, out):
+        a, sa, b, sb = ops
+        B.te_fp8_gemm(a, E4, sa, b, E4, sb, out, gran=B.TE_GRAN_MX_BLOCK32)
+
+    def gemm_bf16(w, stage, out):
+        t = BT[w.name]
+        if stage == "fprop":
+            B.te_fp8_gemm(X[w.name], "BF16", None, W[w.name], "BF16", None, out)
+        elif stage == "dgrad":
+            B.te_fp8_gemm(DY[w.name], "BF16", None, t["wT"], "BF16", None, out)
+        else:
+            B.te_fp8_gemm(t["dyT"], "BF16", None, t["xT"], "BF16", None, out)
+
+    Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def run_mode(mode, rec):
+        """Enqueue one layer of `mode`; rec collects (key, ev_start, ev_mid, ev_end)."""
+        for li, w in enumerate(weights):
+            for stage in ("fprop", "dgrad", "wgrad"):
+                out = OUT[w.name][stage]
+                e0, e1, e2 = Ev(), Ev(), Ev()
+                e0.record()
+                if mode == "bf16":
+                    e1.record()
+                    gemm_bf16(w, stage, out)
+                elif mode == "fp8_delayed_autocast":
+                    ops = quant_fp8(w, li, stage, DEL)
+                    e1.record()
+                    gemm_fp8(ops, out)
+                elif mode == "fp8_current_autocast":
+                    ops = quant_fp8(w, li, stage, CUR)
+                    e1.record()
+                    gemm_fp8(ops, out)
+                elif mode == "fp8_current_prequant":
+                    e1.record()
+                    gemm_fp8(prequant_fp8[(w.name, stage)], out)
+                elif mode == "mxfp8_autocast":
+                    ops = quant_mx(w, stage)
+                    e1.record()
+                    gemm_mx(ops, out)
+                elif mode == "mxfp8_prequant":
+                    e1.record()
+                    gemm_mx(prequant_mx[(w.name, stage)], out)
+                e2.record()
+                rec.append((mode, w.name, stage, e0, e1, e2))
+        if mode == "fp8_delayed_autocast":
+            e0, e2 = Ev(), Ev()
+            e0.record()
+            B.te_scale_update(hist4, s4, si4, E4, B.TE_AMAX_MAX, 0)
+            B.te_scale_update(hist5, s5, si5, E5, B.TE_AMAX_MAX, 0)
+            e2.record()
+            rec.append((mode, "scale_update", "-", e0, e0, e2))
+
+    log("preparing pre-quantized operands")
+    prepare_prequant()
+    log(f"warmup {args.warmup} steps")
+    for _ in range(max(args.warmup, 0)):
+        rec = []
+        for mode in modes:
+            run_mode(mode, rec)
+    # delayed scaling reaches steady state after 16 updates; warmup steps count toward it
+    if "fp8_delayed_autocast" in modes:
+        for _ in range(max(0, 17 - args.warmup)):
+            run_mode("fp8_delayed_autocast", [])
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    recs = []
+    step_ms = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        es, ee = Ev(), Ev()
+        es.record()
+        rec = []
+        for mode in modes:
+            run_mode(mode, rec)
+        ee.record()
+        recs.append(rec)
+        step_ms.append((es, ee))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"timed region {wall:.2f}s")
+
+    # ---------------- reduce timings ----------------
+    per_layer = {m: [] for m in modes}
+    quant_ms = {m: [] for m in modes}
+    gemm_ms = {m: [] for m in modes}
+    per_gemm = {m: {} for m in modes}
+    for rec in recs:
+        acc = {m: 0.0 for m in modes}
+        accq = {m: 0.0 for m in modes}
+        accg = {m: 0.0 for m in modes}
+        for mode, wname, stage, e0, e1, e2 in rec:
+            tot = e0.elapsed_time(e2)
+            g = e1.elapsed_time(e2) if wname != "scale_update" else 0.0
+            acc[mode] += tot
+            accg[mode] += g
+            accq[mode] += tot - g
+            if wname != "scale_update":
+                per_gemm[mode].setdefault(f"{wname}.{stage}", []).append(g)
+        for m in modes:
+            per_layer[m].append(acc[m])
+            quant_ms[m].append(accq[m])
+            gemm_ms[m].append(accg[m])
+    med = lambda v: float(np.median(v))  # noqa: E731
+    pct = lambda v, q: float(np.percentile(v, q))  # noqa: E731
+    ms_layer = {m: med(per_layer[m]) for m in modes}
+    result_modes = {}
+    for m in modes:
+        result_modes[m] = {
+            "ms_per_layer": round(ms_layer[m], 4),
+            "p10": round(pct(per_layer[m], 10), 4), "p90": round(pct(per_layer[m], 90), 4),
+            "tflops": round(LAYER_FLOPS / (ms_layer[m] * 1e-3) / 1e12, 1),
+            "gemm_ms": round(med(gemm_ms[m]), 4),
+            "quant_ms": round(med(quant_ms[m]), 4),
+        }
+    step_total = [a.elapsed_time(b) for a, b in step_ms]
+
+    headline = "fp8_delayed_autocast" if "fp8_delayed_autocast" in modes else modes[0]
+    value = LAYER_FLOPS / (ms_layer[headline] * 1e-3) / 1e12
+
+    # roofline of the dominant kernel: the FP8 GEMM (kernel-only launches of the pre-quantize mode)
+    roof = None
+    gm = "fp8_current_prequant" if "fp8_current_prequant" in modes else None
+    if gm:
+        flops = sum(g.flops for g in gemms)
+        t_ms = sum(med(per_gemm[gm][f"{g.weight}.{g.stage}"]) for g in gemms)
+        achieved = flops / (t_ms * 1e-3) / 1e12 / 1.0
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MI355X_FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MI355X_FP8_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "k_gemm<KIND_FP8> (12 launches, 256x256x128 tiles)",
+                "avg_launch_ms": round(t_ms / len(gemms), 4)}
+    roof_q = None
+    if "fp8_delayed_autocast" in modes:
+        n_el = sum(2 * (M * w.in_features + w.out_features * w.in_features + M * w.out_features) for w in weights)
+        qbytes = 3 * n_el
+        qms = med(quant_ms["fp8_delayed_autocast"])
+        roof_q = {"bound": "hbm", "achieved": round(qbytes / (qms * 1e-3) / 1e9, 1), "peak": MI355X_HBM_GBS,
+                  "unit": "GB/s", "frac": round(qbytes / (qms * 1e-3) / 1e9 / MI355X_HBM_GBS, 4),
+                  "traffic": None, "algorithmic_bytes_per_layer": qbytes,
+                  "kernel": "delayed amax+cast / cast-transpose (24 launches + 2 scale updates per layer)"}
+
+    asym = None
+    if gm:
+        f = med(per_gemm[gm]["qkv.fprop"])
+        d = med(per_gemm[gm]["qkv.dgrad"])
+        asym = {"qkv_fprop_ms": round(f, 4), "qkv_dgrad_ms": round(d, 4), "dgrad_over_fprop": round(d / f, 3)}
+
+    per_gemm_out = {m: {k: round(med(v), 4) for k, v in per_gemm[m].items()} for m in modes}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, args.cpu_rows, log)
+
+    line = {
+        "metric": "FP8 GEMM TFLOP/s + ms/layer (autocast & pre-quantize), CodonFM-5B shapes",
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(med(step_total), 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": "CodonFM-5B-shaped layer: hidden 4096, intermediate 16384, M=31x512=15872; "
+                               "12 GEMMs (Fprop/Dgrad/Wgrad of QKV, attn-out, MLP-up, MLP-down)",
+                   "value_mode": headline, "layer_tflop": round(LAYER_FLOPS / 1e12, 3),
+                   "parallelism": "none (1 GPU)"},
+        "modes": result_modes,
+        "qkv_asymmetry": asym,
+        "per_gemm_ms": per_gemm_out,
+        "roofline": roof,
+        "roofline_quant": roof_q,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cfg, rows, log, cols=1024):
+    """The oracle, untuned, on a bounded sample of the same work: for each of the 12
+    GEMMs, `rows` x `cols` outputs over the full k, including the current-scaling amax
+    and cast of the sampled operand rows; reported as TFLOP/s of the sampled GEMM work."""
+    import oracle as O
+    from fp8_precision_transformer_amd import synth
+    from fp8_precision_transformer_amd.shapes import layer_gemms
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    gemms = layer_gemms(cfg)
+    total_flops = 0
+    t_total = 0.0
+    for gi, g in enumerate(gemms):
+        c = min(cols, g.n)
+        a32 = synth.activations((rows, g.k), 77, gi, 0, 0)
+        b32 = synth.normal((c, g.k), 0.02, 77, gi, 1, 0)
+        t0 = time.perf_counter()
+        sa = O.current_scale(O.amax(a32), O.E4M3)
+        sb = O.current_scale(O.amax(b32), O.E4M3)
+        aq = O.scaled_cast(a32, sa, O.E4M3)
+        bq = O.scaled_cast(b32, sb, O.E4M3)
+        O.gemm_per_tensor(aq, O.E4M3, O.scale_inverse(sa), bq, O.E4M3, O.scale_inverse(sb), out="bf16")
+        t_total += time.perf_counter() - t0
+        total_flops += 2 * rows * c * g.k
+    log(f"cpu oracle: {total_flops / 1e9:.1f} GFLOP in {t_total:.1f}s")
+    return {"value": round(total_flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{rows} rows x {cols} columns x full k of each of the 12 GEMMs "
+                      f"({total_flops / 1e9:.1f} GFLOP), current-scaling amax and casts of the sampled "
+                      f"operands included; {t_total:.1f} s on the host"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+"""Thin Python binding of libte_mi355x.so: argument marshalling only.
+
+Every call takes torch tensors that already live on the GPU, checks that they
+are contiguous and on one device, passes their data pointers, sizes and dtype
+codes to the C ABI (include/te_mi355x.h) together with the current HIP stream,
+and raises ``TEError`` with the library's message on any non-OK status.  No
+arithmetic of the method happens here; there is no fallback: if the library is
+missing, loading fails loudly.
+
+The library must bind to the same HIP runtime as PyTorch so that streams and
+device pointers are shared.  PyTorch is imported first; the library's
+dependency on ``libamdhip64.so.7`` is then satisfied by the copy already loaded.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+import torch  # noqa: F401  (loads PyTorch's HIP runtime before the library)
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libte_mi355x.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "te_mi355x.h")
+
+# te_status
+TE_OK, TE_ERR_NULL, TE_ERR_SHAPE, TE_ERR_DTYPE, TE_ERR_ALIGN, TE_ERR_UNSUPPORTED, TE_ERR_HIP, TE_ERR_ARG = range(8)
+STATUS_NAMES = ["TE_OK", "TE_ERR_NULL", "TE_ERR_SHAPE", "TE_ERR_DTYPE", "TE_ERR_ALIGN",
+                "TE_ERR_UNSUPPORTED", "TE_ERR_HIP", "TE_ERR_ARG"]
+# te_dtype
+TE_F32, TE_BF16, TE_E4M3, TE_E5M2, TE_E8M0 = range(5)
+# te_scaling, te_amax_algo, te_granularity
+TE_SCALE_DELAYED, TE_SCALE_CURRENT = 0, 1
+TE_AMAX_MAX, TE_AMAX_MOST_RECENT = 0, 1
+TE_GRAN_TENSOR, TE_GRAN_MX_BLOCK32 = 0, 1
+
+FP8_CODES = {"E4M3": TE_E4M3, "E5M2": TE_E5M2}
+
+
+class TEError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+        super().__init__(f"{name}: {msg}")
+        self.status = status
+
+
+_lib = None
+_lock = threading.Lock()
+
+_vp, _i64, _i32, _fp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+
+_SIGNATURES = {
+    "te_amax_cast": [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp],
+    "te_cast_transpose": [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp],
+    "te_scale_update": [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp],
+    "te_fp8_gemm": [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp, _i32, _vp],
+    "te_mxfp8_quantize": [_vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp],
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libte_mi355x.so (built by ``__graft_entry__.build()``); raises if missing."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                    "(there is no CPU or PyTorch fallback for this path)")
+            L = ctypes.CDLL(LIB_PATH)
+            for name, args in _SIGNATURES.items():
+                f = getattr(L, name)
+                f.argtypes = args
+                f.restype = ctypes.c_int
+            L.te_get_last_error.restype = ctypes.c_char_p
+            L.te_get_last_error.argtypes = []
+            L.te_version.restype = ctypes.c_char_p
+            L.te_version.argtypes = []
+            _lib = L
+    return _lib
+
+
+def header_functions(path: str = HEADER):
+    """Names of the functions include/te_mi355x.h declares."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(te_[a-z0-9_]+)\s*\(", text)))
+
+
+def _check(status: int):
+    if status != TE_OK:
+        raise TEError(status, lib().te_get_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _hp_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return TE_F32
+    if t.dtype == torch.bfloat16:
+        return TE_BF16
+    raise TypeError(f"unsupported input dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _fp8_code(fmt) -> int:
+    if isinstance(fmt, int):
+        return fmt
+    return FP8_CODES[str(fmt).upper()]
+
+
+def _need(t: torch.Tensor, name: str, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _2d(x: torch.Tensor):
+    if x.dim() == 2:
+        return x.shape[0], x.shape[1]
+    if x.dim() == 1:
+        return 1, x.shape[0]
+    return x.numel() // x.shape[-1], x.shape[-1]
+
+
+def te_amax_cast(x, out_dtype, mode, margin, scale, scale_inv, amax, out=None, stream=None):
+    for n, t in (("x", x), ("scale", scale), ("scale_inv", scale_inv), ("amax", amax), ("out", out)):
+        _need(t, n)
+    rows, cols = _2d(x)
+    _check(lib().te_amax_cast(_ptr(x), _hp_code(x), rows, cols, _fp8_code(out_dtype), int(mode), int(margin),
+                              _ptr(scale), _ptr(scale_inv), _ptr(amax), _ptr(out), _stream(stream)))
+
+
+def te_cast_transpose(x, out_dtype, mode, margin, scale, scale_inv, amax, out_row=None, out_col=None,
+                      stream=None):
+    for n, t in (("x", x), ("scale", scale), ("scale_inv", scale_inv), ("amax", amax),
+                 ("out_row", out_row), ("out_col", out_col)):
+        _need(t, n)
+    rows, cols = _2d(x)
+    _check(lib().te_cast_transpose(_ptr(x), _hp_code(x), rows, cols, _fp8_code(out_dtype), int(mode),
+                                   int(margin), _ptr(scale), _ptr(scale_inv), _ptr(amax), _ptr(out_row),
+                                   _ptr(out_col), _stream(stream)))
+
+
+def te_scale_update(amax_history, scale, scale_inv, fp8_dtype, algo=TE_AMAX_MAX, margin=0, stream=None):
+    for n, t in (("amax_history", amax_history), ("scale", scale), ("scale_inv", scale_inv)):
+        _need(t, n, torch.float32)
+    n_t, hist_len = (amax_history.shape[0], amax_history.shape[1]) if amax_history.dim() == 2 else (1, amax_history.shape[0])
+    _check(lib().te_scale_update(_ptr(amax_history), _ptr(scale), _ptr(scale_inv), n_t, hist_len,
+                                 _fp8_code(fp8_dtype), int(algo), int(margin), _stream(stream)))
+
+
+def te_fp8_gemm(a, a_dtype, a_scale, b, b_dtype, b_scale, d, bias=None, gran=TE_GRAN_TENSOR, stream=None):
+    """D[m, n] = A[m, k] . B[n, k]^T.  a, b: uint8 FP8 codes (or bf16 tensors with
+    a_dtype = b_dtype = "BF16"); a_scale/b_scale: fp32 [1] scale_inv or uint8 E8M0."""
+    for n, t in (("a", a), ("b", b), ("d", d), ("bias", bias), ("a_scale", a_scale), ("b_scale", b_scale)):
+        _need(t, n)
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k:
+        raise ValueError(f"k mismatch: a {tuple(a.shape)} b {tuple(b.shape)}")
+    if tuple(d.shape) != (m, n):
+        raise ValueError(f"d must be [{m}, {n}]")
+    ad = TE_BF16 if str(a_dtype).upper() == "BF16" else _fp8_code(a_dtype)
+    bd = TE_BF16 if str(b_dtype).upper() == "BF16" else _fp8_code(b_dtype)
+    dd = _hp_code(d)
+    bias_code = _hp_code(bias) if bias is not None else TE_F32
+    _check(lib().te_fp8_gemm(_ptr(a), ad, _ptr(a_scale), _ptr(b), bd, _ptr(b_scale), int(gran), m, n, k,
+                             _ptr(bias), bias_code, _ptr(d), dd, _stream(stream)))
+
+
+def te_mxfp8_quantize(x, elem_dtype, out_row=None, scale_row=None, out_col=None, scale_col=None, stream=None):
+    for n, t in (("x", x), ("out_row", out_row), ("scale_row", scale_row), ("out_col", out_col),
+                 ("scale_col", scale_col)):
+        _need(t, n)
+    rows, cols = _2d(x)
+    _check(lib().te_mxfp8_quantize(_ptr(x), _hp_code(x), rows, cols, _fp8_code(elem_dtype), _ptr(out_row),
+                                   _ptr(scale_row), _ptr(out_col), _ptr(scale_col), _stream(stream)))
+
+
+def version() -> str:
+    return lib().te_version().decode()

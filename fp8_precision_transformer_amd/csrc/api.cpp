@@ -1,0 +1,238 @@
+// C ABI of the FP8 linear-layer path (declared in include/te_mi355x.h).
+//
+// Every entry point validates its arguments on the host before any launch, then
+// enqueues kernels on the caller's stream.  Errors never throw across the ABI:
+// they return a te_status and leave text in a thread-local buffer.  Nothing
+// falls back to another precision: an unsupported combination is an error.
+// TE_LOG_LEVEL=1 prints each distinct dispatched kernel variant once,
+// TE_LOG_LEVEL=2 prints every launch (the pages' [LP-opt] "実モデルにおける結果の
+// 解釈" recommends checking which kernels actually run).
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <set>
+#include <string>
+
+#include "../../include/te_mi355x.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+te_status fail(te_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+int log_level() {
+  static int lvl = [] {
+    const char* e = std::getenv("TE_LOG_LEVEL");
+    return e ? std::atoi(e) : 0;
+  }();
+  return lvl;
+}
+
+void log_dispatch(const char* op, const char* variant, const char* detail) {
+  const int lvl = log_level();
+  if (lvl <= 0) return;
+  static std::mutex mu;
+  static std::set<std::string> seen;
+  std::lock_guard<std::mutex> lock(mu);
+  std::string key = std::string(op) + ":" + variant;
+  if (lvl == 1 && !seen.insert(key).second) return;
+  std::fprintf(stderr, "[te_mi355x] %s -> %s %s\n", op, variant, detail ? detail : "");
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// gfx950 check, once per device (the device list is small and fixed per process).
+te_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(TE_ERR_HIP, "hipGetDevice failed");
+  static std::mutex mu;
+  static int state[64] = {0};  // 0 unknown, 1 ok, 2 bad
+  if (dev < 0 || dev >= 64) return fail(TE_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (state[dev] == 0) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return fail(TE_ERR_HIP, "hipGetDeviceProperties failed");
+      state[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+      if (state[dev] == 2)
+        return fail(TE_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only", dev,
+                    prop.gcnArchName);
+    }
+  }
+  if (state[dev] == 2) return fail(TE_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return TE_OK;
+}
+
+te_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(TE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  g_err[0] = '\0';
+  return TE_OK;
+}
+
+bool is_fp8(int d) { return d == TE_E4M3 || d == TE_E5M2; }
+bool is_hp(int d) { return d == TE_F32 || d == TE_BF16; }
+
+te_status check_cast_common(const void* x, int x_dtype, int64_t rows, int64_t cols, int out_dtype,
+                            int mode, int margin, const float* scale, const float* scale_inv,
+                            const float* amax) {
+  if (rows < 0 || cols < 0) return fail(TE_ERR_SHAPE, "negative shape (%lld, %lld)", (long long)rows, (long long)cols);
+  if (!is_hp(x_dtype)) return fail(TE_ERR_DTYPE, "x_dtype must be TE_F32 or TE_BF16 (got %d)", x_dtype);
+  if (!is_fp8(out_dtype)) return fail(TE_ERR_DTYPE, "out_dtype must be TE_E4M3 or TE_E5M2 (got %d)", out_dtype);
+  if (mode != TE_SCALE_DELAYED && mode != TE_SCALE_CURRENT) return fail(TE_ERR_ARG, "bad scaling mode %d", mode);
+  if (margin < 0 || margin > 126) return fail(TE_ERR_ARG, "margin must be in [0, 126] (got %d)", margin);
+  if (!scale || !scale_inv || !amax) return fail(TE_ERR_NULL, "scale, scale_inv and amax are required");
+  if (rows * cols > 0 && !x) return fail(TE_ERR_NULL, "x is NULL");
+  if (x && !aligned16(x)) return fail(TE_ERR_ALIGN, "x is not 16-byte aligned");
+  if (cols != 0 && rows > (int64_t(1) << 62) / cols) return fail(TE_ERR_SHAPE, "shape too large");
+  return TE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* te_get_last_error(void) { return g_err; }
+
+const char* te_version(void) { return "te_mi355x 0.1 (gfx950)"; }
+
+te_status te_amax_cast(const void* x, int x_dtype, int64_t rows, int64_t cols, int out_dtype, int mode,
+                       int margin, float* scale, float* scale_inv, float* amax, uint8_t* out,
+                       void* stream) {
+  te_status st = check_cast_common(x, x_dtype, rows, cols, out_dtype, mode, margin, scale, scale_inv, amax);
+  if (st != TE_OK) return st;
+  if (out && !aligned16(out)) return fail(TE_ERR_ALIGN, "out is not 16-byte aligned");
+  if ((st = check_device()) != TE_OK) return st;
+  log_dispatch("te_amax_cast", mode == TE_SCALE_CURRENT ? "amax_pass+cast_pass" : "fused_amax_cast",
+               out_dtype == TE_E5M2 ? "E5M2" : "E4M3");
+  return hip_status(te::launch_amax_cast(x, x_dtype, rows * cols, out_dtype == TE_E5M2, mode == TE_SCALE_CURRENT,
+                                         margin, scale, scale_inv, amax, out,
+                                         static_cast<hipStream_t>(stream)),
+                    "te_amax_cast launch");
+}
+
+te_status te_cast_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols, int out_dtype, int mode,
+                            int margin, float* scale, float* scale_inv, float* amax, uint8_t* out_row,
+                            uint8_t* out_col, void* stream) {
+  te_status st = check_cast_common(x, x_dtype, rows, cols, out_dtype, mode, margin, scale, scale_inv, amax);
+  if (st != TE_OK) return st;
+  if (!out_row && !out_col) return fail(TE_ERR_NULL, "out_row and out_col are both NULL");
+  if ((out_row && !aligned16(out_row)) || (out_col && !aligned16(out_col)))
+    return fail(TE_ERR_ALIGN, "outputs must be 16-byte aligned");
+  if ((rows + 127) / 128 > 65535) return fail(TE_ERR_SHAPE, "rows too large for the tile grid");
+  if ((st = check_device()) != TE_OK) return st;
+  log_dispatch("te_cast_transpose", "tile128x64", out_dtype == TE_E5M2 ? "E5M2" : "E4M3");
+  return hip_status(te::launch_cast_transpose(x, x_dtype, rows, cols, out_dtype == TE_E5M2,
+                                              mode == TE_SCALE_CURRENT, margin, scale, scale_inv, amax,
+                                              out_row, out_col, static_cast<hipStream_t>(stream)),
+                    "te_cast_transpose launch");
+}
+
+te_status te_scale_update(float* amax_history, float* scale, float* scale_inv, int n, int hist_len,
+                          int fp8_dtype, int algo, int margin, void* stream) {
+  if (n < 0) return fail(TE_ERR_SHAPE, "n must be >= 0");
+  if (hist_len < 1 || hist_len > 4096) return fail(TE_ERR_SHAPE, "hist_len must be in [1, 4096]");
+  if (!is_fp8(fp8_dtype)) return fail(TE_ERR_DTYPE, "fp8_dtype must be TE_E4M3 or TE_E5M2");
+  if (algo != TE_AMAX_MAX && algo != TE_AMAX_MOST_RECENT) return fail(TE_ERR_ARG, "bad amax algo %d", algo);
+  if (margin < 0 || margin > 126) return fail(TE_ERR_ARG, "margin must be in [0, 126]");
+  if (n > 0 && (!amax_history || !scale || !scale_inv)) return fail(TE_ERR_NULL, "NULL state pointer");
+  te_status st = check_device();
+  if (st != TE_OK) return st;
+  log_dispatch("te_scale_update", algo == TE_AMAX_MAX ? "max" : "most_recent", "");
+  return hip_status(te::launch_scale_update(amax_history, scale, scale_inv, n, hist_len, fp8_dtype == TE_E5M2,
+                                            algo == TE_AMAX_MOST_RECENT, margin, static_cast<hipStream_t>(stream)),
+                    "te_scale_update launch");
+}
+
+te_status te_fp8_gemm(const void* a, int a_dtype, const void* a_scale, const void* b, int b_dtype,
+                      const void* b_scale, int gran, int64_t m, int64_t n, int64_t k, const void* bias,
+                      int bias_dtype, void* d, int d_dtype, void* stream) {
+  if (m < 0 || n < 0 || k < 0) return fail(TE_ERR_SHAPE, "negative GEMM shape");
+  if (n % 16 != 0 || k % 16 != 0)
+    return fail(TE_ERR_SHAPE, "n and k must be multiples of 16 (got n=%lld k=%lld)", (long long)n, (long long)k);
+  if (gran != TE_GRAN_TENSOR && gran != TE_GRAN_MX_BLOCK32) return fail(TE_ERR_ARG, "bad granularity %d", gran);
+  const bool bf16 = a_dtype == TE_BF16 && b_dtype == TE_BF16;
+  if (!bf16 && !(is_fp8(a_dtype) && is_fp8(b_dtype)))
+    return fail(TE_ERR_DTYPE, "a/b dtypes must both be FP8 (E4M3/E5M2) or both TE_BF16 (got %d, %d)", a_dtype, b_dtype);
+  if (bf16 && gran != TE_GRAN_TENSOR) return fail(TE_ERR_UNSUPPORTED, "BF16 GEMM takes no block scales");
+  if (gran == TE_GRAN_MX_BLOCK32 && k % 32 != 0) return fail(TE_ERR_SHAPE, "MX GEMM needs k %% 32 == 0");
+  if (d_dtype != TE_BF16 && d_dtype != TE_F32) return fail(TE_ERR_DTYPE, "d_dtype must be TE_BF16 or TE_F32");
+  if (bias && bias_dtype != TE_BF16 && bias_dtype != TE_F32) return fail(TE_ERR_DTYPE, "bias_dtype must be TE_BF16 or TE_F32");
+  if (m >= (int64_t(1) << 31) || n >= (int64_t(1) << 31)) return fail(TE_ERR_SHAPE, "m and n must be < 2^31");
+  const int64_t kb = k * (bf16 ? 2 : 1);
+  if (kb * 256 >= (int64_t(1) << 32)) return fail(TE_ERR_SHAPE, "k too large (256 rows of k must fit 4 GiB)");
+  if (m == 0 || n == 0) {
+    g_err[0] = '\0';
+    return TE_OK;
+  }
+  if (k == 0) return fail(TE_ERR_SHAPE, "k must be > 0 when m and n are");
+  if (!a || !b || !d) return fail(TE_ERR_NULL, "a, b and d are required");
+  if (!bf16 && (!a_scale || !b_scale)) return fail(TE_ERR_NULL, "FP8 GEMM needs a_scale and b_scale");
+  if (!aligned16(a) || !aligned16(b) || !aligned16(d)) return fail(TE_ERR_ALIGN, "a, b, d must be 16-byte aligned");
+  if (gran == TE_GRAN_MX_BLOCK32 && (!aligned16(a_scale) || !aligned16(b_scale)))
+    return fail(TE_ERR_ALIGN, "MX scale arrays must be 16-byte aligned");
+  te_status st = check_device();
+  if (st != TE_OK) return st;
+  te::GemmArgs g;
+  g.a = a;
+  g.b = b;
+  g.a_scale = a_scale;
+  g.b_scale = b_scale;
+  g.bias = bias;
+  g.d = d;
+  g.m = m;
+  g.n = n;
+  g.k = k;
+  g.a_fmt = a_dtype;
+  g.b_fmt = b_dtype;
+  g.mx = gran == TE_GRAN_MX_BLOCK32;
+  g.bias_bf16 = bias_dtype == TE_BF16;
+  g.d_bf16 = d_dtype == TE_BF16;
+  hipError_t e = te::launch_gemm(g, static_cast<hipStream_t>(stream));
+  if (log_level() > 0) {
+    char detail[128];
+    std::snprintf(detail, sizeof(detail), "m=%lld n=%lld k=%lld", (long long)m, (long long)n, (long long)k);
+    log_dispatch("te_fp8_gemm", te::last_gemm_variant(), detail);
+  }
+  return hip_status(e, "te_fp8_gemm launch");
+}
+
+te_status te_mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int elem_dtype,
+                            uint8_t* out_row, uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col,
+                            void* stream) {
+  if (rows < 0 || cols < 0) return fail(TE_ERR_SHAPE, "negative shape");
+  if (!is_hp(x_dtype)) return fail(TE_ERR_DTYPE, "x_dtype must be TE_F32 or TE_BF16");
+  if (!is_fp8(elem_dtype)) return fail(TE_ERR_DTYPE, "elem_dtype must be TE_E4M3 or TE_E5M2");
+  const bool row = out_row || scale_row, col = out_col || scale_col;
+  if (!row && !col) return fail(TE_ERR_NULL, "both output pairs are NULL");
+  if ((out_row == nullptr) != (scale_row == nullptr)) return fail(TE_ERR_NULL, "out_row and scale_row go together");
+  if ((out_col == nullptr) != (scale_col == nullptr)) return fail(TE_ERR_NULL, "out_col and scale_col go together");
+  if (row && cols % 32 != 0) return fail(TE_ERR_SHAPE, "row-wise MXFP8 needs cols %% 32 == 0");
+  if (col && rows % 32 != 0) return fail(TE_ERR_SHAPE, "column-wise MXFP8 needs rows %% 32 == 0");
+  if (rows * cols > 0 && !x) return fail(TE_ERR_NULL, "x is NULL");
+  if ((x && !aligned16(x)) || (out_row && !aligned16(out_row)) || (out_col && !aligned16(out_col)))
+    return fail(TE_ERR_ALIGN, "x and outputs must be 16-byte aligned");
+  if ((rows + 127) / 128 > 65535) return fail(TE_ERR_SHAPE, "rows too large for the tile grid");
+  te_status st = check_device();
+  if (st != TE_OK) return st;
+  log_dispatch("te_mxfp8_quantize", row && col ? "tile128x64_row+col" : (row ? "tile128x64_row" : "tile128x64_col"),
+               elem_dtype == TE_E5M2 ? "E5M2" : "E4M3");
+  return hip_status(te::launch_mxfp8_quantize(x, x_dtype, rows, cols, elem_dtype == TE_E5M2, out_row, scale_row,
+                                              out_col, scale_col, static_cast<hipStream_t>(stream)),
+                    "te_mxfp8_quantize launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Internal launcher declarations shared by the C-ABI layer (api.cpp) and the
+// kernel translation units.  Host-side only; arguments are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace te {
+
+// dtype codes mirror te_dtype in te_mi355x.h
+enum : int { F32 = 0, BF16 = 1, E4M3 = 2, E5M2 = 3, E8M0 = 4 };
+
+// ---- quantizers (quant.hip) ----
+hipError_t launch_amax_cast(const void* x, int x_dtype, int64_t n, int out_e5m2, int current,
+                            int margin, float* scale, float* scale_inv, float* amax,
+                            uint8_t* out, hipStream_t s);
+
+hipError_t launch_cast_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                                 int out_e5m2, int current, int margin, float* scale,
+                                 float* scale_inv, float* amax, uint8_t* out_row,
+                                 uint8_t* out_col, hipStream_t s);
+
+hipError_t launch_scale_update(float* hist, float* scale, float* scale_inv, int n, int hist_len,
+                               int e5m2, int most_recent, int margin, hipStream_t s);
+
+hipError_t launch_mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                                 int e5m2, uint8_t* out_row, uint8_t* scale_row,
+                                 uint8_t* out_col, uint8_t* scale_col, hipStream_t s);
+
+// ---- GEMM (gemm.hip) ----
+struct GemmArgs {
+  const void* a;
+  const void* b;
+  const void* a_scale;  // float* scale_inv (tensor) or uint8 E8M0 (MX) or null (bf16)
+  const void* b_scale;
+  const void* bias;
+  void* d;
+  int64_t m, n, k;       // elements
+  int a_fmt, b_fmt;      // E4M3 / E5M2 / BF16
+  int mx;                // 1: MX block-32 scales
+  int bias_bf16;         // bias dtype: 0 f32, 1 bf16
+  int d_bf16;            // output dtype: 0 f32, 1 bf16
+};
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
+
+// Name of the kernel variant the last launch_gemm on this thread dispatched
+// (for logging; see TE_LOG_LEVEL in api.cpp).
+const char* last_gemm_variant();
+
+}  // namespace te

@@ -37,6 +37,7 @@ def generator(*key: int) -> np.random.Generator:
 
 
 def _chunked(shape, key, fill):
+    """Fill a float32 array chunk by chunk; fill(gen, out_slice) writes the slice in place."""
     n = int(np.prod(shape)) if len(shape) else 1
     out = np.empty(n, dtype=np.float32)
     starts = list(range(0, n, CHUNK))
@@ -44,8 +45,7 @@ def _chunked(shape, key, fill):
     def work(ci):
         s = starts[ci]
         e = min(n, s + CHUNK)
-        g = generator(*key, ci)
-        out[s:e] = fill(g, e - s)
+        fill(generator(*key, ci), out[s:e])
 
     workers = max(1, min(8, os.cpu_count() or 1, len(starts)))
     if workers == 1:
@@ -58,12 +58,17 @@ def _chunked(shape, key, fill):
 
 
 def uniform01(shape, *key) -> np.ndarray:
-    return _chunked(shape, key, lambda g, k: g.random(k, dtype=np.float32))
+    return _chunked(shape, key, lambda g, o: g.random(dtype=np.float32, out=o))
 
 
 def normal(shape, std, *key) -> np.ndarray:
     std = np.float32(std)
-    return _chunked(shape, key, lambda g, k: g.standard_normal(k, dtype=np.float32) * std)
+
+    def fill(g, o):
+        g.standard_normal(dtype=np.float32, out=o)
+        o *= std
+
+    return _chunked(shape, key, fill)
 
 
 def activations(shape, *key, outlier_frac=1e-3, outlier_mult=50.0) -> np.ndarray:
@@ -80,9 +85,20 @@ def activations(shape, *key, outlier_frac=1e-3, outlier_mult=50.0) -> np.ndarray
 
 
 def grads(shape, *key, nu=3.0, scale=1e-3) -> np.ndarray:
-    """Student-t(nu) times scale."""
-    sc = np.float64(scale)
-    return _chunked(shape, key, lambda g, k: (g.standard_t(nu, k) * sc).astype(np.float32))
+    """Student-t(nu) times scale, sampled as sqrt(nu/2) * Z / sqrt(G) with Z ~ N(0,1) and
+    G ~ Gamma(nu/2, 1) (the ratio of a normal and a chi-square root)."""
+    c = np.float32(np.sqrt(nu / 2.0) * scale)
+
+    def fill(g, o):
+        g.standard_normal(dtype=np.float32, out=o)
+        gam = np.empty_like(o)
+        g.standard_gamma(nu / 2.0, dtype=np.float32, out=gam)
+        np.maximum(gam, np.float32(1e-30), out=gam)  # a zero draw would give an infinite sample
+        np.sqrt(gam, out=gam)
+        o /= gam
+        o *= c
+
+    return _chunked(shape, key, fill)
 
 
 def to_bf16_bits(x32: np.ndarray) -> np.ndarray:

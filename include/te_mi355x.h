@@ -1,0 +1,211 @@
+/*
+ * te_mi355x.h -- C ABI of the MI355X (gfx950) per-tensor scaled FP8 linear-layer path.
+ *
+ * Pages cited (by title; sections are the pages' own headings):
+ *   [TE-summary] "NVIDIA Transformer Engine - 大規模Transformer向け高速低精度学習"
+ *   [TE-readme]  "transformerengine" (README summary)
+ *   [FP8-intro]  "Introduction to FP8 training using Transformer Engine"
+ *                (NVIDIA technical blog, Japanese edition)
+ *   [LP-opt]     "How to Optimize Transformer-Based Models for Low-Precision Training"
+ *                (NVIDIA technical blog, Japanese translation)
+ *
+ * [TE-readme] says the library carries a framework-agnostic C++ API so that
+ * other deep-learning libraries can add FP8; this header is that API reduced to
+ * the five operations of the FP8 linear layer.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller allocates
+ *     and owns every buffer, including the scaling state.  The library keeps no
+ *     pointer after a call returns, allocates nothing and holds no global state
+ *     besides a per-thread error string and a per-device architecture check.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
+ *     default stream).  There is no host synchronization inside.  Scale, amax
+ *     and history values never leave the device.
+ *   - Layout is row-major.  A matrix [R, C] has C contiguous elements per row.
+ *   - Pointers must be 16-byte aligned (TE_ERR_ALIGN otherwise).
+ *   - Arguments are validated on the host before any launch; a rejected call
+ *     launches nothing, returns a te_status and sets te_get_last_error().  A
+ *     launch failure returns TE_ERR_HIP.  No exception or abort crosses the ABI.
+ *   - An unsupported combination returns TE_ERR_UNSUPPORTED; nothing falls back
+ *     silently to another precision ([LP-opt] "実モデルにおける結果の解釈" warns
+ *     that silent fallback hides itself as matching performance).
+ *   - The first call on a device checks that it is gfx950 (TE_ERR_UNSUPPORTED
+ *     otherwise).
+ *   - Calls that write the same buffers must not overlap; calls on one stream
+ *     are ordered by the stream.
+ *
+ * FP8 formats: E4M3 (bias 7, no infinities, max 448) and E5M2 (bias 15, max
+ * 57344), per the FP8 paper that [TE-summary] "導入とリソース" points to.  The
+ * cast rounds to nearest even and saturates (finite overflow and +-Inf map to
+ * +-max; NaN maps to a NaN code).
+ */
+#ifndef TE_MI355X_H
+#define TE_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TE_OK = 0,
+  TE_ERR_NULL = 1,        /* a required pointer is NULL */
+  TE_ERR_SHAPE = 2,       /* a size is negative or breaks a divisibility rule */
+  TE_ERR_DTYPE = 3,       /* a dtype is not allowed for that argument */
+  TE_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  TE_ERR_UNSUPPORTED = 5, /* valid request this library does not implement, or not gfx950 */
+  TE_ERR_HIP = 6,         /* the HIP runtime reported an error (launch or device query) */
+  TE_ERR_ARG = 7          /* an enum or scalar argument is out of range */
+} te_status;
+
+typedef enum { TE_F32 = 0, TE_BF16 = 1, TE_E4M3 = 2, TE_E5M2 = 3, TE_E8M0 = 4 } te_dtype;
+
+/* [FP8-intro] "FP8 Training について": one scale per tensor, refreshed every step.
+ * DELAYED: the scale comes from the amax history of earlier steps
+ * ([FP8-intro] "Transformer Engine の使い方": DelayedScaling); CURRENT: from this
+ * tensor's own amax ([LP-opt] "実モデルにおける結果の解釈", FP8 CurrentScaling). */
+typedef enum { TE_SCALE_DELAYED = 0, TE_SCALE_CURRENT = 1 } te_scaling;
+
+/* [FP8-intro] "Transformer Engine 統合済みライブラリの利用" (NeMo keys):
+ * fp8_amax_compute_algo is 'max' or 'most_recent'. */
+typedef enum { TE_AMAX_MAX = 0, TE_AMAX_MOST_RECENT = 1 } te_amax_algo;
+
+/* TENSOR: one fp32 scale_inv per operand.  MX_BLOCK32: one E8M0 exponent per 32
+ * consecutive elements along K (MXFP8, [TE-summary] "主な機能"). */
+typedef enum { TE_GRAN_TENSOR = 0, TE_GRAN_MX_BLOCK32 = 1 } te_granularity;
+
+/*
+ * te_amax_cast -- amax reduction and scaled saturating cast of one tensor to FP8.
+ *
+ * Defines: [FP8-intro] "FP8 Training について" (per-tensor scaling factor, cast
+ * to FP8 at compute time); [TE-summary] "主な機能" (amax tracking);
+ * [LP-opt] "autocast モードの使用と事前量子化の比較" (inputs are quantized before
+ * each GEMM in autocast mode).
+ *
+ *   x          [rows, cols] of x_dtype (TE_F32 or TE_BF16).
+ *   out_dtype  TE_E4M3 (forward tensors) or TE_E5M2 (gradients) -- HYBRID.
+ *   mode       TE_SCALE_DELAYED: reads *scale (set by te_scale_update).
+ *              TE_SCALE_CURRENT: computes amax first, then
+ *                *scale = fl32(fp8_max / amax) * 2^-margin (overflow -> FLT_MAX;
+ *                amax 0 or non-finite -> 1.0), and casts with it (two passes
+ *                over x: the amax must exist before the first element is cast).
+ *   margin     >= 0; scale multiplier 2^-margin (CURRENT only; DELAYED applies
+ *              its margin in te_scale_update).
+ *   scale      [1] fp32.  DELAYED: read.  CURRENT: written.
+ *   scale_inv  [1] fp32, written = fl32(1 / scale used).
+ *   amax       [1] fp32, written = max_i |x_i| (overwritten, not accumulated;
+ *              point it at slot 0 of the tensor's amax history for DELAYED).
+ *              NaN inputs make amax unspecified.
+ *   out        [rows, cols] uint8 codes, out_i = satRNE(fl32(x_i * scale)).
+ *              May be NULL: then only amax (and, for CURRENT, scale/scale_inv)
+ *              is produced.
+ * Any rows, cols >= 0 (0 elements: amax = 0 and, for CURRENT, scale = 1).
+ */
+te_status te_amax_cast(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                       int out_dtype, int mode, int margin,
+                       float* scale, float* scale_inv, float* amax,
+                       uint8_t* out, void* stream);
+
+/*
+ * te_cast_transpose -- te_amax_cast that also (or only) writes the byte transpose.
+ *
+ * Not named on the pages; needed because every GEMM here is "TN" (both
+ * operands K-contiguous): Dgrad consumes W^T and Wgrad consumes X^T and dY^T
+ * ([LP-opt] "autocast モードの使用と事前量子化の比較": Fprop, Dgrad and Wgrad are
+ * separate GEMMs).
+ *
+ * Arguments as te_amax_cast, plus
+ *   out_row  [rows, cols] uint8 or NULL.
+ *   out_col  [cols, rows] uint8 or NULL; out_col[c, r] == out_row[r, c] byte for byte.
+ * At least one of out_row / out_col must be non-NULL.
+ */
+te_status te_cast_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                            int out_dtype, int mode, int margin,
+                            float* scale, float* scale_inv, float* amax,
+                            uint8_t* out_row, uint8_t* out_col, void* stream);
+
+/*
+ * te_scale_update -- delayed-scaling update of n tensors of one FP8 format.
+ *
+ * Defines: [FP8-intro] "Transformer Engine の使い方" (DelayedScaling with
+ * amax_history_len=16, amax_compute_algo="max"); [FP8-intro] "Transformer Engine
+ * 統合済みライブラリの利用" (margin, update interval 1, 'max' or 'most_recent').
+ *
+ *   amax_history  [n, hist_len] fp32, slot 0 = newest (filled by te_amax_cast).
+ *   scale, scale_inv  [n] fp32, read and written.
+ * For each tensor t:  a = max(hist[t, :]) (TE_AMAX_MAX) or hist[t, 0]
+ * (TE_AMAX_MOST_RECENT);  if a is finite and > 0: scale = fl32(fp8_max / a)
+ * (overflow -> FLT_MAX) * 2^-margin, else scale unchanged;  scale_inv =
+ * fl32(1/scale);  then the history rolls: hist[t, i] = hist[t, i-1] for i >= 1,
+ * hist[t, 0] = 0.  fp8_dtype (TE_E4M3 / TE_E5M2) selects fp8_max.
+ * n >= 0, 1 <= hist_len <= 4096.
+ */
+te_status te_scale_update(float* amax_history, float* scale, float* scale_inv,
+                          int n, int hist_len, int fp8_dtype, int algo, int margin,
+                          void* stream);
+
+/*
+ * te_fp8_gemm -- D[m, n] = A[m, k] . B[n, k]^T with a dequantizing epilogue.
+ *
+ * Defines: [FP8-intro] "FP8 Training について" (FP8 tensor-core GEMM, twice the
+ * FLOPS of FP16/BF16); [LP-opt] "autocast モードの使用と事前量子化の比較" (Fprop,
+ * Dgrad, Wgrad benchmarked separately); [FP8-intro] "Transformer Engine の使い方"
+ * (te.Linear with bias).
+ *
+ *   a, b       A [m, k], B [n, k] row-major (k contiguous in both: "TN").
+ *   a_dtype, b_dtype  TE_E4M3 / TE_E5M2 in any combination (HYBRID Dgrad and
+ *              Wgrad use E5M2 x E4M3), or both TE_BF16 for the BF16 baseline.
+ *   gran = TE_GRAN_TENSOR: a_scale, b_scale are float* [1] scale_inv values
+ *              (NULL for BF16):  D = fl32(fl32(acc * a_scale) * b_scale) + bias.
+ *   gran = TE_GRAN_MX_BLOCK32: a_scale uint8 E8M0 [m, k/32], b_scale uint8 E8M0
+ *              [n, k/32] (row-major); element formats E4M3/E5M2;
+ *              D = sum_blocks 2^(ea-127) 2^(eb-127) (block dot) + bias.  k % 32 == 0.
+ *   acc        fp32 accumulation on the matrix cores.
+ *   bias       [n] of bias_dtype (TE_F32 or TE_BF16, widened to fp32) or NULL.
+ *   d          [m, n] of d_dtype (TE_BF16, rounded to nearest even, or TE_F32).
+ * Shape rules: m >= 0; n % 16 == 0 and k % 16 == 0 ([FP8-intro] "HuggingFace BERT
+ * を例にした Transformer Engine の適用": Linear dims must be multiples of 16 for
+ * the tensor cores), k > 0 unless m == 0 or n == 0.
+ */
+te_status te_fp8_gemm(const void* a, int a_dtype, const void* a_scale,
+                      const void* b, int b_dtype, const void* b_scale,
+                      int gran, int64_t m, int64_t n, int64_t k,
+                      const void* bias, int bias_dtype,
+                      void* d, int d_dtype, void* stream);
+
+/*
+ * te_mxfp8_quantize -- MXFP8 block quantization, row-wise and/or column-wise.
+ *
+ * Defines: [TE-summary] "主な機能" and [TE-readme] (MXFP8 recipe); [LP-opt]
+ * "autocast モードの使用と事前量子化の比較" (per-block scale computation and format
+ * conversion are part of the autocast cost).  Block rule (OCP MX v1.0 reading):
+ * for 32 consecutive elements, e = floor(log2(max|x|)) - emax_elem (8 for E4M3,
+ * 15 for E5M2), clamped to [-127, 127]; scale code = e + 127 (127 for an all-zero
+ * block); elements = satRNE(x * 2^-e).
+ *
+ *   x          [rows, cols] of x_dtype (TE_F32 or TE_BF16).
+ *   elem_dtype TE_E4M3 (or TE_E5M2).
+ *   out_row    [rows, cols] uint8, blocks along cols; scale_row [rows, cols/32] E8M0.
+ *   out_col    [cols, rows] uint8 = MXFP8 of x^T (blocks along rows, an
+ *              independent quantization, not a transpose of out_row);
+ *              scale_col [cols, rows/32] E8M0.
+ * Either pair may be NULL (not both).  Row pair needs cols % 32 == 0; col pair
+ * needs rows % 32 == 0.
+ */
+te_status te_mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                            int elem_dtype, uint8_t* out_row, uint8_t* scale_row,
+                            uint8_t* out_col, uint8_t* scale_col, void* stream);
+
+/* Text of the last error on the calling thread ("" if none).  Host pointer owned
+ * by the library, valid until the next call on this thread. */
+const char* te_get_last_error(void);
+
+/* Library version string (host, static). */
+const char* te_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TE_MI355X_H */

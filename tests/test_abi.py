@@ -1,0 +1,117 @@
+"""C-ABI boundary on the host: the library loads, exports every function that
+include/te_mi355x.h declares, and rejects invalid arguments with the right
+status before any HIP call (no compute, no GPU needed)."""
+
+import ctypes
+import os
+
+import pytest
+
+from fp8_precision_transformer_amd import binding as B
+
+needs_lib = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="library not built")
+
+FAKE = ctypes.c_void_p(0x10000)        # never dereferenced: validation fails first
+FAKE_MIS = ctypes.c_void_p(0x10008)    # 8-byte aligned only
+
+
+@needs_lib
+def test_exports_every_header_function():
+    L = B.lib()
+    names = B.header_functions()
+    assert set(names) >= {"te_amax_cast", "te_cast_transpose", "te_scale_update", "te_fp8_gemm",
+                          "te_mxfp8_quantize", "te_get_last_error"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert b"gfx950" in L.te_version()
+
+
+def _gemm(**kw):
+    args = dict(a=FAKE, a_dtype=B.TE_E4M3, a_scale=FAKE, b=FAKE, b_dtype=B.TE_E4M3, b_scale=FAKE,
+                gran=B.TE_GRAN_TENSOR, m=64, n=64, k=64, bias=None, bias_dtype=B.TE_F32, d=FAKE,
+                d_dtype=B.TE_BF16, stream=None)
+    args.update(kw)
+    return B.lib().te_fp8_gemm(*args.values())
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=15), B.TE_ERR_SHAPE),
+    (dict(k=24), B.TE_ERR_SHAPE),
+    (dict(m=-1), B.TE_ERR_SHAPE),
+    (dict(a_dtype=B.TE_F32), B.TE_ERR_DTYPE),
+    (dict(a_dtype=B.TE_BF16), B.TE_ERR_DTYPE),
+    (dict(d_dtype=B.TE_E4M3), B.TE_ERR_DTYPE),
+    (dict(gran=9), B.TE_ERR_ARG),
+    (dict(gran=B.TE_GRAN_MX_BLOCK32, k=48), B.TE_ERR_SHAPE),
+    (dict(a_dtype=B.TE_BF16, b_dtype=B.TE_BF16, gran=B.TE_GRAN_MX_BLOCK32), B.TE_ERR_UNSUPPORTED),
+    (dict(a=None), B.TE_ERR_NULL),
+    (dict(a_scale=None), B.TE_ERR_NULL),
+    (dict(d=FAKE_MIS), B.TE_ERR_ALIGN),
+    (dict(k=0), B.TE_ERR_SHAPE),
+    (dict(bias=FAKE, bias_dtype=B.TE_E5M2), B.TE_ERR_DTYPE),
+])
+def test_gemm_validation(kw, status):
+    assert _gemm(**kw) == status
+    assert len(B.lib().te_get_last_error()) > 0
+
+
+@needs_lib
+def test_gemm_empty_is_ok_without_launch():
+    assert _gemm(m=0) == B.TE_OK
+    assert _gemm(n=0, a=None, b=None, d=None) == B.TE_OK
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=-1), B.TE_ERR_SHAPE),
+    (dict(x_dtype=B.TE_E4M3), B.TE_ERR_DTYPE),
+    (dict(out_dtype=B.TE_BF16), B.TE_ERR_DTYPE),
+    (dict(mode=5), B.TE_ERR_ARG),
+    (dict(margin=-1), B.TE_ERR_ARG),
+    (dict(scale=None), B.TE_ERR_NULL),
+    (dict(amax=None), B.TE_ERR_NULL),
+    (dict(x=FAKE_MIS), B.TE_ERR_ALIGN),
+    (dict(out=FAKE_MIS), B.TE_ERR_ALIGN),
+])
+def test_amax_cast_validation(kw, status):
+    args = dict(x=FAKE, x_dtype=B.TE_BF16, rows=4, cols=4, out_dtype=B.TE_E4M3, mode=B.TE_SCALE_DELAYED,
+                margin=0, scale=FAKE, scale_inv=FAKE, amax=FAKE, out=FAKE, stream=None)
+    args.update(kw)
+    assert B.lib().te_amax_cast(*args.values()) == status
+
+
+@needs_lib
+def test_cast_transpose_needs_an_output():
+    assert B.lib().te_cast_transpose(FAKE, B.TE_BF16, 4, 4, B.TE_E4M3, 0, 0, FAKE, FAKE, FAKE,
+                                     None, None, None) == B.TE_ERR_NULL
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), B.TE_ERR_SHAPE),
+    (dict(hist_len=0), B.TE_ERR_SHAPE),
+    (dict(fp8_dtype=B.TE_F32), B.TE_ERR_DTYPE),
+    (dict(algo=3), B.TE_ERR_ARG),
+    (dict(hist=None), B.TE_ERR_NULL),
+])
+def test_scale_update_validation(kw, status):
+    args = dict(hist=FAKE, scale=FAKE, scale_inv=FAKE, n=4, hist_len=16, fp8_dtype=B.TE_E4M3,
+                algo=B.TE_AMAX_MAX, margin=0, stream=None)
+    args.update(kw)
+    assert B.lib().te_scale_update(*args.values()) == status
+
+
+@needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(cols=48), B.TE_ERR_SHAPE),
+    (dict(out_row=None, scale_row=None, rows=48), B.TE_ERR_SHAPE),
+    (dict(scale_row=None), B.TE_ERR_NULL),
+    (dict(out_row=None, scale_row=None, out_col=None, scale_col=None), B.TE_ERR_NULL),
+    (dict(elem_dtype=B.TE_E8M0), B.TE_ERR_DTYPE),
+])
+def test_mxfp8_validation(kw, status):
+    args = dict(x=FAKE, x_dtype=B.TE_BF16, rows=64, cols=64, elem_dtype=B.TE_E4M3, out_row=FAKE,
+                scale_row=FAKE, out_col=FAKE, scale_col=FAKE, stream=None)
+    args.update(kw)
+    assert B.lib().te_mxfp8_quantize(*args.values()) == status

@@ -1,0 +1,194 @@
+"""GPU parity of the GEMMs (per-tensor FP8, MXFP8, BF16) against the CPU oracle.
+
+Tolerance (max relative error with the 1e-3 * max|ref| floor of oracle.rel_err):
+1e-2 for bf16 output, 1e-3 for fp32 output.  Where the result is exact in any
+summation order (integer-valued operands, |sum| < 2^24, power-of-two scales)
+the fp32 output must match bit for bit.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from fp8_precision_transformer_amd import binding as B
+from fp8_precision_transformer_amd import synth
+from fp8_precision_transformer_amd.shapes import CODONFM_5B, layer_gemms
+
+from gpu_util import DEV, dev_f32, dev_u8, host, scalar
+
+pytestmark = pytest.mark.gpu
+
+FMTS = {"E4M3": O.E4M3, "E5M2": O.E5M2}
+TOL = {"bf16": 1e-2, "f32": 1e-3}
+
+
+def _seed(*key) -> int:
+    return zlib.crc32(repr(key).encode()) & 0xFFFF
+
+
+def _quantized(shape, fmt, key, kind="act"):
+    """Seeded FP8 codes of a realistic tensor: current-scaled cast of synthetic data."""
+    x = synth.activations(shape, *key) if kind == "act" else synth.grads(shape, *key)
+    f = FMTS[fmt]
+    s = O.current_scale(O.amax(x), f)
+    return O.scaled_cast(x, s, f), O.scale_inverse(s)
+
+
+def _out(m, n, odt):
+    return torch.empty((m, n), dtype=torch.bfloat16 if odt == "bf16" else torch.float32, device=DEV)
+
+
+GEMM_SHAPES = [(16, 16, 16), (1, 16, 128), (300, 272, 400), (256, 256, 128), (513, 512, 1024),
+               (1024, 768, 768), (64, 2304, 768), (4096, 48, 272)]
+
+
+@pytest.mark.parametrize("mnk", GEMM_SHAPES, ids=str)
+@pytest.mark.parametrize("fa,fb", [("E4M3", "E4M3"), ("E5M2", "E4M3"), ("E4M3", "E5M2"), ("E5M2", "E5M2")])
+@pytest.mark.parametrize("odt", ["bf16", "f32"])
+@pytest.mark.parametrize("bias", [None, "f32", "bf16"])
+def test_fp8_gemm_parity(mnk, fa, fb, odt, bias):
+    m, n, k = mnk
+    sd = _seed(mnk, fa, fb, odt, bias)
+    a, sa = _quantized((m, k), fa, (11, sd, 0, 0), "act" if fa == "E4M3" else "grad")
+    b, sb = _quantized((n, k), fb, (11, sd, 1, 0))
+    bias_h = synth.normal((n,), 0.02, 11, sd, 2, 0) if bias else None
+    if bias == "bf16":
+        bits = synth.to_bf16_bits(bias_h)
+        bias_d = torch.from_numpy(bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+        bias_h = synth.bf16_bits_as_f32(bits)
+    elif bias == "f32":
+        bias_d = dev_f32(bias_h)
+    else:
+        bias_d = None
+    d = _out(m, n, odt)
+    B.te_fp8_gemm(dev_u8(a), fa, scalar(float(sa)), dev_u8(b), fb, scalar(float(sb)), d, bias=bias_d)
+    ref = O.gemm_per_tensor(a, FMTS[fa], sa, b, FMTS[fb], sb, bias=bias_h, out=odt)
+    err = O.rel_err(host(d), ref)
+    assert err <= TOL[odt], err
+
+
+@pytest.mark.parametrize("mnk", [(64, 64, 128), (200, 96, 512), (512, 512, 2048)], ids=str)
+def test_fp8_gemm_exact_integer_operands(mnk):
+    """Integer-valued FP8 operands with |sum| < 2^24: the fp32 result is exact in any order."""
+    m, n, k = mnk
+    rng = np.random.default_rng(_seed(mnk))
+    ints = np.arange(-16, 17)
+    codes = O.encode(ints.astype(np.float32), O.E4M3)
+    a = codes[rng.integers(0, len(ints), (m, k))]
+    b = codes[rng.integers(0, len(ints), (n, k))]
+    d = _out(m, n, "f32")
+    B.te_fp8_gemm(dev_u8(a), "E4M3", scalar(0.5), dev_u8(b), "E4M3", scalar(4.0), d)
+    ref = O.gemm_per_tensor(a, O.E4M3, 0.5, b, O.E4M3, 4.0, out="f32")
+    np.testing.assert_array_equal(host(d), ref)
+
+
+def test_fp8_gemm_identity_and_bias_only():
+    k = 256
+    rng = np.random.default_rng(3)
+    a = O.encode(rng.standard_normal((96, k)).astype(np.float32) * 10, O.E5M2)
+    eye = np.where(np.eye(k, dtype=bool), 0x38, 0).astype(np.uint8)
+    d = _out(96, k, "f32")
+    B.te_fp8_gemm(dev_u8(a), "E5M2", scalar(0.25), dev_u8(eye), "E4M3", scalar(2.0), d)
+    np.testing.assert_array_equal(host(d), (O.decode_table(O.E5M2)[a] * 0.5).astype(np.float32))
+    bias = rng.standard_normal(k).astype(np.float32)
+    z = np.zeros((33, k), np.uint8)
+    d2 = _out(33, k, "f32")
+    B.te_fp8_gemm(dev_u8(z), "E4M3", scalar(3.0), dev_u8(eye), "E4M3", scalar(5.0), d2, bias=dev_f32(bias))
+    np.testing.assert_array_equal(host(d2), np.broadcast_to(bias, (33, k)))
+
+
+@pytest.mark.parametrize("mnk", [(16, 16, 32), (300, 272, 416), (1024, 768, 768), (256, 512, 4096)], ids=str)
+def test_bf16_gemm_parity(mnk):
+    m, n, k = mnk
+    sd = _seed(mnk)
+    ab = synth.to_bf16_bits(synth.activations((m, k), 12, sd, 0, 0))
+    bb = synth.to_bf16_bits(synth.normal((n, k), 0.02, 12, sd, 1, 0))
+    ad = torch.from_numpy(ab.view(np.int16)).to(DEV).view(torch.bfloat16)
+    bd = torch.from_numpy(bb.view(np.int16)).to(DEV).view(torch.bfloat16)
+    for odt in ("bf16", "f32"):
+        d = _out(m, n, odt)
+        B.te_fp8_gemm(ad, "BF16", None, bd, "BF16", None, d)
+        ref = O.gemm_bf16(ab, bb, out=odt)
+        err = O.rel_err(host(d), ref)
+        assert err <= TOL[odt], (odt, err)
+
+
+@pytest.mark.parametrize("mnk", [(32, 32, 64), (300, 272, 416), (1024, 768, 768), (256, 256, 4096),
+                                 (64, 128, 96)], ids=str)
+@pytest.mark.parametrize("fa,fb", [("E4M3", "E4M3"), ("E5M2", "E4M3")])
+def test_mx_gemm_parity(mnk, fa, fb):
+    m, n, k = mnk
+    sd = _seed(mnk, fa, fb)
+    xa = synth.activations((m, k), 13, sd, 0, 0) if fa == "E4M3" else synth.grads((m, k), 13, sd, 0, 0)
+    xb = synth.normal((n, k), 0.02, 13, sd, 1, 0)
+    qa, ea = O.mxfp8_quantize(xa, FMTS[fa])
+    qb, eb = O.mxfp8_quantize(xb, FMTS[fb])
+    bias = synth.normal((n,), 0.02, 13, sd, 2, 0)
+    for odt in ("bf16", "f32"):
+        d = _out(m, n, odt)
+        B.te_fp8_gemm(dev_u8(qa), fa, dev_u8(ea), dev_u8(qb), fb, dev_u8(eb), d, bias=dev_f32(bias),
+                      gran=B.TE_GRAN_MX_BLOCK32)
+        ref = O.gemm_mx(qa, ea, FMTS[fa], qb, eb, FMTS[fb], bias=bias, out=odt)
+        err = O.rel_err(host(d), ref)
+        assert err <= TOL[odt], (odt, err)
+
+
+def test_mx_gemm_unit_scales_equal_per_tensor_exactly():
+    rng = np.random.default_rng(9)
+    m, n, k = 128, 256, 512
+    ints = np.arange(-16, 17)
+    codes = O.encode(ints.astype(np.float32), O.E4M3)
+    a = codes[rng.integers(0, len(ints), (m, k))]
+    b = codes[rng.integers(0, len(ints), (n, k))]
+    ea = np.full((m, k // 32), 127, np.uint8)
+    eb = np.full((n, k // 32), 127, np.uint8)
+    d1, d2 = _out(m, n, "f32"), _out(m, n, "f32")
+    B.te_fp8_gemm(dev_u8(a), "E4M3", dev_u8(ea), dev_u8(b), "E4M3", dev_u8(eb), d1, gran=B.TE_GRAN_MX_BLOCK32)
+    B.te_fp8_gemm(dev_u8(a), "E4M3", scalar(1.0), dev_u8(b), "E4M3", scalar(1.0), d2)
+    assert torch.equal(d1, d2)
+    # power-of-two block scales are exact as well: scale every block of row 0 by 2^3
+    ea2 = ea.copy()
+    ea2[0, :] = 130
+    d3 = _out(m, n, "f32")
+    B.te_fp8_gemm(dev_u8(a), "E4M3", dev_u8(ea2), dev_u8(b), "E4M3", dev_u8(eb), d3, gran=B.TE_GRAN_MX_BLOCK32)
+    np.testing.assert_array_equal(host(d3), O.gemm_mx(a, ea2, O.E4M3, b, eb, O.E4M3, out="f32"))
+
+
+def test_gemm_empty_and_bad_shape_raise():
+    d = torch.empty((0, 16), dtype=torch.bfloat16, device=DEV)
+    a = torch.empty((0, 32), dtype=torch.uint8, device=DEV)
+    b = torch.zeros((16, 32), dtype=torch.uint8, device=DEV)
+    B.te_fp8_gemm(a, "E4M3", scalar(1.0), b, "E4M3", scalar(1.0), d)  # m == 0: no launch, OK
+    with pytest.raises(B.TEError):
+        bad = torch.zeros((16, 24), dtype=torch.uint8, device=DEV)
+        B.te_fp8_gemm(bad, "E4M3", scalar(1.0), bad, "E4M3", scalar(1.0),
+                      torch.empty((16, 16), dtype=torch.float32, device=DEV))
+
+
+@pytest.mark.parametrize("stage", ["fprop", "dgrad", "wgrad"])
+@pytest.mark.parametrize("weight", ["qkv", "mlp_down"])
+def test_fp8_gemm_full_5b_shape_sampled(stage, weight):
+    """The 5B-layer shapes at full size, in the launch configuration the benchmark
+    times; the oracle checks 96 sampled rows x 384 sampled columns."""
+    g = {(x.weight, x.stage): x for x in layer_gemms(CODONFM_5B)}[(weight, stage)]
+    fa = "E4M3" if stage == "fprop" else "E5M2"
+    rng = np.random.default_rng(_seed(weight, stage))
+    # random finite codes of mid-range magnitude with random signs (drawn as bytes, so the
+    # full-size operands cost no host-side float work)
+    def codes(shape, fmt):
+        mag = rng.integers(0x18, 0x48, shape, dtype=np.uint8)
+        return mag | (rng.integers(0, 2, shape, dtype=np.uint8) << 7)
+    a = codes((g.m, g.k), fa)
+    b = codes((g.n, g.k), "E4M3")
+    d = _out(g.m, g.n, "bf16")
+    B.te_fp8_gemm(dev_u8(a), fa, scalar(1 / 64), dev_u8(b), "E4M3", scalar(1 / 64), d)
+    rows = np.sort(rng.choice(g.m, 96, replace=False))
+    cols = np.sort(rng.choice(g.n, 384, replace=False))
+    rows[-1] = g.m - 1
+    cols[-1] = g.n - 1
+    ref = O.gemm_per_tensor(a[rows], FMTS[fa], np.float32(1 / 64), b[cols], O.E4M3, np.float32(1 / 64), out="bf16")
+    got = host(d)[np.ix_(rows, cols)]
+    assert O.rel_err(got, ref) <= TOL["bf16"]

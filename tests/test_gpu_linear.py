@@ -1,0 +1,127 @@
+"""End-to-end runs of the Linear layer through the C ABI against the oracle.
+
+The 768 -> 768 layer of [FP8-intro] "Transformer Engine の使い方" for 20 steps
+of delayed scaling (history 16, max, margin 0, HYBRID): every step's FP8 bytes,
+amax history, scale and scale_inv bit-exact; the bf16 output within 1e-2.
+Also: backward (Dgrad/Wgrad) with current scaling, the MXFP8 recipe, and
+resume of the scaling state from a checkpoint.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from fp8_precision_transformer_amd import synth
+from fp8_precision_transformer_amd.linear import Linear, fp8_autocast
+from fp8_precision_transformer_amd.recipe import (DelayedScaling, Float8CurrentScaling, Format,
+                                                  MXFP8BlockScaling)
+
+from gpu_util import DEV, dev_f32, host
+
+pytestmark = pytest.mark.gpu
+
+CFG = 1
+
+
+def _layer(seed=0):
+    lin = Linear(768, 768, bias=True)
+    w = synth.normal((768, 768), 0.02, CFG, 0, synth.T_W, seed)
+    b = synth.normal((768,), 0.02, CFG, 0, synth.T_BIAS, seed)
+    with torch.no_grad():
+        lin.weight.copy_(dev_f32(w))
+        lin.bias.copy_(dev_f32(b))
+    return lin, w, b
+
+
+def test_linear_768_delayed_20_steps_bit_exact_state():
+    recipe = DelayedScaling(fp8_format=Format.HYBRID, amax_history_len=16, amax_compute_algo="max")
+    lin, w, b = _layer()
+    lin.keep_fp8_tensors = True
+    sx = O.DelayedScalingState(O.E4M3, 16, "max", 0)
+    sw = O.DelayedScalingState(O.E4M3, 16, "max", 0)
+    for t in range(20):
+        x = synth.uniform01((1024, 768), CFG, 0, synth.T_X, t)
+        with torch.no_grad(), fp8_autocast(enabled=True, fp8_recipe=recipe):
+            y = lin(dev_f32(x))
+        xq, sxi = sx.cast(x)
+        wq, swi = sw.cast(w)
+        ref = O.gemm_per_tensor(xq, O.E4M3, sxi, wq, O.E4M3, swi, bias=b, out="bf16")
+        sx.update()
+        sw.update()
+        np.testing.assert_array_equal(host(lin.last_fp8["xq"]), xq, err_msg=f"step {t} xq")
+        np.testing.assert_array_equal(host(lin.last_fp8["wq"]), wq, err_msg=f"step {t} wq")
+        st = lin.fp8_state_dict()
+        np.testing.assert_array_equal(host(st["amax_history"])[0], sx.hist, err_msg=f"step {t}")
+        np.testing.assert_array_equal(host(st["amax_history"])[1], sw.hist, err_msg=f"step {t}")
+        assert host(st["scale"])[0] == sx.scale and host(st["scale"])[1] == sw.scale, t
+        assert host(st["scale_inv"])[0] == sx.scale_inv and host(st["scale_inv"])[1] == sw.scale_inv, t
+        assert O.rel_err(host(y), ref) <= 1e-2, t
+
+
+def test_linear_state_resume_is_bit_identical():
+    recipe = DelayedScaling()
+    xs = [synth.uniform01((256, 768), CFG, 1, synth.T_X, t) for t in range(20)]
+    lin, _, _ = _layer(1)
+    outs = []
+    for t in range(20):
+        with torch.no_grad(), fp8_autocast(fp8_recipe=recipe):
+            outs.append(lin(dev_f32(xs[t])).clone())
+        if t == 9:
+            saved = lin.fp8_state_dict()
+    lin2, _, _ = _layer(1)
+    lin2.load_fp8_state_dict(saved)
+    for t in range(10, 20):
+        with torch.no_grad(), fp8_autocast(fp8_recipe=recipe):
+            y = lin2(dev_f32(xs[t]))
+        assert torch.equal(y, outs[t]), t
+
+
+def test_linear_backward_current_scaling():
+    recipe = Float8CurrentScaling(fp8_format=Format.HYBRID)
+    lin, w, b = _layer(2)
+    lin.keep_fp8_tensors = True
+    x = synth.activations((512, 768), 2, 0, synth.T_X, 0)
+    dy = synth.grads((512, 768), 2, 0, synth.T_DY, 0)
+    xd = dev_f32(x).requires_grad_(True)
+    with fp8_autocast(fp8_recipe=recipe):
+        y = lin(xd)
+    y.backward(dev_f32(dy).to(torch.bfloat16))
+    dy_b = host(dev_f32(dy).to(torch.bfloat16))
+    sx = O.current_scale(O.amax(x), O.E4M3)
+    swt = O.current_scale(O.amax(w), O.E4M3)
+    sdy = O.current_scale(O.amax(dy_b), O.E5M2)
+    xq, wq = O.scaled_cast(x, sx, O.E4M3), O.scaled_cast(w, swt, O.E4M3)
+    dyq = O.scaled_cast(dy_b, sdy, O.E5M2)
+    np.testing.assert_array_equal(host(lin.last_fp8["xq"]), xq)
+    ref_y = O.gemm_per_tensor(xq, O.E4M3, O.scale_inverse(sx), wq, O.E4M3, O.scale_inverse(swt), bias=b)
+    assert O.rel_err(host(y), ref_y) <= 1e-2
+    ref_dx = O.gemm_per_tensor(dyq, O.E5M2, O.scale_inverse(sdy), np.ascontiguousarray(wq.T), O.E4M3,
+                               O.scale_inverse(swt), out="bf16")
+    assert O.rel_err(host(xd.grad), ref_dx) <= 1e-2
+    ref_dw = O.gemm_per_tensor(np.ascontiguousarray(dyq.T), O.E5M2, O.scale_inverse(sdy),
+                               np.ascontiguousarray(xq.T), O.E4M3, O.scale_inverse(sx), out="f32")
+    assert O.rel_err(host(lin.weight.grad), ref_dw) <= 1e-3
+    np.testing.assert_allclose(host(lin.bias.grad), dy_b.astype(np.float64).sum(0), rtol=1e-4, atol=1e-6)
+
+
+def test_linear_mxfp8_forward():
+    lin, w, b = _layer(3)
+    x = synth.activations((256, 768), 3, 0, synth.T_X, 0)
+    with torch.no_grad(), fp8_autocast(fp8_recipe=MXFP8BlockScaling()):
+        y = lin(dev_f32(x))
+    qa, ea = O.mxfp8_quantize(x)
+    qb, eb = O.mxfp8_quantize(w)
+    ref = O.gemm_mx(qa, ea, O.E4M3, qb, eb, O.E4M3, bias=b)
+    assert O.rel_err(host(y), ref) <= 1e-2
+
+
+def test_linear_outside_autocast_uses_bf16_gemm():
+    lin, w, b = _layer(4)
+    x = synth.activations((64, 768), 4, 0, synth.T_X, 0)
+    with torch.no_grad():
+        y = lin(dev_f32(x))
+    xb = synth.to_bf16_bits(x)
+    wb = synth.to_bf16_bits(w)
+    ref = O.gemm_bf16(xb, wb, bias=b)
+    assert O.rel_err(host(y), ref) <= 1e-2
