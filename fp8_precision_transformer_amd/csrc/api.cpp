@@ -173,7 +173,7 @@ te_status te_fp8_gemm(const void* a, int a_dtype, const void* a_scale, const voi
   if (bias && bias_dtype != TE_BF16 && bias_dtype != TE_F32) return fail(TE_ERR_DTYPE, "bias_dtype must be TE_BF16 or TE_F32");
   if (m >= (int64_t(1) << 31) || n >= (int64_t(1) << 31)) return fail(TE_ERR_SHAPE, "m and n must be < 2^31");
   const int64_t kb = k * (bf16 ? 2 : 1);
-  if (kb * 256 >= (int64_t(1) << 32)) return fail(TE_ERR_SHAPE, "k too large (256 rows of k must fit 4 GiB)");
+  if (kb * 256 >= (int64_t(1) << 31)) return fail(TE_ERR_SHAPE, "k too large (256 rows of k must fit 2 GiB)");
   if (m == 0 || n == 0) {
     g_err[0] = '\0';
     return TE_OK;

@@ -182,19 +182,23 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(Params p) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
       }
     } else {
-      auto sub = [&](auto S) {  // 64-element k sub-step; lane holds 32 contiguous k
+      // 64-element k sub-step.  Operand layout of v_mfma_*_32x32x64_f8f6f4: lane l
+      // (row l % 32, half h = l / 32) holds k = 16h + [0, 16) in VGPRs 0-3 and
+      // k = 32 + 16h + [0, 16) in VGPRs 4-7; the 32-element scale block b is
+      // k = [32b, 32b + 32) and takes its E8M0 scale from lane (row, b).
+      auto sub = [&](auto S) {
         constexpr int s = decltype(S)::value;
-        const int c0 = s * 4 + lk * 2;
+        const int c_lo = s * 4 + lk, c_hi = s * 4 + 2 + lk;
         v8i af[4], bf[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = wm + i * 32 + lr;
-          const v4u lo = *reinterpret_cast<const v4u*>(sA + row * BKB + ((c0 ^ swk) << 4));
-          const v4u hi = *reinterpret_cast<const v4u*>(sA + row * BKB + (((c0 + 1) ^ swk) << 4));
+          const v4u lo = *reinterpret_cast<const v4u*>(sA + row * BKB + ((c_lo ^ swk) << 4));
+          const v4u hi = *reinterpret_cast<const v4u*>(sA + row * BKB + ((c_hi ^ swk) << 4));
           af[i] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           const int col = wn + i * 32 + lr;
-          const v4u lo2 = *reinterpret_cast<const v4u*>(sB + col * BKB + ((c0 ^ swk) << 4));
-          const v4u hi2 = *reinterpret_cast<const v4u*>(sB + col * BKB + (((c0 + 1) ^ swk) << 4));
+          const v4u lo2 = *reinterpret_cast<const v4u*>(sB + col * BKB + ((c_lo ^ swk) << 4));
+          const v4u hi2 = *reinterpret_cast<const v4u*>(sB + col * BKB + ((c_hi ^ swk) << 4));
           bf[i] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo2, hi2, 0, 1, 2, 3, 4, 5, 6, 7));
         }
 #pragma unroll
@@ -202,7 +206,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(Params p) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             if constexpr (KIND == KIND_MX) {
-              // byte (2s + lk) of the stage's scale dword is this lane's 32-block
+              // lane (row, b) supplies block b of this sub-step: byte 2s + b of the stage dword
               acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                   af[i], bf[j], acc[i][j], AF, BF, 2 * s, static_cast<int>(sa_cur[i] >> (8 * lk)),
                   2 * s, static_cast<int>(sb_cur[j] >> (8 * lk)));
@@ -276,13 +280,403 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(Params p) {
   }
 }
 
+// ============================================================================
+// v2 pipeline: direct-to-LDS loads into a 4-deep ring of 64-byte k stages,
+// fragments double-buffered in registers one stage ahead.
+//
+// LDS: A slots [0, 64K) and B slots [64K, 128K), 16 KB each = 256 rows x 64 B;
+// MX adds a 2 KB scale slot per stage at 128K.  buffer_load_dwordx4 ... lds
+// writes lane j's 16 bytes to M0 + 16 j, so the swizzle is applied on the
+// global side: the lane that lands at (row, physical chunk pc) fetches logical
+// chunk pc ^ g(row), g(row) = ((row >> 1) ^ (row >> 2)) & 3, so the 8- or
+// 16-lane groups of a fragment read (one logical chunk, consecutive rows) hit
+// distinct banks.  Out-of-range buffer offsets read as zero, which zero-fills
+// rows past m or n and chunks past k.  Loads run three stages ahead; one
+// barrier per stage publishes stage t+1 and retires stage t-1's slot.  The
+// k loop is unrolled by four so ring slot and register set are compile-time
+// constants: every fragment read is one lane base register plus an immediate.
+// ============================================================================
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ void raw_buffer_load_lds(v4i rsrc, __attribute__((address_space(3))) uint32_t* lds,
+                                    int size, int voffset, int soffset, int offset,
+                                    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+__device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  v4i r;
+  r[0] = static_cast<int>(a & 0xffffffffu);
+  r[1] = static_cast<int>(a >> 32);  // stride 0: raw byte-addressed buffer
+  r[2] = static_cast<int>(bytes);    // num_records: offsets at or past it read as 0
+  r[3] = 0x00020000;
+  return r;
+}
+
+constexpr int SK = 64;                  // k bytes per stage
+constexpr int NBUF = 4;                 // stages in the LDS ring
+constexpr int kOpStage = BM * SK;       // 16 KB: one operand, one stage
+constexpr int kBOff = NBUF * kOpStage;  // B slots start at 64 KB
+constexpr int kScOff = 2 * kBOff;       // MX scale slots start at 128 KB
+constexpr int kScaleSlot = 2048;        // per stage: one E8M0 dword per row of A (1 KB) and B (1 KB)
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ int g4(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+
+// s_waitcnt immediate, gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4], lgkmcnt [11:8] = 0
+constexpr int wait_vm_lgkm0(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4); }
+
+template <int KIND, int AF, int BF>
+__global__ __launch_bounds__(NT, 1) void k_gemm2(Params p) {
+  constexpr bool MX = KIND == KIND_MX;
+  constexpr int kLds = kScOff + (MX ? NBUF * kScaleSlot : 0);
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
+
+  const int nb = p.nbm * p.nbn;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, idx = bid >> 3;
+  const int per = nb >> 3, rem = nb & 7;
+  const int lin = xcd * per + (xcd < rem ? xcd : rem) + idx;
+  const int gspan = kGroupM * p.nbn;
+  const int group = lin / gspan;
+  const int first_m = group * kGroupM;
+  const int gsz = (p.nbm - first_m) < kGroupM ? (p.nbm - first_m) : kGroupM;
+  const int in_g = lin - group * gspan;
+  const int tm = first_m + in_g % gsz;
+  const int tn = in_g / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases stay scalar
+  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const int lr = lane & 31, lk = lane >> 5;
+
+  const int rows_a = (p.M - m0) < BM ? (p.M - m0) : BM;
+  const int rows_b = (p.N - n0) < BN ? (p.N - n0) : BN;
+  const v4i rsA = make_rsrc(p.a + static_cast<int64_t>(m0) * p.KB, static_cast<uint32_t>(rows_a) * p.KB);
+  const v4i rsB = make_rsrc(p.b + static_cast<int64_t>(n0) * p.KB, static_cast<uint32_t>(rows_b) * p.KB);
+  v4i rsSA{}, rsSB{};
+  if constexpr (MX) {
+    rsSA = make_rsrc(static_cast<const uint8_t*>(p.a_scale) + static_cast<int64_t>(m0) * p.kblocks,
+                     static_cast<uint32_t>(rows_a) * p.kblocks);
+    rsSB = make_rsrc(static_cast<const uint8_t*>(p.b_scale) + static_cast<int64_t>(n0) * p.kblocks,
+                     static_cast<uint32_t>(rows_b) * p.kblocks);
+  }
+
+  // load mapping: wave w moves rows [64w, 64w + 64) of A and of B, 16 rows per instruction
+  uint32_t ld_off[4];
+  int ld_cb[4];  // logical chunk byte offset within the stage row
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = wave * 64 + q * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ g4(row);
+    ld_cb[q] = c * 16;
+    ld_off[q] = static_cast<uint32_t>(row) * static_cast<uint32_t>(p.KB) + c * 16;
+  }
+  // MX: lane l of wave w fetches the scale dword of row 64 w + l that covers this
+  // stage and its neighbour (E8M0 codes 4 (kt / 2) .. + 3; needs k % 128 == 0)
+  const uint32_t sc_off = static_cast<uint32_t>(wave * 64 + lane) * static_cast<uint32_t>(p.kblocks);
+
+  auto issue = [&](auto SLOT, int kt) {
+    constexpr int slot = decltype(SLOT)::value;
+    const uint32_t kb = static_cast<uint32_t>(kt) * SK;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t off = (kb + ld_cb[q] < static_cast<uint32_t>(p.KB)) ? ld_off[q] + kb : kOOB;
+      const int base = slot * kOpStage + (wave * 64 + q * 16) * SK;
+      raw_buffer_load_lds(rsA, (__attribute__((address_space(3))) uint32_t*)(smem + base), 16,
+                          static_cast<int>(off), 0, 0, 0);
+      raw_buffer_load_lds(rsB, (__attribute__((address_space(3))) uint32_t*)(smem + kBOff + base), 16,
+                          static_cast<int>(off), 0, 0, 0);
+    }
+    if constexpr (MX) {
+      const int base = kScOff + slot * kScaleSlot + wave * 256;
+      const int off = static_cast<int>(sc_off + 4 * (kt >> 1));
+      raw_buffer_load_lds(rsSA, (__attribute__((address_space(3))) uint32_t*)(smem + base), 4, off, 0, 0, 0);
+      raw_buffer_load_lds(rsSB, (__attribute__((address_space(3))) uint32_t*)(smem + base + 1024), 4, off, 0,
+                          0, 0);
+    }
+  };
+
+  // fragment read addresses: row = wm + 32 i + lr has g4(row) = g4(lr); the chunk
+  // pair of a lane is (lk, 2 + lk)
+  const int ra_lo = (wm + lr) * SK + ((lk ^ g4(lr)) << 4);
+  const int ra_hi = (wm + lr) * SK + (((2 + lk) ^ g4(lr)) << 4);
+  const int rb_lo = kBOff + (wn + lr) * SK + ((lk ^ g4(lr)) << 4);
+  const int rb_hi = kBOff + (wn + lr) * SK + (((2 + lk) ^ g4(lr)) << 4);
+
+  v8i fa[2][4], fb[2][4];
+  uint32_t xa[2][4], xb[2][4];  // MX: this lane's scale bytes (block lk of a stage pair)
+  auto read_frags = [&](auto SLOT, auto SET) {
+    constexpr int slot = decltype(SLOT)::value;
+    constexpr int set = decltype(SET)::value;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int o = slot * kOpStage + i * 32 * SK;
+      const v4u lo = *reinterpret_cast<const v4u*>(smem + ra_lo + o);
+      const v4u hi = *reinterpret_cast<const v4u*>(smem + ra_hi + o);
+      fa[set][i] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      const v4u lo2 = *reinterpret_cast<const v4u*>(smem + rb_lo + o);
+      const v4u hi2 = *reinterpret_cast<const v4u*>(smem + rb_hi + o);
+      fb[set][i] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo2, hi2, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    if constexpr (MX) {
+      const uint32_t* ss = reinterpret_cast<const uint32_t*>(smem + kScOff + slot * kScaleSlot);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xa[set][i] = ss[wm + i * 32 + lr] >> (8 * lk);
+        xb[set][i] = ss[256 + wn + i * 32 + lr] >> (8 * lk);
+      }
+    }
+  };
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{0};
+
+  auto mfma = [&](auto SET) {
+    constexpr int set = decltype(SET)::value;
+    if constexpr (KIND == KIND_BF16) {
+      // a 64-byte stage is 32 bf16: the low half of the fragment is k [8 lk, 8 lk + 8), the
+      // high half k [16 + 8 lk, 16 + 8 lk + 8): two 32x32x16 steps
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const v8i a = fa[set][i], b = fb[set][j];
+            const v8bf av = __builtin_bit_cast(v8bf, h ? __builtin_shufflevector(a, a, 4, 5, 6, 7)
+                                                       : __builtin_shufflevector(a, a, 0, 1, 2, 3));
+            const v8bf bv = __builtin_bit_cast(v8bf, h ? __builtin_shufflevector(b, b, 4, 5, 6, 7)
+                                                       : __builtin_shufflevector(b, b, 0, 1, 2, 3));
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i][j], 0, 0, 0);
+          }
+    } else if constexpr (MX) {
+      // stage kt (kt & 1 == set) takes byte 2 set of the lane's shifted pair dword: the
+      // lane half lk supplies block lk (see the operand layout note of the v1 kernel)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fa[set][i], fb[set][j], acc[i][j], AF, BF, 2 * set, static_cast<int>(xa[set][i]), 2 * set,
+              static_cast<int>(xb[set][j]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[set][i], fb[set][j], acc[i][j],
+                                                                     AF, BF, 0, 0, 0, 0);
+    }
+  };
+  // Part 0 of a stage's MFMAs (the ones issued before the barrier) is fragment row 0;
+  // part 1 is rows 1-3.  BF16 runs two 32x32x16 half-steps per row.
+  auto mfma_part = [&](auto SET, auto PART) {
+    constexpr int set = decltype(SET)::value;
+    constexpr int i0 = decltype(PART)::value == 0 ? 0 : 1;
+    constexpr int i1 = decltype(PART)::value == 0 ? 1 : 4;
+#pragma unroll
+    for (int i = i0; i < i1; ++i) {
+      if constexpr (KIND == KIND_BF16) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const v8i a = fa[set][i], b = fb[set][j];
+            const v8bf av = __builtin_bit_cast(v8bf, h ? __builtin_shufflevector(a, a, 4, 5, 6, 7)
+                                                       : __builtin_shufflevector(a, a, 0, 1, 2, 3));
+            const v8bf bv = __builtin_bit_cast(v8bf, h ? __builtin_shufflevector(b, b, 4, 5, 6, 7)
+                                                       : __builtin_shufflevector(b, b, 0, 1, 2, 3));
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i][j], 0, 0, 0);
+          }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[set][i], fb[set][j], acc[i][j],
+                                                                     AF, BF, 0, 0, 0, 0);
+      }
+    }
+  };
+
+  const int KT = p.KT;
+  constexpr int LPS = 8;  // loads per thread per stage
+
+  // One pipeline step on stage kt (ring slot S = kt % 4, register set S % 2).  The
+  // fragments of stage kt are already in registers, so once every wave has passed
+  // this step's barrier, stage kt's slot is free and receives stage kt+4 (four stages
+  // of prefetch in a four-slot ring).  Before the barrier: row 0's MFMAs; after it:
+  // the loads of stage kt+4 and the reads of stage kt+1 ride on rows 1-3.  With one
+  // wave per SIMD, everything that is not an MFMA has to issue in an MFMA's shadow.
+  auto step = [&](auto SLOT, int kt, auto STEADY) {
+    constexpr int S = decltype(SLOT)::value;
+    constexpr bool steady = decltype(STEADY)::value;
+    mfma_part(ic<S & 1>{}, ic<0>{});
+    if (steady || kt + 1 < KT) {
+      // stage kt+1 has landed once at most the stages issued after it are in flight;
+      // lgkmcnt(0): this wave's reads of stage kt are done before anyone refills its slot
+      const int after = steady ? 2 : ((KT - 1 < kt + 3 ? KT - 1 : kt + 3) - (kt + 1));
+      if (after >= 2) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * LPS));
+      else if (after == 1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(LPS));
+      else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+      __builtin_amdgcn_s_barrier();
+    }
+    if (steady || kt + 4 < KT) issue(ic<S>{}, kt + 4);
+    if (steady || kt + 1 < KT) read_frags(ic<(S + 1) & 3>{}, ic<(S + 1) & 1>{});
+    mfma_part(ic<S & 1>{}, ic<1>{});
+    if constexpr (steady) {
+      if constexpr (KIND == KIND_BF16) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (to LDS)
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (to LDS)
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // prologue: four stages in flight, stage 0 published and read
+  issue(ic<0>{}, 0);
+  if (KT > 1) issue(ic<1>{}, 1);
+  if (KT > 2) issue(ic<2>{}, 2);
+  if (KT > 3) issue(ic<3>{}, 3);
+  if (KT > 3) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(3 * LPS));
+  else if (KT > 2) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * LPS));
+  else if (KT > 1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(LPS));
+  else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+  __builtin_amdgcn_s_barrier();
+  read_frags(ic<0>{}, ic<0>{});
+
+  // steady state without branches (kt + 4 < KT for all four steps), then the tail
+  int kt = 0;
+  for (; kt + 7 < KT; kt += 4) {
+    step(ic<0>{}, kt, std::true_type{});
+    step(ic<1>{}, kt + 1, std::true_type{});
+    step(ic<2>{}, kt + 2, std::true_type{});
+    step(ic<3>{}, kt + 3, std::true_type{});
+  }
+  for (; kt + 3 < KT; kt += 4) {
+    step(ic<0>{}, kt, std::false_type{});
+    step(ic<1>{}, kt + 1, std::false_type{});
+    step(ic<2>{}, kt + 2, std::false_type{});
+    step(ic<3>{}, kt + 3, std::false_type{});
+  }
+  if (kt < KT) step(ic<0>{}, kt, std::false_type{});
+  if (kt + 1 < KT) step(ic<1>{}, kt + 1, std::false_type{});
+  if (kt + 2 < KT) step(ic<2>{}, kt + 2, std::false_type{});
+
+  // ---- epilogue: scale, bias, round; staged through LDS for full-row 16-byte stores ----
+  // Each wave owns a 128 x 128 block; it is written out in two passes of 64 rows.
+  // Pass: the wave's fp32 values go to its own LDS region (64 rows x 128 floats; a
+  // half-wave writes 32 consecutive floats of one row), then each lane reads 8 (bf16
+  // out) or 4 (fp32 out) consecutive floats of a row and stores 16 bytes.
+  float sa = 1.0f, sb = 1.0f;
+  if constexpr (KIND == KIND_FP8) {
+    sa = *static_cast<const float*>(p.a_scale);
+    sb = *static_cast<const float*>(p.b_scale);
+  }
+  float bias_v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int col = n0 + wn + j * 32 + lr;
+    bias_v[j] = 0.0f;
+    if (p.bias != nullptr && col < p.N)
+      bias_v[j] = p.bias_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p.bias)[col]) << 16)
+                              : static_cast<const float*>(p.bias)[col];
+  }
+  constexpr int kEpPitch = 512;                  // bytes per staged row
+  constexpr int kEpRegion = 64 * kEpPitch;       // 33 KB per wave
+  static_assert(4 * kEpRegion <= kScOff, "epilogue staging must fit in the operand ring");
+  float* ep = reinterpret_cast<float*>(smem + wave * kEpRegion);
+  __syncthreads();  // every wave is done with the operand ring
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = pass * 2 + ii;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float val = acc[i][j][v];
+          if constexpr (KIND == KIND_FP8) val = __fmul_rn(__fmul_rn(val, sa), sb);
+          if (p.bias != nullptr) val = __fadd_rn(val, bias_v[j]);
+          const int r = ii * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
+          ep[r * (kEpPitch / 4) + j * 32 + lr] = val;
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
+    __builtin_amdgcn_wave_barrier();
+    const int row0 = m0 + wm + pass * 64;
+    const int col0 = n0 + wn;
+    if (p.d_bf16) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int r = t * 4 + (lane >> 4);
+        const int c = (lane & 15) * 8;
+        const float4 lo = *reinterpret_cast<const float4*>(ep + r * (kEpPitch / 4) + c);
+        const float4 hi = *reinterpret_cast<const float4*>(ep + r * (kEpPitch / 4) + c + 4);
+        const int grow = row0 + r, gcol = col0 + c;
+        if (grow < p.M && gcol < p.N) {
+          uint4 o;
+          o.x = f32_to_bf16_bits(lo.x) | (f32_to_bf16_bits(lo.y) << 16);
+          o.y = f32_to_bf16_bits(lo.z) | (f32_to_bf16_bits(lo.w) << 16);
+          o.z = f32_to_bf16_bits(hi.x) | (f32_to_bf16_bits(hi.y) << 16);
+          o.w = f32_to_bf16_bits(hi.z) | (f32_to_bf16_bits(hi.w) << 16);
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol) = o;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 32; ++t) {
+        const int r = t * 2 + (lane >> 5);
+        const int c = (lane & 31) * 4;
+        const float4 v4 = *reinterpret_cast<const float4*>(ep + r * (kEpPitch / 4) + c);
+        const int grow = row0 + r, gcol = col0 + c;
+        if (grow < p.M && gcol < p.N)
+          *reinterpret_cast<float4*>(static_cast<float*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol) = v4;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 thread_local const char* g_last_variant = "none";
 
 template <int KIND, int AF, int BF>
-hipError_t run(const Params& p, hipStream_t s, const char* name) {
+hipError_t run(Params p, hipStream_t s, const char* name) {
   g_last_variant = name;
   const int nb = p.nbm * p.nbn;
-  hipLaunchKernelGGL((k_gemm<KIND, AF, BF>), dim3(nb), dim3(NT), 0, s, p);
+  if constexpr (KIND == KIND_MX) {
+    // the scaled MFMA makes the v2 register schedule copy accumulators between AGPRs
+    // and VGPRs; the MX path keeps the v1 kernel until that is resolved
+    hipLaunchKernelGGL((k_gemm<KIND_MX, AF, BF>), dim3(nb), dim3(NT), 0, s, p);
+  } else {
+    p.KT = (p.KB + SK - 1) / SK;
+    hipLaunchKernelGGL((k_gemm2<KIND, AF, BF>), dim3(nb), dim3(NT), 0, s, p);
+  }
   return hipGetLastError();
 }
 
@@ -311,17 +705,17 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   p.d_bf16 = g.d_bf16;
   // f8f6f4 format codes: 0 = E4M3, 1 = E5M2
   const int af = (g.a_fmt == E5M2) ? 1 : 0, bf = (g.b_fmt == E5M2) ? 1 : 0;
-  if (g.a_fmt == BF16) return run<KIND_BF16, 0, 0>(p, s, "gemm_bf16_256x256x64");
+  if (g.a_fmt == BF16) return run<KIND_BF16, 0, 0>(p, s, "gemm2_bf16_256x256x32_ring4");
   if (g.mx) {
     if (af == 0 && bf == 0) return run<KIND_MX, 0, 0>(p, s, "gemm_mx_e4m3_e4m3_256x256x128");
     if (af == 1 && bf == 0) return run<KIND_MX, 1, 0>(p, s, "gemm_mx_e5m2_e4m3_256x256x128");
     if (af == 0 && bf == 1) return run<KIND_MX, 0, 1>(p, s, "gemm_mx_e4m3_e5m2_256x256x128");
     return run<KIND_MX, 1, 1>(p, s, "gemm_mx_e5m2_e5m2_256x256x128");
   }
-  if (af == 0 && bf == 0) return run<KIND_FP8, 0, 0>(p, s, "gemm_fp8_e4m3_e4m3_256x256x128");
-  if (af == 1 && bf == 0) return run<KIND_FP8, 1, 0>(p, s, "gemm_fp8_e5m2_e4m3_256x256x128");
-  if (af == 0 && bf == 1) return run<KIND_FP8, 0, 1>(p, s, "gemm_fp8_e4m3_e5m2_256x256x128");
-  return run<KIND_FP8, 1, 1>(p, s, "gemm_fp8_e5m2_e5m2_256x256x128");
+  if (af == 0 && bf == 0) return run<KIND_FP8, 0, 0>(p, s, "gemm2_fp8_e4m3_e4m3_256x256x64_ring4");
+  if (af == 1 && bf == 0) return run<KIND_FP8, 1, 0>(p, s, "gemm2_fp8_e5m2_e4m3_256x256x64_ring4");
+  if (af == 0 && bf == 1) return run<KIND_FP8, 0, 1>(p, s, "gemm2_fp8_e4m3_e5m2_256x256x64_ring4");
+  return run<KIND_FP8, 1, 1>(p, s, "gemm2_fp8_e5m2_e5m2_256x256x64_ring4");
 }
 
 }  // namespace te
