@@ -19,6 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libte_mi355x.so")
 SOURCES = ["api.cpp", "quant.hip", "gemm.hip"]
+PEAK_LIB = os.path.join(PKG, "libte_peak.so")  # MFMA-only throughput probe (microbench tooling)
+PEAK_SOURCES = ["peak.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",
@@ -61,14 +63,15 @@ def build(verbose: bool = False, extra_flags=None) -> str:
             print(r.stderr, file=sys.stderr)
         return obj
 
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [cc, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    with ThreadPoolExecutor(len(SOURCES) + len(PEAK_SOURCES)) as ex:
+        objs = list(ex.map(compile_one, SOURCES + PEAK_SOURCES))
+    for lib, lib_objs in ((LIB, objs[:len(SOURCES)]), (PEAK_LIB, objs[len(SOURCES):])):
+        tmp = lib + ".tmp"
+        cmd = [cc, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + lib_objs
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -281,20 +281,11 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(Params p) {
 }
 
 // ============================================================================
-// v2 pipeline: direct-to-LDS loads into a 4-deep ring of 64-byte k stages,
-// fragments double-buffered in registers one stage ahead.
-//
-// LDS: A slots [0, 64K) and B slots [64K, 128K), 16 KB each = 256 rows x 64 B;
-// MX adds a 2 KB scale slot per stage at 128K.  buffer_load_dwordx4 ... lds
-// writes lane j's 16 bytes to M0 + 16 j, so the swizzle is applied on the
-// global side: the lane that lands at (row, physical chunk pc) fetches logical
-// chunk pc ^ g(row), g(row) = ((row >> 1) ^ (row >> 2)) & 3, so the 8- or
-// 16-lane groups of a fragment read (one logical chunk, consecutive rows) hit
-// distinct banks.  Out-of-range buffer offsets read as zero, which zero-fills
-// rows past m or n and chunks past k.  Loads run three stages ahead; one
-// barrier per stage publishes stage t+1 and retires stage t-1's slot.  The
-// k loop is unrolled by four so ring slot and register set are compile-time
-// constants: every fragment read is one lane base register plus an immediate.
+// Direct-to-LDS loads: buffer_load_dwordx4 ... lds writes lane j's 16 bytes to
+// M0 + 16 j, so any LDS swizzle is applied on the global side (the lane that
+// lands at a physical chunk fetches the logical chunk mapped there).  Buffer
+// offsets at or past num_records read as zero, which zero-fills rows past m or
+// n and chunks past k.
 // ============================================================================
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -312,24 +303,34 @@ __device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
   return r;
 }
 
-constexpr int SK = 64;                  // k bytes per stage
-constexpr int NBUF = 4;                 // stages in the LDS ring
-constexpr int kOpStage = BM * SK;       // 16 KB: one operand, one stage
-constexpr int kBOff = NBUF * kOpStage;  // B slots start at 64 KB
-constexpr int kScOff = 2 * kBOff;       // MX scale slots start at 128 KB
-constexpr int kScaleSlot = 2048;        // per stage: one E8M0 dword per row of A (1 KB) and B (1 KB)
+constexpr int SK = 64;  // k bytes per MFMA stage
 constexpr uint32_t kOOB = 0x80000000u;
-
-__device__ __forceinline__ int g4(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 
 // s_waitcnt immediate, gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4], lgkmcnt [11:8] = 0
 constexpr int wait_vm_lgkm0(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4); }
 
+// ============================================================================
+// Pair pipeline: stage pairs loaded as full 128-byte lines.
+//
+// The k loop still computes 64-byte stages (16 FP8 MFMAs of 32x32x64 per wave),
+// but global data arrives two stages at a time: a 128-byte slice of each of the
+// tile's 256 A rows and 256 B rows (64 KB), so every load request is a whole
+// cache line.  LDS holds two such pair slots (A at [0, 64K), B at [64K, 128K),
+// 32 KB each), rows of 8 chunks of 16 bytes stored at chunk ^ f(row),
+// f(r) = (r & 7) ^ ((r >> 3) & 3), which keeps the 8- and 16-lane groups of a
+// fragment read (one logical chunk, consecutive rows) on distinct banks.  One
+// barrier per pair publishes pair p+1 and frees pair p's slot; pair p+2 is then
+// loaded into it while pair p+1 is consumed (two steps of latency budget).
+// ============================================================================
+constexpr int PK = 128;                  // k bytes per pair slot row
+constexpr int kPairOp = BM * PK;         // 32 KB: one operand, one pair
+constexpr int kPB = 2 * kPairOp;         // B pair slots start at 64 KB
+
+__device__ __forceinline__ int f8(int row) { return (row & 7) ^ ((row >> 3) & 3); }
+
 template <int KIND, int AF, int BF>
-__global__ __launch_bounds__(NT, 1) void k_gemm2(Params p) {
-  constexpr bool MX = KIND == KIND_MX;
-  constexpr int kLds = kScOff + (MX ? NBUF * kScaleSlot : 0);
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
+__global__ __launch_bounds__(NT, 1) void k_gemm3(Params p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kPB];
 
   const int nb = p.nbm * p.nbn;
   const int bid = blockIdx.x;
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm2(Params p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
   const int lr = lane & 31, lk = lane >> 5;
 
@@ -355,78 +356,57 @@ __global__ __launch_bounds__(NT, 1) void k_gemm2(Params p) {
   const int rows_b = (p.N - n0) < BN ? (p.N - n0) : BN;
   const v4i rsA = make_rsrc(p.a + static_cast<int64_t>(m0) * p.KB, static_cast<uint32_t>(rows_a) * p.KB);
   const v4i rsB = make_rsrc(p.b + static_cast<int64_t>(n0) * p.KB, static_cast<uint32_t>(rows_b) * p.KB);
-  v4i rsSA{}, rsSB{};
-  if constexpr (MX) {
-    rsSA = make_rsrc(static_cast<const uint8_t*>(p.a_scale) + static_cast<int64_t>(m0) * p.kblocks,
-                     static_cast<uint32_t>(rows_a) * p.kblocks);
-    rsSB = make_rsrc(static_cast<const uint8_t*>(p.b_scale) + static_cast<int64_t>(n0) * p.kblocks,
-                     static_cast<uint32_t>(rows_b) * p.kblocks);
-  }
 
-  // load mapping: wave w moves rows [64w, 64w + 64) of A and of B, 16 rows per instruction
-  uint32_t ld_off[4];
-  int ld_cb[4];  // logical chunk byte offset within the stage row
+  // load mapping: wave w moves rows [64w, 64w + 64) of A and of B, 8 rows per instruction
+  // (lane j: row 8q + j/8, physical chunk j % 8, logical chunk (j % 8) ^ f(row))
+  uint32_t ld_off[8];
+  int ld_cb[8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int row = wave * 64 + q * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ g4(row);
+  for (int q = 0; q < 8; ++q) {
+    const int row = wave * 64 + q * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ f8(row);
     ld_cb[q] = c * 16;
     ld_off[q] = static_cast<uint32_t>(row) * static_cast<uint32_t>(p.KB) + c * 16;
   }
-  // MX: lane l of wave w fetches the scale dword of row 64 w + l that covers this
-  // stage and its neighbour (E8M0 codes 4 (kt / 2) .. + 3; needs k % 128 == 0)
-  const uint32_t sc_off = static_cast<uint32_t>(wave * 64 + lane) * static_cast<uint32_t>(p.kblocks);
-
-  auto issue = [&](auto SLOT, int kt) {
+  auto issue_pair = [&](auto SLOT, int pr) {
     constexpr int slot = decltype(SLOT)::value;
-    const uint32_t kb = static_cast<uint32_t>(kt) * SK;
+    const uint32_t kb = static_cast<uint32_t>(pr) * PK;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 8; ++q) {
       const uint32_t off = (kb + ld_cb[q] < static_cast<uint32_t>(p.KB)) ? ld_off[q] + kb : kOOB;
-      const int base = slot * kOpStage + (wave * 64 + q * 16) * SK;
+      const int base = slot * kPairOp + (wave * 64 + q * 8) * PK;
       raw_buffer_load_lds(rsA, (__attribute__((address_space(3))) uint32_t*)(smem + base), 16,
                           static_cast<int>(off), 0, 0, 0);
-      raw_buffer_load_lds(rsB, (__attribute__((address_space(3))) uint32_t*)(smem + kBOff + base), 16,
+      raw_buffer_load_lds(rsB, (__attribute__((address_space(3))) uint32_t*)(smem + kPB + base), 16,
                           static_cast<int>(off), 0, 0, 0);
-    }
-    if constexpr (MX) {
-      const int base = kScOff + slot * kScaleSlot + wave * 256;
-      const int off = static_cast<int>(sc_off + 4 * (kt >> 1));
-      raw_buffer_load_lds(rsSA, (__attribute__((address_space(3))) uint32_t*)(smem + base), 4, off, 0, 0, 0);
-      raw_buffer_load_lds(rsSB, (__attribute__((address_space(3))) uint32_t*)(smem + base + 1024), 4, off, 0,
-                          0, 0);
     }
   };
 
-  // fragment read addresses: row = wm + 32 i + lr has g4(row) = g4(lr); the chunk
-  // pair of a lane is (lk, 2 + lk)
-  const int ra_lo = (wm + lr) * SK + ((lk ^ g4(lr)) << 4);
-  const int ra_hi = (wm + lr) * SK + (((2 + lk) ^ g4(lr)) << 4);
-  const int rb_lo = kBOff + (wn + lr) * SK + ((lk ^ g4(lr)) << 4);
-  const int rb_hi = kBOff + (wn + lr) * SK + (((2 + lk) ^ g4(lr)) << 4);
-
+  // fragment reads: row = wm + 32 i + lr has f(row) = f(lr); stage half h uses logical
+  // chunks 4h + lk (low 16 bytes) and 4h + 2 + lk (high 16 bytes)
+  const int fk = f8(lr);
+  int ra[2][2], rb[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    ra[h][0] = (wm + lr) * PK + (((4 * h + lk) ^ fk) << 4);
+    ra[h][1] = (wm + lr) * PK + (((4 * h + 2 + lk) ^ fk) << 4);
+    rb[h][0] = kPB + (wn + lr) * PK + (((4 * h + lk) ^ fk) << 4);
+    rb[h][1] = kPB + (wn + lr) * PK + (((4 * h + 2 + lk) ^ fk) << 4);
+  }
   v8i fa[2][4], fb[2][4];
-  uint32_t xa[2][4], xb[2][4];  // MX: this lane's scale bytes (block lk of a stage pair)
-  auto read_frags = [&](auto SLOT, auto SET) {
+  auto read_frags = [&](auto SLOT, auto HALF, auto SET) {
     constexpr int slot = decltype(SLOT)::value;
+    constexpr int h = decltype(HALF)::value;
     constexpr int set = decltype(SET)::value;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int o = slot * kOpStage + i * 32 * SK;
-      const v4u lo = *reinterpret_cast<const v4u*>(smem + ra_lo + o);
-      const v4u hi = *reinterpret_cast<const v4u*>(smem + ra_hi + o);
+      const int o = slot * kPairOp + i * 32 * PK;
+      const v4u lo = *reinterpret_cast<const v4u*>(smem + ra[h][0] + o);
+      const v4u hi = *reinterpret_cast<const v4u*>(smem + ra[h][1] + o);
       fa[set][i] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      const v4u lo2 = *reinterpret_cast<const v4u*>(smem + rb_lo + o);
-      const v4u hi2 = *reinterpret_cast<const v4u*>(smem + rb_hi + o);
+      const v4u lo2 = *reinterpret_cast<const v4u*>(smem + rb[h][0] + o);
+      const v4u hi2 = *reinterpret_cast<const v4u*>(smem + rb[h][1] + o);
       fb[set][i] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo2, hi2, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-    if constexpr (MX) {
-      const uint32_t* ss = reinterpret_cast<const uint32_t*>(smem + kScOff + slot * kScaleSlot);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xa[set][i] = ss[wm + i * 32 + lr] >> (8 * lk);
-        xb[set][i] = ss[256 + wn + i * 32 + lr] >> (8 * lk);
-      }
     }
   };
 
@@ -436,45 +416,7 @@ __global__ __launch_bounds__(NT, 1) void k_gemm2(Params p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{0};
 
-  auto mfma = [&](auto SET) {
-    constexpr int set = decltype(SET)::value;
-    if constexpr (KIND == KIND_BF16) {
-      // a 64-byte stage is 32 bf16: the low half of the fragment is k [8 lk, 8 lk + 8), the
-      // high half k [16 + 8 lk, 16 + 8 lk + 8): two 32x32x16 steps
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const v8i a = fa[set][i], b = fb[set][j];
-            const v8bf av = __builtin_bit_cast(v8bf, h ? __builtin_shufflevector(a, a, 4, 5, 6, 7)
-                                                       : __builtin_shufflevector(a, a, 0, 1, 2, 3));
-            const v8bf bv = __builtin_bit_cast(v8bf, h ? __builtin_shufflevector(b, b, 4, 5, 6, 7)
-                                                       : __builtin_shufflevector(b, b, 0, 1, 2, 3));
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i][j], 0, 0, 0);
-          }
-    } else if constexpr (MX) {
-      // stage kt (kt & 1 == set) takes byte 2 set of the lane's shifted pair dword: the
-      // lane half lk supplies block lk (see the operand layout note of the v1 kernel)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fa[set][i], fb[set][j], acc[i][j], AF, BF, 2 * set, static_cast<int>(xa[set][i]), 2 * set,
-              static_cast<int>(xb[set][j]));
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[set][i], fb[set][j], acc[i][j],
-                                                                     AF, BF, 0, 0, 0, 0);
-    }
-  };
-  // Part 0 of a stage's MFMAs (the ones issued before the barrier) is fragment row 0;
-  // part 1 is rows 1-3.  BF16 runs two 32x32x16 half-steps per row.
+  // part 0 = fragment row 0, part 1 = rows 1-3 (BF16: two 32x32x16 half-steps per row)
   auto mfma_part = [&](auto SET, auto PART) {
     constexpr int set = decltype(SET)::value;
     constexpr int i0 = decltype(PART)::value == 0 ? 0 : 1;
@@ -483,14 +425,14 @@ __global__ __launch_bounds__(NT, 1) void k_gemm2(Params p) {
     for (int i = i0; i < i1; ++i) {
       if constexpr (KIND == KIND_BF16) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const v8i a = fa[set][i], b = fb[set][j];
-            const v8bf av = __builtin_bit_cast(v8bf, h ? __builtin_shufflevector(a, a, 4, 5, 6, 7)
-                                                       : __builtin_shufflevector(a, a, 0, 1, 2, 3));
-            const v8bf bv = __builtin_bit_cast(v8bf, h ? __builtin_shufflevector(b, b, 4, 5, 6, 7)
-                                                       : __builtin_shufflevector(b, b, 0, 1, 2, 3));
+            const v8bf av = __builtin_bit_cast(v8bf, hh ? __builtin_shufflevector(a, a, 4, 5, 6, 7)
+                                                        : __builtin_shufflevector(a, a, 0, 1, 2, 3));
+            const v8bf bv = __builtin_bit_cast(v8bf, hh ? __builtin_shufflevector(b, b, 4, 5, 6, 7)
+                                                        : __builtin_shufflevector(b, b, 0, 1, 2, 3));
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i][j], 0, 0, 0);
           }
       } else {
@@ -502,74 +444,91 @@ __global__ __launch_bounds__(NT, 1) void k_gemm2(Params p) {
     }
   };
 
-  const int KT = p.KT;
-  constexpr int LPS = 8;  // loads per thread per stage
+  const int KT = p.KT;             // 64-byte stages
+  const int NP = (KT + 1) >> 1;    // pairs
+  constexpr int LPP = 16;          // loads per thread per pair
 
-  // One pipeline step on stage kt (ring slot S = kt % 4, register set S % 2).  The
-  // fragments of stage kt are already in registers, so once every wave has passed
-  // this step's barrier, stage kt's slot is free and receives stage kt+4 (four stages
-  // of prefetch in a four-slot ring).  Before the barrier: row 0's MFMAs; after it:
-  // the loads of stage kt+4 and the reads of stage kt+1 ride on rows 1-3.  With one
-  // wave per SIMD, everything that is not an MFMA has to issue in an MFMA's shadow.
-  auto step = [&](auto SLOT, int kt, auto STEADY) {
-    constexpr int S = decltype(SLOT)::value;
+  // Step kt computes stage kt (register set kt & 1) and reads stage kt+1's fragments.
+  // Even kt: stage kt+1 is the other half of the same pair slot, already published.
+  // Odd kt: stage kt+1 opens pair (kt+1)/2: wait for it, barrier (which also retires
+  // the slot of pair (kt-1)/2, whose last reads happened in step kt-1), then issue
+  // pair (kt+1)/2 + 1 into that slot.
+  auto step = [&](auto SLOTH, int kt, auto STEADY) {
+    constexpr int SH = decltype(SLOTH)::value;  // kt % 4
+    constexpr int set = SH & 1;
+    constexpr int slot = SH >> 1;               // pair slot of stage kt
     constexpr bool steady = decltype(STEADY)::value;
-    mfma_part(ic<S & 1>{}, ic<0>{});
-    if (steady || kt + 1 < KT) {
-      // stage kt+1 has landed once at most the stages issued after it are in flight;
-      // lgkmcnt(0): this wave's reads of stage kt are done before anyone refills its slot
-      const int after = steady ? 2 : ((KT - 1 < kt + 3 ? KT - 1 : kt + 3) - (kt + 1));
-      if (after >= 2) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * LPS));
-      else if (after == 1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(LPS));
-      else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-      __builtin_amdgcn_s_barrier();
+    constexpr bool odd = (SH & 1) != 0;
+    mfma_part(ic<set>{}, ic<0>{});
+    if constexpr (odd) {
+      if (steady || kt + 1 < KT) {
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+        __builtin_amdgcn_s_barrier();
+        if (steady || (kt + 1) / 2 + 1 < NP) issue_pair(ic<slot>{}, (kt + 1) / 2 + 1);
+        read_frags(ic<slot ^ 1>{}, ic<0>{}, ic<set ^ 1>{});
+      }
+    } else {
+      if (steady || kt + 1 < KT) read_frags(ic<slot>{}, ic<1>{}, ic<set ^ 1>{});
     }
-    if (steady || kt + 4 < KT) issue(ic<S>{}, kt + 4);
-    if (steady || kt + 1 < KT) read_frags(ic<(S + 1) & 3>{}, ic<(S + 1) & 1>{});
-    mfma_part(ic<S & 1>{}, ic<1>{});
+    mfma_part(ic<set>{}, ic<1>{});
     if constexpr (steady) {
       if constexpr (KIND == KIND_BF16) {
+        // 24 MFMAs of 32 cycles
+        if constexpr (odd) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (to LDS)
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          for (int t = 0; t < 8; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
         }
       } else {
+        // 12 MFMAs of 64 cycles
+        if constexpr (odd) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (to LDS)
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-        }
+          for (int t = 0; t < 8; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // 2 VMEM (to LDS)
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
+          }
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          for (int t = 0; t < 4; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          }
         }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // prologue: four stages in flight, stage 0 published and read
-  issue(ic<0>{}, 0);
-  if (KT > 1) issue(ic<1>{}, 1);
-  if (KT > 2) issue(ic<2>{}, 2);
-  if (KT > 3) issue(ic<3>{}, 3);
-  if (KT > 3) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(3 * LPS));
-  else if (KT > 2) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(2 * LPS));
-  else if (KT > 1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(LPS));
+  // prologue: pairs 0 and 1 in flight, pair 0 published, stage 0 read
+  issue_pair(ic<0>{}, 0);
+  if (NP > 1) issue_pair(ic<1>{}, 1);
+  if (NP > 1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(LPP));
   else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
   __builtin_amdgcn_s_barrier();
-  read_frags(ic<0>{}, ic<0>{});
+  read_frags(ic<0>{}, ic<0>{}, ic<0>{});
 
-  // steady state without branches (kt + 4 < KT for all four steps), then the tail
   int kt = 0;
-  for (; kt + 7 < KT; kt += 4) {
+  for (; kt + 7 < KT; kt += 4) {  // every step of the four has all of its work
     step(ic<0>{}, kt, std::true_type{});
     step(ic<1>{}, kt + 1, std::true_type{});
     step(ic<2>{}, kt + 2, std::true_type{});
@@ -605,8 +564,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm2(Params p) {
                               : static_cast<const float*>(p.bias)[col];
   }
   constexpr int kEpPitch = 512;                  // bytes per staged row
-  constexpr int kEpRegion = 64 * kEpPitch;       // 33 KB per wave
-  static_assert(4 * kEpRegion <= kScOff, "epilogue staging must fit in the operand ring");
+  constexpr int kEpRegion = 64 * kEpPitch;       // 32 KB per wave
+  static_assert(4 * kEpRegion <= 2 * kPB, "epilogue staging must fit in the pair slots");
   float* ep = reinterpret_cast<float*>(smem + wave * kEpRegion);
   __syncthreads();  // every wave is done with the operand ring
 #pragma unroll
@@ -670,12 +629,12 @@ hipError_t run(Params p, hipStream_t s, const char* name) {
   g_last_variant = name;
   const int nb = p.nbm * p.nbn;
   if constexpr (KIND == KIND_MX) {
-    // the scaled MFMA makes the v2 register schedule copy accumulators between AGPRs
-    // and VGPRs; the MX path keeps the v1 kernel until that is resolved
+    // the scaled MFMA makes the pair-pipeline register schedule copy accumulators
+    // between AGPRs and VGPRs; the MX path keeps the two-stage kernel for now
     hipLaunchKernelGGL((k_gemm<KIND_MX, AF, BF>), dim3(nb), dim3(NT), 0, s, p);
   } else {
     p.KT = (p.KB + SK - 1) / SK;
-    hipLaunchKernelGGL((k_gemm2<KIND, AF, BF>), dim3(nb), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL((k_gemm3<KIND, AF, BF>), dim3(nb), dim3(NT), 0, s, p);
   }
   return hipGetLastError();
 }
@@ -705,17 +664,17 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   p.d_bf16 = g.d_bf16;
   // f8f6f4 format codes: 0 = E4M3, 1 = E5M2
   const int af = (g.a_fmt == E5M2) ? 1 : 0, bf = (g.b_fmt == E5M2) ? 1 : 0;
-  if (g.a_fmt == BF16) return run<KIND_BF16, 0, 0>(p, s, "gemm2_bf16_256x256x32_ring4");
+  if (g.a_fmt == BF16) return run<KIND_BF16, 0, 0>(p, s, "gemm3_bf16_256x256x32_pairs");
   if (g.mx) {
     if (af == 0 && bf == 0) return run<KIND_MX, 0, 0>(p, s, "gemm_mx_e4m3_e4m3_256x256x128");
     if (af == 1 && bf == 0) return run<KIND_MX, 1, 0>(p, s, "gemm_mx_e5m2_e4m3_256x256x128");
     if (af == 0 && bf == 1) return run<KIND_MX, 0, 1>(p, s, "gemm_mx_e4m3_e5m2_256x256x128");
     return run<KIND_MX, 1, 1>(p, s, "gemm_mx_e5m2_e5m2_256x256x128");
   }
-  if (af == 0 && bf == 0) return run<KIND_FP8, 0, 0>(p, s, "gemm2_fp8_e4m3_e4m3_256x256x64_ring4");
-  if (af == 1 && bf == 0) return run<KIND_FP8, 1, 0>(p, s, "gemm2_fp8_e5m2_e4m3_256x256x64_ring4");
-  if (af == 0 && bf == 1) return run<KIND_FP8, 0, 1>(p, s, "gemm2_fp8_e4m3_e5m2_256x256x64_ring4");
-  return run<KIND_FP8, 1, 1>(p, s, "gemm2_fp8_e5m2_e5m2_256x256x64_ring4");
+  if (af == 0 && bf == 0) return run<KIND_FP8, 0, 0>(p, s, "gemm3_fp8_e4m3_e4m3_256x256x64_pairs");
+  if (af == 1 && bf == 0) return run<KIND_FP8, 1, 0>(p, s, "gemm3_fp8_e5m2_e4m3_256x256x64_pairs");
+  if (af == 0 && bf == 1) return run<KIND_FP8, 0, 1>(p, s, "gemm3_fp8_e4m3_e5m2_256x256x64_pairs");
+  return run<KIND_FP8, 1, 1>(p, s, "gemm3_fp8_e5m2_e5m2_256x256x64_pairs");
 }
 
 }  // namespace te

@@ -1,0 +1,47 @@
+// MFMA-only throughput probe: register operands, no memory traffic in the loop.
+// Measures the sustained FP8 (32x32x64 f8f6f4) and BF16 (32x32x16) matrix-core
+// rate of the device under the clocks it actually runs, as a ceiling beside the
+// published peak.  Built into libte_peak.so; driven by microbench.py ("peak").
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+template <bool BF16>
+__global__ __launch_bounds__(256, 1) void k_peak(const int* seed, float* out, int iters) {
+  const int t = threadIdx.x + seed[0];
+  v8i a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (t * 131 + i * 7) & 0x3f3f3f3f;
+    b[i] = (t * 17 + i * 3) & 0x3f3f3f3f;
+  }
+  v16f acc[16];
+  for (int i = 0; i < 16; ++i) acc[i] = v16f{0};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if constexpr (BF16) {
+        const v8bf av = __builtin_bit_cast(v8bf, __builtin_shufflevector(a, a, 0, 1, 2, 3));
+        const v8bf bv = __builtin_bit_cast(v8bf, __builtin_shufflevector(b, b, 0, 1, 2, 3));
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i], 0, 0, 0);
+      } else {
+        acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i], 0, 0, 0, 0, 0, 0);
+      }
+    }
+  }
+  float s = 0.f;
+  for (int i = 0; i < 16; ++i)
+    for (int j = 0; j < 16; ++j) s += acc[i][j];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+extern "C" int te_peak_launch(int bf16, int blocks, int iters, const int* seed, float* out, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (bf16)
+    hipLaunchKernelGGL((k_peak<true>), dim3(blocks), dim3(256), 0, st, seed, out, iters);
+  else
+    hipLaunchKernelGGL((k_peak<false>), dim3(blocks), dim3(256), 0, st, seed, out, iters);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}

@@ -95,6 +95,32 @@ def cast(args):
                       "gbs": round(nbytes / ms / 1e6, 1)}), flush=True)
 
 
+def peak(args):
+    """Sustained MFMA rate with register operands only (the clocks the device really runs)."""
+    import ctypes
+    import os
+    from .build import PEAK_LIB
+
+    if not os.path.exists(PEAK_LIB):
+        raise RuntimeError(f"{PEAK_LIB} missing: run __graft_entry__.build()")
+    L = ctypes.CDLL(PEAK_LIB)
+    L.te_peak_launch.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 3
+    dev = "cuda:0"
+    seed = torch.zeros(1, dtype=torch.int32, device=dev)
+    blocks = 256 * args.waves_per_cu  # one 4-wave block per CU per wave slot
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for kind in ("fp8", "bf16"):
+        bf = 1 if kind == "bf16" else 0
+        fn = lambda: L.te_peak_launch(bf, blocks, args.iters, ctypes.c_void_p(seed.data_ptr()),  # noqa: E731
+                                      ctypes.c_void_p(out.data_ptr()), st)
+        ms = _time(fn, 5, 2)
+        flop_per_mfma = 2 * 32 * 32 * (16 if bf else 64)
+        fl = float(blocks) * 4 * args.iters * 16 * flop_per_mfma
+        print(json.dumps({"kernel": f"mfma_peak_{kind}", "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1)}),
+              flush=True)
+
+
 def main():
     p = argparse.ArgumentParser()
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -115,9 +141,12 @@ def main():
     c.add_argument("--mode", choices=["delayed", "current"], default="delayed")
     c.add_argument("--iters", type=int, default=20)
     c.add_argument("--warmup", type=int, default=3)
+    k = sub.add_parser("peak")
+    k.add_argument("--iters", type=int, default=4096)
+    k.add_argument("--waves-per-cu", type=int, default=1)
     args = p.parse_args()
     torch.cuda.set_device(0)
-    {"gemm": gemm, "cast": cast}[args.cmd](args)
+    {"gemm": gemm, "cast": cast, "peak": peak}[args.cmd](args)
 
 
 if __name__ == "__main__":
