@@ -10,6 +10,11 @@
 // for current scaling, whose amax must exist before the first cast) and written
 // once per output layout.  Loads and stores are 16 bytes per lane.
 
+#include <map>
+#include <mutex>
+#include <type_traits>
+#include <utility>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -73,10 +78,71 @@ __global__ void k_current_scale(const float* amax, float* scale, float* scale_in
 }
 
 // ----------------------------------------------------------------------------
-// flat amax / cast.  MODE 0: amax + cast with *scale (delayed).  MODE 1: amax
+// flat amax / cast over 16-element chunks, persistent blocks, two chunks per
+// lane in flight.  MODE 0: amax + cast with *scale (delayed).  MODE 1: amax
 // only.  MODE 2: cast with the current scale derived from *amax (block 0 also
-// publishes scale and scale_inv).
+// publishes scale and scale_inv); chunks are visited last-to-first so the tail
+// of the input, read last by the amax pass, is reused from the last-level cache.
 // ----------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ void unpack16(const uint4& u, float* v);
+template <>
+__device__ __forceinline__ void unpack16<uint16_t>(const uint4& u, float* v) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_lo(w[i]);
+    v[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+template <>
+__device__ __forceinline__ void unpack16<float>(const uint4& u, float* v) {
+  v[0] = __uint_as_float(u.x);
+  v[1] = __uint_as_float(u.y);
+  v[2] = __uint_as_float(u.z);
+  v[3] = __uint_as_float(u.w);
+}
+
+template <typename T>
+__device__ __forceinline__ uint32_t raw_bits(const T* p);
+template <>
+__device__ __forceinline__ uint32_t raw_bits<uint16_t>(const uint16_t* p) { return *p; }
+template <>
+__device__ __forceinline__ uint32_t raw_bits<float>(const float* p) { return __float_as_uint(*p); }
+
+// Running max of |x| over raw input words, kept as magnitude bits: for
+// non-negative floats the bit patterns order as the values do, so an unsigned
+// max is the float max, and a NaN (bits above +inf) wins, as in a plain max.
+// bf16: two 16-bit magnitudes per word, combined with a packed 16-bit max.
+template <typename T>
+__device__ __forceinline__ uint32_t absmax_bits(uint32_t m, const uint4& u);
+template <>
+__device__ __forceinline__ uint32_t absmax_bits<uint16_t>(uint32_t m, const uint4& u) {
+  typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+  v2u16 a = __builtin_bit_cast(v2u16, m);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const v2u16 b = __builtin_bit_cast(v2u16, w[i] & 0x7fff7fffu);
+    a = __builtin_elementwise_max(a, b);
+  }
+  return __builtin_bit_cast(uint32_t, a);
+}
+template <>
+__device__ __forceinline__ uint32_t absmax_bits<float>(uint32_t m, const uint4& u) {
+  m = max(m, u.x & 0x7fffffffu);
+  m = max(m, u.y & 0x7fffffffu);
+  m = max(m, u.z & 0x7fffffffu);
+  m = max(m, u.w & 0x7fffffffu);
+  return m;
+}
+// the float value of a running max from absmax_bits
+template <typename T>
+__device__ __forceinline__ float absmax_value(uint32_t m) {
+  if constexpr (sizeof(T) == 2) return __uint_as_float(max(m & 0xffffu, m >> 16) << 16);
+  else return __uint_as_float(m);
+}
+
 template <typename T, bool E5M2, int MODE>
 __global__ __launch_bounds__(kThreads) void k_amax_cast(const T* __restrict__ x, int64_t n,
                                                         float* __restrict__ scale,
@@ -94,136 +160,266 @@ __global__ __launch_bounds__(kThreads) void k_amax_cast(const T* __restrict__ x,
       *scale_inv = 1.0f / s;
     }
   }
-  float m = 0.0f;
-  const int64_t nv = n >> 4;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < nv; i += stride) {
-    float v[16];
-    In<T>::load16(x + i * 16, v);
+  // a chunk is 16 elements = NW 16-byte words
+  constexpr int NW = 16 * static_cast<int>(sizeof(T)) / 16;
+  constexpr int EW = 16 / static_cast<int>(sizeof(T));
+  uint32_t m = 0u;  // running max of |x| as magnitude bits
+  auto load = [&](uint4* raw, int64_t c) {
+#pragma unroll
+    for (int k = 0; k < NW; ++k) raw[k] = reinterpret_cast<const uint4*>(x + c * 16)[k];
+  };
+  auto chunk = [&](const uint4* raw, int64_t c) {
     if constexpr (kAmax) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
+      for (int k = 0; k < NW; ++k) m = absmax_bits<T>(m, raw[k]);
     }
     if constexpr (kCast) {
+      float v[16];
+#pragma unroll
+      for (int k = 0; k < NW; ++k) unpack16<T>(raw[k], v + k * EW);
       uint4 q;
       q.x = quant4<E5M2>(v[0], v[1], v[2], v[3], s);
       q.y = quant4<E5M2>(v[4], v[5], v[6], v[7], s);
       q.z = quant4<E5M2>(v[8], v[9], v[10], v[11], s);
       q.w = quant4<E5M2>(v[12], v[13], v[14], v[15], s);
-      *reinterpret_cast<uint4*>(out + i * 16) = q;
+      *reinterpret_cast<uint4*>(out + c * 16) = q;
     }
+  };
+  const int64_t nv = n >> 4;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  auto at = [&](int64_t i) { return MODE == 2 ? nv - 1 - i : i; };
+  int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  for (; i + stride < nv; i += 2 * stride) {
+    const int64_t c0 = at(i), c1 = at(i + stride);
+    uint4 r0[NW], r1[NW];
+    load(r0, c0);
+    load(r1, c1);
+    chunk(r0, c0);
+    chunk(r1, c1);
+  }
+  if (i < nv) {
+    uint4 r0[NW];
+    load(r0, at(i));
+    chunk(r0, at(i));
   }
   if (blockIdx.x == 0) {  // tail of fewer than 16 elements
     const int64_t t = nv * 16 + threadIdx.x;
     if (t < n) {
-      const float v = In<T>::load1(x + t);
-      if constexpr (kAmax) m = __builtin_fmaxf(m, __builtin_fabsf(v));
-      if constexpr (kCast) out[t] = static_cast<uint8_t>(quant4<E5M2>(v, 0.f, 0.f, 0.f, s) & 0xffu);
+      const uint32_t b = raw_bits<T>(x + t);
+      if constexpr (kAmax) m = absmax_bits<T>(m, make_uint4(b, 0u, 0u, 0u));
+      if constexpr (kCast) {
+        const float v = sizeof(T) == 2 ? __uint_as_float(b << 16) : __uint_as_float(b);
+        out[t] = static_cast<uint8_t>(quant4<E5M2>(v, 0.f, 0.f, 0.f, s) & 0xffu);
+      }
     }
   }
-  if constexpr (kAmax) block_amax_atomic(m, amax);
+  if constexpr (kAmax) block_amax_atomic(absmax_value<T>(m), amax);
 }
 
 // ----------------------------------------------------------------------------
-// cast + transpose over 128 x 64 tiles.  MODE 0: amax + cast with *scale.
-// MODE 2: cast with the current scale from *amax.  The FP8 bytes of the tile go
-// through LDS; each wave then gathers 32 rows of 64 columns and writes them as
-// 32-byte runs of out_col.
+// cast + transpose, persistent blocks over 128 x 128 tiles.  MODE 0: amax +
+// cast with *scale.  MODE 2: cast with the current scale from *amax, tiles
+// visited last-to-first so that the end of the input, read last by the amax
+// pass, is still in the last-level cache when it is read again.
+//
+// Loads: 16 bytes per lane, a tile row is 256 (bf16) or 512 (fp32) contiguous
+// bytes.  Row-wise FP8 output: 8 or 4 bytes per lane, 128-byte rows.  The tile's
+// FP8 bytes go through LDS (pitch 132 bytes); for the transposed output each
+// lane reads a 16 x 4 byte block as 16 dwords, transposes it with byte permutes
+// and writes four 16-byte column runs; 8 consecutive lanes complete one
+// 128-byte line of out_col.  The next tile's loads are issued before the
+// current tile is converted, so each block keeps a tile in flight.
 // ----------------------------------------------------------------------------
-constexpr int kTR = 128, kTC = 64, kPitch = kTC + 4;
+constexpr int kCT = 128;             // tile edge
+constexpr int kCTPitch = kCT + 4;    // LDS bytes per tile row
 
 template <typename T>
-__device__ __forceinline__ bool rows_vec_ok(int64_t cols) {
-  return (cols % (16 / sizeof(T))) == 0;  // every row starts 16-byte aligned
+struct CTMap {
+  static constexpr int E = 16 / static_cast<int>(sizeof(T));  // elements per 16-byte load
+  static constexpr int LPR = kCT / E;                          // lanes per tile row
+  static constexpr int RPP = kThreads / LPR;                   // tile rows per pass
+  static constexpr int NP = kCT / RPP;                         // passes per tile
+};
+
+// Whole tiles take the vector path when rows and columns are vector-aligned and
+// every offset inside a tile fits in 31 bits.
+template <typename T>
+__host__ __device__ __forceinline__ bool ct_vec_ok(int64_t R, int64_t C) {
+  constexpr int64_t E = 16 / static_cast<int64_t>(sizeof(T));
+  return (C % E) == 0 && (R % 16) == 0 && C * kCT * static_cast<int64_t>(sizeof(T)) < (int64_t{1} << 31) &&
+         R * kCT < (int64_t{1} << 31);
 }
 
-template <typename T, bool E5M2, int MODE>
+// FAST = true: the whole tiles, 16-byte loads, vector stores, 32-bit offsets
+// inside a tile (the host checks that they fit).  FAST = false: the ragged
+// right column and bottom row of tiles (or every tile when rows or columns are
+// not vector-aligned), with element loads and byte stores under bounds checks.
+template <typename T, bool E5M2, int MODE, bool FAST>
 __global__ __launch_bounds__(kThreads) void k_cast_transpose(
     const T* __restrict__ x, int64_t R, int64_t C, float* __restrict__ scale,
     float* __restrict__ scale_inv, float* __restrict__ amax, uint8_t* __restrict__ out_row,
     uint8_t* __restrict__ out_col, int margin) {
-  __shared__ uint32_t tile[kTR * kPitch / 4];
-  uint8_t* tb = reinterpret_cast<uint8_t*>(tile);
+  using M = CTMap<T>;
+  constexpr int E = M::E, NP = M::NP, RPP = M::RPP;
+  constexpr int kBits = 8 * static_cast<int>(sizeof(T));
+  __shared__ uint32_t lds[kCT * kCTPitch / 4];
 
   float s = 1.0f;
   if constexpr (MODE == 0) s = *scale;
   if constexpr (MODE == 2) {
     s = scale_from_amax(*amax, Fp8Traits<E5M2>::max, margin, 1.0f);
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
       *scale = s;
       *scale_inv = 1.0f / s;
     }
   }
-  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kTR;
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kTC;
+  const int64_t ntc = (C + kCT - 1) / kCT, ntr = (R + kCT - 1) / kCT;
+  const int64_t nfc = C / kCT, nfr = R / kCT;  // whole tiles
+  const bool vec_ok = ct_vec_ok<T>(R, C);
+  const int64_t ntiles = FAST ? nfr * nfc : (vec_ok ? ntr * ntc - nfr * nfc : ntr * ntc);
   const int t = threadIdx.x;
-  const int lr = t >> 1, lc = (t & 1) * 32;
-  const int64_t r = r0 + lr;
-  const bool full = (r0 + kTR <= R) && (c0 + kTC <= C);
+  const int prow = t / M::LPR, pcol = (t % M::LPR) * E;  // load / row-output position in a pass
+  const int cg = t >> 3, rg = t & 7;                     // transposed output: columns 4cg.., rows 16rg..
+  const uint32_t ld_off = static_cast<uint32_t>((prow * C + pcol) * static_cast<int64_t>(sizeof(T)));
+  const uint32_t ld_pass = static_cast<uint32_t>(RPP * C * static_cast<int64_t>(sizeof(T)));
+  const uint32_t ro_off = static_cast<uint32_t>(prow * C + pcol);
+  const uint32_t ro_pass = static_cast<uint32_t>(RPP * C);
+  const uint32_t co_off = static_cast<uint32_t>(4 * cg * R + 16 * rg);
+  const uint32_t co_col = static_cast<uint32_t>(R);
+  uint32_t m = 0u;  // running max of |x| as magnitude bits
 
-  float v[32];
-  if (full && rows_vec_ok<T>(C)) {
-    const T* p = x + r * C + c0 + lc;
-    In<T>::load16(p, v);
-    In<T>::load16(p + 16, v + 16);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const int64_t c = c0 + lc + j;
-      v[j] = (r < R && c < C) ? In<T>::load1(x + r * C + c) : 0.0f;
+  auto origin = [&](int64_t i, int64_t& r0, int64_t& c0) {
+    if (FAST) {
+      const int64_t tile = MODE == 2 ? ntiles - 1 - i : i;
+      r0 = (tile / nfc) * kCT;
+      c0 = (tile % nfc) * kCT;
+    } else if (!vec_ok) {
+      r0 = (i / ntc) * kCT;
+      c0 = (i % ntc) * kCT;
+    } else if (i < nfr * (ntc - nfc)) {  // right column of ragged tiles
+      r0 = (i / (ntc - nfc)) * kCT;
+      c0 = (nfc + i % (ntc - nfc)) * kCT;
+    } else {  // bottom row
+      const int64_t j = i - nfr * (ntc - nfc);
+      r0 = (nfr + j / ntc) * kCT;
+      c0 = (j % ntc) * kCT;
     }
-  }
-  float m = 0.0f;
-  if constexpr (MODE == 0) {
+    return FAST;
+  };
+  // FAST: one 16-byte load per pass; otherwise element loads with bounds checks
+  // (outside the matrix reads as 0), packed into the same raw words.
+  auto load = [&](uint4* raw, int64_t r0, int64_t c0, bool) {
+    if constexpr (FAST) {
+      const uint8_t* base = reinterpret_cast<const uint8_t*>(x + r0 * C + c0);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) m = __builtin_fmaxf(m, __builtin_fabsf(v[j]));
-  }
-  uint32_t q[8];
+      for (int p = 0; p < NP; ++p) raw[p] = *reinterpret_cast<const uint4*>(base + ld_off + p * ld_pass);
+    } else {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) q[j] = quant4<E5M2>(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3], s);
-
-  if (out_row != nullptr) {
-    if (full && (C % 16) == 0) {
-      uint4* o = reinterpret_cast<uint4*>(out_row + r * C + c0 + lc);
-      o[0] = make_uint4(q[0], q[1], q[2], q[3]);
-      o[1] = make_uint4(q[4], q[5], q[6], q[7]);
-    } else if (r < R) {
+      for (int p = 0; p < NP; ++p) {
+        const int64_t r = r0 + p * RPP + prow;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const int64_t c = c0 + lc + j;
-        if (c < C) out_row[r * C + c] = static_cast<uint8_t>(q[j >> 2] >> (8 * (j & 3)));
+        for (int j = 0; j < E; ++j) {
+          const int64_t c = c0 + pcol + j;
+          const uint32_t b = (r < R && c < C) ? raw_bits<T>(x + r * C + c) : 0u;
+          w[(j * kBits) / 32] |= b << ((j * kBits) % 32);
+        }
+        raw[p] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
-  }
-  if (out_col != nullptr) {
+  };
+  auto process = [&](const uint4* raw, int64_t r0, int64_t c0, bool) {
+    __syncthreads();  // the previous tile's LDS reads are done
+    uint8_t* orow = out_row + r0 * C + c0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) tile[(lr * kPitch + lc) / 4 + j] = q[j];
+    for (int p = 0; p < NP; ++p) {
+      const int lr = p * RPP + prow;
+      float v[E];
+      unpack16<T>(raw[p], v);
+      if constexpr (MODE == 0) m = absmax_bits<T>(m, raw[p]);
+      uint32_t q[E / 4];
+#pragma unroll
+      for (int j = 0; j < E / 4; ++j) {
+        q[j] = quant4<E5M2>(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3], s);
+        lds[(lr * kCTPitch + pcol) / 4 + j] = q[j];
+      }
+      if (out_row != nullptr) {
+        if constexpr (FAST) {
+          uint8_t* o = orow + ro_off + p * ro_pass;
+          if constexpr (E == 8) *reinterpret_cast<uint2*>(o) = make_uint2(q[0], q[1]);
+          else *reinterpret_cast<uint32_t*>(o) = q[0];
+        } else if (r0 + lr < R) {
+          uint8_t* o = out_row + (r0 + lr) * C + c0 + pcol;
+#pragma unroll
+          for (int j = 0; j < E; ++j)
+            if (c0 + pcol + j < C) o[j] = static_cast<uint8_t>(q[j >> 2] >> (8 * (j & 3)));
+        }
+      }
+    }
+    if (out_col == nullptr) return;
     __syncthreads();
-    const int oc = t & 63, seg = t >> 6;
-    uint32_t w[8];
+    uint32_t d[16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int rr = seg * 32 + 4 * j;
-      w[j] = static_cast<uint32_t>(tb[(rr + 0) * kPitch + oc]) |
-             (static_cast<uint32_t>(tb[(rr + 1) * kPitch + oc]) << 8) |
-             (static_cast<uint32_t>(tb[(rr + 2) * kPitch + oc]) << 16) |
-             (static_cast<uint32_t>(tb[(rr + 3) * kPitch + oc]) << 24);
+    for (int k = 0; k < 16; ++k) d[k] = lds[((16 * rg + k) * kCTPitch) / 4 + cg];
+    // w[i][j]: column 4cg + i, rows 16rg + 4j .. 16rg + 4j + 3 (row-minor bytes)
+    uint32_t w[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t d0 = d[4 * j], d1 = d[4 * j + 1], d2 = d[4 * j + 2], d3 = d[4 * j + 3];
+      const uint32_t lo01 = __builtin_amdgcn_perm(d1, d0, 0x05010400u);  // d0.b0 d1.b0 d0.b1 d1.b1
+      const uint32_t hi01 = __builtin_amdgcn_perm(d1, d0, 0x07030602u);  // d0.b2 d1.b2 d0.b3 d1.b3
+      const uint32_t lo23 = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
+      const uint32_t hi23 = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
+      w[0][j] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+      w[1][j] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+      w[2][j] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+      w[3][j] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
     }
-    const int64_t c = c0 + oc;
-    const int64_t rb = r0 + seg * 32;
-    if (c < C) {
-      if (full && (R % 16) == 0) {
-        uint4* o = reinterpret_cast<uint4*>(out_col + c * R + rb);
-        o[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        o[1] = make_uint4(w[4], w[5], w[6], w[7]);
-      } else {
+    if constexpr (FAST) {
+      uint8_t* ocol = out_col + c0 * R + r0;
 #pragma unroll
-        for (int j = 0; j < 32; ++j)
-          if (rb + j < R) out_col[c * R + rb + j] = static_cast<uint8_t>(w[j >> 2] >> (8 * (j & 3)));
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint4*>(ocol + co_off + i * co_col) = make_uint4(w[i][0], w[i][1], w[i][2], w[i][3]);
+    } else {
+      const int64_t rb = r0 + 16 * rg;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t c = c0 + 4 * cg + i;
+        if (c < C) {
+          uint8_t* o = out_col + c * R + rb;
+#pragma unroll
+          for (int k = 0; k < 16; ++k)
+            if (rb + k < R) o[k] = static_cast<uint8_t>(w[i][k >> 2] >> (8 * (k & 3)));
+        }
       }
     }
+  };
+
+  int64_t i = blockIdx.x;
+  if (i < ntiles) {
+    uint4 cur[NP], nxt[NP];
+    int64_t r0, c0;
+    bool fast = origin(i, r0, c0);
+    load(cur, r0, c0, fast);
+    for (;;) {
+      const int64_t inext = i + gridDim.x;
+      int64_t r1 = 0, c1 = 0;
+      bool fast1 = false;
+      if (inext < ntiles) {
+        fast1 = origin(inext, r1, c1);
+        load(nxt, r1, c1, fast1);
+      }
+      process(cur, r0, c0, fast);
+      if (inext >= ntiles) break;
+      i = inext;
+      r0 = r1;
+      c0 = c1;
+      fast = fast1;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) cur[p] = nxt[p];
+    }
   }
-  if constexpr (MODE == 0) block_amax_atomic(m, amax);
+  if constexpr (MODE == 0) block_amax_atomic(absmax_value<T>(m), amax);
 }
 
 // ----------------------------------------------------------------------------
@@ -282,7 +478,13 @@ __device__ __forceinline__ void mx_block32(const float* v, uint32_t* q, uint8_t*
                       saturate<E5M2>(__builtin_ldexpf(v[4 * j + 3], -e)));
 }
 
-constexpr int kMxPitch = kTC + 1;  // floats
+constexpr int kTR = 128, kTC = 64;  // MXFP8 tile
+constexpr int kMxPitch = kTC + 1;   // floats
+
+template <typename T>
+__device__ __forceinline__ bool rows_vec_ok(int64_t cols) {
+  return (cols % (16 / sizeof(T))) == 0;  // every row starts 16-byte aligned
+}
 
 template <typename T, bool E5M2>
 __global__ __launch_bounds__(kThreads) void k_mxfp8(const T* __restrict__ x, int64_t R, int64_t C,
@@ -347,31 +549,57 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8(const T* __restrict__ x, int
   }
 }
 
-int flat_grid(int64_t nv) {
-  int64_t g = (nv + kThreads - 1) / kThreads;
+// Blocks of `kernel` (kThreads threads) resident at once on the current device,
+// capped at kMaxBlocksPerCU per compute unit; cached per kernel and device.
+constexpr int kMaxBlocksPerCU = 8;
+
+int resident_blocks(const void* kernel) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(kernel, dev);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 1, cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  if (per_cu > kMaxBlocksPerCU) per_cu = kMaxBlocksPerCU;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  const int g = per_cu * cus;
+  cache.emplace(key, g);
+  return g;
+}
+
+// Persistent grid: one block per `per_block` work units, at most one full wave of resident blocks.
+int persistent_grid(const void* kernel, int64_t units, int64_t per_block) {
+  int64_t g = (units + per_block - 1) / per_block;
+  const int64_t cap = resident_blocks(kernel);
+  if (g > cap) g = cap;
   if (g < 1) g = 1;
-  if (g > 2048) g = 2048;  // 8 resident blocks per CU on 256 CUs; grid-stride beyond that
   return static_cast<int>(g);
+}
+
+template <typename T, bool E5M2, int MODE>
+void launch_flat(const T* x, int64_t n, int margin, float* scale, float* scale_inv, float* amax,
+                 uint8_t* out, hipStream_t st) {
+  const auto fn = k_amax_cast<T, E5M2, MODE>;
+  const int g = persistent_grid(reinterpret_cast<const void*>(fn), n >> 4, kThreads);
+  hipLaunchKernelGGL(fn, dim3(g), dim3(kThreads), 0, st, x, n, scale, scale_inv, amax, out, margin);
 }
 
 template <typename T, bool E5M2>
 hipError_t amax_cast_t(const T* x, int64_t n, int current, int margin, float* scale,
                        float* scale_inv, float* amax, uint8_t* out, hipStream_t st) {
-  const int g = flat_grid(n >> 4);
   hipLaunchKernelGGL(k_prologue, dim3(1), dim3(1), 0, st, amax, scale, scale_inv, current ? 0 : 1);
   if (!current) {
-    if (out)
-      hipLaunchKernelGGL((k_amax_cast<T, E5M2, 0>), dim3(g), dim3(kThreads), 0, st, x, n, scale,
-                         scale_inv, amax, out, margin);
-    else
-      hipLaunchKernelGGL((k_amax_cast<T, E5M2, 1>), dim3(g), dim3(kThreads), 0, st, x, n, scale,
-                         scale_inv, amax, out, margin);
+    if (out) launch_flat<T, E5M2, 0>(x, n, margin, scale, scale_inv, amax, out, st);
+    else launch_flat<T, E5M2, 1>(x, n, margin, scale, scale_inv, amax, out, st);
   } else {
-    hipLaunchKernelGGL((k_amax_cast<T, E5M2, 1>), dim3(g), dim3(kThreads), 0, st, x, n, scale,
-                       scale_inv, amax, out, margin);
+    launch_flat<T, E5M2, 1>(x, n, margin, scale, scale_inv, amax, out, st);
     if (out)
-      hipLaunchKernelGGL((k_amax_cast<T, E5M2, 2>), dim3(g), dim3(kThreads), 0, st, x, n, scale,
-                         scale_inv, amax, out, margin);
+      launch_flat<T, E5M2, 2>(x, n, margin, scale, scale_inv, amax, out, st);
     else
       hipLaunchKernelGGL(k_current_scale, dim3(1), dim3(1), 0, st, amax, scale, scale_inv,
                          Fp8Traits<E5M2>::max, margin);
@@ -379,11 +607,29 @@ hipError_t amax_cast_t(const T* x, int64_t n, int current, int margin, float* sc
   return hipGetLastError();
 }
 
+template <typename T, bool E5M2, int MODE>
+void ct_launch(const T* x, int64_t R, int64_t C, int margin, float* scale, float* scale_inv,
+               float* amax, uint8_t* out_row, uint8_t* out_col, hipStream_t st) {
+  const int64_t whole = ct_vec_ok<T>(R, C) ? (R / kCT) * (C / kCT) : 0;
+  const int64_t ragged = ((R + kCT - 1) / kCT) * ((C + kCT - 1) / kCT) - whole;
+  if (whole > 0) {
+    const auto fn = k_cast_transpose<T, E5M2, MODE, true>;
+    const int g = persistent_grid(reinterpret_cast<const void*>(fn), whole, 1);
+    hipLaunchKernelGGL(fn, dim3(g), dim3(kThreads), 0, st, x, R, C, scale, scale_inv, amax, out_row,
+                       out_col, margin);
+  }
+  if (ragged > 0) {
+    const auto fn = k_cast_transpose<T, E5M2, MODE, false>;
+    const int g = persistent_grid(reinterpret_cast<const void*>(fn), ragged, 1);
+    hipLaunchKernelGGL(fn, dim3(g), dim3(kThreads), 0, st, x, R, C, scale, scale_inv, amax, out_row,
+                       out_col, margin);
+  }
+}
+
 template <typename T, bool E5M2>
 hipError_t cast_transpose_t(const T* x, int64_t R, int64_t C, int current, int margin,
                             float* scale, float* scale_inv, float* amax, uint8_t* out_row,
                             uint8_t* out_col, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>((C + kTC - 1) / kTC), static_cast<unsigned>((R + kTR - 1) / kTR));
   hipLaunchKernelGGL(k_prologue, dim3(1), dim3(1), 0, st, amax, scale, scale_inv, current ? 0 : 1);
   if (R == 0 || C == 0) {
     if (current)
@@ -391,16 +637,9 @@ hipError_t cast_transpose_t(const T* x, int64_t R, int64_t C, int current, int m
                          Fp8Traits<E5M2>::max, margin);
     return hipGetLastError();
   }
-  if (!current) {
-    hipLaunchKernelGGL((k_cast_transpose<T, E5M2, 0>), grid, dim3(kThreads), 0, st, x, R, C, scale,
-                       scale_inv, amax, out_row, out_col, margin);
-  } else {
-    const int g = flat_grid((R * C) >> 4);
-    hipLaunchKernelGGL((k_amax_cast<T, E5M2, 1>), dim3(g), dim3(kThreads), 0, st, x, R * C, scale,
-                       scale_inv, amax, nullptr, margin);
-    hipLaunchKernelGGL((k_cast_transpose<T, E5M2, 2>), grid, dim3(kThreads), 0, st, x, R, C, scale,
-                       scale_inv, amax, out_row, out_col, margin);
-  }
+  if (current) launch_flat<T, E5M2, 1>(x, R * C, margin, scale, scale_inv, amax, nullptr, st);
+  if (current) ct_launch<T, E5M2, 2>(x, R, C, margin, scale, scale_inv, amax, out_row, out_col, st);
+  else ct_launch<T, E5M2, 0>(x, R, C, margin, scale, scale_inv, amax, out_row, out_col, st);
   return hipGetLastError();
 }
 

@@ -116,7 +116,10 @@ def test_current_scaling_edge_amax():
         np.testing.assert_array_equal(host(out), O.scaled_cast(vals, np.float32(expect), O.E4M3))
 
 
-CT_SHAPES = [(128, 64), (300, 200), (1, 17), (77, 128), (4096, 768), (768, 3072), (33, 1)]
+# whole 128 x 128 tiles only, ragged only, both (bf16 rows need cols % 8, fp32 cols % 4,
+# and the transposed rows need rows % 16), and more tiles than resident blocks
+CT_SHAPES = [(128, 64), (300, 200), (1, 17), (77, 128), (4096, 768), (768, 3072), (33, 1),
+             (272, 392), (400, 260), (16, 16), (3072, 8192)]
 
 
 @pytest.mark.parametrize("shape", CT_SHAPES, ids=str)
@@ -151,6 +154,50 @@ def test_cast_transpose_parity(shape, xdt, mode, outs):
         np.testing.assert_array_equal(host(out_col), host(out_row).T)
     assert host(am)[0] == O.amax(xh)
     assert host(scale)[0] == ref_s and host(sinv)[0] == O.scale_inverse(ref_s)
+
+
+def test_cast_transpose_full_size_sampled():
+    """The 15872 x 4096 layer input (delayed, E4M3): amax and scales exact, and sampled rows
+    and columns of both layouts equal the oracle's cast of those rows and columns."""
+    R, C = 15872, 4096
+    x32 = synth.activations((R, C), 9, 4242, 0, 0)
+    xd, xh = input_pair(x32, "bf16")
+    out_row = torch.empty((R, C), dtype=torch.uint8, device=DEV)
+    out_col = torch.empty((C, R), dtype=torch.uint8, device=DEV)
+    s_in = np.float32(96.0)
+    scale, sinv, am = scalar(float(s_in)), empty_f32(), empty_f32()
+    B.te_cast_transpose(xd, "E4M3", B.TE_SCALE_DELAYED, 0, scale, sinv, am, out_row, out_col)
+    assert host(am)[0] == O.amax(xh)
+    assert host(sinv)[0] == O.scale_inverse(s_in)
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.r_[0, R - 1, rng.integers(0, R, 64)])
+    cols = np.unique(np.r_[0, C - 1, rng.integers(0, C, 64)])
+    got_r = out_row[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    np.testing.assert_array_equal(got_r, O.scaled_cast(xh[rows], s_in, O.E4M3))
+    got_c = out_col[torch.from_numpy(cols).to(DEV)].cpu().numpy()
+    np.testing.assert_array_equal(got_c, O.scaled_cast(np.ascontiguousarray(xh[:, cols].T), s_in, O.E4M3))
+
+
+def test_amax_propagates_nan():
+    """A NaN anywhere in the input makes amax NaN, as the oracle's plain max does; the other
+    elements still cast as the oracle casts them."""
+    x32 = synth.activations((256, 384), 9, 8, 0, 0)
+    x32[100, 200] = np.nan
+    for xdt in ("bf16", "f32"):
+        xd, xh = input_pair(x32, xdt)
+        assert np.isnan(O.amax(xh))
+        s_in = np.float32(4.0)
+        for fn in ("flat", "ct"):
+            am, out = empty_f32(), torch.empty((256, 384), dtype=torch.uint8, device=DEV)
+            am.zero_()
+            if fn == "flat":
+                B.te_amax_cast(xd, "E4M3", B.TE_SCALE_DELAYED, 0, scalar(float(s_in)), empty_f32(), am, out)
+            else:
+                B.te_cast_transpose(xd, "E4M3", B.TE_SCALE_DELAYED, 0, scalar(float(s_in)), empty_f32(), am,
+                                    out, None)
+            assert np.isnan(host(am)[0]), (xdt, fn)
+            nbad, _ = nan_aware_equal(host(out), O.scaled_cast(xh, s_in, O.E4M3), O.decode_table(O.E4M3))
+            assert nbad == 0, (xdt, fn)
 
 
 def test_cast_transpose_row_equals_amax_cast():
