@@ -38,6 +38,27 @@ MI355X_FP8_PEAK_TFLOPS = 5000.0   # dense FP8 MFMA (published)
 MI355X_BF16_PEAK_TFLOPS = 2500.0  # dense BF16 MFMA (published)
 MI355X_HBM_GBS = 8000.0           # HBM3E (published)
 
+# HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per
+# dispatch), each scaled by the factor that makes the same counter read the known size
+# of a plain 1 GiB device copy.  A figure is reported only while the kernel source it was
+# measured on is unchanged (sha256 of the file); otherwise traffic is null.
+MEASURED_TRAFFIC = {
+    # FP8 GEMM: mean over the layer's 12 GEMM launches (microbench layer --kind fp8)
+    "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip", "sha256": None,
+                 "bytes_per_launch": None},
+}
+
+
+def measured_traffic(key):
+    import hashlib
+    rec = MEASURED_TRAFFIC.get(key)
+    if not rec or rec["sha256"] is None:
+        return None
+    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
+            return None
+    return rec["bytes_per_launch"]
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -323,9 +344,12 @@ def main():
         t_ms = sum(med(per_gemm[gm][f"{g.weight}.{g.stage}"]) for g in gemms)
         achieved = flops / (t_ms * 1e-3) / 1e12 / 1.0
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MI355X_FP8_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / MI355X_FP8_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "k_gemm<KIND_FP8> (12 launches, 256x256x128 tiles)",
-                "avg_launch_ms": round(t_ms / len(gemms), 4)}
+                "unit": "TFLOP/s", "frac": round(achieved / MI355X_FP8_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic("gemm_fp8"),
+                "kernel": "k_gemm3 FP8 (256x256 tiles, 64-byte k stages loaded in 128-byte pairs); "
+                          "12 launches per layer, achieved = layer FLOP / summed launch time",
+                "avg_launch_ms": round(t_ms / len(gemms), 4),
+                "flop_per_launch": int(flops / len(gemms))}
     roof_q = None
     if "fp8_delayed_autocast" in modes:
         n_el = sum(2 * (M * w.in_features + w.out_features * w.in_features + M * w.out_features) for w in weights)

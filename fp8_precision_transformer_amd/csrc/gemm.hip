@@ -35,6 +35,15 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Two fp32 values to packed bf16 (x in the low half), round to nearest even, by the
+// gfx950 packed convert (v_cvt_pk_bf16_f32); a NaN stays a NaN.
+__device__ __forceinline__ unsigned bf16x2_rne(float x, float y) {
+  const v2bf v = {static_cast<__bf16>(x), static_cast<__bf16>(y)};
+  return __builtin_bit_cast(unsigned, v);
+}
 
 constexpr int BM = 256, BN = 256, BKB = 128, NT = 256;
 constexpr int kTileBytes = BM * BKB;  // one operand, one stage
@@ -622,6 +631,269 @@ __global__ __launch_bounds__(NT, 1) void k_gemm3(Params p) {
   }
 }
 
+// ============================================================================
+// Ping-pong pipeline: 8 waves, two per SIMD, in two groups of four.
+//
+// Each wave owns a 128 x 64 block of the 256 x 256 tile (waves 4 apart share a
+// SIMD, the same 128 rows and neighbouring 64-column halves).  The groups
+// alternate between a compute phase (16 FP8 MFMAs over one 128-byte k stage
+// held in registers, about 1024 cycles) and a memory phase (the next stage's
+// fragments from LDS; group 0 also issues the global->LDS loads of the stage
+// after that), so on every SIMD one wave keeps the matrix core busy while the
+// other waits on LDS and memory.  Two barriers per stage keep the rhythm:
+//
+//   phase 2s   : group 0 computes stage s    | group 1 reads stage s
+//   barrier X  : group 0 has waited for its loads of stage s+1 -> stage s+1
+//                is visible; group 1 has its stage-s fragments
+//   phase 2s+1 : group 0 reads stage s+1 and | group 1 computes stage s
+//                loads stage s+2 into the slot of stage s (read by both
+//                groups before X)
+//   barrier Y
+//
+// Loads get two phases (one stage) of latency.  LDS: two 64 KB stage slots in
+// the layout of the pair pipeline above (A [0, 64K), B [64K, 128K), rows of 8
+// swizzled 16-byte chunks).  Correctness does not depend on which SIMD a wave
+// lands on; only the overlap does.
+// ============================================================================
+constexpr int NT8 = 512;
+
+template <int KIND, int AF, int BF>
+__global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kPB];
+
+  const int nb = p.nbm * p.nbn;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, idx = bid >> 3;
+  const int per = nb >> 3, rem = nb & 7;
+  const int lin = xcd * per + (xcd < rem ? xcd : rem) + idx;
+  const int gspan = kGroupM * p.nbn;
+  const int group = lin / gspan;
+  const int first_m = group * kGroupM;
+  const int gsz = (p.nbm - first_m) < kGroupM ? (p.nbm - first_m) : kGroupM;
+  const int in_g = lin - group * gspan;
+  const int tm = first_m + in_g % gsz;
+  const int tn = in_g / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, q4 = wave & 3;
+  const int wm = (q4 >> 1) * 128, wn = (q4 & 1) * 128 + grp * 64;
+  const int lr = lane & 31, lk = lane >> 5;
+
+  const int rows_a = (p.M - m0) < BM ? (p.M - m0) : BM;
+  const int rows_b = (p.N - n0) < BN ? (p.N - n0) : BN;
+  const v4i rsA = make_rsrc(p.a + static_cast<int64_t>(m0) * p.KB, static_cast<uint32_t>(rows_a) * p.KB);
+  const v4i rsB = make_rsrc(p.b + static_cast<int64_t>(n0) * p.KB, static_cast<uint32_t>(rows_b) * p.KB);
+
+  // global->LDS (group 0): wave q4 moves rows [64 q4, 64 q4 + 64) of A and of B, 8 rows
+  // per instruction t (lane j: row 64 q4 + 8t + j/8, physical chunk j % 8, logical chunk
+  // (j % 8) ^ f(row) = c0 ^ (t & 3) with c0 = (j % 8) ^ (j / 8))
+  const int c0 = (lane & 7) ^ (lane >> 3);
+  const uint32_t ld_base = static_cast<uint32_t>(q4 * 64 + (lane >> 3)) * static_cast<uint32_t>(p.KB);
+  auto issue_stage = [&](auto SLOT, int st) {
+    constexpr int slot = decltype(SLOT)::value;
+    const uint32_t kb = static_cast<uint32_t>(st) * PK;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t cb = static_cast<uint32_t>((c0 ^ (t & 3)) << 4);
+      const uint32_t off = (kb + cb < static_cast<uint32_t>(p.KB))
+                               ? ld_base + static_cast<uint32_t>(t * 8) * static_cast<uint32_t>(p.KB) + kb + cb
+                               : kOOB;
+      const int base = slot * kPairOp + (q4 * 64 + t * 8) * PK;
+      raw_buffer_load_lds(rsA, (__attribute__((address_space(3))) uint32_t*)(smem + base), 16,
+                          static_cast<int>(off), 0, 0, 0);
+      raw_buffer_load_lds(rsB, (__attribute__((address_space(3))) uint32_t*)(smem + kPB + base), 16,
+                          static_cast<int>(off), 0, 0, 0);
+    }
+  };
+  constexpr int kLoadsPerStage = 16;
+
+  // fragments: A rows wm + 32 i + lr (i < 4), B rows wn + 32 j + lr (j < 2); k step h of
+  // the stage uses logical chunks 4h + lk (low 16 bytes) and 4h + 2 + lk (high 16 bytes)
+  // A row base wm + lr (a multiple of 128 bytes) or'd with the swizzled chunk: chunk
+  // 4h + lk + 2x is (lk ^ f(lr)) ^ (4h + 2x), i.e. the address bits 6 and 5 flip
+  const int fk = f8(lr);
+  const int ra0 = (wm + lr) * PK + ((lk ^ fk) << 4);
+  const int rb0 = kPB + (wn + lr) * PK + ((lk ^ fk) << 4);
+  v8i fa[2][4], fb[2][2];
+  auto read_stage = [&](auto SLOT) {
+    constexpr int slot = decltype(SLOT)::value;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int alo = ra0 ^ (h << 6), ahi = ra0 ^ (h << 6) ^ 32;
+      const int blo = rb0 ^ (h << 6), bhi = rb0 ^ (h << 6) ^ 32;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = slot * kPairOp + i * 32 * PK;
+        const v4u lo = *reinterpret_cast<const v4u*>(smem + alo + o);
+        const v4u hi = *reinterpret_cast<const v4u*>(smem + ahi + o);
+        fa[h][i] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int o = slot * kPairOp + j * 32 * PK;
+        const v4u lo = *reinterpret_cast<const v4u*>(smem + blo + o);
+        const v4u hi = *reinterpret_cast<const v4u*>(smem + bhi + o);
+        fb[h][j] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    }
+  };
+
+  v16f acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{0};
+
+  auto compute = [&]() {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (KIND == KIND_BF16) {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const v8i a = fa[h][i], b = fb[h][j];
+              const v8bf av = __builtin_bit_cast(v8bf, hh ? __builtin_shufflevector(a, a, 4, 5, 6, 7)
+                                                          : __builtin_shufflevector(a, a, 0, 1, 2, 3));
+              const v8bf bv = __builtin_bit_cast(v8bf, hh ? __builtin_shufflevector(b, b, 4, 5, 6, 7)
+                                                          : __builtin_shufflevector(b, b, 0, 1, 2, 3));
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i][j], 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[h][i], fb[h][j], acc[i][j], AF, BF,
+                                                                       0, 0, 0, 0);
+        }
+      }
+  };
+
+  const int S = (p.KB + PK - 1) / PK;  // 128-byte k stages (a ragged end reads as zeros)
+
+  // Both groups run the same loop body, compute stage s | barrier | read stage s+1 |
+  // barrier, so compute and fragment reads are one code path; group 1 runs it one
+  // phase behind group 0 (one extra barrier before its loop, matched by one after
+  // group 0's).  Group 0 alone waits for and issues the global->LDS loads.
+  if (grp == 0) {
+    issue_stage(ic<0>{}, 0);
+    if (S > 1) {
+      issue_stage(ic<1>{}, 1);
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kLoadsPerStage));
+    } else {
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+    }
+  }
+  __builtin_amdgcn_s_barrier();  // stage 0 visible
+  read_stage(ic<0>{});
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
+  __builtin_amdgcn_s_barrier();
+  if (grp == 1) __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+
+  auto iter = [&](auto SLOT, int s) {
+    constexpr int slot = decltype(SLOT)::value;
+    compute();
+    __builtin_amdgcn_sched_barrier(0);
+    if (grp == 0 && s + 1 < S) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));  // stage s+1 landed
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + 1 < S) read_stage(ic<slot ^ 1>{});
+    if (grp == 0 && s + 2 < S) issue_stage(ic<slot>{}, s + 2);  // the slot of stage s is free
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int s = 0;
+  for (; s + 1 < S; s += 2) {
+    iter(ic<0>{}, s);
+    iter(ic<1>{}, s + 1);
+  }
+  if (s < S) iter(ic<0>{}, s);
+  if (grp == 0) __builtin_amdgcn_s_barrier();
+
+  // ---- epilogue: scale, bias, round; staged through LDS for full-row 16-byte stores ----
+  // Each wave owns a 128 x 64 block, written in two passes of 64 rows through its own
+  // 16 KB LDS region (64 rows x 64 floats): a half-wave writes 32 consecutive floats
+  // of a row, then each lane reads 8 (bf16 out) or 4 (fp32 out) consecutive floats.
+  float sa = 1.0f, sb = 1.0f;
+  if constexpr (KIND == KIND_FP8) {
+    sa = *static_cast<const float*>(p.a_scale);
+    sb = *static_cast<const float*>(p.b_scale);
+  }
+  float bias_v[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = n0 + wn + j * 32 + lr;
+    bias_v[j] = 0.0f;
+    if (p.bias != nullptr && col < p.N)
+      bias_v[j] = p.bias_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p.bias)[col]) << 16)
+                              : static_cast<const float*>(p.bias)[col];
+  }
+  constexpr int kEpPitch = 256;             // bytes per staged row (64 floats)
+  constexpr int kEpRegion = 64 * kEpPitch;  // 16 KB per wave
+  static_assert(8 * kEpRegion <= 2 * kPB, "epilogue staging must fit in the stage slots");
+  float* ep = reinterpret_cast<float*>(smem + wave * kEpRegion);
+  // every wave's last LDS reads finished before the final barrier of the k loop
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = pass * 2 + ii;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float val = acc[i][j][v];
+          if constexpr (KIND == KIND_FP8) val = __fmul_rn(__fmul_rn(val, sa), sb);
+          if (p.bias != nullptr) val = __fadd_rn(val, bias_v[j]);
+          const int r = ii * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
+          ep[r * (kEpPitch / 4) + j * 32 + lr] = val;
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
+    __builtin_amdgcn_wave_barrier();
+    const int row0 = m0 + wm + pass * 64;
+    const int col0 = n0 + wn;
+    // Output goes out with nontemporal stores: a tile round writes as much as the L2
+    // holds, and cached stores would evict the operand panels the next k steps reuse.
+    if (p.d_bf16) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int r = t * 8 + (lane >> 3);
+        const int c = (lane & 7) * 8;
+        const float4 lo = *reinterpret_cast<const float4*>(ep + r * (kEpPitch / 4) + c);
+        const float4 hi = *reinterpret_cast<const float4*>(ep + r * (kEpPitch / 4) + c + 4);
+        const int grow = row0 + r, gcol = col0 + c;
+        if (grow < p.M && gcol < p.N) {
+          const v4u o = {bf16x2_rne(lo.x, lo.y), bf16x2_rne(lo.z, lo.w), bf16x2_rne(hi.x, hi.y),
+                         bf16x2_rne(hi.z, hi.w)};
+          __builtin_nontemporal_store(
+              o, reinterpret_cast<v4u*>(static_cast<uint16_t*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int r = t * 4 + (lane >> 4);
+        const int c = (lane & 15) * 4;
+        const v4f v4 = *reinterpret_cast<const v4f*>(ep + r * (kEpPitch / 4) + c);
+        const int grow = row0 + r, gcol = col0 + c;
+        if (grow < p.M && gcol < p.N)
+          __builtin_nontemporal_store(v4, reinterpret_cast<v4f*>(static_cast<float*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol));
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 thread_local const char* g_last_variant = "none";
 
 template <int KIND, int AF, int BF>
@@ -634,7 +906,7 @@ hipError_t run(Params p, hipStream_t s, const char* name) {
     hipLaunchKernelGGL((k_gemm<KIND_MX, AF, BF>), dim3(nb), dim3(NT), 0, s, p);
   } else {
     p.KT = (p.KB + SK - 1) / SK;
-    hipLaunchKernelGGL((k_gemm3<KIND, AF, BF>), dim3(nb), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL((k_gemm4<KIND, AF, BF>), dim3(nb), dim3(NT8), 0, s, p);
   }
   return hipGetLastError();
 }
@@ -664,17 +936,17 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   p.d_bf16 = g.d_bf16;
   // f8f6f4 format codes: 0 = E4M3, 1 = E5M2
   const int af = (g.a_fmt == E5M2) ? 1 : 0, bf = (g.b_fmt == E5M2) ? 1 : 0;
-  if (g.a_fmt == BF16) return run<KIND_BF16, 0, 0>(p, s, "gemm3_bf16_256x256x32_pairs");
+  if (g.a_fmt == BF16) return run<KIND_BF16, 0, 0>(p, s, "gemm4_bf16_256x256_pingpong");
   if (g.mx) {
     if (af == 0 && bf == 0) return run<KIND_MX, 0, 0>(p, s, "gemm_mx_e4m3_e4m3_256x256x128");
     if (af == 1 && bf == 0) return run<KIND_MX, 1, 0>(p, s, "gemm_mx_e5m2_e4m3_256x256x128");
     if (af == 0 && bf == 1) return run<KIND_MX, 0, 1>(p, s, "gemm_mx_e4m3_e5m2_256x256x128");
     return run<KIND_MX, 1, 1>(p, s, "gemm_mx_e5m2_e5m2_256x256x128");
   }
-  if (af == 0 && bf == 0) return run<KIND_FP8, 0, 0>(p, s, "gemm3_fp8_e4m3_e4m3_256x256x64_pairs");
-  if (af == 1 && bf == 0) return run<KIND_FP8, 1, 0>(p, s, "gemm3_fp8_e5m2_e4m3_256x256x64_pairs");
-  if (af == 0 && bf == 1) return run<KIND_FP8, 0, 1>(p, s, "gemm3_fp8_e4m3_e5m2_256x256x64_pairs");
-  return run<KIND_FP8, 1, 1>(p, s, "gemm3_fp8_e5m2_e5m2_256x256x64_pairs");
+  if (af == 0 && bf == 0) return run<KIND_FP8, 0, 0>(p, s, "gemm4_fp8_e4m3_e4m3_256x256_pingpong");
+  if (af == 1 && bf == 0) return run<KIND_FP8, 1, 0>(p, s, "gemm4_fp8_e5m2_e4m3_256x256_pingpong");
+  if (af == 0 && bf == 1) return run<KIND_FP8, 0, 1>(p, s, "gemm4_fp8_e4m3_e5m2_256x256_pingpong");
+  return run<KIND_FP8, 1, 1>(p, s, "gemm4_fp8_e5m2_e5m2_256x256_pingpong");
 }
 
 }  // namespace te

@@ -1,7 +1,9 @@
-// MFMA-only throughput probe: register operands, no memory traffic in the loop.
-// Measures the sustained FP8 (32x32x64 f8f6f4) and BF16 (32x32x16) matrix-core
-// rate of the device under the clocks it actually runs, as a ceiling beside the
-// published peak.  Built into libte_peak.so; driven by microbench.py ("peak").
+// Measurement probes, built into libte_peak.so and driven by microbench.py:
+//  - k_peak: MFMA-only throughput with register operands, no memory traffic in the
+//    loop: the sustained FP8 (32x32x64 f8f6f4) and BF16 (32x32x16) matrix-core rate
+//    under the clocks the device actually runs, as a ceiling beside the published peak;
+//  - k_copy: a plain 16-byte-per-lane device copy of known size, the reference that
+//    HBM byte counters (FETCH_SIZE, WRITE_SIZE) are calibrated against.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,5 +45,21 @@ extern "C" int te_peak_launch(int bf16, int blocks, int iters, const int* seed, 
     hipLaunchKernelGGL((k_peak<true>), dim3(blocks), dim3(256), 0, st, seed, out, iters);
   else
     hipLaunchKernelGGL((k_peak<false>), dim3(blocks), dim3(256), 0, st, seed, out, iters);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+// grid-stride copy of n16 16-byte words
+__global__ __launch_bounds__(256) void k_copy(const uint4* __restrict__ src, uint4* __restrict__ dst, int64_t n16) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+extern "C" int te_copy_launch(const void* src, void* dst, int64_t n16, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int64_t g = (n16 + 255) / 256;
+  if (g > 4096) g = 4096;
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL(k_copy, dim3(static_cast<unsigned>(g)), dim3(256), 0, st, static_cast<const uint4*>(src),
+                     static_cast<uint4*>(dst), n16);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }

@@ -2,6 +2,8 @@
 
     python -m fp8_precision_transformer_amd.microbench gemm --m 15872 --n 12288 --k 4096
     python -m fp8_precision_transformer_amd.microbench cast --rows 15872 --cols 16384
+    python -m fp8_precision_transformer_amd.microbench layer --kind fp8
+    python -m fp8_precision_transformer_amd.microbench copy --mib 1024
 
 Operands are random bytes / values drawn on the GPU (timing only; parity lives in
 tests/).  Each launch is timed with HIP events on the launch stream; the report
@@ -64,6 +66,106 @@ def gemm(args):
                       "tflops": round(fl / ms / 1e9, 1)}), flush=True)
 
 
+def _operands(kind, m, n, k, g, dev, fa="E4M3", fb="E4M3"):
+    """Random operands of one GEMM drawn on the GPU: finite mid-range FP8 codes with
+    random signs (unit MX scales), or bf16 normals."""
+    if kind == "bf16":
+        a = torch.randn((m, k), device=dev, generator=g).to(torch.bfloat16)
+        b = (torch.randn((n, k), device=dev, generator=g) * 0.02).to(torch.bfloat16)
+        return a, "BF16", None, b, "BF16", None, B.TE_GRAN_TENSOR
+
+    def codes(r, c):
+        return (torch.randint(0x18, 0x48, (r, c), device=dev, generator=g, dtype=torch.int32) |
+                (torch.randint(0, 2, (r, c), device=dev, generator=g, dtype=torch.int32) << 7)).to(torch.uint8)
+    a, b = codes(m, k), codes(n, k)
+    if kind == "mx":
+        sa = torch.full((m, k // 32), 127, dtype=torch.uint8, device=dev)
+        sb = torch.full((n, k // 32), 127, dtype=torch.uint8, device=dev)
+        return a, fa, sa, b, fb, sb, B.TE_GRAN_MX_BLOCK32
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    return a, fa, one, b, fb, one, B.TE_GRAN_TENSOR
+
+
+def layer(args):
+    """The 12 GEMMs of the CodonFM-5B-shaped layer (Fprop E4M3 x E4M3, Dgrad and Wgrad
+    E5M2 x E4M3 for the per-tensor kind), each launched --iters times; one JSON line per
+    GEMM and one for the layer (sum of medians)."""
+    from .shapes import CODONFM_5B, layer_gemms
+    dev = "cuda:0"
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    total_ms, total_fl = 0.0, 0.0
+    for gm in layer_gemms(CODONFM_5B):
+        fa = "E4M3" if (gm.stage == "fprop" or args.kind != "fp8") else "E5M2"
+        a, fa, sa, b, fb, sb, gran = _operands(args.kind, gm.m, gm.n, gm.k, g, dev, fa, "E4M3")
+        d = torch.empty((gm.m, gm.n), dtype=torch.bfloat16, device=dev)
+        ms = _time(lambda: B.te_fp8_gemm(a, fa, sa, b, fb, sb, d, gran=gran), args.iters, args.warmup)
+        total_ms += ms
+        total_fl += gm.flops
+        print(json.dumps({"kernel": f"gemm_{args.kind}", "gemm": f"{gm.weight}.{gm.stage}", "m": gm.m, "n": gm.n,
+                          "k": gm.k, "ms": round(ms, 5), "tflops": round(gm.flops / ms / 1e9, 1)}), flush=True)
+        del a, b, d
+    print(json.dumps({"kernel": f"gemm_{args.kind}", "gemm": "layer", "ms": round(total_ms, 4),
+                      "tflops": round(total_fl / total_ms / 1e9, 1)}), flush=True)
+
+
+def lib(args):
+    """The same 12 layer GEMMs through the vendor library (torch._scaled_mm -> hipBLASLt
+    for FP8, torch.matmul for BF16): a timing reference beside this library's kernels,
+    not part of its path."""
+    from .shapes import CODONFM_5B, layer_gemms
+    dev = "cuda:0"
+    total_ms, total_fl = 0.0, 0.0
+    one = torch.ones((), dtype=torch.float32, device=dev)
+    for gm in layer_gemms(CODONFM_5B):
+        a = torch.randn((gm.m, gm.k), device=dev).to(torch.bfloat16)
+        b = (torch.randn((gm.n, gm.k), device=dev) * 0.02).to(torch.bfloat16)
+        if args.kind == "fp8":
+            fa = torch.float8_e4m3fn if (gm.stage == "fprop" or not args.hybrid) else torch.float8_e5m2
+            a8, b8 = a.to(fa), b.to(torch.float8_e4m3fn)
+            fn = lambda: torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)  # noqa: E731
+        else:
+            bt = b.t()
+            fn = lambda: torch.matmul(a, bt)  # noqa: E731
+        ms = _time(fn, args.iters, args.warmup)
+        total_ms += ms
+        total_fl += gm.flops
+        print(json.dumps({"kernel": f"lib_{args.kind}", "gemm": f"{gm.weight}.{gm.stage}", "ms": round(ms, 5),
+                          "tflops": round(gm.flops / ms / 1e9, 1)}), flush=True)
+    print(json.dumps({"kernel": f"lib_{args.kind}", "gemm": "layer", "ms": round(total_ms, 4),
+                      "tflops": round(total_fl / total_ms / 1e9, 1)}), flush=True)
+
+
+def _peak_lib():
+    import ctypes
+    import os
+    from .build import PEAK_LIB
+
+    if not os.path.exists(PEAK_LIB):
+        raise RuntimeError(f"{PEAK_LIB} missing: run __graft_entry__.build()")
+    L = ctypes.CDLL(PEAK_LIB)
+    L.te_peak_launch.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 3
+    L.te_copy_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    return L
+
+
+def copy(args):
+    """A plain device copy (k_copy, 16 bytes per lane) of --mib MiB: the known-size
+    reference that HBM byte counters are calibrated against."""
+    import ctypes
+    L = _peak_lib()
+    dev = "cuda:0"
+    n = args.mib * (1 << 20)
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ms = _time(lambda: L.te_copy_launch(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                        n // 16, st), args.iters, args.warmup)
+    assert torch.equal(src, dst)
+    print(json.dumps({"kernel": "k_copy", "bytes_read": n, "bytes_written": n, "ms": round(ms, 5),
+                      "gbs": round(2 * n / ms / 1e6, 1)}), flush=True)
+
+
 def cast(args):
     dev = "cuda:0"
     x = torch.randn((args.rows, args.cols), device=dev).to(torch.bfloat16)
@@ -98,13 +200,7 @@ def cast(args):
 def peak(args):
     """Sustained MFMA rate with register operands only (the clocks the device really runs)."""
     import ctypes
-    import os
-    from .build import PEAK_LIB
-
-    if not os.path.exists(PEAK_LIB):
-        raise RuntimeError(f"{PEAK_LIB} missing: run __graft_entry__.build()")
-    L = ctypes.CDLL(PEAK_LIB)
-    L.te_peak_launch.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 3
+    L = _peak_lib()
     dev = "cuda:0"
     seed = torch.zeros(1, dtype=torch.int32, device=dev)
     blocks = 256 * args.waves_per_cu  # one 4-wave block per CU per wave slot
@@ -141,12 +237,25 @@ def main():
     c.add_argument("--mode", choices=["delayed", "current"], default="delayed")
     c.add_argument("--iters", type=int, default=20)
     c.add_argument("--warmup", type=int, default=3)
+    ly = sub.add_parser("layer")
+    ly.add_argument("--kind", choices=["fp8", "mx", "bf16"], default="fp8")
+    ly.add_argument("--iters", type=int, default=10)
+    ly.add_argument("--warmup", type=int, default=2)
+    lb = sub.add_parser("lib")
+    lb.add_argument("--kind", choices=["fp8", "bf16"], default="fp8")
+    lb.add_argument("--hybrid", action="store_true", help="E5M2 left operand for Dgrad/Wgrad")
+    lb.add_argument("--iters", type=int, default=10)
+    lb.add_argument("--warmup", type=int, default=2)
+    cp = sub.add_parser("copy")
+    cp.add_argument("--mib", type=int, default=1024)
+    cp.add_argument("--iters", type=int, default=10)
+    cp.add_argument("--warmup", type=int, default=2)
     k = sub.add_parser("peak")
     k.add_argument("--iters", type=int, default=4096)
     k.add_argument("--waves-per-cu", type=int, default=1)
     args = p.parse_args()
     torch.cuda.set_device(0)
-    {"gemm": gemm, "cast": cast, "peak": peak}[args.cmd](args)
+    {"gemm": gemm, "cast": cast, "peak": peak, "layer": layer, "copy": copy, "lib": lib}[args.cmd](args)
 
 
 if __name__ == "__main__":
