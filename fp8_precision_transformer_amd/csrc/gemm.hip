@@ -659,7 +659,10 @@ constexpr int NT8 = 512;
 
 template <int KIND, int AF, int BF>
 __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kPB];
+  constexpr bool MX = KIND == KIND_MX;
+  // MX: per stage slot, one dword of four E8M0 block scales per row of A (1 KB) and of B (1 KB)
+  constexpr int kScOff = 2 * kPB, kScSlot = 2048;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kPB + (MX ? 2 * kScSlot : 0)];
 
   const int nb = p.nbm * p.nbn;
   const int bid = blockIdx.x;
@@ -692,9 +695,26 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
   // (j % 8) ^ f(row) = c0 ^ (t & 3) with c0 = (j % 8) ^ (j / 8))
   const int c0 = (lane & 7) ^ (lane >> 3);
   const uint32_t ld_base = static_cast<uint32_t>(q4 * 64 + (lane >> 3)) * static_cast<uint32_t>(p.KB);
+  // MX scales (k % 128 == 0 here): stage st of row r is the dword at r * kblocks + 4 st;
+  // lane l of group-0 wave q4 fetches row 64 q4 + l of A and of B (rows past m or n read 0)
+  v4i rsSA = {0, 0, 0, 0}, rsSB = {0, 0, 0, 0};
+  if constexpr (MX) {
+    rsSA = make_rsrc(static_cast<const uint8_t*>(p.a_scale) + static_cast<int64_t>(m0) * p.kblocks,
+                     static_cast<uint32_t>(rows_a) * p.kblocks);
+    rsSB = make_rsrc(static_cast<const uint8_t*>(p.b_scale) + static_cast<int64_t>(n0) * p.kblocks,
+                     static_cast<uint32_t>(rows_b) * p.kblocks);
+  }
+  const uint32_t sc_off = static_cast<uint32_t>(q4 * 64 + lane) * static_cast<uint32_t>(p.kblocks);
   auto issue_stage = [&](auto SLOT, int st) {
     constexpr int slot = decltype(SLOT)::value;
     const uint32_t kb = static_cast<uint32_t>(st) * PK;
+    if constexpr (MX) {
+      const int sbase = kScOff + slot * kScSlot + q4 * 256;
+      raw_buffer_load_lds(rsSA, (__attribute__((address_space(3))) uint32_t*)(smem + sbase), 4,
+                          static_cast<int>(sc_off + 4u * st), 0, 0, 0);
+      raw_buffer_load_lds(rsSB, (__attribute__((address_space(3))) uint32_t*)(smem + sbase + 1024), 4,
+                          static_cast<int>(sc_off + 4u * st), 0, 0, 0);
+    }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const uint32_t cb = static_cast<uint32_t>((c0 ^ (t & 3)) << 4);
@@ -708,20 +728,44 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
                           static_cast<int>(off), 0, 0, 0);
     }
   };
-  constexpr int kLoadsPerStage = 16;
+  constexpr int kLoadsPerStage = MX ? 18 : 16;
+
+  // A phase covers NH of the stage's two 64-byte k steps: both for FP8 and BF16; one
+  // for MX, whose scaled MFMA needs a fresh accumulator tuple per instruction and so
+  // cannot also hold a whole stage of fragments within 256 registers.
+  constexpr int NH = MX ? 1 : 2;
+  constexpr int PPS = 2 / NH;  // phases per stage and group
 
   // fragments: A rows wm + 32 i + lr (i < 4), B rows wn + 32 j + lr (j < 2); k step h of
-  // the stage uses logical chunks 4h + lk (low 16 bytes) and 4h + 2 + lk (high 16 bytes)
+  // the stage uses logical chunks 4h + lk (low 16 bytes) and 4h + 2 + lk (high 16 bytes).
   // A row base wm + lr (a multiple of 128 bytes) or'd with the swizzled chunk: chunk
   // 4h + lk + 2x is (lk ^ f(lr)) ^ (4h + 2x), i.e. the address bits 6 and 5 flip
   const int fk = f8(lr);
   const int ra0 = (wm + lr) * PK + ((lk ^ fk) << 4);
   const int rb0 = kPB + (wn + lr) * PK + ((lk ^ fk) << 4);
-  v8i fa[2][4], fb[2][2];
-  auto read_stage = [&](auto SLOT) {
+  v8i fa[NH][4], fb[NH][2];
+  // MX: this lane's block scales for the stage.  A lane supplies the scale of block
+  // 2h + lk of its row for k step h; two row groups share a dword: byte 2h + g holds
+  // row group 2p + g (A: dwords p = 0, 1; B: one dword for its two row groups).
+  uint32_t sa2[2] = {0u, 0u}, sb1 = 0u;
+  // read the fragments of part P (k steps P*NH ..) of the stage in SLOT
+  auto read_part = [&](auto SLOT, auto PART) {
     constexpr int slot = decltype(SLOT)::value;
+    constexpr int part = decltype(PART)::value;
+    if constexpr (MX) {
+      if constexpr (part == 0) {
+        const uint32_t* sc = reinterpret_cast<const uint32_t*>(smem + kScOff + slot * kScSlot);
+        auto pack = [&](uint32_t w0, uint32_t w1) {
+          return ((w0 >> (8 * lk)) & 0x00ff00ffu) | (((w1 >> (8 * lk)) & 0x00ff00ffu) << 8);
+        };
+        sa2[0] = pack(sc[wm + lr], sc[wm + 32 + lr]);
+        sa2[1] = pack(sc[wm + 64 + lr], sc[wm + 96 + lr]);
+        sb1 = pack(sc[256 + wn + lr], sc[256 + wn + 32 + lr]);
+      }
+    }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int hh = 0; hh < NH; ++hh) {
+      const int h = part * NH + hh;
       const int alo = ra0 ^ (h << 6), ahi = ra0 ^ (h << 6) ^ 32;
       const int blo = rb0 ^ (h << 6), bhi = rb0 ^ (h << 6) ^ 32;
 #pragma unroll
@@ -729,14 +773,14 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
         const int o = slot * kPairOp + i * 32 * PK;
         const v4u lo = *reinterpret_cast<const v4u*>(smem + alo + o);
         const v4u hi = *reinterpret_cast<const v4u*>(smem + ahi + o);
-        fa[h][i] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        fa[hh][i] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int o = slot * kPairOp + j * 32 * PK;
         const v4u lo = *reinterpret_cast<const v4u*>(smem + blo + o);
         const v4u hi = *reinterpret_cast<const v4u*>(smem + bhi + o);
-        fb[h][j] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        fb[hh][j] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
   };
@@ -747,38 +791,61 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = v16f{0};
 
-  auto compute = [&]() {
+  // MX MFMA for k step H, A row group I, B row group J: opsel picks byte 2H + (group & 1)
+  // of the packed scale dwords
+  auto mfma_mx = [&](auto H, auto I, auto J, const v8i& a, const v8i& b) {
+    constexpr int h = decltype(H)::value, i = decltype(I)::value, j = decltype(J)::value;
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        a, b, acc[i][j], AF, BF, 2 * h + (i & 1), static_cast<int>(sa2[i >> 1]), 2 * h + j, static_cast<int>(sb1));
+  };
+  auto compute_part = [&](auto PART) {
+    constexpr int part = decltype(PART)::value;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int hh = 0; hh < NH; ++hh) {
+      if constexpr (KIND == KIND_BF16) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (KIND == KIND_BF16) {
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
+          for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-              const v8i a = fa[h][i], b = fb[h][j];
-              const v8bf av = __builtin_bit_cast(v8bf, hh ? __builtin_shufflevector(a, a, 4, 5, 6, 7)
-                                                          : __builtin_shufflevector(a, a, 0, 1, 2, 3));
-              const v8bf bv = __builtin_bit_cast(v8bf, hh ? __builtin_shufflevector(b, b, 4, 5, 6, 7)
-                                                          : __builtin_shufflevector(b, b, 0, 1, 2, 3));
+              const v8i a = fa[hh][i], b = fb[hh][j];
+              const v8bf av = __builtin_bit_cast(v8bf, q ? __builtin_shufflevector(a, a, 4, 5, 6, 7)
+                                                         : __builtin_shufflevector(a, a, 0, 1, 2, 3));
+              const v8bf bv = __builtin_bit_cast(v8bf, q ? __builtin_shufflevector(b, b, 4, 5, 6, 7)
+                                                         : __builtin_shufflevector(b, b, 0, 1, 2, 3));
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i][j], 0, 0, 0);
             }
-        } else {
+      } else if constexpr (MX) {
+        constexpr int h = part;  // NH == 1
+        mfma_mx(ic<h>{}, ic<0>{}, ic<0>{}, fa[0][0], fb[0][0]);
+        mfma_mx(ic<h>{}, ic<0>{}, ic<1>{}, fa[0][0], fb[0][1]);
+        mfma_mx(ic<h>{}, ic<1>{}, ic<0>{}, fa[0][1], fb[0][0]);
+        mfma_mx(ic<h>{}, ic<1>{}, ic<1>{}, fa[0][1], fb[0][1]);
+        mfma_mx(ic<h>{}, ic<2>{}, ic<0>{}, fa[0][2], fb[0][0]);
+        mfma_mx(ic<h>{}, ic<2>{}, ic<1>{}, fa[0][2], fb[0][1]);
+        mfma_mx(ic<h>{}, ic<3>{}, ic<0>{}, fa[0][3], fb[0][0]);
+        mfma_mx(ic<h>{}, ic<3>{}, ic<1>{}, fa[0][3], fb[0][1]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[h][i], fb[h][j], acc[i][j], AF, BF,
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[hh][i], fb[hh][j], acc[i][j], AF, BF,
                                                                        0, 0, 0, 0);
-        }
       }
+    }
   };
 
   const int S = (p.KB + PK - 1) / PK;  // 128-byte k stages (a ragged end reads as zeros)
+  const int T = S * PPS;               // phases per group
 
-  // Both groups run the same loop body, compute stage s | barrier | read stage s+1 |
+  // Both groups run the same loop body, compute part u | barrier | read part u+1 |
   // barrier, so compute and fragment reads are one code path; group 1 runs it one
   // phase behind group 0 (one extra barrier before its loop, matched by one after
-  // group 0's).  Group 0 alone waits for and issues the global->LDS loads.
+  // group 0's).  Group 0 alone waits for and issues the global->LDS loads: at the end
+  // of a stage's last part it waits for the next stage, and after the barrier it loads
+  // the stage after that into the slot both groups have finished reading.
   if (grp == 0) {
     issue_stage(ic<0>{}, 0);
     if (S > 1) {
@@ -789,32 +856,53 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
     }
   }
   __builtin_amdgcn_s_barrier();  // stage 0 visible
-  read_stage(ic<0>{});
+  read_part(ic<0>{}, ic<0>{});
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
   __builtin_amdgcn_s_barrier();
   if (grp == 1) __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
-  auto iter = [&](auto SLOT, int s) {
-    constexpr int slot = decltype(SLOT)::value;
-    compute();
+  // phase u = PPS * s + part; U = u mod 2 PPS fixes slot and part at compile time
+  auto iter = [&](auto U, int u) {
+    constexpr int uu = decltype(U)::value;
+    constexpr int slot = (uu / PPS) & 1, part = uu % PPS;
+    constexpr bool last_part = part == PPS - 1;
+    constexpr int nslot = last_part ? (slot ^ 1) : slot, npart = last_part ? 0 : part + 1;
+    const int s = u / PPS;
+    compute_part(ic<part>{});
+    if constexpr (MX) {
+      // pin the phase's scaled MFMAs here: left free, the optimizer gathers them across
+      // phases and the live fragments overflow the register file
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(acc[i][j]));
+    }
     __builtin_amdgcn_sched_barrier(0);
-    if (grp == 0 && s + 1 < S) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));  // stage s+1 landed
+    if (last_part && grp == 0 && s + 1 < S) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));  // stage s+1 landed
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    if (s + 1 < S) read_stage(ic<slot ^ 1>{});
-    if (grp == 0 && s + 2 < S) issue_stage(ic<slot>{}, s + 2);  // the slot of stage s is free
+    if (u + 1 < T) read_part(ic<nslot>{}, ic<npart>{});
+    if (last_part && grp == 0 && s + 2 < S) issue_stage(ic<slot>{}, s + 2);  // the slot of stage s is free
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
-  int s = 0;
-  for (; s + 1 < S; s += 2) {
-    iter(ic<0>{}, s);
-    iter(ic<1>{}, s + 1);
+  int u = 0;
+  for (; u + 2 * PPS - 1 < T; u += 2 * PPS) {
+    iter(ic<0>{}, u);
+    iter(ic<1>{}, u + 1);
+    if constexpr (PPS == 2) {
+      iter(ic<2>{}, u + 2);
+      iter(ic<3>{}, u + 3);
+    }
   }
-  if (s < S) iter(ic<0>{}, s);
+  if (u < T) iter(ic<0>{}, u);
+  if (u + 1 < T) iter(ic<1>{}, u + 1);
+  if constexpr (PPS == 2) {
+    if (u + 2 < T) iter(ic<2>{}, u + 2);
+  }
   if (grp == 0) __builtin_amdgcn_s_barrier();
 
   // ---- epilogue: scale, bias, round; staged through LDS for full-row 16-byte stores ----
@@ -900,9 +988,9 @@ template <int KIND, int AF, int BF>
 hipError_t run(Params p, hipStream_t s, const char* name) {
   g_last_variant = name;
   const int nb = p.nbm * p.nbn;
-  if constexpr (KIND == KIND_MX) {
-    // the scaled MFMA makes the pair-pipeline register schedule copy accumulators
-    // between AGPRs and VGPRs; the MX path keeps the two-stage kernel for now
+  if (KIND == KIND_MX && (p.kblocks & 3) != 0) {
+    // a k that is not a multiple of 128 leaves a partial scale dword per stage: the
+    // two-stage kernel fills it per byte
     hipLaunchKernelGGL((k_gemm<KIND_MX, AF, BF>), dim3(nb), dim3(NT), 0, s, p);
   } else {
     p.KT = (p.KB + SK - 1) / SK;
@@ -938,10 +1026,10 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   const int af = (g.a_fmt == E5M2) ? 1 : 0, bf = (g.b_fmt == E5M2) ? 1 : 0;
   if (g.a_fmt == BF16) return run<KIND_BF16, 0, 0>(p, s, "gemm4_bf16_256x256_pingpong");
   if (g.mx) {
-    if (af == 0 && bf == 0) return run<KIND_MX, 0, 0>(p, s, "gemm_mx_e4m3_e4m3_256x256x128");
-    if (af == 1 && bf == 0) return run<KIND_MX, 1, 0>(p, s, "gemm_mx_e5m2_e4m3_256x256x128");
-    if (af == 0 && bf == 1) return run<KIND_MX, 0, 1>(p, s, "gemm_mx_e4m3_e5m2_256x256x128");
-    return run<KIND_MX, 1, 1>(p, s, "gemm_mx_e5m2_e5m2_256x256x128");
+    if (af == 0 && bf == 0) return run<KIND_MX, 0, 0>(p, s, "gemm4_mx_e4m3_e4m3_256x256_pingpong");
+    if (af == 1 && bf == 0) return run<KIND_MX, 1, 0>(p, s, "gemm4_mx_e5m2_e4m3_256x256_pingpong");
+    if (af == 0 && bf == 1) return run<KIND_MX, 0, 1>(p, s, "gemm4_mx_e4m3_e5m2_256x256_pingpong");
+    return run<KIND_MX, 1, 1>(p, s, "gemm4_mx_e5m2_e5m2_256x256_pingpong");
   }
   if (af == 0 && bf == 0) return run<KIND_FP8, 0, 0>(p, s, "gemm4_fp8_e4m3_e4m3_256x256_pingpong");
   if (af == 1 && bf == 0) return run<KIND_FP8, 1, 0>(p, s, "gemm4_fp8_e5m2_e4m3_256x256_pingpong");

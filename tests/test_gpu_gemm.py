@@ -122,8 +122,10 @@ def test_bf16_gemm_parity(mnk):
         assert err <= TOL[odt], (odt, err)
 
 
+# k % 128 == 0 takes the ping-pong kernel (scales loaded a dword per row and stage), other
+# k the two-stage kernel; ragged m and n in both
 @pytest.mark.parametrize("mnk", [(32, 32, 64), (300, 272, 416), (1024, 768, 768), (256, 256, 4096),
-                                 (64, 128, 96)], ids=str)
+                                 (64, 128, 96), (520, 400, 640)], ids=str)
 @pytest.mark.parametrize("fa,fb", [("E4M3", "E4M3"), ("E5M2", "E4M3")])
 def test_mx_gemm_parity(mnk, fa, fb):
     m, n, k = mnk
