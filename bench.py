@@ -44,8 +44,9 @@ MI355X_HBM_GBS = 8000.0           # HBM3E (published)
 # measured on is unchanged (sha256 of the file); otherwise traffic is null.
 MEASURED_TRAFFIC = {
     # FP8 GEMM: mean over the layer's 12 GEMM launches (microbench layer --kind fp8)
-    "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip", "sha256": None,
-                 "bytes_per_launch": None},
+    "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
+                 "sha256": "ee0c545daa6102feabf3211d7cc2d281aeed4e35f4cb7775dbcfa8f39554a71e",
+                 "bytes_per_launch": 1677534397},
 }
 
 
@@ -67,7 +68,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--modes", default="all")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=48, help="sampled output rows per GEMM for the oracle")
+    p.add_argument("--cpu-rows", type=int, default=640, help="sampled output rows per GEMM for the oracle")
     return p.parse_args()
 
 
@@ -346,8 +347,9 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MI355X_FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MI355X_FP8_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic("gemm_fp8"),
-                "kernel": "k_gemm3 FP8 (256x256 tiles, 64-byte k stages loaded in 128-byte pairs); "
-                          "12 launches per layer, achieved = layer FLOP / summed launch time",
+                "kernel": "k_gemm4 FP8 (256x256 tiles, 8 waves in ping-pong, 128-byte k stages); "
+                          "12 launches per layer, achieved = layer FLOP / summed launch time; "
+                          "traffic = mean HBM bytes per launch",
                 "avg_launch_ms": round(t_ms / len(gemms), 4),
                 "flop_per_launch": int(flops / len(gemms))}
     roof_q = None

@@ -8,22 +8,20 @@
 // Wgrad of each weight are separate GEMMs with different aspect ratios;
 // [TE-summary] "主な機能": MXFP8 block scaling.
 //
-// One kernel template serves three operand kinds:
+// Operand kinds:
 //   FP8  per-tensor scaled E4M3/E5M2 (any mix), v_mfma_f32_32x32x64_f8f6f4;
 //        epilogue d = fl32(fl32(acc * sa_inv) * sb_inv) + bias;
 //   MX   E4M3/E5M2 elements with one E8M0 exponent per 32 elements along k,
 //        v_mfma_scale_f32_32x32x64_f8f6f4 (the matrix core applies the scales);
 //   BF16 comparison GEMM, v_mfma_f32_32x32x16_bf16.
 //
-// Tiling: 256 x 256 output tile per workgroup of 4 waves (2 x 2), each wave owns
-// a 128 x 128 block = 4 x 4 MFMA tiles of 32 x 32 (256 fp32 accumulators per
-// lane).  The k loop advances 128 bytes per stage (128 FP8 or 64 BF16 elements);
-// A and B stages (32 KB each) are double-buffered in LDS (128 KB of the 160 KB).
-// Global loads for stage t+1 are issued before the MFMAs of stage t, so their
-// latency hides behind 32 MFMAs per wave.  LDS rows are 128 bytes = 8 chunks
-// of 16 bytes stored at chunk ^ (row & 7), so the 32 rows a wave reads for one
-// fragment hit distinct banks.  Workgroups are remapped so each of the 8 XCDs
-// (own L2) runs a contiguous, row-grouped range of tiles.
+// Two kernels, both with a 256 x 256 output tile per workgroup and an
+// XCD-aware tile order (each of the 8 XCDs, with its own L2, runs a
+// contiguous, row-grouped range of tiles):
+//   k_gemm4  8 waves in two ping-pong groups (see its header): every FP8 and
+//            BF16 GEMM, and MX GEMMs with k a multiple of 128;
+//   k_gemm   4 waves of 128 x 128, two-stage LDS pipeline with register
+//            staging: MX GEMMs whose k is not a multiple of 128.
 
 #include "device_common.hpp"
 #include "internal.hpp"
@@ -71,6 +69,14 @@ using ic = std::integral_constant<int, V>;
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BKB + ((chunk ^ (row & 7)) << 4); }
 
+// ============================================================================
+// Two-stage kernel (MX GEMMs with k not a multiple of 128): 4 waves (2 x 2), each
+// owning a 128 x 128 block = 4 x 4 MFMA tiles of 32 x 32.  The k loop advances
+// 128 bytes per stage; A and B stages (32 KB each) are double-buffered in LDS,
+// rows of 8 chunks of 16 bytes stored at chunk ^ (row & 7).  Global loads for
+// stage t+1 go through registers while the MFMAs of stage t run.  Scale dwords
+// of a partial last k stage are assembled per byte.
+// ============================================================================
 template <int KIND, int AF, int BF>
 __global__ __launch_bounds__(NT, 1) void k_gemm(Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * kTileBytes];
@@ -312,324 +318,24 @@ __device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
   return r;
 }
 
-constexpr int SK = 64;  // k bytes per MFMA stage
 constexpr uint32_t kOOB = 0x80000000u;
 
 // s_waitcnt immediate, gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4], lgkmcnt [11:8] = 0
 constexpr int wait_vm_lgkm0(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4); }
 
 // ============================================================================
-// Pair pipeline: stage pairs loaded as full 128-byte lines.
-//
-// The k loop still computes 64-byte stages (16 FP8 MFMAs of 32x32x64 per wave),
-// but global data arrives two stages at a time: a 128-byte slice of each of the
-// tile's 256 A rows and 256 B rows (64 KB), so every load request is a whole
-// cache line.  LDS holds two such pair slots (A at [0, 64K), B at [64K, 128K),
-// 32 KB each), rows of 8 chunks of 16 bytes stored at chunk ^ f(row),
-// f(r) = (r & 7) ^ ((r >> 3) & 3), which keeps the 8- and 16-lane groups of a
-// fragment read (one logical chunk, consecutive rows) on distinct banks.  One
-// barrier per pair publishes pair p+1 and frees pair p's slot; pair p+2 is then
-// loaded into it while pair p+1 is consumed (two steps of latency budget).
+// LDS layout of a 128-byte k stage: a 128-byte slice of each of the tile's 256 A
+// rows and 256 B rows (64 KB), loaded as whole cache lines.  Two stage slots: A
+// at [0, 64K), B at [64K, 128K), 32 KB each; rows of 8 chunks of 16 bytes stored
+// at chunk ^ f(row), f(r) = (r & 7) ^ ((r >> 3) & 3), which keeps the 8- and
+// 16-lane groups of a fragment read (one logical chunk, consecutive rows) on
+// distinct banks.
 // ============================================================================
-constexpr int PK = 128;                  // k bytes per pair slot row
-constexpr int kPairOp = BM * PK;         // 32 KB: one operand, one pair
-constexpr int kPB = 2 * kPairOp;         // B pair slots start at 64 KB
+constexpr int PK = 128;                  // k bytes per stage row
+constexpr int kPairOp = BM * PK;         // 32 KB: one operand, one stage
+constexpr int kPB = 2 * kPairOp;         // B stage slots start at 64 KB
 
 __device__ __forceinline__ int f8(int row) { return (row & 7) ^ ((row >> 3) & 3); }
-
-template <int KIND, int AF, int BF>
-__global__ __launch_bounds__(NT, 1) void k_gemm3(Params p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kPB];
-
-  const int nb = p.nbm * p.nbn;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, idx = bid >> 3;
-  const int per = nb >> 3, rem = nb & 7;
-  const int lin = xcd * per + (xcd < rem ? xcd : rem) + idx;
-  const int gspan = kGroupM * p.nbn;
-  const int group = lin / gspan;
-  const int first_m = group * kGroupM;
-  const int gsz = (p.nbm - first_m) < kGroupM ? (p.nbm - first_m) : kGroupM;
-  const int in_g = lin - group * gspan;
-  const int tm = first_m + in_g % gsz;
-  const int tn = in_g / gsz;
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
-  const int lr = lane & 31, lk = lane >> 5;
-
-  const int rows_a = (p.M - m0) < BM ? (p.M - m0) : BM;
-  const int rows_b = (p.N - n0) < BN ? (p.N - n0) : BN;
-  const v4i rsA = make_rsrc(p.a + static_cast<int64_t>(m0) * p.KB, static_cast<uint32_t>(rows_a) * p.KB);
-  const v4i rsB = make_rsrc(p.b + static_cast<int64_t>(n0) * p.KB, static_cast<uint32_t>(rows_b) * p.KB);
-
-  // load mapping: wave w moves rows [64w, 64w + 64) of A and of B, 8 rows per instruction
-  // (lane j: row 8q + j/8, physical chunk j % 8, logical chunk (j % 8) ^ f(row))
-  uint32_t ld_off[8];
-  int ld_cb[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int row = wave * 64 + q * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ f8(row);
-    ld_cb[q] = c * 16;
-    ld_off[q] = static_cast<uint32_t>(row) * static_cast<uint32_t>(p.KB) + c * 16;
-  }
-  auto issue_pair = [&](auto SLOT, int pr) {
-    constexpr int slot = decltype(SLOT)::value;
-    const uint32_t kb = static_cast<uint32_t>(pr) * PK;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint32_t off = (kb + ld_cb[q] < static_cast<uint32_t>(p.KB)) ? ld_off[q] + kb : kOOB;
-      const int base = slot * kPairOp + (wave * 64 + q * 8) * PK;
-      raw_buffer_load_lds(rsA, (__attribute__((address_space(3))) uint32_t*)(smem + base), 16,
-                          static_cast<int>(off), 0, 0, 0);
-      raw_buffer_load_lds(rsB, (__attribute__((address_space(3))) uint32_t*)(smem + kPB + base), 16,
-                          static_cast<int>(off), 0, 0, 0);
-    }
-  };
-
-  // fragment reads: row = wm + 32 i + lr has f(row) = f(lr); stage half h uses logical
-  // chunks 4h + lk (low 16 bytes) and 4h + 2 + lk (high 16 bytes)
-  const int fk = f8(lr);
-  int ra[2][2], rb[2][2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    ra[h][0] = (wm + lr) * PK + (((4 * h + lk) ^ fk) << 4);
-    ra[h][1] = (wm + lr) * PK + (((4 * h + 2 + lk) ^ fk) << 4);
-    rb[h][0] = kPB + (wn + lr) * PK + (((4 * h + lk) ^ fk) << 4);
-    rb[h][1] = kPB + (wn + lr) * PK + (((4 * h + 2 + lk) ^ fk) << 4);
-  }
-  v8i fa[2][4], fb[2][4];
-  auto read_frags = [&](auto SLOT, auto HALF, auto SET) {
-    constexpr int slot = decltype(SLOT)::value;
-    constexpr int h = decltype(HALF)::value;
-    constexpr int set = decltype(SET)::value;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int o = slot * kPairOp + i * 32 * PK;
-      const v4u lo = *reinterpret_cast<const v4u*>(smem + ra[h][0] + o);
-      const v4u hi = *reinterpret_cast<const v4u*>(smem + ra[h][1] + o);
-      fa[set][i] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      const v4u lo2 = *reinterpret_cast<const v4u*>(smem + rb[h][0] + o);
-      const v4u hi2 = *reinterpret_cast<const v4u*>(smem + rb[h][1] + o);
-      fb[set][i] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo2, hi2, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-  };
-
-  v16f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{0};
-
-  // part 0 = fragment row 0, part 1 = rows 1-3 (BF16: two 32x32x16 half-steps per row)
-  auto mfma_part = [&](auto SET, auto PART) {
-    constexpr int set = decltype(SET)::value;
-    constexpr int i0 = decltype(PART)::value == 0 ? 0 : 1;
-    constexpr int i1 = decltype(PART)::value == 0 ? 1 : 4;
-#pragma unroll
-    for (int i = i0; i < i1; ++i) {
-      if constexpr (KIND == KIND_BF16) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const v8i a = fa[set][i], b = fb[set][j];
-            const v8bf av = __builtin_bit_cast(v8bf, hh ? __builtin_shufflevector(a, a, 4, 5, 6, 7)
-                                                        : __builtin_shufflevector(a, a, 0, 1, 2, 3));
-            const v8bf bv = __builtin_bit_cast(v8bf, hh ? __builtin_shufflevector(b, b, 4, 5, 6, 7)
-                                                        : __builtin_shufflevector(b, b, 0, 1, 2, 3));
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i][j], 0, 0, 0);
-          }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[set][i], fb[set][j], acc[i][j],
-                                                                     AF, BF, 0, 0, 0, 0);
-      }
-    }
-  };
-
-  const int KT = p.KT;             // 64-byte stages
-  const int NP = (KT + 1) >> 1;    // pairs
-  constexpr int LPP = 16;          // loads per thread per pair
-
-  // Step kt computes stage kt (register set kt & 1) and reads stage kt+1's fragments.
-  // Even kt: stage kt+1 is the other half of the same pair slot, already published.
-  // Odd kt: stage kt+1 opens pair (kt+1)/2: wait for it, barrier (which also retires
-  // the slot of pair (kt-1)/2, whose last reads happened in step kt-1), then issue
-  // pair (kt+1)/2 + 1 into that slot.
-  auto step = [&](auto SLOTH, int kt, auto STEADY) {
-    constexpr int SH = decltype(SLOTH)::value;  // kt % 4
-    constexpr int set = SH & 1;
-    constexpr int slot = SH >> 1;               // pair slot of stage kt
-    constexpr bool steady = decltype(STEADY)::value;
-    constexpr bool odd = (SH & 1) != 0;
-    mfma_part(ic<set>{}, ic<0>{});
-    if constexpr (odd) {
-      if (steady || kt + 1 < KT) {
-        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-        __builtin_amdgcn_s_barrier();
-        if (steady || (kt + 1) / 2 + 1 < NP) issue_pair(ic<slot>{}, (kt + 1) / 2 + 1);
-        read_frags(ic<slot ^ 1>{}, ic<0>{}, ic<set ^ 1>{});
-      }
-    } else {
-      if (steady || kt + 1 < KT) read_frags(ic<slot>{}, ic<1>{}, ic<set ^ 1>{});
-    }
-    mfma_part(ic<set>{}, ic<1>{});
-    if constexpr (steady) {
-      if constexpr (KIND == KIND_BF16) {
-        // 24 MFMAs of 32 cycles
-        if constexpr (odd) {
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          }
-        } else {
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-        }
-      } else {
-        // 12 MFMAs of 64 cycles
-        if constexpr (odd) {
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // 2 VMEM (to LDS)
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
-          }
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          }
-        } else {
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          }
-        }
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // prologue: pairs 0 and 1 in flight, pair 0 published, stage 0 read
-  issue_pair(ic<0>{}, 0);
-  if (NP > 1) issue_pair(ic<1>{}, 1);
-  if (NP > 1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(LPP));
-  else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-  __builtin_amdgcn_s_barrier();
-  read_frags(ic<0>{}, ic<0>{}, ic<0>{});
-
-  int kt = 0;
-  for (; kt + 7 < KT; kt += 4) {  // every step of the four has all of its work
-    step(ic<0>{}, kt, std::true_type{});
-    step(ic<1>{}, kt + 1, std::true_type{});
-    step(ic<2>{}, kt + 2, std::true_type{});
-    step(ic<3>{}, kt + 3, std::true_type{});
-  }
-  for (; kt + 3 < KT; kt += 4) {
-    step(ic<0>{}, kt, std::false_type{});
-    step(ic<1>{}, kt + 1, std::false_type{});
-    step(ic<2>{}, kt + 2, std::false_type{});
-    step(ic<3>{}, kt + 3, std::false_type{});
-  }
-  if (kt < KT) step(ic<0>{}, kt, std::false_type{});
-  if (kt + 1 < KT) step(ic<1>{}, kt + 1, std::false_type{});
-  if (kt + 2 < KT) step(ic<2>{}, kt + 2, std::false_type{});
-
-  // ---- epilogue: scale, bias, round; staged through LDS for full-row 16-byte stores ----
-  // Each wave owns a 128 x 128 block; it is written out in two passes of 64 rows.
-  // Pass: the wave's fp32 values go to its own LDS region (64 rows x 128 floats; a
-  // half-wave writes 32 consecutive floats of one row), then each lane reads 8 (bf16
-  // out) or 4 (fp32 out) consecutive floats of a row and stores 16 bytes.
-  float sa = 1.0f, sb = 1.0f;
-  if constexpr (KIND == KIND_FP8) {
-    sa = *static_cast<const float*>(p.a_scale);
-    sb = *static_cast<const float*>(p.b_scale);
-  }
-  float bias_v[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int col = n0 + wn + j * 32 + lr;
-    bias_v[j] = 0.0f;
-    if (p.bias != nullptr && col < p.N)
-      bias_v[j] = p.bias_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p.bias)[col]) << 16)
-                              : static_cast<const float*>(p.bias)[col];
-  }
-  constexpr int kEpPitch = 512;                  // bytes per staged row
-  constexpr int kEpRegion = 64 * kEpPitch;       // 32 KB per wave
-  static_assert(4 * kEpRegion <= 2 * kPB, "epilogue staging must fit in the pair slots");
-  float* ep = reinterpret_cast<float*>(smem + wave * kEpRegion);
-  __syncthreads();  // every wave is done with the operand ring
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      const int i = pass * 2 + ii;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float val = acc[i][j][v];
-          if constexpr (KIND == KIND_FP8) val = __fmul_rn(__fmul_rn(val, sa), sb);
-          if (p.bias != nullptr) val = __fadd_rn(val, bias_v[j]);
-          const int r = ii * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
-          ep[r * (kEpPitch / 4) + j * 32 + lr] = val;
-        }
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
-    __builtin_amdgcn_wave_barrier();
-    const int row0 = m0 + wm + pass * 64;
-    const int col0 = n0 + wn;
-    if (p.d_bf16) {
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int r = t * 4 + (lane >> 4);
-        const int c = (lane & 15) * 8;
-        const float4 lo = *reinterpret_cast<const float4*>(ep + r * (kEpPitch / 4) + c);
-        const float4 hi = *reinterpret_cast<const float4*>(ep + r * (kEpPitch / 4) + c + 4);
-        const int grow = row0 + r, gcol = col0 + c;
-        if (grow < p.M && gcol < p.N) {
-          uint4 o;
-          o.x = f32_to_bf16_bits(lo.x) | (f32_to_bf16_bits(lo.y) << 16);
-          o.y = f32_to_bf16_bits(lo.z) | (f32_to_bf16_bits(lo.w) << 16);
-          o.z = f32_to_bf16_bits(hi.x) | (f32_to_bf16_bits(hi.y) << 16);
-          o.w = f32_to_bf16_bits(hi.z) | (f32_to_bf16_bits(hi.w) << 16);
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol) = o;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < 32; ++t) {
-        const int r = t * 2 + (lane >> 5);
-        const int c = (lane & 31) * 4;
-        const float4 v4 = *reinterpret_cast<const float4*>(ep + r * (kEpPitch / 4) + c);
-        const int grow = row0 + r, gcol = col0 + c;
-        if (grow < p.M && gcol < p.N)
-          *reinterpret_cast<float4*>(static_cast<float*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol) = v4;
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
-    __builtin_amdgcn_wave_barrier();
-  }
-}
 
 // ============================================================================
 // Ping-pong pipeline: 8 waves, two per SIMD, in two groups of four.
@@ -993,7 +699,6 @@ hipError_t run(Params p, hipStream_t s, const char* name) {
     // two-stage kernel fills it per byte
     hipLaunchKernelGGL((k_gemm<KIND_MX, AF, BF>), dim3(nb), dim3(NT), 0, s, p);
   } else {
-    p.KT = (p.KB + SK - 1) / SK;
     hipLaunchKernelGGL((k_gemm4<KIND, AF, BF>), dim3(nb), dim3(NT8), 0, s, p);
   }
   return hipGetLastError();

@@ -17,7 +17,8 @@
  *   - Pointers are DEVICE pointers unless marked (host).  The caller allocates
  *     and owns every buffer, including the scaling state.  The library keeps no
  *     pointer after a call returns, allocates nothing and holds no global state
- *     besides a per-thread error string and a per-device architecture check.
+ *     besides a per-thread error string, a per-device architecture check and a
+ *     per-device cache of kernel occupancies (the quantizers' grid sizes).
  *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
  *     default stream).  There is no host synchronization inside.  Scale, amax
  *     and history values never leave the device.

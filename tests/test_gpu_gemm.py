@@ -166,6 +166,40 @@ def test_mx_gemm_unit_scales_equal_per_tensor_exactly():
     np.testing.assert_array_equal(host(d3), O.gemm_mx(a, ea2, O.E4M3, b, eb, O.E4M3, out="f32"))
 
 
+@pytest.mark.parametrize("mnk", [(1024, 768, 768), (512, 512, 4096)], ids=str)
+@pytest.mark.parametrize("fa", ["E4M3", "E5M2"])
+@pytest.mark.parametrize("odt", ["bf16", "f32"])
+def test_fp8_gemm_error_is_the_matrix_core_arithmetic(mnk, fa, odt):
+    """Cross-check of where the element-wise gap to the oracle comes from: the vendor
+    library's FP8 GEMM (torch._scaled_mm on hipBLASLt) on the same codes and scales runs
+    on the same matrix-core instruction and lands on this library's result up to fp32
+    summation order (f32 out) or one bf16 rounding step (bf16 out), while both differ
+    from the oracle's exact sums by the truncating 8-product groups."""
+    if not hasattr(torch, "_scaled_mm"):
+        pytest.skip("torch._scaled_mm is not available")
+    m, n, k = mnk
+    sd = _seed(mnk, fa, odt, "lib")
+    a, sa = _quantized((m, k), fa, (17, sd, 0, 0), "act" if fa == "E4M3" else "grad")
+    b, sb = _quantized((n, k), "E4M3", (17, sd, 1, 0))
+    td = {"E4M3": torch.float8_e4m3fn, "E5M2": torch.float8_e5m2}
+    odt_t = torch.bfloat16 if odt == "bf16" else torch.float32
+    d = _out(m, n, odt)
+    B.te_fp8_gemm(dev_u8(a), fa, scalar(float(sa)), dev_u8(b), "E4M3", scalar(float(sb)), d)
+    lib = torch._scaled_mm(dev_u8(a).view(td[fa]), dev_u8(b).view(td["E4M3"]).t(), scale_a=scalar(float(sa))[0],
+                           scale_b=scalar(float(sb))[0], out_dtype=odt_t)
+    ours, theirs = host(d).astype(np.float64), host(lib).astype(np.float64)
+    ref = O.gemm_per_tensor(a, FMTS[fa], sa, b, O.E4M3, sb, out=odt)
+    scale = float(np.abs(ref).max())
+    if odt == "f32":
+        assert np.abs(ours - theirs).max() <= 1e-5 * scale
+    else:
+        gap = np.abs(ours - theirs)
+        assert np.all(gap <= 2.0 ** -7 * np.maximum(np.abs(ours), np.abs(theirs)) + 1e-5 * scale)
+    # both sit equally far from the oracle (max relative error, denominator floored at 1e-3 max|r|)
+    e_ours, e_lib = O.rel_err(ours, ref), O.rel_err(theirs, ref)
+    assert abs(e_ours - e_lib) <= 0.1 * max(e_ours, e_lib) + 1e-4, (e_ours, e_lib)
+
+
 def test_gemm_empty_and_bad_shape_raise():
     d = torch.empty((0, 16), dtype=torch.bfloat16, device=DEV)
     a = torch.empty((0, 32), dtype=torch.uint8, device=DEV)
