@@ -366,9 +366,15 @@ constexpr int NT8 = 512;
 template <int KIND, int AF, int BF>
 __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
   constexpr bool MX = KIND == KIND_MX;
-  // MX: per stage slot, one dword of four E8M0 block scales per row of A (1 KB) and of B (1 KB)
+  // FP8/BF16 (SPLIT): A in two stage slots, B in three, and the two groups share the
+  // loads (group 0 A, group 1 B, in their own memory phases).  MX: two slots each, all
+  // loads from group 0, plus per stage slot one dword of four E8M0 block scales per
+  // row of A (1 KB) and of B (1 KB).
+  constexpr bool SPLIT = !MX;
   constexpr int kScOff = 2 * kPB, kScSlot = 2048;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kPB + (MX ? 2 * kScSlot : 0)];
+  constexpr int kLds = SPLIT ? kPB + 3 * kPairOp : 2 * kPB + 2 * kScSlot;
+  static_assert(kLds <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
 
   const int nb = p.nbm * p.nbn;
   const int bid = blockIdx.x;
@@ -396,7 +402,7 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
   const v4i rsA = make_rsrc(p.a + static_cast<int64_t>(m0) * p.KB, static_cast<uint32_t>(rows_a) * p.KB);
   const v4i rsB = make_rsrc(p.b + static_cast<int64_t>(n0) * p.KB, static_cast<uint32_t>(rows_b) * p.KB);
 
-  // global->LDS (group 0): wave q4 moves rows [64 q4, 64 q4 + 64) of A and of B, 8 rows
+  // global->LDS: wave q4 moves rows [64 q4, 64 q4 + 64) of A and/or of B, 8 rows
   // per instruction t (lane j: row 64 q4 + 8t + j/8, physical chunk j % 8, logical chunk
   // (j % 8) ^ f(row) = c0 ^ (t & 3) with c0 = (j % 8) ^ (j / 8))
   const int c0 = (lane & 7) ^ (lane >> 3);
@@ -435,6 +441,22 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
     }
   };
   constexpr int kLoadsPerStage = MX ? 18 : 16;
+  // SPLIT: one operand of one stage (8 loads per lane), into the slot at byte offset off
+  auto issue_op = [&](const v4i& rs, int off_slot, int st) {
+    const uint32_t kb = static_cast<uint32_t>(st) * PK;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t cb = static_cast<uint32_t>((c0 ^ (t & 3)) << 4);
+      const uint32_t off = (kb + cb < static_cast<uint32_t>(p.KB))
+                               ? ld_base + static_cast<uint32_t>(t * 8) * static_cast<uint32_t>(p.KB) + kb + cb
+                               : kOOB;
+      const int base = off_slot + (q4 * 64 + t * 8) * PK;
+      raw_buffer_load_lds(rs, (__attribute__((address_space(3))) uint32_t*)(smem + base), 16,
+                          static_cast<int>(off), 0, 0, 0);
+    }
+  };
+  auto issue_a = [&](auto SLOT, int st) { issue_op(rsA, decltype(SLOT)::value * kPairOp, st); };
+  auto issue_b = [&](int st) { issue_op(rsB, kPB + (st % 3) * kPairOp, st); };
 
   // A phase covers NH of the stage's two 64-byte k steps: both for FP8 and BF16; one
   // for MX, whose scaled MFMA needs a fresh accumulator tuple per instruction and so
@@ -454,10 +476,11 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
   // 2h + lk of its row for k step h; two row groups share a dword: byte 2h + g holds
   // row group 2p + g (A: dwords p = 0, 1; B: one dword for its two row groups).
   uint32_t sa2[2] = {0u, 0u}, sb1 = 0u;
-  // read the fragments of part P (k steps P*NH ..) of the stage in SLOT
-  auto read_part = [&](auto SLOT, auto PART) {
+  // read the fragments of part P (k steps P*NH ..) of stage st, whose A is in SLOT
+  auto read_part = [&](auto SLOT, auto PART, int st) {
     constexpr int slot = decltype(SLOT)::value;
     constexpr int part = decltype(PART)::value;
+    const int boff = (SPLIT ? st % 3 : slot) * kPairOp;
     if constexpr (MX) {
       if constexpr (part == 0) {
         const uint32_t* sc = reinterpret_cast<const uint32_t*>(smem + kScOff + slot * kScSlot);
@@ -483,9 +506,9 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int o = slot * kPairOp + j * 32 * PK;
-        const v4u lo = *reinterpret_cast<const v4u*>(smem + blo + o);
-        const v4u hi = *reinterpret_cast<const v4u*>(smem + bhi + o);
+        const int o = j * 32 * PK;
+        const v4u lo = *reinterpret_cast<const v4u*>(smem + (blo + boff) + o);
+        const v4u hi = *reinterpret_cast<const v4u*>(smem + (bhi + boff) + o);
         fb[hh][j] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
@@ -552,7 +575,19 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
   // group 0's).  Group 0 alone waits for and issues the global->LDS loads: at the end
   // of a stage's last part it waits for the next stage, and after the barrier it loads
   // the stage after that into the slot both groups have finished reading.
-  if (grp == 0) {
+  if constexpr (SPLIT) {
+    // group 0 loads A of stages 0 and 1, group 1 B of stages 0, 1 and (after the
+    // prologue) 2; each waits for its stage-0 half before the first barrier
+    if (grp == 0) {
+      issue_a(ic<0>{}, 0);
+      if (S > 1) issue_a(ic<1>{}, 1);
+    } else {
+      issue_b(0);
+      if (S > 1) issue_b(1);
+    }
+    if (S > 1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(8));
+    else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+  } else if (grp == 0) {
     issue_stage(ic<0>{}, 0);
     if (S > 1) {
       issue_stage(ic<1>{}, 1);
@@ -562,13 +597,23 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
     }
   }
   __builtin_amdgcn_s_barrier();  // stage 0 visible
-  read_part(ic<0>{}, ic<0>{});
+  read_part(ic<0>{}, ic<0>{}, 0);
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
   __builtin_amdgcn_s_barrier();
-  if (grp == 1) __builtin_amdgcn_s_barrier();
+  if (grp == 1) {
+    if constexpr (SPLIT) {
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));  // B of stage 1 landed
+      if (S > 2) issue_b(2);                         // its slot has never been used
+    }
+    __builtin_amdgcn_s_barrier();
+  }
   __builtin_amdgcn_sched_barrier(0);
 
-  // phase u = PPS * s + part; U = u mod 2 PPS fixes slot and part at compile time
+  // phase u = PPS * s + part; U = u mod 2 PPS fixes slot and part at compile time.
+  // Group 0 at the end of a stage's last part waits for its loads of stage s+1 (A, or
+  // everything without SPLIT) and after the barrier loads stage s+2 into the slot both
+  // groups have finished reading.  Group 1 (SPLIT) in its memory phase after stage s
+  // waits for B of stage s+2 and loads B of stage s+3 into the slot of stage s.
   auto iter = [&](auto U, int u) {
     constexpr int uu = decltype(U)::value;
     constexpr int slot = (uu / PPS) & 1, part = uu % PPS;
@@ -588,8 +633,16 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
     if (last_part && grp == 0 && s + 1 < S) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));  // stage s+1 landed
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    if (u + 1 < T) read_part(ic<nslot>{}, ic<npart>{});
-    if (last_part && grp == 0 && s + 2 < S) issue_stage(ic<slot>{}, s + 2);  // the slot of stage s is free
+    if (u + 1 < T) read_part(ic<nslot>{}, ic<npart>{}, last_part ? s + 1 : s);
+    if constexpr (SPLIT) {
+      if (last_part && grp == 0 && s + 2 < S) issue_a(ic<slot>{}, s + 2);  // the A slot of stage s is free
+      if (last_part && grp == 1) {
+        if (s + 2 < S) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));  // B of stage s+2 landed
+        if (s + 3 < S) issue_b(s + 3);                                // into the B slot of stage s
+      }
+    } else {
+      if (last_part && grp == 0 && s + 2 < S) issue_stage(ic<slot>{}, s + 2);  // the slot of stage s is free
+    }
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
