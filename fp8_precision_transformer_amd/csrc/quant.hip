@@ -308,27 +308,26 @@ __global__ __launch_bounds__(kThreads) void k_cast_transpose(
   };
   // FAST: one 16-byte load per pass; otherwise element loads with bounds checks
   // (outside the matrix reads as 0), packed into the same raw words.
-  auto load = [&](uint4* raw, int64_t r0, int64_t c0, bool) {
+  auto load1 = [&](int p, int64_t r0, int64_t c0) {
     if constexpr (FAST) {
       const uint8_t* base = reinterpret_cast<const uint8_t*>(x + r0 * C + c0);
-#pragma unroll
-      for (int p = 0; p < NP; ++p) raw[p] = *reinterpret_cast<const uint4*>(base + ld_off + p * ld_pass);
+      return *reinterpret_cast<const uint4*>(base + ld_off + p * ld_pass);
     } else {
+      const int64_t r = r0 + p * RPP + prow;
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const int64_t r = r0 + p * RPP + prow;
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int j = 0; j < E; ++j) {
-          const int64_t c = c0 + pcol + j;
-          const uint32_t b = (r < R && c < C) ? raw_bits<T>(x + r * C + c) : 0u;
-          w[(j * kBits) / 32] |= b << ((j * kBits) % 32);
-        }
-        raw[p] = make_uint4(w[0], w[1], w[2], w[3]);
+      for (int j = 0; j < E; ++j) {
+        const int64_t c = c0 + pcol + j;
+        const uint32_t b = (r < R && c < C) ? raw_bits<T>(x + r * C + c) : 0u;
+        w[(j * kBits) / 32] |= b << ((j * kBits) % 32);
       }
+      return make_uint4(w[0], w[1], w[2], w[3]);
     }
   };
-  auto process = [&](const uint4* raw, int64_t r0, int64_t c0, bool) {
+  // The tile's registers are reloaded with the next tile as soon as they are consumed:
+  // pass by pass without the transposed copy, after all passes with it (the transposed
+  // stores then run with the next tile's loads in flight).
+  auto process = [&](uint4 (&raw)[NP], int64_t r0, int64_t c0, bool has1, int64_t r1, int64_t c1) {
     __syncthreads();  // the previous tile's LDS reads are done
     uint8_t* orow = out_row + r0 * C + c0;
 #pragma unroll
@@ -355,8 +354,13 @@ __global__ __launch_bounds__(kThreads) void k_cast_transpose(
             if (c0 + pcol + j < C) o[j] = static_cast<uint8_t>(q[j >> 2] >> (8 * (j & 3)));
         }
       }
+      if (has1 && out_col == nullptr) raw[p] = load1(p, r1, c1);
     }
     if (out_col == nullptr) return;
+    if (has1) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) raw[p] = load1(p, r1, c1);
+    }
     __syncthreads();
     uint32_t d[16];
 #pragma unroll
@@ -397,26 +401,21 @@ __global__ __launch_bounds__(kThreads) void k_cast_transpose(
 
   int64_t i = blockIdx.x;
   if (i < ntiles) {
-    uint4 cur[NP], nxt[NP];
+    uint4 raw[NP];
     int64_t r0, c0;
-    bool fast = origin(i, r0, c0);
-    load(cur, r0, c0, fast);
+    origin(i, r0, c0);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) raw[p] = load1(p, r0, c0);
     for (;;) {
-      const int64_t inext = i + gridDim.x;
+      const int64_t i1 = i + gridDim.x;
+      const bool has1 = i1 < ntiles;
       int64_t r1 = 0, c1 = 0;
-      bool fast1 = false;
-      if (inext < ntiles) {
-        fast1 = origin(inext, r1, c1);
-        load(nxt, r1, c1, fast1);
-      }
-      process(cur, r0, c0, fast);
-      if (inext >= ntiles) break;
-      i = inext;
+      if (has1) origin(i1, r1, c1);
+      process(raw, r0, c0, has1, r1, c1);
+      if (!has1) break;
+      i = i1;
       r0 = r1;
       c0 = c1;
-      fast = fast1;
-#pragma unroll
-      for (int p = 0; p < NP; ++p) cur[p] = nxt[p];
     }
   }
   if constexpr (MODE == 0) block_amax_atomic(absmax_value<T>(m), amax);
@@ -465,10 +464,10 @@ __device__ __forceinline__ int mx_exponent(float am) {
 
 template <bool E5M2>
 __device__ __forceinline__ void mx_block32(const float* v, uint32_t* q, uint8_t* code) {
-  float am = 0.0f;
+  uint32_t mb = 0u;  // block amax as magnitude bits: a NaN wins, as in a plain max
 #pragma unroll
-  for (int j = 0; j < 32; ++j) am = __builtin_fmaxf(am, __builtin_fabsf(v[j]));
-  const int e = mx_exponent<E5M2>(am);
+  for (int j = 0; j < 32; ++j) mb = max(mb, __float_as_uint(v[j]) & 0x7fffffffu);
+  const int e = mx_exponent<E5M2>(__uint_as_float(mb));
   *code = static_cast<uint8_t>(e + 127);
 #pragma unroll
   for (int j = 0; j < 8; ++j)
@@ -546,6 +545,162 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8(const T* __restrict__ x, int
       }
       scale_col[c * (R / 32) + rb / 32] = code;
     }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// MXFP8, bf16 input, whole 128 x 128 tiles (rows and cols multiples of 128):
+// persistent blocks, the next tile's loads in flight, as the cast-transpose.
+// Row-wise: a 32-element block of a row is 4 lanes x 8 elements; its amax is a
+// bit-pattern max reduced over the 4 lanes, and lane 16g writes the row's four
+// E8M0 codes of the tile as one dword.  Column-wise: the raw bf16 tile goes
+// through LDS (pitch 272 bytes); thread t quantizes columns 2(t%64), 2(t%64)+1
+// over rows 32(t/64) .. +31 (one block each), reading one dword per row; the
+// codes are staged back through the same LDS so that out_col goes out as whole
+// 128-byte lines and scale_col as one dword of four block codes per column.
+// ----------------------------------------------------------------------------
+constexpr int kMxTPitch = 272;  // LDS bytes per tile row (128 bf16 + 16)
+constexpr int kMxQPitch = 144;  // LDS bytes per staged output row (128 codes + 16)
+static_assert(kCT * kMxQPitch + 4 * kCT <= kCT * kMxTPitch, "column staging reuses the tile");
+
+template <bool E5M2>
+__device__ __forceinline__ void mx_quant8(const uint4& raw, int e, uint32_t& q0, uint32_t& q1) {
+  float v[8];
+  unpack16<uint16_t>(raw, v);
+  float w[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w[j] = saturate<E5M2>(__builtin_ldexpf(v[j], -e));
+  q0 = cvt4<E5M2>(w[0], w[1], w[2], w[3]);
+  q1 = cvt4<E5M2>(w[4], w[5], w[6], w[7]);
+}
+
+template <bool E5M2, bool ROW, bool COL>
+__global__ __launch_bounds__(kThreads) void k_mxfp8_tiles(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                          uint8_t* __restrict__ out_row,
+                                                          uint8_t* __restrict__ scale_row,
+                                                          uint8_t* __restrict__ out_col,
+                                                          uint8_t* __restrict__ scale_col) {
+  constexpr int NP = 8, RPP = 16;  // passes of 16 rows, 16 lanes x 8 elements per row
+  __shared__ __attribute__((aligned(16))) uint8_t tile[COL ? kCT * kMxTPitch : 16];
+  const int64_t ntc = C / kCT;
+  const int64_t ntiles = ntc * (R / kCT);
+  const int t = threadIdx.x, lane = t & 63;
+  const int prow = t >> 4, pcol = (t & 15) * 8;
+  const uint32_t ld_off = static_cast<uint32_t>((prow * C + pcol) * 2);
+  const uint32_t ld_pass = static_cast<uint32_t>(RPP * C * 2);
+  auto origin = [&](int64_t i, int64_t& r0, int64_t& c0) {
+    r0 = (i / ntc) * kCT;
+    c0 = (i % ntc) * kCT;
+  };
+  // one 16-byte load of pass p of the tile at (r0, c0)
+  auto load1 = [&](int p, int64_t r0, int64_t c0) {
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(x + r0 * C + c0);
+    return *reinterpret_cast<const uint4*>(base + ld_off + p * ld_pass);
+  };
+  // The tile's registers are reloaded with the next tile as soon as they are consumed:
+  // pass by pass without the column copy, after all passes with it (the column work
+  // then runs with the next tile's loads in flight).
+  auto process = [&](uint4 (&raw)[NP], int64_t r0, int64_t c0, bool has1, int64_t r1, int64_t c1) {
+    if constexpr (COL) __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int lr = p * RPP + prow;
+      if constexpr (COL) *reinterpret_cast<uint4*>(tile + lr * kMxTPitch + pcol * 2) = raw[p];
+      if constexpr (ROW) {
+        uint32_t m = absmax_bits<uint16_t>(0u, raw[p]);
+        m = max(m & 0xffffu, m >> 16);
+        m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 1, 64)));
+        m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 2, 64)));
+        const int e = mx_exponent<E5M2>(__uint_as_float(m << 16));
+        uint32_t q0, q1;
+        mx_quant8<E5M2>(raw[p], e, q0, q1);
+        const int64_t r = r0 + lr;
+        *reinterpret_cast<uint2*>(out_row + r * C + c0 + pcol) = make_uint2(q0, q1);
+        const uint32_t code = static_cast<uint32_t>(e + 127);
+        const uint32_t k1 = static_cast<uint32_t>(__shfl(static_cast<int>(code), lane + 4, 64));
+        const uint32_t k2 = static_cast<uint32_t>(__shfl(static_cast<int>(code), lane + 8, 64));
+        const uint32_t k3 = static_cast<uint32_t>(__shfl(static_cast<int>(code), lane + 12, 64));
+        if ((lane & 15) == 0)
+          *reinterpret_cast<uint32_t*>(scale_row + r * (C / 32) + c0 / 32) = code | (k1 << 8) | (k2 << 16) | (k3 << 24);
+      }
+      if constexpr (!COL) {
+        if (has1) raw[p] = load1(p, r1, c1);
+      }
+    }
+    if constexpr (COL) {
+      if (has1) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) raw[p] = load1(p, r1, c1);
+      }
+    }
+    if constexpr (COL) {
+      __syncthreads();
+      const int cp = t & 63, blk = t >> 6;
+      uint32_t d[32];
+#pragma unroll
+      for (int k = 0; k < 32; ++k) d[k] = *reinterpret_cast<const uint32_t*>(tile + (32 * blk + k) * kMxTPitch + 4 * cp);
+      uint32_t mm = 0u;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) mm = absmax_bits<uint16_t>(mm, make_uint4(d[k], 0u, 0u, 0u));
+      uint32_t q[2][8];
+      int e[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {  // h = 0: column 2cp (low halves), 1: column 2cp + 1
+        const uint32_t m = h ? (mm >> 16) : (mm & 0xffffu);
+        e[h] = mx_exponent<E5M2>(__uint_as_float(m << 16));
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          float w[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t b = h ? (d[4 * g + j] & 0xffff0000u) : (d[4 * g + j] << 16);
+            w[j] = saturate<E5M2>(__builtin_ldexpf(__uint_as_float(b), -e[h]));
+          }
+          q[h][g] = cvt4<E5M2>(w[0], w[1], w[2], w[3]);
+        }
+      }
+      // Stage the transposed bytes (Q[col][row], pitch 144) and the codes (one dword
+      // of four blocks per column) in the tile's LDS, then write whole 128-byte lines
+      // of out_col and one code dword per column.
+      __syncthreads();  // every thread has read its column pair
+      uint8_t* qt = tile;
+      uint8_t* qs = tile + kCT * kMxQPitch;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint4* dst = reinterpret_cast<uint4*>(qt + (2 * cp + h) * kMxQPitch + 32 * blk);
+        dst[0] = make_uint4(q[h][0], q[h][1], q[h][2], q[h][3]);
+        dst[1] = make_uint4(q[h][4], q[h][5], q[h][6], q[h][7]);
+        qs[(2 * cp + h) * 4 + blk] = static_cast<uint8_t>(e[h] + 127);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int c = (t >> 3) + 32 * k, chunk = t & 7;
+        const uint4 v = *reinterpret_cast<const uint4*>(qt + c * kMxQPitch + 16 * chunk);
+        *reinterpret_cast<uint4*>(out_col + (c0 + c) * R + r0 + 16 * chunk) = v;
+      }
+      if (t < kCT)
+        *reinterpret_cast<uint32_t*>(scale_col + (c0 + t) * (R / 32) + r0 / 32) =
+            *reinterpret_cast<const uint32_t*>(qs + 4 * t);
+    }
+  };
+  int64_t i = blockIdx.x;
+  if (i >= ntiles) return;
+  uint4 raw[NP];
+  int64_t r0, c0;
+  origin(i, r0, c0);
+#pragma unroll
+  for (int p = 0; p < NP; ++p) raw[p] = load1(p, r0, c0);
+  for (;;) {
+    const int64_t i1 = i + gridDim.x;
+    const bool has1 = i1 < ntiles;
+    int64_t r1 = 0, c1 = 0;
+    if (has1) origin(i1, r1, c1);
+    process(raw, r0, c0, has1, r1, c1);
+    if (!has1) break;
+    i = i1;
+    r0 = r1;
+    c0 = c1;
   }
 }
 
@@ -643,10 +798,31 @@ hipError_t cast_transpose_t(const T* x, int64_t R, int64_t C, int current, int m
   return hipGetLastError();
 }
 
+template <bool E5M2, bool ROW, bool COL>
+void mx_tiles_launch(const uint16_t* x, int64_t R, int64_t C, uint8_t* out_row, uint8_t* scale_row,
+                     uint8_t* out_col, uint8_t* scale_col, hipStream_t st) {
+  const auto fn = k_mxfp8_tiles<E5M2, ROW, COL>;
+  const int g = persistent_grid(reinterpret_cast<const void*>(fn), (R / kCT) * (C / kCT), 1);
+  hipLaunchKernelGGL(fn, dim3(g), dim3(kThreads), 0, st, x, R, C, out_row, scale_row, out_col, scale_col);
+}
+
 template <typename T, bool E5M2>
 hipError_t mxfp8_t(const T* x, int64_t R, int64_t C, uint8_t* out_row, uint8_t* scale_row,
                    uint8_t* out_col, uint8_t* scale_col, hipStream_t st) {
   if (R == 0 || C == 0) return hipSuccess;
+  // bf16 matrices of whole 128 x 128 tiles take the persistent tile kernel (32-bit
+  // offsets inside a tile; the row-wise codes go out as dwords)
+  if constexpr (sizeof(T) == 2) {
+    const bool row = out_row != nullptr, col = out_col != nullptr;
+    if (R % kCT == 0 && C % kCT == 0 && C * kCT * 2 < (int64_t{1} << 31) && R * kCT < (int64_t{1} << 31) &&
+        (!row || (reinterpret_cast<uintptr_t>(scale_row) & 3u) == 0) &&
+        (!col || (reinterpret_cast<uintptr_t>(scale_col) & 3u) == 0)) {
+      if (row && col) mx_tiles_launch<E5M2, true, true>(x, R, C, out_row, scale_row, out_col, scale_col, st);
+      else if (row) mx_tiles_launch<E5M2, true, false>(x, R, C, out_row, scale_row, out_col, scale_col, st);
+      else mx_tiles_launch<E5M2, false, true>(x, R, C, out_row, scale_row, out_col, scale_col, st);
+      return hipGetLastError();
+    }
+  }
   const dim3 grid(static_cast<unsigned>((C + kTC - 1) / kTC), static_cast<unsigned>((R + kTR - 1) / kTR));
   hipLaunchKernelGGL((k_mxfp8<T, E5M2>), grid, dim3(kThreads), 0, st, x, R, C, out_row, scale_row,
                      out_col, scale_col);

@@ -187,11 +187,23 @@ def cast(args):
         o2 = torch.empty((C, R), dtype=torch.uint8, device=dev)
         fn = lambda: B.te_cast_transpose(x, "E4M3", mode, 0, scale, si, am, o1, o2)  # noqa: E731
         nbytes = R * C * (6 if mode == B.TE_SCALE_CURRENT else 4)
-    else:  # mx
+    elif args.op == "mx":  # row-wise copy
         o1 = torch.empty((R, C), dtype=torch.uint8, device=dev)
         s1 = torch.empty((R, C // 32), dtype=torch.uint8, device=dev)
         fn = lambda: B.te_mxfp8_quantize(x, "E4M3", o1, s1)  # noqa: E731
         nbytes = R * C * 3 + R * C // 32
+    elif args.op == "mxcol":  # column-wise copy
+        o2 = torch.empty((C, R), dtype=torch.uint8, device=dev)
+        s2 = torch.empty((C, R // 32), dtype=torch.uint8, device=dev)
+        fn = lambda: B.te_mxfp8_quantize(x, "E4M3", None, None, o2, s2)  # noqa: E731
+        nbytes = R * C * 3 + R * C // 32
+    else:  # mxboth
+        o1 = torch.empty((R, C), dtype=torch.uint8, device=dev)
+        s1 = torch.empty((R, C // 32), dtype=torch.uint8, device=dev)
+        o2 = torch.empty((C, R), dtype=torch.uint8, device=dev)
+        s2 = torch.empty((C, R // 32), dtype=torch.uint8, device=dev)
+        fn = lambda: B.te_mxfp8_quantize(x, "E4M3", o1, s1, o2, s2)  # noqa: E731
+        nbytes = R * C * 4 + 2 * (R * C // 32)
     ms = _time(fn, args.iters, args.warmup)
     print(json.dumps({"kernel": f"{args.op}_{args.mode}", "rows": R, "cols": C, "ms": round(ms, 5),
                       "gbs": round(nbytes / ms / 1e6, 1)}), flush=True)
@@ -233,7 +245,7 @@ def main():
     c = sub.add_parser("cast")
     c.add_argument("--rows", type=int, default=15872)
     c.add_argument("--cols", type=int, default=16384)
-    c.add_argument("--op", choices=["cast", "transpose", "both", "mx"], default="cast")
+    c.add_argument("--op", choices=["cast", "transpose", "both", "mx", "mxcol", "mxboth"], default="cast")
     c.add_argument("--mode", choices=["delayed", "current"], default="delayed")
     c.add_argument("--iters", type=int, default=20)
     c.add_argument("--warmup", type=int, default=3)

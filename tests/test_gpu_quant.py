@@ -263,6 +263,53 @@ def test_mxfp8_parity(shape, xdt, fmt):
     np.testing.assert_array_equal(host(out_col), q_c)
 
 
+@pytest.mark.parametrize("shape", [(256, 384), (4608, 4096)], ids=str)
+@pytest.mark.parametrize("which", ["row", "col", "both"])
+def test_mxfp8_whole_tiles(shape, which):
+    """bf16 matrices of whole 128 x 128 tiles go through the persistent tile kernel
+    (4608 x 4096 has more tiles than resident blocks); E4M3 and one copy or both."""
+    R, C = shape
+    x32 = synth.activations(shape, 9, R + C, 4, 0)
+    x32[:2, :32] = 0.0
+    xd, xh = input_pair(x32, "bf16")
+    orow = torch.empty((R, C), dtype=torch.uint8, device=DEV) if which != "col" else None
+    srow = torch.empty((R, C // 32), dtype=torch.uint8, device=DEV) if which != "col" else None
+    ocol = torch.empty((C, R), dtype=torch.uint8, device=DEV) if which != "row" else None
+    scol = torch.empty((C, R // 32), dtype=torch.uint8, device=DEV) if which != "row" else None
+    B.te_mxfp8_quantize(xd, "E4M3", orow, srow, ocol, scol)
+    if orow is not None:
+        q, e = O.mxfp8_quantize(xh, O.E4M3)
+        np.testing.assert_array_equal(host(srow), e)
+        np.testing.assert_array_equal(host(orow), q)
+    if ocol is not None:
+        q, e = O.mxfp8_quantize(np.ascontiguousarray(xh.T), O.E4M3)
+        np.testing.assert_array_equal(host(scol), e)
+        np.testing.assert_array_equal(host(ocol), q)
+
+
+@pytest.mark.parametrize("shape", [(128, 128), (96, 160)], ids=str)
+def test_mxfp8_nan_block(shape):
+    """A NaN in a block makes its amax NaN, as the oracle's plain max does: shared
+    exponent 0 (code 127), the other elements cast at scale 1 (the NaN stays a NaN)."""
+    R, C = shape
+    x32 = synth.activations(shape, 9, 3, 5, 0) * np.float32(1000.0)
+    x32[5, 40] = np.nan
+    x32[70 % R, 3] = np.nan
+    xd, xh = input_pair(x32, "bf16")
+    orow = torch.empty((R, C), dtype=torch.uint8, device=DEV)
+    srow = torch.empty((R, C // 32), dtype=torch.uint8, device=DEV)
+    ocol = torch.empty((C, R), dtype=torch.uint8, device=DEV)
+    scol = torch.empty((C, R // 32), dtype=torch.uint8, device=DEV)
+    B.te_mxfp8_quantize(xd, "E4M3", orow, srow, ocol, scol)
+    q, e = O.mxfp8_quantize(xh, O.E4M3)
+    assert e[5, 1] == 127
+    np.testing.assert_array_equal(host(srow), e)
+    assert nan_aware_equal(host(orow), q, O.decode_table(O.E4M3))[0] == 0
+    q, e = O.mxfp8_quantize(np.ascontiguousarray(xh.T), O.E4M3)
+    np.testing.assert_array_equal(host(scol), e)
+    assert nan_aware_equal(host(ocol), q, O.decode_table(O.E4M3))[0] == 0
+
+
 def test_mxfp8_row_only_and_col_only():
     x32 = synth.activations((64, 96), 9, 1, 3, 0)
     xd, xh = input_pair(x32, "bf16")
