@@ -45,8 +45,8 @@ MI355X_HBM_GBS = 8000.0           # HBM3E (published)
 MEASURED_TRAFFIC = {
     # FP8 GEMM: mean over the layer's 12 GEMM launches (microbench layer --kind fp8)
     "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                 "sha256": "ee0c545daa6102feabf3211d7cc2d281aeed4e35f4cb7775dbcfa8f39554a71e",
-                 "bytes_per_launch": 1677534397},
+                 "sha256": "ee14512ec2ec146d9e2fde01cb830996477d8fa4060c0512a91b19ca76906d3a",
+                 "bytes_per_launch": 1531924241},
 }
 
 
@@ -68,7 +68,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--modes", default="all")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=640, help="sampled output rows per GEMM for the oracle")
+    p.add_argument("--cpu-rows", type=int, default=2304, help="sampled output rows per GEMM for the oracle")
     return p.parse_args()
 
 

@@ -68,25 +68,4 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Block max (blockDim.x threads, multiple of 64) of non-negative floats folded
-// into *dst with an integer atomic max on the float bits.  Every step compares
-// bit patterns, which order as the values do for non-negative floats and put a
-// NaN above +inf, so a NaN anywhere wins as in a plain max.  Order-independent,
-// hence deterministic.
-__device__ __forceinline__ void block_amax_atomic(float v, float* dst) {
-  __shared__ uint32_t red[16];
-  uint32_t b = __float_as_uint(v);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) b = max(b, static_cast<uint32_t>(__shfl_xor(static_cast<int>(b), off, 64)));
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  if (lane == 0) red[wid] = b;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t m = red[0];
-    const int nw = blockDim.x >> 6;
-    for (int i = 1; i < nw; ++i) m = max(m, red[i]);
-    atomicMax(reinterpret_cast<unsigned int*>(dst), m);
-  }
-}
-
 }  // namespace te

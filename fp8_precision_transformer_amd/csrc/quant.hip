@@ -10,6 +10,7 @@
 // for current scaling, whose amax must exist before the first cast) and written
 // once per output layout.  Loads and stores are 16 bytes per lane.
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <type_traits>
@@ -62,11 +63,96 @@ struct In<float> {
 };
 
 // ----------------------------------------------------------------------------
-// prologue: zero amax; for delayed scaling also publish scale_inv = 1/scale
+// empty input: amax = 0; for delayed scaling also publish scale_inv = 1/scale
 // ----------------------------------------------------------------------------
 __global__ void k_prologue(float* amax, const float* scale, float* scale_inv, int delayed) {
   *amax = 0.0f;
   if (delayed) *scale_inv = 1.0f / *scale;
+}
+
+// ----------------------------------------------------------------------------
+// Grid-wide amax in the quantizing launch itself.  One atomic per block on the
+// amax word would queue every block's update on one address at the end of the
+// launch (several microseconds for a couple of thousand blocks), and the word
+// would need a zeroing launch first.  Instead block b folds its maximum
+// (magnitude bits; NaN, whose bits are largest, wins) into the max word of group
+// b % kAmaxGroups and then arrives at that group's counter; the last arrival of
+// a group folds the group max into the top max word and arrives at the top
+// counter, and the last arrival there -- the last block of the grid -- writes
+// *amax (the max with the value already there when `acc` is set, for a second
+// launch over the same tensor).  Every word is cleared by the read that consumes
+// it, ready for the next launch.  At most 64 blocks queue on one address.
+//
+// Ordering: every access to the workspace is a device-scope atomic read-modify-
+// write, performed where all of them are, and each arrival is issued only after
+// the preceding max has returned, i.e. has been performed; so when a counter
+// reaches its count, every max folded before those arrivals is already in the
+// max word.  No release fence is needed, which matters: a device-scope release
+// writes back the whole L2 of the XCD, and one per block costs more than the
+// contended atomics it replaces.  The workspace belongs to one stream (launches
+// on one stream run one after another).
+// ----------------------------------------------------------------------------
+constexpr int kAmaxGroups = 32;
+constexpr int kAmaxLine = 64;          // words per 256-byte line: [0] max bits, [1] arrivals
+constexpr int kAmaxMaxBlocks = 4096;   // persistent grids are capped below this
+
+struct AmaxWork {
+  uint32_t grp[kAmaxGroups * kAmaxLine];
+  uint32_t top[kAmaxLine];
+};
+
+// flags of the quantizing kernels
+constexpr int kAccAmax = 1;     // *amax = max(*amax, amax of this launch)
+constexpr int kPublishInv = 2;  // block 0 writes scale_inv = 1 / scale (delayed scaling)
+
+__device__ __forceinline__ uint32_t rmw_max(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t rmw_add(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t rmw_take(uint32_t* p) {  // read and clear
+  return __hip_atomic_exchange(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// wait until the returned value of an atomic is here (it has been performed);
+// the memory clobber keeps later accesses from being moved above
+__device__ __forceinline__ void performed(uint32_t v) {
+  asm volatile("s_waitcnt vmcnt(0)" : : "v"(v) : "memory");
+}
+
+// Every block of the grid calls this exactly once, with all kThreads threads.
+__device__ __forceinline__ void grid_amax(float v, float* amax, AmaxWork* w, bool acc) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t b = __float_as_uint(v);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) b = max(b, static_cast<uint32_t>(__shfl_xor(static_cast<int>(b), off, 64)));
+  if (lane == 0) red[wid] = b;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  uint32_t mb = red[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) mb = max(mb, red[i]);
+  const int G = static_cast<int>(gridDim.x), blk = static_cast<int>(blockIdx.x);
+  const int g = blk % kAmaxGroups;
+  const uint32_t members = static_cast<uint32_t>((G - 1 - g) / kAmaxGroups + 1);
+  const uint32_t groups = static_cast<uint32_t>(min(G, kAmaxGroups));
+  uint32_t* gw = w->grp + g * kAmaxLine;
+  performed(rmw_max(gw, mb));
+  if (rmw_add(gw + 1, 1u) != members - 1) return;
+  const uint32_t gm = rmw_take(gw);
+  performed(rmw_take(gw + 1));
+  performed(rmw_max(w->top, gm));
+  if (rmw_add(w->top + 1, 1u) != groups - 1) return;
+  uint32_t r = rmw_take(w->top);
+  performed(rmw_take(w->top + 1));
+  if (acc) r = max(r, __float_as_uint(*amax));
+  *amax = __uint_as_float(r);
+}
+
+__global__ void k_zero_words(uint32_t* p, int n) {
+  const int i = static_cast<int>(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < n) p[i] = 0u;
 }
 
 // Finalize current scaling without a cast: scale and scale_inv from amax.
@@ -148,11 +234,15 @@ __global__ __launch_bounds__(kThreads) void k_amax_cast(const T* __restrict__ x,
                                                         float* __restrict__ scale,
                                                         float* __restrict__ scale_inv,
                                                         float* __restrict__ amax,
-                                                        uint8_t* __restrict__ out, int margin) {
+                                                        uint8_t* __restrict__ out, int margin,
+                                                        AmaxWork* __restrict__ work, int flags) {
   constexpr bool kAmax = MODE != 2;
   constexpr bool kCast = MODE != 1;
   float s = 1.0f;
   if constexpr (MODE == 0) s = *scale;
+  if constexpr (MODE != 2) {
+    if ((flags & kPublishInv) && blockIdx.x == 0 && threadIdx.x == 0) *scale_inv = 1.0f / *scale;
+  }
   if constexpr (MODE == 2) {
     s = scale_from_amax(*amax, Fp8Traits<E5M2>::max, margin, 1.0f);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -213,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void k_amax_cast(const T* __restrict__ x,
       }
     }
   }
-  if constexpr (kAmax) block_amax_atomic(absmax_value<T>(m), amax);
+  if constexpr (kAmax) grid_amax(absmax_value<T>(m), amax, work, (flags & kAccAmax) != 0);
 }
 
 // ----------------------------------------------------------------------------
@@ -258,14 +348,17 @@ template <typename T, bool E5M2, int MODE, bool FAST>
 __global__ __launch_bounds__(kThreads) void k_cast_transpose(
     const T* __restrict__ x, int64_t R, int64_t C, float* __restrict__ scale,
     float* __restrict__ scale_inv, float* __restrict__ amax, uint8_t* __restrict__ out_row,
-    uint8_t* __restrict__ out_col, int margin) {
+    uint8_t* __restrict__ out_col, int margin, AmaxWork* __restrict__ work, int flags) {
   using M = CTMap<T>;
   constexpr int E = M::E, NP = M::NP, RPP = M::RPP;
   constexpr int kBits = 8 * static_cast<int>(sizeof(T));
   __shared__ uint32_t lds[kCT * kCTPitch / 4];
 
   float s = 1.0f;
-  if constexpr (MODE == 0) s = *scale;
+  if constexpr (MODE == 0) {
+    s = *scale;
+    if ((flags & kPublishInv) && blockIdx.x == 0 && threadIdx.x == 0) *scale_inv = 1.0f / s;
+  }
   if constexpr (MODE == 2) {
     s = scale_from_amax(*amax, Fp8Traits<E5M2>::max, margin, 1.0f);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -418,7 +511,7 @@ __global__ __launch_bounds__(kThreads) void k_cast_transpose(
       c0 = c1;
     }
   }
-  if constexpr (MODE == 0) block_amax_atomic(absmax_value<T>(m), amax);
+  if constexpr (MODE == 0) grid_amax(absmax_value<T>(m), amax, work, (flags & kAccAmax) != 0);
 }
 
 // ----------------------------------------------------------------------------
@@ -704,15 +797,13 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_tiles(const uint16_t* __rest
   }
 }
 
-// Blocks of `kernel` (kThreads threads) resident at once on the current device,
-// capped at kMaxBlocksPerCU per compute unit; cached per kernel and device.
-constexpr int kMaxBlocksPerCU = 8;
-
-int resident_blocks(const void* kernel) {
+// Blocks of `kernel` (kThreads threads) that fit at once on one compute unit, and the
+// compute units of the current device; cached per kernel and device.
+std::pair<int, int> occupancy(const void* kernel) {
   static std::mutex mu;
-  static std::map<std::pair<const void*, int>, int> cache;
+  static std::map<std::pair<const void*, int>, std::pair<int, int>> cache;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipGetDevice(&dev) != hipSuccess) return {1, 256};
   std::lock_guard<std::mutex> lock(mu);
   const auto key = std::make_pair(kernel, dev);
   auto it = cache.find(key);
@@ -720,41 +811,77 @@ int resident_blocks(const void* kernel) {
   int per_cu = 1, cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess || per_cu < 1)
     per_cu = 1;
-  if (per_cu > kMaxBlocksPerCU) per_cu = kMaxBlocksPerCU;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-  const int g = per_cu * cus;
-  cache.emplace(key, g);
-  return g;
+  const auto v = std::make_pair(per_cu, cus);
+  cache.emplace(key, v);
+  return v;
 }
 
-// Persistent grid: one block per `per_block` work units, at most one full wave of resident blocks.
-int persistent_grid(const void* kernel, int64_t units, int64_t per_block) {
+// Persistent grid: one block per `per_block` work units, at most max_per_cu resident
+// blocks per compute unit.
+int persistent_grid(const void* kernel, int64_t units, int64_t per_block, int max_per_cu) {
   int64_t g = (units + per_block - 1) / per_block;
-  const int64_t cap = resident_blocks(kernel);
+  const auto oc = occupancy(kernel);
+  const int64_t cap = std::min<int64_t>(static_cast<int64_t>(std::min(oc.first, max_per_cu)) * oc.second,
+                                       kAmaxMaxBlocks);
   if (g > cap) g = cap;
   if (g < 1) g = 1;
   return static_cast<int>(g);
 }
 
+// Resident blocks per compute unit for each persistent kernel, measured on the
+// 5B-layer tensors: two blocks (eight waves) per CU stream best for the flat cast,
+// the cast-transpose and the row-wise MX copy; the column-wise MX copy, which
+// spends more time per tile in LDS, prefers a full CU.
+constexpr int kCapFlat = 2;
+constexpr int kCapCT = 2;
+constexpr int kCapMxRow = 2;
+constexpr int kCapMxCol = 8;
+
+// The grid-amax workspace of (current device, stream), allocated and zeroed (by a
+// kernel on that stream) at the first quantizing call on the stream, kept until
+// the process ends.
+AmaxWork* amax_work(hipStream_t st) {
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, AmaxWork*> ws;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(dev, st);
+  auto it = ws.find(key);
+  if (it != ws.end()) return it->second;
+  void* p = nullptr;
+  if (hipMalloc(&p, sizeof(AmaxWork)) != hipSuccess) return nullptr;
+  constexpr int nw = static_cast<int>(sizeof(AmaxWork) / 4);
+  hipLaunchKernelGGL(k_zero_words, dim3((nw + 255) / 256), dim3(256), 0, st, static_cast<uint32_t*>(p), nw);
+  if (hipGetLastError() != hipSuccess) {
+    (void)hipFree(p);
+    return nullptr;
+  }
+  ws.emplace(key, static_cast<AmaxWork*>(p));
+  return static_cast<AmaxWork*>(p);
+}
+
 template <typename T, bool E5M2, int MODE>
 void launch_flat(const T* x, int64_t n, int margin, float* scale, float* scale_inv, float* amax,
-                 uint8_t* out, hipStream_t st) {
+                 uint8_t* out, AmaxWork* work, int flags, hipStream_t st) {
   const auto fn = k_amax_cast<T, E5M2, MODE>;
-  const int g = persistent_grid(reinterpret_cast<const void*>(fn), n >> 4, kThreads);
-  hipLaunchKernelGGL(fn, dim3(g), dim3(kThreads), 0, st, x, n, scale, scale_inv, amax, out, margin);
+  const int g = persistent_grid(reinterpret_cast<const void*>(fn), n >> 4, kThreads, kCapFlat);
+  hipLaunchKernelGGL(fn, dim3(g), dim3(kThreads), 0, st, x, n, scale, scale_inv, amax, out, margin, work, flags);
 }
 
 template <typename T, bool E5M2>
 hipError_t amax_cast_t(const T* x, int64_t n, int current, int margin, float* scale,
                        float* scale_inv, float* amax, uint8_t* out, hipStream_t st) {
-  hipLaunchKernelGGL(k_prologue, dim3(1), dim3(1), 0, st, amax, scale, scale_inv, current ? 0 : 1);
+  AmaxWork* w = amax_work(st);
+  if (w == nullptr) return hipErrorOutOfMemory;
   if (!current) {
-    if (out) launch_flat<T, E5M2, 0>(x, n, margin, scale, scale_inv, amax, out, st);
-    else launch_flat<T, E5M2, 1>(x, n, margin, scale, scale_inv, amax, out, st);
+    if (out) launch_flat<T, E5M2, 0>(x, n, margin, scale, scale_inv, amax, out, w, kPublishInv, st);
+    else launch_flat<T, E5M2, 1>(x, n, margin, scale, scale_inv, amax, out, w, kPublishInv, st);
   } else {
-    launch_flat<T, E5M2, 1>(x, n, margin, scale, scale_inv, amax, out, st);
+    launch_flat<T, E5M2, 1>(x, n, margin, scale, scale_inv, amax, out, w, 0, st);
     if (out)
-      launch_flat<T, E5M2, 2>(x, n, margin, scale, scale_inv, amax, out, st);
+      launch_flat<T, E5M2, 2>(x, n, margin, scale, scale_inv, amax, out, w, 0, st);
     else
       hipLaunchKernelGGL(k_current_scale, dim3(1), dim3(1), 0, st, amax, scale, scale_inv,
                          Fp8Traits<E5M2>::max, margin);
@@ -764,20 +891,20 @@ hipError_t amax_cast_t(const T* x, int64_t n, int current, int margin, float* sc
 
 template <typename T, bool E5M2, int MODE>
 void ct_launch(const T* x, int64_t R, int64_t C, int margin, float* scale, float* scale_inv,
-               float* amax, uint8_t* out_row, uint8_t* out_col, hipStream_t st) {
+               float* amax, uint8_t* out_row, uint8_t* out_col, AmaxWork* work, int flags, hipStream_t st) {
   const int64_t whole = ct_vec_ok<T>(R, C) ? (R / kCT) * (C / kCT) : 0;
   const int64_t ragged = ((R + kCT - 1) / kCT) * ((C + kCT - 1) / kCT) - whole;
   if (whole > 0) {
     const auto fn = k_cast_transpose<T, E5M2, MODE, true>;
-    const int g = persistent_grid(reinterpret_cast<const void*>(fn), whole, 1);
+    const int g = persistent_grid(reinterpret_cast<const void*>(fn), whole, 1, kCapCT);
     hipLaunchKernelGGL(fn, dim3(g), dim3(kThreads), 0, st, x, R, C, scale, scale_inv, amax, out_row,
-                       out_col, margin);
+                       out_col, margin, work, flags);
   }
-  if (ragged > 0) {
+  if (ragged > 0) {  // the edge tiles' amax joins the whole tiles'
     const auto fn = k_cast_transpose<T, E5M2, MODE, false>;
-    const int g = persistent_grid(reinterpret_cast<const void*>(fn), ragged, 1);
+    const int g = persistent_grid(reinterpret_cast<const void*>(fn), ragged, 1, kCapCT);
     hipLaunchKernelGGL(fn, dim3(g), dim3(kThreads), 0, st, x, R, C, scale, scale_inv, amax, out_row,
-                       out_col, margin);
+                       out_col, margin, work, whole > 0 ? flags | kAccAmax : flags);
   }
 }
 
@@ -785,16 +912,21 @@ template <typename T, bool E5M2>
 hipError_t cast_transpose_t(const T* x, int64_t R, int64_t C, int current, int margin,
                             float* scale, float* scale_inv, float* amax, uint8_t* out_row,
                             uint8_t* out_col, hipStream_t st) {
-  hipLaunchKernelGGL(k_prologue, dim3(1), dim3(1), 0, st, amax, scale, scale_inv, current ? 0 : 1);
   if (R == 0 || C == 0) {
+    hipLaunchKernelGGL(k_prologue, dim3(1), dim3(1), 0, st, amax, scale, scale_inv, current ? 0 : 1);
     if (current)
       hipLaunchKernelGGL(k_current_scale, dim3(1), dim3(1), 0, st, amax, scale, scale_inv,
                          Fp8Traits<E5M2>::max, margin);
     return hipGetLastError();
   }
-  if (current) launch_flat<T, E5M2, 1>(x, R * C, margin, scale, scale_inv, amax, nullptr, st);
-  if (current) ct_launch<T, E5M2, 2>(x, R, C, margin, scale, scale_inv, amax, out_row, out_col, st);
-  else ct_launch<T, E5M2, 0>(x, R, C, margin, scale, scale_inv, amax, out_row, out_col, st);
+  AmaxWork* w = amax_work(st);
+  if (w == nullptr) return hipErrorOutOfMemory;
+  if (current) {
+    launch_flat<T, E5M2, 1>(x, R * C, margin, scale, scale_inv, amax, nullptr, w, 0, st);
+    ct_launch<T, E5M2, 2>(x, R, C, margin, scale, scale_inv, amax, out_row, out_col, w, 0, st);
+  } else {
+    ct_launch<T, E5M2, 0>(x, R, C, margin, scale, scale_inv, amax, out_row, out_col, w, kPublishInv, st);
+  }
   return hipGetLastError();
 }
 
@@ -802,7 +934,7 @@ template <bool E5M2, bool ROW, bool COL>
 void mx_tiles_launch(const uint16_t* x, int64_t R, int64_t C, uint8_t* out_row, uint8_t* scale_row,
                      uint8_t* out_col, uint8_t* scale_col, hipStream_t st) {
   const auto fn = k_mxfp8_tiles<E5M2, ROW, COL>;
-  const int g = persistent_grid(reinterpret_cast<const void*>(fn), (R / kCT) * (C / kCT), 1);
+  const int g = persistent_grid(reinterpret_cast<const void*>(fn), (R / kCT) * (C / kCT), 1, COL ? kCapMxCol : kCapMxRow);
   hipLaunchKernelGGL(fn, dim3(g), dim3(kThreads), 0, st, x, R, C, out_row, scale_row, out_col, scale_col);
 }
 

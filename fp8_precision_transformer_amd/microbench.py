@@ -145,13 +145,16 @@ def _peak_lib():
         raise RuntimeError(f"{PEAK_LIB} missing: run __graft_entry__.build()")
     L = ctypes.CDLL(PEAK_LIB)
     L.te_peak_launch.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 3
-    L.te_copy_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    L.te_copy_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    L.te_read_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     return L
 
 
 def copy(args):
     """A plain device copy (k_copy, 16 bytes per lane) of --mib MiB: the known-size
-    reference that HBM byte counters are calibrated against."""
+    reference that HBM byte counters are calibrated against.  With --sweep it also
+    times the copy and a read-only stream (k_read) over several grid sizes: the
+    practical streaming rates a memory-bound kernel on this chip can reach."""
     import ctypes
     L = _peak_lib()
     dev = "cuda:0"
@@ -159,11 +162,17 @@ def copy(args):
     src = torch.ones(n // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    ms = _time(lambda: L.te_copy_launch(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
-                                        n // 16, st), args.iters, args.warmup)
+    ps, pd = ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr())
+    for grid in ([0] + ([1024, 2048, 4096, 8192] if args.sweep else [])):
+        ms = _time(lambda: L.te_copy_launch(ps, pd, n // 16, grid, st), args.iters, args.warmup)
+        print(json.dumps({"kernel": "k_copy", "grid": grid or min(4096, n // 4096), "bytes_read": n,
+                          "bytes_written": n, "ms": round(ms, 5), "gbs": round(2 * n / ms / 1e6, 1)}), flush=True)
     assert torch.equal(src, dst)
-    print(json.dumps({"kernel": "k_copy", "bytes_read": n, "bytes_written": n, "ms": round(ms, 5),
-                      "gbs": round(2 * n / ms / 1e6, 1)}), flush=True)
+    if args.sweep:
+        for grid in (1024, 2048, 4096, 8192):
+            ms = _time(lambda: L.te_read_launch(ps, pd, n // 16, grid, st), args.iters, args.warmup)
+            print(json.dumps({"kernel": "k_read", "grid": grid, "bytes_read": n, "bytes_written": 0,
+                              "ms": round(ms, 5), "gbs": round(n / ms / 1e6, 1)}), flush=True)
 
 
 def cast(args):
@@ -262,6 +271,7 @@ def main():
     cp.add_argument("--mib", type=int, default=1024)
     cp.add_argument("--iters", type=int, default=10)
     cp.add_argument("--warmup", type=int, default=2)
+    cp.add_argument("--sweep", action="store_true", help="also time copy and read-only streams over grid sizes")
     k = sub.add_parser("peak")
     k.add_argument("--iters", type=int, default=4096)
     k.add_argument("--waves-per-cu", type=int, default=1)

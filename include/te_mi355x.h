@@ -16,9 +16,16 @@
  * Conventions shared by every entry point:
  *   - Pointers are DEVICE pointers unless marked (host).  The caller allocates
  *     and owns every buffer, including the scaling state.  The library keeps no
- *     pointer after a call returns, allocates nothing and holds no global state
- *     besides a per-thread error string, a per-device architecture check and a
- *     per-device cache of kernel occupancies (the quantizers' grid sizes).
+ *     pointer to them after a call returns.  Its own state: a per-thread error
+ *     string, a per-device architecture check, a per-device cache of kernel
+ *     occupancies (the quantizers' grid sizes) and, for te_amax_cast and
+ *     te_cast_transpose, one 8448-byte device workspace per (device, stream)
+ *     pair holding the counters of the grid-wide amax reduction.  The first
+ *     such call on a pair allocates it (hipMalloc) and clears it with a kernel
+ *     on that stream; it lives until the process ends.  Make that first call
+ *     outside stream capture.  Calls on one stream run one after another and
+ *     so share the workspace safely; calls on different streams use different
+ *     workspaces.
  *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
  *     default stream).  There is no host synchronization inside.  Scale, amax
  *     and history values never leave the device.
@@ -97,7 +104,8 @@ typedef enum { TE_GRAN_TENSOR = 0, TE_GRAN_MX_BLOCK32 = 1 } te_granularity;
  *   scale_inv  [1] fp32, written = fl32(1 / scale used).
  *   amax       [1] fp32, written = max_i |x_i| (overwritten, not accumulated;
  *              point it at slot 0 of the tensor's amax history for DELAYED).
- *              NaN inputs make amax unspecified.
+ *              A NaN input makes amax NaN (the max is taken over magnitude
+ *              bit patterns, where NaN ranks above +Inf).
  *   out        [rows, cols] uint8 codes, out_i = satRNE(fl32(x_i * scale)).
  *              May be NULL: then only amax (and, for CURRENT, scale/scale_inv)
  *              is produced.

@@ -344,3 +344,40 @@ def test_quantizers_deterministic_and_stream_ordered():
     assert torch.equal(outs[0][1], outs[1][1])
     ref_s = O.current_scale(O.amax(xh), O.E4M3)
     np.testing.assert_array_equal(host(outs[0][0]), O.scaled_cast(xh, ref_s, O.E4M3).T)
+
+
+def test_grid_amax_across_streams_and_grid_sizes():
+    """The grid-wide amax keeps its counters in a workspace per stream and clears them at
+    the end of every launch: back-to-back launches of very different grid sizes (one
+    block up to a full persistent grid), the whole-tile + edge-tile pair of the
+    cast-transpose, and interleaved launches on two streams each give the oracle's amax,
+    bit for bit, and the delayed-scaling scale_inv."""
+    shapes = [(16, 16), (4096, 4096), (1, 7), (15872 // 4, 4096), (272, 392), (3000, 1000), (128, 128)]
+    xs = []
+    for i, shp in enumerate(shapes):
+        x32 = synth.activations(shp, 9, 40 + i, 0, 0)
+        xd, xh = input_pair(x32, "bf16")
+        xs.append((xd, O.amax(xh)))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    results = []
+    for rep in range(3):
+        for i, (xd, _) in enumerate(xs):
+            st = streams[(i + rep) % 2]
+            am, sinv = empty_f32(), empty_f32()
+            am.fill_(-1.0)
+            sinv.fill_(-1.0)
+            s_in = float(2 ** (i - 3))
+            s_t = scalar(s_in)
+            st.wait_stream(torch.cuda.current_stream())  # the fills and inputs above
+            with torch.cuda.stream(st):
+                if (i + rep) % 3 == 0:
+                    B.te_amax_cast(xd, "E4M3", B.TE_SCALE_DELAYED, 0, s_t, sinv, am, None, stream=st)
+                else:
+                    o = torch.empty(xd.shape[::-1], dtype=torch.uint8, device=DEV)
+                    B.te_cast_transpose(xd, "E4M3", B.TE_SCALE_DELAYED, 0, s_t, sinv, am, None, o,
+                                        stream=st)
+            results.append((i, s_in, am, sinv, s_t))
+    torch.cuda.synchronize()
+    for i, s_in, am, sinv, _ in results:
+        assert host(am)[0] == xs[i][1], (i, host(am)[0], xs[i][1])
+        assert host(sinv)[0] == O.scale_inverse(np.float32(s_in)), i
