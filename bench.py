@@ -132,8 +132,12 @@ def main():
         OUT[w.name] = dict(fprop=bf(M, N), dgrad=bf(M, K), wgrad=bf(N, K))
     # scaling state: E4M3 group = X (0..3) and W (4..7); E5M2 group = dY (0..3)
     L = 16
-    hist4, s4, si4 = f32(8, L), torch.ones(8, device=dev), torch.ones(8, device=dev)
-    hist5, s5, si5 = f32(4, L), torch.ones(4, device=dev), torch.ones(4, device=dev)
+
+    def new_delayed_state():
+        return (f32(8, L), torch.ones(8, device=dev), torch.ones(8, device=dev),
+                f32(4, L), torch.ones(4, device=dev), torch.ones(4, device=dev))
+
+    DSTATE = {"fp8_delayed_autocast": new_delayed_state(), "fp8_delayed_shared": new_delayed_state()}
     new_cur = lambda: {w.name: {t: (f32(1), f32(1), f32(1)) for t in ("x", "w", "dy")} for w in weights}  # noqa: E731
     cur = new_cur()
     # BF16 transposed operands (materialised once; the BF16 GEMM is TN)
@@ -152,7 +156,7 @@ def main():
     MXB = mx_buffers()
 
     modes_all = ["bf16", "fp8_delayed_autocast", "fp8_current_autocast", "fp8_current_prequant",
-                 "mxfp8_autocast", "mxfp8_prequant"]
+                 "mxfp8_autocast", "mxfp8_prequant", "fp8_delayed_shared", "fp8_current_shared", "mxfp8_shared"]
     modes = modes_all if args.modes == "all" else args.modes.split(",")
     if "bf16" in modes:
         for w in weights:
@@ -161,16 +165,21 @@ def main():
 
     E4, E5, DEL, CUR = "E4M3", "E5M2", B.TE_SCALE_DELAYED, B.TE_SCALE_CURRENT
 
+    def scaling(w, li, mode, dstate=None, cset=None):
+        """(scale, scale_inv, amax) of X, W and dY of one weight: slots of the delayed
+        history, or current-scaling scalars."""
+        if mode == DEL:
+            hist4, s4, si4, hist5, s5, si5 = dstate or DSTATE["fp8_delayed_autocast"]
+            return ((s4[li:li + 1], si4[li:li + 1], hist4[li, 0:1]),
+                    (s4[4 + li:5 + li], si4[4 + li:5 + li], hist4[4 + li, 0:1]),
+                    (s5[li:li + 1], si5[li:li + 1], hist5[li, 0:1]))
+        c = (cset or cur)[w.name]
+        return c["x"], c["w"], c["dy"]
+
     def quant_fp8(w, li, stage, mode, qset=None, cset=None):
         """Quantize the two operands one GEMM needs, from their natural bf16 layout."""
         q = (qset or Q)[w.name]
-        if mode == DEL:
-            sx = (s4[li:li + 1], si4[li:li + 1], hist4[li, 0:1])
-            sw = (s4[4 + li:5 + li], si4[4 + li:5 + li], hist4[4 + li, 0:1])
-            sg = (s5[li:li + 1], si5[li:li + 1], hist5[li, 0:1])
-        else:
-            c = (cset or cur)[w.name]
-            sx, sw, sg = c["x"], c["w"], c["dy"]
+        sx, sw, sg = scaling(w, li, mode, cset=cset)
         if stage == "fprop":
             B.te_amax_cast(X[w.name], E4, mode, 0, *sx, q["x"])
             B.te_amax_cast(W[w.name], E4, mode, 0, *sw, q["w"])
@@ -210,6 +219,36 @@ def main():
                 if mx_pre is not None:
                     prequant_mx[(w.name, stage)] = quant_mx(w, stage, mx_pre)
         torch.cuda.synchronize()
+
+    # Shared quantization (the layer schedule of TE's autocast, where the forward's FP8
+    # copies of X and W are kept for the backward): each of X, W, dY is cast once per
+    # step into both its row copy and its transposed copy, and the three GEMMs reuse them.
+    QS = fp8_buffers() if any(m in modes for m in ("fp8_delayed_shared", "fp8_current_shared")) else None
+    CS = new_cur()
+    MXS = mx_buffers() if "mxfp8_shared" in modes else None
+
+    def quant_fp8_shared(w, li, stage, mode):
+        q = QS[w.name]
+        sx, sw, sg = scaling(w, li, mode, DSTATE["fp8_delayed_shared"], CS)
+        if stage == "fprop":
+            B.te_cast_transpose(X[w.name], E4, mode, 0, *sx, q["x"], q["xT"])
+            B.te_cast_transpose(W[w.name], E4, mode, 0, *sw, q["w"], q["wT"])
+            return (q["x"], E4, sx[1], q["w"], E4, sw[1])
+        if stage == "dgrad":
+            B.te_cast_transpose(DY[w.name], E5, mode, 0, *sg, q["dy"], q["dyT"])
+            return (q["dy"], E5, sg[1], q["wT"], E4, sw[1])
+        return (q["dyT"], E5, sg[1], q["xT"], E4, sx[1])
+
+    def quant_mx_shared(w, stage):
+        b = MXS[w.name]
+        if stage == "fprop":
+            B.te_mxfp8_quantize(X[w.name], E4, b["x"], b["xs"], b["xT"], b["xTs"])
+            B.te_mxfp8_quantize(W[w.name], E4, b["w"], b["ws"], b["wT"], b["wTs"])
+            return (b["x"], b["xs"], b["w"], b["ws"])
+        if stage == "dgrad":
+            B.te_mxfp8_quantize(DY[w.name], E4, b["dy"], b["dys"], b["dyT"], b["dyTs"])
+            return (b["dy"], b["dys"], b["wT"], b["wTs"])
+        return (b["dyT"], b["dyTs"], b["xT"], b["xTs"])
 
     def gemm_fp8(ops, out):
         a, fa, sa, b, fb, sb = ops
@@ -258,9 +297,18 @@ def main():
                 elif mode == "mxfp8_prequant":
                     e1.record()
                     gemm_mx(prequant_mx[(w.name, stage)], out)
+                elif mode in ("fp8_delayed_shared", "fp8_current_shared"):
+                    ops = quant_fp8_shared(w, li, stage, DEL if mode == "fp8_delayed_shared" else CUR)
+                    e1.record()
+                    gemm_fp8(ops, out)
+                elif mode == "mxfp8_shared":
+                    ops = quant_mx_shared(w, stage)
+                    e1.record()
+                    gemm_mx(ops, out)
                 e2.record()
                 rec.append((mode, w.name, stage, e0, e1, e2))
-        if mode == "fp8_delayed_autocast":
+        if mode in DSTATE:
+            hist4, s4, si4, hist5, s5, si5 = DSTATE[mode]
             e0, e2 = Ev(), Ev()
             e0.record()
             B.te_scale_update(hist4, s4, si4, E4, B.TE_AMAX_MAX, 0)
@@ -276,9 +324,10 @@ def main():
         for mode in modes:
             run_mode(mode, rec)
     # delayed scaling reaches steady state after 16 updates; warmup steps count toward it
-    if "fp8_delayed_autocast" in modes:
-        for _ in range(max(0, 17 - args.warmup)):
-            run_mode("fp8_delayed_autocast", [])
+    for m in DSTATE:
+        if m in modes:
+            for _ in range(max(0, 17 - args.warmup)):
+                run_mode(m, [])
     torch.cuda.synchronize()
 
     log(f"timing {args.steps} steps")
@@ -362,6 +411,16 @@ def main():
                   "traffic": None, "algorithmic_bytes_per_layer": qbytes,
                   "kernel": "delayed amax+cast / cast-transpose (24 launches + 2 scale updates per layer)"}
 
+    shared = None
+    if "fp8_delayed_shared" in modes:
+        # each of X, W, dY cast once into row and transposed copies: 2 read + 2 write bytes per element
+        n_sh = sum(M * w.in_features + w.out_features * w.in_features + M * w.out_features for w in weights)
+        sbytes = 4 * n_sh
+        sms = med(quant_ms["fp8_delayed_shared"])
+        shared = {"quant_bytes_per_layer": sbytes, "delayed_quant_ms": round(sms, 4),
+                  "delayed_quant_gbs": round(sbytes / (sms * 1e-3) / 1e9, 1),
+                  "frac_of_8tbs": round(sbytes / (sms * 1e-3) / 1e9 / MI355X_HBM_GBS, 4)}
+
     asym = None
     if gm:
         f = med(per_gemm[gm]["qkv.fprop"])
@@ -396,6 +455,7 @@ def main():
         "per_gemm_ms": per_gemm_out,
         "roofline": roof,
         "roofline_quant": roof_q,
+        "shared_quantization": shared,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
