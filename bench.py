@@ -68,6 +68,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--modes", default="all")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-latency", action="store_true", help="skip the small, launch-bound configurations")
     p.add_argument("--cpu-rows", type=int, default=2304, help="sampled output rows per GEMM for the oracle")
     return p.parse_args()
 
@@ -429,6 +430,10 @@ def main():
 
     per_gemm_out = {m: {k: round(med(v), 4) for k, v in per_gemm[m].items()} for m in modes}
 
+    lat = None
+    if not args.no_latency:
+        lat = latency_configs(log)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, args.cpu_rows, log)
@@ -456,9 +461,36 @@ def main():
         "roofline": roof,
         "roofline_quant": roof_q,
         "shared_quantization": shared,
+        "latency_configs": lat,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def latency_configs(log, iters=50):
+    """The small configurations, bound by launch latency rather than by the kernels:
+    the 768 -> 768 Linear forward step (1024 tokens, delayed scaling) and a BERT-base
+    layer (Fprop, Dgrad, Wgrad of four weights, current scaling, shared quantization),
+    each timed eagerly and replayed from a HIP graph captured once."""
+    import torch
+
+    from fp8_precision_transformer_amd.shapes import BERT_BASE
+    from fp8_precision_transformer_amd.steps import LayerStep, LinearForwardStep, capture, time_step
+
+    out = {}
+    for name, make in (("linear_768_forward_step", lambda st: LinearForwardStep(st)),
+                       ("bert_base_layer_step", lambda st: LayerStep(BERT_BASE, st))):
+        st = torch.cuda.Stream()
+        step = make(st)
+        step.run()  # first call on the stream allocates its amax workspace
+        torch.cuda.synchronize()
+        eager = time_step(step, iters)
+        g = capture(step)
+        graph = time_step(step, iters, graph=g)
+        out[name] = {"eager_us": round(eager, 1), "graph_us": round(graph, 1),
+                     "tflops_graph": round(step.flops / (graph * 1e-6) / 1e12, 1), "gflop": round(step.flops / 1e9, 2)}
+        log(f"{name}: eager {eager:.1f} us, graph {graph:.1f} us")
+    return out
 
 
 def cpu_baseline(cfg, rows, log, cols=1024):
