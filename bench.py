@@ -45,8 +45,8 @@ MI355X_HBM_GBS = 8000.0           # HBM3E (published)
 MEASURED_TRAFFIC = {
     # FP8 GEMM: mean over the layer's 12 GEMM launches (microbench layer --kind fp8)
     "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                 "sha256": "ee14512ec2ec146d9e2fde01cb830996477d8fa4060c0512a91b19ca76906d3a",
-                 "bytes_per_launch": 1531924241},
+                 "sha256": "60cd38c331d109a08cb76713c4ce75bccf8fbc152b94c136acf1829c36b695f4",
+                 "bytes_per_launch": 1516034243},
 }
 
 
@@ -251,6 +251,8 @@ def main():
             return (b["dy"], b["dys"], b["wT"], b["wTs"])
         return (b["dyT"], b["dyTs"], b["xT"], b["xTs"])
 
+    variants = {}  # mode -> kernel variants its GEMMs dispatched (te_gemm_variant)
+
     def gemm_fp8(ops, out):
         a, fa, sa, b, fb, sb = ops
         B.te_fp8_gemm(a, fa, sa, b, fb, sb, out)
@@ -307,6 +309,7 @@ def main():
                     e1.record()
                     gemm_mx(ops, out)
                 e2.record()
+                variants.setdefault(mode, set()).add(B.te_gemm_variant())
                 rec.append((mode, w.name, stage, e0, e1, e2))
         if mode in DSTATE:
             hist4, s4, si4, hist5, s5, si5 = DSTATE[mode]
@@ -348,6 +351,14 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log(f"timed region {wall:.2f}s")
+    # every mode's GEMMs must have run on the matrix-core path of its precision
+    want = {"bf16": "gemm4_bf16_", "mxfp8": "gemm4_mx_", "fp8": "gemm4_fp8_"}
+    for m, vs in variants.items():
+        prefix = next(v for k, v in want.items() if m.startswith(k))
+        bad = [v for v in vs if not v.startswith(prefix)]
+        if bad:
+            print(json.dumps({"error": f"mode {m} dispatched {bad}, expected {prefix}*"}), flush=True)
+            sys.exit(3)
 
     # ---------------- reduce timings ----------------
     per_layer = {m: [] for m in modes}
@@ -462,6 +473,7 @@ def main():
         "roofline_quant": roof_q,
         "shared_quantization": shared,
         "latency_configs": lat,
+        "dispatched_variants": {m: sorted(v) for m, v in variants.items()},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

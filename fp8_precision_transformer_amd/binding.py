@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
             L.te_get_last_error.argtypes = []
             L.te_version.restype = ctypes.c_char_p
             L.te_version.argtypes = []
+            L.te_gemm_variant.restype = ctypes.c_char_p
+            L.te_gemm_variant.argtypes = []
             _lib = L
     return _lib
 
@@ -194,3 +196,8 @@ def te_mxfp8_quantize(x, elem_dtype, out_row=None, scale_row=None, out_col=None,
 
 def version() -> str:
     return lib().te_version().decode()
+
+
+def te_gemm_variant() -> str:
+    """Kernel variant of the last te_fp8_gemm on this thread."""
+    return lib().te_gemm_variant().decode()

@@ -109,6 +109,8 @@ const char* te_get_last_error(void) { return g_err; }
 
 const char* te_version(void) { return "te_mi355x 0.1 (gfx950)"; }
 
+const char* te_gemm_variant(void) { return te::last_gemm_variant(); }
+
 te_status te_amax_cast(const void* x, int x_dtype, int64_t rows, int64_t cols, int out_dtype, int mode,
                        int margin, float* scale, float* scale_inv, float* amax, uint8_t* out,
                        void* stream) {

@@ -750,6 +750,7 @@ hipError_t run(Params p, hipStream_t s, const char* name) {
   if (KIND == KIND_MX && (p.kblocks & 3) != 0) {
     // a k that is not a multiple of 128 leaves a partial scale dword per stage: the
     // two-stage kernel fills it per byte
+    g_last_variant = "gemm_mx_256x256_twostage";
     hipLaunchKernelGGL((k_gemm<KIND_MX, AF, BF>), dim3(nb), dim3(NT), 0, s, p);
   } else {
     hipLaunchKernelGGL((k_gemm4<KIND, AF, BF>), dim3(nb), dim3(NT8), 0, s, p);

@@ -213,6 +213,13 @@ const char* te_get_last_error(void);
 /* Library version string (host, static). */
 const char* te_version(void);
 
+/* Name of the GEMM kernel variant the last te_fp8_gemm call on the calling thread
+ * dispatched (e.g. "gemm4_fp8_e4m3_e4m3_256x256_pingpong"), or "none" before the
+ * first call.  Host pointer to a static string.  Lets a caller check which matrix-core
+ * path ran: [LP-opt] "実モデルにおける結果の解釈" warns that a silent fallback to
+ * another precision shows up only as unchanged performance. */
+const char* te_gemm_variant(void);
+
 #ifdef __cplusplus
 }
 #endif

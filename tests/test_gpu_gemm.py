@@ -236,3 +236,29 @@ def test_fp8_gemm_full_5b_shape_sampled(stage, weight):
     got = host(d)[np.ix_(rows, cols)]
     check_fp8_gemm(got, ref, O.decode_table(FMTS[fa])[a[rows]], O.decode_table(O.E4M3)[b[cols]],
                    (1 / 64) ** 2, "bf16")
+
+
+def test_dispatched_variant_is_the_requested_matrix_core_path():
+    """te_gemm_variant names the kernel that ran: the FP8, MX and BF16 requests each take
+    their own matrix-core path (no silent fallback to another precision), and an MX GEMM
+    whose k is not a multiple of 128 takes the two-stage kernel."""
+    m, n = 256, 256
+    rng = np.random.default_rng(3)
+    for k in (256, 160):
+        a = dev_u8(rng.integers(0, 0x30, (m, k), dtype=np.uint8))
+        b = dev_u8(rng.integers(0, 0x30, (n, k), dtype=np.uint8))
+        ea = dev_u8(np.full((m, k // 32), 127, np.uint8))
+        eb = dev_u8(np.full((n, k // 32), 127, np.uint8))
+        d = _out(m, n, "f32")
+        for fa, fb in (("E4M3", "E4M3"), ("E5M2", "E4M3")):
+            B.te_fp8_gemm(a, fa, scalar(1.0), b, fb, scalar(1.0), d)
+            assert B.te_gemm_variant() == f"gemm4_fp8_{fa.lower()}_{fb.lower()}_256x256_pingpong"
+            B.te_fp8_gemm(a, fa, ea, b, fb, eb, d, gran=B.TE_GRAN_MX_BLOCK32)
+            want = (f"gemm4_mx_{fa.lower()}_{fb.lower()}_256x256_pingpong" if k % 128 == 0
+                    else "gemm_mx_256x256_twostage")
+            assert B.te_gemm_variant() == want
+        xb = torch.zeros((m, k), dtype=torch.bfloat16, device=DEV)
+        wb = torch.zeros((n, k), dtype=torch.bfloat16, device=DEV)
+        B.te_fp8_gemm(xb, "BF16", None, wb, "BF16", None, d)
+        assert B.te_gemm_variant() == "gemm4_bf16_256x256_pingpong"
+    torch.cuda.synchronize()
