@@ -54,8 +54,11 @@ _vp, _i64, _i32, _fp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_v
 _SIGNATURES = {
     "te_amax_cast": [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp],
     "te_cast_transpose": [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp],
+    "te_cast_transpose_dbias": [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
+                                _vp],
     "te_scale_update": [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp],
     "te_fp8_gemm": [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp, _i32, _vp],
+    "te_fp8_gemm_accumulate": [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp, _vp],
     "te_mxfp8_quantize": [_vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp],
 }
 
@@ -80,6 +83,8 @@ def lib() -> ctypes.CDLL:
             L.te_version.argtypes = []
             L.te_gemm_variant.restype = ctypes.c_char_p
             L.te_gemm_variant.argtypes = []
+            L.te_cast_transpose_dbias_workspace_bytes.restype = ctypes.c_int64
+            L.te_cast_transpose_dbias_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
             _lib = L
     return _lib
 
@@ -158,6 +163,24 @@ def te_cast_transpose(x, out_dtype, mode, margin, scale, scale_inv, amax, out_ro
                                    _ptr(out_col), _stream(stream)))
 
 
+def te_cast_transpose_dbias_workspace_bytes(rows, cols) -> int:
+    return int(lib().te_cast_transpose_dbias_workspace_bytes(int(rows), int(cols)))
+
+
+def te_cast_transpose_dbias(x, out_dtype, mode, margin, scale, scale_inv, amax, dbias, workspace,
+                            out_row=None, out_col=None, stream=None):
+    """te_cast_transpose plus dbias[c] = sum_r x[r, c] (fp32) from the same pass; workspace:
+    a device tensor of at least te_cast_transpose_dbias_workspace_bytes(rows, cols) bytes."""
+    for n, t in (("x", x), ("scale", scale), ("scale_inv", scale_inv), ("amax", amax),
+                 ("out_row", out_row), ("out_col", out_col), ("dbias", dbias), ("workspace", workspace)):
+        _need(t, n)
+    rows, cols = _2d(x)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().te_cast_transpose_dbias(_ptr(x), _hp_code(x), rows, cols, _fp8_code(out_dtype), int(mode),
+                                         int(margin), _ptr(scale), _ptr(scale_inv), _ptr(amax), _ptr(out_row),
+                                         _ptr(out_col), _ptr(dbias), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
 def te_scale_update(amax_history, scale, scale_inv, fp8_dtype, algo=TE_AMAX_MAX, margin=0, stream=None):
     for n, t in (("amax_history", amax_history), ("scale", scale), ("scale_inv", scale_inv)):
         _need(t, n, torch.float32)
@@ -166,9 +189,11 @@ def te_scale_update(amax_history, scale, scale_inv, fp8_dtype, algo=TE_AMAX_MAX,
                                  _fp8_code(fp8_dtype), int(algo), int(margin), _stream(stream)))
 
 
-def te_fp8_gemm(a, a_dtype, a_scale, b, b_dtype, b_scale, d, bias=None, gran=TE_GRAN_TENSOR, stream=None):
+def te_fp8_gemm(a, a_dtype, a_scale, b, b_dtype, b_scale, d, bias=None, gran=TE_GRAN_TENSOR, stream=None,
+                accumulate=False):
     """D[m, n] = A[m, k] . B[n, k]^T.  a, b: uint8 FP8 codes (or bf16 tensors with
-    a_dtype = b_dtype = "BF16"); a_scale/b_scale: fp32 [1] scale_inv or uint8 E8M0."""
+    a_dtype = b_dtype = "BF16"); a_scale/b_scale: fp32 [1] scale_inv or uint8 E8M0.
+    accumulate=True (fp32 d only) adds the result into d (te_fp8_gemm_accumulate)."""
     for n, t in (("a", a), ("b", b), ("d", d), ("bias", bias), ("a_scale", a_scale), ("b_scale", b_scale)):
         _need(t, n)
     m, k = a.shape
@@ -181,6 +206,12 @@ def te_fp8_gemm(a, a_dtype, a_scale, b, b_dtype, b_scale, d, bias=None, gran=TE_
     bd = TE_BF16 if str(b_dtype).upper() == "BF16" else _fp8_code(b_dtype)
     dd = _hp_code(d)
     bias_code = _hp_code(bias) if bias is not None else TE_F32
+    if accumulate:
+        if dd != TE_F32:
+            raise ValueError("accumulate needs an fp32 d")
+        _check(lib().te_fp8_gemm_accumulate(_ptr(a), ad, _ptr(a_scale), _ptr(b), bd, _ptr(b_scale), int(gran), m,
+                                            n, k, _ptr(bias), bias_code, _ptr(d), _stream(stream)))
+        return
     _check(lib().te_fp8_gemm(_ptr(a), ad, _ptr(a_scale), _ptr(b), bd, _ptr(b_scale), int(gran), m, n, k,
                              _ptr(bias), bias_code, _ptr(d), dd, _stream(stream)))
 

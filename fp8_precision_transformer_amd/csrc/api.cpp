@@ -131,7 +131,7 @@ te_status te_cast_transpose(const void* x, int x_dtype, int64_t rows, int64_t co
                             uint8_t* out_col, void* stream) {
   te_status st = check_cast_common(x, x_dtype, rows, cols, out_dtype, mode, margin, scale, scale_inv, amax);
   if (st != TE_OK) return st;
-  if (!out_row && !out_col) return fail(TE_ERR_NULL, "out_row and out_col are both NULL");
+  if (rows * cols > 0 && !out_row && !out_col) return fail(TE_ERR_NULL, "out_row and out_col are both NULL");
   if ((out_row && !aligned16(out_row)) || (out_col && !aligned16(out_col)))
     return fail(TE_ERR_ALIGN, "outputs must be 16-byte aligned");
   if ((rows + 127) / 128 > 65535) return fail(TE_ERR_SHAPE, "rows too large for the tile grid");
@@ -139,8 +139,39 @@ te_status te_cast_transpose(const void* x, int x_dtype, int64_t rows, int64_t co
   log_dispatch("te_cast_transpose", "tile128x64", out_dtype == TE_E5M2 ? "E5M2" : "E4M3");
   return hip_status(te::launch_cast_transpose(x, x_dtype, rows, cols, out_dtype == TE_E5M2,
                                               mode == TE_SCALE_CURRENT, margin, scale, scale_inv, amax,
-                                              out_row, out_col, static_cast<hipStream_t>(stream)),
+                                              out_row, out_col, nullptr, nullptr,
+                                              static_cast<hipStream_t>(stream)),
                     "te_cast_transpose launch");
+}
+
+int64_t te_cast_transpose_dbias_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return -1;
+  return ((rows + 127) / 128) * cols * static_cast<int64_t>(sizeof(float));
+}
+
+te_status te_cast_transpose_dbias(const void* x, int x_dtype, int64_t rows, int64_t cols, int out_dtype,
+                                  int mode, int margin, float* scale, float* scale_inv, float* amax,
+                                  uint8_t* out_row, uint8_t* out_col, float* dbias, void* workspace,
+                                  int64_t workspace_bytes, void* stream) {
+  te_status st = check_cast_common(x, x_dtype, rows, cols, out_dtype, mode, margin, scale, scale_inv, amax);
+  if (st != TE_OK) return st;
+  if (rows * cols > 0 && !out_row && !out_col) return fail(TE_ERR_NULL, "out_row and out_col are both NULL");
+  if ((out_row && !aligned16(out_row)) || (out_col && !aligned16(out_col)))
+    return fail(TE_ERR_ALIGN, "outputs must be 16-byte aligned");
+  if ((rows + 127) / 128 > 65535) return fail(TE_ERR_SHAPE, "rows too large for the tile grid");
+  if (cols > 0 && !dbias) return fail(TE_ERR_NULL, "dbias is NULL");
+  const int64_t need = te_cast_transpose_dbias_workspace_bytes(rows, cols);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(TE_ERR_ARG, "workspace of %lld bytes needed (got %lld)", (long long)need, (long long)workspace_bytes);
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0)
+    return fail(TE_ERR_ALIGN, "workspace must be 4-byte aligned");
+  if ((st = check_device()) != TE_OK) return st;
+  log_dispatch("te_cast_transpose_dbias", "tile128x128_colsum", out_dtype == TE_E5M2 ? "E5M2" : "E4M3");
+  return hip_status(te::launch_cast_transpose(x, x_dtype, rows, cols, out_dtype == TE_E5M2,
+                                              mode == TE_SCALE_CURRENT, margin, scale, scale_inv, amax,
+                                              out_row, out_col, dbias, static_cast<float*>(workspace),
+                                              static_cast<hipStream_t>(stream)),
+                    "te_cast_transpose_dbias launch");
 }
 
 te_status te_scale_update(float* amax_history, float* scale, float* scale_inv, int n, int hist_len,
@@ -159,9 +190,9 @@ te_status te_scale_update(float* amax_history, float* scale, float* scale_inv, i
                     "te_scale_update launch");
 }
 
-te_status te_fp8_gemm(const void* a, int a_dtype, const void* a_scale, const void* b, int b_dtype,
-                      const void* b_scale, int gran, int64_t m, int64_t n, int64_t k, const void* bias,
-                      int bias_dtype, void* d, int d_dtype, void* stream) {
+static te_status gemm_impl(const void* a, int a_dtype, const void* a_scale, const void* b, int b_dtype,
+                           const void* b_scale, int gran, int64_t m, int64_t n, int64_t k, const void* bias,
+                           int bias_dtype, void* d, int d_dtype, int accumulate, void* stream) {
   if (m < 0 || n < 0 || k < 0) return fail(TE_ERR_SHAPE, "negative GEMM shape");
   if (n % 16 != 0 || k % 16 != 0)
     return fail(TE_ERR_SHAPE, "n and k must be multiples of 16 (got n=%lld k=%lld)", (long long)n, (long long)k);
@@ -203,6 +234,7 @@ te_status te_fp8_gemm(const void* a, int a_dtype, const void* a_scale, const voi
   g.mx = gran == TE_GRAN_MX_BLOCK32;
   g.bias_bf16 = bias_dtype == TE_BF16;
   g.d_bf16 = d_dtype == TE_BF16;
+  g.accumulate = accumulate;
   hipError_t e = te::launch_gemm(g, static_cast<hipStream_t>(stream));
   if (log_level() > 0) {
     char detail[128];
@@ -210,6 +242,20 @@ te_status te_fp8_gemm(const void* a, int a_dtype, const void* a_scale, const voi
     log_dispatch("te_fp8_gemm", te::last_gemm_variant(), detail);
   }
   return hip_status(e, "te_fp8_gemm launch");
+}
+
+te_status te_fp8_gemm(const void* a, int a_dtype, const void* a_scale, const void* b, int b_dtype,
+                      const void* b_scale, int gran, int64_t m, int64_t n, int64_t k, const void* bias,
+                      int bias_dtype, void* d, int d_dtype, void* stream) {
+  return gemm_impl(a, a_dtype, a_scale, b, b_dtype, b_scale, gran, m, n, k, bias, bias_dtype, d, d_dtype, 0,
+                   stream);
+}
+
+te_status te_fp8_gemm_accumulate(const void* a, int a_dtype, const void* a_scale, const void* b, int b_dtype,
+                                 const void* b_scale, int gran, int64_t m, int64_t n, int64_t k,
+                                 const void* bias, int bias_dtype, float* d, void* stream) {
+  return gemm_impl(a, a_dtype, a_scale, b, b_dtype, b_scale, gran, m, n, k, bias, bias_dtype, d, TE_F32, 1,
+                   stream);
 }
 
 te_status te_mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int elem_dtype,

@@ -62,6 +62,7 @@ struct Params {
   int kblocks;       // MX: 32-element blocks per row (k / 32)
   int nbm, nbn;      // tile grid
   int bias_bf16, d_bf16;
+  int accumulate;    // fp32 D only: D = fl32(D_old + result)
 };
 
 template <int V>
@@ -287,6 +288,8 @@ __global__ __launch_bounds__(NT, 1) void k_gemm(Params p) {
           const int64_t o = static_cast<int64_t>(row) * p.N + col;
           if (p.d_bf16)
             static_cast<uint16_t*>(p.d)[o] = static_cast<uint16_t>(f32_to_bf16_bits(val));
+          else if (p.accumulate)
+            static_cast<float*>(p.d)[o] = __fadd_rn(static_cast<float*>(p.d)[o], val);
           else
             static_cast<float*>(p.d)[o] = val;
         }
@@ -730,10 +733,17 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
       for (int t = 0; t < 16; ++t) {
         const int r = t * 4 + (lane >> 4);
         const int c = (lane & 15) * 4;
-        const v4f v4 = *reinterpret_cast<const v4f*>(ep + r * (kEpPitch / 4) + c);
+        v4f v4 = *reinterpret_cast<const v4f*>(ep + r * (kEpPitch / 4) + c);
         const int grow = row0 + r, gcol = col0 + c;
-        if (grow < p.M && gcol < p.N)
-          __builtin_nontemporal_store(v4, reinterpret_cast<v4f*>(static_cast<float*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol));
+        if (grow < p.M && gcol < p.N) {
+          v4f* dst = reinterpret_cast<v4f*>(static_cast<float*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol);
+          if (p.accumulate) {  // fp32 main-gradient accumulation: D = fl32(D_old + result)
+            const v4f old = __builtin_nontemporal_load(dst);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v4[q] = __fadd_rn(old[q], v4[q]);
+          }
+          __builtin_nontemporal_store(v4, dst);
+        }
       }
     }
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
@@ -781,6 +791,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   p.nbn = static_cast<int>((g.n + BN - 1) / BN);
   p.bias_bf16 = g.bias_bf16;
   p.d_bf16 = g.d_bf16;
+  p.accumulate = g.accumulate;
   // f8f6f4 format codes: 0 = E4M3, 1 = E5M2
   const int af = (g.a_fmt == E5M2) ? 1 : 0, bf = (g.b_fmt == E5M2) ? 1 : 0;
   if (g.a_fmt == BF16) return run<KIND_BF16, 0, 0>(p, s, "gemm4_bf16_256x256_pingpong");

@@ -18,7 +18,7 @@ hipError_t launch_amax_cast(const void* x, int x_dtype, int64_t n, int out_e5m2,
 hipError_t launch_cast_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols,
                                  int out_e5m2, int current, int margin, float* scale,
                                  float* scale_inv, float* amax, uint8_t* out_row,
-                                 uint8_t* out_col, hipStream_t s);
+                                 uint8_t* out_col, float* dbias, float* dbias_part, hipStream_t s);
 
 hipError_t launch_scale_update(float* hist, float* scale, float* scale_inv, int n, int hist_len,
                                int e5m2, int most_recent, int margin, hipStream_t s);
@@ -40,6 +40,7 @@ struct GemmArgs {
   int mx;                // 1: MX block-32 scales
   int bias_bf16;         // bias dtype: 0 f32, 1 bf16
   int d_bf16;            // output dtype: 0 f32, 1 bf16
+  int accumulate;        // 1: fp32 D = fl32(D_old + result)
 };
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);

@@ -344,15 +344,19 @@ __host__ __device__ __forceinline__ bool ct_vec_ok(int64_t R, int64_t C) {
 // inside a tile (the host checks that they fit).  FAST = false: the ragged
 // right column and bottom row of tiles (or every tile when rows or columns are
 // not vector-aligned), with element loads and byte stores under bounds checks.
-template <typename T, bool E5M2, int MODE, bool FAST>
+template <typename T, bool E5M2, int MODE, bool FAST, bool DBIAS = false>
 __global__ __launch_bounds__(kThreads) void k_cast_transpose(
     const T* __restrict__ x, int64_t R, int64_t C, float* __restrict__ scale,
     float* __restrict__ scale_inv, float* __restrict__ amax, uint8_t* __restrict__ out_row,
-    uint8_t* __restrict__ out_col, int margin, AmaxWork* __restrict__ work, int flags) {
+    uint8_t* __restrict__ out_col, int margin, AmaxWork* __restrict__ work, int flags,
+    float* __restrict__ dbias_part) {
   using M = CTMap<T>;
   constexpr int E = M::E, NP = M::NP, RPP = M::RPP;
   constexpr int kBits = 8 * static_cast<int>(sizeof(T));
   __shared__ uint32_t lds[kCT * kCTPitch / 4];
+  // DBIAS: per tile, column sums of the tile's rows, reduced over the lanes of one
+  // column through LDS: red[tile row group][column]
+  __shared__ float red[DBIAS ? RPP * kCT : 1];
 
   float s = 1.0f;
   if constexpr (MODE == 0) {
@@ -423,11 +427,18 @@ __global__ __launch_bounds__(kThreads) void k_cast_transpose(
   auto process = [&](uint4 (&raw)[NP], int64_t r0, int64_t c0, bool has1, int64_t r1, int64_t c1) {
     __syncthreads();  // the previous tile's LDS reads are done
     uint8_t* orow = out_row + r0 * C + c0;
+    float cs[E];  // DBIAS: this lane's column sums over its rows of the tile (rows past R read 0)
+#pragma unroll
+    for (int j = 0; j < E; ++j) cs[j] = 0.0f;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const int lr = p * RPP + prow;
       float v[E];
       unpack16<T>(raw[p], v);
+      if constexpr (DBIAS) {
+#pragma unroll
+        for (int j = 0; j < E; ++j) cs[j] = __fadd_rn(cs[j], v[j]);
+      }
       if constexpr (MODE == 0) m = absmax_bits<T>(m, raw[p]);
       uint32_t q[E / 4];
 #pragma unroll
@@ -448,6 +459,19 @@ __global__ __launch_bounds__(kThreads) void k_cast_transpose(
         }
       }
       if (has1 && out_col == nullptr) raw[p] = load1(p, r1, c1);
+    }
+    if constexpr (DBIAS) {
+      // tile column sums, rows in a fixed order (lane passes, then lane groups), so the
+      // result does not depend on scheduling; one partial per (tile row, column)
+#pragma unroll
+      for (int j = 0; j < E; ++j) red[prow * kCT + pcol + j] = cs[j];
+      __syncthreads();
+      if (t < kCT && c0 + t < C) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int g = 0; g < RPP; ++g) acc = __fadd_rn(acc, red[g * kCT + t]);
+        dbias_part[(r0 / kCT) * C + c0 + t] = acc;
+      }
     }
     if (out_col == nullptr) return;
     if (has1) {
@@ -512,6 +536,31 @@ __global__ __launch_bounds__(kThreads) void k_cast_transpose(
     }
   }
   if constexpr (MODE == 0) grid_amax(absmax_value<T>(m), amax, work, (flags & kAccAmax) != 0);
+}
+
+// dbias[c] = sum over tile rows of the partial column sums (0 when R == 0), in a fixed
+// order: a block takes 64 columns; thread (q, c) sums tile rows q, q + 4, q + 8, ... in
+// four interleaved accumulators (four loads in flight), then the four accumulators and
+// the four quarters q are added in index order.
+constexpr int kDbCols = 64;
+__global__ __launch_bounds__(256) void k_dbias_reduce(const float* __restrict__ part, int64_t ntr, int64_t C,
+                                                      float* __restrict__ dbias) {
+  __shared__ float red[4][kDbCols];
+  const int q = threadIdx.x / kDbCols, cl = threadIdx.x % kDbCols;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * kDbCols + cl;
+  float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (c < C) {
+    int64_t r = q;
+    for (; r + 12 < ntr; r += 16) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a[u] = __fadd_rn(a[u], part[(r + 4 * u) * C + c]);
+    }
+    for (int u = 0; r < ntr; r += 4, ++u) a[u & 3] = __fadd_rn(a[u & 3], part[r * C + c]);
+  }
+  red[q][cl] = __fadd_rn(__fadd_rn(a[0], a[1]), __fadd_rn(a[2], a[3]));
+  __syncthreads();
+  if (q == 0 && c < C)
+    dbias[c] = __fadd_rn(__fadd_rn(red[0][cl], red[1][cl]), __fadd_rn(red[2][cl], red[3][cl]));
 }
 
 // ----------------------------------------------------------------------------
@@ -889,43 +938,51 @@ hipError_t amax_cast_t(const T* x, int64_t n, int current, int margin, float* sc
   return hipGetLastError();
 }
 
-template <typename T, bool E5M2, int MODE>
+template <typename T, bool E5M2, int MODE, bool DBIAS>
 void ct_launch(const T* x, int64_t R, int64_t C, int margin, float* scale, float* scale_inv,
-               float* amax, uint8_t* out_row, uint8_t* out_col, AmaxWork* work, int flags, hipStream_t st) {
+               float* amax, uint8_t* out_row, uint8_t* out_col, AmaxWork* work, int flags, float* part,
+               hipStream_t st) {
   const int64_t whole = ct_vec_ok<T>(R, C) ? (R / kCT) * (C / kCT) : 0;
   const int64_t ragged = ((R + kCT - 1) / kCT) * ((C + kCT - 1) / kCT) - whole;
   if (whole > 0) {
-    const auto fn = k_cast_transpose<T, E5M2, MODE, true>;
+    const auto fn = k_cast_transpose<T, E5M2, MODE, true, DBIAS>;
     const int g = persistent_grid(reinterpret_cast<const void*>(fn), whole, 1, kCapCT);
     hipLaunchKernelGGL(fn, dim3(g), dim3(kThreads), 0, st, x, R, C, scale, scale_inv, amax, out_row,
-                       out_col, margin, work, flags);
+                       out_col, margin, work, flags, part);
   }
   if (ragged > 0) {  // the edge tiles' amax joins the whole tiles'
-    const auto fn = k_cast_transpose<T, E5M2, MODE, false>;
+    const auto fn = k_cast_transpose<T, E5M2, MODE, false, DBIAS>;
     const int g = persistent_grid(reinterpret_cast<const void*>(fn), ragged, 1, kCapCT);
     hipLaunchKernelGGL(fn, dim3(g), dim3(kThreads), 0, st, x, R, C, scale, scale_inv, amax, out_row,
-                       out_col, margin, work, whole > 0 ? flags | kAccAmax : flags);
+                       out_col, margin, work, whole > 0 ? flags | kAccAmax : flags, part);
   }
 }
 
 template <typename T, bool E5M2>
 hipError_t cast_transpose_t(const T* x, int64_t R, int64_t C, int current, int margin,
                             float* scale, float* scale_inv, float* amax, uint8_t* out_row,
-                            uint8_t* out_col, hipStream_t st) {
+                            uint8_t* out_col, float* dbias, float* part, hipStream_t st) {
   if (R == 0 || C == 0) {
     hipLaunchKernelGGL(k_prologue, dim3(1), dim3(1), 0, st, amax, scale, scale_inv, current ? 0 : 1);
     if (current)
       hipLaunchKernelGGL(k_current_scale, dim3(1), dim3(1), 0, st, amax, scale, scale_inv,
                          Fp8Traits<E5M2>::max, margin);
+    if (dbias != nullptr && C > 0)  // a sum over no rows
+      hipLaunchKernelGGL(k_dbias_reduce, dim3(static_cast<unsigned>((C + kDbCols - 1) / kDbCols)), dim3(256), 0, st,
+                         part, int64_t{0}, C, dbias);
     return hipGetLastError();
   }
   AmaxWork* w = amax_work(st);
   if (w == nullptr) return hipErrorOutOfMemory;
-  if (current) {
-    launch_flat<T, E5M2, 1>(x, R * C, margin, scale, scale_inv, amax, nullptr, w, 0, st);
-    ct_launch<T, E5M2, 2>(x, R, C, margin, scale, scale_inv, amax, out_row, out_col, w, 0, st);
+  if (current) launch_flat<T, E5M2, 1>(x, R * C, margin, scale, scale_inv, amax, nullptr, w, 0, st);
+  if (dbias != nullptr) {
+    if (current) ct_launch<T, E5M2, 2, true>(x, R, C, margin, scale, scale_inv, amax, out_row, out_col, w, 0, part, st);
+    else ct_launch<T, E5M2, 0, true>(x, R, C, margin, scale, scale_inv, amax, out_row, out_col, w, kPublishInv, part, st);
+    hipLaunchKernelGGL(k_dbias_reduce, dim3(static_cast<unsigned>((C + kDbCols - 1) / kDbCols)), dim3(256), 0, st, part,
+                       (R + kCT - 1) / kCT, C, dbias);
   } else {
-    ct_launch<T, E5M2, 0>(x, R, C, margin, scale, scale_inv, amax, out_row, out_col, w, kPublishInv, st);
+    if (current) ct_launch<T, E5M2, 2, false>(x, R, C, margin, scale, scale_inv, amax, out_row, out_col, w, 0, nullptr, st);
+    else ct_launch<T, E5M2, 0, false>(x, R, C, margin, scale, scale_inv, amax, out_row, out_col, w, kPublishInv, nullptr, st);
   }
   return hipGetLastError();
 }
@@ -976,12 +1033,12 @@ hipError_t launch_amax_cast(const void* x, int x_dtype, int64_t n, int out_e5m2,
 hipError_t launch_cast_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols,
                                  int out_e5m2, int current, int margin, float* scale,
                                  float* scale_inv, float* amax, uint8_t* out_row,
-                                 uint8_t* out_col, hipStream_t s) {
+                                 uint8_t* out_col, float* dbias, float* dbias_part, hipStream_t s) {
   if (x_dtype == BF16)
-    return out_e5m2 ? cast_transpose_t<uint16_t, true>(static_cast<const uint16_t*>(x), rows, cols, current, margin, scale, scale_inv, amax, out_row, out_col, s)
-                    : cast_transpose_t<uint16_t, false>(static_cast<const uint16_t*>(x), rows, cols, current, margin, scale, scale_inv, amax, out_row, out_col, s);
-  return out_e5m2 ? cast_transpose_t<float, true>(static_cast<const float*>(x), rows, cols, current, margin, scale, scale_inv, amax, out_row, out_col, s)
-                  : cast_transpose_t<float, false>(static_cast<const float*>(x), rows, cols, current, margin, scale, scale_inv, amax, out_row, out_col, s);
+    return out_e5m2 ? cast_transpose_t<uint16_t, true>(static_cast<const uint16_t*>(x), rows, cols, current, margin, scale, scale_inv, amax, out_row, out_col, dbias, dbias_part, s)
+                    : cast_transpose_t<uint16_t, false>(static_cast<const uint16_t*>(x), rows, cols, current, margin, scale, scale_inv, amax, out_row, out_col, dbias, dbias_part, s);
+  return out_e5m2 ? cast_transpose_t<float, true>(static_cast<const float*>(x), rows, cols, current, margin, scale, scale_inv, amax, out_row, out_col, dbias, dbias_part, s)
+                  : cast_transpose_t<float, false>(static_cast<const float*>(x), rows, cols, current, margin, scale, scale_inv, amax, out_row, out_col, dbias, dbias_part, s);
 }
 
 hipError_t launch_scale_update(float* hist, float* scale, float* scale_inv, int n, int hist_len,

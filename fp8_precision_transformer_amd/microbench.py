@@ -196,6 +196,14 @@ def cast(args):
         o2 = torch.empty((C, R), dtype=torch.uint8, device=dev)
         fn = lambda: B.te_cast_transpose(x, "E4M3", mode, 0, scale, si, am, o1, o2)  # noqa: E731
         nbytes = R * C * (6 if mode == B.TE_SCALE_CURRENT else 4)
+    elif args.op == "bothdbias":  # both copies plus the bias gradient (column sums) of x
+        o1 = torch.empty((R, C), dtype=torch.uint8, device=dev)
+        o2 = torch.empty((C, R), dtype=torch.uint8, device=dev)
+        db = torch.empty(C, dtype=torch.float32, device=dev)
+        ws = torch.empty(max(B.te_cast_transpose_dbias_workspace_bytes(R, C) // 4, 1), dtype=torch.float32,
+                         device=dev)
+        fn = lambda: B.te_cast_transpose_dbias(x, "E5M2", mode, 0, scale, si, am, db, ws, o1, o2)  # noqa: E731
+        nbytes = R * C * (6 if mode == B.TE_SCALE_CURRENT else 4) + C * 4
     elif args.op == "mx":  # row-wise copy
         o1 = torch.empty((R, C), dtype=torch.uint8, device=dev)
         s1 = torch.empty((R, C // 32), dtype=torch.uint8, device=dev)
@@ -254,7 +262,8 @@ def main():
     c = sub.add_parser("cast")
     c.add_argument("--rows", type=int, default=15872)
     c.add_argument("--cols", type=int, default=16384)
-    c.add_argument("--op", choices=["cast", "transpose", "both", "mx", "mxcol", "mxboth"], default="cast")
+    c.add_argument("--op", choices=["cast", "transpose", "both", "bothdbias", "mx", "mxcol", "mxboth"],
+                   default="cast")
     c.add_argument("--mode", choices=["delayed", "current"], default="delayed")
     c.add_argument("--iters", type=int, default=20)
     c.add_argument("--warmup", type=int, default=3)

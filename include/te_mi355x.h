@@ -127,12 +127,41 @@ te_status te_amax_cast(const void* x, int x_dtype, int64_t rows, int64_t cols,
  * Arguments as te_amax_cast, plus
  *   out_row  [rows, cols] uint8 or NULL.
  *   out_col  [cols, rows] uint8 or NULL; out_col[c, r] == out_row[r, c] byte for byte.
- * At least one of out_row / out_col must be non-NULL.
+ * At least one of out_row / out_col must be non-NULL (unless rows * cols == 0).
  */
 te_status te_cast_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols,
                             int out_dtype, int mode, int margin,
                             float* scale, float* scale_inv, float* amax,
                             uint8_t* out_row, uint8_t* out_col, void* stream);
+
+/*
+ * te_cast_transpose_dbias -- te_cast_transpose of an output gradient dY that also
+ * returns its bias gradient, read in the same pass over dY.
+ *
+ * Defines: the backward of te.Linear(..., bias=True) ([FP8-intro] "Transformer
+ * Engine の使い方"): for y = x W^T + b the bias gradient is the sum of dY over its
+ * rows (tokens); reading it from the pass that casts dY saves a second read of dY.
+ *
+ * Arguments as te_cast_transpose, plus
+ *   dbias      [cols] fp32, written: dbias[c] = sum_r x[r, c], summed in fp32 in a
+ *              fixed order (within each 128-row tile, then over tiles in row
+ *              order), so the result is reproducible run to run.  NULL only if
+ *              cols == 0.
+ *   workspace  device scratch of at least te_cast_transpose_dbias_workspace_bytes(
+ *              rows, cols) bytes (per-tile partial sums), 4-byte aligned, owned by
+ *              the caller; contents on entry are ignored.  NULL if that size is 0.
+ *   workspace_bytes  its size (TE_ERR_ARG if too small).
+ * rows == 0 gives dbias = 0.
+ */
+te_status te_cast_transpose_dbias(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                                  int out_dtype, int mode, int margin,
+                                  float* scale, float* scale_inv, float* amax,
+                                  uint8_t* out_row, uint8_t* out_col, float* dbias,
+                                  void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes te_cast_transpose_dbias needs for [rows, cols]: ceil(rows / 128)
+ * * cols * 4 (host only, no GPU call); -1 for negative sizes. */
+int64_t te_cast_transpose_dbias_workspace_bytes(int64_t rows, int64_t cols);
 
 /*
  * te_scale_update -- delayed-scaling update of n tensors of one FP8 format.
@@ -182,6 +211,25 @@ te_status te_fp8_gemm(const void* a, int a_dtype, const void* a_scale,
                       int gran, int64_t m, int64_t n, int64_t k,
                       const void* bias, int bias_dtype,
                       void* d, int d_dtype, void* stream);
+
+/*
+ * te_fp8_gemm_accumulate -- te_fp8_gemm that adds its result into an fp32 D:
+ * D[i, j] = fl32(D_old[i, j] + r[i, j]), r the te_fp8_gemm result of the same
+ * arguments (scaled, plus bias).
+ *
+ * Defines: Wgrad computed in FP8 ([FP8-intro] "統合済みライブラリの利用", the
+ * fp8_wgrad key) and accumulated into the weight's fp32 gradient across
+ * micro-batches, the main-gradient reading of a Wgrad whose output is fp32.
+ *
+ *   d          [m, n] fp32, read and written (the caller initialises it).
+ * Every other argument, shape rule and error as te_fp8_gemm.  Calls on one D
+ * must not overlap (each element is read, added to and written by one thread).
+ */
+te_status te_fp8_gemm_accumulate(const void* a, int a_dtype, const void* a_scale,
+                                 const void* b, int b_dtype, const void* b_scale,
+                                 int gran, int64_t m, int64_t n, int64_t k,
+                                 const void* bias, int bias_dtype,
+                                 float* d, void* stream);
 
 /*
  * te_mxfp8_quantize -- MXFP8 block quantization, row-wise and/or column-wise.

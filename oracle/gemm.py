@@ -21,6 +21,10 @@ Readings (the design doc lists them):
   * MXFP8: acc = sum over 32-blocks of 2^(ea-127) * 2^(eb-127) * (block dot
     product), all exact in float64, rounded once to fp32; bias as above.
 
+  * bias gradient: the backward of y = x W^T + b gives db[c] = sum over rows
+    of dy[r, c]; the oracle returns that sum in float64 (exact to float64
+    rounding), and a GPU sum in fp32 is held to the fp32 summation bound.
+
 Pins (tests/test_oracle_gemm.py): brute-force triple loop on tiny shapes,
 integer-valued operands (exact in any order), identity operand, bias-only,
 power-of-two scale linearity, MX with all codes 127 equal to per-tensor,
@@ -99,6 +103,12 @@ def gemm_bf16(a_bits, b_bits, bias=None, out: str = "bf16") -> np.ndarray:
     b = bf16_bits_to_f32(b_bits).astype(np.float64)
     acc = (a @ b.T).astype(np.float32)
     return _epilogue(acc, bias, out)
+
+
+def bias_grad(dy) -> np.ndarray:
+    """Bias gradient of y = x W^T + b ([FP8-intro] "Transformer Engine の使い方",
+    te.Linear with bias): db[c] = sum_r dy[r, c], summed in float64."""
+    return np.asarray(dy, dtype=np.float64).sum(axis=0)
 
 
 def rel_err(d, r) -> float:

@@ -262,3 +262,56 @@ def test_dispatched_variant_is_the_requested_matrix_core_path():
         B.te_fp8_gemm(xb, "BF16", None, wb, "BF16", None, d)
         assert B.te_gemm_variant() == "gemm4_bf16_256x256_pingpong"
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("mnk", [(300, 272, 416), (1024, 768, 768), (256, 512, 4096)], ids=str)
+@pytest.mark.parametrize("gran", ["tensor", "mx"])
+def test_gemm_accumulate_into_fp32(mnk, gran):
+    """te_fp8_gemm_accumulate (Wgrad into an fp32 main gradient): D = fl32(D_old + r),
+    twice in a row, within the matrix-core bound of D_old + r (+ r)."""
+    m, n, k = mnk
+    sd = _seed(mnk, gran, "acc")
+    d_old = synth.normal((m, n), 1.0, 14, sd, 3, 0)
+    bias = synth.normal((n,), 0.02, 14, sd, 2, 0)
+    if gran == "tensor":
+        a, sa = _quantized((m, k), "E5M2", (14, sd, 0, 0), "grad")
+        b, sb = _quantized((n, k), "E4M3", (14, sd, 1, 0))
+        args = (dev_u8(a), "E5M2", scalar(float(sa)), dev_u8(b), "E4M3", scalar(float(sb)))
+        prod = O.gemm_per_tensor(a, O.E5M2, sa, b, O.E4M3, sb, bias=bias, out="f32").astype(np.float64)
+        av, bv, sc = O.decode_table(O.E5M2)[a], O.decode_table(O.E4M3)[b], np.float64(sa) * np.float64(sb)
+        kw = {}
+    else:
+        xa = synth.grads((m, k), 14, sd, 0, 0)
+        xb = synth.normal((n, k), 0.02, 14, sd, 1, 0)
+        a, ea = O.mxfp8_quantize(xa, O.E4M3)
+        b, eb = O.mxfp8_quantize(xb, O.E4M3)
+        args = (dev_u8(a), "E4M3", dev_u8(ea), dev_u8(b), "E4M3", dev_u8(eb))
+        prod = O.gemm_mx(a, ea, O.E4M3, b, eb, O.E4M3, bias=bias, out="f32").astype(np.float64)
+        av = O.decode_table(O.E4M3)[a] * np.repeat(O.e8m0_to_float(ea), 32, axis=1)
+        bv = O.decode_table(O.E4M3)[b] * np.repeat(O.e8m0_to_float(eb), 32, axis=1)
+        sc = 1.0
+        kw = {"gran": B.TE_GRAN_MX_BLOCK32}
+    d = dev_f32(d_old)
+    for rep in (1, 2):
+        B.te_fp8_gemm(*args, d, bias=dev_f32(bias), accumulate=True, **kw)
+        ref = d_old.astype(np.float64) + rep * prod
+        check_fp8_gemm(host(d), ref, av, bv, rep * sc, "f32")
+
+
+def test_gemm_accumulate_exact_integer_operands():
+    """Integer operands, power-of-two scales and an integer D_old: every sum is exact, so
+    D_old + A.B^T comes out bit for bit; a bf16 D is rejected."""
+    m, n, k = 200, 96, 512
+    rng = np.random.default_rng(21)
+    ints = np.arange(-16, 17)
+    codes = O.encode(ints.astype(np.float32), O.E4M3)
+    a = codes[rng.integers(0, len(ints), (m, k))]
+    b = codes[rng.integers(0, len(ints), (n, k))]
+    d_old = rng.integers(-1000, 1000, (m, n)).astype(np.float32)
+    d = dev_f32(d_old)
+    B.te_fp8_gemm(dev_u8(a), "E4M3", scalar(0.5), dev_u8(b), "E4M3", scalar(4.0), d, accumulate=True)
+    ref = d_old + O.gemm_per_tensor(a, O.E4M3, 0.5, b, O.E4M3, 4.0, out="f32")
+    np.testing.assert_array_equal(host(d), ref)
+    with pytest.raises(ValueError):
+        B.te_fp8_gemm(dev_u8(a), "E4M3", scalar(0.5), dev_u8(b), "E4M3", scalar(4.0), _out(m, n, "bf16"),
+                      accumulate=True)

@@ -381,3 +381,58 @@ def test_grid_amax_across_streams_and_grid_sizes():
     for i, s_in, am, sinv, _ in results:
         assert host(am)[0] == xs[i][1], (i, host(am)[0], xs[i][1])
         assert host(sinv)[0] == O.scale_inverse(np.float32(s_in)), i
+
+
+DBIAS_SHAPES = [(128, 128), (300, 200), (4096, 768), (77, 128), (1, 17), (256, 16), (0, 64), (1984, 4096)]
+
+
+@pytest.mark.parametrize("shape", DBIAS_SHAPES, ids=str)
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+@pytest.mark.parametrize("mode", ["delayed", "current"])
+@pytest.mark.parametrize("outs", ["both", "col"])
+def test_cast_transpose_dbias(shape, xdt, mode, outs):
+    """te_cast_transpose_dbias: the E5M2 codes, amax and scales exactly as
+    te_cast_transpose gives them, plus dbias[c] = sum_r dy[r, c] within the fp32
+    summation bound of the oracle's float64 sum, identical on a second run."""
+    R, C = shape
+    seed = _seed(shape, xdt, mode, outs, "dbias")
+    x32 = synth.grads(shape, 9, seed, 3, 0)
+    xd, xh = input_pair(x32, xdt)
+    out_row = torch.empty((R, C), dtype=torch.uint8, device=DEV) if outs == "both" else None
+    out_col = torch.empty((C, R), dtype=torch.uint8, device=DEV)
+    nbytes = B.te_cast_transpose_dbias_workspace_bytes(R, C)
+    assert nbytes == -(-R // 128) * C * 4
+    ws = torch.full((max(nbytes // 4, 1),), float("nan"), dtype=torch.float32, device=DEV)
+    results = []
+    for _ in range(2):
+        am, sinv, db = empty_f32(), empty_f32(), empty_f32(C)
+        if mode == "delayed":
+            s_in = np.float32(2048.0)
+            scale = scalar(float(s_in))
+            B.te_cast_transpose_dbias(xd, "E5M2", B.TE_SCALE_DELAYED, 0, scale, sinv, am, db, ws, out_row, out_col)
+            ref_s = s_in
+        else:
+            scale = empty_f32()
+            B.te_cast_transpose_dbias(xd, "E5M2", B.TE_SCALE_CURRENT, 0, scale, sinv, am, db, ws, out_row, out_col)
+            ref_s = O.current_scale(O.amax(xh), O.E5M2)
+        results.append(host(db))
+    ref_row, ref_col = O.cast_transpose(xh, ref_s, O.E5M2)
+    np.testing.assert_array_equal(host(out_col), ref_col)
+    if out_row is not None:
+        np.testing.assert_array_equal(host(out_row), ref_row)
+    assert host(am)[0] == O.amax(xh)
+    assert host(scale)[0] == ref_s and host(sinv)[0] == O.scale_inverse(ref_s)
+    ref = O.bias_grad(xh)
+    bound = R * 2.0 ** -24 * np.abs(xh.astype(np.float64)).sum(axis=0)
+    got = results[0].astype(np.float64)
+    assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) - bound))
+    np.testing.assert_array_equal(results[0], results[1])
+
+
+def test_cast_transpose_dbias_rejects_small_workspace():
+    x = torch.zeros((256, 128), dtype=torch.bfloat16, device=DEV)
+    col = torch.empty((128, 256), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(10, dtype=torch.float32, device=DEV)
+    with pytest.raises(B.TEError):
+        B.te_cast_transpose_dbias(x, "E5M2", B.TE_SCALE_CURRENT, 0, empty_f32(), empty_f32(), empty_f32(),
+                                  empty_f32(128), ws, None, col)

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (E4M3, E5M2, bf16_bits_to_f32, bf16_round_bits, decode, decode_table,
+from oracle import (E4M3, E5M2, bias_grad, bf16_bits_to_f32, bf16_round_bits, decode, decode_table,
                     encode, gemm_bf16, gemm_mx, gemm_per_tensor, rel_err, e8m0_to_float)
 
 
@@ -158,3 +158,22 @@ def test_rel_err_definition():
     # near-zero reference uses the 1e-3 * max floor
     r2 = np.array([0.0, 1000.0])
     assert abs(rel_err(np.array([0.5, 1000.0]), r2) - 0.5) < 1e-12
+
+
+def test_bias_grad_pins():
+    """bias_grad against a Python double loop on a tiny input, the closed form of a
+    rank-one dy (every row the same vector v: db = R v), and the gradient of the bias
+    by finite differences of sum(y * dy) with y = x W^T + b (linear in b, so exact)."""
+    rng = np.random.default_rng(5)
+    dy = rng.standard_normal((7, 5)).astype(np.float32)
+    loop = [sum(float(dy[r, c]) for r in range(7)) for c in range(5)]
+    np.testing.assert_allclose(bias_grad(dy), loop, rtol=0, atol=1e-12)
+    v = rng.integers(-50, 50, 6).astype(np.float32)
+    np.testing.assert_array_equal(bias_grad(np.tile(v, (13, 1))), 13.0 * v.astype(np.float64))
+    x = rng.standard_normal((9, 4))
+    w = rng.standard_normal((3, 4))
+    b = rng.standard_normal(3)
+    g = rng.standard_normal((9, 3))
+    loss = lambda bb: float(np.sum((x @ w.T + bb) * g))  # noqa: E731
+    fd = np.array([loss(b + np.eye(3)[c]) - loss(b) for c in range(3)])
+    np.testing.assert_allclose(bias_grad(g), fd, rtol=1e-12, atol=1e-12)
