@@ -54,6 +54,8 @@ _vp, _i64, _i32, _fp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_v
 _SIGNATURES = {
     "te_amax_cast": [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp],
     "te_cast_transpose": [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp],
+    "te_layernorm_fp8": [_vp, _i32, _i64, _i64, _vp, _vp, _i32, ctypes.c_float, _i32, _i32, _i32, _vp, _vp, _vp,
+                         _vp, _vp, _vp, _vp],
     "te_cast_transpose_dbias": [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                                 _vp],
     "te_scale_update": [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp],
@@ -179,6 +181,20 @@ def te_cast_transpose_dbias(x, out_dtype, mode, margin, scale, scale_inv, amax, 
     _check(lib().te_cast_transpose_dbias(_ptr(x), _hp_code(x), rows, cols, _fp8_code(out_dtype), int(mode),
                                          int(margin), _ptr(scale), _ptr(scale_inv), _ptr(amax), _ptr(out_row),
                                          _ptr(out_col), _ptr(dbias), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def te_layernorm_fp8(x, gamma, beta, eps, out_dtype, mode, margin, scale, scale_inv, amax, out, mu=None,
+                     rsigma=None, stream=None):
+    """LayerNorm of x over its last axis, written as FP8 codes into out (see the header)."""
+    for n, t in (("x", x), ("gamma", gamma), ("beta", beta), ("scale", scale), ("scale_inv", scale_inv),
+                 ("amax", amax), ("out", out), ("mu", mu), ("rsigma", rsigma)):
+        _need(t, n)
+    if gamma.dtype != beta.dtype:
+        raise ValueError("gamma and beta must share a dtype")
+    rows, cols = _2d(x)
+    _check(lib().te_layernorm_fp8(_ptr(x), _hp_code(x), rows, cols, _ptr(gamma), _ptr(beta), _hp_code(gamma),
+                                  float(eps), _fp8_code(out_dtype), int(mode), int(margin), _ptr(scale),
+                                  _ptr(scale_inv), _ptr(amax), _ptr(out), _ptr(mu), _ptr(rsigma), _stream(stream)))
 
 
 def te_scale_update(amax_history, scale, scale_inv, fp8_dtype, algo=TE_AMAX_MAX, margin=0, stream=None):

@@ -174,6 +174,28 @@ te_status te_cast_transpose_dbias(const void* x, int x_dtype, int64_t rows, int6
                     "te_cast_transpose_dbias launch");
 }
 
+te_status te_layernorm_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, const void* gamma,
+                           const void* beta, int param_dtype, float eps, int out_dtype, int mode, int margin,
+                           float* scale, float* scale_inv, float* amax, uint8_t* out, float* mu, float* rsigma,
+                           void* stream) {
+  te_status st = check_cast_common(x, x_dtype, rows, cols, out_dtype, mode, margin, scale, scale_inv, amax);
+  if (st != TE_OK) return st;
+  if (rows > 0 && cols == 0) return fail(TE_ERR_SHAPE, "LayerNorm needs cols > 0");
+  if (cols % 16 != 0) return fail(TE_ERR_SHAPE, "cols must be a multiple of 16 (got %lld)", (long long)cols);
+  if (!is_hp(param_dtype)) return fail(TE_ERR_DTYPE, "param_dtype must be TE_F32 or TE_BF16 (got %d)", param_dtype);
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(TE_ERR_ARG, "eps must be finite and >= 0");
+  if (rows > 0 && (!gamma || !beta || !out)) return fail(TE_ERR_NULL, "gamma, beta and out are required");
+  if ((out && !aligned16(out)) || (gamma && !aligned16(gamma)) || (beta && !aligned16(beta)))
+    return fail(TE_ERR_ALIGN, "out, gamma and beta must be 16-byte aligned");
+  if ((st = check_device()) != TE_OK) return st;
+  log_dispatch("te_layernorm_fp8", mode == TE_SCALE_CURRENT ? "row_per_block_two_pass" : "row_per_block",
+               out_dtype == TE_E5M2 ? "E5M2" : "E4M3");
+  return hip_status(te::launch_layernorm_fp8(x, x_dtype, rows, cols, gamma, beta, param_dtype, eps,
+                                             out_dtype == TE_E5M2, mode == TE_SCALE_CURRENT, margin, scale,
+                                             scale_inv, amax, out, mu, rsigma, static_cast<hipStream_t>(stream)),
+                    "te_layernorm_fp8 launch");
+}
+
 te_status te_scale_update(float* amax_history, float* scale, float* scale_inv, int n, int hist_len,
                           int fp8_dtype, int algo, int margin, void* stream) {
   if (n < 0) return fail(TE_ERR_SHAPE, "n must be >= 0");

@@ -20,6 +20,11 @@ hipError_t launch_cast_transpose(const void* x, int x_dtype, int64_t rows, int64
                                  float* scale_inv, float* amax, uint8_t* out_row,
                                  uint8_t* out_col, float* dbias, float* dbias_part, hipStream_t s);
 
+hipError_t launch_layernorm_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, const void* gamma,
+                                const void* beta, int param_dtype, float eps, int out_e5m2, int current,
+                                int margin, float* scale, float* scale_inv, float* amax, uint8_t* out,
+                                float* mu, float* rsigma, hipStream_t s);
+
 hipError_t launch_scale_update(float* hist, float* scale, float* scale_inv, int n, int hist_len,
                                int e5m2, int most_recent, int margin, hipStream_t s);
 

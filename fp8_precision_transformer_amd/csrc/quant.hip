@@ -564,6 +564,171 @@ __global__ __launch_bounds__(256) void k_dbias_reduce(const float* __restrict__ 
 }
 
 // ----------------------------------------------------------------------------
+// LayerNorm over the last axis with the output written as FP8 codes (te.LayerNorm,
+// whose output feeds the QKV and MLP-up GEMMs, fused with the cast of that output):
+//   mu = mean_c x, var = mean_c (x - mu)^2, rsigma = 1 / sqrt(var + eps),
+//   y = ((x - mu) * rsigma) * gamma + beta,  q = satRNE(fl32(y * scale)),
+// every operation a separately rounded fp32 operation.  One wave per row (a block
+// holds four rows, persistent over row groups): lane l takes the 16-byte chunks
+// l, l + 64, ... of the row; up to kLnReg chunks per lane (4096 bf16 / 2048 fp32
+// columns) stay in registers, wider rows are re-read from cache for the second and
+// third pass.  Sums run per lane in chunk order, then over the wave by an xor
+// butterfly (every lane ends with the same bits), so a run is reproducible and no
+// block barrier is needed.  MODE 0: delayed scaling (amax of y + cast in one
+// launch); MODE 1: current scaling's first pass (statistics, amax of y); MODE 2: its
+// cast pass with the scale from *amax.
+// ----------------------------------------------------------------------------
+constexpr int kLnReg = 8;
+
+// EV consecutive gamma or beta values from column c (16-byte aligned vectors)
+template <typename P, int EV>
+__device__ __forceinline__ void load_params(const P* p, int64_t c, float* out) {
+  if constexpr (sizeof(P) == 4) {
+#pragma unroll
+    for (int k = 0; k < EV / 4; ++k) {
+      const float4 f = *reinterpret_cast<const float4*>(p + c + 4 * k);
+      out[4 * k] = f.x;
+      out[4 * k + 1] = f.y;
+      out[4 * k + 2] = f.z;
+      out[4 * k + 3] = f.w;
+    }
+  } else if constexpr (EV == 8) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p + c);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = bf16_lo(w[i]);
+      out[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+    const uint2 u = *reinterpret_cast<const uint2*>(p + c);
+    out[0] = bf16_lo(u.x);
+    out[1] = bf16_hi(u.x);
+    out[2] = bf16_lo(u.y);
+    out[3] = bf16_hi(u.y);
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = __fadd_rn(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+template <typename T, typename P, bool E5M2, int MODE>
+__global__ __launch_bounds__(kThreads) void k_layernorm(const T* __restrict__ x, int64_t R, int64_t C,
+                                                        const P* __restrict__ gamma, const P* __restrict__ beta,
+                                                        float eps, float* __restrict__ scale,
+                                                        float* __restrict__ scale_inv, float* __restrict__ amax,
+                                                        uint8_t* __restrict__ out, float* __restrict__ mu_out,
+                                                        float* __restrict__ rs_out, int margin,
+                                                        AmaxWork* __restrict__ work, int flags) {
+  constexpr int EV = 16 / static_cast<int>(sizeof(T));  // elements per 16-byte chunk
+  constexpr int kWaves = kThreads / 64;
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  float s = 1.0f;
+  if constexpr (MODE == 0) {
+    s = *scale;
+    if ((flags & kPublishInv) && blockIdx.x == 0 && t == 0) *scale_inv = 1.0f / s;
+  }
+  if constexpr (MODE == 2) {
+    s = scale_from_amax(*amax, Fp8Traits<E5M2>::max, margin, 1.0f);
+    if (blockIdx.x == 0 && t == 0) {
+      *scale = s;
+      *scale_inv = 1.0f / s;
+    }
+  }
+  const int64_t nch = C / EV;
+  const bool in_regs = nch <= 64 * kLnReg;
+  const float inv_c = 1.0f / static_cast<float>(C);
+  uint32_t m = 0u;  // running max of |y| as magnitude bits
+  for (int64_t row = static_cast<int64_t>(blockIdx.x) * kWaves + wid; row < R;
+       row += static_cast<int64_t>(gridDim.x) * kWaves) {
+    const T* xr = x + row * C;
+    auto load = [&](int64_t ch) { return *reinterpret_cast<const uint4*>(xr + ch * EV); };
+    uint4 reg[kLnReg];
+    float acc = 0.0f;
+    if (in_regs) {
+#pragma unroll
+      for (int k = 0; k < kLnReg; ++k) {
+        const int64_t ch = lane + 64 * k;
+        if (ch < nch) reg[k] = load(ch);
+      }
+#pragma unroll
+      for (int k = 0; k < kLnReg; ++k) {
+        if (lane + 64 * k < nch) {
+          float v[EV];
+          unpack16<T>(reg[k], v);
+#pragma unroll
+          for (int j = 0; j < EV; ++j) acc = __fadd_rn(acc, v[j]);
+        }
+      }
+    } else {
+      for (int64_t ch = lane; ch < nch; ch += 64) {
+        float v[EV];
+        unpack16<T>(load(ch), v);
+#pragma unroll
+        for (int j = 0; j < EV; ++j) acc = __fadd_rn(acc, v[j]);
+      }
+    }
+    const float mean = __fmul_rn(wave_sum(acc), inv_c);
+    // squared deviations, then the output, chunk by chunk (from registers or cache)
+    auto sq_chunk = [&](const uint4& raw) {
+      float v[EV];
+      unpack16<T>(raw, v);
+#pragma unroll
+      for (int j = 0; j < EV; ++j) {
+        const float d = __fsub_rn(v[j], mean);
+        acc = __fadd_rn(acc, __fmul_rn(d, d));
+      }
+    };
+    acc = 0.0f;
+    if (in_regs) {
+#pragma unroll
+      for (int k = 0; k < kLnReg; ++k)
+        if (lane + 64 * k < nch) sq_chunk(reg[k]);
+    } else {
+      for (int64_t ch = lane; ch < nch; ch += 64) sq_chunk(load(ch));
+    }
+    const float var = __fmul_rn(wave_sum(acc), inv_c);
+    const float rs = 1.0f / __fsqrt_rn(__fadd_rn(var, eps));
+    if (MODE != 2 && lane == 0) {
+      if (mu_out != nullptr) mu_out[row] = mean;
+      if (rs_out != nullptr) rs_out[row] = rs;
+    }
+    auto out_chunk = [&](const uint4& raw, int64_t ch) {
+      float v[EV], y[EV], g[EV], b[EV];
+      unpack16<T>(raw, v);
+      load_params<P, EV>(gamma, ch * EV, g);
+      load_params<P, EV>(beta, ch * EV, b);
+#pragma unroll
+      for (int j = 0; j < EV; ++j) {
+        y[j] = __fadd_rn(__fmul_rn(__fmul_rn(__fsub_rn(v[j], mean), rs), g[j]), b[j]);
+        if constexpr (MODE != 2) m = max(m, __float_as_uint(y[j]) & 0x7fffffffu);
+      }
+      if constexpr (MODE != 1) {
+        uint8_t* o = out + row * C + ch * EV;
+        if constexpr (EV == 8)
+          *reinterpret_cast<uint2*>(o) = make_uint2(quant4<E5M2>(y[0], y[1], y[2], y[3], s),
+                                                    quant4<E5M2>(y[4], y[5], y[6], y[7], s));
+        else
+          *reinterpret_cast<uint32_t*>(o) = quant4<E5M2>(y[0], y[1], y[2], y[3], s);
+      }
+    };
+    if (in_regs) {
+#pragma unroll
+      for (int k = 0; k < kLnReg; ++k) {
+        const int64_t ch = lane + 64 * k;
+        if (ch < nch) out_chunk(reg[k], ch);
+      }
+    } else {
+      for (int64_t ch = lane; ch < nch; ch += 64) out_chunk(load(ch), ch);
+    }
+  }
+  if constexpr (MODE != 2) grid_amax(__uint_as_float(m), amax, work, (flags & kAccAmax) != 0);
+}
+
+// ----------------------------------------------------------------------------
 // delayed-scaling update, one thread per tensor
 // ----------------------------------------------------------------------------
 __global__ void k_scale_update(float* __restrict__ hist, float* __restrict__ scale,
@@ -886,6 +1051,7 @@ constexpr int kCapFlat = 2;
 constexpr int kCapCT = 2;
 constexpr int kCapMxRow = 2;
 constexpr int kCapMxCol = 8;
+constexpr int kCapLn = 8;  // LayerNorm: four rows per block, one per wave
 
 // The grid-amax workspace of (current device, stream), allocated and zeroed (by a
 // kernel on that stream) at the first quantizing call on the stream, kept until
@@ -1018,6 +1184,46 @@ hipError_t mxfp8_t(const T* x, int64_t R, int64_t C, uint8_t* out_row, uint8_t* 
   return hipGetLastError();
 }
 
+template <typename T, typename P, bool E5M2, int MODE>
+void ln_launch(const T* x, int64_t R, int64_t C, const P* g, const P* b, float eps, int margin, float* scale,
+               float* sinv, float* amax, uint8_t* out, float* mu, float* rs, AmaxWork* w, int flags,
+               hipStream_t st) {
+  const auto fn = k_layernorm<T, P, E5M2, MODE>;
+  const int grid = persistent_grid(reinterpret_cast<const void*>(fn), R, kThreads / 64, kCapLn);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), 0, st, x, R, C, g, b, eps, scale, sinv, amax, out, mu, rs,
+                     margin, w, flags);
+}
+
+template <typename T, typename P, bool E5M2>
+hipError_t layernorm_t(const T* x, int64_t R, int64_t C, const P* g, const P* b, float eps, int current,
+                       int margin, float* scale, float* sinv, float* amax, uint8_t* out, float* mu, float* rs,
+                       hipStream_t st) {
+  if (R == 0) {
+    hipLaunchKernelGGL(k_prologue, dim3(1), dim3(1), 0, st, amax, scale, sinv, current ? 0 : 1);
+    if (current)
+      hipLaunchKernelGGL(k_current_scale, dim3(1), dim3(1), 0, st, amax, scale, sinv, Fp8Traits<E5M2>::max,
+                         margin);
+    return hipGetLastError();
+  }
+  AmaxWork* w = amax_work(st);
+  if (w == nullptr) return hipErrorOutOfMemory;
+  if (!current) {
+    ln_launch<T, P, E5M2, 0>(x, R, C, g, b, eps, margin, scale, sinv, amax, out, mu, rs, w, kPublishInv, st);
+  } else {
+    ln_launch<T, P, E5M2, 1>(x, R, C, g, b, eps, margin, scale, sinv, amax, out, mu, rs, w, 0, st);
+    ln_launch<T, P, E5M2, 2>(x, R, C, g, b, eps, margin, scale, sinv, amax, out, mu, rs, w, 0, st);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, typename P>
+hipError_t layernorm_fmt(const T* x, int64_t R, int64_t C, const P* g, const P* b, float eps, int e5m2,
+                         int current, int margin, float* scale, float* sinv, float* amax, uint8_t* out,
+                         float* mu, float* rs, hipStream_t st) {
+  return e5m2 ? layernorm_t<T, P, true>(x, R, C, g, b, eps, current, margin, scale, sinv, amax, out, mu, rs, st)
+              : layernorm_t<T, P, false>(x, R, C, g, b, eps, current, margin, scale, sinv, amax, out, mu, rs, st);
+}
+
 }  // namespace
 
 hipError_t launch_amax_cast(const void* x, int x_dtype, int64_t n, int out_e5m2, int current,
@@ -1058,6 +1264,26 @@ hipError_t launch_mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64
                 : mxfp8_t<uint16_t, false>(static_cast<const uint16_t*>(x), rows, cols, out_row, scale_row, out_col, scale_col, s);
   return e5m2 ? mxfp8_t<float, true>(static_cast<const float*>(x), rows, cols, out_row, scale_row, out_col, scale_col, s)
               : mxfp8_t<float, false>(static_cast<const float*>(x), rows, cols, out_row, scale_row, out_col, scale_col, s);
+}
+
+hipError_t launch_layernorm_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, const void* gamma,
+                                const void* beta, int param_dtype, float eps, int out_e5m2, int current,
+                                int margin, float* scale, float* scale_inv, float* amax, uint8_t* out,
+                                float* mu, float* rsigma, hipStream_t s) {
+  if (x_dtype == BF16) {
+    const auto* xx = static_cast<const uint16_t*>(x);
+    if (param_dtype == BF16)
+      return layernorm_fmt(xx, rows, cols, static_cast<const uint16_t*>(gamma), static_cast<const uint16_t*>(beta),
+                           eps, out_e5m2, current, margin, scale, scale_inv, amax, out, mu, rsigma, s);
+    return layernorm_fmt(xx, rows, cols, static_cast<const float*>(gamma), static_cast<const float*>(beta), eps,
+                         out_e5m2, current, margin, scale, scale_inv, amax, out, mu, rsigma, s);
+  }
+  const auto* xx = static_cast<const float*>(x);
+  if (param_dtype == BF16)
+    return layernorm_fmt(xx, rows, cols, static_cast<const uint16_t*>(gamma), static_cast<const uint16_t*>(beta),
+                         eps, out_e5m2, current, margin, scale, scale_inv, amax, out, mu, rsigma, s);
+  return layernorm_fmt(xx, rows, cols, static_cast<const float*>(gamma), static_cast<const float*>(beta), eps,
+                       out_e5m2, current, margin, scale, scale_inv, amax, out, mu, rsigma, s);
 }
 
 }  // namespace te

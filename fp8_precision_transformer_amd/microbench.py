@@ -204,6 +204,12 @@ def cast(args):
                          device=dev)
         fn = lambda: B.te_cast_transpose_dbias(x, "E5M2", mode, 0, scale, si, am, db, ws, o1, o2)  # noqa: E731
         nbytes = R * C * (6 if mode == B.TE_SCALE_CURRENT else 4) + C * 4
+    elif args.op == "ln":  # LayerNorm over the rows, written as FP8 codes
+        out = torch.empty((R, C), dtype=torch.uint8, device=dev)
+        g = torch.ones(C, device=dev)
+        b = torch.zeros(C, device=dev)
+        fn = lambda: B.te_layernorm_fp8(x, g, b, 1e-5, "E4M3", mode, 0, scale, si, am, out)  # noqa: E731
+        nbytes = R * C * (5 if mode == B.TE_SCALE_CURRENT else 3)
     elif args.op == "mx":  # row-wise copy
         o1 = torch.empty((R, C), dtype=torch.uint8, device=dev)
         s1 = torch.empty((R, C // 32), dtype=torch.uint8, device=dev)
@@ -262,7 +268,7 @@ def main():
     c = sub.add_parser("cast")
     c.add_argument("--rows", type=int, default=15872)
     c.add_argument("--cols", type=int, default=16384)
-    c.add_argument("--op", choices=["cast", "transpose", "both", "bothdbias", "mx", "mxcol", "mxboth"],
+    c.add_argument("--op", choices=["cast", "transpose", "both", "bothdbias", "ln", "mx", "mxcol", "mxboth"],
                    default="cast")
     c.add_argument("--mode", choices=["delayed", "current"], default="delayed")
     c.add_argument("--iters", type=int, default=20)

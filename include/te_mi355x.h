@@ -164,6 +164,38 @@ te_status te_cast_transpose_dbias(const void* x, int x_dtype, int64_t rows, int6
 int64_t te_cast_transpose_dbias_workspace_bytes(int64_t rows, int64_t cols);
 
 /*
+ * te_layernorm_fp8 -- LayerNorm over the last axis, its output written directly as
+ * FP8 codes with per-tensor scaling.
+ *
+ * Defines: te.LayerNorm, the drop-in for nn.LayerNorm(normalized_shape, eps) with
+ * weight and bias ([FP8-intro] "Transformer Engine の使い方": module list;
+ * "HuggingFace BERT を例にした Transformer Engine の適用": the conversion keeps eps,
+ * weight and bias).  Its output is the input of the QKV and MLP-up GEMMs, so the
+ * cast those GEMMs need is done in the normalization pass (one read of x instead of
+ * two, no high-precision output).  Per row r:
+ *   mu = mean_c x[r, c], var = mean_c (x[r, c] - mu)^2 (biased, as nn.LayerNorm),
+ *   rsigma = 1 / sqrt(var + eps),
+ *   y[r, c] = ((x[r, c] - mu) * rsigma) * gamma[c] + beta[c],
+ *   out[r, c] = satRNE(fl32(y[r, c] * scale)),
+ * each step an fp32 operation (sums in a fixed order: reproducible run to run).
+ *
+ *   x          [rows, cols] of x_dtype (TE_F32 or TE_BF16); cols % 16 == 0, cols > 0
+ *              when rows > 0.
+ *   gamma, beta  [cols] of param_dtype (TE_F32 or TE_BF16), 16-byte aligned.
+ *   eps        >= 0.
+ *   out_dtype, mode, margin, scale, scale_inv, amax  as te_amax_cast, with amax the
+ *              max |y| (the tensor that is cast).  TE_SCALE_CURRENT reads x twice
+ *              (statistics and amax, then the cast).
+ *   out        [rows, cols] uint8 codes.
+ *   mu, rsigma [rows] fp32, written (the backward's saved statistics), or NULL.
+ */
+te_status te_layernorm_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                           const void* gamma, const void* beta, int param_dtype, float eps,
+                           int out_dtype, int mode, int margin,
+                           float* scale, float* scale_inv, float* amax,
+                           uint8_t* out, float* mu, float* rsigma, void* stream);
+
+/*
  * te_scale_update -- delayed-scaling update of n tensors of one FP8 format.
  *
  * Defines: [FP8-intro] "Transformer Engine の使い方" (DelayedScaling with
