@@ -30,13 +30,13 @@ TE_OK, TE_ERR_NULL, TE_ERR_SHAPE, TE_ERR_DTYPE, TE_ERR_ALIGN, TE_ERR_UNSUPPORTED
 STATUS_NAMES = ["TE_OK", "TE_ERR_NULL", "TE_ERR_SHAPE", "TE_ERR_DTYPE", "TE_ERR_ALIGN",
                 "TE_ERR_UNSUPPORTED", "TE_ERR_HIP", "TE_ERR_ARG"]
 # te_dtype
-TE_F32, TE_BF16, TE_E4M3, TE_E5M2, TE_E8M0 = range(5)
+TE_F32, TE_BF16, TE_E4M3, TE_E5M2, TE_E8M0, TE_E2M1 = range(6)
 # te_scaling, te_amax_algo, te_granularity
 TE_SCALE_DELAYED, TE_SCALE_CURRENT = 0, 1
 TE_AMAX_MAX, TE_AMAX_MOST_RECENT = 0, 1
 TE_GRAN_TENSOR, TE_GRAN_MX_BLOCK32 = 0, 1
 
-FP8_CODES = {"E4M3": TE_E4M3, "E5M2": TE_E5M2}
+FP8_CODES = {"E4M3": TE_E4M3, "E5M2": TE_E5M2, "E2M1": TE_E2M1}
 
 
 class TEError(RuntimeError):
@@ -62,6 +62,7 @@ _SIGNATURES = {
     "te_fp8_gemm": [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp, _i32, _vp],
     "te_fp8_gemm_accumulate": [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp, _vp],
     "te_mxfp8_quantize": [_vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp],
+    "te_mxfp4_quantize": [_vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
 }
 
 
@@ -208,18 +209,20 @@ def te_scale_update(amax_history, scale, scale_inv, fp8_dtype, algo=TE_AMAX_MAX,
 def te_fp8_gemm(a, a_dtype, a_scale, b, b_dtype, b_scale, d, bias=None, gran=TE_GRAN_TENSOR, stream=None,
                 accumulate=False):
     """D[m, n] = A[m, k] . B[n, k]^T.  a, b: uint8 FP8 codes (or bf16 tensors with
-    a_dtype = b_dtype = "BF16"); a_scale/b_scale: fp32 [1] scale_inv or uint8 E8M0.
+    a_dtype = b_dtype = "BF16", or packed MXFP4 codes [m, k/2], [n, k/2] with
+    a_dtype = b_dtype = "E2M1"); a_scale/b_scale: fp32 [1] scale_inv or uint8 E8M0.
     accumulate=True (fp32 d only) adds the result into d (te_fp8_gemm_accumulate)."""
     for n, t in (("a", a), ("b", b), ("d", d), ("bias", bias), ("a_scale", a_scale), ("b_scale", b_scale)):
         _need(t, n)
-    m, k = a.shape
-    n = b.shape[0]
-    if b.shape[1] != k:
-        raise ValueError(f"k mismatch: a {tuple(a.shape)} b {tuple(b.shape)}")
-    if tuple(d.shape) != (m, n):
-        raise ValueError(f"d must be [{m}, {n}]")
     ad = TE_BF16 if str(a_dtype).upper() == "BF16" else _fp8_code(a_dtype)
     bd = TE_BF16 if str(b_dtype).upper() == "BF16" else _fp8_code(b_dtype)
+    m, kb = a.shape
+    n = b.shape[0]
+    if b.shape[1] != kb:
+        raise ValueError(f"k mismatch: a {tuple(a.shape)} b {tuple(b.shape)}")
+    k = 2 * kb if ad == TE_E2M1 else kb  # E2M1: two elements per byte
+    if tuple(d.shape) != (m, n):
+        raise ValueError(f"d must be [{m}, {n}]")
     dd = _hp_code(d)
     bias_code = _hp_code(bias) if bias is not None else TE_F32
     if accumulate:
@@ -239,6 +242,17 @@ def te_mxfp8_quantize(x, elem_dtype, out_row=None, scale_row=None, out_col=None,
     rows, cols = _2d(x)
     _check(lib().te_mxfp8_quantize(_ptr(x), _hp_code(x), rows, cols, _fp8_code(elem_dtype), _ptr(out_row),
                                    _ptr(scale_row), _ptr(out_col), _ptr(scale_col), _stream(stream)))
+
+
+def te_mxfp4_quantize(x, out_row=None, scale_row=None, out_col=None, scale_col=None, stream=None):
+    """MXFP4 of x: out_row uint8 [rows, cols/2] (two codes per byte) with scale_row
+    [rows, cols/32]; out_col uint8 [cols, rows/2] with scale_col [cols, rows/32]."""
+    for n, t in (("x", x), ("out_row", out_row), ("scale_row", scale_row), ("out_col", out_col),
+                 ("scale_col", scale_col)):
+        _need(t, n)
+    rows, cols = _2d(x)
+    _check(lib().te_mxfp4_quantize(_ptr(x), _hp_code(x), rows, cols, _ptr(out_row), _ptr(scale_row),
+                                   _ptr(out_col), _ptr(scale_col), _stream(stream)))
 
 
 def version() -> str:

@@ -220,14 +220,18 @@ static te_status gemm_impl(const void* a, int a_dtype, const void* a_scale, cons
     return fail(TE_ERR_SHAPE, "n and k must be multiples of 16 (got n=%lld k=%lld)", (long long)n, (long long)k);
   if (gran != TE_GRAN_TENSOR && gran != TE_GRAN_MX_BLOCK32) return fail(TE_ERR_ARG, "bad granularity %d", gran);
   const bool bf16 = a_dtype == TE_BF16 && b_dtype == TE_BF16;
-  if (!bf16 && !(is_fp8(a_dtype) && is_fp8(b_dtype)))
-    return fail(TE_ERR_DTYPE, "a/b dtypes must both be FP8 (E4M3/E5M2) or both TE_BF16 (got %d, %d)", a_dtype, b_dtype);
+  const bool fp4 = a_dtype == TE_E2M1 && b_dtype == TE_E2M1;
+  if (!bf16 && !fp4 && !(is_fp8(a_dtype) && is_fp8(b_dtype)))
+    return fail(TE_ERR_DTYPE, "a/b dtypes must both be FP8 (E4M3/E5M2), both TE_E2M1 or both TE_BF16 (got %d, %d)",
+                a_dtype, b_dtype);
   if (bf16 && gran != TE_GRAN_TENSOR) return fail(TE_ERR_UNSUPPORTED, "BF16 GEMM takes no block scales");
+  if (fp4 && gran != TE_GRAN_MX_BLOCK32) return fail(TE_ERR_UNSUPPORTED, "E2M1 operands need MX block scales");
+  if (fp4 && k % 256 != 0) return fail(TE_ERR_SHAPE, "MXFP4 GEMM needs k %% 256 == 0 (got k=%lld)", (long long)k);
   if (gran == TE_GRAN_MX_BLOCK32 && k % 32 != 0) return fail(TE_ERR_SHAPE, "MX GEMM needs k %% 32 == 0");
   if (d_dtype != TE_BF16 && d_dtype != TE_F32) return fail(TE_ERR_DTYPE, "d_dtype must be TE_BF16 or TE_F32");
   if (bias && bias_dtype != TE_BF16 && bias_dtype != TE_F32) return fail(TE_ERR_DTYPE, "bias_dtype must be TE_BF16 or TE_F32");
   if (m >= (int64_t(1) << 31) || n >= (int64_t(1) << 31)) return fail(TE_ERR_SHAPE, "m and n must be < 2^31");
-  const int64_t kb = k * (bf16 ? 2 : 1);
+  const int64_t kb = fp4 ? k / 2 : k * (bf16 ? 2 : 1);
   if (kb * 256 >= (int64_t(1) << 31)) return fail(TE_ERR_SHAPE, "k too large (256 rows of k must fit 2 GiB)");
   if (m == 0 || n == 0) {
     g_err[0] = '\0';
@@ -303,6 +307,29 @@ te_status te_mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t co
   return hip_status(te::launch_mxfp8_quantize(x, x_dtype, rows, cols, elem_dtype == TE_E5M2, out_row, scale_row,
                                               out_col, scale_col, static_cast<hipStream_t>(stream)),
                     "te_mxfp8_quantize launch");
+}
+
+te_status te_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* out_row,
+                            uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col, void* stream) {
+  if (rows < 0 || cols < 0) return fail(TE_ERR_SHAPE, "negative shape");
+  if (!is_hp(x_dtype)) return fail(TE_ERR_DTYPE, "x_dtype must be TE_F32 or TE_BF16");
+  const bool row = out_row || scale_row, col = out_col || scale_col;
+  if (!row && !col) return fail(TE_ERR_NULL, "both output pairs are NULL");
+  if ((out_row == nullptr) != (scale_row == nullptr)) return fail(TE_ERR_NULL, "out_row and scale_row go together");
+  if ((out_col == nullptr) != (scale_col == nullptr)) return fail(TE_ERR_NULL, "out_col and scale_col go together");
+  if (row && cols % 32 != 0) return fail(TE_ERR_SHAPE, "row-wise MXFP4 needs cols %% 32 == 0");
+  if (col && rows % 32 != 0) return fail(TE_ERR_SHAPE, "column-wise MXFP4 needs rows %% 32 == 0");
+  if (rows * cols > 0 && !x) return fail(TE_ERR_NULL, "x is NULL");
+  if ((x && !aligned16(x)) || (out_row && !aligned16(out_row)) || (out_col && !aligned16(out_col)))
+    return fail(TE_ERR_ALIGN, "x and outputs must be 16-byte aligned");
+  if ((rows + 127) / 128 > 65535) return fail(TE_ERR_SHAPE, "rows too large for the tile grid");
+  te_status st = check_device();
+  if (st != TE_OK) return st;
+  log_dispatch("te_mxfp4_quantize", row && col ? "tile128x64_row+col" : (row ? "tile128x64_row" : "tile128x64_col"),
+               "E2M1");
+  return hip_status(te::launch_mxfp4_quantize(x, x_dtype, rows, cols, out_row, scale_row, out_col, scale_col,
+                                              static_cast<hipStream_t>(stream)),
+                    "te_mxfp4_quantize launch");
 }
 
 }  // extern "C"

@@ -23,6 +23,8 @@
 //   k_gemm   4 waves of 128 x 128, two-stage LDS pipeline with register
 //            staging: MX GEMMs whose k is not a multiple of 128.
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -47,7 +49,7 @@ constexpr int BM = 256, BN = 256, BKB = 128, NT = 256;
 constexpr int kTileBytes = BM * BKB;  // one operand, one stage
 constexpr int kGroupM = 8;            // tile rows per raster group
 
-enum { KIND_FP8 = 0, KIND_MX = 1, KIND_BF16 = 2 };
+enum { KIND_FP8 = 0, KIND_MX = 1, KIND_BF16 = 2, KIND_MX4 = 3 };
 
 struct Params {
   const uint8_t* a;
@@ -368,13 +370,16 @@ constexpr int NT8 = 512;
 
 template <int KIND, int AF, int BF>
 __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
-  constexpr bool MX = KIND == KIND_MX;
+  constexpr bool MX4 = KIND == KIND_MX4;
+  constexpr bool MX = KIND == KIND_MX || MX4;
   // FP8/BF16 (SPLIT): A in two stage slots, B in three, and the two groups share the
   // loads (group 0 A, group 1 B, in their own memory phases).  MX: two slots each, all
-  // loads from group 0, plus per stage slot one dword of four E8M0 block scales per
-  // row of A (1 KB) and of B (1 KB).
+  // loads from group 0, plus per stage slot the E8M0 block scales of the stage's 128
+  // bytes of each row: one dword (four blocks of 32 FP8 elements) per row of A (1 KB)
+  // and of B (1 KB); MXFP4 two dwords (eight blocks of 32 E2M1 elements), kept as
+  // four 1 KB arrays (A dword 0, A dword 1, B dword 0, B dword 1).
   constexpr bool SPLIT = !MX;
-  constexpr int kScOff = 2 * kPB, kScSlot = 2048;
+  constexpr int kScOff = 2 * kPB, kScSlot = MX4 ? 4096 : 2048;
   constexpr int kLds = SPLIT ? kPB + 3 * kPairOp : 2 * kPB + 2 * kScSlot;
   static_assert(kLds <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
@@ -410,8 +415,9 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
   // (j % 8) ^ f(row) = c0 ^ (t & 3) with c0 = (j % 8) ^ (j / 8))
   const int c0 = (lane & 7) ^ (lane >> 3);
   const uint32_t ld_base = static_cast<uint32_t>(q4 * 64 + (lane >> 3)) * static_cast<uint32_t>(p.KB);
-  // MX scales (k % 128 == 0 here): stage st of row r is the dword at r * kblocks + 4 st;
-  // lane l of group-0 wave q4 fetches row 64 q4 + l of A and of B (rows past m or n read 0)
+  // MX scales (k % 128 == 0 here): stage st of row r is the dword at r * kblocks + 4 st
+  // (MXFP4, k % 256 == 0: the two dwords at r * kblocks + 8 st); lane l of group-0 wave
+  // q4 fetches row 64 q4 + l of A and of B (rows past m or n read 0)
   v4i rsSA = {0, 0, 0, 0}, rsSB = {0, 0, 0, 0};
   if constexpr (MX) {
     rsSA = make_rsrc(static_cast<const uint8_t*>(p.a_scale) + static_cast<int64_t>(m0) * p.kblocks,
@@ -425,10 +431,22 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
     const uint32_t kb = static_cast<uint32_t>(st) * PK;
     if constexpr (MX) {
       const int sbase = kScOff + slot * kScSlot + q4 * 256;
-      raw_buffer_load_lds(rsSA, (__attribute__((address_space(3))) uint32_t*)(smem + sbase), 4,
-                          static_cast<int>(sc_off + 4u * st), 0, 0, 0);
-      raw_buffer_load_lds(rsSB, (__attribute__((address_space(3))) uint32_t*)(smem + sbase + 1024), 4,
-                          static_cast<int>(sc_off + 4u * st), 0, 0, 0);
+      if constexpr (MX4) {
+        const uint32_t so = sc_off + 8u * st;
+        raw_buffer_load_lds(rsSA, (__attribute__((address_space(3))) uint32_t*)(smem + sbase), 4,
+                            static_cast<int>(so), 0, 0, 0);
+        raw_buffer_load_lds(rsSA, (__attribute__((address_space(3))) uint32_t*)(smem + sbase + 1024), 4,
+                            static_cast<int>(so + 4u), 0, 0, 0);
+        raw_buffer_load_lds(rsSB, (__attribute__((address_space(3))) uint32_t*)(smem + sbase + 2048), 4,
+                            static_cast<int>(so), 0, 0, 0);
+        raw_buffer_load_lds(rsSB, (__attribute__((address_space(3))) uint32_t*)(smem + sbase + 3072), 4,
+                            static_cast<int>(so + 4u), 0, 0, 0);
+      } else {
+        raw_buffer_load_lds(rsSA, (__attribute__((address_space(3))) uint32_t*)(smem + sbase), 4,
+                            static_cast<int>(sc_off + 4u * st), 0, 0, 0);
+        raw_buffer_load_lds(rsSB, (__attribute__((address_space(3))) uint32_t*)(smem + sbase + 1024), 4,
+                            static_cast<int>(sc_off + 4u * st), 0, 0, 0);
+      }
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -443,7 +461,7 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
                           static_cast<int>(off), 0, 0, 0);
     }
   };
-  constexpr int kLoadsPerStage = MX ? 18 : 16;
+  constexpr int kLoadsPerStage = MX4 ? 20 : (MX ? 18 : 16);
   // SPLIT: one operand of one stage (8 loads per lane), into the slot at byte offset off
   auto issue_op = [&](const v4i& rs, int off_slot, int st) {
     const uint32_t kb = static_cast<uint32_t>(st) * PK;
@@ -461,11 +479,13 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
   auto issue_a = [&](auto SLOT, int st) { issue_op(rsA, decltype(SLOT)::value * kPairOp, st); };
   auto issue_b = [&](int st) { issue_op(rsB, kPB + (st % 3) * kPairOp, st); };
 
-  // A phase covers NH of the stage's two 64-byte k steps: both for FP8 and BF16; one
-  // for MX, whose scaled MFMA needs a fresh accumulator tuple per instruction and so
-  // cannot also hold a whole stage of fragments within 256 registers.
-  constexpr int NH = MX ? 1 : 2;
-  constexpr int PPS = 2 / NH;  // phases per stage and group
+  // A phase covers NH of the stage's k steps (two of 64 bytes for FP8, MX and BF16,
+  // four of 32 bytes for MXFP4): both for FP8 and BF16; one for MX, whose scaled MFMA
+  // needs a fresh accumulator tuple per instruction and so cannot also hold a whole
+  // stage of fragments within 256 registers; two for MXFP4 (half-size fragments).
+  constexpr int KSTEPS = MX4 ? 4 : 2;
+  constexpr int NH = MX4 ? 2 : (MX ? 1 : 2);
+  constexpr int PPS = KSTEPS / NH;  // phases per stage and group
 
   // fragments: A rows wm + 32 i + lr (i < 4), B rows wn + 32 j + lr (j < 2); k step h of
   // the stage uses logical chunks 4h + lk (low 16 bytes) and 4h + 2 + lk (high 16 bytes).
@@ -474,17 +494,36 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
   const int fk = f8(lr);
   const int ra0 = (wm + lr) * PK + ((lk ^ fk) << 4);
   const int rb0 = kPB + (wn + lr) * PK + ((lk ^ fk) << 4);
-  v8i fa[NH][4], fb[NH][2];
+  // MXFP4 fragments: k step h (64 elements, 32 bytes) of a row is logical chunk
+  // 2h + lk, the 32 elements this lane supplies, so one 16-byte read; the matrix core
+  // reads only the first four registers of an E2M1 operand.
+  using Frag = std::conditional_t<MX4, v4u, v8i>;
+  Frag fa[NH][4], fb[NH][2];
   // MX: this lane's block scales for the stage.  A lane supplies the scale of block
   // 2h + lk of its row for k step h; two row groups share a dword: byte 2h + g holds
   // row group 2p + g (A: dwords p = 0, 1; B: one dword for its two row groups).
+  // MXFP4: one dword per row group, byte x4_sel(h) = block 2h + lk of the row.
   uint32_t sa2[2] = {0u, 0u}, sb1 = 0u;
+  uint32_t sa4[4] = {0u, 0u, 0u, 0u}, sb4[2] = {0u, 0u};
   // read the fragments of part P (k steps P*NH ..) of stage st, whose A is in SLOT
   auto read_part = [&](auto SLOT, auto PART, int st) {
     constexpr int slot = decltype(SLOT)::value;
     constexpr int part = decltype(PART)::value;
     const int boff = (SPLIT ? st % 3 : slot) * kPairOp;
-    if constexpr (MX) {
+    if constexpr (MX4) {
+      if constexpr (part == 0) {
+        // dword 0 of a row holds blocks 0-3 of the stage, dword 1 blocks 4-7; keep the
+        // bytes of this lane's blocks: (b lk, b 2+lk, b 4+lk, b 6+lk) -> bytes (0, 2, 1, 3)
+        const uint32_t* sc = reinterpret_cast<const uint32_t*>(smem + kScOff + slot * kScSlot);
+        auto pack4 = [&](uint32_t d0, uint32_t d1) {
+          return ((d0 >> (8 * lk)) & 0x00ff00ffu) | (((d1 >> (8 * lk)) & 0x00ff00ffu) << 8);
+        };
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sa4[i] = pack4(sc[wm + 32 * i + lr], sc[256 + wm + 32 * i + lr]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) sb4[j] = pack4(sc[512 + wn + 32 * j + lr], sc[768 + wn + 32 * j + lr]);
+      }
+    } else if constexpr (MX) {
       if constexpr (part == 0) {
         const uint32_t* sc = reinterpret_cast<const uint32_t*>(smem + kScOff + slot * kScSlot);
         auto pack = [&](uint32_t w0, uint32_t w1) {
@@ -498,6 +537,14 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh) {
       const int h = part * NH + hh;
+      if constexpr (MX4) {
+        const int ao = ra0 ^ (h << 5), bo = rb0 ^ (h << 5);  // logical chunk 2h + lk
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[hh][i] = *reinterpret_cast<const v4u*>(smem + ao + slot * kPairOp + i * 32 * PK);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fb[hh][j] = *reinterpret_cast<const v4u*>(smem + (bo + boff) + j * 32 * PK);
+        continue;
+      }
       const int alo = ra0 ^ (h << 6), ahi = ra0 ^ (h << 6) ^ 32;
       const int blo = rb0 ^ (h << 6), bhi = rb0 ^ (h << 6) ^ 32;
 #pragma unroll
@@ -505,14 +552,14 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
         const int o = slot * kPairOp + i * 32 * PK;
         const v4u lo = *reinterpret_cast<const v4u*>(smem + alo + o);
         const v4u hi = *reinterpret_cast<const v4u*>(smem + ahi + o);
-        fa[hh][i] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        if constexpr (!MX4) fa[hh][i] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int o = j * 32 * PK;
         const v4u lo = *reinterpret_cast<const v4u*>(smem + (blo + boff) + o);
         const v4u hi = *reinterpret_cast<const v4u*>(smem + (bhi + boff) + o);
-        fb[hh][j] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        if constexpr (!MX4) fb[hh][j] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
   };
@@ -530,11 +577,28 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
         a, b, acc[i][j], AF, BF, 2 * h + (i & 1), static_cast<int>(sa2[i >> 1]), 2 * h + j, static_cast<int>(sb1));
   };
+  // MXFP4 MFMA for k step h: E2M1 operands (format 4) in the low four registers
+  auto mfma_x4 = [&](auto H, int i, int j, const v4u& a, const v4u& b) {
+    constexpr int h = decltype(H)::value;
+    constexpr int sel = ((h & 1) << 1) | (h >> 1);
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        __builtin_bit_cast(v8i, __builtin_shufflevector(a, a, 0, 1, 2, 3, 0, 1, 2, 3)),
+        __builtin_bit_cast(v8i, __builtin_shufflevector(b, b, 0, 1, 2, 3, 0, 1, 2, 3)), acc[i][j], 4, 4, sel,
+        static_cast<int>(sa4[i]), sel, static_cast<int>(sb4[j]));
+  };
   auto compute_part = [&](auto PART) {
     constexpr int part = decltype(PART)::value;
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh) {
-      if constexpr (KIND == KIND_BF16) {
+      if constexpr (MX4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            if (hh == 0) mfma_x4(ic<part * NH>{}, i, j, fa[0][i], fb[0][j]);
+            else mfma_x4(ic<part * NH + 1>{}, i, j, fa[1][i], fb[1][j]);
+          }
+      } else if constexpr (KIND == KIND_BF16) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -784,7 +848,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   p.M = static_cast<int>(g.m);
   p.N = static_cast<int>(g.n);
   const int esz = (g.a_fmt == BF16) ? 2 : 1;
-  p.KB = static_cast<int>(g.k * esz);
+  p.KB = static_cast<int>(g.a_fmt == E2M1 ? g.k / 2 : g.k * esz);
   p.KT = (p.KB + BKB - 1) / BKB;
   p.kblocks = static_cast<int>(g.k / 32);
   p.nbm = static_cast<int>((g.m + BM - 1) / BM);
@@ -795,6 +859,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   // f8f6f4 format codes: 0 = E4M3, 1 = E5M2
   const int af = (g.a_fmt == E5M2) ? 1 : 0, bf = (g.b_fmt == E5M2) ? 1 : 0;
   if (g.a_fmt == BF16) return run<KIND_BF16, 0, 0>(p, s, "gemm4_bf16_256x256_pingpong");
+  if (g.a_fmt == E2M1) return run<KIND_MX4, 4, 4>(p, s, "gemm4_mxfp4_e2m1_e2m1_256x256_pingpong");
   if (g.mx) {
     if (af == 0 && bf == 0) return run<KIND_MX, 0, 0>(p, s, "gemm4_mx_e4m3_e4m3_256x256_pingpong");
     if (af == 1 && bf == 0) return run<KIND_MX, 1, 0>(p, s, "gemm4_mx_e5m2_e4m3_256x256_pingpong");

@@ -8,7 +8,7 @@
 namespace te {
 
 // dtype codes mirror te_dtype in te_mi355x.h
-enum : int { F32 = 0, BF16 = 1, E4M3 = 2, E5M2 = 3, E8M0 = 4 };
+enum : int { F32 = 0, BF16 = 1, E4M3 = 2, E5M2 = 3, E8M0 = 4, E2M1 = 5 };
 
 // ---- quantizers (quant.hip) ----
 hipError_t launch_amax_cast(const void* x, int x_dtype, int64_t n, int out_e5m2, int current,
@@ -31,6 +31,8 @@ hipError_t launch_scale_update(float* hist, float* scale, float* scale_inv, int 
 hipError_t launch_mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols,
                                  int e5m2, uint8_t* out_row, uint8_t* scale_row,
                                  uint8_t* out_col, uint8_t* scale_col, hipStream_t s);
+hipError_t launch_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* out_row,
+                                 uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col, hipStream_t s);
 
 // ---- GEMM (gemm.hip) ----
 struct GemmArgs {
@@ -41,7 +43,7 @@ struct GemmArgs {
   const void* bias;
   void* d;
   int64_t m, n, k;       // elements
-  int a_fmt, b_fmt;      // E4M3 / E5M2 / BF16
+  int a_fmt, b_fmt;      // E4M3 / E5M2 / BF16 / E2M1 (MX only, both operands)
   int mx;                // 1: MX block-32 scales
   int bias_bf16;         // bias dtype: 0 f32, 1 bf16
   int d_bf16;            // output dtype: 0 f32, 1 bf16

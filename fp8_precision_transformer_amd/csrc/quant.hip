@@ -856,6 +856,108 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8(const T* __restrict__ x, int
 }
 
 // ----------------------------------------------------------------------------
+// MXFP4: E2M1 elements with one E8M0 exponent per 32 elements, two codes per byte
+// (element 2i in the low nibble).  Block exponent e = floor(log2 amax) - 2 (4 is the
+// largest E2M1 power of two), clamped to [-127, 127], 127 for an infinite amax; a
+// block holding a NaN takes scale code 255 and is cast with e = 0 (E2M1 has no NaN
+// code: a NaN element becomes +0).  Elements round to nearest, ties to the even
+// mantissa, and saturate at 6.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+  const float a = __builtin_fabsf(y);
+  // midpoints between the magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; on a midpoint the
+  // neighbour with the even mantissa (0, 1, 2, 4) wins, hence > or >=
+  const uint32_t c = static_cast<uint32_t>(a > 0.25f) + static_cast<uint32_t>(a >= 0.75f) +
+                     static_cast<uint32_t>(a > 1.25f) + static_cast<uint32_t>(a >= 1.75f) +
+                     static_cast<uint32_t>(a > 2.5f) + static_cast<uint32_t>(a >= 3.5f) +
+                     static_cast<uint32_t>(a > 5.0f);
+  const uint32_t neg = (__float_as_uint(y) >> 31) & static_cast<uint32_t>(a == a);  // NaN -> +0
+  return c | (neg << 3);
+}
+
+// exponent of a block whose amax magnitude bits are mb (finite or infinite)
+__device__ __forceinline__ int mx4_exponent(uint32_t mb) {
+  if (mb == 0u) return 0;
+  if (mb >= 0x7f800000u) return 127;
+  const int E = static_cast<int>(mb >> 23);
+  const int fl = E ? E - 127 : (31 - __clz(static_cast<int>(mb))) - 149;
+  const int e = fl - 2;
+  return e < -127 ? -127 : e;
+}
+
+// 32 values -> 16 bytes of packed codes (q[w] holds elements 8w .. 8w + 7) and the code
+__device__ __forceinline__ void mx4_block32(const float* v, uint32_t* q, uint8_t* code) {
+  uint32_t mb = 0u;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) mb = max(mb, __float_as_uint(v[j]) & 0x7fffffffu);
+  const bool nan = mb > 0x7f800000u;
+  const int e = nan ? 0 : mx4_exponent(mb);
+  *code = nan ? static_cast<uint8_t>(255) : static_cast<uint8_t>(e + 127);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t d = 0u;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) d |= e2m1_code(__builtin_ldexpf(v[8 * w + n], -e)) << (4 * n);
+    q[w] = d;
+  }
+}
+
+// Tiles of 128 rows x 64 columns, a thread per 32-element row block (row-wise copy)
+// and, through LDS, per 32-element column block (column-wise copy), as k_mxfp8.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_mxfp4(const T* __restrict__ x, int64_t R, int64_t C,
+                                                    uint8_t* __restrict__ out_row,
+                                                    uint8_t* __restrict__ scale_row,
+                                                    uint8_t* __restrict__ out_col,
+                                                    uint8_t* __restrict__ scale_col) {
+  __shared__ float tile[kTR * kMxPitch];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kTR;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kTC;
+  const int t = threadIdx.x;
+  const int lr = t >> 1, lc = (t & 1) * 32;
+  const int64_t r = r0 + lr;
+  const bool full = (r0 + kTR <= R) && (c0 + kTC <= C);
+
+  float v[32];
+  if (full && rows_vec_ok<T>(C)) {
+    const T* p = x + r * C + c0 + lc;
+    In<T>::load16(p, v);
+    In<T>::load16(p + 16, v + 16);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int64_t c = c0 + lc + j;
+      v[j] = (r < R && c < C) ? In<T>::load1(x + r * C + c) : 0.0f;
+    }
+  }
+  if (out_row != nullptr && r < R && c0 + lc < C) {  // cols % 32 == 0: whole blocks
+    uint32_t q[4];
+    uint8_t code;
+    mx4_block32(v, q, &code);
+    *reinterpret_cast<uint4*>(out_row + r * (C / 2) + (c0 + lc) / 2) = make_uint4(q[0], q[1], q[2], q[3]);
+    scale_row[r * (C / 32) + (c0 + lc) / 32] = code;
+  }
+  if (out_col != nullptr) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) tile[lr * kMxPitch + lc + j] = v[j];
+    __syncthreads();
+    const int oc = t & 63, seg = t >> 6;
+    const int64_t c = c0 + oc;
+    const int64_t rb = r0 + seg * 32;
+    if (c < C && rb < R) {  // rows % 32 == 0: whole blocks
+      float w[32];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) w[j] = tile[(seg * 32 + j) * kMxPitch + oc];
+      uint32_t q[4];
+      uint8_t code;
+      mx4_block32(w, q, &code);
+      *reinterpret_cast<uint4*>(out_col + c * (R / 2) + rb / 2) = make_uint4(q[0], q[1], q[2], q[3]);
+      scale_col[c * (R / 32) + rb / 32] = code;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // MXFP8, bf16 input, whole 128 x 128 tiles (rows and cols multiples of 128):
 // persistent blocks, the next tile's loads in flight, as the cast-transpose.
 // Row-wise: a 32-element block of a row is 4 lanes x 8 elements; its amax is a
@@ -1264,6 +1366,19 @@ hipError_t launch_mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64
                 : mxfp8_t<uint16_t, false>(static_cast<const uint16_t*>(x), rows, cols, out_row, scale_row, out_col, scale_col, s);
   return e5m2 ? mxfp8_t<float, true>(static_cast<const float*>(x), rows, cols, out_row, scale_row, out_col, scale_col, s)
               : mxfp8_t<float, false>(static_cast<const float*>(x), rows, cols, out_row, scale_row, out_col, scale_col, s);
+}
+
+hipError_t launch_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* out_row,
+                                 uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col, hipStream_t s) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((cols + kTC - 1) / kTC), static_cast<unsigned>((rows + kTR - 1) / kTR));
+  if (x_dtype == BF16)
+    hipLaunchKernelGGL(k_mxfp4<uint16_t>, grid, dim3(kThreads), 0, s, static_cast<const uint16_t*>(x), rows, cols,
+                       out_row, scale_row, out_col, scale_col);
+  else
+    hipLaunchKernelGGL(k_mxfp4<float>, grid, dim3(kThreads), 0, s, static_cast<const float*>(x), rows, cols, out_row,
+                       scale_row, out_col, scale_col);
+  return hipGetLastError();
 }
 
 hipError_t launch_layernorm_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, const void* gamma,

@@ -51,7 +51,11 @@ def gemm(args):
         b = (torch.randint(0x18, 0x48, (n, k), device=dev, generator=g, dtype=torch.int32) |
              (torch.randint(0, 2, (n, k), device=dev, generator=g, dtype=torch.int32) << 7)).to(torch.uint8)
         fa, fb = args.fa, args.fb
-        if args.kind == "mx":
+        if args.kind == "mx4":  # packed E2M1 pairs: every byte is a valid pair of codes
+            a = torch.randint(0, 256, (m, k // 2), device=dev, generator=g, dtype=torch.int32).to(torch.uint8)
+            b = torch.randint(0, 256, (n, k // 2), device=dev, generator=g, dtype=torch.int32).to(torch.uint8)
+            fa = fb = "E2M1"
+        if args.kind in ("mx", "mx4"):
             sa = torch.full((m, k // 32), 127, dtype=torch.uint8, device=dev)
             sb = torch.full((n, k // 32), 127, dtype=torch.uint8, device=dev)
             gran = B.TE_GRAN_MX_BLOCK32
@@ -220,6 +224,14 @@ def cast(args):
         s2 = torch.empty((C, R // 32), dtype=torch.uint8, device=dev)
         fn = lambda: B.te_mxfp8_quantize(x, "E4M3", None, None, o2, s2)  # noqa: E731
         nbytes = R * C * 3 + R * C // 32
+    elif args.op.startswith("mx4"):  # MXFP4: row-wise, column-wise or both copies
+        row, col = args.op in ("mx4", "mx4both"), args.op in ("mx4col", "mx4both")
+        o1 = torch.empty((R, C // 2), dtype=torch.uint8, device=dev) if row else None
+        s1 = torch.empty((R, C // 32), dtype=torch.uint8, device=dev) if row else None
+        o2 = torch.empty((C, R // 2), dtype=torch.uint8, device=dev) if col else None
+        s2 = torch.empty((C, R // 32), dtype=torch.uint8, device=dev) if col else None
+        fn = lambda: B.te_mxfp4_quantize(x, o1, s1, o2, s2)  # noqa: E731
+        nbytes = R * C * 2 + (int(row) + int(col)) * (R * C // 2 + R * C // 32)
     else:  # mxboth
         o1 = torch.empty((R, C), dtype=torch.uint8, device=dev)
         s1 = torch.empty((R, C // 32), dtype=torch.uint8, device=dev)
@@ -259,7 +271,7 @@ def main():
     g.add_argument("--m", type=int, default=15872)
     g.add_argument("--n", type=int, default=12288)
     g.add_argument("--k", type=int, default=4096)
-    g.add_argument("--kind", choices=["fp8", "mx", "bf16"], default="fp8")
+    g.add_argument("--kind", choices=["fp8", "mx", "mx4", "bf16"], default="fp8")
     g.add_argument("--fa", default="E4M3")
     g.add_argument("--fb", default="E4M3")
     g.add_argument("--out", choices=["bf16", "f32"], default="bf16")
@@ -268,7 +280,8 @@ def main():
     c = sub.add_parser("cast")
     c.add_argument("--rows", type=int, default=15872)
     c.add_argument("--cols", type=int, default=16384)
-    c.add_argument("--op", choices=["cast", "transpose", "both", "bothdbias", "ln", "mx", "mxcol", "mxboth"],
+    c.add_argument("--op", choices=["cast", "transpose", "both", "bothdbias", "ln", "mx", "mxcol", "mxboth", "mx4",
+                                    "mx4col", "mx4both"],
                    default="cast")
     c.add_argument("--mode", choices=["delayed", "current"], default="delayed")
     c.add_argument("--iters", type=int, default=20)

@@ -67,7 +67,8 @@ typedef enum {
   TE_ERR_ARG = 7          /* an enum or scalar argument is out of range */
 } te_status;
 
-typedef enum { TE_F32 = 0, TE_BF16 = 1, TE_E4M3 = 2, TE_E5M2 = 3, TE_E8M0 = 4 } te_dtype;
+/* TE_E2M1: 4-bit MXFP4 elements, two per byte (element 2i in the low nibble). */
+typedef enum { TE_F32 = 0, TE_BF16 = 1, TE_E4M3 = 2, TE_E5M2 = 3, TE_E8M0 = 4, TE_E2M1 = 5 } te_dtype;
 
 /* [FP8-intro] "FP8 Training について": one scale per tensor, refreshed every step.
  * DELAYED: the scale comes from the amax history of earlier steps
@@ -231,6 +232,10 @@ te_status te_scale_update(float* amax_history, float* scale, float* scale_inv,
  *   gran = TE_GRAN_MX_BLOCK32: a_scale uint8 E8M0 [m, k/32], b_scale uint8 E8M0
  *              [n, k/32] (row-major); element formats E4M3/E5M2;
  *              D = sum_blocks 2^(ea-127) 2^(eb-127) (block dot) + bias.  k % 32 == 0.
+ *              MXFP4: a_dtype = b_dtype = TE_E2M1, a and b packed [m, k/2] and
+ *              [n, k/2] bytes, same scale arrays, k % 256 == 0 ([LP-opt]
+ *              "実モデルにおける結果の解釈": FP4 GEMMs against MXFP8 on the same
+ *              shapes; the matrix core applies E8M0 scales per 32 elements).
  *   acc        fp32 accumulation on the matrix cores.
  *   bias       [n] of bias_dtype (TE_F32 or TE_BF16, widened to fp32) or NULL.
  *   d          [m, n] of d_dtype (TE_BF16, rounded to nearest even, or TE_F32).
@@ -284,6 +289,30 @@ te_status te_fp8_gemm_accumulate(const void* a, int a_dtype, const void* a_scale
  */
 te_status te_mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols,
                             int elem_dtype, uint8_t* out_row, uint8_t* scale_row,
+                            uint8_t* out_col, uint8_t* scale_col, void* stream);
+
+/*
+ * te_mxfp4_quantize -- MXFP4 block quantization (E2M1 elements, E8M0 per 32),
+ * row-wise and/or column-wise.
+ *
+ * Defines: [LP-opt] "実モデルにおける結果の解釈" (FP4 block-scaled GEMMs compared
+ * with MXFP8) and the MXFP8 block rule of te_mxfp8_quantize with 4-bit elements
+ * (OCP MX v1.0 reading): for 32 consecutive elements, e = floor(log2(max|x|)) - 2,
+ * clamped to [-127, 127] (127 for an infinite max), scale code e + 127 (127 for an
+ * all-zero block); elements = E2M1 of x * 2^-e, rounded to nearest with ties to the
+ * even mantissa and saturated at +-6, sign of zero kept.  A block holding a NaN gets
+ * scale code 255 and is cast with e = 0, its NaN elements becoming +0.
+ *
+ *   x          [rows, cols] of x_dtype (TE_F32 or TE_BF16).
+ *   out_row    [rows, cols/2] uint8, two codes per byte, blocks along cols;
+ *              scale_row [rows, cols/32] E8M0.
+ *   out_col    [cols, rows/2] uint8 = MXFP4 of x^T (an independent quantization
+ *              with blocks along rows); scale_col [cols, rows/32] E8M0.
+ * Either pair may be NULL (not both).  Row pair needs cols % 32 == 0; col pair
+ * needs rows % 32 == 0.  x and the code outputs 16-byte aligned.
+ */
+te_status te_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                            uint8_t* out_row, uint8_t* scale_row,
                             uint8_t* out_col, uint8_t* scale_col, void* stream);
 
 /* Text of the last error on the calling thread ("" if none).  Host pointer owned

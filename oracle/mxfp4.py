@@ -16,7 +16,8 @@ with 4-bit elements.  Readings (listed in the design doc):
     saturates at +-6; the sign of zero is kept;
   * block scale as in MXFP8: e = floor(log2(amax)) - 2 (6 = 1.5 * 2^2), clamped
     to [-127, 127], code e + 127, 127 for an all-zero block; elements
-    satRNE(x * 2^-e);
+    satRNE(x * 2^-e); an infinite amax has log2 = +inf, so e = 127 (code 254),
+    its infinities saturate to +-6 and the block's finite elements go to 0;
   * a block holding a NaN gets the NaN scale code 255 (E2M1 has no NaN, so the
     scale carries it) and its elements are cast with e = 0, NaN to +0;
   * two codes per byte, element 2i in the low nibble, 2i + 1 in the high one.
@@ -84,8 +85,10 @@ def mxfp4_quantize(x):
     xb = x32.reshape(R, C // BLOCK, BLOCK).astype(np.float64)
     nan = np.any(np.isnan(xb), axis=2)
     am = np.max(np.where(np.isnan(xb), 0.0, np.abs(xb)), axis=2)
-    _, fe = np.frexp(np.where(am > 0, am, 1.0))
+    fin = np.isfinite(am)
+    _, fe = np.frexp(np.where((am > 0) & fin, am, 1.0))
     e = np.where(am > 0, fe.astype(np.int64) - 1 - 2, 0)
+    e = np.where(fin, e, 127)                          # log2 of an infinite amax is +inf
     e = np.where(nan, 0, np.clip(e, -127, 127))
     scale_codes = np.where(nan, 255, e + 127).astype(np.uint8)
     scaled = np.ldexp(xb, (-e)[:, :, None].astype(np.int32))

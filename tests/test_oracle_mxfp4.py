@@ -47,13 +47,16 @@ def test_block_scales_closed_form():
     x[1, 5] = 1.0                      # amax 1 = 2^0 -> e = -2
     x[1, 40] = -3.0 * 2.0 ** -130      # tiny -> clamped to -127
     x[2, 7] = np.nan
+    x[2, 40] = -np.inf                 # infinite amax -> e = 127 (code 254)
+    x[2, 41] = 1.0e30                  # finite, 1e30 * 2^-127 < 0.25 -> 0
     q, e = F.mxfp4_quantize(x)
     np.testing.assert_array_equal(e[0], [132, 127])
-    assert e[1, 0] == 125 and e[1, 1] == 0 and e[2, 0] == 255
+    assert e[1, 0] == 125 and e[1, 1] == 0 and e[2, 0] == 255 and e[2, 1] == 254
     codes = F.unpack(q)
     assert np.all(F.e2m1_decode_table()[codes[0, :32]] == 6.0)
     assert F.e2m1_decode_table()[codes[1, 5]] == 4.0   # 1 * 2^2
     assert codes[2, 7] == 0
+    assert codes[2, 40] == 15 and codes[2, 41] == 0   # -6 and +0
 
 
 def test_pack_layout():
