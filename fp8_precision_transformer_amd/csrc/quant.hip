@@ -885,6 +885,26 @@ __device__ __forceinline__ int mx4_exponent(uint32_t mb) {
   return e < -127 ? -127 : e;
 }
 
+// Eight values (already scaled by 2^-e) -> one dword of codes, value j in nibble j.
+// The gfx950 conversion rounds to nearest even, saturates at 6 and keeps the sign of
+// zero exactly as e2m1_code does, but turns a NaN into +-6: blocks holding a NaN take
+// e2m1_code instead.
+__device__ __forceinline__ uint32_t e2m1_pack8(const float* w) {
+  uint32_t d = 0u;
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, w[0], w[1], 1.0f, 0);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, w[2], w[3], 1.0f, 1);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, w[4], w[5], 1.0f, 2);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, w[6], w[7], 1.0f, 3);
+  return d;
+}
+
+__device__ __forceinline__ uint32_t e2m1_pack8_slow(const float* w) {
+  uint32_t d = 0u;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) d |= e2m1_code(w[n]) << (4 * n);
+  return d;
+}
+
 // 32 values -> 16 bytes of packed codes (q[w] holds elements 8w .. 8w + 7) and the code
 __device__ __forceinline__ void mx4_block32(const float* v, uint32_t* q, uint8_t* code) {
   uint32_t mb = 0u;
@@ -895,10 +915,10 @@ __device__ __forceinline__ void mx4_block32(const float* v, uint32_t* q, uint8_t
   *code = nan ? static_cast<uint8_t>(255) : static_cast<uint8_t>(e + 127);
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    uint32_t d = 0u;
+    float y[8];
 #pragma unroll
-    for (int n = 0; n < 8; ++n) d |= e2m1_code(__builtin_ldexpf(v[8 * w + n], -e)) << (4 * n);
-    q[w] = d;
+    for (int n = 0; n < 8; ++n) y[n] = __builtin_ldexpf(v[8 * w + n], -e);
+    q[w] = nan ? e2m1_pack8_slow(y) : e2m1_pack8(y);
   }
 }
 
@@ -970,6 +990,7 @@ __global__ __launch_bounds__(kThreads) void k_mxfp4(const T* __restrict__ x, int
 // ----------------------------------------------------------------------------
 constexpr int kMxTPitch = 272;  // LDS bytes per tile row (128 bf16 + 16)
 constexpr int kMxQPitch = 144;  // LDS bytes per staged output row (128 codes + 16)
+constexpr int kMx4QPitch = 80;  // MXFP4: 64 bytes of packed codes + 16
 static_assert(kCT * kMxQPitch + 4 * kCT <= kCT * kMxTPitch, "column staging reuses the tile");
 
 template <bool E5M2>
@@ -983,7 +1004,9 @@ __device__ __forceinline__ void mx_quant8(const uint4& raw, int e, uint32_t& q0,
   q1 = cvt4<E5M2>(w[4], w[5], w[6], w[7]);
 }
 
-template <bool E5M2, bool ROW, bool COL>
+// FP4: the same tiles written as MXFP4 (four bytes of codes per lane and pass for the
+// row-wise copy, 64 bytes per column of the tile for the column-wise one).
+template <bool E5M2, bool ROW, bool COL, bool FP4 = false>
 __global__ __launch_bounds__(kThreads) void k_mxfp8_tiles(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                           uint8_t* __restrict__ out_row,
                                                           uint8_t* __restrict__ scale_row,
@@ -1020,12 +1043,25 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_tiles(const uint16_t* __rest
         m = max(m & 0xffffu, m >> 16);
         m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 1, 64)));
         m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 2, 64)));
-        const int e = mx_exponent<E5M2>(__uint_as_float(m << 16));
-        uint32_t q0, q1;
-        mx_quant8<E5M2>(raw[p], e, q0, q1);
         const int64_t r = r0 + lr;
-        *reinterpret_cast<uint2*>(out_row + r * C + c0 + pcol) = make_uint2(q0, q1);
-        const uint32_t code = static_cast<uint32_t>(e + 127);
+        uint32_t code;
+        if constexpr (FP4) {
+          const bool nan = m > 0x7f80u;
+          const int e = nan ? 0 : mx4_exponent(m << 16);
+          float v[8];
+          unpack16<uint16_t>(raw[p], v);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = __builtin_ldexpf(v[j], -e);
+          *reinterpret_cast<uint32_t*>(out_row + r * (C / 2) + (c0 + pcol) / 2) =
+              nan ? e2m1_pack8_slow(v) : e2m1_pack8(v);
+          code = nan ? 255u : static_cast<uint32_t>(e + 127);
+        } else {
+          const int e = mx_exponent<E5M2>(__uint_as_float(m << 16));
+          uint32_t q0, q1;
+          mx_quant8<E5M2>(raw[p], e, q0, q1);
+          *reinterpret_cast<uint2*>(out_row + r * C + c0 + pcol) = make_uint2(q0, q1);
+          code = static_cast<uint32_t>(e + 127);
+        }
         const uint32_t k1 = static_cast<uint32_t>(__shfl(static_cast<int>(code), lane + 4, 64));
         const uint32_t k2 = static_cast<uint32_t>(__shfl(static_cast<int>(code), lane + 8, 64));
         const uint32_t k3 = static_cast<uint32_t>(__shfl(static_cast<int>(code), lane + 12, 64));
@@ -1051,6 +1087,48 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_tiles(const uint16_t* __rest
       uint32_t mm = 0u;
 #pragma unroll
       for (int k = 0; k < 32; ++k) mm = absmax_bits<uint16_t>(mm, make_uint4(d[k], 0u, 0u, 0u));
+      if constexpr (FP4) {
+        uint32_t q[2][4], code[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {  // h = 0: column 2cp (low halves), 1: column 2cp + 1
+          const uint32_t m = h ? (mm >> 16) : (mm & 0xffffu);
+          const bool nan = m > 0x7f80u;
+          const int e = nan ? 0 : mx4_exponent(m << 16);
+          code[h] = nan ? 255u : static_cast<uint32_t>(e + 127);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float w[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const uint32_t b = h ? (d[8 * g + j] & 0xffff0000u) : (d[8 * g + j] << 16);
+              w[j] = __builtin_ldexpf(__uint_as_float(b), -e);
+            }
+            q[h][g] = nan ? e2m1_pack8_slow(w) : e2m1_pack8(w);
+          }
+        }
+        // stage the packed column blocks (Q[col][row / 2], pitch 80) and the codes, then
+        // write each column's 64 bytes and one code dword per column
+        __syncthreads();  // every thread has read its column pair
+        uint8_t* qt = tile;
+        uint8_t* qs = tile + kCT * kMx4QPitch;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          *reinterpret_cast<uint4*>(qt + (2 * cp + h) * kMx4QPitch + 16 * blk) =
+              make_uint4(q[h][0], q[h][1], q[h][2], q[h][3]);
+          qs[(2 * cp + h) * 4 + blk] = static_cast<uint8_t>(code[h]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int c = (t >> 2) + 64 * k, chunk = t & 3;
+          const uint4 v = *reinterpret_cast<const uint4*>(qt + c * kMx4QPitch + 16 * chunk);
+          *reinterpret_cast<uint4*>(out_col + (c0 + c) * (R / 2) + r0 / 2 + 16 * chunk) = v;
+        }
+        if (t < kCT)
+          *reinterpret_cast<uint32_t*>(scale_col + (c0 + t) * (R / 32) + r0 / 32) =
+              *reinterpret_cast<const uint32_t*>(qs + 4 * t);
+        return;
+      }
       uint32_t q[2][8];
       int e[2];
 #pragma unroll
@@ -1255,10 +1333,10 @@ hipError_t cast_transpose_t(const T* x, int64_t R, int64_t C, int current, int m
   return hipGetLastError();
 }
 
-template <bool E5M2, bool ROW, bool COL>
+template <bool E5M2, bool ROW, bool COL, bool FP4 = false>
 void mx_tiles_launch(const uint16_t* x, int64_t R, int64_t C, uint8_t* out_row, uint8_t* scale_row,
                      uint8_t* out_col, uint8_t* scale_col, hipStream_t st) {
-  const auto fn = k_mxfp8_tiles<E5M2, ROW, COL>;
+  const auto fn = k_mxfp8_tiles<E5M2, ROW, COL, FP4>;
   const int g = persistent_grid(reinterpret_cast<const void*>(fn), (R / kCT) * (C / kCT), 1, COL ? kCapMxCol : kCapMxRow);
   hipLaunchKernelGGL(fn, dim3(g), dim3(kThreads), 0, st, x, R, C, out_row, scale_row, out_col, scale_col);
 }
@@ -1371,6 +1449,17 @@ hipError_t launch_mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64
 hipError_t launch_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* out_row,
                                  uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col, hipStream_t s) {
   if (rows == 0 || cols == 0) return hipSuccess;
+  // bf16 matrices of whole 128 x 128 tiles: the persistent tile kernel, as for MXFP8
+  const bool row = out_row != nullptr, col = out_col != nullptr;
+  if (x_dtype == BF16 && rows % kCT == 0 && cols % kCT == 0 && cols * kCT * 2 < (int64_t{1} << 31) &&
+      rows * kCT < (int64_t{1} << 31) && (!row || (reinterpret_cast<uintptr_t>(scale_row) & 3u) == 0) &&
+      (!col || (reinterpret_cast<uintptr_t>(scale_col) & 3u) == 0)) {
+    const auto* xx = static_cast<const uint16_t*>(x);
+    if (row && col) mx_tiles_launch<false, true, true, true>(xx, rows, cols, out_row, scale_row, out_col, scale_col, s);
+    else if (row) mx_tiles_launch<false, true, false, true>(xx, rows, cols, out_row, scale_row, out_col, scale_col, s);
+    else mx_tiles_launch<false, false, true, true>(xx, rows, cols, out_row, scale_row, out_col, scale_col, s);
+    return hipGetLastError();
+  }
   const dim3 grid(static_cast<unsigned>((cols + kTC - 1) / kTC), static_cast<unsigned>((rows + kTR - 1) / kTR));
   if (x_dtype == BF16)
     hipLaunchKernelGGL(k_mxfp4<uint16_t>, grid, dim3(kThreads), 0, s, static_cast<const uint16_t*>(x), rows, cols,

@@ -54,7 +54,9 @@ def _check_quant(got, x32, row=True, col=True):
         np.testing.assert_array_equal(got["qT"], qT)
 
 
-# tiles are 128 rows x 64 columns: ragged in both directions, one tile, several
+# fp32 input and bf16 input of ragged shape take 128 x 64 tiles (ragged in both
+# directions, one tile, several); bf16 input of whole 128 x 128 tiles takes the
+# persistent tile kernel (256 x 384, 1024 x 768)
 QUANT_SHAPES = [(32, 32), (128, 64), (160, 96), (256, 384), (416, 1088), (1024, 768)]
 
 
@@ -68,18 +70,21 @@ def test_mxfp4_quantize_parity(shape, dtype):
 
 
 @pytest.mark.parametrize("which", ["row", "col"])
-def test_mxfp4_quantize_one_direction(which):
-    r, c = 192, 320
+@pytest.mark.parametrize("shape", [(192, 320), (256, 512)], ids=str)
+def test_mxfp4_quantize_one_direction(which, shape):
+    r, c = shape
     x = synth.grads((r, c), 31, 7, 0, 0)
     xd, x32 = input_pair(x, "bf16")
     row, col = which == "row", which == "col"
     _check_quant(_quantize_gpu(xd, r, c, row, col), x32, row, col)
 
 
-def test_mxfp4_quantize_special_blocks():
-    """All-zero, NaN, +-inf, ties at several block scales, fp32 subnormals, -0."""
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mxfp4_quantize_special_blocks(dtype):
+    """All-zero, NaN, +-inf, ties at several block scales, subnormals, -0; NaN and
+    infinities in the column-wise blocks too."""
     rng = np.random.default_rng(5)
-    r, c = 64, 256
+    r, c = 128, 256
     x = (rng.standard_normal((r, c)) * 3).astype(np.float32)
     x[0, 0:32] = 0.0
     x[0, 32:64] = -0.0
@@ -97,10 +102,13 @@ def test_mxfp4_quantize_special_blocks():
     x[10, :32] = np.float32(2.0 ** -140) * np.arange(1, 33, dtype=np.float32)   # fp32 subnormals
     x[11, :32] = np.float32(3.0e38)
     x[12, 96:128] = -np.float32(1e-30)
-    xd = dev_f32(x)
-    _check_quant(_quantize_gpu(xd, r, c), x)
+    x[100, 200] = np.nan
+    x[70:90, 150] = -np.inf
+    xd, x32 = input_pair(x, dtype)
     got = _quantize_gpu(xd, r, c)
+    _check_quant(got, x32)
     assert got["e"][1, 0] == 255 and got["e"][2, 1] == 254 and got["e"][0, 0] == 127
+    assert got["eT"][200, 3] == 255 and got["eT"][150, 2] == 254
 
 
 def test_mxfp4_quantize_bad_shapes():
