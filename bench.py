@@ -12,6 +12,9 @@ One step = one pass of the whole path over the layer in every mode:
   fp8_current_prequant operands quantized once before timing; GEMM kernels only
   mxfp8_autocast       MXFP8 1x32 quantization before each GEMM + MX GEMM
   mxfp8_prequant       MX GEMM kernels only
+  mxfp4_autocast       MXFP4 (E2M1 elements, E8M0 per 32) quantization before each
+                       GEMM + the E2M1 x E2M1 scaled-MFMA GEMM
+  mxfp4_prequant       MXFP4 GEMM kernels only
 Delayed scaling has no pre-quantize number of its own: it relies on the amax
 history, so the page keeps it in autocast mode even with --pre-quantize.
 
@@ -36,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 MI355X_FP8_PEAK_TFLOPS = 5000.0   # dense FP8 MFMA (published)
 MI355X_BF16_PEAK_TFLOPS = 2500.0  # dense BF16 MFMA (published)
+MI355X_FP4_PEAK_TFLOPS = 10100.0  # dense FP4 / FP6 MFMA (published)
 MI355X_HBM_GBS = 8000.0           # HBM3E (published)
 
 # HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per
@@ -45,8 +49,12 @@ MI355X_HBM_GBS = 8000.0           # HBM3E (published)
 MEASURED_TRAFFIC = {
     # FP8 GEMM: mean over the layer's 12 GEMM launches (microbench layer --kind fp8)
     "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                 "sha256": "60cd38c331d109a08cb76713c4ce75bccf8fbc152b94c136acf1829c36b695f4",
-                 "bytes_per_launch": 1516034243},
+                 "sha256": "b20777d0266a3fd06616f96a48882e67382d93f4d34f99aec33f1f634fe4539a",
+                 "bytes_per_launch": 1518914990},
+    # MXFP4 GEMM: the same 12 shapes (microbench layer --kind mx4)
+    "gemm_mxfp4": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
+                   "sha256": "b20777d0266a3fd06616f96a48882e67382d93f4d34f99aec33f1f634fe4539a",
+                   "bytes_per_launch": 894394325},
 }
 
 
@@ -156,9 +164,22 @@ def main():
 
     MXB = mx_buffers()
 
+    # MXFP4 buffers: two E2M1 codes per byte, E8M0 per 32 elements
+    def mx4_buffers():
+        mb = {}
+        for w in weights:
+            K, N = w.in_features, w.out_features
+            mb[w.name] = dict(
+                x=u8(M, K // 2), xs=u8(M, K // 32), xT=u8(K, M // 2), xTs=u8(K, M // 32),
+                w=u8(N, K // 2), ws=u8(N, K // 32), wT=u8(K, N // 2), wTs=u8(K, N // 32),
+                dy=u8(M, N // 2), dys=u8(M, N // 32), dyT=u8(N, M // 2), dyTs=u8(N, M // 32))
+        return mb
+
     modes_all = ["bf16", "fp8_delayed_autocast", "fp8_current_autocast", "fp8_current_prequant",
-                 "mxfp8_autocast", "mxfp8_prequant", "fp8_delayed_shared", "fp8_current_shared", "mxfp8_shared"]
+                 "mxfp8_autocast", "mxfp8_prequant", "fp8_delayed_shared", "fp8_current_shared", "mxfp8_shared",
+                 "mxfp4_autocast", "mxfp4_prequant"]
     modes = modes_all if args.modes == "all" else args.modes.split(",")
+    MX4B = mx4_buffers() if "mxfp4_autocast" in modes else None
     if "bf16" in modes:
         for w in weights:
             BT[w.name] = dict(wT=W[w.name].t().contiguous(), xT=X[w.name].t().contiguous(),
@@ -207,18 +228,35 @@ def main():
         B.te_mxfp8_quantize(X[w.name], E4, None, None, b["xT"], b["xTs"])
         return (b["dyT"], b["dyTs"], b["xT"], b["xTs"])
 
-    prequant_fp8, prequant_mx = {}, {}
+    def quant_mx4(w, stage, bset=None):
+        b = (bset or MX4B)[w.name]
+        if stage == "fprop":
+            B.te_mxfp4_quantize(X[w.name], b["x"], b["xs"])
+            B.te_mxfp4_quantize(W[w.name], b["w"], b["ws"])
+            return (b["x"], b["xs"], b["w"], b["ws"])
+        if stage == "dgrad":
+            B.te_mxfp4_quantize(DY[w.name], b["dy"], b["dys"])
+            B.te_mxfp4_quantize(W[w.name], None, None, b["wT"], b["wTs"])
+            return (b["dy"], b["dys"], b["wT"], b["wTs"])
+        B.te_mxfp4_quantize(DY[w.name], None, None, b["dyT"], b["dyTs"])
+        B.te_mxfp4_quantize(X[w.name], None, None, b["xT"], b["xTs"])
+        return (b["dyT"], b["dyTs"], b["xT"], b["xTs"])
+
+    prequant_fp8, prequant_mx, prequant_mx4 = {}, {}, {}
 
     def prepare_prequant():
         q_pre = fp8_buffers() if "fp8_current_prequant" in modes else None
         c_pre = new_cur()
         mx_pre = mx_buffers() if "mxfp8_prequant" in modes else None
+        mx4_pre = mx4_buffers() if "mxfp4_prequant" in modes else None
         for li, w in enumerate(weights):
             for stage in ("fprop", "dgrad", "wgrad"):
                 if q_pre is not None:
                     prequant_fp8[(w.name, stage)] = quant_fp8(w, li, stage, CUR, q_pre, c_pre)
                 if mx_pre is not None:
                     prequant_mx[(w.name, stage)] = quant_mx(w, stage, mx_pre)
+                if mx4_pre is not None:
+                    prequant_mx4[(w.name, stage)] = quant_mx4(w, stage, mx4_pre)
         torch.cuda.synchronize()
 
     # Shared quantization (the layer schedule of TE's autocast, where the forward's FP8
@@ -260,6 +298,10 @@ def main():
     def gemm_mx(ops, out):
         a, sa, b, sb = ops
         B.te_fp8_gemm(a, E4, sa, b, E4, sb, out, gran=B.TE_GRAN_MX_BLOCK32)
+
+    def gemm_mx4(ops, out):
+        a, sa, b, sb = ops
+        B.te_fp8_gemm(a, "E2M1", sa, b, "E2M1", sb, out, gran=B.TE_GRAN_MX_BLOCK32)
 
     def gemm_bf16(w, stage, out):
         t = BT[w.name]
@@ -308,6 +350,13 @@ def main():
                     ops = quant_mx_shared(w, stage)
                     e1.record()
                     gemm_mx(ops, out)
+                elif mode == "mxfp4_autocast":
+                    ops = quant_mx4(w, stage)
+                    e1.record()
+                    gemm_mx4(ops, out)
+                elif mode == "mxfp4_prequant":
+                    e1.record()
+                    gemm_mx4(prequant_mx4[(w.name, stage)], out)
                 e2.record()
                 variants.setdefault(mode, set()).add(B.te_gemm_variant())
                 rec.append((mode, w.name, stage, e0, e1, e2))
@@ -352,7 +401,7 @@ def main():
     wall = time.perf_counter() - t0
     log(f"timed region {wall:.2f}s")
     # every mode's GEMMs must have run on the matrix-core path of its precision
-    want = {"bf16": "gemm4_bf16_", "mxfp8": "gemm4_mx_", "fp8": "gemm4_fp8_"}
+    want = {"bf16": "gemm4_bf16_", "mxfp8": "gemm4_mx_", "mxfp4": "gemm4_mxfp4_", "fp8": "gemm4_fp8_"}
     for m, vs in variants.items():
         prefix = next(v for k, v in want.items() if m.startswith(k))
         bad = [v for v in vs if not v.startswith(prefix)]
@@ -413,6 +462,17 @@ def main():
                           "traffic = mean HBM bytes per launch",
                 "avg_launch_ms": round(t_ms / len(gemms), 4),
                 "flop_per_launch": int(flops / len(gemms))}
+    # the same for the MXFP4 GEMM against the FP4 peak (the FP4 variant of the layer)
+    roof4 = None
+    if "mxfp4_prequant" in modes:
+        flops = sum(g.flops for g in gemms)
+        t_ms = sum(med(per_gemm["mxfp4_prequant"][f"{g.weight}.{g.stage}"]) for g in gemms)
+        achieved = flops / (t_ms * 1e-3) / 1e12
+        roof4 = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MI355X_FP4_PEAK_TFLOPS,
+                 "unit": "TFLOP/s", "frac": round(achieved / MI355X_FP4_PEAK_TFLOPS, 4),
+                 "traffic": measured_traffic("gemm_mxfp4"),
+                 "kernel": "k_gemm4 MXFP4 (E2M1 x E2M1 scaled MFMA, 256x256 tiles, ping-pong); 12 launches per layer",
+                 "avg_launch_ms": round(t_ms / len(gemms), 4), "flop_per_launch": int(flops / len(gemms))}
     roof_q = None
     if "fp8_delayed_autocast" in modes:
         n_el = sum(2 * (M * w.in_features + w.out_features * w.in_features + M * w.out_features) for w in weights)
@@ -471,6 +531,7 @@ def main():
         "per_gemm_ms": per_gemm_out,
         "roofline": roof,
         "roofline_quant": roof_q,
+        "roofline_mxfp4": roof4,
         "shared_quantization": shared,
         "latency_configs": lat,
         "dispatched_variants": {m: sorted(v) for m, v in variants.items()},

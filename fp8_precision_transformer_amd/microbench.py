@@ -81,6 +81,12 @@ def _operands(kind, m, n, k, g, dev, fa="E4M3", fb="E4M3"):
     def codes(r, c):
         return (torch.randint(0x18, 0x48, (r, c), device=dev, generator=g, dtype=torch.int32) |
                 (torch.randint(0, 2, (r, c), device=dev, generator=g, dtype=torch.int32) << 7)).to(torch.uint8)
+    if kind == "mx4":  # packed E2M1 pairs: every byte is a valid pair of codes
+        a = torch.randint(0, 256, (m, k // 2), device=dev, generator=g, dtype=torch.int32).to(torch.uint8)
+        b = torch.randint(0, 256, (n, k // 2), device=dev, generator=g, dtype=torch.int32).to(torch.uint8)
+        sa = torch.full((m, k // 32), 127, dtype=torch.uint8, device=dev)
+        sb = torch.full((n, k // 32), 127, dtype=torch.uint8, device=dev)
+        return a, "E2M1", sa, b, "E2M1", sb, B.TE_GRAN_MX_BLOCK32
     a, b = codes(m, k), codes(n, k)
     if kind == "mx":
         sa = torch.full((m, k // 32), 127, dtype=torch.uint8, device=dev)
@@ -287,7 +293,7 @@ def main():
     c.add_argument("--iters", type=int, default=20)
     c.add_argument("--warmup", type=int, default=3)
     ly = sub.add_parser("layer")
-    ly.add_argument("--kind", choices=["fp8", "mx", "bf16"], default="fp8")
+    ly.add_argument("--kind", choices=["fp8", "mx", "mx4", "bf16"], default="fp8")
     ly.add_argument("--iters", type=int, default=10)
     ly.add_argument("--warmup", type=int, default=2)
     lb = sub.add_parser("lib")
