@@ -49,12 +49,16 @@ MI355X_HBM_GBS = 8000.0           # HBM3E (published)
 MEASURED_TRAFFIC = {
     # FP8 GEMM: mean over the layer's 12 GEMM launches (microbench layer --kind fp8)
     "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                 "sha256": "b20777d0266a3fd06616f96a48882e67382d93f4d34f99aec33f1f634fe4539a",
-                 "bytes_per_launch": 1518914990},
+                 "sha256": "cf02d15abe95f9bdbaf653de6fe4cc284bd6c061c1d827f8280d02532b14e2d3",
+                 "bytes_per_launch": 1549303926},
+    # MXFP8 GEMM: the same 12 shapes (microbench layer --kind mx)
+    "gemm_mxfp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
+                   "sha256": "cf02d15abe95f9bdbaf653de6fe4cc284bd6c061c1d827f8280d02532b14e2d3",
+                   "bytes_per_launch": 1572452427},
     # MXFP4 GEMM: the same 12 shapes (microbench layer --kind mx4)
     "gemm_mxfp4": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "b20777d0266a3fd06616f96a48882e67382d93f4d34f99aec33f1f634fe4539a",
-                   "bytes_per_launch": 894394325},
+                   "sha256": "cf02d15abe95f9bdbaf653de6fe4cc284bd6c061c1d827f8280d02532b14e2d3",
+                   "bytes_per_launch": 877955610},
 }
 
 
@@ -462,17 +466,22 @@ def main():
                           "traffic = mean HBM bytes per launch",
                 "avg_launch_ms": round(t_ms / len(gemms), 4),
                 "flop_per_launch": int(flops / len(gemms))}
-    # the same for the MXFP4 GEMM against the FP4 peak (the FP4 variant of the layer)
-    roof4 = None
-    if "mxfp4_prequant" in modes:
+    # the same for the block-scaled GEMMs: MXFP8 against the FP8 peak, MXFP4 (the FP4
+    # variant of the layer) against the FP4 peak
+    def mx_roofline(mode, peak, key, kernel):
+        if mode not in modes:
+            return None
         flops = sum(g.flops for g in gemms)
-        t_ms = sum(med(per_gemm["mxfp4_prequant"][f"{g.weight}.{g.stage}"]) for g in gemms)
+        t_ms = sum(med(per_gemm[mode][f"{g.weight}.{g.stage}"]) for g in gemms)
         achieved = flops / (t_ms * 1e-3) / 1e12
-        roof4 = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MI355X_FP4_PEAK_TFLOPS,
-                 "unit": "TFLOP/s", "frac": round(achieved / MI355X_FP4_PEAK_TFLOPS, 4),
-                 "traffic": measured_traffic("gemm_mxfp4"),
-                 "kernel": "k_gemm4 MXFP4 (E2M1 x E2M1 scaled MFMA, 256x256 tiles, ping-pong); 12 launches per layer",
-                 "avg_launch_ms": round(t_ms / len(gemms), 4), "flop_per_launch": int(flops / len(gemms))}
+        return {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": measured_traffic(key), "kernel": kernel,
+                "avg_launch_ms": round(t_ms / len(gemms), 4), "flop_per_launch": int(flops / len(gemms))}
+
+    roof8 = mx_roofline("mxfp8_prequant", MI355X_FP8_PEAK_TFLOPS, "gemm_mxfp8",
+                        "k_gemm4 MXFP8 (E4M3 x E4M3 scaled MFMA, 256x256 tiles, ping-pong); 12 launches per layer")
+    roof4 = mx_roofline("mxfp4_prequant", MI355X_FP4_PEAK_TFLOPS, "gemm_mxfp4",
+                        "k_gemm4 MXFP4 (E2M1 x E2M1 scaled MFMA, 256x256 tiles, ping-pong); 12 launches per layer")
     roof_q = None
     if "fp8_delayed_autocast" in modes:
         n_el = sum(2 * (M * w.in_features + w.out_features * w.in_features + M * w.out_features) for w in weights)
@@ -531,6 +540,7 @@ def main():
         "per_gemm_ms": per_gemm_out,
         "roofline": roof,
         "roofline_quant": roof_q,
+        "roofline_mxfp8": roof8,
         "roofline_mxfp4": roof4,
         "shared_quantization": shared,
         "latency_configs": lat,

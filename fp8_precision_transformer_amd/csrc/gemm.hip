@@ -349,22 +349,24 @@ __device__ __forceinline__ int f8(int row) { return (row & 7) ^ ((row >> 3) & 3)
 // SIMD, the same 128 rows and neighbouring 64-column halves).  The groups
 // alternate between a compute phase (16 FP8 MFMAs over one 128-byte k stage
 // held in registers, about 1024 cycles) and a memory phase (the next stage's
-// fragments from LDS; group 0 also issues the global->LDS loads of the stage
-// after that), so on every SIMD one wave keeps the matrix core busy while the
+// fragments from LDS, plus global->LDS loads of a later stage: A from group 0, B
+// from group 1), so on every SIMD one wave keeps the matrix core busy while the
 // other waits on LDS and memory.  Two barriers per stage keep the rhythm:
 //
 //   phase 2s   : group 0 computes stage s    | group 1 reads stage s
 //   barrier X  : group 0 has waited for its loads of stage s+1 -> stage s+1
 //                is visible; group 1 has its stage-s fragments
 //   phase 2s+1 : group 0 reads stage s+1 and | group 1 computes stage s
-//                loads stage s+2 into the slot of stage s (read by both
+//                loads A of stage s+2 into the
+//                slot of stage s (read by both
 //                groups before X)
-//   barrier Y
+//   barrier Y  : group 1 then reads stage s+1 and loads B of a later stage
+//                into a slot both groups have finished reading
 //
-// Loads get two phases (one stage) of latency.  LDS: two 64 KB stage slots in
-// the layout of the pair pipeline above (A [0, 64K), B [64K, 128K), rows of 8
-// swizzled 16-byte chunks).  Correctness does not depend on which SIMD a wave
-// lands on; only the overlap does.
+// A gets two phases (one stage) of latency, B three.  LDS: stage slots in the
+// layout of the pair pipeline above (A [0, 64K), B from 64K, rows of 8 swizzled
+// 16-byte chunks).  Correctness does not depend on which SIMD a wave lands on;
+// only the overlap does.
 // ============================================================================
 constexpr int NT8 = 512;
 
@@ -372,12 +374,12 @@ template <int KIND, int AF, int BF>
 __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
   constexpr bool MX4 = KIND == KIND_MX4;
   constexpr bool MX = KIND == KIND_MX || MX4;
-  // FP8/BF16 (SPLIT): A in two stage slots, B in three, and the two groups share the
-  // loads (group 0 A, group 1 B, in their own memory phases).  MX: two slots each, all
-  // loads from group 0, plus per stage slot the E8M0 block scales of the stage's 128
-  // bytes of each row: one dword (four blocks of 32 FP8 elements) per row of A (1 KB)
-  // and of B (1 KB); MXFP4 two dwords (eight blocks of 32 E2M1 elements), kept as
-  // four 1 KB arrays (A dword 0, A dword 1, B dword 0, B dword 1).
+  // The two groups share the global->LDS loads, each in its own memory phases: group 0
+  // loads A, group 1 loads B.  FP8/BF16 (SPLIT): A in two stage slots, B in three.  MX:
+  // two slots each (group 0 also loads the scales), plus per stage slot the E8M0 block
+  // scales of the stage's 128 bytes of each row: one dword (four blocks of 32 FP8
+  // elements) per row of A (1 KB) and of B (1 KB); MXFP4 two dwords (eight blocks of 32
+  // E2M1 elements), kept as four 1 KB arrays (A dword 0, A dword 1, B dword 0, B dword 1).
   constexpr bool SPLIT = !MX;
   constexpr int kScOff = 2 * kPB, kScSlot = MX4 ? 4096 : 2048;
   constexpr int kLds = SPLIT ? kPB + 3 * kPairOp : 2 * kPB + 2 * kScSlot;
@@ -426,9 +428,8 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
                      static_cast<uint32_t>(rows_b) * p.kblocks);
   }
   const uint32_t sc_off = static_cast<uint32_t>(q4 * 64 + lane) * static_cast<uint32_t>(p.kblocks);
-  auto issue_stage = [&](auto SLOT, int st) {
+  auto issue_scales = [&](auto SLOT, int st) {
     constexpr int slot = decltype(SLOT)::value;
-    const uint32_t kb = static_cast<uint32_t>(st) * PK;
     if constexpr (MX) {
       const int sbase = kScOff + slot * kScSlot + q4 * 256;
       if constexpr (MX4) {
@@ -448,21 +449,8 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
                             static_cast<int>(sc_off + 4u * st), 0, 0, 0);
       }
     }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const uint32_t cb = static_cast<uint32_t>((c0 ^ (t & 3)) << 4);
-      const uint32_t off = (kb + cb < static_cast<uint32_t>(p.KB))
-                               ? ld_base + static_cast<uint32_t>(t * 8) * static_cast<uint32_t>(p.KB) + kb + cb
-                               : kOOB;
-      const int base = slot * kPairOp + (q4 * 64 + t * 8) * PK;
-      raw_buffer_load_lds(rsA, (__attribute__((address_space(3))) uint32_t*)(smem + base), 16,
-                          static_cast<int>(off), 0, 0, 0);
-      raw_buffer_load_lds(rsB, (__attribute__((address_space(3))) uint32_t*)(smem + kPB + base), 16,
-                          static_cast<int>(off), 0, 0, 0);
-    }
   };
-  constexpr int kLoadsPerStage = MX4 ? 20 : (MX ? 18 : 16);
-  // SPLIT: one operand of one stage (8 loads per lane), into the slot at byte offset off
+  // one operand of one stage (8 loads per lane), into the slot at byte offset off_slot
   auto issue_op = [&](const v4i& rs, int off_slot, int st) {
     const uint32_t kb = static_cast<uint32_t>(st) * PK;
 #pragma unroll
@@ -478,6 +466,9 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
   };
   auto issue_a = [&](auto SLOT, int st) { issue_op(rsA, decltype(SLOT)::value * kPairOp, st); };
   auto issue_b = [&](int st) { issue_op(rsB, kPB + (st % 3) * kPairOp, st); };
+  // MX: group 0 loads A and the scales of a stage, group 1 its B, both into slot st % 2
+  auto issue_b2 = [&](auto SLOT, int st) { issue_op(rsB, kPB + decltype(SLOT)::value * kPairOp, st); };
+  constexpr int kLoadsA = 8 + (MX4 ? 4 : 2);
 
   // A phase covers NH of the stage's k steps (two of 64 bytes for FP8, MX and BF16,
   // four of 32 bytes for MXFP4): both for FP8 and BF16; one for MX, whose scaled MFMA
@@ -639,9 +630,12 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
   // Both groups run the same loop body, compute part u | barrier | read part u+1 |
   // barrier, so compute and fragment reads are one code path; group 1 runs it one
   // phase behind group 0 (one extra barrier before its loop, matched by one after
-  // group 0's).  Group 0 alone waits for and issues the global->LDS loads: at the end
-  // of a stage's last part it waits for the next stage, and after the barrier it loads
-  // the stage after that into the slot both groups have finished reading.
+  // group 0's).  Group 0 waits for its loads of the next stage at the end of a stage's
+  // last part, and after the barrier loads A of the stage after that into the slot both
+  // groups have finished reading.  Group 1 loads B: three slots deep for FP8/BF16; for
+  // MX (two phases per stage) it waits for B of stage s+1 in the memory phase after
+  // part 0 of stage s, and loads B of stage s+2 into the slot of stage s in the one
+  // after the last part, when both groups have read that slot.
   if constexpr (SPLIT) {
     // group 0 loads A of stages 0 and 1, group 1 B of stages 0, 1 and (after the
     // prologue) 2; each waits for its stage-0 half before the first barrier
@@ -654,11 +648,21 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
     }
     if (S > 1) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(8));
     else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
-  } else if (grp == 0) {
-    issue_stage(ic<0>{}, 0);
+  } else {
+    if (grp == 0) {
+      issue_scales(ic<0>{}, 0);
+      issue_a(ic<0>{}, 0);
+      if (S > 1) {
+        issue_scales(ic<1>{}, 1);
+        issue_a(ic<1>{}, 1);
+      }
+    } else {
+      issue_b2(ic<0>{}, 0);
+      if (S > 1) issue_b2(ic<1>{}, 1);
+    }
     if (S > 1) {
-      issue_stage(ic<1>{}, 1);
-      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kLoadsPerStage));
+      if (grp == 0) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(kLoadsA));
+      else __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(8));
     } else {
       __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
     }
@@ -708,7 +712,14 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
         if (s + 3 < S) issue_b(s + 3);                                // into the B slot of stage s
       }
     } else {
-      if (last_part && grp == 0 && s + 2 < S) issue_stage(ic<slot>{}, s + 2);  // the slot of stage s is free
+      if (last_part && grp == 0 && s + 2 < S) {  // the slot of stage s is free
+        issue_scales(ic<slot>{}, s + 2);
+        issue_a(ic<slot>{}, s + 2);
+      }
+      if (grp == 1) {
+        if (!last_part && s + 1 < S) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));  // B of stage s+1 landed
+        if (last_part && s + 2 < S) issue_b2(ic<slot>{}, s + 2);                       // into the slot of stage s
+      }
     }
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
     __builtin_amdgcn_sched_barrier(0);
