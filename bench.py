@@ -50,15 +50,15 @@ MEASURED_TRAFFIC = {
     # FP8 GEMM: mean over the layer's 12 GEMM launches (microbench layer --kind fp8)
     "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
                  "sha256": "cf02d15abe95f9bdbaf653de6fe4cc284bd6c061c1d827f8280d02532b14e2d3",
-                 "bytes_per_launch": 1549303926},
+                 "bytes_per_launch": 1549302390},
     # MXFP8 GEMM: the same 12 shapes (microbench layer --kind mx)
     "gemm_mxfp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
                    "sha256": "cf02d15abe95f9bdbaf653de6fe4cc284bd6c061c1d827f8280d02532b14e2d3",
-                   "bytes_per_launch": 1572452427},
+                   "bytes_per_launch": 1572450863},
     # MXFP4 GEMM: the same 12 shapes (microbench layer --kind mx4)
     "gemm_mxfp4": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
                    "sha256": "cf02d15abe95f9bdbaf653de6fe4cc284bd6c061c1d827f8280d02532b14e2d3",
-                   "bytes_per_launch": 877955610},
+                   "bytes_per_launch": 877954792},
 }
 
 

@@ -44,8 +44,9 @@ def _out(m, n, odt):
     return torch.empty((m, n), dtype=torch.bfloat16 if odt == "bf16" else torch.float32, device=DEV)
 
 
+# k stages of 128 bytes: 1 (k 16, 128), 2 (k 256), 3 (k 272, ragged), 4 (k 400, ragged), 6, 8
 GEMM_SHAPES = [(16, 16, 16), (1, 16, 128), (300, 272, 400), (256, 256, 128), (513, 512, 1024),
-               (1024, 768, 768), (64, 2304, 768), (4096, 48, 272)]
+               (1024, 768, 768), (64, 2304, 768), (4096, 48, 272), (128, 64, 256)]
 
 
 @pytest.mark.parametrize("mnk", GEMM_SHAPES, ids=str)
@@ -123,9 +124,11 @@ def test_bf16_gemm_parity(mnk):
 
 
 # k % 128 == 0 takes the ping-pong kernel (scales loaded a dword per row and stage), other
-# k the two-stage kernel; ragged m and n in both
+# k the two-stage kernel; ragged m and n in both.  Ping-pong stage counts 1, 2, 3 (k 128,
+# 256, 384: the prologue and the loop tail of the split load schedule), 5, 6 and 32.
 @pytest.mark.parametrize("mnk", [(32, 32, 64), (300, 272, 416), (1024, 768, 768), (256, 256, 4096),
-                                 (64, 128, 96), (520, 400, 640)], ids=str)
+                                 (64, 128, 96), (520, 400, 640), (64, 64, 128), (200, 304, 256),
+                                 (256, 512, 384)], ids=str)
 @pytest.mark.parametrize("fa,fb", [("E4M3", "E4M3"), ("E5M2", "E4M3")])
 def test_mx_gemm_parity(mnk, fa, fb):
     m, n, k = mnk
