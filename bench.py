@@ -51,6 +51,11 @@ MEASURED_TRAFFIC = {
     "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
                  "sha256": "cf02d15abe95f9bdbaf653de6fe4cc284bd6c061c1d827f8280d02532b14e2d3",
                  "bytes_per_launch": 1549302390},
+    # delayed-scaling quantizers of one layer in autocast mode (24 casts and cast-transposes),
+    # summed over the layer's launches (bench.py --modes fp8_delayed_autocast under --pmc)
+    "quant_delayed_layer": {"source": "fp8_precision_transformer_amd/csrc/quant.hip",
+                            "sha256": "b44cb52d3fd73ed61767bb60a6223c3f27b32719a281eaf9b14f7c7c17c90442",
+                            "bytes_per_launch": 7452474237},
     # MXFP8 GEMM: the same 12 shapes (microbench layer --kind mx)
     "gemm_mxfp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
                    "sha256": "cf02d15abe95f9bdbaf653de6fe4cc284bd6c061c1d827f8280d02532b14e2d3",
@@ -489,7 +494,8 @@ def main():
         qms = med(quant_ms["fp8_delayed_autocast"])
         roof_q = {"bound": "hbm", "achieved": round(qbytes / (qms * 1e-3) / 1e9, 1), "peak": MI355X_HBM_GBS,
                   "unit": "GB/s", "frac": round(qbytes / (qms * 1e-3) / 1e9 / MI355X_HBM_GBS, 4),
-                  "traffic": None, "algorithmic_bytes_per_layer": qbytes,
+                  "traffic": measured_traffic("quant_delayed_layer"), "traffic_per": "layer",
+                  "algorithmic_bytes_per_layer": qbytes,
                   "kernel": "delayed amax+cast / cast-transpose (24 launches + 2 scale updates per layer)"}
 
     shared = None
