@@ -15,6 +15,11 @@ Scaling state per module (delayed scaling): ``amax_history`` [3, L], ``scale``
 [3], ``scale_inv`` [3] fp32 device tensors; index 0 = input, 1 = weight,
 2 = output gradient.  The forward-pass entries are updated when the autocast
 region exits, the gradient entry at the end of backward (update interval 1).
+
+The bias gradient comes from the pass that casts dY (te_cast_transpose_dbias).
+With the MXFP8 recipe the forward pass also keeps the column-wise MX copies of x
+and W (blocks along the token and output axes), which Wgrad and Dgrad take as
+their k-contiguous operands; that needs a token count that is a multiple of 32.
 """
 
 from __future__ import annotations
@@ -74,13 +79,28 @@ class _FP8LinearFn(torch.autograd.Function):
         N = weight.shape[0]
         fwd = recipe.fp8_format.forward_dtype()
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ctx.module, ctx.recipe = module, recipe
+        ctx.has_bias = bias is not None
+        ctx.w_dtype = weight.dtype
+        ctx.x_dtype = x2.dtype
         if isinstance(recipe, MXFP8BlockScaling):
+            # row-wise copies for Fprop; with a backward, also the column-wise copies
+            # (MX of x^T and W^T, blocks along M and N) for Wgrad and Dgrad
+            if need_grad and M % 32:
+                raise ValueError("MXFP8 backward needs a token count that is a multiple of 32")
             xq, xs = _f8((M, K), dev), _f8((M, K // 32), dev)
             wq, ws = _f8((N, K), dev), _f8((N, K // 32), dev)
-            B.te_mxfp8_quantize(x2, fwd, xq, xs)
-            B.te_mxfp8_quantize(weight, fwd, wq, ws)
+            xqT = _f8((K, M), dev) if need_grad else None
+            xsT = _f8((K, M // 32), dev) if need_grad else None
+            wqT = _f8((K, N), dev) if need_grad else None
+            wsT = _f8((K, N // 32), dev) if need_grad else None
+            B.te_mxfp8_quantize(x2, fwd, xq, xs, xqT, xsT)
+            B.te_mxfp8_quantize(weight, fwd, wq, ws, wqT, wsT)
             B.te_fp8_gemm(xq, fwd, xs, wq, fwd, ws, y, bias=bias, gran=B.TE_GRAN_MX_BLOCK32)
-            ctx.mark_non_differentiable(y)
+            if module.keep_fp8_tensors:
+                module.last_fp8 = {"xq": xq, "xs": xs, "wq": wq, "ws": ws, "xqT": xqT, "xsT": xsT,
+                                   "wqT": wqT, "wsT": wsT}
+            ctx.save_for_backward(xqT, xsT, wqT, wsT)
             return y
         st = module._state(recipe)
         mode = B.TE_SCALE_CURRENT if isinstance(recipe, Float8CurrentScaling) else B.TE_SCALE_DELAYED
@@ -95,35 +115,67 @@ class _FP8LinearFn(torch.autograd.Function):
         B.te_fp8_gemm(xq, fwd, si[0:1], wq, fwd, si[1:2], y, bias=bias)
         if module.keep_fp8_tensors:
             module.last_fp8 = {"xq": xq, "wq": wq, "xqT": xqT, "wqT": wqT}
-        ctx.module, ctx.recipe, ctx.mode = module, recipe, mode
-        ctx.has_bias = bias is not None
-        ctx.w_dtype = weight.dtype
-        ctx.x_dtype = x2.dtype
+        ctx.mode = mode
         ctx.save_for_backward(xqT, wqT)
         return y
 
     @staticmethod
     def backward(ctx, dy):
-        xqT, wqT = ctx.saved_tensors
         module, recipe = ctx.module, ctx.recipe
-        st = module._state(recipe)
         bwd = recipe.fp8_format.backward_dtype()
         fwd = recipe.fp8_format.forward_dtype()
         dy = dy.contiguous()
         M, N = dy.shape
-        K = xqT.shape[0]
         dev = dy.device
+        dx = dw = db = None
+        if isinstance(recipe, MXFP8BlockScaling):
+            xqT, xsT, wqT, wsT = ctx.saved_tensors
+            K = xqT.shape[0]
+            # dY row-wise (blocks along N, the k of Dgrad) and column-wise (blocks along
+            # M, the k of Wgrad)
+            dyq, dys = _f8((M, N), dev), _f8((M, N // 32), dev)
+            dyqT, dysT = _f8((N, M), dev), _f8((N, M // 32), dev)
+            if ctx.has_bias:
+                db = _column_sums(dy, dyq)  # its codes are overwritten just below
+            B.te_mxfp8_quantize(dy, bwd, dyq, dys, dyqT, dysT)
+            dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+            B.te_fp8_gemm(dyq, bwd, dys, wqT, fwd, wsT, dx, gran=B.TE_GRAN_MX_BLOCK32)      # Dgrad
+            dw = torch.empty((N, K), dtype=torch.float32, device=dev)
+            B.te_fp8_gemm(dyqT, bwd, dysT, xqT, fwd, xsT, dw, gran=B.TE_GRAN_MX_BLOCK32)    # Wgrad
+            return dx.to(ctx.x_dtype), dw.to(ctx.w_dtype), db, None, None, None
+        xqT, wqT = ctx.saved_tensors
+        st = module._state(recipe)
+        K = xqT.shape[0]
         h, s, si = st["amax_history"], st["scale"], st["scale_inv"]
         dyq, dyqT = _f8((M, N), dev), _f8((N, M), dev)
-        B.te_cast_transpose(dy, bwd, ctx.mode, recipe.margin, s[2:3], si[2:3], h[2, 0:1], dyq, dyqT)
+        if ctx.has_bias:  # bias gradient from the same pass over dY
+            db = torch.empty(N, dtype=torch.float32, device=dev)
+            ws = _f8(max(B.te_cast_transpose_dbias_workspace_bytes(M, N), 4), dev)
+            B.te_cast_transpose_dbias(dy, bwd, ctx.mode, recipe.margin, s[2:3], si[2:3], h[2, 0:1], db, ws,
+                                      dyq, dyqT)
+        else:
+            B.te_cast_transpose(dy, bwd, ctx.mode, recipe.margin, s[2:3], si[2:3], h[2, 0:1], dyq, dyqT)
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         B.te_fp8_gemm(dyq, bwd, si[2:3], wqT, fwd, si[1:2], dx)              # Dgrad
         dw = torch.empty((N, K), dtype=torch.float32, device=dev)
         B.te_fp8_gemm(dyqT, bwd, si[2:3], xqT, fwd, si[0:1], dw)             # Wgrad
-        db = dy.float().sum(0) if ctx.has_bias else None
         if isinstance(recipe, DelayedScaling):
             module._update_scales(slice(2, 3), bwd, recipe)
         return dx.to(ctx.x_dtype), dw.to(ctx.w_dtype), db, None, None, None
+
+
+def _column_sums(dy, codes):
+    """db[c] = sum_r dY[r, c] in fp32 by the library's dbias pass; the unit-scale E4M3
+    codes it also writes go to `codes` [M, N] and are not used (MXFP8 quantizes dY
+    itself)."""
+    M, N = dy.shape
+    dev = dy.device
+    one = torch.ones(1, dtype=torch.float32, device=dev)
+    si, am = torch.empty(1, dtype=torch.float32, device=dev), torch.empty(1, dtype=torch.float32, device=dev)
+    db = torch.empty(N, dtype=torch.float32, device=dev)
+    ws = _f8(max(B.te_cast_transpose_dbias_workspace_bytes(M, N), 4), dev)
+    B.te_cast_transpose_dbias(dy, "E4M3", B.TE_SCALE_DELAYED, 0, one, si, am, db, ws, codes, None)
+    return db
 
 
 class Linear(torch.nn.Module):
@@ -172,7 +224,7 @@ class Linear(torch.nn.Module):
         st = _current()
         bias = self.bias
         if st is not None and st.enabled:
-            if not isinstance(st.recipe, MXFP8BlockScaling):
+            if isinstance(st.recipe, DelayedScaling):
                 st.modules.append(self)
             need_grad = torch.is_grad_enabled() and (x2.requires_grad or self.weight.requires_grad)
             y = _FP8LinearFn.apply(x2, self.weight, bias, self, st.recipe, need_grad)

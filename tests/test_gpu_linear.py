@@ -108,7 +108,8 @@ def test_linear_backward_current_scaling():
                                np.ascontiguousarray(xq.T), O.E4M3, O.scale_inverse(sx), out="f32")
     check_fp8_gemm(host(lin.weight.grad), ref_dw, t5[dyq.T], t4[xq.T],
                    np.float64(O.scale_inverse(sdy)) * np.float64(O.scale_inverse(sx)), "f32")
-    np.testing.assert_allclose(host(lin.bias.grad), dy_b.astype(np.float64).sum(0), rtol=1e-4, atol=1e-6)
+    # bias gradient from the dbias pass over dY: within the fp32 summation bound
+    assert np.all(np.abs(host(lin.bias.grad).astype(np.float64) - O.bias_grad(dy_b)) <= _dbias_bound(dy_b))
 
 
 def test_linear_mxfp8_forward():
@@ -122,6 +123,55 @@ def test_linear_mxfp8_forward():
     t4 = O.decode_table(O.E4M3)
     check_fp8_gemm(host(y), ref, t4[qa] * np.repeat(O.e8m0_to_float(ea), 32, axis=1),
                    t4[qb] * np.repeat(O.e8m0_to_float(eb), 32, axis=1), 1.0, "bf16")
+
+
+def _dbias_bound(dy):
+    """recursive-summation bound of an fp32 column sum over R rows: R 2^-24 sum |dY|"""
+    return dy.shape[0] * 2.0 ** -24 * np.abs(dy.astype(np.float64)).sum(0) + 1e-30
+
+
+def test_linear_mxfp8_backward():
+    """MXFP8 Fprop, Dgrad and Wgrad: the forward keeps the column-wise MX copies of x and
+    W; dY is quantized row-wise and column-wise; the bias gradient comes from the dbias
+    pass over dY."""
+    lin, w, b = _layer(5)
+    lin.keep_fp8_tensors = True
+    M = 256
+    x = synth.activations((M, 768), 5, 0, synth.T_X, 0)
+    dy = synth.grads((M, 768), 5, 0, synth.T_DY, 0)
+    xd = dev_f32(x).requires_grad_(True)
+    with fp8_autocast(fp8_recipe=MXFP8BlockScaling()):
+        y = lin(xd)
+    y.backward(dev_f32(dy).to(torch.bfloat16))
+    dy_b = host(dev_f32(dy).to(torch.bfloat16)).astype(np.float32)
+    t4 = O.decode_table(O.E4M3)
+
+    def val(q, e):
+        return t4[q] * np.repeat(O.e8m0_to_float(e), 32, axis=1)
+
+    qx, ex = O.mxfp8_quantize(x)
+    qw, ew = O.mxfp8_quantize(w)
+    qxT, exT = O.mxfp8_quantize(np.ascontiguousarray(x.T))
+    qwT, ewT = O.mxfp8_quantize(np.ascontiguousarray(w.T))
+    np.testing.assert_array_equal(host(lin.last_fp8["xqT"]), qxT)
+    np.testing.assert_array_equal(host(lin.last_fp8["wsT"]), ewT)
+    check_fp8_gemm(host(y), O.gemm_mx(qx, ex, O.E4M3, qw, ew, O.E4M3, bias=b), val(qx, ex), val(qw, ew), 1.0,
+                   "bf16")
+    qg, eg = O.mxfp8_quantize(dy_b)
+    qgT, egT = O.mxfp8_quantize(np.ascontiguousarray(dy_b.T))
+    ref_dx = O.gemm_mx(qg, eg, O.E4M3, qwT, ewT, O.E4M3, out="bf16")
+    check_fp8_gemm(host(xd.grad), ref_dx, val(qg, eg), val(qwT, ewT), 1.0, "bf16")
+    ref_dw = O.gemm_mx(qgT, egT, O.E4M3, qxT, exT, O.E4M3, out="f32")
+    check_fp8_gemm(host(lin.weight.grad), ref_dw, val(qgT, egT), val(qxT, exT), 1.0, "f32")
+    db_ref = O.bias_grad(dy_b)
+    assert np.all(np.abs(host(lin.bias.grad).astype(np.float64) - db_ref) <= _dbias_bound(dy_b))
+
+
+def test_linear_mxfp8_backward_needs_32_tokens():
+    lin, _, _ = _layer(6)
+    xd = dev_f32(synth.activations((48, 768), 6, 0, synth.T_X, 0)).requires_grad_(True)
+    with pytest.raises(ValueError), fp8_autocast(fp8_recipe=MXFP8BlockScaling()):
+        lin(xd)
 
 
 def test_linear_outside_autocast_uses_bf16_gemm():
