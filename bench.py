@@ -45,24 +45,26 @@ MI355X_HBM_GBS = 8000.0           # HBM3E (published)
 # HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per
 # dispatch), each scaled by the factor that makes the same counter read the known size
 # of a plain 1 GiB device copy.  A figure is reported only while the kernel source it was
-# measured on is unchanged (sha256 of the file); otherwise traffic is null.
+# measured on is unchanged (sha256 of the file); otherwise traffic is null.  (A source
+# hash is updated without a new measurement only when an edit changes comments alone and
+# the device assembly of the file is identical.)
 MEASURED_TRAFFIC = {
     # FP8 GEMM: mean over the layer's 12 GEMM launches (microbench layer --kind fp8)
     "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                 "sha256": "cf02d15abe95f9bdbaf653de6fe4cc284bd6c061c1d827f8280d02532b14e2d3",
+                 "sha256": "6384227bc9413cdd49a7b1283792d2e65aeebff892ce18ed647383dd71fa3e07",
                  "bytes_per_launch": 1549302390},
     # delayed-scaling quantizers of one layer in autocast mode (24 casts and cast-transposes),
     # summed over the layer's launches (bench.py --modes fp8_delayed_autocast under --pmc)
     "quant_delayed_layer": {"source": "fp8_precision_transformer_amd/csrc/quant.hip",
-                            "sha256": "b44cb52d3fd73ed61767bb60a6223c3f27b32719a281eaf9b14f7c7c17c90442",
+                            "sha256": "895553736c8c076ce66d8232ff90bbe9cec91aebb456f9e8d2affce73b9bc0af",
                             "bytes_per_launch": 7452474237},
     # MXFP8 GEMM: the same 12 shapes (microbench layer --kind mx)
     "gemm_mxfp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "cf02d15abe95f9bdbaf653de6fe4cc284bd6c061c1d827f8280d02532b14e2d3",
+                   "sha256": "6384227bc9413cdd49a7b1283792d2e65aeebff892ce18ed647383dd71fa3e07",
                    "bytes_per_launch": 1572450863},
     # MXFP4 GEMM: the same 12 shapes (microbench layer --kind mx4)
     "gemm_mxfp4": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "cf02d15abe95f9bdbaf653de6fe4cc284bd6c061c1d827f8280d02532b14e2d3",
+                   "sha256": "6384227bc9413cdd49a7b1283792d2e65aeebff892ce18ed647383dd71fa3e07",
                    "bytes_per_launch": 877954792},
 }
 

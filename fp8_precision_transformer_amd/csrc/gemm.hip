@@ -13,6 +13,8 @@
 //        epilogue d = fl32(fl32(acc * sa_inv) * sb_inv) + bias;
 //   MX   E4M3/E5M2 elements with one E8M0 exponent per 32 elements along k,
 //        v_mfma_scale_f32_32x32x64_f8f6f4 (the matrix core applies the scales);
+//   MX4  E2M1 elements (two per byte) with one E8M0 exponent per 32, the same
+//        scaled instruction with the FP4 operand format (MXFP4);
 //   BF16 comparison GEMM, v_mfma_f32_32x32x16_bf16.
 //
 // Two kernels, both with a 256 x 256 output tile per workgroup and an

@@ -1,5 +1,6 @@
-// Quantizer kernels for gfx950: amax + scaled FP8 cast, fused cast + transpose,
-// delayed-scaling update, MXFP8 block quantization.
+// Quantizer kernels for gfx950: amax + scaled FP8 cast, fused cast + transpose (with
+// the bias gradient of the tensor as an option), delayed-scaling update, MXFP8 and
+// MXFP4 block quantization, LayerNorm written straight as FP8.
 //
 // Pages: [FP8-intro] = "Introduction to FP8 training using Transformer Engine"
 // (NVIDIA blog, Japanese edition); [LP-opt] = "How to Optimize Transformer-Based
