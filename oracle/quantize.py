@@ -195,3 +195,40 @@ def mxfp8_quantize(x, fmt: FP8Format = E4M3, block: int = 32):
     scaled = np.ldexp(xb, (-e)[:, :, None].astype(np.int32)).astype(np.float32)
     q = encode(scaled, fmt).reshape(R, C)
     return q, codes_e8m0
+
+
+def mx_scales_panel(e8m0, panel: int = 256) -> np.ndarray:
+    """E8M0 block scales [R, C/32] (row r, block b along the row) rearranged into the
+    panel layout a GEMM reads a k stage at a time: rows in panels of 256; within a
+    panel, for each group of four consecutive blocks g (128 elements), the 256 rows'
+    dwords of that group are contiguous.  Byte of (r, b):
+        4 * ((r // 256) * G + b // 4) * 256 + 4 * (r % 256) + b % 4,   G = C / 128.
+    Returns uint8 [ceil(R / 256) * 256 * G * 4]; bytes of the padding rows of the last
+    panel are 127 (they belong to no row).  Needs C % 128 == 0.
+
+    Not on the pages: the layout only reorders the scales of the MX block rule (OCP MX
+    v1.0 reading of [TE-summary] "主な機能" MXFP8), so that the four scale bytes of one
+    row and 128-element stage are one dword and a stage's dwords of 256 rows are one
+    contiguous kilobyte."""
+    e = np.asarray(e8m0, dtype=np.uint8)
+    R, nb = e.shape
+    if nb % 4:
+        raise ValueError("the panel layout needs a multiple of four blocks (128 elements) per row")
+    G = nb // 4
+    P = -(-R // panel)
+    out = np.full(P * panel * G * 4, 127, np.uint8)
+    for r in range(R):
+        for b in range(nb):
+            out[4 * ((r // panel) * G + b // 4) * panel + 4 * (r % panel) + b % 4] = e[r, b]
+    return out
+
+
+def mx_scales_from_panel(panel_bytes, rows: int, blocks: int, panel: int = 256) -> np.ndarray:
+    """Inverse of mx_scales_panel: [rows, blocks] E8M0 from the panel layout."""
+    p = np.asarray(panel_bytes, dtype=np.uint8)
+    G = blocks // 4
+    out = np.empty((rows, blocks), np.uint8)
+    for r in range(rows):
+        for b in range(blocks):
+            out[r, b] = p[4 * ((r // panel) * G + b // 4) * panel + 4 * (r % panel) + b % 4]
+    return out

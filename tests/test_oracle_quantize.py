@@ -13,6 +13,8 @@ import os
 import numpy as np
 import pytest
 
+import oracle as O
+
 from oracle import (E4M3, E5M2, DelayedScalingState, amax, current_scale, decode_table,
                     delayed_update, encode, mxfp8_quantize, scale_inverse, scaled_cast,
                     cast_transpose)
@@ -209,3 +211,35 @@ def test_mxfp8_zero_block_and_clamp():
     y = np.full((1, 32), np.finfo(np.float32).smallest_subnormal, dtype=np.float32)
     qy, ey = mxfp8_quantize(y)
     assert ey[0, 0] == 0 and (qy == 0).all()
+
+
+def test_mx_scales_panel_layout_positions():
+    """The panel layout of the MX scales, pinned at positions worked out by hand from
+    its definition: 256-row panels; in a panel, the dwords (four block bytes) of one
+    128-element group for all 256 rows are contiguous."""
+    R, nb = 3, 8  # 256 columns: two groups of four blocks
+    e = np.array([[10 * r + b for b in range(nb)] for r in range(R)], np.uint8)
+    p = O.mx_scales_panel(e)
+    assert p.shape == (256 * 2 * 4,)
+    assert p[0] == 0 and p[3] == 3          # row 0, blocks 0 and 3: first dword of group 0
+    assert p[4] == 10                       # row 1, block 0: the next dword
+    assert p[1024] == 4                     # row 0, block 4: group 1 starts after 256 dwords
+    assert p[1024 + 8 + 1] == 25            # row 2, block 5
+    assert p[1024 + 8 + 3] == 27            # row 2, block 7
+    assert p[12] == 127 and p[1024 + 1020] == 127  # padding rows 3 and 255
+    # second panel: 300 rows, 384 columns (three groups); row 257 block 2
+    e2 = np.zeros((300, 12), np.uint8)
+    e2[257, 2] = 200
+    p2 = O.mx_scales_panel(e2)
+    assert p2.shape == (2 * 256 * 3 * 4,)
+    assert p2[4 * (1 * 3 + 0) * 256 + 4 * 1 + 2] == 200
+    assert int(np.count_nonzero(p2 == 200)) == 1
+
+
+def test_mx_scales_panel_round_trip():
+    rng = np.random.default_rng(11)
+    for R, nb in ((1, 4), (255, 8), (256, 4), (300, 12), (513, 16)):
+        e = rng.integers(0, 256, (R, nb)).astype(np.uint8)
+        np.testing.assert_array_equal(O.mx_scales_from_panel(O.mx_scales_panel(e), R, nb), e)
+    with pytest.raises(ValueError):
+        O.mx_scales_panel(np.zeros((4, 6), np.uint8))
