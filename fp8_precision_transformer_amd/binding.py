@@ -34,7 +34,7 @@ TE_F32, TE_BF16, TE_E4M3, TE_E5M2, TE_E8M0, TE_E2M1 = range(6)
 # te_scaling, te_amax_algo, te_granularity
 TE_SCALE_DELAYED, TE_SCALE_CURRENT = 0, 1
 TE_AMAX_MAX, TE_AMAX_MOST_RECENT = 0, 1
-TE_GRAN_TENSOR, TE_GRAN_MX_BLOCK32 = 0, 1
+TE_GRAN_TENSOR, TE_GRAN_MX_BLOCK32, TE_GRAN_MX_BLOCK32_PANEL = 0, 1, 2
 
 FP8_CODES = {"E4M3": TE_E4M3, "E5M2": TE_E5M2, "E2M1": TE_E2M1}
 
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
             L.te_gemm_variant.argtypes = []
             L.te_cast_transpose_dbias_workspace_bytes.restype = ctypes.c_int64
             L.te_cast_transpose_dbias_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
+            L.te_mx_scale_panel_bytes.restype = ctypes.c_int64
+            L.te_mx_scale_panel_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
             _lib = L
     return _lib
 
@@ -164,6 +166,11 @@ def te_cast_transpose(x, out_dtype, mode, margin, scale, scale_inv, amax, out_ro
     _check(lib().te_cast_transpose(_ptr(x), _hp_code(x), rows, cols, _fp8_code(out_dtype), int(mode),
                                    int(margin), _ptr(scale), _ptr(scale_inv), _ptr(amax), _ptr(out_row),
                                    _ptr(out_col), _stream(stream)))
+
+
+def te_mx_scale_panel_bytes(rows, cols) -> int:
+    """Bytes of E8M0 scales in the panel layout for [rows, cols] (cols % 128 == 0)."""
+    return int(lib().te_mx_scale_panel_bytes(int(rows), int(cols)))
 
 
 def te_cast_transpose_dbias_workspace_bytes(rows, cols) -> int:

@@ -149,6 +149,11 @@ int64_t te_cast_transpose_dbias_workspace_bytes(int64_t rows, int64_t cols) {
   return ((rows + 127) / 128) * cols * static_cast<int64_t>(sizeof(float));
 }
 
+int64_t te_mx_scale_panel_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0 || cols % 128 != 0) return -1;
+  return ((rows + 255) / 256) * 256 * (cols / 32);
+}
+
 te_status te_cast_transpose_dbias(const void* x, int x_dtype, int64_t rows, int64_t cols, int out_dtype,
                                   int mode, int margin, float* scale, float* scale_inv, float* amax,
                                   uint8_t* out_row, uint8_t* out_col, float* dbias, void* workspace,
@@ -218,7 +223,11 @@ static te_status gemm_impl(const void* a, int a_dtype, const void* a_scale, cons
   if (m < 0 || n < 0 || k < 0) return fail(TE_ERR_SHAPE, "negative GEMM shape");
   if (n % 16 != 0 || k % 16 != 0)
     return fail(TE_ERR_SHAPE, "n and k must be multiples of 16 (got n=%lld k=%lld)", (long long)n, (long long)k);
-  if (gran != TE_GRAN_TENSOR && gran != TE_GRAN_MX_BLOCK32) return fail(TE_ERR_ARG, "bad granularity %d", gran);
+  if (gran != TE_GRAN_TENSOR && gran != TE_GRAN_MX_BLOCK32 && gran != TE_GRAN_MX_BLOCK32_PANEL)
+    return fail(TE_ERR_ARG, "bad granularity %d", gran);
+  const bool panel = gran == TE_GRAN_MX_BLOCK32_PANEL;
+  if (panel) gran = TE_GRAN_MX_BLOCK32;  // same checks as the row-major MX layout, plus k % 128
+  if (panel && k % 128 != 0) return fail(TE_ERR_SHAPE, "MX panel scales need k %% 128 == 0 (got k=%lld)", (long long)k);
   const bool bf16 = a_dtype == TE_BF16 && b_dtype == TE_BF16;
   const bool fp4 = a_dtype == TE_E2M1 && b_dtype == TE_E2M1;
   if (!bf16 && !fp4 && !(is_fp8(a_dtype) && is_fp8(b_dtype)))
@@ -258,6 +267,7 @@ static te_status gemm_impl(const void* a, int a_dtype, const void* a_scale, cons
   g.a_fmt = a_dtype;
   g.b_fmt = b_dtype;
   g.mx = gran == TE_GRAN_MX_BLOCK32;
+  g.mx_panel = panel ? 1 : 0;
   g.bias_bf16 = bias_dtype == TE_BF16;
   g.d_bf16 = d_dtype == TE_BF16;
   g.accumulate = accumulate;

@@ -372,17 +372,21 @@ __device__ __forceinline__ int f8(int row) { return (row & 7) ^ ((row >> 3) & 3)
 // ============================================================================
 constexpr int NT8 = 512;
 
-template <int KIND, int AF, int BF>
+template <int KIND, int AF, int BF, bool PANEL = false>
 __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
   constexpr bool MX4 = KIND == KIND_MX4;
   constexpr bool MX = KIND == KIND_MX || MX4;
+  // PANEL (MX only): the E8M0 scales come in the panel layout, so every wave loads the
+  // scales of its own rows straight into registers as whole lines, and LDS holds A in
+  // two stage slots and B in three, as for FP8.
+  constexpr bool RSC = MX && PANEL;
   // The two groups share the global->LDS loads, each in its own memory phases: group 0
   // loads A, group 1 loads B.  FP8/BF16 (SPLIT): A in two stage slots, B in three.  MX:
   // two slots each (group 0 also loads the scales), plus per stage slot the E8M0 block
   // scales of the stage's 128 bytes of each row: one dword (four blocks of 32 FP8
   // elements) per row of A (1 KB) and of B (1 KB); MXFP4 two dwords (eight blocks of 32
   // E2M1 elements), kept as four 1 KB arrays (A dword 0, A dword 1, B dword 0, B dword 1).
-  constexpr bool SPLIT = !MX;
+  constexpr bool SPLIT = !MX || PANEL;
   constexpr int kScOff = 2 * kPB, kScSlot = MX4 ? 4096 : 2048;
   constexpr int kLds = SPLIT ? kPB + 3 * kPairOp : 2 * kPB + 2 * kScSlot;
   static_assert(kLds <= 160 * 1024, "LDS budget");
@@ -430,6 +434,40 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
                      static_cast<uint32_t>(rows_b) * p.kblocks);
   }
   const uint32_t sc_off = static_cast<uint32_t>(q4 * 64 + lane) * static_cast<uint32_t>(p.kblocks);
+  const int S = (p.KB + PK - 1) / PK;  // 128-byte k stages (a ragged end reads as zeros)
+  // PANEL scales: in the panel layout the dword of row r and 128-element group g is
+  // dword ((r / 256) * G + g) * 256 + r % 256, G = k / 128; the tile's rows are one
+  // panel (m0 and n0 are multiples of 256), so a stage's dwords of 64 consecutive rows
+  // are 256 contiguous bytes.  Lane l holds A rows wm + l and wm + 64 + l (row groups
+  // lk and 2 + lk of its fragments) and B row wn + l (group lk); the scales of the
+  // other half-wave's row groups come by a lane swap when a stage is packed.  Two
+  // stages (a window) are loaded at a time, one window ahead.  Rows past m or n read
+  // the padding of the last panel: their outputs are never stored.
+  constexpr int SDW = MX4 ? 2 : 1;  // scale dwords per row and stage
+  constexpr int WDW = 2 * SDW;      // per row and window of two stages
+  const uint32_t* scA0 = nullptr;
+  const uint32_t* scA1 = nullptr;
+  const uint32_t* scB = nullptr;
+  if constexpr (RSC) {
+    const int64_t G = p.kblocks / 4;
+    scA0 = static_cast<const uint32_t*>(p.a_scale) + (static_cast<int64_t>(m0 / BM) * G) * 256 + wm + lane;
+    scA1 = scA0 + 64;
+    scB = static_cast<const uint32_t*>(p.b_scale) + (static_cast<int64_t>(n0 / BN) * G) * 256 + wn + lane;
+  }
+  uint32_t nA0[WDW], nA1[WDW], nB[WDW], cA0[WDW], cA1[WDW], cB[WDW];
+  // Stage 2w exists; past the row's last stage the index is clamped to its last dword
+  // (read, never used).  The loads are unconditional: a conditional one would make the
+  // compiler wait on the register's earlier load, and so on every older load in flight.
+  const int last_dw = S * SDW - 1;
+  auto load_window = [&](int w) {
+#pragma unroll
+    for (int d = 0; d < WDW; ++d) {
+      const int64_t i = static_cast<int64_t>(min(w * WDW + d, last_dw)) * 256;
+      nA0[d] = scA0[i];
+      nA1[d] = scA1[i];
+      nB[d] = scB[i];
+    }
+  };
   auto issue_scales = [&](auto SLOT, int st) {
     constexpr int slot = decltype(SLOT)::value;
     if constexpr (MX) {
@@ -503,7 +541,59 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
     constexpr int slot = decltype(SLOT)::value;
     constexpr int part = decltype(PART)::value;
     const int boff = (SPLIT ? st % 3 : slot) * kPairOp;
-    if constexpr (MX4) {
+    if constexpr (RSC) {
+      if constexpr (part == 0) {
+        // stage parity = A slot: an even stage opens a window (its scales are in the
+        // loaded window, which then becomes the current one), an odd stage closes it
+        constexpr bool opens = slot == 0;
+        uint32_t A0[SDW], A1[SDW], Bv[SDW];
+#pragma unroll
+        for (int d = 0; d < SDW; ++d) {
+          A0[d] = opens ? nA0[d] : cA0[SDW + d];
+          A1[d] = opens ? nA1[d] : cA1[SDW + d];
+          Bv[d] = opens ? nB[d] : cB[SDW + d];
+        }
+        if constexpr (opens) {
+#pragma unroll
+          for (int d = 0; d < WDW; ++d) {
+            cA0[d] = nA0[d];
+            cA1[d] = nA1[d];
+            cB[d] = nB[d];
+          }
+        }
+        // row groups: the half-waves hold groups (0, 2) and (1, 3) of A, 0 and 1 of B;
+        // v_permlane32_swap of a register with itself gives every lane the value of lane
+        // l % 32 (lower half-wave) and of lane l % 32 + 32 (upper half-wave)
+        uint32_t G4[4][SDW], H2[2][SDW];
+#pragma unroll
+        for (int d = 0; d < SDW; ++d) {
+          const auto x0 = __builtin_amdgcn_permlane32_swap(A0[d], A0[d], false, false);
+          const auto x1 = __builtin_amdgcn_permlane32_swap(A1[d], A1[d], false, false);
+          const auto xb = __builtin_amdgcn_permlane32_swap(Bv[d], Bv[d], false, false);
+          G4[0][d] = x0[0];
+          G4[1][d] = x0[1];
+          G4[2][d] = x1[0];
+          G4[3][d] = x1[1];
+          H2[0][d] = xb[0];
+          H2[1][d] = xb[1];
+        }
+        // keep the bytes of this lane's blocks (lk, 2 + lk of each dword)
+        auto pick = [&](uint32_t w0, uint32_t w1) {
+          return ((w0 >> (8 * lk)) & 0x00ff00ffu) | (((w1 >> (8 * lk)) & 0x00ff00ffu) << 8);
+        };
+        if constexpr (MX4) {
+          // dword 0 of a row holds blocks 0-3 of the stage, dword 1 blocks 4-7
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sa4[i] = pick(G4[i][0], G4[i][SDW - 1]);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) sb4[j] = pick(H2[j][0], H2[j][SDW - 1]);
+        } else {
+          sa2[0] = pick(G4[0][0], G4[1][0]);
+          sa2[1] = pick(G4[2][0], G4[3][0]);
+          sb1 = pick(H2[0][0], H2[1][0]);
+        }
+      }
+    } else if constexpr (MX4) {
       if constexpr (part == 0) {
         // dword 0 of a row holds blocks 0-3 of the stage, dword 1 blocks 4-7; keep the
         // bytes of this lane's blocks: (b lk, b 2+lk, b 4+lk, b 6+lk) -> bytes (0, 2, 1, 3)
@@ -626,8 +716,7 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
     }
   };
 
-  const int S = (p.KB + PK - 1) / PK;  // 128-byte k stages (a ragged end reads as zeros)
-  const int T = S * PPS;               // phases per group
+  const int T = S * PPS;  // phases per group
 
   // Both groups run the same loop body, compute part u | barrier | read part u+1 |
   // barrier, so compute and fragment reads are one code path; group 1 runs it one
@@ -640,7 +729,9 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
   // after the last part, when both groups have read that slot.
   if constexpr (SPLIT) {
     // group 0 loads A of stages 0 and 1, group 1 B of stages 0, 1 and (after the
-    // prologue) 2; each waits for its stage-0 half before the first barrier
+    // prologue) 2; each waits for its stage-0 half (and, PANEL, the scales of stages 0
+    // and 1, issued first) before the first barrier
+    if constexpr (RSC) load_window(0);
     if (grp == 0) {
       issue_a(ic<0>{}, 0);
       if (S > 1) issue_a(ic<1>{}, 1);
@@ -703,15 +794,24 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
         for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(acc[i][j]));
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (last_part && grp == 0 && s + 1 < S) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));  // stage s+1 landed
+    // PANEL: loads and waits do not depend on s (past the last stage they read zeros
+    // into a free slot), so every path through the loop has the same loads in flight and
+    // the compiler's waits for the scale registers count exactly the younger loads
+    constexpr bool kUncond = RSC;
+    if (last_part && grp == 0 && (kUncond || s + 1 < S)) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));  // stage s+1 landed
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     if (u + 1 < T) read_part(ic<nslot>{}, ic<npart>{}, last_part ? s + 1 : s);
     if constexpr (SPLIT) {
-      if (last_part && grp == 0 && s + 2 < S) issue_a(ic<slot>{}, s + 2);  // the A slot of stage s is free
+      // PANEL: the first phase of a window (part 0 of an even stage) loads the next
+      // window's scales; the part-0 read of its first stage comes three memory phases later
+      if constexpr (RSC) {
+        if (uu == 0) load_window(s / 2 + 1);
+      }
+      if (last_part && grp == 0 && (kUncond || s + 2 < S)) issue_a(ic<slot>{}, s + 2);  // the A slot of stage s is free
       if (last_part && grp == 1) {
-        if (s + 2 < S) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));  // B of stage s+2 landed
-        if (s + 3 < S) issue_b(s + 3);                                // into the B slot of stage s
+        if (kUncond || s + 2 < S) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));  // B of stage s+2 landed
+        if (kUncond || s + 3 < S) issue_b(s + 3);                                // into the B slot of stage s
       }
     } else {
       if (last_part && grp == 0 && s + 2 < S) {  // the slot of stage s is free
@@ -742,6 +842,9 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
   if constexpr (PPS == 2) {
     if (u + 2 < T) iter(ic<2>{}, u + 2);
   }
+  // PANEL: loads issued past the last stage still write LDS; drain them before the
+  // epilogue stages the output there
+  if constexpr (RSC) __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
   if (grp == 0) __builtin_amdgcn_s_barrier();
 
   // ---- epilogue: scale, bias, round; staged through LDS for full-row 16-byte stores ----
@@ -830,17 +933,17 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
 
 thread_local const char* g_last_variant = "none";
 
-template <int KIND, int AF, int BF>
+template <int KIND, int AF, int BF, bool PANEL = false>
 hipError_t run(Params p, hipStream_t s, const char* name) {
   g_last_variant = name;
   const int nb = p.nbm * p.nbn;
-  if (KIND == KIND_MX && (p.kblocks & 3) != 0) {
+  if (KIND == KIND_MX && !PANEL && (p.kblocks & 3) != 0) {
     // a k that is not a multiple of 128 leaves a partial scale dword per stage: the
     // two-stage kernel fills it per byte
     g_last_variant = "gemm_mx_256x256_twostage";
     hipLaunchKernelGGL((k_gemm<KIND_MX, AF, BF>), dim3(nb), dim3(NT), 0, s, p);
   } else {
-    hipLaunchKernelGGL((k_gemm4<KIND, AF, BF>), dim3(nb), dim3(NT8), 0, s, p);
+    hipLaunchKernelGGL((k_gemm4<KIND, AF, BF, PANEL>), dim3(nb), dim3(NT8), 0, s, p);
   }
   return hipGetLastError();
 }
@@ -872,7 +975,16 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   // f8f6f4 format codes: 0 = E4M3, 1 = E5M2
   const int af = (g.a_fmt == E5M2) ? 1 : 0, bf = (g.b_fmt == E5M2) ? 1 : 0;
   if (g.a_fmt == BF16) return run<KIND_BF16, 0, 0>(p, s, "gemm4_bf16_256x256_pingpong");
-  if (g.a_fmt == E2M1) return run<KIND_MX4, 4, 4>(p, s, "gemm4_mxfp4_e2m1_e2m1_256x256_pingpong");
+  if (g.a_fmt == E2M1) {
+    if (g.mx_panel) return run<KIND_MX4, 4, 4, true>(p, s, "gemm4_mxfp4_e2m1_e2m1_256x256_pingpong_panel");
+    return run<KIND_MX4, 4, 4>(p, s, "gemm4_mxfp4_e2m1_e2m1_256x256_pingpong");
+  }
+  if (g.mx && g.mx_panel) {
+    if (af == 0 && bf == 0) return run<KIND_MX, 0, 0, true>(p, s, "gemm4_mx_e4m3_e4m3_256x256_pingpong_panel");
+    if (af == 1 && bf == 0) return run<KIND_MX, 1, 0, true>(p, s, "gemm4_mx_e5m2_e4m3_256x256_pingpong_panel");
+    if (af == 0 && bf == 1) return run<KIND_MX, 0, 1, true>(p, s, "gemm4_mx_e4m3_e5m2_256x256_pingpong_panel");
+    return run<KIND_MX, 1, 1, true>(p, s, "gemm4_mx_e5m2_e5m2_256x256_pingpong_panel");
+  }
   if (g.mx) {
     if (af == 0 && bf == 0) return run<KIND_MX, 0, 0>(p, s, "gemm4_mx_e4m3_e4m3_256x256_pingpong");
     if (af == 1 && bf == 0) return run<KIND_MX, 1, 0>(p, s, "gemm4_mx_e5m2_e4m3_256x256_pingpong");

@@ -45,6 +45,7 @@ struct GemmArgs {
   int64_t m, n, k;       // elements
   int a_fmt, b_fmt;      // E4M3 / E5M2 / BF16 / E2M1 (MX only, both operands)
   int mx;                // 1: MX block-32 scales
+  int mx_panel;          // 1: MX scales in the panel layout (k % 128 == 0)
   int bias_bf16;         // bias dtype: 0 f32, 1 bf16
   int d_bf16;            // output dtype: 0 f32, 1 bf16
   int accumulate;        // 1: fp32 D = fl32(D_old + result)

@@ -81,17 +81,19 @@ def _operands(kind, m, n, k, g, dev, fa="E4M3", fb="E4M3"):
     def codes(r, c):
         return (torch.randint(0x18, 0x48, (r, c), device=dev, generator=g, dtype=torch.int32) |
                 (torch.randint(0, 2, (r, c), device=dev, generator=g, dtype=torch.int32) << 7)).to(torch.uint8)
-    if kind == "mx4":  # packed E2M1 pairs: every byte is a valid pair of codes
+    def unit_scales(rows, panel):  # E8M0 127 in the row-major or the panel layout
+        if panel:
+            return torch.full((B.te_mx_scale_panel_bytes(rows, k),), 127, dtype=torch.uint8, device=dev)
+        return torch.full((rows, k // 32), 127, dtype=torch.uint8, device=dev)
+    panel = kind in ("mxp", "mx4p")
+    gran = B.TE_GRAN_MX_BLOCK32_PANEL if panel else B.TE_GRAN_MX_BLOCK32
+    if kind in ("mx4", "mx4p"):  # packed E2M1 pairs: every byte is a valid pair of codes
         a = torch.randint(0, 256, (m, k // 2), device=dev, generator=g, dtype=torch.int32).to(torch.uint8)
         b = torch.randint(0, 256, (n, k // 2), device=dev, generator=g, dtype=torch.int32).to(torch.uint8)
-        sa = torch.full((m, k // 32), 127, dtype=torch.uint8, device=dev)
-        sb = torch.full((n, k // 32), 127, dtype=torch.uint8, device=dev)
-        return a, "E2M1", sa, b, "E2M1", sb, B.TE_GRAN_MX_BLOCK32
+        return a, "E2M1", unit_scales(m, panel), b, "E2M1", unit_scales(n, panel), gran
     a, b = codes(m, k), codes(n, k)
-    if kind == "mx":
-        sa = torch.full((m, k // 32), 127, dtype=torch.uint8, device=dev)
-        sb = torch.full((n, k // 32), 127, dtype=torch.uint8, device=dev)
-        return a, fa, sa, b, fb, sb, B.TE_GRAN_MX_BLOCK32
+    if kind in ("mx", "mxp"):
+        return a, fa, unit_scales(m, panel), b, fb, unit_scales(n, panel), gran
     one = torch.ones(1, dtype=torch.float32, device=dev)
     return a, fa, one, b, fb, one, B.TE_GRAN_TENSOR
 
@@ -293,7 +295,7 @@ def main():
     c.add_argument("--iters", type=int, default=20)
     c.add_argument("--warmup", type=int, default=3)
     ly = sub.add_parser("layer")
-    ly.add_argument("--kind", choices=["fp8", "mx", "mx4", "bf16"], default="fp8")
+    ly.add_argument("--kind", choices=["fp8", "mx", "mxp", "mx4", "mx4p", "bf16"], default="fp8")
     ly.add_argument("--iters", type=int, default=10)
     ly.add_argument("--warmup", type=int, default=2)
     lb = sub.add_parser("lib")

@@ -82,7 +82,7 @@ typedef enum { TE_AMAX_MAX = 0, TE_AMAX_MOST_RECENT = 1 } te_amax_algo;
 
 /* TENSOR: one fp32 scale_inv per operand.  MX_BLOCK32: one E8M0 exponent per 32
  * consecutive elements along K (MXFP8, [TE-summary] "主な機能"). */
-typedef enum { TE_GRAN_TENSOR = 0, TE_GRAN_MX_BLOCK32 = 1 } te_granularity;
+typedef enum { TE_GRAN_TENSOR = 0, TE_GRAN_MX_BLOCK32 = 1, TE_GRAN_MX_BLOCK32_PANEL = 2 } te_granularity;
 
 /*
  * te_amax_cast -- amax reduction and scaled saturating cast of one tensor to FP8.
@@ -236,6 +236,15 @@ te_status te_scale_update(float* amax_history, float* scale, float* scale_inv,
  *              [n, k/2] bytes, same scale arrays, k % 256 == 0 ([LP-opt]
  *              "実モデルにおける結果の解釈": FP4 GEMMs against MXFP8 on the same
  *              shapes; the matrix core applies E8M0 scales per 32 elements).
+ *   gran = TE_GRAN_MX_BLOCK32_PANEL: as TE_GRAN_MX_BLOCK32 with the same scale
+ *              values in the panel layout (te_mx_scale_panel_bytes): rows in panels
+ *              of 256; in a panel, the dwords (four block scales) of one 128-element
+ *              group of k for the 256 rows are contiguous; byte of (row r, block b) =
+ *              4 ((r / 256) (k / 128) + b / 4) 256 + 4 (r % 256) + b % 4.  a_scale
+ *              and b_scale hold te_mx_scale_panel_bytes(m, k) and (n, k) bytes;
+ *              padding rows are read and never used.  k % 128 == 0 (MXFP4:
+ *              k % 256 == 0).  Same results as TE_GRAN_MX_BLOCK32, bit for bit; the
+ *              GEMM loads a stage's scales as whole cache lines.
  *   acc        fp32 accumulation on the matrix cores.
  *   bias       [n] of bias_dtype (TE_F32 or TE_BF16, widened to fp32) or NULL.
  *   d          [m, n] of d_dtype (TE_BF16, rounded to nearest even, or TE_F32).
@@ -314,6 +323,11 @@ te_status te_mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t co
 te_status te_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols,
                             uint8_t* out_row, uint8_t* scale_row,
                             uint8_t* out_col, uint8_t* scale_col, void* stream);
+
+/* Bytes of E8M0 scales in the panel layout (see te_fp8_gemm) for a matrix of `rows`
+ * rows and `cols` elements per row: ceil(rows / 256) * 256 * cols / 32.  Host only;
+ * -1 if rows < 0 or cols is not a non-negative multiple of 128. */
+int64_t te_mx_scale_panel_bytes(int64_t rows, int64_t cols);
 
 /* Text of the last error on the calling thread ("" if none).  Host pointer owned
  * by the library, valid until the next call on this thread. */

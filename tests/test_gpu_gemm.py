@@ -318,3 +318,44 @@ def test_gemm_accumulate_exact_integer_operands():
     with pytest.raises(ValueError):
         B.te_fp8_gemm(dev_u8(a), "E4M3", scalar(0.5), dev_u8(b), "E4M3", scalar(4.0), _out(m, n, "bf16"),
                       accumulate=True)
+
+
+# Panel-layout scales (the oracle's permutation of the same E8M0 values): bit-identical to
+# the row-major MX GEMM; stage counts 1 to 5 and 32, ragged m and n (padding rows of the
+# last panel are read and never used)
+@pytest.mark.parametrize("mnk", [(64, 64, 128), (200, 304, 256), (256, 512, 384), (300, 272, 512),
+                                 (520, 400, 640), (1024, 768, 768), (256, 256, 4096)], ids=str)
+@pytest.mark.parametrize("fa,fb", [("E4M3", "E4M3"), ("E5M2", "E4M3")])
+def test_mx_gemm_panel_scales_bit_identical(mnk, fa, fb):
+    m, n, k = mnk
+    sd = _seed(mnk, fa, fb, "panel")
+    xa = synth.activations((m, k), 14, sd, 0, 0) if fa == "E4M3" else synth.grads((m, k), 14, sd, 0, 0)
+    xb = synth.normal((n, k), 0.02, 14, sd, 1, 0)
+    qa, ea = O.mxfp8_quantize(xa, FMTS[fa])
+    qb, eb = O.mxfp8_quantize(xb, FMTS[fb])
+    pa, pb = O.mx_scales_panel(ea), O.mx_scales_panel(eb)
+    assert pa.size == B.te_mx_scale_panel_bytes(m, k) and pb.size == B.te_mx_scale_panel_bytes(n, k)
+    bias = synth.normal((n,), 0.02, 14, sd, 2, 0)
+    for odt in ("bf16", "f32"):
+        d1, d2 = _out(m, n, odt), _out(m, n, odt)
+        B.te_fp8_gemm(dev_u8(qa), fa, dev_u8(ea), dev_u8(qb), fb, dev_u8(eb), d1, bias=dev_f32(bias),
+                      gran=B.TE_GRAN_MX_BLOCK32)
+        B.te_fp8_gemm(dev_u8(qa), fa, dev_u8(pa), dev_u8(qb), fb, dev_u8(pb), d2, bias=dev_f32(bias),
+                      gran=B.TE_GRAN_MX_BLOCK32_PANEL)
+        assert B.te_gemm_variant().endswith("_panel")
+        assert torch.equal(d1, d2), (mnk, odt)
+    ref = O.gemm_mx(qa, ea, FMTS[fa], qb, eb, FMTS[fb], bias=bias, out="f32")
+    av = O.decode_table(FMTS[fa])[qa] * np.repeat(O.e8m0_to_float(ea), 32, axis=1)
+    bv = O.decode_table(FMTS[fb])[qb] * np.repeat(O.e8m0_to_float(eb), 32, axis=1)
+    check_fp8_gemm(host(d2), ref, av, bv, 1.0, "f32")
+
+
+def test_mx_gemm_panel_rejects_k_not_multiple_of_128():
+    m, n, k = 64, 64, 96
+    a = torch.zeros((m, k), dtype=torch.uint8, device=DEV)
+    s = torch.full((4096,), 127, dtype=torch.uint8, device=DEV)
+    d = torch.empty((m, n), dtype=torch.float32, device=DEV)
+    with pytest.raises(B.TEError):
+        B.te_fp8_gemm(a, "E4M3", s, a, "E4M3", s, d, gran=B.TE_GRAN_MX_BLOCK32_PANEL)
+    assert B.te_mx_scale_panel_bytes(300, 512) == 512 * 512 // 32
+    assert B.te_mx_scale_panel_bytes(300, 96) == -1

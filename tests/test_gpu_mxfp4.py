@@ -220,3 +220,21 @@ def test_mxfp4_gemm_full_5b_shape_sampled(stage):
     ref = F.gemm_mxfp4(qa[rows], ea[rows], qb[cols], eb[cols], out="bf16")
     check_fp8_gemm(host(d)[np.ix_(rows, cols)], ref, F.dequantize(qa[rows], ea[rows]),
                    F.dequantize(qb[cols], eb[cols]), 1.0, "bf16")
+
+
+# the panel layout of the same scales: bit-identical to the row-major MXFP4 GEMM
+@pytest.mark.parametrize("mnk", [(32, 32, 256), (300, 272, 512), (520, 400, 1280), (1, 16, 256),
+                                 (256, 256, 4096)], ids=str)
+def test_mxfp4_gemm_panel_scales_bit_identical(mnk):
+    m, n, k = mnk
+    sd = _seed(mnk, "panel")
+    qa, ea, qb, eb = _mx4_operands(m, n, k, sd)
+    pa, pb = O.mx_scales_panel(ea), O.mx_scales_panel(eb)
+    for odt in ("bf16", "f32"):
+        d1, d2 = _out(m, n, odt), _out(m, n, odt)
+        B.te_fp8_gemm(dev_u8(qa), "E2M1", dev_u8(ea), dev_u8(qb), "E2M1", dev_u8(eb), d1,
+                      gran=B.TE_GRAN_MX_BLOCK32)
+        B.te_fp8_gemm(dev_u8(qa), "E2M1", dev_u8(pa), dev_u8(qb), "E2M1", dev_u8(pb), d2,
+                      gran=B.TE_GRAN_MX_BLOCK32_PANEL)
+        assert B.te_gemm_variant() == "gemm4_mxfp4_e2m1_e2m1_256x256_pingpong_panel"
+        assert torch.equal(d1, d2), (mnk, odt)
