@@ -10,7 +10,8 @@ One step = one pass of the whole path over the layer in every mode:
                        history 16, max) + GEMM; one scale-update launch per format
   fp8_current_autocast two-pass current scaling before each GEMM + GEMM
   fp8_current_prequant operands quantized once before timing; GEMM kernels only
-  mxfp8_autocast       MXFP8 1x32 quantization before each GEMM + MX GEMM
+  mxfp8_autocast       MXFP8 1x32 quantization before each GEMM + MX GEMM (the E8M0 scales in
+                       the panel layout the GEMM loads as whole lines)
   mxfp8_prequant       MX GEMM kernels only
   mxfp4_autocast       MXFP4 (E2M1 elements, E8M0 per 32) quantization before each
                        GEMM + the E2M1 x E2M1 scaled-MFMA GEMM
@@ -51,21 +52,21 @@ MI355X_HBM_GBS = 8000.0           # HBM3E (published)
 MEASURED_TRAFFIC = {
     # FP8 GEMM: mean over the layer's 12 GEMM launches (microbench layer --kind fp8)
     "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                 "sha256": "6384227bc9413cdd49a7b1283792d2e65aeebff892ce18ed647383dd71fa3e07",
-                 "bytes_per_launch": 1549302390},
+                 "sha256": "9b482bceb26ee336f636c99f123bbd9c29c6d1a9ff5386e4ea9b00538ac4dcba",
+                 "bytes_per_launch": 1516552553},
     # delayed-scaling quantizers of one layer in autocast mode (24 casts and cast-transposes),
     # summed over the layer's launches (bench.py --modes fp8_delayed_autocast under --pmc)
     "quant_delayed_layer": {"source": "fp8_precision_transformer_amd/csrc/quant.hip",
-                            "sha256": "895553736c8c076ce66d8232ff90bbe9cec91aebb456f9e8d2affce73b9bc0af",
-                            "bytes_per_launch": 7452474237},
-    # MXFP8 GEMM: the same 12 shapes (microbench layer --kind mx)
+                            "sha256": "b19ed0d46a4a32b5b7155be60a0d7f802751bec53dc43152bc6d2b8290b5c792",
+                            "bytes_per_launch": 7452341860},
+    # MXFP8 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mxp)
     "gemm_mxfp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "6384227bc9413cdd49a7b1283792d2e65aeebff892ce18ed647383dd71fa3e07",
-                   "bytes_per_launch": 1572450863},
-    # MXFP4 GEMM: the same 12 shapes (microbench layer --kind mx4)
+                   "sha256": "9b482bceb26ee336f636c99f123bbd9c29c6d1a9ff5386e4ea9b00538ac4dcba",
+                   "bytes_per_launch": 1558835362},
+    # MXFP4 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mx4p)
     "gemm_mxfp4": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "6384227bc9413cdd49a7b1283792d2e65aeebff892ce18ed647383dd71fa3e07",
-                   "bytes_per_launch": 877954792},
+                   "sha256": "9b482bceb26ee336f636c99f123bbd9c29c6d1a9ff5386e4ea9b00538ac4dcba",
+                   "bytes_per_launch": 881457028},
 }
 
 
@@ -162,15 +163,17 @@ def main():
     cur = new_cur()
     # BF16 transposed operands (materialised once; the BF16 GEMM is TN)
     BT = {}
-    # MX buffers
+    # MX buffers; the E8M0 scales in the panel layout the GEMM loads as whole lines
+    ps = lambda r, c: u8(B.te_mx_scale_panel_bytes(r, c))  # noqa: E731
+
     def mx_buffers():
         mb = {}
         for w in weights:
             K, N = w.in_features, w.out_features
             mb[w.name] = dict(
-                x=u8(M, K), xs=u8(M, K // 32), xT=u8(K, M), xTs=u8(K, M // 32),
-                w=u8(N, K), ws=u8(N, K // 32), wT=u8(K, N), wTs=u8(K, N // 32),
-                dy=u8(M, N), dys=u8(M, N // 32), dyT=u8(N, M), dyTs=u8(N, M // 32))
+                x=u8(M, K), xs=ps(M, K), xT=u8(K, M), xTs=ps(K, M),
+                w=u8(N, K), ws=ps(N, K), wT=u8(K, N), wTs=ps(K, N),
+                dy=u8(M, N), dys=ps(M, N), dyT=u8(N, M), dyTs=ps(N, M))
         return mb
 
     MXB = mx_buffers()
@@ -181,9 +184,9 @@ def main():
         for w in weights:
             K, N = w.in_features, w.out_features
             mb[w.name] = dict(
-                x=u8(M, K // 2), xs=u8(M, K // 32), xT=u8(K, M // 2), xTs=u8(K, M // 32),
-                w=u8(N, K // 2), ws=u8(N, K // 32), wT=u8(K, N // 2), wTs=u8(K, N // 32),
-                dy=u8(M, N // 2), dys=u8(M, N // 32), dyT=u8(N, M // 2), dyTs=u8(N, M // 32))
+                x=u8(M, K // 2), xs=ps(M, K), xT=u8(K, M // 2), xTs=ps(K, M),
+                w=u8(N, K // 2), ws=ps(N, K), wT=u8(K, N // 2), wTs=ps(K, N),
+                dy=u8(M, N // 2), dys=ps(M, N), dyT=u8(N, M // 2), dyTs=ps(N, M))
         return mb
 
     modes_all = ["bf16", "fp8_delayed_autocast", "fp8_current_autocast", "fp8_current_prequant",
@@ -228,29 +231,29 @@ def main():
     def quant_mx(w, stage, bset=None):
         b = (bset or MXB)[w.name]
         if stage == "fprop":
-            B.te_mxfp8_quantize(X[w.name], E4, b["x"], b["xs"])
-            B.te_mxfp8_quantize(W[w.name], E4, b["w"], b["ws"])
+            B.te_mxfp8_quantize_panel(X[w.name], E4, b["x"], b["xs"])
+            B.te_mxfp8_quantize_panel(W[w.name], E4, b["w"], b["ws"])
             return (b["x"], b["xs"], b["w"], b["ws"])
         if stage == "dgrad":
-            B.te_mxfp8_quantize(DY[w.name], E4, b["dy"], b["dys"])
-            B.te_mxfp8_quantize(W[w.name], E4, None, None, b["wT"], b["wTs"])
+            B.te_mxfp8_quantize_panel(DY[w.name], E4, b["dy"], b["dys"])
+            B.te_mxfp8_quantize_panel(W[w.name], E4, None, None, b["wT"], b["wTs"])
             return (b["dy"], b["dys"], b["wT"], b["wTs"])
-        B.te_mxfp8_quantize(DY[w.name], E4, None, None, b["dyT"], b["dyTs"])
-        B.te_mxfp8_quantize(X[w.name], E4, None, None, b["xT"], b["xTs"])
+        B.te_mxfp8_quantize_panel(DY[w.name], E4, None, None, b["dyT"], b["dyTs"])
+        B.te_mxfp8_quantize_panel(X[w.name], E4, None, None, b["xT"], b["xTs"])
         return (b["dyT"], b["dyTs"], b["xT"], b["xTs"])
 
     def quant_mx4(w, stage, bset=None):
         b = (bset or MX4B)[w.name]
         if stage == "fprop":
-            B.te_mxfp4_quantize(X[w.name], b["x"], b["xs"])
-            B.te_mxfp4_quantize(W[w.name], b["w"], b["ws"])
+            B.te_mxfp4_quantize_panel(X[w.name], b["x"], b["xs"])
+            B.te_mxfp4_quantize_panel(W[w.name], b["w"], b["ws"])
             return (b["x"], b["xs"], b["w"], b["ws"])
         if stage == "dgrad":
-            B.te_mxfp4_quantize(DY[w.name], b["dy"], b["dys"])
-            B.te_mxfp4_quantize(W[w.name], None, None, b["wT"], b["wTs"])
+            B.te_mxfp4_quantize_panel(DY[w.name], b["dy"], b["dys"])
+            B.te_mxfp4_quantize_panel(W[w.name], None, None, b["wT"], b["wTs"])
             return (b["dy"], b["dys"], b["wT"], b["wTs"])
-        B.te_mxfp4_quantize(DY[w.name], None, None, b["dyT"], b["dyTs"])
-        B.te_mxfp4_quantize(X[w.name], None, None, b["xT"], b["xTs"])
+        B.te_mxfp4_quantize_panel(DY[w.name], None, None, b["dyT"], b["dyTs"])
+        B.te_mxfp4_quantize_panel(X[w.name], None, None, b["xT"], b["xTs"])
         return (b["dyT"], b["dyTs"], b["xT"], b["xTs"])
 
     prequant_fp8, prequant_mx, prequant_mx4 = {}, {}, {}
@@ -292,11 +295,11 @@ def main():
     def quant_mx_shared(w, stage):
         b = MXS[w.name]
         if stage == "fprop":
-            B.te_mxfp8_quantize(X[w.name], E4, b["x"], b["xs"], b["xT"], b["xTs"])
-            B.te_mxfp8_quantize(W[w.name], E4, b["w"], b["ws"], b["wT"], b["wTs"])
+            B.te_mxfp8_quantize_panel(X[w.name], E4, b["x"], b["xs"], b["xT"], b["xTs"])
+            B.te_mxfp8_quantize_panel(W[w.name], E4, b["w"], b["ws"], b["wT"], b["wTs"])
             return (b["x"], b["xs"], b["w"], b["ws"])
         if stage == "dgrad":
-            B.te_mxfp8_quantize(DY[w.name], E4, b["dy"], b["dys"], b["dyT"], b["dyTs"])
+            B.te_mxfp8_quantize_panel(DY[w.name], E4, b["dy"], b["dys"], b["dyT"], b["dyTs"])
             return (b["dy"], b["dys"], b["wT"], b["wTs"])
         return (b["dyT"], b["dyTs"], b["xT"], b["xTs"])
 
@@ -308,11 +311,11 @@ def main():
 
     def gemm_mx(ops, out):
         a, sa, b, sb = ops
-        B.te_fp8_gemm(a, E4, sa, b, E4, sb, out, gran=B.TE_GRAN_MX_BLOCK32)
+        B.te_fp8_gemm(a, E4, sa, b, E4, sb, out, gran=B.TE_GRAN_MX_BLOCK32_PANEL)
 
     def gemm_mx4(ops, out):
         a, sa, b, sb = ops
-        B.te_fp8_gemm(a, "E2M1", sa, b, "E2M1", sb, out, gran=B.TE_GRAN_MX_BLOCK32)
+        B.te_fp8_gemm(a, "E2M1", sa, b, "E2M1", sb, out, gran=B.TE_GRAN_MX_BLOCK32_PANEL)
 
     def gemm_bf16(w, stage, out):
         t = BT[w.name]
@@ -486,9 +489,9 @@ def main():
                 "avg_launch_ms": round(t_ms / len(gemms), 4), "flop_per_launch": int(flops / len(gemms))}
 
     roof8 = mx_roofline("mxfp8_prequant", MI355X_FP8_PEAK_TFLOPS, "gemm_mxfp8",
-                        "k_gemm4 MXFP8 (E4M3 x E4M3 scaled MFMA, 256x256 tiles, ping-pong); 12 launches per layer")
+                        "k_gemm4 MXFP8 (E4M3 x E4M3 scaled MFMA, E8M0 scales in the panel layout, 256x256 tiles, ping-pong); 12 launches per layer")
     roof4 = mx_roofline("mxfp4_prequant", MI355X_FP4_PEAK_TFLOPS, "gemm_mxfp4",
-                        "k_gemm4 MXFP4 (E2M1 x E2M1 scaled MFMA, 256x256 tiles, ping-pong); 12 launches per layer")
+                        "k_gemm4 MXFP4 (E2M1 x E2M1 scaled MFMA, E8M0 scales in the panel layout, 256x256 tiles, ping-pong); 12 launches per layer")
     roof_q = None
     if "fp8_delayed_autocast" in modes:
         n_el = sum(2 * (M * w.in_features + w.out_features * w.in_features + M * w.out_features) for w in weights)

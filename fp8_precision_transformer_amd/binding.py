@@ -63,6 +63,8 @@ _SIGNATURES = {
     "te_fp8_gemm_accumulate": [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp, _vp],
     "te_mxfp8_quantize": [_vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp],
     "te_mxfp4_quantize": [_vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
+    "te_mxfp8_quantize_panel": [_vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp],
+    "te_mxfp4_quantize_panel": [_vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
 }
 
 
@@ -260,6 +262,28 @@ def te_mxfp4_quantize(x, out_row=None, scale_row=None, out_col=None, scale_col=N
     rows, cols = _2d(x)
     _check(lib().te_mxfp4_quantize(_ptr(x), _hp_code(x), rows, cols, _ptr(out_row), _ptr(scale_row),
                                    _ptr(out_col), _ptr(scale_col), _stream(stream)))
+
+
+def te_mxfp8_quantize_panel(x, elem_dtype, out_row=None, scale_row=None, out_col=None, scale_col=None,
+                            stream=None):
+    """te_mxfp8_quantize with the scales in the panel layout: scale_row uint8
+    [te_mx_scale_panel_bytes(rows, cols)], scale_col [te_mx_scale_panel_bytes(cols, rows)]."""
+    for n, t in (("x", x), ("out_row", out_row), ("scale_row", scale_row), ("out_col", out_col),
+                 ("scale_col", scale_col)):
+        _need(t, n)
+    rows, cols = _2d(x)
+    _check(lib().te_mxfp8_quantize_panel(_ptr(x), _hp_code(x), rows, cols, _fp8_code(elem_dtype), _ptr(out_row),
+                                         _ptr(scale_row), _ptr(out_col), _ptr(scale_col), _stream(stream)))
+
+
+def te_mxfp4_quantize_panel(x, out_row=None, scale_row=None, out_col=None, scale_col=None, stream=None):
+    """te_mxfp4_quantize with the scales in the panel layout (see te_mxfp8_quantize_panel)."""
+    for n, t in (("x", x), ("out_row", out_row), ("scale_row", scale_row), ("out_col", out_col),
+                 ("scale_col", scale_col)):
+        _need(t, n)
+    rows, cols = _2d(x)
+    _check(lib().te_mxfp4_quantize_panel(_ptr(x), _hp_code(x), rows, cols, _ptr(out_row), _ptr(scale_row),
+                                         _ptr(out_col), _ptr(scale_col), _stream(stream)))
 
 
 def version() -> str:

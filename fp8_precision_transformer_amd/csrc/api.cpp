@@ -342,4 +342,47 @@ te_status te_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t co
                     "te_mxfp4_quantize launch");
 }
 
+// MX quantization with the scales in the GEMM's panel layout (te_fp8_gemm with
+// TE_GRAN_MX_BLOCK32_PANEL): bf16 input of whole 128 x 128 tiles only.
+static te_status mx_quantize_panel(const char* name, const void* x, int x_dtype, int64_t rows, int64_t cols,
+                                   int fp4, int elem_dtype, uint8_t* out_row, uint8_t* scale_row, uint8_t* out_col,
+                                   uint8_t* scale_col, void* stream) {
+  if (rows < 0 || cols < 0) return fail(TE_ERR_SHAPE, "negative shape");
+  if (x_dtype != TE_BF16) return fail(TE_ERR_UNSUPPORTED, "%s: panel scales need TE_BF16 input", name);
+  if (!fp4 && !is_fp8(elem_dtype)) return fail(TE_ERR_DTYPE, "elem_dtype must be TE_E4M3 or TE_E5M2");
+  const bool row = out_row || scale_row, col = out_col || scale_col;
+  if (!row && !col) return fail(TE_ERR_NULL, "both output pairs are NULL");
+  if ((out_row == nullptr) != (scale_row == nullptr)) return fail(TE_ERR_NULL, "out_row and scale_row go together");
+  if ((out_col == nullptr) != (scale_col == nullptr)) return fail(TE_ERR_NULL, "out_col and scale_col go together");
+  if (rows % 128 != 0 || cols % 128 != 0)
+    return fail(TE_ERR_UNSUPPORTED, "%s: panel scales need rows and cols multiples of 128 (got %lld x %lld)", name,
+                (long long)rows, (long long)cols);
+  if (cols * 128 * 2 >= (int64_t(1) << 31) || rows * 128 >= (int64_t(1) << 31))
+    return fail(TE_ERR_SHAPE, "%s: a 128-row (column) band must fit 2 GiB", name);
+  if (rows * cols > 0 && !x) return fail(TE_ERR_NULL, "x is NULL");
+  if ((x && !aligned16(x)) || (out_row && !aligned16(out_row)) || (out_col && !aligned16(out_col)) ||
+      (scale_row && !aligned16(scale_row)) || (scale_col && !aligned16(scale_col)))
+    return fail(TE_ERR_ALIGN, "x, outputs and scale arrays must be 16-byte aligned");
+  te_status st = check_device();
+  if (st != TE_OK) return st;
+  log_dispatch(name, row && col ? "tile128x128_row+col_panel" : (row ? "tile128x128_row_panel" : "tile128x128_col_panel"),
+               fp4 ? "E2M1" : (elem_dtype == TE_E5M2 ? "E5M2" : "E4M3"));
+  return hip_status(te::launch_mx_quantize_panel(x, rows, cols, fp4, !fp4 && elem_dtype == TE_E5M2, out_row, scale_row,
+                                                 out_col, scale_col, static_cast<hipStream_t>(stream)),
+                    name);
+}
+
+te_status te_mxfp8_quantize_panel(const void* x, int x_dtype, int64_t rows, int64_t cols, int elem_dtype,
+                                  uint8_t* out_row, uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col,
+                                  void* stream) {
+  return mx_quantize_panel("te_mxfp8_quantize_panel", x, x_dtype, rows, cols, 0, elem_dtype, out_row, scale_row,
+                           out_col, scale_col, stream);
+}
+
+te_status te_mxfp4_quantize_panel(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* out_row,
+                                  uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col, void* stream) {
+  return mx_quantize_panel("te_mxfp4_quantize_panel", x, x_dtype, rows, cols, 1, TE_E4M3, out_row, scale_row, out_col,
+                           scale_col, stream);
+}
+
 }  // extern "C"

@@ -31,6 +31,9 @@ hipError_t launch_scale_update(float* hist, float* scale, float* scale_inv, int 
 hipError_t launch_mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols,
                                  int e5m2, uint8_t* out_row, uint8_t* scale_row,
                                  uint8_t* out_col, uint8_t* scale_col, hipStream_t s);
+hipError_t launch_mx_quantize_panel(const void* x, int64_t rows, int64_t cols, int fp4, int e5m2,
+                                    uint8_t* out_row, uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col,
+                                    hipStream_t s);
 hipError_t launch_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* out_row,
                                  uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col, hipStream_t s);
 

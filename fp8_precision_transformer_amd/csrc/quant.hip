@@ -1007,12 +1007,22 @@ __device__ __forceinline__ void mx_quant8(const uint4& raw, int e, uint32_t& q0,
 
 // FP4: the same tiles written as MXFP4 (four bytes of codes per lane and pass for the
 // row-wise copy, 64 bytes per column of the tile for the column-wise one).
-template <bool E5M2, bool ROW, bool COL, bool FP4 = false>
+// PANEL: the E8M0 scales go out in the GEMM's panel layout: the dword of row r and
+// 128-element group g is dword ((r / 256) * G + g) * 256 + r % 256 (G = groups per row),
+// so a tile's 128 row dwords are 512 contiguous bytes instead of 128 scattered ones.
+template <bool E5M2, bool ROW, bool COL, bool FP4 = false, bool PANEL = false>
 __global__ __launch_bounds__(kThreads) void k_mxfp8_tiles(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                           uint8_t* __restrict__ out_row,
                                                           uint8_t* __restrict__ scale_row,
                                                           uint8_t* __restrict__ out_col,
                                                           uint8_t* __restrict__ scale_col) {
+  // the scale dword of (row r of a copy with `cols` elements per row, group of c0)
+  auto scale_dw = [](uint8_t* base, int64_t r, int64_t cols, int64_t c0) {
+    if constexpr (PANEL)
+      return reinterpret_cast<uint32_t*>(base) + ((r >> 8) * (cols >> 7) + (c0 >> 7)) * 256 + (r & 255);
+    else
+      return reinterpret_cast<uint32_t*>(base + r * (cols / 32) + c0 / 32);
+  };
   constexpr int NP = 8, RPP = 16;  // passes of 16 rows, 16 lanes x 8 elements per row
   __shared__ __attribute__((aligned(16))) uint8_t tile[COL ? kCT * kMxTPitch : 16];
   const int64_t ntc = C / kCT;
@@ -1067,7 +1077,7 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_tiles(const uint16_t* __rest
         const uint32_t k2 = static_cast<uint32_t>(__shfl(static_cast<int>(code), lane + 8, 64));
         const uint32_t k3 = static_cast<uint32_t>(__shfl(static_cast<int>(code), lane + 12, 64));
         if ((lane & 15) == 0)
-          *reinterpret_cast<uint32_t*>(scale_row + r * (C / 32) + c0 / 32) = code | (k1 << 8) | (k2 << 16) | (k3 << 24);
+          *scale_dw(scale_row, r, C, c0) = code | (k1 << 8) | (k2 << 16) | (k3 << 24);
       }
       if constexpr (!COL) {
         if (has1) raw[p] = load1(p, r1, c1);
@@ -1126,8 +1136,7 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_tiles(const uint16_t* __rest
           *reinterpret_cast<uint4*>(out_col + (c0 + c) * (R / 2) + r0 / 2 + 16 * chunk) = v;
         }
         if (t < kCT)
-          *reinterpret_cast<uint32_t*>(scale_col + (c0 + t) * (R / 32) + r0 / 32) =
-              *reinterpret_cast<const uint32_t*>(qs + 4 * t);
+          *scale_dw(scale_col, c0 + t, R, r0) = *reinterpret_cast<const uint32_t*>(qs + 4 * t);
         return;
       }
       uint32_t q[2][8];
@@ -1168,8 +1177,7 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_tiles(const uint16_t* __rest
         *reinterpret_cast<uint4*>(out_col + (c0 + c) * R + r0 + 16 * chunk) = v;
       }
       if (t < kCT)
-        *reinterpret_cast<uint32_t*>(scale_col + (c0 + t) * (R / 32) + r0 / 32) =
-            *reinterpret_cast<const uint32_t*>(qs + 4 * t);
+        *scale_dw(scale_col, c0 + t, R, r0) = *reinterpret_cast<const uint32_t*>(qs + 4 * t);
     }
   };
   int64_t i = blockIdx.x;
@@ -1334,10 +1342,10 @@ hipError_t cast_transpose_t(const T* x, int64_t R, int64_t C, int current, int m
   return hipGetLastError();
 }
 
-template <bool E5M2, bool ROW, bool COL, bool FP4 = false>
+template <bool E5M2, bool ROW, bool COL, bool FP4 = false, bool PANEL = false>
 void mx_tiles_launch(const uint16_t* x, int64_t R, int64_t C, uint8_t* out_row, uint8_t* scale_row,
                      uint8_t* out_col, uint8_t* scale_col, hipStream_t st) {
-  const auto fn = k_mxfp8_tiles<E5M2, ROW, COL, FP4>;
+  const auto fn = k_mxfp8_tiles<E5M2, ROW, COL, FP4, PANEL>;
   const int g = persistent_grid(reinterpret_cast<const void*>(fn), (R / kCT) * (C / kCT), 1, COL ? kCapMxCol : kCapMxRow);
   hipLaunchKernelGGL(fn, dim3(g), dim3(kThreads), 0, st, x, R, C, out_row, scale_row, out_col, scale_col);
 }
@@ -1468,6 +1476,28 @@ hipError_t launch_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int64
   else
     hipLaunchKernelGGL(k_mxfp4<float>, grid, dim3(kThreads), 0, s, static_cast<const float*>(x), rows, cols, out_row,
                        scale_row, out_col, scale_col);
+  return hipGetLastError();
+}
+
+template <bool E5M2, bool FP4>
+void mx_panel_launch(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* out_row, uint8_t* scale_row,
+                     uint8_t* out_col, uint8_t* scale_col, hipStream_t s) {
+  const bool row = out_row != nullptr, col = out_col != nullptr;
+  if (row && col) mx_tiles_launch<E5M2, true, true, FP4, true>(x, rows, cols, out_row, scale_row, out_col, scale_col, s);
+  else if (row) mx_tiles_launch<E5M2, true, false, FP4, true>(x, rows, cols, out_row, scale_row, out_col, scale_col, s);
+  else mx_tiles_launch<E5M2, false, true, FP4, true>(x, rows, cols, out_row, scale_row, out_col, scale_col, s);
+}
+
+// MX quantization with the scales in the panel layout: bf16 input of whole 128 x 128
+// tiles only (the caller checks), the persistent tile kernel.
+hipError_t launch_mx_quantize_panel(const void* x, int64_t rows, int64_t cols, int fp4, int e5m2,
+                                    uint8_t* out_row, uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col,
+                                    hipStream_t s) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  const auto* xx = static_cast<const uint16_t*>(x);
+  if (fp4) mx_panel_launch<false, true>(xx, rows, cols, out_row, scale_row, out_col, scale_col, s);
+  else if (e5m2) mx_panel_launch<true, false>(xx, rows, cols, out_row, scale_row, out_col, scale_col, s);
+  else mx_panel_launch<false, false>(xx, rows, cols, out_row, scale_row, out_col, scale_col, s);
   return hipGetLastError();
 }
 

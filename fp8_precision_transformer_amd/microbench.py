@@ -232,7 +232,7 @@ def cast(args):
         s2 = torch.empty((C, R // 32), dtype=torch.uint8, device=dev)
         fn = lambda: B.te_mxfp8_quantize(x, "E4M3", None, None, o2, s2)  # noqa: E731
         nbytes = R * C * 3 + R * C // 32
-    elif args.op.startswith("mx4"):  # MXFP4: row-wise, column-wise or both copies
+    elif args.op in ("mx4", "mx4col", "mx4both"):  # MXFP4: row-wise, column-wise or both copies
         row, col = args.op in ("mx4", "mx4both"), args.op in ("mx4col", "mx4both")
         o1 = torch.empty((R, C // 2), dtype=torch.uint8, device=dev) if row else None
         s1 = torch.empty((R, C // 32), dtype=torch.uint8, device=dev) if row else None
@@ -240,6 +240,20 @@ def cast(args):
         s2 = torch.empty((C, R // 32), dtype=torch.uint8, device=dev) if col else None
         fn = lambda: B.te_mxfp4_quantize(x, o1, s1, o2, s2)  # noqa: E731
         nbytes = R * C * 2 + (int(row) + int(col)) * (R * C // 2 + R * C // 32)
+    elif args.op.startswith("mxp") or args.op.startswith("mx4p"):  # panel-layout scales: row, col or both
+        fp4 = args.op.startswith("mx4p")
+        kind = args.op[4:] if fp4 else args.op[3:]
+        row, col = kind in ("", "both"), kind in ("col", "both")
+        eb = 2 if fp4 else 1
+        o1 = torch.empty((R, C // eb), dtype=torch.uint8, device=dev) if row else None
+        s1 = torch.empty(B.te_mx_scale_panel_bytes(R, C), dtype=torch.uint8, device=dev) if row else None
+        o2 = torch.empty((C, R // eb), dtype=torch.uint8, device=dev) if col else None
+        s2 = torch.empty(B.te_mx_scale_panel_bytes(C, R), dtype=torch.uint8, device=dev) if col else None
+        if fp4:
+            fn = lambda: B.te_mxfp4_quantize_panel(x, o1, s1, o2, s2)  # noqa: E731
+        else:
+            fn = lambda: B.te_mxfp8_quantize_panel(x, "E4M3", o1, s1, o2, s2)  # noqa: E731
+        nbytes = R * C * 2 + (int(row) + int(col)) * (R * C // eb + R * C // 32)
     else:  # mxboth
         o1 = torch.empty((R, C), dtype=torch.uint8, device=dev)
         s1 = torch.empty((R, C // 32), dtype=torch.uint8, device=dev)
@@ -289,7 +303,7 @@ def main():
     c.add_argument("--rows", type=int, default=15872)
     c.add_argument("--cols", type=int, default=16384)
     c.add_argument("--op", choices=["cast", "transpose", "both", "bothdbias", "ln", "mx", "mxcol", "mxboth", "mx4",
-                                    "mx4col", "mx4both"],
+                                    "mx4col", "mx4both", "mxp", "mxpcol", "mxpboth", "mx4p", "mx4pcol", "mx4pboth"],
                    default="cast")
     c.add_argument("--mode", choices=["delayed", "current"], default="delayed")
     c.add_argument("--iters", type=int, default=20)

@@ -324,6 +324,31 @@ te_status te_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t co
                             uint8_t* out_row, uint8_t* scale_row,
                             uint8_t* out_col, uint8_t* scale_col, void* stream);
 
+/*
+ * te_mxfp8_quantize_panel / te_mxfp4_quantize_panel -- te_mxfp8_quantize /
+ * te_mxfp4_quantize with the E8M0 scales written in the panel layout that
+ * te_fp8_gemm reads with TE_GRAN_MX_BLOCK32_PANEL (same codes, same scale values).
+ *
+ * Defines: the MX block rule of te_mxfp8_quantize (te_mxfp4_quantize for E2M1);
+ * the layout only reorders the scales (see te_fp8_gemm).
+ *
+ *   x          [rows, cols] TE_BF16 (other input types: TE_ERR_UNSUPPORTED).
+ *   out_row, out_col  as in te_mxfp8_quantize / te_mxfp4_quantize.
+ *   scale_row  te_mx_scale_panel_bytes(rows, cols) bytes: the scales of the row-wise
+ *              copy (rows of cols elements).
+ *   scale_col  te_mx_scale_panel_bytes(cols, rows) bytes: the scales of the
+ *              column-wise copy (x^T: cols rows of rows elements).
+ *   Padding rows of the last panel are not written.
+ * rows % 128 == 0 and cols % 128 == 0 (TE_ERR_UNSUPPORTED otherwise); all pointers
+ * 16-byte aligned.  Either pair may be NULL (not both).
+ */
+te_status te_mxfp8_quantize_panel(const void* x, int x_dtype, int64_t rows, int64_t cols, int elem_dtype,
+                                  uint8_t* out_row, uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col,
+                                  void* stream);
+te_status te_mxfp4_quantize_panel(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                                  uint8_t* out_row, uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col,
+                                  void* stream);
+
 /* Bytes of E8M0 scales in the panel layout (see te_fp8_gemm) for a matrix of `rows`
  * rows and `cols` elements per row: ceil(rows / 256) * 256 * cols / 32.  Host only;
  * -1 if rows < 0 or cols is not a non-negative multiple of 128. */

@@ -238,3 +238,24 @@ def test_mxfp4_gemm_panel_scales_bit_identical(mnk):
                       gran=B.TE_GRAN_MX_BLOCK32_PANEL)
         assert B.te_gemm_variant() == "gemm4_mxfp4_e2m1_e2m1_256x256_pingpong_panel"
         assert torch.equal(d1, d2), (mnk, odt)
+
+
+@pytest.mark.parametrize("shape", [(128, 256), (384, 512), (256, 4096)], ids=str)
+@pytest.mark.parametrize("which", ["row", "col", "both"])
+def test_mxfp4_panel_scales(shape, which):
+    R, C = shape
+    x32 = synth.activations(shape, 38, R + C, 0, 0)
+    xd, xh = input_pair(x32, "bf16")
+    orow = torch.empty((R, C // 2), dtype=torch.uint8, device=DEV) if which != "col" else None
+    srow = torch.empty(B.te_mx_scale_panel_bytes(R, C), dtype=torch.uint8, device=DEV) if which != "col" else None
+    ocol = torch.empty((C, R // 2), dtype=torch.uint8, device=DEV) if which != "row" else None
+    scol = torch.empty(B.te_mx_scale_panel_bytes(C, R), dtype=torch.uint8, device=DEV) if which != "row" else None
+    B.te_mxfp4_quantize_panel(xd, orow, srow, ocol, scol)
+    if orow is not None:
+        q, e = F.mxfp4_quantize(xh)
+        np.testing.assert_array_equal(host(orow), q)
+        np.testing.assert_array_equal(O.mx_scales_from_panel(host(srow), R, C // 32), e)
+    if ocol is not None:
+        q, e = F.mxfp4_quantize(np.ascontiguousarray(xh.T))
+        np.testing.assert_array_equal(host(ocol), q)
+        np.testing.assert_array_equal(O.mx_scales_from_panel(host(scol), C, R // 32), e)

@@ -436,3 +436,70 @@ def test_cast_transpose_dbias_rejects_small_workspace():
     with pytest.raises(B.TEError):
         B.te_cast_transpose_dbias(x, "E5M2", B.TE_SCALE_CURRENT, 0, empty_f32(), empty_f32(), empty_f32(),
                                   empty_f32(128), ws, None, col)
+
+
+# Panel-layout scales: the same codes, and scale bytes that read back (through the
+# oracle's inverse of the panel layout) as the oracle's [rows, cols/32] scales; 384 rows
+# or columns leave a partial second panel
+@pytest.mark.parametrize("shape", [(128, 128), (256, 384), (384, 1024), (4608, 4096)], ids=str)
+@pytest.mark.parametrize("fmt", ["E4M3", "E5M2"])
+@pytest.mark.parametrize("which", ["row", "col", "both"])
+def test_mxfp8_panel_scales(shape, fmt, which):
+    f = FMTS[fmt]
+    R, C = shape
+    x32 = synth.activations(shape, 9, R + C, 5, 0)
+    x32[:2, :32] = 0.0
+    xd, xh = input_pair(x32, "bf16")
+    orow = torch.empty((R, C), dtype=torch.uint8, device=DEV) if which != "col" else None
+    srow = torch.empty(B.te_mx_scale_panel_bytes(R, C), dtype=torch.uint8, device=DEV) if which != "col" else None
+    ocol = torch.empty((C, R), dtype=torch.uint8, device=DEV) if which != "row" else None
+    scol = torch.empty(B.te_mx_scale_panel_bytes(C, R), dtype=torch.uint8, device=DEV) if which != "row" else None
+    B.te_mxfp8_quantize_panel(xd, fmt, orow, srow, ocol, scol)
+    if orow is not None:
+        q, e = O.mxfp8_quantize(xh, f)
+        np.testing.assert_array_equal(host(orow), q)
+        np.testing.assert_array_equal(O.mx_scales_from_panel(host(srow), R, C // 32), e)
+    if ocol is not None:
+        q, e = O.mxfp8_quantize(np.ascontiguousarray(xh.T), f)
+        np.testing.assert_array_equal(host(ocol), q)
+        np.testing.assert_array_equal(O.mx_scales_from_panel(host(scol), C, R // 32), e)
+
+
+def test_mxfp8_panel_rejects_what_the_tile_kernel_does_not_take():
+    x = torch.zeros((256, 256), dtype=torch.float32, device=DEV)
+    o = torch.empty((256, 256), dtype=torch.uint8, device=DEV)
+    s = torch.empty(B.te_mx_scale_panel_bytes(256, 256), dtype=torch.uint8, device=DEV)
+    with pytest.raises(B.TEError) as e:
+        B.te_mxfp8_quantize_panel(x, "E4M3", o, s)  # fp32 input
+    assert e.value.status == B.TE_ERR_UNSUPPORTED
+    xb = torch.zeros((192, 256), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(B.TEError) as e:
+        B.te_mxfp8_quantize_panel(xb, "E4M3", o[:192], s)  # 192 rows: not whole 128-row tiles
+    assert e.value.status == B.TE_ERR_UNSUPPORTED
+
+
+def test_mxfp8_panel_quantize_then_gemm_matches_row_major():
+    """quantize (panel) -> GEMM (panel) equals quantize -> GEMM (row-major), bit for bit,
+    for Fprop and for Wgrad from the column-wise copies."""
+    M, N, K = 384, 256, 512
+    xd, _ = input_pair(synth.activations((M, K), 9, 1, 6, 0), "bf16")
+    wd, _ = input_pair(synth.normal((N, K), 0.02, 9, 1, 7, 0), "bf16")
+    gd, _ = input_pair(synth.grads((M, N), 9, 1, 8, 0), "bf16")
+    u8 = lambda *s: torch.empty(s, dtype=torch.uint8, device=DEV)  # noqa: E731
+    outs = []
+    for panel in (False, True):
+        q = B.te_mxfp8_quantize_panel if panel else B.te_mxfp8_quantize
+        sz = (lambda r, c: (B.te_mx_scale_panel_bytes(r, c),)) if panel else (lambda r, c: (r, c // 32))
+        gran = B.TE_GRAN_MX_BLOCK32_PANEL if panel else B.TE_GRAN_MX_BLOCK32
+        xq, xs, xqT, xsT = u8(M, K), u8(*sz(M, K)), u8(K, M), u8(*sz(K, M))
+        wq, ws = u8(N, K), u8(*sz(N, K))
+        gqT, gsT = u8(N, M), u8(*sz(N, M))
+        q(xd, "E4M3", xq, xs, xqT, xsT)
+        q(wd, "E4M3", wq, ws)
+        q(gd, "E4M3", None, None, gqT, gsT)
+        y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        dw = torch.empty((N, K), dtype=torch.float32, device=DEV)
+        B.te_fp8_gemm(xq, "E4M3", xs, wq, "E4M3", ws, y, gran=gran)
+        B.te_fp8_gemm(gqT, "E4M3", gsT, xqT, "E4M3", xsT, dw, gran=gran)
+        outs.append((y, dw))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
