@@ -57,6 +57,55 @@ def test_gemm_validation(kw, status):
 
 
 @needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(gran=B.TE_GRAN_MX_BLOCK32_PANEL, k=96), B.TE_ERR_SHAPE),           # panel scales: k % 128
+    (dict(gran=B.TE_GRAN_MX_BLOCK32_PANEL, a_dtype=B.TE_E2M1, b_dtype=B.TE_E2M1, k=128), B.TE_ERR_SHAPE),
+    (dict(gran=B.TE_GRAN_MX_BLOCK32_PANEL, a_scale=FAKE_MIS), B.TE_ERR_ALIGN),
+    (dict(gran=3), B.TE_ERR_ARG),
+])
+def test_gemm_panel_validation(kw, status):
+    kw.setdefault("k", 128)
+    assert _gemm(**kw) == status
+
+
+def _mx_panel(fp4=False, **kw):
+    args = dict(x=FAKE, x_dtype=B.TE_BF16, rows=256, cols=256, elem_dtype=B.TE_E4M3, out_row=FAKE,
+                scale_row=FAKE, out_col=None, scale_col=None, stream=None)
+    args.update(kw)
+    if fp4:
+        args.pop("elem_dtype")
+        return B.lib().te_mxfp4_quantize_panel(*args.values())
+    return B.lib().te_mxfp8_quantize_panel(*args.values())
+
+
+@needs_lib
+@pytest.mark.parametrize("fp4", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(x_dtype=B.TE_F32), B.TE_ERR_UNSUPPORTED),        # the panel path takes bf16 only
+    (dict(rows=192), B.TE_ERR_UNSUPPORTED),                # whole 128 x 128 tiles only
+    (dict(cols=160), B.TE_ERR_UNSUPPORTED),
+    (dict(rows=-1), B.TE_ERR_SHAPE),
+    (dict(out_row=None, scale_row=None), B.TE_ERR_NULL),    # both pairs NULL
+    (dict(scale_row=None), B.TE_ERR_NULL),                  # a pair half NULL
+    (dict(scale_row=FAKE_MIS), B.TE_ERR_ALIGN),
+])
+def test_mx_quantize_panel_validation(fp4, kw, status):
+    assert _mx_panel(fp4, **kw) == status
+    assert len(B.lib().te_get_last_error()) > 0
+
+
+@needs_lib
+def test_mx_scale_panel_bytes():
+    L = B.lib()
+    assert B.te_mx_scale_panel_bytes(256, 128) == 256 * 4
+    assert B.te_mx_scale_panel_bytes(257, 128) == 512 * 4      # whole 256-row panels
+    assert B.te_mx_scale_panel_bytes(15872, 4096) == 15872 * 128
+    assert B.te_mx_scale_panel_bytes(0, 128) == 0
+    assert B.te_mx_scale_panel_bytes(100, 96) == -1 and B.te_mx_scale_panel_bytes(-1, 128) == -1
+    assert L.te_mx_scale_panel_bytes(300, 512) == 512 * 512 // 32
+
+
+@needs_lib
 def test_gemm_empty_is_ok_without_launch():
     assert _gemm(m=0) == B.TE_OK
     assert _gemm(n=0, a=None, b=None, d=None) == B.TE_OK
