@@ -64,6 +64,8 @@ _SIGNATURES = {
     "te_mxfp8_quantize": [_vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp],
     "te_mxfp4_quantize": [_vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
     "te_mxfp8_quantize_panel": [_vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp],
+    "te_fp8_gemm_splitk": [_vp, _i32, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _i32, _i32, _vp, _i64,
+                           _vp],
     "te_mxfp4_quantize_panel": [_vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
 }
 
@@ -92,6 +94,8 @@ def lib() -> ctypes.CDLL:
             L.te_cast_transpose_dbias_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
             L.te_mx_scale_panel_bytes.restype = ctypes.c_int64
             L.te_mx_scale_panel_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
+            L.te_fp8_gemm_splitk_workspace_bytes.restype = ctypes.c_int64
+            L.te_fp8_gemm_splitk_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
             _lib = L
     return _lib
 
@@ -242,6 +246,29 @@ def te_fp8_gemm(a, a_dtype, a_scale, b, b_dtype, b_scale, d, bias=None, gran=TE_
         return
     _check(lib().te_fp8_gemm(_ptr(a), ad, _ptr(a_scale), _ptr(b), bd, _ptr(b_scale), int(gran), m, n, k,
                              _ptr(bias), bias_code, _ptr(d), dd, _stream(stream)))
+
+
+def te_fp8_gemm_splitk_workspace_bytes(m, n, splits) -> int:
+    return int(lib().te_fp8_gemm_splitk_workspace_bytes(int(m), int(n), int(splits)))
+
+
+def te_fp8_gemm_splitk(a, a_dtype, a_scale, b, b_dtype, b_scale, d, splits, workspace, bias=None, stream=None):
+    """te_fp8_gemm (per-tensor FP8 or BF16) with k split `splits` ways; workspace: a device
+    tensor of at least te_fp8_gemm_splitk_workspace_bytes(m, n, splits) bytes."""
+    for n_, t in (("a", a), ("b", b), ("d", d), ("bias", bias), ("a_scale", a_scale), ("b_scale", b_scale),
+                  ("workspace", workspace)):
+        _need(t, n_)
+    ad = TE_BF16 if str(a_dtype).upper() == "BF16" else _fp8_code(a_dtype)
+    bd = TE_BF16 if str(b_dtype).upper() == "BF16" else _fp8_code(b_dtype)
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k or tuple(d.shape) != (m, n):
+        raise ValueError(f"shape mismatch: a {tuple(a.shape)} b {tuple(b.shape)} d {tuple(d.shape)}")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    bias_code = _hp_code(bias) if bias is not None else TE_F32
+    _check(lib().te_fp8_gemm_splitk(_ptr(a), ad, _ptr(a_scale), _ptr(b), bd, _ptr(b_scale), m, n, k, _ptr(bias),
+                                    bias_code, _ptr(d), _hp_code(d), int(splits), _ptr(workspace), ws_bytes,
+                                    _stream(stream)))
 
 
 def te_mxfp8_quantize(x, elem_dtype, out_row=None, scale_row=None, out_col=None, scale_col=None, stream=None):

@@ -219,7 +219,8 @@ te_status te_scale_update(float* amax_history, float* scale, float* scale_inv, i
 
 static te_status gemm_impl(const void* a, int a_dtype, const void* a_scale, const void* b, int b_dtype,
                            const void* b_scale, int gran, int64_t m, int64_t n, int64_t k, const void* bias,
-                           int bias_dtype, void* d, int d_dtype, int accumulate, void* stream) {
+                           int bias_dtype, void* d, int d_dtype, int accumulate, void* stream, int splits = 1,
+                           void* workspace = nullptr, int64_t workspace_bytes = 0) {
   if (m < 0 || n < 0 || k < 0) return fail(TE_ERR_SHAPE, "negative GEMM shape");
   if (n % 16 != 0 || k % 16 != 0)
     return fail(TE_ERR_SHAPE, "n and k must be multiples of 16 (got n=%lld k=%lld)", (long long)n, (long long)k);
@@ -271,6 +272,22 @@ static te_status gemm_impl(const void* a, int a_dtype, const void* a_scale, cons
   g.bias_bf16 = bias_dtype == TE_BF16;
   g.d_bf16 = d_dtype == TE_BF16;
   g.accumulate = accumulate;
+  if (splits > 1) {
+    // split-K: per-tensor FP8 or BF16, at most one split per 128-byte k stage, and an
+    // fp32 workspace of splits * m * n floats
+    const int64_t stages = (kb + 127) / 128;
+    if (gran != TE_GRAN_TENSOR) return fail(TE_ERR_UNSUPPORTED, "split-K takes per-tensor FP8 or BF16 operands");
+    if (accumulate) return fail(TE_ERR_UNSUPPORTED, "split-K does not accumulate into D");
+    if (splits > stages || splits > 64)
+      return fail(TE_ERR_ARG, "splits must be <= the k stages (%lld) and <= 64 (got %d)", (long long)stages, splits);
+    if (m * n * splits >= (int64_t(1) << 31)) return fail(TE_ERR_SHAPE, "split-K workspace above 2^31 floats");
+    if (!workspace || !aligned16(workspace)) return fail(TE_ERR_ALIGN, "split-K needs a 16-byte aligned workspace");
+    if (workspace_bytes < splits * m * n * static_cast<int64_t>(sizeof(float)))
+      return fail(TE_ERR_ARG, "split-K workspace too small: %lld bytes for %lld", (long long)workspace_bytes,
+                  (long long)(splits * m * n * static_cast<int64_t>(sizeof(float))));
+    g.splits = splits;
+    g.workspace = workspace;
+  }
   hipError_t e = te::launch_gemm(g, static_cast<hipStream_t>(stream));
   if (log_level() > 0) {
     char detail[128];
@@ -285,6 +302,20 @@ te_status te_fp8_gemm(const void* a, int a_dtype, const void* a_scale, const voi
                       int bias_dtype, void* d, int d_dtype, void* stream) {
   return gemm_impl(a, a_dtype, a_scale, b, b_dtype, b_scale, gran, m, n, k, bias, bias_dtype, d, d_dtype, 0,
                    stream);
+}
+
+int64_t te_fp8_gemm_splitk_workspace_bytes(int64_t m, int64_t n, int splits) {
+  if (m < 0 || n < 0 || splits < 1) return -1;
+  return splits > 1 ? static_cast<int64_t>(splits) * m * n * static_cast<int64_t>(sizeof(float)) : 0;
+}
+
+te_status te_fp8_gemm_splitk(const void* a, int a_dtype, const void* a_scale, const void* b, int b_dtype,
+                             const void* b_scale, int64_t m, int64_t n, int64_t k, const void* bias, int bias_dtype,
+                             void* d, int d_dtype, int splits, void* workspace, int64_t workspace_bytes,
+                             void* stream) {
+  if (splits < 1) return fail(TE_ERR_ARG, "splits must be >= 1 (got %d)", splits);
+  return gemm_impl(a, a_dtype, a_scale, b, b_dtype, b_scale, TE_GRAN_TENSOR, m, n, k, bias, bias_dtype, d, d_dtype,
+                   0, stream, splits, workspace, workspace_bytes);
 }
 
 te_status te_fp8_gemm_accumulate(const void* a, int a_dtype, const void* a_scale, const void* b, int b_dtype,

@@ -25,6 +25,9 @@
 //   k_gemm   4 waves of 128 x 128, two-stage LDS pipeline with register
 //            staging: MX GEMMs whose k is not a multiple of 128.
 
+#include <map>
+#include <mutex>
+#include <string>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -67,6 +70,9 @@ struct Params {
   int nbm, nbn;      // tile grid
   int bias_bf16, d_bf16;
   int accumulate;    // fp32 D only: D = fl32(D_old + result)
+  int splits;        // k splits (split-K); 1 = the whole k per tile
+  int partial;       // 1: write raw fp32 sums of this split to d + split * M * N (no scale, bias)
+  float* partial_ws; // split-K: [splits, M, N] fp32 workspace
 };
 
 template <int V>
@@ -393,7 +399,9 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLds];
 
   const int nb = p.nbm * p.nbn;
-  const int bid = blockIdx.x;
+  // split-K: blocks [z * nb, (z + 1) * nb) take k split z of every tile
+  const int zsplit = static_cast<int>(blockIdx.x) / nb;
+  const int bid = static_cast<int>(blockIdx.x) - zsplit * nb;
   const int xcd = bid & 7, idx = bid >> 3;
   const int per = nb >> 3, rem = nb & 7;
   const int lin = xcd * per + (xcd < rem ? xcd : rem) + idx;
@@ -434,7 +442,11 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
                      static_cast<uint32_t>(rows_b) * p.kblocks);
   }
   const uint32_t sc_off = static_cast<uint32_t>(q4 * 64 + lane) * static_cast<uint32_t>(p.kblocks);
-  const int S = (p.KB + PK - 1) / PK;  // 128-byte k stages (a ragged end reads as zeros)
+  // 128-byte k stages (a ragged end reads as zeros); split z takes stages
+  // [z S_all / splits, (z + 1) S_all / splits) (MX: one split)
+  const int S_all = (p.KB + PK - 1) / PK;
+  const int s_begin = zsplit * S_all / p.splits;
+  const int S = (zsplit + 1) * S_all / p.splits - s_begin;
   // PANEL scales: in the panel layout the dword of row r and 128-element group g is
   // dword ((r / 256) * G + g) * 256 + r % 256, G = k / 128; the tile's rows are one
   // panel (m0 and n0 are multiples of 256), so a stage's dwords of 64 consecutive rows
@@ -492,7 +504,7 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
   };
   // one operand of one stage (8 loads per lane), into the slot at byte offset off_slot
   auto issue_op = [&](const v4i& rs, int off_slot, int st) {
-    const uint32_t kb = static_cast<uint32_t>(st) * PK;
+    const uint32_t kb = static_cast<uint32_t>(s_begin + st) * PK;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const uint32_t cb = static_cast<uint32_t>((c0 ^ (t & 3)) << 4);
@@ -880,8 +892,10 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           float val = acc[i][j][v];
-          if constexpr (KIND == KIND_FP8) val = __fmul_rn(__fmul_rn(val, sa), sb);
-          if (p.bias != nullptr) val = __fadd_rn(val, bias_v[j]);
+          if (!p.partial) {
+            if constexpr (KIND == KIND_FP8) val = __fmul_rn(__fmul_rn(val, sa), sb);
+            if (p.bias != nullptr) val = __fadd_rn(val, bias_v[j]);
+          }
           const int r = ii * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
           ep[r * (kEpPitch / 4) + j * 32 + lr] = val;
         }
@@ -916,7 +930,8 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
         v4f v4 = *reinterpret_cast<const v4f*>(ep + r * (kEpPitch / 4) + c);
         const int grow = row0 + r, gcol = col0 + c;
         if (grow < p.M && gcol < p.N) {
-          v4f* dst = reinterpret_cast<v4f*>(static_cast<float*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol);
+          float* dbase = static_cast<float*>(p.d) + (p.partial ? static_cast<int64_t>(zsplit) * p.M * p.N : 0);
+          v4f* dst = reinterpret_cast<v4f*>(dbase + static_cast<int64_t>(grow) * p.N + gcol);
           if (p.accumulate) {  // fp32 main-gradient accumulation: D = fl32(D_old + result)
             const v4f old = __builtin_nontemporal_load(dst);
 #pragma unroll
@@ -931,12 +946,86 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
   }
 }
 
+// Split-K reduction: D = epilogue(sum over splits of the fp32 partials, in split
+// order), the epilogue of k_gemm4: fl32(fl32(acc * sa) * sb) for FP8, then + bias,
+// then bf16 (round to nearest even) or fp32.  Four consecutive outputs per thread
+// (n % 16 == 0, so a group never crosses a row).
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ ws, int splits, int64_t mn, int n,
+                                                       const float* __restrict__ a_scale,
+                                                       const float* __restrict__ b_scale, int fp8,
+                                                       const void* __restrict__ bias, int bias_bf16,
+                                                       void* __restrict__ d, int d_bf16) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= mn) return;
+  auto part = [&](int z) { return __builtin_nontemporal_load(reinterpret_cast<const v4f*>(ws + static_cast<int64_t>(z) * mn + i)); };
+  auto add = [&](v4f& x, const v4f& v) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[q] = __fadd_rn(x[q], v[q]);
+  };
+  v4f acc = part(0);
+  int z = 1;
+  // four loads in flight per step, added in split order
+  for (; z + 3 < splits; z += 4) {
+    const v4f v0 = part(z), v1 = part(z + 1), v2 = part(z + 2), v3 = part(z + 3);
+    add(acc, v0);
+    add(acc, v1);
+    add(acc, v2);
+    add(acc, v3);
+  }
+  for (; z < splits; ++z) add(acc, part(z));
+  const float sa = fp8 ? *a_scale : 1.0f, sb = fp8 ? *b_scale : 1.0f;
+  const int col = static_cast<int>(i % n);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float val = acc[q];
+    if (fp8) val = __fmul_rn(__fmul_rn(val, sa), sb);
+    if (bias != nullptr)
+      val = __fadd_rn(val, bias_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(bias)[col + q]) << 16)
+                                     : static_cast<const float*>(bias)[col + q]);
+    acc[q] = val;
+  }
+  if (d_bf16) {
+    const uint2 o = {bf16x2_rne(acc[0], acc[1]), bf16x2_rne(acc[2], acc[3])};
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(d) + i) = o;
+  } else {
+    *reinterpret_cast<v4f*>(static_cast<float*>(d) + i) = acc;
+  }
+}
+
 thread_local const char* g_last_variant = "none";
+
+// "<name>_splitk" for a variant name (stable pointers: the names are few and fixed)
+const char* splitk_name(const char* name) {
+  static std::mutex mu;
+  static std::map<std::string, std::string> names;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = names.find(name);
+  if (it == names.end()) it = names.emplace(name, std::string(name) + "_splitk").first;
+  return it->second.c_str();
+}
 
 template <int KIND, int AF, int BF, bool PANEL = false>
 hipError_t run(Params p, hipStream_t s, const char* name) {
   g_last_variant = name;
   const int nb = p.nbm * p.nbn;
+  if (p.splits > 1) {
+    // split-K (per-tensor FP8 and BF16 only): partial sums of every split into the
+    // workspace, then the reduction with the epilogue
+    g_last_variant = splitk_name(name);
+    Params q = p;
+    q.d = q.partial_ws;
+    q.d_bf16 = 0;
+    q.accumulate = 0;
+    q.bias = nullptr;
+    q.partial = 1;
+    hipLaunchKernelGGL((k_gemm4<KIND, AF, BF>), dim3(nb * p.splits), dim3(NT8), 0, s, q);
+    const int64_t mn = static_cast<int64_t>(p.M) * p.N;
+    hipLaunchKernelGGL(k_splitk_reduce, dim3(static_cast<unsigned>((mn / 4 + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const float*>(p.partial_ws), p.splits, mn, p.N,
+                       static_cast<const float*>(p.a_scale), static_cast<const float*>(p.b_scale),
+                       KIND == KIND_FP8 ? 1 : 0, p.bias, p.bias_bf16, p.d, p.d_bf16);
+    return hipGetLastError();
+  }
   if (KIND == KIND_MX && !PANEL && (p.kblocks & 3) != 0) {
     // a k that is not a multiple of 128 leaves a partial scale dword per stage: the
     // two-stage kernel fills it per byte
@@ -972,6 +1061,9 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   p.bias_bf16 = g.bias_bf16;
   p.d_bf16 = g.d_bf16;
   p.accumulate = g.accumulate;
+  p.splits = g.splits > 1 ? g.splits : 1;
+  p.partial = 0;
+  p.partial_ws = static_cast<float*>(g.workspace);
   // f8f6f4 format codes: 0 = E4M3, 1 = E5M2
   const int af = (g.a_fmt == E5M2) ? 1 : 0, bf = (g.b_fmt == E5M2) ? 1 : 0;
   if (g.a_fmt == BF16) return run<KIND_BF16, 0, 0>(p, s, "gemm4_bf16_256x256_pingpong");

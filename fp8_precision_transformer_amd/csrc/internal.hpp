@@ -52,6 +52,8 @@ struct GemmArgs {
   int bias_bf16;         // bias dtype: 0 f32, 1 bf16
   int d_bf16;            // output dtype: 0 f32, 1 bf16
   int accumulate;        // 1: fp32 D = fl32(D_old + result)
+  int splits = 1;        // split-K: k splits (per-tensor FP8 / BF16 only)
+  void* workspace = nullptr;  // split-K: [splits, m, n] fp32
 };
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);

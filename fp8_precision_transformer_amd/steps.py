@@ -77,9 +77,20 @@ class LinearForwardStep:
                 "scale_inv": self.scale_inv}
 
 
+def splitk_splits(m: int, n: int, k_bytes: int, cus: int = 256, max_splits: int = 3) -> int:
+    """k splits for a GEMM whose 256 x 256 tiles leave most compute units idle: enough
+    workgroups to fill them, at least four 128-byte k stages per split, and at most
+    `max_splits` (every split adds m * n fp32 partials to write and read back)."""
+    tiles = -(-m // 256) * -(-n // 256)
+    stages = -(-k_bytes // 128)
+    return max(1, min(cus // tiles, stages // 4, max_splits))
+
+
 class LayerStep:
     """Fprop, Dgrad and Wgrad of a layer's four linear weights, current scaling, each
-    of X, W, dY cast once into row and transposed copies."""
+    of X, W, dY cast once into row and transposed copies.  GEMMs with few output tiles
+    (the Wgrad and Dgrad of a small layer) split k over more workgroups
+    (te_fp8_gemm_splitk)."""
 
     def __init__(self, cfg: ModelConfig, stream: torch.cuda.Stream, dev="cuda:0", cfg_id=2):
         self.stream = stream
@@ -101,6 +112,21 @@ class LayerStep:
                 sc={k: (f1(), f1(), f1()) for k in ("x", "w", "dy")},
                 y=bf(M, N), dx=bf(M, K), dw=bf(N, K))
             self.flops += 3 * 2 * M * N * K
+        # split-K plans (splits, workspace) of the Fprop, Dgrad and Wgrad GEMMs
+        self.splits = {}
+        for w in self.weights:
+            K, N = w.in_features, w.out_features
+            for stage, (m, n, k) in (("fprop", (M, N, K)), ("dgrad", (M, K, N)), ("wgrad", (N, K, M))):
+                sp = splitk_splits(m, n, k)
+                ws = u8(B.te_fp8_gemm_splitk_workspace_bytes(m, n, sp)) if sp > 1 else None
+                self.splits[(w.name, stage)] = (sp, ws)
+
+    def _gemm(self, key, a, fa, sa, b, fb, sb, d):
+        sp, ws = self.splits[key]
+        if sp > 1:
+            B.te_fp8_gemm_splitk(a, fa, sa, b, fb, sb, d, sp, ws, stream=self.stream)
+        else:
+            B.te_fp8_gemm(a, fa, sa, b, fb, sb, d, stream=self.stream)
 
     def run(self):
         s, cur = self.stream, B.TE_SCALE_CURRENT
@@ -109,10 +135,10 @@ class LayerStep:
             sx, sw, sg = t["sc"]["x"], t["sc"]["w"], t["sc"]["dy"]
             B.te_cast_transpose(t["X"], E4, cur, 0, *sx, t["x"], t["xT"], stream=s)
             B.te_cast_transpose(t["W"], E4, cur, 0, *sw, t["w"], t["wT"], stream=s)
-            B.te_fp8_gemm(t["x"], E4, sx[1], t["w"], E4, sw[1], t["y"], stream=s)
+            self._gemm((w.name, "fprop"), t["x"], E4, sx[1], t["w"], E4, sw[1], t["y"])
             B.te_cast_transpose(t["DY"], E5, cur, 0, *sg, t["dy"], t["dyT"], stream=s)
-            B.te_fp8_gemm(t["dy"], E5, sg[1], t["wT"], E4, sw[1], t["dx"], stream=s)
-            B.te_fp8_gemm(t["dyT"], E5, sg[1], t["xT"], E4, sx[1], t["dw"], stream=s)
+            self._gemm((w.name, "dgrad"), t["dy"], E5, sg[1], t["wT"], E4, sw[1], t["dx"])
+            self._gemm((w.name, "wgrad"), t["dyT"], E5, sg[1], t["xT"], E4, sx[1], t["dw"])
 
     def outputs(self):
         out = {}

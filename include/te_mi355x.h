@@ -325,6 +325,33 @@ te_status te_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t co
                             uint8_t* out_col, uint8_t* scale_col, void* stream);
 
 /*
+ * te_fp8_gemm_splitk -- te_fp8_gemm (per-tensor FP8 or BF16 operands) with k split into
+ * `splits` ranges of whole 128-byte stages, each range's fp32 sums written to a
+ * workspace, then added in split order and put through the same epilogue
+ * (fl32(fl32(acc * a_scale) * b_scale) + bias, bf16 or fp32).
+ *
+ * For GEMMs with few output tiles and a long k (the Wgrad and Dgrad GEMMs of small
+ * layers, [LP-opt] "autocast モードの使用と事前量子化の比較": Fprop, Dgrad and Wgrad
+ * have different aspect ratios): more workgroups than the 256 x 256 tiles give.
+ *
+ *   Arguments as te_fp8_gemm with gran = TE_GRAN_TENSOR, plus
+ *   splits     1 .. min(64, ceil(k bytes / 128)); 1 is te_fp8_gemm.
+ *   workspace  device, 16-byte aligned, >= te_fp8_gemm_splitk_workspace_bytes(m, n,
+ *              splits) bytes, owned by the caller; contents on entry are ignored.
+ * The sum is the same fp32 accumulation in a different order (deterministic: split
+ * order fixed).  Other granularities or accumulation: TE_ERR_UNSUPPORTED.
+ */
+te_status te_fp8_gemm_splitk(const void* a, int a_dtype, const void* a_scale,
+                             const void* b, int b_dtype, const void* b_scale,
+                             int64_t m, int64_t n, int64_t k, const void* bias, int bias_dtype,
+                             void* d, int d_dtype, int splits, void* workspace,
+                             int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes of te_fp8_gemm_splitk: splits * m * n * 4 (0 for splits == 1; -1 for
+ * negative sizes or splits < 1).  Host only. */
+int64_t te_fp8_gemm_splitk_workspace_bytes(int64_t m, int64_t n, int splits);
+
+/*
  * te_mxfp8_quantize_panel / te_mxfp4_quantize_panel -- te_mxfp8_quantize /
  * te_mxfp4_quantize with the E8M0 scales written in the panel layout that
  * te_fp8_gemm reads with TE_GRAN_MX_BLOCK32_PANEL (same codes, same scale values).

@@ -359,3 +359,82 @@ def test_mx_gemm_panel_rejects_k_not_multiple_of_128():
         B.te_fp8_gemm(a, "E4M3", s, a, "E4M3", s, d, gran=B.TE_GRAN_MX_BLOCK32_PANEL)
     assert B.te_mx_scale_panel_bytes(300, 512) == 512 * 512 // 32
     assert B.te_mx_scale_panel_bytes(300, 96) == -1
+
+
+# Split-K: k in `splits` ranges of whole stages, fp32 partial sums added in split order,
+# then the epilogue.  Shapes with few tiles and long k (the Wgrad of small layers), a
+# ragged k with one stage per split, ragged m and n; E5M2 x E4M3 as in Wgrad.
+SPLITK_CASES = [((768, 768, 4096), 8), ((300, 272, 1024), 3), ((64, 2304, 768), 6), ((130, 48, 400), 4),
+                ((2304, 768, 4096), 7), ((512, 512, 2048), 1)]
+
+
+@pytest.mark.parametrize("mnk,splits", SPLITK_CASES, ids=str)
+@pytest.mark.parametrize("odt", ["bf16", "f32"])
+def test_fp8_gemm_splitk(mnk, splits, odt):
+    m, n, k = mnk
+    sd = _seed(mnk, splits, odt, "splitk")
+    xa = synth.grads((m, k), 15, sd, 0, 0)
+    xb = synth.activations((n, k), 15, sd, 1, 0)
+    sa, sb = O.current_scale(O.amax(xa), O.E5M2), O.current_scale(O.amax(xb), O.E4M3)
+    qa, qb = O.scaled_cast(xa, sa, O.E5M2), O.scaled_cast(xb, sb, O.E4M3)
+    bias = synth.normal((n,), 0.02, 15, sd, 2, 0)
+    ws = torch.empty(max(B.te_fp8_gemm_splitk_workspace_bytes(m, n, splits), 16), dtype=torch.uint8, device=DEV)
+    d = _out(m, n, odt)
+    args = (dev_u8(qa), "E5M2", scalar(O.scale_inverse(sa)), dev_u8(qb), "E4M3", scalar(O.scale_inverse(sb)))
+    B.te_fp8_gemm_splitk(*args, d, splits, ws, bias=dev_f32(bias))
+    if splits > 1:
+        assert B.te_gemm_variant().endswith("_splitk")
+    ref = O.gemm_per_tensor(qa, O.E5M2, O.scale_inverse(sa), qb, O.E4M3, O.scale_inverse(sb), bias=bias, out=odt)
+    t4, t5 = O.decode_table(O.E4M3), O.decode_table(O.E5M2)
+    check_fp8_gemm(host(d), ref, t5[qa], t4[qb],
+                   np.float64(O.scale_inverse(sa)) * np.float64(O.scale_inverse(sb)), odt)
+    d2 = _out(m, n, odt)  # deterministic: the split order is fixed
+    B.te_fp8_gemm_splitk(*args, d2, splits, ws, bias=dev_f32(bias))
+    assert torch.equal(d, d2)
+    if splits == 1:  # one split is te_fp8_gemm, bit for bit
+        d3 = _out(m, n, odt)
+        B.te_fp8_gemm(*args, d3, bias=dev_f32(bias))
+        assert torch.equal(d, d3)
+
+
+def test_fp8_gemm_splitk_integer_operands_exact():
+    """integer-valued codes with |sum| < 2^24: every partial and every split sum is exact,
+    so the split-K result equals the exact product bit for bit"""
+    rng = np.random.default_rng(21)
+    m, n, k = 256, 128, 2048
+    ints = np.arange(-8, 9)
+    codes = O.encode(ints.astype(np.float32), O.E4M3)
+    a = codes[rng.integers(0, len(ints), (m, k))]
+    b = codes[rng.integers(0, len(ints), (n, k))]
+    d = _out(m, n, "f32")
+    ws = torch.empty(B.te_fp8_gemm_splitk_workspace_bytes(m, n, 5), dtype=torch.uint8, device=DEV)
+    B.te_fp8_gemm_splitk(dev_u8(a), "E4M3", scalar(1.0), dev_u8(b), "E4M3", scalar(1.0), d, 5, ws)
+    np.testing.assert_array_equal(host(d), O.gemm_per_tensor(a, O.E4M3, np.float32(1), b, O.E4M3, np.float32(1),
+                                                             out="f32"))
+
+
+def test_bf16_gemm_splitk():
+    m, n, k = 768, 768, 3072
+    a32 = synth.activations((m, k), 16, 0, 0, 0)
+    b32 = synth.normal((n, k), 0.02, 16, 0, 1, 0)
+    ab, bb = synth.to_bf16_bits(a32), synth.to_bf16_bits(b32)
+    ad = torch.from_numpy(ab.view(np.int16)).to(DEV).view(torch.bfloat16)
+    bd = torch.from_numpy(bb.view(np.int16)).to(DEV).view(torch.bfloat16)
+    d = _out(m, n, "f32")
+    ws = torch.empty(B.te_fp8_gemm_splitk_workspace_bytes(m, n, 6), dtype=torch.uint8, device=DEV)
+    B.te_fp8_gemm_splitk(ad, "BF16", None, bd, "BF16", None, d, 6, ws)
+    assert O.rel_err(host(d), O.gemm_bf16(ab, bb, out="f32")) <= 1e-3
+
+
+def test_fp8_gemm_splitk_rejects():
+    a = torch.zeros((64, 256), dtype=torch.uint8, device=DEV)
+    one = scalar(1.0)
+    d = _out(64, 64, "f32")
+    ws = torch.empty(B.te_fp8_gemm_splitk_workspace_bytes(64, 64, 2), dtype=torch.uint8, device=DEV)
+    for splits, w, status in ((3, ws, B.TE_ERR_ARG),          # 3 splits of 2 stages
+                              (2, ws[:1024], B.TE_ERR_ARG),   # workspace too small
+                              (2, ws[1:], B.TE_ERR_ALIGN),    # misaligned workspace
+                              (0, ws, B.TE_ERR_ARG)):
+        with pytest.raises(B.TEError) as e:
+            B.te_fp8_gemm_splitk(a, "E4M3", one, a, "E4M3", one, d, splits, w)
+        assert e.value.status == status, (splits, status)
