@@ -14,7 +14,7 @@ bit fields:
   E5M2: 1 sign, 5 exponent (bias 15), 2 mantissa bits, IEEE-like: S.11111.00 is
         infinity, S.11111.{01,10,11} are NaN.  Largest finite 1.75 * 2^15 = 57344.
 
-Readings taken where the pages are silent (all listed in the design doc):
+Readings taken where the pages are silent:
   * rounding is round-to-nearest, ties to even;
   * the cast saturates: finite values at or above the largest finite magnitude,
     and infinities, map to +-max;

@@ -11,7 +11,7 @@ three GEMMs of each linear layer are benchmarked separately).
 high-precision master weights; [FP8-intro] "Transformer Engine の使い方":
 ``te.Linear(768, 768, bias=True)`` -- a bias is added to the output.
 
-Readings (the design doc lists them):
+Readings taken where the pages are silent:
   * accumulation: every FP8 x FP8 product is exact; the oracle sums them in
     float64 and rounds once to fp32 ("fp32-accumulated" read as an fp32 result
     of the exact sum, so the reference does not depend on summation order);

@@ -8,7 +8,7 @@ recipe needs E4M3 scales per 16 elements, a random Hadamard transform and
 stochastic rounding, which a matrix core with E8M0 scales per 32 elements does
 not apply.  The FP4 variant built here is therefore MXFP4 (OCP Microscaling
 Formats v1.0), the block format of the MXFP8 recipe ([TE-summary] "主な機能")
-with 4-bit elements.  Readings (listed in the design doc):
+with 4-bit elements.  Readings:
 
   * E2M1: 1 sign, 2 exponent bits (bias 1), 1 mantissa bit; magnitudes
     0, 0.5 (subnormal), 1, 1.5, 2, 3, 4, 6; no infinity or NaN codes;

@@ -17,7 +17,7 @@ What the pages fix:
     on the amax history; current scaling is named beside it.
   * [TE-summary] "主な機能" / [TE-readme]: MXFP8 (block-scaled FP8).
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   * scale = fp8_max / amax in fp32 (correctly rounded division), times 2^-margin;
     overflow -> FLT_MAX; amax == 0 or non-finite -> 1.0 (current) or keep the
     previous scale (delayed);
