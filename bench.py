@@ -53,20 +53,20 @@ MEASURED_TRAFFIC = {
     # FP8 GEMM: mean over the layer's 12 GEMM launches (microbench layer --kind fp8)
     "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
                  "sha256": "ed2c3453583171418f6c3dfe847b806db69abd9ea83a758791e098cd75787c58",
-                 "bytes_per_launch": 1526102808},
+                 "bytes_per_launch": 1524420710},
     # delayed-scaling quantizers of one layer in autocast mode (24 casts and cast-transposes),
     # summed over the layer's launches (bench.py --modes fp8_delayed_autocast under --pmc)
     "quant_delayed_layer": {"source": "fp8_precision_transformer_amd/csrc/quant.hip",
-                            "sha256": "b19ed0d46a4a32b5b7155be60a0d7f802751bec53dc43152bc6d2b8290b5c792",
-                            "bytes_per_launch": 7452344229},
+                            "sha256": "b6b1fa4aa0d6ba2c16fd4352e0aedd6710c58fe3aa0cbb8241a60fc648379706",
+                            "bytes_per_launch": 7452358044},
     # MXFP8 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mxp)
     "gemm_mxfp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
                    "sha256": "ed2c3453583171418f6c3dfe847b806db69abd9ea83a758791e098cd75787c58",
-                   "bytes_per_launch": 1567626972},
+                   "bytes_per_launch": 1577146226},
     # MXFP4 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mx4p)
     "gemm_mxfp4": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
                    "sha256": "ed2c3453583171418f6c3dfe847b806db69abd9ea83a758791e098cd75787c58",
-                   "bytes_per_launch": 881406652},
+                   "bytes_per_launch": 881435377},
 }
 
 

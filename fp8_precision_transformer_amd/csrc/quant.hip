@@ -763,6 +763,7 @@ __device__ __forceinline__ int mx_exponent(float am) {
   if (!(am > 0.0f)) return 0;  // all-zero block -> 2^0 (code 127)
   const uint32_t u = __float_as_uint(am);
   const int E = static_cast<int>((u >> 23) & 0xffu);
+  if (E == 255) return 127;  // infinite amax: log2 = +inf, clamped (code 254)
   const int fl = E ? E - 127 : (31 - __clz(static_cast<int>(u & 0x7fffffu))) - 149;
   int e = fl - Fp8Traits<E5M2>::emax_elem;
   e = e < -127 ? -127 : e;
@@ -1005,6 +1006,49 @@ __device__ __forceinline__ void mx_quant8(const uint4& raw, int e, uint32_t& q0,
   q1 = cvt4<E5M2>(w[4], w[5], w[6], w[7]);
 }
 
+
+// The row-wise MXFP8 quantization of one lane's eight bf16 values with the gfx950
+// scaled convert, which divides by the scale 2^e and rounds to nearest even in one
+// step but does not saturate: values beyond the format's maximum come out as NaN or
+// infinity.  The magnitudes are therefore clamped first, in the bf16 bit domain, to
+// max * 2^e (exact in bf16: both maxima carry two mantissa bits), which yields what
+// saturating after the exact division yields.  The caller takes this path only for
+// blocks of finite values with e > -127 (scale 2^e a normal float, max * 2^e finite);
+// it gives the same codes as mx_quant8 on every such input.
+typedef short mx_s2 __attribute__((ext_vector_type(2)));
+typedef __bf16 mx_b2 __attribute__((ext_vector_type(2)));
+typedef unsigned short mx_u2 __attribute__((ext_vector_type(2)));
+template <bool E5M2>
+__device__ __forceinline__ void mx_quant8_scaled(const uint4& raw, int e, uint32_t& q0, uint32_t& q1) {
+  constexpr int kMaxBits = E5M2 ? 0x4760 : 0x43e0;  // bf16 bits of 57344 / 448
+  const uint32_t lim = static_cast<uint32_t>(kMaxBits + e * 128);
+  const mx_u2 lim2 = {static_cast<unsigned short>(lim), static_cast<unsigned short>(lim)};
+  const float sc = __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  uint32_t c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const mx_u2 mag = __builtin_bit_cast(mx_u2, w[i] & 0x7fff7fffu);
+    const uint32_t cl = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(mag, lim2)) | (w[i] & 0x80008000u);
+    c[i] = cl;
+  }
+  const mx_s2 z = {0, 0};
+  mx_s2 r0, r1;
+  if constexpr (E5M2) {
+    r0 = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(z, __builtin_bit_cast(mx_b2, c[0]), sc, false);
+    r0 = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(r0, __builtin_bit_cast(mx_b2, c[1]), sc, true);
+    r1 = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(z, __builtin_bit_cast(mx_b2, c[2]), sc, false);
+    r1 = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(r1, __builtin_bit_cast(mx_b2, c[3]), sc, true);
+  } else {
+    r0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(z, __builtin_bit_cast(mx_b2, c[0]), sc, false);
+    r0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r0, __builtin_bit_cast(mx_b2, c[1]), sc, true);
+    r1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(z, __builtin_bit_cast(mx_b2, c[2]), sc, false);
+    r1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r1, __builtin_bit_cast(mx_b2, c[3]), sc, true);
+  }
+  q0 = __builtin_bit_cast(uint32_t, r0);
+  q1 = __builtin_bit_cast(uint32_t, r1);
+}
+
 // FP4: the same tiles written as MXFP4 (four bytes of codes per lane and pass for the
 // row-wise copy, 64 bytes per column of the tile for the column-wise one).
 // PANEL: the E8M0 scales go out in the GEMM's panel layout: the dword of row r and
@@ -1052,8 +1096,8 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_tiles(const uint16_t* __rest
       if constexpr (ROW) {
         uint32_t m = absmax_bits<uint16_t>(0u, raw[p]);
         m = max(m & 0xffffu, m >> 16);
-        m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 1, 64)));
-        m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 2, 64)));
+        m = max(m, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(m), 0xb1, 0xf, 0xf, false)));
+        m = max(m, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(m), 0x4e, 0xf, 0xf, false)));
         const int64_t r = r0 + lr;
         uint32_t code;
         if constexpr (FP4) {
@@ -1069,13 +1113,14 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_tiles(const uint16_t* __rest
         } else {
           const int e = mx_exponent<E5M2>(__uint_as_float(m << 16));
           uint32_t q0, q1;
-          mx_quant8<E5M2>(raw[p], e, q0, q1);
+          if (m < 0x7f80u && e > -127) mx_quant8_scaled<E5M2>(raw[p], e, q0, q1);
+          else mx_quant8<E5M2>(raw[p], e, q0, q1);
           *reinterpret_cast<uint2*>(out_row + r * C + c0 + pcol) = make_uint2(q0, q1);
           code = static_cast<uint32_t>(e + 127);
         }
-        const uint32_t k1 = static_cast<uint32_t>(__shfl(static_cast<int>(code), lane + 4, 64));
-        const uint32_t k2 = static_cast<uint32_t>(__shfl(static_cast<int>(code), lane + 8, 64));
-        const uint32_t k3 = static_cast<uint32_t>(__shfl(static_cast<int>(code), lane + 12, 64));
+        const uint32_t k1 = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(code), 0x104, 0xf, 0xf, true));
+        const uint32_t k2 = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(code), 0x108, 0xf, 0xf, true));
+        const uint32_t k3 = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(code), 0x10c, 0xf, 0xf, true));
         if ((lane & 15) == 0)
           *scale_dw(scale_row, r, C, c0) = code | (k1 << 8) | (k2 << 16) | (k3 << 24);
       }

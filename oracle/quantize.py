@@ -29,8 +29,8 @@ Readings where the pages are silent:
   * MXFP8 (OCP MX v1.0 reading): blocks of 32 consecutive elements along the
     GEMM's reduction axis; E8M0 shared exponent e = floor(log2 amax_block) - 8
     (8 = exponent of E4M3's largest power of two), clamped to [-127, 127],
-    code e + 127; an all-zero block gets code 127; elements are
-    encode_E4M3(x * 2^-e) (saturating).
+    code e + 127; an all-zero block gets code 127, an infinite amax
+    (log2 = +inf) code 254; elements are encode_E4M3(x * 2^-e) (saturating).
 
 Parity: amax, scale, cast, delayed update and MXFP8 are pinned by closed forms,
 brute force and invariants in tests/test_oracle_quantize.py.  The MXFP8
@@ -189,7 +189,10 @@ def mxfp8_quantize(x, fmt: FP8Format = E4M3, block: int = 32):
     am = np.max(np.abs(xb), axis=2)
     # exponent of the element format's largest power of two (256 for E4M3, 2^15 for E5M2)
     emax_elem = int(np.floor(np.log2(fmt.max)))
-    e = np.where(am > 0, _floor_log2(np.where(am > 0, am, 1.0)) - emax_elem, 0)
+    fin = np.isfinite(am)
+    pos = (am > 0) & fin
+    e = np.where(pos, _floor_log2(np.where(pos, am, 1.0)) - emax_elem, 0)
+    e = np.where(np.isinf(am), 127, e)  # log2 of an infinite amax is +inf: the clamp's top
     e = np.clip(e, -127, 127)
     codes_e8m0 = (e + 127).astype(np.uint8)
     scaled = np.ldexp(xb, (-e)[:, :, None].astype(np.int32)).astype(np.float32)

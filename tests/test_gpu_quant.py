@@ -503,3 +503,48 @@ def test_mxfp8_panel_quantize_then_gemm_matches_row_major():
         B.te_fp8_gemm(gqT, "E4M3", gsT, xqT, "E4M3", xsT, dw, gran=gran)
         outs.append((y, dw))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def _every_bf16_then_extreme_blocks(R, C, seed):
+    """fp32 values exact in bf16: the 65536 bf16 bit patterns in order (NaN, infinities,
+    subnormals, signed zeros), then 32-element blocks of N(0, 1) * 2^k with k uniform in
+    [-140, 127], so block maxima reach both ends of the exponent clamp, fall in the band
+    that saturates after scaling, and overflow bf16 to infinity."""
+    rng = np.random.default_rng(seed)
+    k = rng.integers(-140, 128, (R * C) // 32)
+    x = (rng.standard_normal(((R * C) // 32, 32)) * np.exp2(k.astype(np.float64))[:, None]).reshape(R, C)
+    with np.errstate(over="ignore"):
+        x = x.astype(np.float32)
+    x[-1, 0], x[-1, 64] = np.inf, -np.inf  # infinities in blocks of finite values
+    bits = synth.to_bf16_bits(x).reshape(-1)
+    bits[:65536] = np.arange(65536, dtype=bits.dtype)
+    return synth.bf16_bits_as_f32(bits).reshape(R, C)
+
+
+@pytest.mark.parametrize("fmt", ["E4M3", "E5M2"])
+@pytest.mark.parametrize("shape,panel", [((512, 512), False), ((512, 512), True), ((416, 160), False)], ids=str)
+def test_mxfp8_every_bf16_pattern_and_extreme_blocks(fmt, shape, panel):
+    """Row and column copies of every bf16 bit pattern and of blocks at the ends of the
+    exponent range against the oracle (any NaN code where the oracle has a NaN): the tile
+    kernel with row-major and panel-layout scales, and the general kernel (160 columns)."""
+    f = FMTS[fmt]
+    R, C = shape
+    x32 = _every_bf16_then_extreme_blocks(R, C, R + C + panel)
+    assert np.isnan(x32).any() and np.isinf(x32).any()
+    xd, xh = input_pair(x32, "bf16")
+    keep = ~np.isnan(x32)  # the device copy carries one NaN payload; every other pattern as is
+    np.testing.assert_array_equal(xh.view(np.uint32)[keep], x32.view(np.uint32)[keep])
+    sbytes = (lambda r, c: B.te_mx_scale_panel_bytes(r, c)) if panel else (lambda r, c: r * (c // 32))
+    orow = torch.empty((R, C), dtype=torch.uint8, device=DEV)
+    srow = torch.empty(sbytes(R, C), dtype=torch.uint8, device=DEV)
+    ocol = torch.empty((C, R), dtype=torch.uint8, device=DEV)
+    scol = torch.empty(sbytes(C, R), dtype=torch.uint8, device=DEV)
+    (B.te_mxfp8_quantize_panel if panel else B.te_mxfp8_quantize)(xd, fmt, orow, srow, ocol, scol)
+    tbl = O.decode_table(f)
+    for xs, o, s, r, c in ((xh, orow, srow, R, C), (np.ascontiguousarray(xh.T), ocol, scol, C, R)):
+        q, e = O.mxfp8_quantize(xs, f)
+        assert (e == 254).any() and (xs is not xh or (e == 0).any())
+        got_e = O.mx_scales_from_panel(host(s), r, c // 32) if panel else host(s).reshape(r, c // 32)
+        np.testing.assert_array_equal(got_e, e)
+        bad, where = nan_aware_equal(host(o), q, tbl)
+        assert bad == 0, where

@@ -213,6 +213,24 @@ def test_mxfp8_zero_block_and_clamp():
     assert ey[0, 0] == 0 and (qy == 0).all()
 
 
+def test_mxfp8_infinite_and_nan_blocks():
+    """An infinite block max has log2 = +inf, so the exponent takes the clamp's top, 127
+    (code 254): the infinities saturate to the format's largest magnitude and finite
+    elements, divided by 2^127, round to zero. A NaN makes the block max NaN, which is
+    not > 0, so that block keeps e = 0 (code 127) and its NaN stays a NaN."""
+    x = np.zeros((1, 96), dtype=np.float32)
+    x[0, 0], x[0, 1], x[0, 2] = np.inf, 3.0, -np.float32(2.0 ** 100)
+    x[0, 32], x[0, 33], x[0, 34] = -np.inf, np.nan, 1.5
+    x[0, 64], x[0, 65] = np.inf, -np.inf
+    for fmt, top in ((E4M3, 0x7E), (E5M2, 0x7B)):
+        q, e = mxfp8_quantize(x, fmt)
+        assert list(e[0]) == [254, 127, 254]
+        assert q[0, 0] == top and q[0, 1] == 0 and q[0, 2] == 0x80  # -2^100 / 2^127 -> -0
+        assert q[0, 32] == top | 0x80 and np.isnan(O.decode_table(fmt)[q[0, 33]])
+        assert q[0, 34] == encode(np.float32(1.5), fmt)           # scale 2^0
+        assert q[0, 64] == top and q[0, 65] == top | 0x80
+
+
 def test_mx_scales_panel_layout_positions():
     """The panel layout of the MX scales, pinned at positions worked out by hand from
     its definition: 256-row panels; in a panel, the dwords (four block bytes) of one
