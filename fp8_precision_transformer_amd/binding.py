@@ -32,7 +32,7 @@ STATUS_NAMES = ["TE_OK", "TE_ERR_NULL", "TE_ERR_SHAPE", "TE_ERR_DTYPE", "TE_ERR_
 # te_dtype
 TE_F32, TE_BF16, TE_E4M3, TE_E5M2, TE_E8M0, TE_E2M1 = range(6)
 # te_scaling, te_amax_algo, te_granularity
-TE_SCALE_DELAYED, TE_SCALE_CURRENT = 0, 1
+TE_SCALE_DELAYED, TE_SCALE_CURRENT, TE_SCALE_CURRENT_FROM_AMAX = 0, 1, 2
 TE_AMAX_MAX, TE_AMAX_MOST_RECENT = 0, 1
 TE_GRAN_TENSOR, TE_GRAN_MX_BLOCK32, TE_GRAN_MX_BLOCK32_PANEL = 0, 1, 2
 
@@ -52,10 +52,10 @@ _lock = threading.Lock()
 _vp, _i64, _i32, _fp = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
 
 _SIGNATURES = {
-    "te_amax_cast": [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp],
-    "te_cast_transpose": [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp],
+    "te_amax_cast": [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp],
+    "te_cast_transpose": [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "te_layernorm_fp8": [_vp, _i32, _i64, _i64, _vp, _vp, _i32, ctypes.c_float, _i32, _i32, _i32, _vp, _vp, _vp,
-                         _vp, _vp, _vp, _vp],
+                         _vp, _vp, _vp, _vp, _vp],
     "te_cast_transpose_dbias": [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                                 _vp],
     "te_scale_update": [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp],
@@ -96,6 +96,8 @@ def lib() -> ctypes.CDLL:
             L.te_mx_scale_panel_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
             L.te_fp8_gemm_splitk_workspace_bytes.restype = ctypes.c_int64
             L.te_fp8_gemm_splitk_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
+            L.te_amax_workspace_bytes.restype = ctypes.c_int64
+            L.te_amax_workspace_bytes.argtypes = []
             _lib = L
     return _lib
 
@@ -155,23 +157,38 @@ def _2d(x: torch.Tensor):
     return x.numel() // x.shape[-1], x.shape[-1]
 
 
-def te_amax_cast(x, out_dtype, mode, margin, scale, scale_inv, amax, out=None, stream=None):
-    for n, t in (("x", x), ("scale", scale), ("scale_inv", scale_inv), ("amax", amax), ("out", out)):
+def te_amax_workspace_bytes() -> int:
+    return int(lib().te_amax_workspace_bytes())
+
+
+def amax_workspace(device=None) -> torch.Tensor:
+    """A new zeroed amax workspace (te_amax_workspace_bytes() bytes) on `device`, for the
+    caller to keep and pass to the amax-producing calls.  Calls that may run at the
+    same time need different workspaces."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    return torch.zeros(te_amax_workspace_bytes(), dtype=torch.uint8, device=dev)
+
+
+def te_amax_cast(x, out_dtype, mode, margin, scale, scale_inv, amax, out=None, workspace=None, stream=None):
+    """workspace: an amax workspace (amax_workspace()); None only for TE_SCALE_CURRENT_FROM_AMAX."""
+    for n, t in (("x", x), ("scale", scale), ("scale_inv", scale_inv), ("amax", amax), ("out", out),
+                 ("workspace", workspace)):
         _need(t, n)
     rows, cols = _2d(x)
     _check(lib().te_amax_cast(_ptr(x), _hp_code(x), rows, cols, _fp8_code(out_dtype), int(mode), int(margin),
-                              _ptr(scale), _ptr(scale_inv), _ptr(amax), _ptr(out), _stream(stream)))
+                              _ptr(scale), _ptr(scale_inv), _ptr(amax), _ptr(out), _ptr(workspace),
+                              _stream(stream)))
 
 
 def te_cast_transpose(x, out_dtype, mode, margin, scale, scale_inv, amax, out_row=None, out_col=None,
-                      stream=None):
+                      workspace=None, stream=None):
     for n, t in (("x", x), ("scale", scale), ("scale_inv", scale_inv), ("amax", amax),
-                 ("out_row", out_row), ("out_col", out_col)):
+                 ("out_row", out_row), ("out_col", out_col), ("workspace", workspace)):
         _need(t, n)
     rows, cols = _2d(x)
     _check(lib().te_cast_transpose(_ptr(x), _hp_code(x), rows, cols, _fp8_code(out_dtype), int(mode),
                                    int(margin), _ptr(scale), _ptr(scale_inv), _ptr(amax), _ptr(out_row),
-                                   _ptr(out_col), _stream(stream)))
+                                   _ptr(out_col), _ptr(workspace), _stream(stream)))
 
 
 def te_mx_scale_panel_bytes(rows, cols) -> int:
@@ -183,10 +200,17 @@ def te_cast_transpose_dbias_workspace_bytes(rows, cols) -> int:
     return int(lib().te_cast_transpose_dbias_workspace_bytes(int(rows), int(cols)))
 
 
+def dbias_workspace(rows, cols, device=None) -> torch.Tensor:
+    """A new workspace for te_cast_transpose_dbias of [rows, cols] (its amax part zeroed)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    return torch.zeros(te_cast_transpose_dbias_workspace_bytes(rows, cols), dtype=torch.uint8, device=dev)
+
+
 def te_cast_transpose_dbias(x, out_dtype, mode, margin, scale, scale_inv, amax, dbias, workspace,
                             out_row=None, out_col=None, stream=None):
     """te_cast_transpose plus dbias[c] = sum_r x[r, c] (fp32) from the same pass; workspace:
-    a device tensor of at least te_cast_transpose_dbias_workspace_bytes(rows, cols) bytes."""
+    a device tensor of at least te_cast_transpose_dbias_workspace_bytes(rows, cols) bytes whose
+    first te_amax_workspace_bytes() bytes are an amax workspace (dbias_workspace())."""
     for n, t in (("x", x), ("scale", scale), ("scale_inv", scale_inv), ("amax", amax),
                  ("out_row", out_row), ("out_col", out_col), ("dbias", dbias), ("workspace", workspace)):
         _need(t, n)
@@ -198,17 +222,19 @@ def te_cast_transpose_dbias(x, out_dtype, mode, margin, scale, scale_inv, amax, 
 
 
 def te_layernorm_fp8(x, gamma, beta, eps, out_dtype, mode, margin, scale, scale_inv, amax, out, mu=None,
-                     rsigma=None, stream=None):
-    """LayerNorm of x over its last axis, written as FP8 codes into out (see the header)."""
+                     rsigma=None, workspace=None, stream=None):
+    """LayerNorm of x over its last axis, written as FP8 codes into out (see the header);
+    workspace: an amax workspace (amax_workspace())."""
     for n, t in (("x", x), ("gamma", gamma), ("beta", beta), ("scale", scale), ("scale_inv", scale_inv),
-                 ("amax", amax), ("out", out), ("mu", mu), ("rsigma", rsigma)):
+                 ("amax", amax), ("out", out), ("mu", mu), ("rsigma", rsigma), ("workspace", workspace)):
         _need(t, n)
     if gamma.dtype != beta.dtype:
         raise ValueError("gamma and beta must share a dtype")
     rows, cols = _2d(x)
     _check(lib().te_layernorm_fp8(_ptr(x), _hp_code(x), rows, cols, _ptr(gamma), _ptr(beta), _hp_code(gamma),
                                   float(eps), _fp8_code(out_dtype), int(mode), int(margin), _ptr(scale),
-                                  _ptr(scale_inv), _ptr(amax), _ptr(out), _ptr(mu), _ptr(rsigma), _stream(stream)))
+                                  _ptr(scale_inv), _ptr(amax), _ptr(out), _ptr(mu), _ptr(rsigma), _ptr(workspace),
+                                  _stream(stream)))
 
 
 def te_scale_update(amax_history, scale, scale_inv, fp8_dtype, algo=TE_AMAX_MAX, margin=0, stream=None):

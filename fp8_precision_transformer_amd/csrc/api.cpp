@@ -54,26 +54,17 @@ void log_dispatch(const char* op, const char* variant, const char* detail) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// gfx950 check, once per device (the device list is small and fixed per process).
+// gfx950 check on every call (the runtime's device attributes; nothing is cached here):
+// gfx950 reports compute capability 9.5.
 te_status check_device() {
-  int dev = 0;
+  int dev = 0, major = 0, minor = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(TE_ERR_HIP, "hipGetDevice failed");
-  static std::mutex mu;
-  static int state[64] = {0};  // 0 unknown, 1 ok, 2 bad
-  if (dev < 0 || dev >= 64) return fail(TE_ERR_UNSUPPORTED, "device index %d out of range", dev);
-  {
-    std::lock_guard<std::mutex> lock(mu);
-    if (state[dev] == 0) {
-      hipDeviceProp_t prop;
-      if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
-        return fail(TE_ERR_HIP, "hipGetDeviceProperties failed");
-      state[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
-      if (state[dev] == 2)
-        return fail(TE_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only", dev,
-                    prop.gcnArchName);
-    }
-  }
-  if (state[dev] == 2) return fail(TE_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  if (hipDeviceGetAttribute(&major, hipDeviceAttributeComputeCapabilityMajor, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&minor, hipDeviceAttributeComputeCapabilityMinor, dev) != hipSuccess)
+    return fail(TE_ERR_HIP, "hipDeviceGetAttribute failed");
+  if (major != 9 || minor != 5)
+    return fail(TE_ERR_UNSUPPORTED, "device %d has compute capability %d.%d; this library is built for gfx950 (9.5) only",
+                dev, major, minor);
   return TE_OK;
 }
 
@@ -92,7 +83,8 @@ te_status check_cast_common(const void* x, int x_dtype, int64_t rows, int64_t co
   if (rows < 0 || cols < 0) return fail(TE_ERR_SHAPE, "negative shape (%lld, %lld)", (long long)rows, (long long)cols);
   if (!is_hp(x_dtype)) return fail(TE_ERR_DTYPE, "x_dtype must be TE_F32 or TE_BF16 (got %d)", x_dtype);
   if (!is_fp8(out_dtype)) return fail(TE_ERR_DTYPE, "out_dtype must be TE_E4M3 or TE_E5M2 (got %d)", out_dtype);
-  if (mode != TE_SCALE_DELAYED && mode != TE_SCALE_CURRENT) return fail(TE_ERR_ARG, "bad scaling mode %d", mode);
+  if (mode != TE_SCALE_DELAYED && mode != TE_SCALE_CURRENT && mode != TE_SCALE_CURRENT_FROM_AMAX)
+    return fail(TE_ERR_ARG, "bad scaling mode %d", mode);
   if (margin < 0 || margin > 126) return fail(TE_ERR_ARG, "margin must be in [0, 126] (got %d)", margin);
   if (!scale || !scale_inv || !amax) return fail(TE_ERR_NULL, "scale, scale_inv and amax are required");
   if (rows * cols > 0 && !x) return fail(TE_ERR_NULL, "x is NULL");
@@ -100,6 +92,17 @@ te_status check_cast_common(const void* x, int x_dtype, int64_t rows, int64_t co
   if (cols != 0 && rows > (int64_t(1) << 62) / cols) return fail(TE_ERR_SHAPE, "shape too large");
   return TE_OK;
 }
+
+// The grid-amax workspace of a call whose mode reduces an amax (every mode but
+// TE_SCALE_CURRENT_FROM_AMAX): required, 16-byte aligned.
+te_status check_amax_workspace(const void* ws, bool needed) {
+  if (!needed) return TE_OK;
+  if (!ws) return fail(TE_ERR_NULL, "amax_workspace is NULL (te_amax_workspace_bytes() bytes, zeroed before first use)");
+  if (!aligned16(ws)) return fail(TE_ERR_ALIGN, "amax_workspace is not 16-byte aligned");
+  return TE_OK;
+}
+
+constexpr int64_t kAmaxWsBytes = 8448;  // sizeof(te::AmaxWork)
 
 }  // namespace
 
@@ -111,42 +114,46 @@ const char* te_version(void) { return "te_mi355x 0.1 (gfx950)"; }
 
 const char* te_gemm_variant(void) { return te::last_gemm_variant(); }
 
+int64_t te_amax_workspace_bytes(void) { return kAmaxWsBytes; }
+
 te_status te_amax_cast(const void* x, int x_dtype, int64_t rows, int64_t cols, int out_dtype, int mode,
                        int margin, float* scale, float* scale_inv, float* amax, uint8_t* out,
-                       void* stream) {
+                       void* amax_workspace, void* stream) {
   te_status st = check_cast_common(x, x_dtype, rows, cols, out_dtype, mode, margin, scale, scale_inv, amax);
   if (st != TE_OK) return st;
   if (out && !aligned16(out)) return fail(TE_ERR_ALIGN, "out is not 16-byte aligned");
+  if ((st = check_amax_workspace(amax_workspace, mode != TE_SCALE_CURRENT_FROM_AMAX)) != TE_OK) return st;
   if ((st = check_device()) != TE_OK) return st;
-  log_dispatch("te_amax_cast", mode == TE_SCALE_CURRENT ? "amax_pass+cast_pass" : "fused_amax_cast",
+  log_dispatch("te_amax_cast",
+               mode == TE_SCALE_CURRENT ? "amax_pass+cast_pass"
+                                        : (mode == TE_SCALE_DELAYED ? "fused_amax_cast" : "cast_pass_from_amax"),
                out_dtype == TE_E5M2 ? "E5M2" : "E4M3");
-  return hip_status(te::launch_amax_cast(x, x_dtype, rows * cols, out_dtype == TE_E5M2, mode == TE_SCALE_CURRENT,
-                                         margin, scale, scale_inv, amax, out,
-                                         static_cast<hipStream_t>(stream)),
+  return hip_status(te::launch_amax_cast(x, x_dtype, rows * cols, out_dtype == TE_E5M2, mode, margin, scale,
+                                         scale_inv, amax, out, amax_workspace, static_cast<hipStream_t>(stream)),
                     "te_amax_cast launch");
 }
 
 te_status te_cast_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols, int out_dtype, int mode,
                             int margin, float* scale, float* scale_inv, float* amax, uint8_t* out_row,
-                            uint8_t* out_col, void* stream) {
+                            uint8_t* out_col, void* amax_workspace, void* stream) {
   te_status st = check_cast_common(x, x_dtype, rows, cols, out_dtype, mode, margin, scale, scale_inv, amax);
   if (st != TE_OK) return st;
   if (rows * cols > 0 && !out_row && !out_col) return fail(TE_ERR_NULL, "out_row and out_col are both NULL");
   if ((out_row && !aligned16(out_row)) || (out_col && !aligned16(out_col)))
     return fail(TE_ERR_ALIGN, "outputs must be 16-byte aligned");
   if ((rows + 127) / 128 > 65535) return fail(TE_ERR_SHAPE, "rows too large for the tile grid");
+  if ((st = check_amax_workspace(amax_workspace, mode != TE_SCALE_CURRENT_FROM_AMAX)) != TE_OK) return st;
   if ((st = check_device()) != TE_OK) return st;
-  log_dispatch("te_cast_transpose", "tile128x64", out_dtype == TE_E5M2 ? "E5M2" : "E4M3");
-  return hip_status(te::launch_cast_transpose(x, x_dtype, rows, cols, out_dtype == TE_E5M2,
-                                              mode == TE_SCALE_CURRENT, margin, scale, scale_inv, amax,
-                                              out_row, out_col, nullptr, nullptr,
+  log_dispatch("te_cast_transpose", "tile128x128", out_dtype == TE_E5M2 ? "E5M2" : "E4M3");
+  return hip_status(te::launch_cast_transpose(x, x_dtype, rows, cols, out_dtype == TE_E5M2, mode, margin, scale,
+                                              scale_inv, amax, out_row, out_col, nullptr, nullptr, amax_workspace,
                                               static_cast<hipStream_t>(stream)),
                     "te_cast_transpose launch");
 }
 
 int64_t te_cast_transpose_dbias_workspace_bytes(int64_t rows, int64_t cols) {
   if (rows < 0 || cols < 0) return -1;
-  return ((rows + 127) / 128) * cols * static_cast<int64_t>(sizeof(float));
+  return kAmaxWsBytes + ((rows + 127) / 128) * cols * static_cast<int64_t>(sizeof(float));
 }
 
 int64_t te_mx_scale_panel_bytes(int64_t rows, int64_t cols) {
@@ -166,15 +173,15 @@ te_status te_cast_transpose_dbias(const void* x, int x_dtype, int64_t rows, int6
   if ((rows + 127) / 128 > 65535) return fail(TE_ERR_SHAPE, "rows too large for the tile grid");
   if (cols > 0 && !dbias) return fail(TE_ERR_NULL, "dbias is NULL");
   const int64_t need = te_cast_transpose_dbias_workspace_bytes(rows, cols);
-  if (need > 0 && (!workspace || workspace_bytes < need))
+  if (!workspace || workspace_bytes < need)
     return fail(TE_ERR_ARG, "workspace of %lld bytes needed (got %lld)", (long long)need, (long long)workspace_bytes);
-  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0)
-    return fail(TE_ERR_ALIGN, "workspace must be 4-byte aligned");
+  if (!aligned16(workspace)) return fail(TE_ERR_ALIGN, "workspace must be 16-byte aligned");
   if ((st = check_device()) != TE_OK) return st;
   log_dispatch("te_cast_transpose_dbias", "tile128x128_colsum", out_dtype == TE_E5M2 ? "E5M2" : "E4M3");
-  return hip_status(te::launch_cast_transpose(x, x_dtype, rows, cols, out_dtype == TE_E5M2,
-                                              mode == TE_SCALE_CURRENT, margin, scale, scale_inv, amax,
-                                              out_row, out_col, dbias, static_cast<float*>(workspace),
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  return hip_status(te::launch_cast_transpose(x, x_dtype, rows, cols, out_dtype == TE_E5M2, mode, margin, scale,
+                                              scale_inv, amax, out_row, out_col, dbias,
+                                              reinterpret_cast<float*>(ws + kAmaxWsBytes), ws,
                                               static_cast<hipStream_t>(stream)),
                     "te_cast_transpose_dbias launch");
 }
@@ -182,9 +189,11 @@ te_status te_cast_transpose_dbias(const void* x, int x_dtype, int64_t rows, int6
 te_status te_layernorm_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, const void* gamma,
                            const void* beta, int param_dtype, float eps, int out_dtype, int mode, int margin,
                            float* scale, float* scale_inv, float* amax, uint8_t* out, float* mu, float* rsigma,
-                           void* stream) {
+                           void* amax_workspace, void* stream) {
   te_status st = check_cast_common(x, x_dtype, rows, cols, out_dtype, mode, margin, scale, scale_inv, amax);
   if (st != TE_OK) return st;
+  if (mode == TE_SCALE_CURRENT_FROM_AMAX)
+    return fail(TE_ERR_UNSUPPORTED, "te_layernorm_fp8 computes the amax of its own output (delayed or current)");
   if (rows > 0 && cols == 0) return fail(TE_ERR_SHAPE, "LayerNorm needs cols > 0");
   if (cols % 16 != 0) return fail(TE_ERR_SHAPE, "cols must be a multiple of 16 (got %lld)", (long long)cols);
   if (!is_hp(param_dtype)) return fail(TE_ERR_DTYPE, "param_dtype must be TE_F32 or TE_BF16 (got %d)", param_dtype);
@@ -192,12 +201,14 @@ te_status te_layernorm_fp8(const void* x, int x_dtype, int64_t rows, int64_t col
   if (rows > 0 && (!gamma || !beta || !out)) return fail(TE_ERR_NULL, "gamma, beta and out are required");
   if ((out && !aligned16(out)) || (gamma && !aligned16(gamma)) || (beta && !aligned16(beta)))
     return fail(TE_ERR_ALIGN, "out, gamma and beta must be 16-byte aligned");
+  if ((st = check_amax_workspace(amax_workspace, true)) != TE_OK) return st;
   if ((st = check_device()) != TE_OK) return st;
   log_dispatch("te_layernorm_fp8", mode == TE_SCALE_CURRENT ? "row_per_block_two_pass" : "row_per_block",
                out_dtype == TE_E5M2 ? "E5M2" : "E4M3");
   return hip_status(te::launch_layernorm_fp8(x, x_dtype, rows, cols, gamma, beta, param_dtype, eps,
                                              out_dtype == TE_E5M2, mode == TE_SCALE_CURRENT, margin, scale,
-                                             scale_inv, amax, out, mu, rsigma, static_cast<hipStream_t>(stream)),
+                                             scale_inv, amax, out, mu, rsigma, amax_workspace,
+                                             static_cast<hipStream_t>(stream)),
                     "te_layernorm_fp8 launch");
 }
 

@@ -11,19 +11,23 @@ namespace te {
 enum : int { F32 = 0, BF16 = 1, E4M3 = 2, E5M2 = 3, E8M0 = 4, E2M1 = 5 };
 
 // ---- quantizers (quant.hip) ----
-hipError_t launch_amax_cast(const void* x, int x_dtype, int64_t n, int out_e5m2, int current,
+// Scaling modes of the quantizers: 0 delayed, 1 current (amax pass + cast pass),
+// 2 current with the amax already in *amax (cast pass only).  `ws`: the caller's
+// grid-amax workspace (AmaxWork, grid_amax.hpp).
+hipError_t launch_amax_cast(const void* x, int x_dtype, int64_t n, int out_e5m2, int mode,
                             int margin, float* scale, float* scale_inv, float* amax,
-                            uint8_t* out, hipStream_t s);
+                            uint8_t* out, void* ws, hipStream_t s);
 
 hipError_t launch_cast_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols,
-                                 int out_e5m2, int current, int margin, float* scale,
+                                 int out_e5m2, int mode, int margin, float* scale,
                                  float* scale_inv, float* amax, uint8_t* out_row,
-                                 uint8_t* out_col, float* dbias, float* dbias_part, hipStream_t s);
+                                 uint8_t* out_col, float* dbias, float* dbias_part, void* ws,
+                                 hipStream_t s);
 
 hipError_t launch_layernorm_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, const void* gamma,
                                 const void* beta, int param_dtype, float eps, int out_e5m2, int current,
                                 int margin, float* scale, float* scale_inv, float* amax, uint8_t* out,
-                                float* mu, float* rsigma, hipStream_t s);
+                                float* mu, float* rsigma, void* ws, hipStream_t s);
 
 hipError_t launch_scale_update(float* hist, float* scale, float* scale_inv, int n, int hist_len,
                                int e5m2, int most_recent, int margin, hipStream_t s);

@@ -12,12 +12,11 @@
 // once per output layout.  Loads and stores are 16 bytes per lane.
 
 #include <algorithm>
-#include <map>
-#include <mutex>
 #include <type_traits>
 #include <utility>
 
 #include "device_common.hpp"
+#include "grid_amax.hpp"
 #include "internal.hpp"
 
 namespace te {
@@ -71,89 +70,14 @@ __global__ void k_prologue(float* amax, const float* scale, float* scale_inv, in
   if (delayed) *scale_inv = 1.0f / *scale;
 }
 
-// ----------------------------------------------------------------------------
-// Grid-wide amax in the quantizing launch itself.  One atomic per block on the
-// amax word would queue every block's update on one address at the end of the
-// launch (several microseconds for a couple of thousand blocks), and the word
-// would need a zeroing launch first.  Instead block b folds its maximum
-// (magnitude bits; NaN, whose bits are largest, wins) into the max word of group
-// b % kAmaxGroups and then arrives at that group's counter; the last arrival of
-// a group folds the group max into the top max word and arrives at the top
-// counter, and the last arrival there -- the last block of the grid -- writes
-// *amax (the max with the value already there when `acc` is set, for a second
-// launch over the same tensor).  Every word is cleared by the read that consumes
-// it, ready for the next launch.  At most 64 blocks queue on one address.
-//
-// Ordering: every access to the workspace is a device-scope atomic read-modify-
-// write, performed where all of them are, and each arrival is issued only after
-// the preceding max has returned, i.e. has been performed; so when a counter
-// reaches its count, every max folded before those arrivals is already in the
-// max word.  No release fence is needed, which matters: a device-scope release
-// writes back the whole L2 of the XCD, and one per block costs more than the
-// contended atomics it replaces.  The workspace belongs to one stream (launches
-// on one stream run one after another).
-// ----------------------------------------------------------------------------
-constexpr int kAmaxGroups = 32;
-constexpr int kAmaxLine = 64;          // words per 256-byte line: [0] max bits, [1] arrivals
-constexpr int kAmaxMaxBlocks = 4096;   // persistent grids are capped below this
-
-struct AmaxWork {
-  uint32_t grp[kAmaxGroups * kAmaxLine];
-  uint32_t top[kAmaxLine];
-};
-
-// flags of the quantizing kernels
+// flags of the quantizing kernels (the grid-wide amax itself is in grid_amax.hpp)
 constexpr int kAccAmax = 1;     // *amax = max(*amax, amax of this launch)
 constexpr int kPublishInv = 2;  // block 0 writes scale_inv = 1 / scale (delayed scaling)
 
-__device__ __forceinline__ uint32_t rmw_max(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t rmw_add(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t rmw_take(uint32_t* p) {  // read and clear
-  return __hip_atomic_exchange(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// wait until the returned value of an atomic is here (it has been performed);
-// the memory clobber keeps later accesses from being moved above
-__device__ __forceinline__ void performed(uint32_t v) {
-  asm volatile("s_waitcnt vmcnt(0)" : : "v"(v) : "memory");
-}
-
-// Every block of the grid calls this exactly once, with all kThreads threads.
-__device__ __forceinline__ void grid_amax(float v, float* amax, AmaxWork* w, bool acc) {
+// grid_amax for the 256-thread quantizer blocks
+__device__ __forceinline__ void grid_amax_q(float v, float* amax, AmaxWork* w, bool acc) {
   __shared__ uint32_t red[kThreads / 64];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  uint32_t b = __float_as_uint(v);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) b = max(b, static_cast<uint32_t>(__shfl_xor(static_cast<int>(b), off, 64)));
-  if (lane == 0) red[wid] = b;
-  __syncthreads();
-  if (threadIdx.x != 0) return;
-  uint32_t mb = red[0];
-#pragma unroll
-  for (int i = 1; i < kThreads / 64; ++i) mb = max(mb, red[i]);
-  const int G = static_cast<int>(gridDim.x), blk = static_cast<int>(blockIdx.x);
-  const int g = blk % kAmaxGroups;
-  const uint32_t members = static_cast<uint32_t>((G - 1 - g) / kAmaxGroups + 1);
-  const uint32_t groups = static_cast<uint32_t>(min(G, kAmaxGroups));
-  uint32_t* gw = w->grp + g * kAmaxLine;
-  performed(rmw_max(gw, mb));
-  if (rmw_add(gw + 1, 1u) != members - 1) return;
-  const uint32_t gm = rmw_take(gw);
-  performed(rmw_take(gw + 1));
-  performed(rmw_max(w->top, gm));
-  if (rmw_add(w->top + 1, 1u) != groups - 1) return;
-  uint32_t r = rmw_take(w->top);
-  performed(rmw_take(w->top + 1));
-  if (acc) r = max(r, __float_as_uint(*amax));
-  *amax = __uint_as_float(r);
-}
-
-__global__ void k_zero_words(uint32_t* p, int n) {
-  const int i = static_cast<int>(blockIdx.x * blockDim.x + threadIdx.x);
-  if (i < n) p[i] = 0u;
+  grid_amax<kThreads>(v, amax, w, acc, red);
 }
 
 // Finalize current scaling without a cast: scale and scale_inv from amax.
@@ -304,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void k_amax_cast(const T* __restrict__ x,
       }
     }
   }
-  if constexpr (kAmax) grid_amax(absmax_value<T>(m), amax, work, (flags & kAccAmax) != 0);
+  if constexpr (kAmax) grid_amax_q(absmax_value<T>(m), amax, work, (flags & kAccAmax) != 0);
 }
 
 // ----------------------------------------------------------------------------
@@ -536,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void k_cast_transpose(
       c0 = c1;
     }
   }
-  if constexpr (MODE == 0) grid_amax(absmax_value<T>(m), amax, work, (flags & kAccAmax) != 0);
+  if constexpr (MODE == 0) grid_amax_q(absmax_value<T>(m), amax, work, (flags & kAccAmax) != 0);
 }
 
 // dbias[c] = sum over tile rows of the partial column sums (0 when R == 0), in a fixed
@@ -726,7 +650,7 @@ __global__ __launch_bounds__(kThreads) void k_layernorm(const T* __restrict__ x,
       for (int64_t ch = lane; ch < nch; ch += 64) out_chunk(load(ch), ch);
     }
   }
-  if constexpr (MODE != 2) grid_amax(__uint_as_float(m), amax, work, (flags & kAccAmax) != 0);
+  if constexpr (MODE != 2) grid_amax_q(__uint_as_float(m), amax, work, (flags & kAccAmax) != 0);
 }
 
 // ----------------------------------------------------------------------------
@@ -1246,23 +1170,15 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_tiles(const uint16_t* __rest
 }
 
 // Blocks of `kernel` (kThreads threads) that fit at once on one compute unit, and the
-// compute units of the current device; cached per kernel and device.
+// compute units of the current device, asked of the runtime at every launch (the
+// library keeps no cache of them).
 std::pair<int, int> occupancy(const void* kernel) {
-  static std::mutex mu;
-  static std::map<std::pair<const void*, int>, std::pair<int, int>> cache;
-  int dev = 0;
+  int dev = 0, per_cu = 1, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess) return {1, 256};
-  std::lock_guard<std::mutex> lock(mu);
-  const auto key = std::make_pair(kernel, dev);
-  auto it = cache.find(key);
-  if (it != cache.end()) return it->second;
-  int per_cu = 1, cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess || per_cu < 1)
     per_cu = 1;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-  const auto v = std::make_pair(per_cu, cus);
-  cache.emplace(key, v);
-  return v;
+  return {per_cu, cus};
 }
 
 // Persistent grid: one block per `per_block` work units, at most max_per_cu resident
@@ -1287,30 +1203,6 @@ constexpr int kCapMxRow = 2;
 constexpr int kCapMxCol = 8;
 constexpr int kCapLn = 8;  // LayerNorm: four rows per block, one per wave
 
-// The grid-amax workspace of (current device, stream), allocated and zeroed (by a
-// kernel on that stream) at the first quantizing call on the stream, kept until
-// the process ends.
-AmaxWork* amax_work(hipStream_t st) {
-  static std::mutex mu;
-  static std::map<std::pair<int, hipStream_t>, AmaxWork*> ws;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-  std::lock_guard<std::mutex> lock(mu);
-  const auto key = std::make_pair(dev, st);
-  auto it = ws.find(key);
-  if (it != ws.end()) return it->second;
-  void* p = nullptr;
-  if (hipMalloc(&p, sizeof(AmaxWork)) != hipSuccess) return nullptr;
-  constexpr int nw = static_cast<int>(sizeof(AmaxWork) / 4);
-  hipLaunchKernelGGL(k_zero_words, dim3((nw + 255) / 256), dim3(256), 0, st, static_cast<uint32_t*>(p), nw);
-  if (hipGetLastError() != hipSuccess) {
-    (void)hipFree(p);
-    return nullptr;
-  }
-  ws.emplace(key, static_cast<AmaxWork*>(p));
-  return static_cast<AmaxWork*>(p);
-}
-
 template <typename T, bool E5M2, int MODE>
 void launch_flat(const T* x, int64_t n, int margin, float* scale, float* scale_inv, float* amax,
                  uint8_t* out, AmaxWork* work, int flags, hipStream_t st) {
@@ -1319,22 +1211,23 @@ void launch_flat(const T* x, int64_t n, int margin, float* scale, float* scale_i
   hipLaunchKernelGGL(fn, dim3(g), dim3(kThreads), 0, st, x, n, scale, scale_inv, amax, out, margin, work, flags);
 }
 
+// mode: 0 delayed (one pass: amax + cast with *scale), 1 current (amax pass, then the
+// cast pass with the scale from it), 2 current with the amax already in *amax (the cast
+// pass only).
 template <typename T, bool E5M2>
-hipError_t amax_cast_t(const T* x, int64_t n, int current, int margin, float* scale,
-                       float* scale_inv, float* amax, uint8_t* out, hipStream_t st) {
-  AmaxWork* w = amax_work(st);
-  if (w == nullptr) return hipErrorOutOfMemory;
-  if (!current) {
+hipError_t amax_cast_t(const T* x, int64_t n, int mode, int margin, float* scale, float* scale_inv, float* amax,
+                       uint8_t* out, AmaxWork* w, hipStream_t st) {
+  if (mode == 0) {
     if (out) launch_flat<T, E5M2, 0>(x, n, margin, scale, scale_inv, amax, out, w, kPublishInv, st);
     else launch_flat<T, E5M2, 1>(x, n, margin, scale, scale_inv, amax, out, w, kPublishInv, st);
-  } else {
-    launch_flat<T, E5M2, 1>(x, n, margin, scale, scale_inv, amax, out, w, 0, st);
-    if (out)
-      launch_flat<T, E5M2, 2>(x, n, margin, scale, scale_inv, amax, out, w, 0, st);
-    else
-      hipLaunchKernelGGL(k_current_scale, dim3(1), dim3(1), 0, st, amax, scale, scale_inv,
-                         Fp8Traits<E5M2>::max, margin);
+    return hipGetLastError();
   }
+  if (mode == 1) launch_flat<T, E5M2, 1>(x, n, margin, scale, scale_inv, amax, out, w, 0, st);
+  if (out)
+    launch_flat<T, E5M2, 2>(x, n, margin, scale, scale_inv, amax, out, w, 0, st);
+  else
+    hipLaunchKernelGGL(k_current_scale, dim3(1), dim3(1), 0, st, amax, scale, scale_inv, Fp8Traits<E5M2>::max,
+                       margin);
   return hipGetLastError();
 }
 
@@ -1359,11 +1252,12 @@ void ct_launch(const T* x, int64_t R, int64_t C, int margin, float* scale, float
 }
 
 template <typename T, bool E5M2>
-hipError_t cast_transpose_t(const T* x, int64_t R, int64_t C, int current, int margin,
-                            float* scale, float* scale_inv, float* amax, uint8_t* out_row,
-                            uint8_t* out_col, float* dbias, float* part, hipStream_t st) {
+hipError_t cast_transpose_t(const T* x, int64_t R, int64_t C, int mode, int margin, float* scale, float* scale_inv,
+                            float* amax, uint8_t* out_row, uint8_t* out_col, float* dbias, float* part,
+                            AmaxWork* w, hipStream_t st) {
+  const bool current = mode != 0;
   if (R == 0 || C == 0) {
-    hipLaunchKernelGGL(k_prologue, dim3(1), dim3(1), 0, st, amax, scale, scale_inv, current ? 0 : 1);
+    if (mode != 2) hipLaunchKernelGGL(k_prologue, dim3(1), dim3(1), 0, st, amax, scale, scale_inv, current ? 0 : 1);
     if (current)
       hipLaunchKernelGGL(k_current_scale, dim3(1), dim3(1), 0, st, amax, scale, scale_inv,
                          Fp8Traits<E5M2>::max, margin);
@@ -1372,9 +1266,7 @@ hipError_t cast_transpose_t(const T* x, int64_t R, int64_t C, int current, int m
                          part, int64_t{0}, C, dbias);
     return hipGetLastError();
   }
-  AmaxWork* w = amax_work(st);
-  if (w == nullptr) return hipErrorOutOfMemory;
-  if (current) launch_flat<T, E5M2, 1>(x, R * C, margin, scale, scale_inv, amax, nullptr, w, 0, st);
+  if (mode == 1) launch_flat<T, E5M2, 1>(x, R * C, margin, scale, scale_inv, amax, nullptr, w, 0, st);
   if (dbias != nullptr) {
     if (current) ct_launch<T, E5M2, 2, true>(x, R, C, margin, scale, scale_inv, amax, out_row, out_col, w, 0, part, st);
     else ct_launch<T, E5M2, 0, true>(x, R, C, margin, scale, scale_inv, amax, out_row, out_col, w, kPublishInv, part, st);
@@ -1431,7 +1323,7 @@ void ln_launch(const T* x, int64_t R, int64_t C, const P* g, const P* b, float e
 template <typename T, typename P, bool E5M2>
 hipError_t layernorm_t(const T* x, int64_t R, int64_t C, const P* g, const P* b, float eps, int current,
                        int margin, float* scale, float* sinv, float* amax, uint8_t* out, float* mu, float* rs,
-                       hipStream_t st) {
+                       AmaxWork* w, hipStream_t st) {
   if (R == 0) {
     hipLaunchKernelGGL(k_prologue, dim3(1), dim3(1), 0, st, amax, scale, sinv, current ? 0 : 1);
     if (current)
@@ -1439,8 +1331,6 @@ hipError_t layernorm_t(const T* x, int64_t R, int64_t C, const P* g, const P* b,
                          margin);
     return hipGetLastError();
   }
-  AmaxWork* w = amax_work(st);
-  if (w == nullptr) return hipErrorOutOfMemory;
   if (!current) {
     ln_launch<T, P, E5M2, 0>(x, R, C, g, b, eps, margin, scale, sinv, amax, out, mu, rs, w, kPublishInv, st);
   } else {
@@ -1453,32 +1343,32 @@ hipError_t layernorm_t(const T* x, int64_t R, int64_t C, const P* g, const P* b,
 template <typename T, typename P>
 hipError_t layernorm_fmt(const T* x, int64_t R, int64_t C, const P* g, const P* b, float eps, int e5m2,
                          int current, int margin, float* scale, float* sinv, float* amax, uint8_t* out,
-                         float* mu, float* rs, hipStream_t st) {
-  return e5m2 ? layernorm_t<T, P, true>(x, R, C, g, b, eps, current, margin, scale, sinv, amax, out, mu, rs, st)
-              : layernorm_t<T, P, false>(x, R, C, g, b, eps, current, margin, scale, sinv, amax, out, mu, rs, st);
+                         float* mu, float* rs, AmaxWork* w, hipStream_t st) {
+  return e5m2 ? layernorm_t<T, P, true>(x, R, C, g, b, eps, current, margin, scale, sinv, amax, out, mu, rs, w, st)
+              : layernorm_t<T, P, false>(x, R, C, g, b, eps, current, margin, scale, sinv, amax, out, mu, rs, w, st);
 }
 
 }  // namespace
 
-hipError_t launch_amax_cast(const void* x, int x_dtype, int64_t n, int out_e5m2, int current,
-                            int margin, float* scale, float* scale_inv, float* amax, uint8_t* out,
-                            hipStream_t s) {
+hipError_t launch_amax_cast(const void* x, int x_dtype, int64_t n, int out_e5m2, int mode, int margin, float* scale,
+                            float* scale_inv, float* amax, uint8_t* out, void* ws, hipStream_t s) {
+  auto* w = static_cast<AmaxWork*>(ws);
   if (x_dtype == BF16)
-    return out_e5m2 ? amax_cast_t<uint16_t, true>(static_cast<const uint16_t*>(x), n, current, margin, scale, scale_inv, amax, out, s)
-                    : amax_cast_t<uint16_t, false>(static_cast<const uint16_t*>(x), n, current, margin, scale, scale_inv, amax, out, s);
-  return out_e5m2 ? amax_cast_t<float, true>(static_cast<const float*>(x), n, current, margin, scale, scale_inv, amax, out, s)
-                  : amax_cast_t<float, false>(static_cast<const float*>(x), n, current, margin, scale, scale_inv, amax, out, s);
+    return out_e5m2 ? amax_cast_t<uint16_t, true>(static_cast<const uint16_t*>(x), n, mode, margin, scale, scale_inv, amax, out, w, s)
+                    : amax_cast_t<uint16_t, false>(static_cast<const uint16_t*>(x), n, mode, margin, scale, scale_inv, amax, out, w, s);
+  return out_e5m2 ? amax_cast_t<float, true>(static_cast<const float*>(x), n, mode, margin, scale, scale_inv, amax, out, w, s)
+                  : amax_cast_t<float, false>(static_cast<const float*>(x), n, mode, margin, scale, scale_inv, amax, out, w, s);
 }
 
-hipError_t launch_cast_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols,
-                                 int out_e5m2, int current, int margin, float* scale,
-                                 float* scale_inv, float* amax, uint8_t* out_row,
-                                 uint8_t* out_col, float* dbias, float* dbias_part, hipStream_t s) {
+hipError_t launch_cast_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols, int out_e5m2, int mode,
+                                 int margin, float* scale, float* scale_inv, float* amax, uint8_t* out_row,
+                                 uint8_t* out_col, float* dbias, float* dbias_part, void* ws, hipStream_t s) {
+  auto* w = static_cast<AmaxWork*>(ws);
   if (x_dtype == BF16)
-    return out_e5m2 ? cast_transpose_t<uint16_t, true>(static_cast<const uint16_t*>(x), rows, cols, current, margin, scale, scale_inv, amax, out_row, out_col, dbias, dbias_part, s)
-                    : cast_transpose_t<uint16_t, false>(static_cast<const uint16_t*>(x), rows, cols, current, margin, scale, scale_inv, amax, out_row, out_col, dbias, dbias_part, s);
-  return out_e5m2 ? cast_transpose_t<float, true>(static_cast<const float*>(x), rows, cols, current, margin, scale, scale_inv, amax, out_row, out_col, dbias, dbias_part, s)
-                  : cast_transpose_t<float, false>(static_cast<const float*>(x), rows, cols, current, margin, scale, scale_inv, amax, out_row, out_col, dbias, dbias_part, s);
+    return out_e5m2 ? cast_transpose_t<uint16_t, true>(static_cast<const uint16_t*>(x), rows, cols, mode, margin, scale, scale_inv, amax, out_row, out_col, dbias, dbias_part, w, s)
+                    : cast_transpose_t<uint16_t, false>(static_cast<const uint16_t*>(x), rows, cols, mode, margin, scale, scale_inv, amax, out_row, out_col, dbias, dbias_part, w, s);
+  return out_e5m2 ? cast_transpose_t<float, true>(static_cast<const float*>(x), rows, cols, mode, margin, scale, scale_inv, amax, out_row, out_col, dbias, dbias_part, w, s)
+                  : cast_transpose_t<float, false>(static_cast<const float*>(x), rows, cols, mode, margin, scale, scale_inv, amax, out_row, out_col, dbias, dbias_part, w, s);
 }
 
 hipError_t launch_scale_update(float* hist, float* scale, float* scale_inv, int n, int hist_len,
@@ -1549,21 +1439,22 @@ hipError_t launch_mx_quantize_panel(const void* x, int64_t rows, int64_t cols, i
 hipError_t launch_layernorm_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, const void* gamma,
                                 const void* beta, int param_dtype, float eps, int out_e5m2, int current,
                                 int margin, float* scale, float* scale_inv, float* amax, uint8_t* out,
-                                float* mu, float* rsigma, hipStream_t s) {
+                                float* mu, float* rsigma, void* ws, hipStream_t s) {
+  auto* w = static_cast<AmaxWork*>(ws);
   if (x_dtype == BF16) {
     const auto* xx = static_cast<const uint16_t*>(x);
     if (param_dtype == BF16)
       return layernorm_fmt(xx, rows, cols, static_cast<const uint16_t*>(gamma), static_cast<const uint16_t*>(beta),
-                           eps, out_e5m2, current, margin, scale, scale_inv, amax, out, mu, rsigma, s);
+                           eps, out_e5m2, current, margin, scale, scale_inv, amax, out, mu, rsigma, w, s);
     return layernorm_fmt(xx, rows, cols, static_cast<const float*>(gamma), static_cast<const float*>(beta), eps,
-                         out_e5m2, current, margin, scale, scale_inv, amax, out, mu, rsigma, s);
+                         out_e5m2, current, margin, scale, scale_inv, amax, out, mu, rsigma, w, s);
   }
   const auto* xx = static_cast<const float*>(x);
   if (param_dtype == BF16)
     return layernorm_fmt(xx, rows, cols, static_cast<const uint16_t*>(gamma), static_cast<const uint16_t*>(beta),
-                         eps, out_e5m2, current, margin, scale, scale_inv, amax, out, mu, rsigma, s);
+                         eps, out_e5m2, current, margin, scale, scale_inv, amax, out, mu, rsigma, w, s);
   return layernorm_fmt(xx, rows, cols, static_cast<const float*>(gamma), static_cast<const float*>(beta), eps,
-                       out_e5m2, current, margin, scale, scale_inv, amax, out, mu, rsigma, s);
+                       out_e5m2, current, margin, scale, scale_inv, amax, out, mu, rsigma, w, s);
 }
 
 }  // namespace te

@@ -195,32 +195,32 @@ def cast(args):
     si = torch.empty(1, device=dev)
     am = torch.empty(1, device=dev)
     mode = B.TE_SCALE_CURRENT if args.mode == "current" else B.TE_SCALE_DELAYED
+    wsa = B.amax_workspace(torch.device(dev))
     if args.op == "cast":
         out = torch.empty((R, C), dtype=torch.uint8, device=dev)
-        fn = lambda: B.te_amax_cast(x, "E4M3", mode, 0, scale, si, am, out)  # noqa: E731
+        fn = lambda: B.te_amax_cast(x, "E4M3", mode, 0, scale, si, am, out, workspace=wsa)  # noqa: E731
         nbytes = R * C * (5 if mode == B.TE_SCALE_CURRENT else 3)
     elif args.op == "transpose":
         out = torch.empty((C, R), dtype=torch.uint8, device=dev)
-        fn = lambda: B.te_cast_transpose(x, "E4M3", mode, 0, scale, si, am, None, out)  # noqa: E731
+        fn = lambda: B.te_cast_transpose(x, "E4M3", mode, 0, scale, si, am, None, out, workspace=wsa)  # noqa: E731
         nbytes = R * C * (5 if mode == B.TE_SCALE_CURRENT else 3)
     elif args.op == "both":
         o1 = torch.empty((R, C), dtype=torch.uint8, device=dev)
         o2 = torch.empty((C, R), dtype=torch.uint8, device=dev)
-        fn = lambda: B.te_cast_transpose(x, "E4M3", mode, 0, scale, si, am, o1, o2)  # noqa: E731
+        fn = lambda: B.te_cast_transpose(x, "E4M3", mode, 0, scale, si, am, o1, o2, workspace=wsa)  # noqa: E731
         nbytes = R * C * (6 if mode == B.TE_SCALE_CURRENT else 4)
     elif args.op == "bothdbias":  # both copies plus the bias gradient (column sums) of x
         o1 = torch.empty((R, C), dtype=torch.uint8, device=dev)
         o2 = torch.empty((C, R), dtype=torch.uint8, device=dev)
         db = torch.empty(C, dtype=torch.float32, device=dev)
-        ws = torch.empty(max(B.te_cast_transpose_dbias_workspace_bytes(R, C) // 4, 1), dtype=torch.float32,
-                         device=dev)
+        ws = B.dbias_workspace(R, C, torch.device(dev))
         fn = lambda: B.te_cast_transpose_dbias(x, "E5M2", mode, 0, scale, si, am, db, ws, o1, o2)  # noqa: E731
         nbytes = R * C * (6 if mode == B.TE_SCALE_CURRENT else 4) + C * 4
     elif args.op == "ln":  # LayerNorm over the rows, written as FP8 codes
         out = torch.empty((R, C), dtype=torch.uint8, device=dev)
         g = torch.ones(C, device=dev)
         b = torch.zeros(C, device=dev)
-        fn = lambda: B.te_layernorm_fp8(x, g, b, 1e-5, "E4M3", mode, 0, scale, si, am, out)  # noqa: E731
+        fn = lambda: B.te_layernorm_fp8(x, g, b, 1e-5, "E4M3", mode, 0, scale, si, am, out, workspace=wsa)  # noqa: E731
         nbytes = R * C * (5 if mode == B.TE_SCALE_CURRENT else 3)
     elif args.op == "mx":  # row-wise copy
         o1 = torch.empty((R, C), dtype=torch.uint8, device=dev)

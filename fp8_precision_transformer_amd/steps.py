@@ -1,9 +1,11 @@
 """Whole steps of the FP8 linear-layer path, enqueued through the C ABI on one stream.
 
-A step object owns its device buffers and enqueues every kernel of one step with
-``run()``, so the same step can be timed eagerly or captured once into a HIP graph
-and replayed (``capture``): the small configurations are bound by launch latency,
-not by the kernels.
+A step object owns its device buffers, its amax workspace included, and enqueues
+every kernel of one step with ``run()``, so the same step can be timed eagerly or
+captured once into a HIP graph and replayed (``capture``): the small configurations
+are bound by launch latency, not by the kernels.  A graph captured from a step uses
+that step's workspace, so it can be replayed on any stream while other work (with
+its own workspace) runs beside it.
 
 - ``LinearForwardStep``: the 768 -> 768 Linear layer of [FP8-intro] "Transformer
   Engine の使い方" on 1024 tokens of fp32 input, delayed scaling (history 16, max,
@@ -53,6 +55,7 @@ class LinearForwardStep:
         self.xq = torch.empty((t, f), dtype=torch.uint8, device=dev)
         self.wq = torch.empty((f, f), dtype=torch.uint8, device=dev)
         self.y = torch.empty((t, f), dtype=torch.bfloat16, device=dev)
+        self.ws = B.amax_workspace(dev)
         self.flops = 2 * t * f * f
 
     def reset(self):
@@ -65,9 +68,9 @@ class LinearForwardStep:
     def run(self):
         s = self.stream
         B.te_amax_cast(self.x, E4, B.TE_SCALE_DELAYED, 0, self.scale[0:1], self.scale_inv[0:1],
-                       self.hist[0, 0:1], self.xq, stream=s)
+                       self.hist[0, 0:1], self.xq, workspace=self.ws, stream=s)
         B.te_amax_cast(self.w, E4, B.TE_SCALE_DELAYED, 0, self.scale[1:2], self.scale_inv[1:2],
-                       self.hist[1, 0:1], self.wq, stream=s)
+                       self.hist[1, 0:1], self.wq, workspace=self.ws, stream=s)
         B.te_fp8_gemm(self.xq, E4, self.scale_inv[0:1], self.wq, E4, self.scale_inv[1:2], self.y,
                       bias=self.b, stream=s)
         B.te_scale_update(self.hist, self.scale, self.scale_inv, E4, B.TE_AMAX_MAX, 0, stream=s)
@@ -101,6 +104,7 @@ class LayerStep:
         bf = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=dev)  # noqa: E731
         f1 = lambda: torch.ones(1, dtype=torch.float32, device=dev)  # noqa: E731
         self.t = {}
+        self.ws = B.amax_workspace(dev)
         self.flops = 0
         for li, w in enumerate(self.weights):
             K, N = w.in_features, w.out_features
@@ -133,10 +137,10 @@ class LayerStep:
         for w in self.weights:
             t = self.t[w.name]
             sx, sw, sg = t["sc"]["x"], t["sc"]["w"], t["sc"]["dy"]
-            B.te_cast_transpose(t["X"], E4, cur, 0, *sx, t["x"], t["xT"], stream=s)
-            B.te_cast_transpose(t["W"], E4, cur, 0, *sw, t["w"], t["wT"], stream=s)
+            B.te_cast_transpose(t["X"], E4, cur, 0, *sx, t["x"], t["xT"], workspace=self.ws, stream=s)
+            B.te_cast_transpose(t["W"], E4, cur, 0, *sw, t["w"], t["wT"], workspace=self.ws, stream=s)
             self._gemm((w.name, "fprop"), t["x"], E4, sx[1], t["w"], E4, sw[1], t["y"])
-            B.te_cast_transpose(t["DY"], E5, cur, 0, *sg, t["dy"], t["dyT"], stream=s)
+            B.te_cast_transpose(t["DY"], E5, cur, 0, *sg, t["dy"], t["dyT"], workspace=self.ws, stream=s)
             self._gemm((w.name, "dgrad"), t["dy"], E5, sg[1], t["wT"], E4, sw[1], t["dx"])
             self._gemm((w.name, "wgrad"), t["dyT"], E5, sg[1], t["xT"], E4, sx[1], t["dw"])
 
@@ -152,9 +156,8 @@ class LayerStep:
 
 
 def capture(step) -> torch.cuda.CUDAGraph:
-    """Capture one ``step.run()`` on the step's stream into a HIP graph.  Run the step
-    eagerly once before: the first quantizing call on a stream allocates that stream's
-    amax workspace, which must not happen during capture."""
+    """Capture one ``step.run()`` on the step's stream into a HIP graph (the step's
+    buffers and workspace are allocated already, so the capture allocates nothing)."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=step.stream, capture_error_mode="thread_local"):
         step.run()

@@ -15,17 +15,21 @@
  *
  * Conventions shared by every entry point:
  *   - Pointers are DEVICE pointers unless marked (host).  The caller allocates
- *     and owns every buffer, including the scaling state.  The library keeps no
- *     pointer to them after a call returns.  Its own state: a per-thread error
- *     string, a per-device architecture check, a per-device cache of kernel
- *     occupancies (the quantizers' grid sizes) and, for te_amax_cast and
- *     te_cast_transpose, one 8448-byte device workspace per (device, stream)
- *     pair holding the counters of the grid-wide amax reduction.  The first
- *     such call on a pair allocates it (hipMalloc) and clears it with a kernel
- *     on that stream; it lives until the process ends.  Make that first call
- *     outside stream capture.  Calls on one stream run one after another and
- *     so share the workspace safely; calls on different streams use different
- *     workspaces.
+ *     and owns every buffer, including the scaling state and every workspace.
+ *     The library allocates no memory, keeps no pointer to the caller's buffers
+ *     after a call returns and caches nothing between calls: its only state is
+ *     a per-thread error string and the name of the last GEMM variant
+ *     (te_gemm_variant), both diagnostics.
+ *   - Amax workspace.  Calls that reduce an amax over a whole tensor inside one
+ *     launch (te_amax_cast, te_cast_transpose, te_cast_transpose_dbias,
+ *     te_layernorm_fp8, te_fp8_gemm_amax) keep the counters of that grid-wide
+ *     reduction in a caller-owned device workspace of te_amax_workspace_bytes()
+ *     bytes, 16-byte aligned, which must be all zero before its first use
+ *     (e.g. cleared once at allocation).  Every launch that completes leaves it
+ *     all zero again, so it can be reused without clearing.  Calls that may run
+ *     at the same time (on different streams, or a captured graph replayed
+ *     beside eager work) must use different workspaces; calls on one stream run
+ *     one after another and may share one.
  *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
  *     default stream).  There is no host synchronization inside.  Scale, amax
  *     and history values never leave the device.
@@ -73,8 +77,11 @@ typedef enum { TE_F32 = 0, TE_BF16 = 1, TE_E4M3 = 2, TE_E5M2 = 3, TE_E8M0 = 4, T
 /* [FP8-intro] "FP8 Training について": one scale per tensor, refreshed every step.
  * DELAYED: the scale comes from the amax history of earlier steps
  * ([FP8-intro] "Transformer Engine の使い方": DelayedScaling); CURRENT: from this
- * tensor's own amax ([LP-opt] "実モデルにおける結果の解釈", FP8 CurrentScaling). */
-typedef enum { TE_SCALE_DELAYED = 0, TE_SCALE_CURRENT = 1 } te_scaling;
+ * tensor's own amax ([LP-opt] "実モデルにおける結果の解釈", FP8 CurrentScaling).
+ * CURRENT_FROM_AMAX: current scaling whose amax is already in *amax, produced by
+ * the launch that wrote the tensor (te_fp8_gemm_amax), so the cast reads the
+ * tensor once instead of twice. */
+typedef enum { TE_SCALE_DELAYED = 0, TE_SCALE_CURRENT = 1, TE_SCALE_CURRENT_FROM_AMAX = 2 } te_scaling;
 
 /* [FP8-intro] "Transformer Engine 統合済みライブラリの利用" (NeMo keys):
  * fp8_amax_compute_algo is 'max' or 'most_recent'. */
@@ -99,23 +106,31 @@ typedef enum { TE_GRAN_TENSOR = 0, TE_GRAN_MX_BLOCK32 = 1, TE_GRAN_MX_BLOCK32_PA
  *                *scale = fl32(fp8_max / amax) * 2^-margin (overflow -> FLT_MAX;
  *                amax 0 or non-finite -> 1.0), and casts with it (two passes
  *                over x: the amax must exist before the first element is cast).
- *   margin     >= 0; scale multiplier 2^-margin (CURRENT only; DELAYED applies
- *              its margin in te_scale_update).
- *   scale      [1] fp32.  DELAYED: read.  CURRENT: written.
+ *              TE_SCALE_CURRENT_FROM_AMAX: as TE_SCALE_CURRENT with *amax read
+ *                instead of computed (one pass over x).
+ *   margin     >= 0; scale multiplier 2^-margin (CURRENT modes only; DELAYED
+ *              applies its margin in te_scale_update).
+ *   scale      [1] fp32.  DELAYED: read.  CURRENT modes: written.
  *   scale_inv  [1] fp32, written = fl32(1 / scale used).
  *   amax       [1] fp32, written = max_i |x_i| (overwritten, not accumulated;
- *              point it at slot 0 of the tensor's amax history for DELAYED).
+ *              point it at slot 0 of the tensor's amax history for DELAYED);
+ *              read-only for TE_SCALE_CURRENT_FROM_AMAX.
  *              A NaN input makes amax NaN (the max is taken over magnitude
  *              bit patterns, where NaN ranks above +Inf).
  *   out        [rows, cols] uint8 codes, out_i = satRNE(fl32(x_i * scale)).
  *              May be NULL: then only amax (and, for CURRENT, scale/scale_inv)
  *              is produced.
+ *   amax_workspace  the amax workspace (see the conventions above); may be NULL
+ *              for TE_SCALE_CURRENT_FROM_AMAX, which reduces nothing.
  * Any rows, cols >= 0 (0 elements: amax = 0 and, for CURRENT, scale = 1).
  */
 te_status te_amax_cast(const void* x, int x_dtype, int64_t rows, int64_t cols,
                        int out_dtype, int mode, int margin,
                        float* scale, float* scale_inv, float* amax,
-                       uint8_t* out, void* stream);
+                       uint8_t* out, void* amax_workspace, void* stream);
+
+/* Bytes of the amax workspace (8448; see the conventions above).  Host only. */
+int64_t te_amax_workspace_bytes(void);
 
 /*
  * te_cast_transpose -- te_amax_cast that also (or only) writes the byte transpose.
@@ -125,7 +140,7 @@ te_status te_amax_cast(const void* x, int x_dtype, int64_t rows, int64_t cols,
  * ([LP-opt] "autocast モードの使用と事前量子化の比較": Fprop, Dgrad and Wgrad are
  * separate GEMMs).
  *
- * Arguments as te_amax_cast, plus
+ * Arguments as te_amax_cast (amax_workspace included), plus
  *   out_row  [rows, cols] uint8 or NULL.
  *   out_col  [cols, rows] uint8 or NULL; out_col[c, r] == out_row[r, c] byte for byte.
  * At least one of out_row / out_col must be non-NULL (unless rows * cols == 0).
@@ -133,7 +148,7 @@ te_status te_amax_cast(const void* x, int x_dtype, int64_t rows, int64_t cols,
 te_status te_cast_transpose(const void* x, int x_dtype, int64_t rows, int64_t cols,
                             int out_dtype, int mode, int margin,
                             float* scale, float* scale_inv, float* amax,
-                            uint8_t* out_row, uint8_t* out_col, void* stream);
+                            uint8_t* out_row, uint8_t* out_col, void* amax_workspace, void* stream);
 
 /*
  * te_cast_transpose_dbias -- te_cast_transpose of an output gradient dY that also
@@ -149,8 +164,11 @@ te_status te_cast_transpose(const void* x, int x_dtype, int64_t rows, int64_t co
  *              order), so the result is reproducible run to run.  NULL only if
  *              cols == 0.
  *   workspace  device scratch of at least te_cast_transpose_dbias_workspace_bytes(
- *              rows, cols) bytes (per-tile partial sums), 4-byte aligned, owned by
- *              the caller; contents on entry are ignored.  NULL if that size is 0.
+ *              rows, cols) bytes, 16-byte aligned, owned by the caller: the first
+ *              te_amax_workspace_bytes() bytes are the amax workspace (all zero
+ *              before the first use, left zero by every call, see the conventions
+ *              above), the rest holds per-tile partial sums (contents on entry
+ *              ignored).
  *   workspace_bytes  its size (TE_ERR_ARG if too small).
  * rows == 0 gives dbias = 0.
  */
@@ -160,8 +178,9 @@ te_status te_cast_transpose_dbias(const void* x, int x_dtype, int64_t rows, int6
                                   uint8_t* out_row, uint8_t* out_col, float* dbias,
                                   void* workspace, int64_t workspace_bytes, void* stream);
 
-/* Workspace bytes te_cast_transpose_dbias needs for [rows, cols]: ceil(rows / 128)
- * * cols * 4 (host only, no GPU call); -1 for negative sizes. */
+/* Workspace bytes te_cast_transpose_dbias needs for [rows, cols]:
+ * te_amax_workspace_bytes() + ceil(rows / 128) * cols * 4 (host only, no GPU call);
+ * -1 for negative sizes. */
 int64_t te_cast_transpose_dbias_workspace_bytes(int64_t rows, int64_t cols);
 
 /*
@@ -189,12 +208,16 @@ int64_t te_cast_transpose_dbias_workspace_bytes(int64_t rows, int64_t cols);
  *              (statistics and amax, then the cast).
  *   out        [rows, cols] uint8 codes.
  *   mu, rsigma [rows] fp32, written (the backward's saved statistics), or NULL.
+ *   amax_workspace  the amax workspace (required).
+ * mode TE_SCALE_CURRENT_FROM_AMAX: TE_ERR_UNSUPPORTED (the amax is of y, which only
+ * this call produces).
  */
 te_status te_layernorm_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols,
                            const void* gamma, const void* beta, int param_dtype, float eps,
                            int out_dtype, int mode, int margin,
                            float* scale, float* scale_inv, float* amax,
-                           uint8_t* out, float* mu, float* rsigma, void* stream);
+                           uint8_t* out, float* mu, float* rsigma, void* amax_workspace,
+                           void* stream);
 
 /*
  * te_scale_update -- delayed-scaling update of n tensors of one FP8 format.
@@ -285,7 +308,12 @@ te_status te_fp8_gemm_accumulate(const void* a, int a_dtype, const void* a_scale
  * conversion are part of the autocast cost).  Block rule (OCP MX v1.0 reading):
  * for 32 consecutive elements, e = floor(log2(max|x|)) - emax_elem (8 for E4M3,
  * 15 for E5M2), clamped to [-127, 127]; scale code = e + 127 (127 for an all-zero
- * block); elements = satRNE(x * 2^-e).
+ * block); elements = satRNE(x * 2^-e).  Special blocks: an infinite max reads as
+ * log2 = +inf, so the code is 254 (the clamp's top), the infinities saturate to
+ * +-max and the finite elements go to 0; a block holding a NaN has a NaN max,
+ * which is not > 0, so it keeps code 127 and its NaN elements stay NaN codes.
+ * (MXFP4 differs on NaN blocks, see te_mxfp4_quantize: E2M1 has no NaN code, so
+ * there the NaN travels in the scale, code 255.)
  *
  *   x          [rows, cols] of x_dtype (TE_F32 or TE_BF16).
  *   elem_dtype TE_E4M3 (or TE_E5M2).

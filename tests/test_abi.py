@@ -122,10 +122,13 @@ def test_gemm_empty_is_ok_without_launch():
     (dict(amax=None), B.TE_ERR_NULL),
     (dict(x=FAKE_MIS), B.TE_ERR_ALIGN),
     (dict(out=FAKE_MIS), B.TE_ERR_ALIGN),
+    (dict(workspace=None), B.TE_ERR_NULL),
+    (dict(workspace=None, mode=B.TE_SCALE_CURRENT), B.TE_ERR_NULL),
+    (dict(workspace=FAKE_MIS), B.TE_ERR_ALIGN),
 ])
 def test_amax_cast_validation(kw, status):
     args = dict(x=FAKE, x_dtype=B.TE_BF16, rows=4, cols=4, out_dtype=B.TE_E4M3, mode=B.TE_SCALE_DELAYED,
-                margin=0, scale=FAKE, scale_inv=FAKE, amax=FAKE, out=FAKE, stream=None)
+                margin=0, scale=FAKE, scale_inv=FAKE, amax=FAKE, out=FAKE, workspace=FAKE, stream=None)
     args.update(kw)
     assert B.lib().te_amax_cast(*args.values()) == status
 
@@ -133,7 +136,23 @@ def test_amax_cast_validation(kw, status):
 @needs_lib
 def test_cast_transpose_needs_an_output():
     assert B.lib().te_cast_transpose(FAKE, B.TE_BF16, 4, 4, B.TE_E4M3, 0, 0, FAKE, FAKE, FAKE,
-                                     None, None, None) == B.TE_ERR_NULL
+                                     None, None, FAKE, None) == B.TE_ERR_NULL
+    # the amax workspace is required for every mode that reduces an amax
+    for mode in (B.TE_SCALE_DELAYED, B.TE_SCALE_CURRENT):
+        assert B.lib().te_cast_transpose(FAKE, B.TE_BF16, 4, 4, B.TE_E4M3, mode, 0, FAKE, FAKE, FAKE,
+                                         FAKE, None, None, None) == B.TE_ERR_NULL
+
+
+@needs_lib
+def test_workspace_sizes():
+    """The amax workspace is the 32 group lines and the top line of the grid-wide
+    reduction (33 x 256 bytes); the dbias workspace is that plus one fp32 partial sum per
+    128-row tile and column."""
+    assert B.te_amax_workspace_bytes() == 33 * 256
+    assert B.te_cast_transpose_dbias_workspace_bytes(128, 16) == 33 * 256 + 16 * 4
+    assert B.te_cast_transpose_dbias_workspace_bytes(129, 16) == 33 * 256 + 2 * 16 * 4
+    assert B.te_cast_transpose_dbias_workspace_bytes(0, 16) == 33 * 256
+    assert B.te_cast_transpose_dbias_workspace_bytes(-1, 16) == -1
 
 
 @needs_lib

@@ -17,7 +17,7 @@ import oracle as O
 from fp8_precision_transformer_amd import binding as B
 from fp8_precision_transformer_amd import synth
 
-from gpu_util import DEV, check_fp8_gemm, empty_f32, host, input_pair
+from gpu_util import DEV, amax_ws, check_fp8_gemm, empty_f32, host, input_pair
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +35,7 @@ def _quantize(x32, fmt):
     row = torch.empty((R, C), dtype=torch.uint8, device=DEV)
     col = torch.empty((C, R), dtype=torch.uint8, device=DEV)
     scale, sinv, am = empty_f32(), empty_f32(), empty_f32()
-    B.te_cast_transpose(xd, fmt, B.TE_SCALE_CURRENT, 0, scale, sinv, am, row, col)
+    B.te_cast_transpose(xd, fmt, B.TE_SCALE_CURRENT, 0, scale, sinv, am, row, col, workspace=amax_ws())
     f = FMTS[fmt]
     s = O.current_scale(O.amax(xh), f)
     ref_row, ref_col = O.cast_transpose(xh, s, f)

@@ -8,13 +8,17 @@ history, scales).  This checks that the library's launches are capture-safe: no
 allocation, no host synchronization and no memset node inside a step.
 """
 
+import numpy as np
 import pytest
 import torch
 
+import oracle as O
+from fp8_precision_transformer_amd import binding as B
+from fp8_precision_transformer_amd import synth
 from fp8_precision_transformer_amd.shapes import BERT_BASE
 from fp8_precision_transformer_amd.steps import LayerStep, LinearForwardStep, capture
 
-from gpu_util import DEV
+from gpu_util import DEV, empty_f32, host, input_pair, new_ws
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +35,7 @@ def _check(step, ref, tag):
 def test_linear_step_graph_replays_match_eager():
     st = torch.cuda.Stream()
     step = LinearForwardStep(st)
-    step.run()                      # first call on the stream: workspace and caches
+    step.run()
     torch.cuda.synchronize()
     step.reset()
     refs = []
@@ -75,3 +79,42 @@ def test_bert_layer_step_graph_replays_match_eager():
             v = step.outputs()[k]
             v.zero_() if v.dtype != torch.float32 else v.fill_(float("nan"))
         torch.cuda.synchronize()
+
+
+def test_graph_captured_on_one_stream_replays_on_another_beside_eager_quantizers():
+    """A layer step captured on stream S (with the step's own amax workspace) is replayed
+    on stream T while eager current-scaling casts, with a workspace of their own, run on
+    S at the same time: every amax of the replayed step and of the eager casts equals the
+    oracle's, bit for bit, on every round."""
+    S, T = torch.cuda.Stream(), torch.cuda.Stream()
+    step = LayerStep(BERT_BASE, S)
+    torch.cuda.synchronize()
+    g = capture(step)
+    big = [input_pair(synth.activations((4096, 4096), 9, 70 + i, 0, 0), "bf16") for i in range(3)]
+    ref_step = {(w.name, k): O.amax(host(step.t[w.name][key]))
+                for w in step.weights for k, key in (("x", "X"), ("w", "W"), ("dy", "DY"))}
+    ws_eager = new_ws()
+    torch.cuda.synchronize()
+    for rnd in range(3):
+        for w in step.weights:
+            for k in ("x", "w", "dy"):
+                step.t[w.name]["sc"][k][2].fill_(-1.0)
+        eager = []
+        outs = [torch.empty((4096, 4096), dtype=torch.uint8, device=DEV) for _ in big]
+        ams = [empty_f32() for _ in big]
+        torch.cuda.synchronize()
+        with torch.cuda.stream(T):
+            g.replay()
+        with torch.cuda.stream(S):
+            for (xd, xh), o, am in zip(big, outs, ams):
+                B.te_cast_transpose(xd, "E4M3", B.TE_SCALE_CURRENT, 0, empty_f32(), empty_f32(), am, None, o,
+                                    workspace=ws_eager, stream=S)
+                eager.append((am, xh))
+        torch.cuda.synchronize()
+        for (wname, k), ref in ref_step.items():
+            got = host(step.t[wname]["sc"][k][2])[0]
+            assert got == ref, (rnd, wname, k, got, ref)
+        for i, (am, xh) in enumerate(eager):
+            assert host(am)[0] == O.amax(xh), (rnd, i)
+        np.testing.assert_array_equal(host(outs[0]), O.scaled_cast(big[0][1], O.current_scale(O.amax(big[0][1]),
+                                                                                                O.E4M3), O.E4M3).T)

@@ -2,9 +2,12 @@
 
 The 768 -> 768 layer of [FP8-intro] "Transformer Engine の使い方" for 20 steps
 of delayed scaling (history 16, max, margin 0, HYBRID): every step's FP8 bytes,
-amax history, scale and scale_inv bit-exact; the bf16 output within 1e-2.
-Also: backward (Dgrad/Wgrad) with current scaling, the MXFP8 recipe, and
-resume of the scaling state from a checkpoint.
+amax history, scale and scale_inv bit-exact; the bf16 output within the
+matrix-core error bound of the oracle's exact product.
+Also: backward (Dgrad/Wgrad) with delayed scaling after the autocast exit's
+update, one scale update per format group, current scaling, the MXFP8 recipe, and
+resume of the scaling state from a checkpoint.  GEMM outputs are checked with
+``check_fp8_gemm`` (the matrix-core error model of ``tests/mfma_model.py``).
 """
 
 import numpy as np
@@ -76,6 +79,76 @@ def test_linear_state_resume_is_bit_identical():
         with torch.no_grad(), fp8_autocast(fp8_recipe=recipe):
             y = lin2(dev_f32(xs[t]))
         assert torch.equal(y, outs[t]), t
+
+
+@pytest.fixture
+def fresh_pools():
+    """Modules registered by earlier tests share the delayed-scaling pools; start empty."""
+    from fp8_precision_transformer_amd import linear as linear_mod
+    linear_mod._pools.clear()
+    yield
+
+
+def test_linear_backward_delayed_scaling_uses_the_forward_scales(fresh_pools):
+    """Delayed scaling, forward inside fp8_autocast and backward after its exit (the exit's
+    scale update rewrites the scaling state before backward runs): Dgrad and Wgrad must
+    dequantize W^T and X^T with the scale_inv their forward casts used, and dY with the
+    gradient group's scale.  Four steps against the oracle's delayed-scaling state machine;
+    the gradient group updates at the first exit after a backward."""
+    recipe = DelayedScaling(fp8_format=Format.HYBRID, amax_history_len=16, amax_compute_algo="max")
+    lin, w, b = _layer(7)
+    lin.keep_fp8_tensors = True
+    M = 256
+    sx = O.DelayedScalingState(O.E4M3, 16, "max", 0)
+    sw = O.DelayedScalingState(O.E4M3, 16, "max", 0)
+    sg = O.DelayedScalingState(O.E5M2, 16, "max", 0)
+    t4, t5 = O.decode_table(O.E4M3), O.decode_table(O.E5M2)
+    for t in range(4):
+        x = synth.activations((M, 768), 7, 0, synth.T_X, t)
+        dy = synth.grads((M, 768), 7, 0, synth.T_DY, t)
+        xd = dev_f32(x).requires_grad_(True)
+        lin.weight.grad = None
+        with fp8_autocast(fp8_recipe=recipe):
+            y = lin(xd)
+        xq, sxi = sx.cast(x)
+        wq, swi = sw.cast(w)
+        sx.update()
+        sw.update()
+        if t > 0:
+            sg.update()  # the exit after a backward updates the gradient group
+        dyb = dev_f32(dy).to(torch.bfloat16)
+        y.backward(dyb)
+        dy_b = host(dyb)
+        dyq, sgi = sg.cast(dy_b)
+        np.testing.assert_array_equal(host(lin.last_fp8["xq"]), xq, err_msg=f"step {t}")
+        st = lin.fp8_state_dict()
+        np.testing.assert_array_equal(host(st["amax_history"])[2], sg.hist, err_msg=f"step {t} dY history")
+        assert host(st["scale"])[2] == sg.scale and host(st["scale_inv"])[2] == sg.scale_inv, t
+        ref_dx = O.gemm_per_tensor(dyq, O.E5M2, sgi, np.ascontiguousarray(wq.T), O.E4M3, swi, out="bf16")
+        check_fp8_gemm(host(xd.grad), ref_dx, t5[dyq], t4[wq.T], np.float64(sgi) * np.float64(swi), "bf16")
+        ref_dw = O.gemm_per_tensor(np.ascontiguousarray(dyq.T), O.E5M2, sgi, np.ascontiguousarray(xq.T), O.E4M3,
+                                   sxi, out="f32")
+        check_fp8_gemm(host(lin.weight.grad), ref_dw, t5[dyq.T], t4[xq.T], np.float64(sgi) * np.float64(sxi), "f32")
+
+
+def test_autocast_exit_updates_each_format_group_once(monkeypatch, fresh_pools):
+    """Three modules under one recipe: the exit issues one te_scale_update for the forward
+    (E4M3) group of all of them, and, after a backward, one for the gradient group."""
+    from fp8_precision_transformer_amd import binding as Bm
+    recipe = DelayedScaling(amax_history_len=16)
+    layers = [_layer(10 + i)[0] for i in range(3)]
+    calls = []
+    real = Bm.te_scale_update
+    monkeypatch.setattr(Bm, "te_scale_update", lambda *a, **k: (calls.append(a[3]), real(*a, **k)))
+    x = dev_f32(synth.activations((64, 768), 8, 0, synth.T_X, 0)).requires_grad_(True)
+    with fp8_autocast(fp8_recipe=recipe):
+        y = layers[2](layers[1](layers[0](x)))
+    assert calls == ["E4M3"], calls
+    y.float().sum().backward()
+    calls.clear()
+    with torch.no_grad(), fp8_autocast(fp8_recipe=recipe):
+        layers[2](layers[1](layers[0](x)))
+    assert calls == ["E4M3", "E5M2"], calls
 
 
 def test_linear_backward_current_scaling():

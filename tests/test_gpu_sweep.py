@@ -17,7 +17,7 @@ import oracle as O
 from fp8_precision_transformer_amd import binding as B
 from fp8_precision_transformer_amd import synth
 
-from gpu_util import DEV, dev_bf16_from_bits, host
+from gpu_util import DEV, amax_ws, dev_bf16_from_bits, host
 
 pytestmark = pytest.mark.gpu
 
@@ -48,9 +48,9 @@ def test_delayed_sweep_24_layers_16_steps_drift():
         for l in range(LAYERS):
             xd = dev_bf16_from_bits(xs[l][0])
             B.te_amax_cast(xd, "E4M3", B.TE_SCALE_DELAYED, 0, scale[2 * l:2 * l + 1], sinv[2 * l:2 * l + 1],
-                           hist[2 * l, 0:1], outs[l])
+                           hist[2 * l, 0:1], outs[l], workspace=amax_ws())
             B.te_amax_cast(wd[l], "E4M3", B.TE_SCALE_DELAYED, 0, scale[2 * l + 1:2 * l + 2],
-                           sinv[2 * l + 1:2 * l + 2], hist[2 * l + 1, 0:1], wouts[l])
+                           sinv[2 * l + 1:2 * l + 2], hist[2 * l + 1, 0:1], wouts[l], workspace=amax_ws())
         got_hist_pre = host(hist)
         for l in range(LAYERS):
             xq, _ = ref[2 * l].cast(xs[l][1])

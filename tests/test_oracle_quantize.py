@@ -213,6 +213,49 @@ def test_mxfp8_zero_block_and_clamp():
     assert ey[0, 0] == 0 and (qy == 0).all()
 
 
+def test_mxfp8_e5m2_closed_form_codes():
+    """E5M2 elements (largest power of two 2^15): block code floor(log2 amax) - 15 + 127,
+    worked by hand for a block of max 1.5 * 2^j: the max scales to 1.5 * 2^15 = 49152,
+    E5M2 exponent field 30, mantissa 10 -> 0x7A; 1.9 * 2^j scales into [57344, 65536) and
+    saturates to 0x7B; 2^(j-30), 2^(j-31), 2^(j-32) scale to 2^-15, 2^-16 (two and one
+    times the smallest subnormal: codes 0x02, 0x01) and 2^-17 (the tie between 0 and
+    2^-16, to even: 0x00)."""
+    for j in (-20, 0, 7, 40):
+        x = np.zeros((2, 32), dtype=np.float32)
+        x[0, 0] = np.float32(1.5 * 2.0 ** j)
+        x[0, 1] = np.float32(-(2.0 ** (j - 30)))
+        x[0, 2] = np.float32(2.0 ** (j - 31))
+        x[0, 3] = np.float32(2.0 ** (j - 32))
+        x[1, 5] = np.float32(-1.9 * 2.0 ** j)
+        x[1, 6] = np.float32(1.0 * 2.0 ** j)
+        q, e = mxfp8_quantize(x, E5M2)
+        assert e[0, 0] == j - 15 + 127 and e[1, 0] == j - 15 + 127
+        assert q[0, 0] == 0x7A and q[0, 1] == 0x82 and q[0, 2] == 0x01 and q[0, 3] == 0x00
+        assert q[1, 5] == 0xFB                 # -1.9 * 2^15 saturates to -57344
+        assert q[1, 6] == 0x78                 # 2^15: exponent field 30, mantissa 0
+        assert (q[0, 4:] == 0).all() and q[1, 0] == 0
+
+
+def test_mxfp8_e5m2_zero_block_and_clamp():
+    x = np.zeros((2, 64), dtype=np.float32)
+    x[1, 32:] = np.float32(2.0 ** 120)
+    q, e = mxfp8_quantize(x, E5M2)
+    assert e[0, 0] == 127 and e[0, 1] == 127 and e[1, 0] == 127   # all-zero blocks
+    assert e[1, 1] == 120 - 15 + 127
+    assert (q[1, 32:] == 0x78).all()   # 2^120 / 2^105 = 2^15
+    assert (q[0] == 0).all()
+    # fp32 subnormals: floor(log2) = -149, e = -164 clamps to -127 (code 0); the
+    # elements scale to 2^-22, below E5M2's smallest subnormal 2^-16: +0
+    y = np.full((1, 32), np.finfo(np.float32).smallest_subnormal, dtype=np.float32)
+    qy, ey = mxfp8_quantize(y, E5M2)
+    assert ey[0, 0] == 0 and (qy == 0).all()
+    # e = -127 exactly (amax 2^-112) keeps the scaled elements in range: 2^-112 * 2^127 = 2^15
+    z = np.zeros((1, 32), dtype=np.float32)
+    z[0, 0] = np.float32(2.0 ** -112)
+    qz, ez = mxfp8_quantize(z, E5M2)
+    assert ez[0, 0] == 0 and qz[0, 0] == 0x78
+
+
 def test_mxfp8_infinite_and_nan_blocks():
     """An infinite block max has log2 = +inf, so the exponent takes the clamp's top, 127
     (code 254): the infinities saturate to the format's largest magnitude and finite
