@@ -58,6 +58,8 @@ _SIGNATURES = {
                          _vp, _vp, _vp, _vp, _vp],
     "te_cast_transpose_dbias": [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                                 _vp],
+    "te_cast_transpose_dbias_noalloc": [_vp, _i32, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                        _vp],
     "te_scale_update": [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp],
     "te_fp8_gemm": [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp, _i32, _vp],
     "te_fp8_gemm_accumulate": [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp, _vp],
@@ -98,6 +100,8 @@ def lib() -> ctypes.CDLL:
             L.te_fp8_gemm_splitk_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
             L.te_amax_workspace_bytes.restype = ctypes.c_int64
             L.te_amax_workspace_bytes.argtypes = []
+            L.te_cast_transpose_dbias_noalloc_max_bytes.restype = ctypes.c_int64
+            L.te_cast_transpose_dbias_noalloc_max_bytes.argtypes = []
             _lib = L
     return _lib
 
@@ -219,6 +223,23 @@ def te_cast_transpose_dbias(x, out_dtype, mode, margin, scale, scale_inv, amax, 
     _check(lib().te_cast_transpose_dbias(_ptr(x), _hp_code(x), rows, cols, _fp8_code(out_dtype), int(mode),
                                          int(margin), _ptr(scale), _ptr(scale_inv), _ptr(amax), _ptr(out_row),
                                          _ptr(out_col), _ptr(dbias), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def te_cast_transpose_dbias_noalloc(x, out_dtype, mode, margin, scale, scale_inv, amax, dbias, out_row=None,
+                                    out_col=None, stream=None):
+    """te_cast_transpose_dbias with the library's static scratch instead of a workspace
+    (allocates nothing; calls that overlap on one GPU race)."""
+    for n, t in (("x", x), ("scale", scale), ("scale_inv", scale_inv), ("amax", amax),
+                 ("out_row", out_row), ("out_col", out_col), ("dbias", dbias)):
+        _need(t, n)
+    rows, cols = _2d(x)
+    _check(lib().te_cast_transpose_dbias_noalloc(_ptr(x), _hp_code(x), rows, cols, _fp8_code(out_dtype), int(mode),
+                                                 int(margin), _ptr(scale), _ptr(scale_inv), _ptr(amax),
+                                                 _ptr(out_row), _ptr(out_col), _ptr(dbias), _stream(stream)))
+
+
+def te_cast_transpose_dbias_noalloc_max_bytes() -> int:
+    return int(lib().te_cast_transpose_dbias_noalloc_max_bytes())
 
 
 def te_layernorm_fp8(x, gamma, beta, eps, out_dtype, mode, margin, scale, scale_inv, amax, out, mu=None,

@@ -186,6 +186,37 @@ te_status te_cast_transpose_dbias(const void* x, int x_dtype, int64_t rows, int6
                     "te_cast_transpose_dbias launch");
 }
 
+int64_t te_cast_transpose_dbias_noalloc_max_bytes(void) { return te::kStaticScratchBytes; }
+
+te_status te_cast_transpose_dbias_noalloc(const void* x, int x_dtype, int64_t rows, int64_t cols, int out_dtype,
+                                          int mode, int margin, float* scale, float* scale_inv, float* amax,
+                                          uint8_t* out_row, uint8_t* out_col, float* dbias, void* stream) {
+  te_status st = check_cast_common(x, x_dtype, rows, cols, out_dtype, mode, margin, scale, scale_inv, amax);
+  if (st != TE_OK) return st;
+  if (rows * cols > 0 && !out_row && !out_col) return fail(TE_ERR_NULL, "out_row and out_col are both NULL");
+  if ((out_row && !aligned16(out_row)) || (out_col && !aligned16(out_col)))
+    return fail(TE_ERR_ALIGN, "outputs must be 16-byte aligned");
+  if ((rows + 127) / 128 > 65535) return fail(TE_ERR_SHAPE, "rows too large for the tile grid");
+  if (cols > 0 && !dbias) return fail(TE_ERR_NULL, "dbias is NULL");
+  const int64_t need = te_cast_transpose_dbias_workspace_bytes(rows, cols);
+  if (need > te::kStaticScratchBytes)
+    return fail(TE_ERR_SHAPE,
+                "te_cast_transpose_dbias_noalloc: [%lld, %lld] needs %lld bytes of scratch, above the static "
+                "maximum of %lld (use te_cast_transpose_dbias with a workspace)",
+                (long long)rows, (long long)cols, (long long)need, (long long)te::kStaticScratchBytes);
+  if ((st = check_device()) != TE_OK) return st;
+  void* ws = nullptr;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = hip_status(te::static_scratch(&ws, s), "te_cast_transpose_dbias_noalloc scratch")) != TE_OK) return st;
+  log_dispatch("te_cast_transpose_dbias_noalloc", "tile128x128_colsum_static_scratch",
+               out_dtype == TE_E5M2 ? "E5M2" : "E4M3");
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  return hip_status(te::launch_cast_transpose(x, x_dtype, rows, cols, out_dtype == TE_E5M2, mode, margin, scale,
+                                              scale_inv, amax, out_row, out_col, dbias,
+                                              reinterpret_cast<float*>(w + kAmaxWsBytes), w, s),
+                    "te_cast_transpose_dbias_noalloc launch");
+}
+
 te_status te_layernorm_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, const void* gamma,
                            const void* beta, int param_dtype, float eps, int out_dtype, int mode, int margin,
                            float* scale, float* scale_inv, float* amax, uint8_t* out, float* mu, float* rsigma,

@@ -24,6 +24,12 @@ hipError_t launch_cast_transpose(const void* x, int x_dtype, int64_t rows, int64
                                  uint8_t* out_col, float* dbias, float* dbias_part, void* ws,
                                  hipStream_t s);
 
+// Size of the static scratch of te_cast_transpose_dbias_noalloc (quant.hip), and its
+// device address on the current device (first call on a device: hipGetSymbolAddress and
+// a clear of the amax counters on stream s).
+constexpr int64_t kStaticScratchBytes = int64_t{16} << 20;
+hipError_t static_scratch(void** ptr, hipStream_t s);
+
 hipError_t launch_layernorm_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, const void* gamma,
                                 const void* beta, int param_dtype, float eps, int out_e5m2, int current,
                                 int margin, float* scale, float* scale_inv, float* amax, uint8_t* out,

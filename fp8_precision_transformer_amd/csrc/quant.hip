@@ -12,6 +12,7 @@
 // once per output layout.  Loads and stores are 16 bytes per lane.
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -1349,6 +1350,47 @@ hipError_t layernorm_fmt(const T* x, int64_t R, int64_t C, const P* g, const P* 
 }
 
 }  // namespace
+
+// ----------------------------------------------------------------------------
+// Static scratch for te_cast_transpose_dbias_noalloc (callers that cannot allocate):
+// the amax counters (the first kAmaxScratch bytes) and the per-tile partial sums of the
+// bias gradient.  Each GPU the library runs on holds its own copy until the process
+// ends.  Host code never uses the array's name as an address: the device address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+// ----------------------------------------------------------------------------
+constexpr int64_t kAmaxScratch = sizeof(AmaxWork);
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+__global__ void k_clear_words(uint32_t* p, int n) {
+  const int i = static_cast<int>(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t static_scratch(void** ptr, hipStream_t s) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* dev_ptr[kMaxDev] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    // the counters start at zero (static storage is zero at load; cleared once more here
+    // by a kernel, which a stream capture records like any other launch)
+    constexpr int nw = static_cast<int>(kAmaxScratch / 4);
+    hipLaunchKernelGGL(k_clear_words, dim3((nw + 255) / 256), dim3(256), 0, s, static_cast<uint32_t*>(p), nw);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dev_ptr[dev] = p;
+  }
+  *ptr = dev_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_amax_cast(const void* x, int x_dtype, int64_t n, int out_e5m2, int mode, int margin, float* scale,
                             float* scale_inv, float* amax, uint8_t* out, void* ws, hipStream_t s) {

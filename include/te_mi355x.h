@@ -184,6 +184,30 @@ te_status te_cast_transpose_dbias(const void* x, int x_dtype, int64_t rows, int6
 int64_t te_cast_transpose_dbias_workspace_bytes(int64_t rows, int64_t cols);
 
 /*
+ * te_cast_transpose_dbias_noalloc -- te_cast_transpose_dbias for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments and results as te_cast_transpose_dbias, but
+ * no workspace argument: the amax counters and the per-tile partial sums live in a
+ * static scratch array of the library (te_cast_transpose_dbias_noalloc_max_bytes(),
+ * 16 MiB), one copy per GPU, held until the process ends.  The call allocates nothing.
+ *   - Shapes whose te_cast_transpose_dbias_workspace_bytes(rows, cols) exceeds that
+ *     maximum are rejected with TE_ERR_SHAPE (e.g. 15872 x 16384 needs 8.1 MB and fits;
+ *     cols = 16384 fits up to 32640 rows).
+ *   - Every call on a GPU shares that GPU's scratch: calls that may overlap in time on
+ *     one GPU (different streams, a replayed graph beside eager calls) race and must be
+ *     ordered by the caller.  Each completed call leaves the amax counters at zero; the
+ *     first call on a device also enqueues a clear of them on its stream.
+ */
+te_status te_cast_transpose_dbias_noalloc(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                                          int out_dtype, int mode, int margin,
+                                          float* scale, float* scale_inv, float* amax,
+                                          uint8_t* out_row, uint8_t* out_col, float* dbias,
+                                          void* stream);
+
+/* Bytes of the static scratch of te_cast_transpose_dbias_noalloc (host only). */
+int64_t te_cast_transpose_dbias_noalloc_max_bytes(void);
+
+/*
  * te_layernorm_fp8 -- LayerNorm over the last axis, its output written directly as
  * FP8 codes with per-tensor scaling.
  *

@@ -183,3 +183,16 @@ def test_mxfp8_validation(kw, status):
                 scale_row=FAKE, out_col=FAKE, scale_col=FAKE, stream=None)
     args.update(kw)
     assert B.lib().te_mxfp8_quantize(*args.values()) == status
+
+
+@needs_lib
+def test_noalloc_dbias_rejects_shapes_above_its_scratch_before_any_launch():
+    """Validation on the host: a shape whose partial sums exceed the static scratch is
+    TE_ERR_SHAPE before any device call."""
+    assert B.te_cast_transpose_dbias_noalloc_max_bytes() == 16 << 20
+    st = B.lib().te_cast_transpose_dbias_noalloc(FAKE, B.TE_BF16, 40000, 16384, B.TE_E5M2, B.TE_SCALE_CURRENT, 0,
+                                                 FAKE, FAKE, FAKE, None, FAKE, FAKE, None)
+    assert st == B.TE_ERR_SHAPE and b"static maximum" in B.lib().te_get_last_error()
+    st = B.lib().te_cast_transpose_dbias_noalloc(FAKE, B.TE_BF16, 64, 64, B.TE_E5M2, B.TE_SCALE_CURRENT, 0,
+                                                 FAKE, FAKE, FAKE, None, FAKE, None, None)
+    assert st == B.TE_ERR_NULL  # dbias required
