@@ -37,13 +37,13 @@ from .quantize import (
     mx_scales_from_panel,
     e8m0_to_float,
 )
-from .gemm import gemm_per_tensor, gemm_mx, gemm_bf16, bf16_round_bits, bf16_bits_to_f32, rel_err, bias_grad
+from .gemm import gemm_per_tensor, gemm_with_amax, gemm_mx, gemm_bf16, bf16_round_bits, bf16_bits_to_f32, rel_err, bias_grad
 from .layernorm import layernorm
 
 __all__ = [
     "E4M3", "E5M2", "FP8Format", "decode", "decode_table", "encode", "fp8_format",
     "amax", "current_scale", "scale_inverse", "scaled_cast", "cast_transpose",
     "DelayedScalingState", "delayed_update", "mxfp8_quantize", "e8m0_to_float", "mx_scales_panel", "mx_scales_from_panel",
-    "gemm_per_tensor", "gemm_mx", "gemm_bf16", "bf16_round_bits", "bf16_bits_to_f32",
+    "gemm_per_tensor", "gemm_with_amax", "gemm_mx", "gemm_bf16", "bf16_round_bits", "bf16_bits_to_f32",
     "rel_err", "bias_grad", "layernorm",
 ]

@@ -24,6 +24,13 @@ Readings taken where the pages are silent:
   * bias gradient: the backward of y = x W^T + b gives db[c] = sum over rows
     of dy[r, c]; the oracle returns that sum in float64 (exact to float64
     rounding), and a GPU sum in fp32 is held to the fp32 summation bound.
+  * amax of a GEMM output ([LP-opt] "実モデルにおける結果の解釈": the per-tensor
+    amax costs an extra memory pass; [FP8-intro] "FP8 Training について": every
+    tensor that is cast to FP8 carries its own scale, the next layer's input
+    included): the amax of the tensor as stored (bf16 or fp32 output), or, when
+    the output itself is written as FP8 with a given scale (delayed scaling of the
+    next layer's input), of the fp32 values before that cast, which is the value a
+    separate cast of the fp32 output would record.
 
 Pins (tests/test_oracle_gemm.py): brute-force triple loop on tiny shapes,
 integer-valued operands (exact in any order), identity operand, bias-only,
@@ -37,7 +44,7 @@ from __future__ import annotations
 import numpy as np
 
 from .formats import FP8Format, decode_table
-from .quantize import e8m0_to_float
+from .quantize import amax, e8m0_to_float, scaled_cast
 
 
 def bf16_round_bits(x) -> np.ndarray:
@@ -82,6 +89,23 @@ def gemm_per_tensor(a_codes, a_fmt: FP8Format, a_scale_inv, b_codes, b_fmt: FP8F
         d = (acc * np.float32(a_scale_inv)).astype(np.float32)
         d = (d * np.float32(b_scale_inv)).astype(np.float32)
     return _epilogue(d, bias, out)
+
+
+def gemm_with_amax(a_codes, a_fmt: FP8Format, a_scale_inv, b_codes, b_fmt: FP8Format, b_scale_inv,
+                   bias=None, out: str = "bf16", out_scale=None, out_fmt: FP8Format = None):
+    """The per-tensor GEMM of ``gemm_per_tensor`` together with the amax of its output.
+
+    out "bf16" / "f32": returns (d, amax) with amax = max |d| over the stored values.
+    out "fp8": the fp32 result d32 (bias added) is cast with ``out_scale`` to ``out_fmt``
+    exactly as ``scaled_cast`` casts any tensor; returns (codes, amax = max |d32|).
+    """
+    if out in ("bf16", "f32"):
+        d = gemm_per_tensor(a_codes, a_fmt, a_scale_inv, b_codes, b_fmt, b_scale_inv, bias=bias, out=out)
+        return d, amax(d)
+    if out != "fp8":
+        raise ValueError(out)
+    d32 = gemm_per_tensor(a_codes, a_fmt, a_scale_inv, b_codes, b_fmt, b_scale_inv, bias=bias, out="f32")
+    return scaled_cast(d32, out_scale, out_fmt), amax(d32)
 
 
 def gemm_mx(a_codes, a_e8m0, a_fmt: FP8Format, b_codes, b_e8m0, b_fmt: FP8Format,

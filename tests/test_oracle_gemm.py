@@ -13,6 +13,8 @@ import numpy as np
 import pytest
 import torch
 
+import oracle as O
+
 from oracle import (E4M3, E5M2, bias_grad, bf16_bits_to_f32, bf16_round_bits, decode, decode_table,
                     encode, gemm_bf16, gemm_mx, gemm_per_tensor, rel_err, e8m0_to_float)
 
@@ -177,3 +179,46 @@ def test_bias_grad_pins():
     loss = lambda bb: float(np.sum((x @ w.T + bb) * g))  # noqa: E731
     fd = np.array([loss(b + np.eye(3)[c]) - loss(b) for c in range(3)])
     np.testing.assert_allclose(bias_grad(g), fd, rtol=1e-12, atol=1e-12)
+
+
+def test_gemm_with_amax_brute_force_and_bf16_relation():
+    """amax of the stored output, by a Python loop over the oracle's own output and, for
+    bf16, the closed form bf16(max |d32|): rounding to bf16 is monotone in |d|, so the
+    largest stored magnitude is the rounding of the largest fp32 one."""
+    rng = np.random.default_rng(11)
+    m, n, k = 9, 16, 32
+    a = rng.integers(0, 256, (m, k)).astype(np.uint8)
+    b = rng.integers(0, 256, (n, k)).astype(np.uint8)
+    a[a == 0x7F] = 0x7E
+    a[a == 0xFF] = 0xFE
+    b[(b & 0x7F) == 0x7F] = 0x38
+    bias = rng.standard_normal(n).astype(np.float32)
+    for out in ("bf16", "f32"):
+        d, am = O.gemm_with_amax(a, O.E4M3, np.float32(0.5), b, O.E4M3, np.float32(0.25), bias=bias, out=out)
+        ref = max(abs(float(v)) for v in d.reshape(-1))
+        assert am == np.float32(ref)
+    d32, am32 = O.gemm_with_amax(a, O.E4M3, np.float32(0.5), b, O.E4M3, np.float32(0.25), bias=bias, out="f32")
+    _, am16 = O.gemm_with_amax(a, O.E4M3, np.float32(0.5), b, O.E4M3, np.float32(0.25), bias=bias, out="bf16")
+    assert am16 == O.bf16_bits_to_f32(O.bf16_round_bits(np.array([am32], np.float32)))[0]
+
+
+def test_gemm_with_amax_fp8_output_worked_by_hand():
+    """FP8 output: the fp32 result cast with the given scale.  Integer operands 1 (0x38)
+    and 2 (0x40): a row of k = 3 ones times a row of twos gives 6; scale 8 -> 48 =
+    1.5 * 2^5, E4M3 field 5 + 7 = 12, mantissa 100 -> 0x64.  A result of 1000 at scale 1
+    saturates to 0x7E while the amax keeps 1000 (the amax is of the values before the
+    cast, as a separate cast of the fp32 output would record it)."""
+    a = np.full((1, 16), 0x00, np.uint8)
+    a[0, :3] = 0x38
+    b = np.full((1, 16), 0x40, np.uint8)
+    q, am = O.gemm_with_amax(a, O.E4M3, np.float32(1), b, O.E4M3, np.float32(1), out="fp8",
+                             out_scale=np.float32(8), out_fmt=O.E4M3)
+    assert q[0, 0] == 0x64 and am == 6.0
+    bias = np.array([994.0], np.float32)
+    q, am = O.gemm_with_amax(a, O.E4M3, np.float32(1), b, O.E4M3, np.float32(1), bias=bias, out="fp8",
+                             out_scale=np.float32(1), out_fmt=O.E4M3)
+    assert q[0, 0] == 0x7E and am == 1000.0
+    # E5M2 output of -6 at scale 1/2: -3 = -1.5 * 2^1, field 1 + 15 = 16, mantissa 10 -> 0xC2
+    q, am = O.gemm_with_amax(a, O.E4M3, np.float32(-1), b, O.E4M3, np.float32(1), out="fp8",
+                             out_scale=np.float32(0.5), out_fmt=O.E5M2)
+    assert q[0, 0] == 0xC2 and am == 6.0
