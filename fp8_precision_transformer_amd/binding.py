@@ -62,6 +62,8 @@ _SIGNATURES = {
                                         _vp],
     "te_scale_update": [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp],
     "te_fp8_gemm": [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp, _i32, _vp],
+    "te_fp8_gemm_amax": [_vp, _i32, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _i32, _vp, _vp, _vp,
+                         _vp, _vp],
     "te_fp8_gemm_accumulate": [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp, _vp],
     "te_mxfp8_quantize": [_vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp],
     "te_mxfp4_quantize": [_vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
@@ -293,6 +295,44 @@ def te_fp8_gemm(a, a_dtype, a_scale, b, b_dtype, b_scale, d, bias=None, gran=TE_
         return
     _check(lib().te_fp8_gemm(_ptr(a), ad, _ptr(a_scale), _ptr(b), bd, _ptr(b_scale), int(gran), m, n, k,
                              _ptr(bias), bias_code, _ptr(d), dd, _stream(stream)))
+
+
+def te_fp8_gemm_amax(a, a_dtype, a_scale, b, b_dtype, b_scale, d, amax, workspace, bias=None, d_scale=None,
+                     d_scale_inv=None, stream=None):
+    """te_fp8_gemm (per-tensor FP8 or BF16) that also writes amax = max |D| of the stored bf16
+    or fp32 output d; workspace: an amax workspace.  FP8 output: te_fp8_gemm_amax_fp8."""
+    for n_, t in (("a", a), ("b", b), ("d", d), ("bias", bias), ("a_scale", a_scale), ("b_scale", b_scale),
+                  ("amax", amax), ("workspace", workspace)):
+        _need(t, n_)
+    ad = TE_BF16 if str(a_dtype).upper() == "BF16" else _fp8_code(a_dtype)
+    bd = TE_BF16 if str(b_dtype).upper() == "BF16" else _fp8_code(b_dtype)
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k or tuple(d.shape) != (m, n):
+        raise ValueError(f"shape mismatch: a {tuple(a.shape)} b {tuple(b.shape)} d {tuple(d.shape)}")
+    bias_code = _hp_code(bias) if bias is not None else TE_F32
+    _check(lib().te_fp8_gemm_amax(_ptr(a), ad, _ptr(a_scale), _ptr(b), bd, _ptr(b_scale), m, n, k, _ptr(bias),
+                                  bias_code, _ptr(d), _hp_code(d), None, None, _ptr(amax), _ptr(workspace),
+                                  _stream(stream)))
+
+
+def te_fp8_gemm_amax_fp8(a, a_dtype, a_scale, b, b_dtype, b_scale, d, d_dtype, d_scale, d_scale_inv, amax,
+                         workspace, bias=None, stream=None):
+    """te_fp8_gemm_amax writing D [m, n] as FP8 codes (uint8) of d_dtype ("E4M3"/"E5M2")
+    with the scale d_scale; d_scale_inv written; amax of the fp32 results before the cast."""
+    for n_, t in (("a", a), ("b", b), ("d", d), ("bias", bias), ("a_scale", a_scale), ("b_scale", b_scale),
+                  ("d_scale", d_scale), ("d_scale_inv", d_scale_inv), ("amax", amax), ("workspace", workspace)):
+        _need(t, n_)
+    ad = TE_BF16 if str(a_dtype).upper() == "BF16" else _fp8_code(a_dtype)
+    bd = TE_BF16 if str(b_dtype).upper() == "BF16" else _fp8_code(b_dtype)
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k or tuple(d.shape) != (m, n) or d.dtype != torch.uint8:
+        raise ValueError(f"shape mismatch: a {tuple(a.shape)} b {tuple(b.shape)} d {tuple(d.shape)} {d.dtype}")
+    bias_code = _hp_code(bias) if bias is not None else TE_F32
+    _check(lib().te_fp8_gemm_amax(_ptr(a), ad, _ptr(a_scale), _ptr(b), bd, _ptr(b_scale), m, n, k, _ptr(bias),
+                                  bias_code, _ptr(d), _fp8_code(d_dtype), _ptr(d_scale), _ptr(d_scale_inv),
+                                  _ptr(amax), _ptr(workspace), _stream(stream)))
 
 
 def te_fp8_gemm_splitk_workspace_bytes(m, n, splits) -> int:

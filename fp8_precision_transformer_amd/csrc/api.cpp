@@ -259,10 +259,18 @@ te_status te_scale_update(float* amax_history, float* scale, float* scale_inv, i
                     "te_scale_update launch");
 }
 
+// The fused epilogue of te_fp8_gemm_amax: amax of the output, FP8 output with a scale.
+struct FusedOut {
+  float* amax;
+  void* amax_ws;
+  const float* d_scale;
+  float* d_scale_inv;
+};
+
 static te_status gemm_impl(const void* a, int a_dtype, const void* a_scale, const void* b, int b_dtype,
                            const void* b_scale, int gran, int64_t m, int64_t n, int64_t k, const void* bias,
                            int bias_dtype, void* d, int d_dtype, int accumulate, void* stream, int splits = 1,
-                           void* workspace = nullptr, int64_t workspace_bytes = 0) {
+                           void* workspace = nullptr, int64_t workspace_bytes = 0, const FusedOut* fz = nullptr) {
   if (m < 0 || n < 0 || k < 0) return fail(TE_ERR_SHAPE, "negative GEMM shape");
   if (n % 16 != 0 || k % 16 != 0)
     return fail(TE_ERR_SHAPE, "n and k must be multiples of 16 (got n=%lld k=%lld)", (long long)n, (long long)k);
@@ -280,12 +288,35 @@ static te_status gemm_impl(const void* a, int a_dtype, const void* a_scale, cons
   if (fp4 && gran != TE_GRAN_MX_BLOCK32) return fail(TE_ERR_UNSUPPORTED, "E2M1 operands need MX block scales");
   if (fp4 && k % 256 != 0) return fail(TE_ERR_SHAPE, "MXFP4 GEMM needs k %% 256 == 0 (got k=%lld)", (long long)k);
   if (gran == TE_GRAN_MX_BLOCK32 && k % 32 != 0) return fail(TE_ERR_SHAPE, "MX GEMM needs k %% 32 == 0");
-  if (d_dtype != TE_BF16 && d_dtype != TE_F32) return fail(TE_ERR_DTYPE, "d_dtype must be TE_BF16 or TE_F32");
+  const bool d_fp8 = fz != nullptr && is_fp8(d_dtype);
+  if (d_dtype != TE_BF16 && d_dtype != TE_F32 && !d_fp8)
+    return fail(TE_ERR_DTYPE, fz ? "d_dtype must be TE_BF16, TE_F32, TE_E4M3 or TE_E5M2"
+                                 : "d_dtype must be TE_BF16 or TE_F32");
+  if (fz) {
+    if (gran != TE_GRAN_TENSOR) return fail(TE_ERR_UNSUPPORTED, "te_fp8_gemm_amax takes per-tensor FP8 or BF16 operands");
+    if (!fz->amax) return fail(TE_ERR_NULL, "amax is required");
+    if (d_fp8 && (!fz->d_scale || !fz->d_scale_inv))
+      return fail(TE_ERR_NULL, "an FP8 output needs d_scale and d_scale_inv");
+    if (!fz->amax_ws) return fail(TE_ERR_NULL, "amax_workspace is NULL (te_amax_workspace_bytes() bytes, zeroed)");
+    if (!aligned16(fz->amax_ws)) return fail(TE_ERR_ALIGN, "amax_workspace is not 16-byte aligned");
+  }
   if (bias && bias_dtype != TE_BF16 && bias_dtype != TE_F32) return fail(TE_ERR_DTYPE, "bias_dtype must be TE_BF16 or TE_F32");
   if (m >= (int64_t(1) << 31) || n >= (int64_t(1) << 31)) return fail(TE_ERR_SHAPE, "m and n must be < 2^31");
   const int64_t kb = fp4 ? k / 2 : k * (bf16 ? 2 : 1);
   if (kb * 256 >= (int64_t(1) << 31)) return fail(TE_ERR_SHAPE, "k too large (256 rows of k must fit 2 GiB)");
   if (m == 0 || n == 0) {
+    if (fz) {  // an empty output still reports amax = 0 (and the FP8 output's scale_inv)
+      te_status st0 = check_device();
+      if (st0 != TE_OK) return st0;
+      te::GemmArgs g0;
+      g0.m = m;
+      g0.n = n;
+      g0.amax = fz->amax;
+      g0.d_scale = fz->d_scale;
+      g0.d_scale_inv = fz->d_scale_inv;
+      g0.d_fp8 = d_fp8 ? (d_dtype == TE_E5M2 ? 2 : 1) : 0;
+      return hip_status(te::launch_gemm(g0, static_cast<hipStream_t>(stream)), "te_fp8_gemm_amax launch");
+    }
     g_err[0] = '\0';
     return TE_OK;
   }
@@ -314,6 +345,14 @@ static te_status gemm_impl(const void* a, int a_dtype, const void* a_scale, cons
   g.bias_bf16 = bias_dtype == TE_BF16;
   g.d_bf16 = d_dtype == TE_BF16;
   g.accumulate = accumulate;
+  if (fz) {
+    g.amax = fz->amax;
+    g.amax_ws = fz->amax_ws;
+    g.d_scale = fz->d_scale;
+    g.d_scale_inv = fz->d_scale_inv;
+    g.d_fp8 = d_fp8 ? (d_dtype == TE_E5M2 ? 2 : 1) : 0;
+    g.d_bf16 = d_dtype == TE_BF16;
+  }
   if (splits > 1) {
     // split-K: per-tensor FP8 or BF16, at most one split per 128-byte k stage, and an
     // fp32 workspace of splits * m * n floats
@@ -344,6 +383,15 @@ te_status te_fp8_gemm(const void* a, int a_dtype, const void* a_scale, const voi
                       int bias_dtype, void* d, int d_dtype, void* stream) {
   return gemm_impl(a, a_dtype, a_scale, b, b_dtype, b_scale, gran, m, n, k, bias, bias_dtype, d, d_dtype, 0,
                    stream);
+}
+
+te_status te_fp8_gemm_amax(const void* a, int a_dtype, const void* a_scale, const void* b, int b_dtype,
+                           const void* b_scale, int64_t m, int64_t n, int64_t k, const void* bias, int bias_dtype,
+                           void* d, int d_dtype, const float* d_scale, float* d_scale_inv, float* amax,
+                           void* amax_workspace, void* stream) {
+  const FusedOut fz{amax, amax_workspace, d_scale, d_scale_inv};
+  return gemm_impl(a, a_dtype, a_scale, b, b_dtype, b_scale, TE_GRAN_TENSOR, m, n, k, bias, bias_dtype, d, d_dtype, 0,
+                   stream, 1, nullptr, 0, &fz);
 }
 
 int64_t te_fp8_gemm_splitk_workspace_bytes(int64_t m, int64_t n, int splits) {

@@ -31,6 +31,7 @@
 #include <type_traits>
 
 #include "device_common.hpp"
+#include "grid_amax.hpp"
 #include "internal.hpp"
 
 namespace te {
@@ -38,6 +39,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
@@ -73,6 +75,12 @@ struct Params {
   int splits;        // k splits (split-K); 1 = the whole k per tile
   int partial;       // 1: write raw fp32 sums of this split to d + split * M * N (no scale, bias)
   float* partial_ws; // split-K: [splits, M, N] fp32 workspace
+  // fused epilogue (k_gemm4<..., FUSED>): amax of the output and optional FP8 output
+  float* amax;             // [1] written: max |D| (bf16 / fp32: as stored; FP8: before the cast)
+  void* amax_ws;           // the caller's grid-amax workspace (AmaxWork)
+  const float* d_scale;    // FP8 output: the scale of the cast
+  float* d_scale_inv;      // FP8 output: written 1 / d_scale by block 0
+  int d_fp8;               // 0: bf16 / fp32 output; 1: E4M3; 2: E5M2
 };
 
 template <int V>
@@ -378,7 +386,9 @@ __device__ __forceinline__ int f8(int row) { return (row & 7) ^ ((row >> 3) & 3)
 // ============================================================================
 constexpr int NT8 = 512;
 
-template <int KIND, int AF, int BF, bool PANEL = false>
+// FUSED: the epilogue also reduces max |D| over the grid into *p.amax (the caller's
+// workspace holds the counters) and can write D as FP8 codes with the scale *p.d_scale.
+template <int KIND, int AF, int BF, bool PANEL = false, bool FUSED = false>
 __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
   constexpr bool MX4 = KIND == KIND_MX4;
   constexpr bool MX = KIND == KIND_MX || MX4;
@@ -881,6 +891,16 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
   constexpr int kEpRegion = 64 * kEpPitch;  // 16 KB per wave
   static_assert(8 * kEpRegion <= 2 * kPB, "epilogue staging must fit in the stage slots");
   float* ep = reinterpret_cast<float*>(smem + wave * kEpRegion);
+  // FUSED: running max of |D| over this lane's stored outputs, as magnitude bits (NaN,
+  // whose bits are largest, wins); FP8 output scale
+  uint32_t mbits = 0u;
+  float s_out = 1.0f;
+  if constexpr (FUSED) {
+    if (p.d_fp8) {
+      s_out = *p.d_scale;
+      if (blockIdx.x == 0 && tid == 0) *p.d_scale_inv = 1.0f / s_out;
+    }
+  }
   // every wave's last LDS reads finished before the final barrier of the k loop
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
@@ -907,7 +927,32 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
     const int col0 = n0 + wn;
     // Output goes out with nontemporal stores: a tile round writes as much as the L2
     // holds, and cached stores would evict the operand panels the next k steps reuse.
-    if (p.d_bf16) {
+    if (FUSED && p.d_fp8) {
+      // FP8 codes of eight consecutive outputs per lane: satRNE(fl32(d * scale))
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int r = t * 8 + (lane >> 3);
+        const int c = (lane & 7) * 8;
+        const float4 lo = *reinterpret_cast<const float4*>(ep + r * (kEpPitch / 4) + c);
+        const float4 hi = *reinterpret_cast<const float4*>(ep + r * (kEpPitch / 4) + c + 4);
+        const int grow = row0 + r, gcol = col0 + c;
+        if (grow < p.M && gcol < p.N) {
+          const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+          for (int q = 0; q < 8; ++q) mbits = max(mbits, __float_as_uint(v[q]) & 0x7fffffffu);
+          v2u o;
+          if (p.d_fp8 == 2) {
+            o[0] = quant4<true>(v[0], v[1], v[2], v[3], s_out);
+            o[1] = quant4<true>(v[4], v[5], v[6], v[7], s_out);
+          } else {
+            o[0] = quant4<false>(v[0], v[1], v[2], v[3], s_out);
+            o[1] = quant4<false>(v[4], v[5], v[6], v[7], s_out);
+          }
+          __builtin_nontemporal_store(
+              o, reinterpret_cast<v2u*>(static_cast<uint8_t*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol));
+        }
+      }
+    } else if (p.d_bf16) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const int r = t * 8 + (lane >> 3);
@@ -918,6 +963,11 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
         if (grow < p.M && gcol < p.N) {
           const v4u o = {bf16x2_rne(lo.x, lo.y), bf16x2_rne(lo.z, lo.w), bf16x2_rne(hi.x, hi.y),
                          bf16x2_rne(hi.z, hi.w)};
+          if constexpr (FUSED) {  // the stored bf16 magnitudes, widened: max over both halves
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              mbits = max(mbits, max((o[q] << 16) & 0x7fffffffu, o[q] & 0x7fff0000u));
+          }
           __builtin_nontemporal_store(
               o, reinterpret_cast<v4u*>(static_cast<uint16_t*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol));
         }
@@ -937,12 +987,21 @@ __global__ __launch_bounds__(NT8, 1) void k_gemm4(Params p) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) v4[q] = __fadd_rn(old[q], v4[q]);
           }
+          if constexpr (FUSED) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) mbits = max(mbits, __float_as_uint(v4[q]) & 0x7fffffffu);
+          }
           __builtin_nontemporal_store(v4, dst);
         }
       }
     }
     __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
     __builtin_amdgcn_wave_barrier();
+  }
+  if constexpr (FUSED) {
+    // the third B stage slot [128 KB, 160 KB) is not used by the epilogue's staging
+    grid_amax<NT8>(__uint_as_float(mbits), p.amax, static_cast<AmaxWork*>(p.amax_ws), false,
+                   reinterpret_cast<uint32_t*>(smem + 2 * kPB));
   }
 }
 
@@ -1004,7 +1063,7 @@ const char* splitk_name(const char* name) {
   return it->second.c_str();
 }
 
-template <int KIND, int AF, int BF, bool PANEL = false>
+template <int KIND, int AF, int BF, bool PANEL = false, bool FUSED = false>
 hipError_t run(Params p, hipStream_t s, const char* name) {
   g_last_variant = name;
   const int nb = p.nbm * p.nbn;
@@ -1032,9 +1091,15 @@ hipError_t run(Params p, hipStream_t s, const char* name) {
     g_last_variant = "gemm_mx_256x256_twostage";
     hipLaunchKernelGGL((k_gemm<KIND_MX, AF, BF>), dim3(nb), dim3(NT), 0, s, p);
   } else {
-    hipLaunchKernelGGL((k_gemm4<KIND, AF, BF, PANEL>), dim3(nb), dim3(NT8), 0, s, p);
+    hipLaunchKernelGGL((k_gemm4<KIND, AF, BF, PANEL, FUSED>), dim3(nb), dim3(NT8), 0, s, p);
   }
   return hipGetLastError();
+}
+
+// empty output with the fused epilogue: amax = 0, and the FP8 output's scale_inv
+__global__ void k_gemm_amax_empty(float* amax, const float* d_scale, float* d_scale_inv) {
+  *amax = 0.0f;
+  if (d_scale != nullptr) *d_scale_inv = 1.0f / *d_scale;
 }
 
 }  // namespace
@@ -1042,7 +1107,14 @@ hipError_t run(Params p, hipStream_t s, const char* name) {
 const char* last_gemm_variant() { return g_last_variant; }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
-  if (g.m == 0 || g.n == 0) return hipSuccess;
+  if (g.m == 0 || g.n == 0) {
+    if (g.amax != nullptr) {
+      hipLaunchKernelGGL(k_gemm_amax_empty, dim3(1), dim3(1), 0, s, g.amax, g.d_fp8 ? g.d_scale : nullptr,
+                         g.d_scale_inv);
+      return hipGetLastError();
+    }
+    return hipSuccess;
+  }
   Params p;
   p.a = static_cast<const uint8_t*>(g.a);
   p.b = static_cast<const uint8_t*>(g.b);
@@ -1064,8 +1136,20 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   p.splits = g.splits > 1 ? g.splits : 1;
   p.partial = 0;
   p.partial_ws = static_cast<float*>(g.workspace);
+  p.amax = g.amax;
+  p.amax_ws = g.amax_ws;
+  p.d_scale = g.d_scale;
+  p.d_scale_inv = g.d_scale_inv;
+  p.d_fp8 = g.d_fp8;
   // f8f6f4 format codes: 0 = E4M3, 1 = E5M2
   const int af = (g.a_fmt == E5M2) ? 1 : 0, bf = (g.b_fmt == E5M2) ? 1 : 0;
+  if (g.amax != nullptr) {  // fused amax epilogue (per-tensor FP8 and BF16, no split-K; checked by the caller)
+    if (g.a_fmt == BF16) return run<KIND_BF16, 0, 0, false, true>(p, s, "gemm4_bf16_256x256_pingpong_amax");
+    if (af == 0 && bf == 0) return run<KIND_FP8, 0, 0, false, true>(p, s, "gemm4_fp8_e4m3_e4m3_256x256_pingpong_amax");
+    if (af == 1 && bf == 0) return run<KIND_FP8, 1, 0, false, true>(p, s, "gemm4_fp8_e5m2_e4m3_256x256_pingpong_amax");
+    if (af == 0 && bf == 1) return run<KIND_FP8, 0, 1, false, true>(p, s, "gemm4_fp8_e4m3_e5m2_256x256_pingpong_amax");
+    return run<KIND_FP8, 1, 1, false, true>(p, s, "gemm4_fp8_e5m2_e5m2_256x256_pingpong_amax");
+  }
   if (g.a_fmt == BF16) return run<KIND_BF16, 0, 0>(p, s, "gemm4_bf16_256x256_pingpong");
   if (g.a_fmt == E2M1) {
     if (g.mx_panel) return run<KIND_MX4, 4, 4, true>(p, s, "gemm4_mxfp4_e2m1_e2m1_256x256_pingpong_panel");

@@ -64,6 +64,12 @@ struct GemmArgs {
   int accumulate;        // 1: fp32 D = fl32(D_old + result)
   int splits = 1;        // split-K: k splits (per-tensor FP8 / BF16 only)
   void* workspace = nullptr;  // split-K: [splits, m, n] fp32
+  // fused epilogue (te_fp8_gemm_amax): amax of the output, optional FP8 output
+  float* amax = nullptr;
+  void* amax_ws = nullptr;
+  const float* d_scale = nullptr;
+  float* d_scale_inv = nullptr;
+  int d_fp8 = 0;              // 0 none, 1 E4M3, 2 E5M2
 };
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);

@@ -306,6 +306,37 @@ te_status te_fp8_gemm(const void* a, int a_dtype, const void* a_scale,
                       void* d, int d_dtype, void* stream);
 
 /*
+ * te_fp8_gemm_amax -- te_fp8_gemm (per-tensor FP8 or BF16 operands) whose epilogue also
+ * reduces the amax of its output, and can write that output directly as FP8.
+ *
+ * Defines: [LP-opt] "実モデルにおける結果の解釈" (a per-tensor amax needs an extra
+ * memory pass; Current scaling pays that pass on top of Delayed) and [FP8-intro] "FP8
+ * Training について" (every tensor cast to FP8 has its own scale, the next layer's
+ * input included): the GEMM that produces a tensor finds its amax while writing it,
+ * so the next cast needs no amax pass (TE_SCALE_CURRENT_FROM_AMAX), or, with delayed
+ * scaling, writes it as FP8 at once.
+ *
+ *   a, b, scales, m, n, k, bias  as te_fp8_gemm with gran = TE_GRAN_TENSOR.
+ *   d          [m, n] of d_dtype: TE_BF16 or TE_F32 as te_fp8_gemm, or TE_E4M3 /
+ *              TE_E5M2: uint8 codes satRNE(fl32(r * *d_scale)), r the fp32 result
+ *              (scaled, bias added), rounded to nearest even and saturating as
+ *              te_amax_cast does.
+ *   d_scale    [1] fp32, read (FP8 d only, e.g. the tensor's delayed scale); else NULL.
+ *   d_scale_inv [1] fp32, written 1 / *d_scale (FP8 d only); else NULL.
+ *   amax       [1] fp32, written: max |D| over the stored values (bf16 / fp32), or over
+ *              the fp32 results before the cast (FP8), as a separate cast of that
+ *              result would record it; a NaN result makes it NaN; 0 for an empty D.
+ *   amax_workspace  the amax workspace (see the conventions above).
+ * Shape rules and errors as te_fp8_gemm; MX granularities: TE_ERR_UNSUPPORTED.
+ */
+te_status te_fp8_gemm_amax(const void* a, int a_dtype, const void* a_scale,
+                           const void* b, int b_dtype, const void* b_scale,
+                           int64_t m, int64_t n, int64_t k,
+                           const void* bias, int bias_dtype,
+                           void* d, int d_dtype, const float* d_scale, float* d_scale_inv,
+                           float* amax, void* amax_workspace, void* stream);
+
+/*
  * te_fp8_gemm_accumulate -- te_fp8_gemm that adds its result into an fp32 D:
  * D[i, j] = fl32(D_old[i, j] + r[i, j]), r the te_fp8_gemm result of the same
  * arguments (scaled, plus bias).
