@@ -39,6 +39,8 @@ from .quantize import (
 )
 from .gemm import gemm_per_tensor, gemm_with_amax, gemm_mx, gemm_bf16, bf16_round_bits, bf16_bits_to_f32, rel_err, bias_grad
 from .layernorm import layernorm
+from .fp4_recipe import (hadamard, rht16_rows, philox4x64_10, sr_bits16, e2m1_encode_sr, mxfp4_quantize_sr,
+                         mxfp4_quantize_2d)
 
 __all__ = [
     "E4M3", "E5M2", "FP8Format", "decode", "decode_table", "encode", "fp8_format",
@@ -46,4 +48,6 @@ __all__ = [
     "DelayedScalingState", "delayed_update", "mxfp8_quantize", "e8m0_to_float", "mx_scales_panel", "mx_scales_from_panel",
     "gemm_per_tensor", "gemm_with_amax", "gemm_mx", "gemm_bf16", "bf16_round_bits", "bf16_bits_to_f32",
     "rel_err", "bias_grad", "layernorm",
+    "hadamard", "rht16_rows", "philox4x64_10", "sr_bits16", "e2m1_encode_sr", "mxfp4_quantize_sr",
+    "mxfp4_quantize_2d",
 ]

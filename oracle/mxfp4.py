@@ -4,9 +4,8 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 [LP-opt] "実モデルにおける結果の解釈" compares the FP4 tensor-core GEMMs with
 MXFP8 on the same shapes (FP4 1.46-1.66x faster on the large GEMMs); its NVFP4
-recipe needs E4M3 scales per 16 elements, a random Hadamard transform and
-stochastic rounding, which a matrix core with E8M0 scales per 32 elements does
-not apply.  The FP4 variant built here is therefore MXFP4 (OCP Microscaling
+recipe needs E4M3 scales per 16 elements, which a matrix core with E8M0 scales
+per 32 elements does not apply.  The FP4 variant built here is therefore MXFP4 (OCP Microscaling
 Formats v1.0), the block format of the MXFP8 recipe ([TE-summary] "主な機能")
 with 4-bit elements.  Readings:
 
@@ -21,6 +20,9 @@ with 4-bit elements.  Readings:
   * a block holding a NaN gets the NaN scale code 255 (E2M1 has no NaN, so the
     scale carries it) and its elements are cast with e = 0, NaN to +0;
   * two codes per byte, element 2i in the low nibble, 2i + 1 in the high one.
+
+The recipe steps around this quantizer (Hadamard transform, stochastic rounding, 2D
+weight blocks) are in fp4_recipe.py.
 
 Pins (tests/test_oracle_mxfp4.py): the 16-code table from its bit fields, the
 round trip of every code, every midpoint tie, saturation and monotonicity of
@@ -76,6 +78,20 @@ def unpack(packed) -> np.ndarray:
     return out
 
 
+def block_exponent(xb):
+    """The scale rule for blocks along the last axis of xb (float64): (e, e8m0 codes).
+    e = floor(log2 amax) - 2 clamped to [-127, 127]; 0 for an all-zero block; 127 for an
+    infinite amax; a block holding a NaN gets e = 0 and code 255."""
+    nan = np.any(np.isnan(xb), axis=-1)
+    am = np.max(np.where(np.isnan(xb), 0.0, np.abs(xb)), axis=-1)
+    fin = np.isfinite(am)
+    _, fe = np.frexp(np.where((am > 0) & fin, am, 1.0))
+    e = np.where(am > 0, fe.astype(np.int64) - 1 - 2, 0)
+    e = np.where(fin, e, 127)                          # log2 of an infinite amax is +inf
+    e = np.where(nan, 0, np.clip(e, -127, 127))
+    return e, np.where(nan, 255, e + 127).astype(np.uint8)
+
+
 def mxfp4_quantize(x):
     """(packed codes uint8 [R, C/2], e8m0 uint8 [R, C/32]) of the rows of x (fp32 values)."""
     x32 = np.asarray(x, dtype=np.float32)
@@ -83,14 +99,7 @@ def mxfp4_quantize(x):
     if C % BLOCK:
         raise ValueError("row length must be a multiple of 32")
     xb = x32.reshape(R, C // BLOCK, BLOCK).astype(np.float64)
-    nan = np.any(np.isnan(xb), axis=2)
-    am = np.max(np.where(np.isnan(xb), 0.0, np.abs(xb)), axis=2)
-    fin = np.isfinite(am)
-    _, fe = np.frexp(np.where((am > 0) & fin, am, 1.0))
-    e = np.where(am > 0, fe.astype(np.int64) - 1 - 2, 0)
-    e = np.where(fin, e, 127)                          # log2 of an infinite amax is +inf
-    e = np.where(nan, 0, np.clip(e, -127, 127))
-    scale_codes = np.where(nan, 255, e + 127).astype(np.uint8)
+    e, scale_codes = block_exponent(xb)
     scaled = np.ldexp(xb, (-e)[:, :, None].astype(np.int32))
     return pack(e2m1_encode(scaled).reshape(R, C)), scale_codes
 
