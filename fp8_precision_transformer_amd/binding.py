@@ -35,6 +35,8 @@ TE_F32, TE_BF16, TE_E4M3, TE_E5M2, TE_E8M0, TE_E2M1 = range(6)
 TE_SCALE_DELAYED, TE_SCALE_CURRENT, TE_SCALE_CURRENT_FROM_AMAX = 0, 1, 2
 TE_AMAX_MAX, TE_AMAX_MOST_RECENT = 0, 1
 TE_GRAN_TENSOR, TE_GRAN_MX_BLOCK32, TE_GRAN_MX_BLOCK32_PANEL = 0, 1, 2
+# te_mxfp4_quantize_recipe flags
+TE_MX4_RHT, TE_MX4_SR, TE_MX4_2D = 1, 2, 4
 
 FP8_CODES = {"E4M3": TE_E4M3, "E5M2": TE_E5M2, "E2M1": TE_E2M1}
 
@@ -70,6 +72,8 @@ _SIGNATURES = {
     "te_mxfp8_quantize_panel": [_vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp],
     "te_fp8_gemm_splitk": [_vp, _i32, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _i32, _i32, _vp, _i64,
                            _vp],
+    "te_mxfp4_quantize_recipe": [_vp, _i32, _i64, _i64, _i32, ctypes.c_uint32, ctypes.c_uint64, _vp, _vp, _vp, _vp,
+                                 _vp],
     "te_mxfp4_quantize_panel": [_vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
 }
 
@@ -398,6 +402,18 @@ def te_mxfp4_quantize_panel(x, out_row=None, scale_row=None, out_col=None, scale
     rows, cols = _2d(x)
     _check(lib().te_mxfp4_quantize_panel(_ptr(x), _hp_code(x), rows, cols, _ptr(out_row), _ptr(scale_row),
                                          _ptr(out_col), _ptr(scale_col), _stream(stream)))
+
+
+def te_mxfp4_quantize_recipe(x, flags, out_row=None, scale_row=None, out_col=None, scale_col=None, sign_mask=0,
+                             seed=0, stream=None):
+    """MXFP4 with the FP4 recipe steps (TE_MX4_RHT / TE_MX4_SR / TE_MX4_2D), panel-layout scales."""
+    for n, t in (("x", x), ("out_row", out_row), ("scale_row", scale_row), ("out_col", out_col),
+                 ("scale_col", scale_col)):
+        _need(t, n)
+    rows, cols = _2d(x)
+    _check(lib().te_mxfp4_quantize_recipe(_ptr(x), _hp_code(x), rows, cols, int(flags), int(sign_mask) & 0xFFFFFFFF,
+                                          int(seed) & ((1 << 64) - 1), _ptr(out_row), _ptr(scale_row), _ptr(out_col),
+                                          _ptr(scale_col), _stream(stream)))
 
 
 def version() -> str:

@@ -500,6 +500,40 @@ te_status te_mxfp8_quantize_panel(const void* x, int x_dtype, int64_t rows, int6
                            out_col, scale_col, stream);
 }
 
+te_status te_mxfp4_quantize_recipe(const void* x, int x_dtype, int64_t rows, int64_t cols, int flags,
+                                   uint32_t rht_sign_mask, uint64_t sr_seed, uint8_t* out_row, uint8_t* scale_row,
+                                   uint8_t* out_col, uint8_t* scale_col, void* stream) {
+  const char* name = "te_mxfp4_quantize_recipe";
+  if (rows < 0 || cols < 0) return fail(TE_ERR_SHAPE, "negative shape");
+  if (x_dtype != TE_BF16) return fail(TE_ERR_UNSUPPORTED, "%s: TE_BF16 input only", name);
+  if (flags & ~(TE_MX4_RHT | TE_MX4_SR | TE_MX4_2D)) return fail(TE_ERR_ARG, "%s: unknown flags 0x%x", name, flags);
+  const bool rht = flags & TE_MX4_RHT, sr = flags & TE_MX4_SR, two_d = flags & TE_MX4_2D;
+  const bool row = out_row || scale_row, col = out_col || scale_col;
+  if (!row && !col) return fail(TE_ERR_NULL, "both output pairs are NULL");
+  if ((out_row == nullptr) != (scale_row == nullptr)) return fail(TE_ERR_NULL, "out_row and scale_row go together");
+  if ((out_col == nullptr) != (scale_col == nullptr)) return fail(TE_ERR_NULL, "out_col and scale_col go together");
+  if (two_d && (rht || sr)) return fail(TE_ERR_ARG, "%s: TE_MX4_2D (weights) takes neither RHT nor SR", name);
+  if (two_d && !(row && col)) return fail(TE_ERR_NULL, "%s: TE_MX4_2D writes both copies", name);
+  if (rht && !col) return fail(TE_ERR_ARG, "%s: TE_MX4_RHT transforms the column copy, which is missing", name);
+  if (rows % 128 != 0 || cols % 128 != 0)
+    return fail(TE_ERR_UNSUPPORTED, "%s: rows and cols must be multiples of 128 (got %lld x %lld)", name,
+                (long long)rows, (long long)cols);
+  if (cols * 128 * 2 >= (int64_t(1) << 31) || rows * 128 >= (int64_t(1) << 31))
+    return fail(TE_ERR_SHAPE, "%s: a 128-row (column) band must fit 2 GiB", name);
+  if (rows * cols > 0 && !x) return fail(TE_ERR_NULL, "x is NULL");
+  if ((x && !aligned16(x)) || (out_row && !aligned16(out_row)) || (out_col && !aligned16(out_col)) ||
+      (scale_row && !aligned16(scale_row)) || (scale_col && !aligned16(scale_col)))
+    return fail(TE_ERR_ALIGN, "x, outputs and scale arrays must be 16-byte aligned");
+  te_status st = check_device();
+  if (st != TE_OK) return st;
+  log_dispatch(name, two_d ? "tile128x128_2d_blocks" : (sr ? (rht ? "tile128x128_rht_sr" : "tile128x128_sr")
+                                                           : (rht ? "tile128x128_rht" : "tile128x128")),
+               "E2M1");
+  return hip_status(te::launch_mxfp4_recipe(x, rows, cols, rht, sr, two_d, rht_sign_mask, sr_seed, out_row, scale_row,
+                                            out_col, scale_col, static_cast<hipStream_t>(stream)),
+                    name);
+}
+
 te_status te_mxfp4_quantize_panel(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* out_row,
                                   uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col, void* stream) {
   return mx_quantize_panel("te_mxfp4_quantize_panel", x, x_dtype, rows, cols, 1, TE_E4M3, out_row, scale_row, out_col,

@@ -44,6 +44,12 @@ hipError_t launch_mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64
 hipError_t launch_mx_quantize_panel(const void* x, int64_t rows, int64_t cols, int fp4, int e5m2,
                                     uint8_t* out_row, uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col,
                                     hipStream_t s);
+// MXFP4 with the FP4 recipe steps (bf16, whole 128 x 128 tiles, panel-layout scales):
+// rht: Hadamard transform of the column copy (sign_mask); sr: stochastic rounding (seed);
+// two_d: 32 x 32 block scales (both copies).
+hipError_t launch_mxfp4_recipe(const void* x, int64_t rows, int64_t cols, int rht, int sr, int two_d,
+                               uint32_t sign_mask, uint64_t seed, uint8_t* out_row, uint8_t* scale_row,
+                               uint8_t* out_col, uint8_t* scale_col, hipStream_t s);
 hipError_t launch_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* out_row,
                                  uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col, hipStream_t s);
 

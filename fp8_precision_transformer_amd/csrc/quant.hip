@@ -1170,6 +1170,367 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_tiles(const uint16_t* __rest
   }
 }
 
+// ----------------------------------------------------------------------------
+// The FP4 recipe steps around MXFP4 ([LP-opt] "実モデルにおける結果の解釈": a random
+// Hadamard transform of the Wgrad inputs, stochastic rounding of gradients, 2D block
+// scaling of weights).  bf16 input of whole 128 x 128 tiles, E8M0 scales in the panel
+// layout the GEMM loads (same tile walk and staging as k_mxfp8_tiles).
+//
+// Hadamard transform (column copy only: along the rows, which are the Wgrad reduction
+// axis): per 16 consecutive rows, y = (1/4) H16 diag(s) x with s from a 16-bit sign mask;
+// the sum is formed by the fast transform's butterflies in fp64 (pairs i, i + h for h =
+// 1, 2, 4, 8) and rounded once to fp32 after the exact scaling by 1/4.
+//
+// Stochastic rounding: the random 16-bit integer of element i (row-major index in the
+// copy written) is lane i % 16 of Philox4x64-10 with counter (i / 16, copy, 0, 0) and key
+// (seed, 0); lane l is bits 16 (l % 4) .. of output word l / 4.  A scaled magnitude
+// between neighbouring E2M1 magnitudes lo <= a < hi rounds up iff r < 65536 (a - lo) /
+// (hi - lo); every step of that test is exact in fp32.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ void philox4x64_10(uint64_t& c0, uint64_t& c1, uint64_t& c2, uint64_t& c3, uint64_t k0,
+                                              uint64_t k1) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const uint64_t lo0 = M0 * c0, hi0 = __umul64hi(M0, c0);
+    const uint64_t lo1 = M1 * c2, hi1 = __umul64hi(M1, c2);
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+}
+
+// the 16 random 16-bit integers of call `call` of copy `copy` (lane l: r[l / 4] >> 16 (l % 4))
+__device__ __forceinline__ void sr_call(uint64_t call, uint32_t copy, uint64_t seed, uint64_t (&r)[4]) {
+  r[0] = call;
+  r[1] = copy;
+  r[2] = 0;
+  r[3] = 0;
+  philox4x64_10(r[0], r[1], r[2], r[3], seed, 0);
+}
+
+// E2M1 code of an already scaled value y, rounded stochastically with the 16-bit r16;
+// saturates at 6, keeps the sign, NaN -> +0
+__device__ __forceinline__ uint32_t e2m1_sr_code(float y, uint32_t r16) {
+  const float a = __builtin_fabsf(y);
+  if (!(a == a)) return 0u;
+  const uint32_t idx = static_cast<uint32_t>(a >= 0.5f) + static_cast<uint32_t>(a >= 1.0f) +
+                       static_cast<uint32_t>(a >= 1.5f) + static_cast<uint32_t>(a >= 2.0f) +
+                       static_cast<uint32_t>(a >= 3.0f) + static_cast<uint32_t>(a >= 4.0f) +
+                       static_cast<uint32_t>(a >= 6.0f);
+  uint32_t c = 7u;
+  if (idx < 7u) {
+    const float lo = idx <= 4u ? 0.5f * static_cast<float>(idx) : (idx == 5u ? 3.0f : 4.0f);
+    const float inv_w = idx < 4u ? 2.0f : (idx < 6u ? 1.0f : 0.5f);
+    const float p = __fmul_rn(__fsub_rn(a, lo), inv_w);  // exact
+    c = idx + static_cast<uint32_t>(static_cast<float>(r16) < __fmul_rn(p, 65536.0f));
+  }
+  return c | ((__float_as_uint(y) >> 31) << 3);
+}
+
+// in place: v[0..15] <- fl32((1/4) H16 diag(s) v), fp64 butterflies
+__device__ __forceinline__ void rht16(float* v, uint32_t sign_mask) {
+  double t[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) t[j] = ((sign_mask >> j) & 1u) ? -static_cast<double>(v[j]) : static_cast<double>(v[j]);
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((i & h) == 0) {
+        const double a = t[i], b = t[i + h];
+        t[i] = __dadd_rn(a, b);
+        t[i + h] = __dsub_rn(a, b);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = static_cast<float>(t[j] * 0.25);
+}
+
+struct Mx4Recipe {
+  uint32_t sign_mask;  // Hadamard signs of the column copy
+  uint64_t seed;       // stochastic rounding key
+};
+
+// 8 scaled values -> one dword of codes (value j in nibble j): round to nearest even, or
+// stochastically with the random integers of 8 consecutive lanes, the four 16-bit lanes
+// of w0 then those of w1
+template <bool SR>
+__device__ __forceinline__ uint32_t mx4_pack8(const float* w, bool nan, uint64_t w0, uint64_t w1) {
+  if constexpr (SR) {
+    uint32_t d = 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint64_t word = j < 4 ? w0 : w1;
+      d |= e2m1_sr_code(w[j], static_cast<uint32_t>(word >> (16 * (j & 3))) & 0xffffu) << (4 * j);
+    }
+    return d;
+  } else {
+    return nan ? e2m1_pack8_slow(w) : e2m1_pack8(w);
+  }
+}
+
+template <bool ROW, bool COL, bool RHT, bool SR>
+__global__ __launch_bounds__(kThreads) void k_mxfp4_recipe(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                           uint8_t* __restrict__ out_row,
+                                                           uint8_t* __restrict__ scale_row,
+                                                           uint8_t* __restrict__ out_col,
+                                                           uint8_t* __restrict__ scale_col, Mx4Recipe rc) {
+  auto scale_dw = [](uint8_t* base, int64_t r, int64_t cols, int64_t c0) {
+    return reinterpret_cast<uint32_t*>(base) + ((r >> 8) * (cols >> 7) + (c0 >> 7)) * 256 + (r & 255);
+  };
+  constexpr int NP = 8, RPP = 16;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[COL ? kCT * kMxTPitch : 16];
+  const int64_t ntc = C / kCT;
+  const int64_t ntiles = ntc * (R / kCT);
+  const int t = threadIdx.x, lane = t & 63;
+  const int prow = t >> 4, pcol = (t & 15) * 8;
+  const uint32_t ld_off = static_cast<uint32_t>((prow * C + pcol) * 2);
+  const uint32_t ld_pass = static_cast<uint32_t>(RPP * C * 2);
+  auto origin = [&](int64_t i, int64_t& r0, int64_t& c0) {
+    r0 = (i / ntc) * kCT;
+    c0 = (i % ntc) * kCT;
+  };
+  auto load1 = [&](int p, int64_t r0, int64_t c0) {
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(x + r0 * C + c0);
+    return *reinterpret_cast<const uint4*>(base + ld_off + p * ld_pass);
+  };
+  auto process = [&](uint4 (&raw)[NP], int64_t r0, int64_t c0, bool has1, int64_t r1, int64_t c1) {
+    if constexpr (COL) __syncthreads();
+#pragma clang loop unroll(full)
+    for (int p = 0; p < NP; ++p) {
+      const int lr = p * RPP + prow;
+      if constexpr (COL) *reinterpret_cast<uint4*>(tile + lr * kMxTPitch + pcol * 2) = raw[p];
+      if constexpr (ROW) {
+        uint32_t m = absmax_bits<uint16_t>(0u, raw[p]);
+        m = max(m & 0xffffu, m >> 16);
+        m = max(m, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(m), 0xb1, 0xf, 0xf, false)));
+        m = max(m, static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(m), 0x4e, 0xf, 0xf, false)));
+        const int64_t r = r0 + lr;
+        const bool nan = m > 0x7f80u;
+        const int e = nan ? 0 : mx4_exponent(m << 16);
+        float v[8];
+        unpack16<uint16_t>(raw[p], v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = __builtin_ldexpf(v[j], -e);
+        const int64_t i0 = r * C + c0 + pcol;  // row copy: element index of v[0]
+        uint64_t w0 = 0, w1 = 0;
+        if constexpr (SR) {
+          uint64_t a0 = static_cast<uint64_t>(i0 >> 4), a1 = 0, a2 = 0, a3 = 0;
+          philox4x64_10(a0, a1, a2, a3, rc.seed, 0);
+          const bool hi_half = (i0 & 15) != 0;  // lanes 8 .. 15 of the call: words 2, 3
+          w0 = hi_half ? a2 : a0;
+          w1 = hi_half ? a3 : a1;
+        }
+        *reinterpret_cast<uint32_t*>(out_row + r * (C / 2) + (c0 + pcol) / 2) = mx4_pack8<SR>(v, nan, w0, w1);
+        const uint32_t code = nan ? 255u : static_cast<uint32_t>(e + 127);
+        const uint32_t k1 = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(code), 0x104, 0xf, 0xf, true));
+        const uint32_t k2 = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(code), 0x108, 0xf, 0xf, true));
+        const uint32_t k3 = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(code), 0x10c, 0xf, 0xf, true));
+        if ((lane & 15) == 0) *scale_dw(scale_row, r, C, c0) = code | (k1 << 8) | (k2 << 16) | (k3 << 24);
+      }
+      if constexpr (!COL) {
+        if (has1) raw[p] = load1(p, r1, c1);
+      }
+    }
+    if constexpr (COL) {
+      if (has1) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) raw[p] = load1(p, r1, c1);
+      }
+      __syncthreads();
+      const int cp = t & 63, blk = t >> 6;
+      uint32_t q[2][4], code[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {  // h = 0: column 2cp (low halves), 1: column 2cp + 1
+        float v[32];
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+          const uint32_t d = *reinterpret_cast<const uint32_t*>(tile + (32 * blk + k) * kMxTPitch + 4 * cp);
+          v[k] = __uint_as_float(h ? (d & 0xffff0000u) : (d << 16));
+        }
+        if constexpr (RHT) {
+          rht16(v, rc.sign_mask);
+          rht16(v + 16, rc.sign_mask);
+        }
+        uint32_t mb = 0u;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) mb = max(mb, __float_as_uint(v[k]) & 0x7fffffffu);
+        const bool nan = mb > 0x7f800000u;
+        const int e = nan ? 0 : mx4_exponent(mb);
+        code[h] = nan ? 255u : static_cast<uint32_t>(e + 127);
+        const int64_t c = c0 + 2 * cp + h;
+        const int64_t i0 = c * R + r0 + 32 * blk;  // column copy: element index of v[0] (a multiple of 32)
+        uint64_t ra[4] = {0, 0, 0, 0}, rb[4] = {0, 0, 0, 0};
+        if constexpr (SR) {
+          sr_call(static_cast<uint64_t>(i0 >> 4), 1u, rc.seed, ra);
+          sr_call(static_cast<uint64_t>(i0 >> 4) + 1, 1u, rc.seed, rb);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float w[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) w[j] = __builtin_ldexpf(v[8 * g + j], -e);
+          const uint64_t* rw = g < 2 ? ra : rb;  // lanes 8 (g % 2) .. of the call
+          q[h][g] = mx4_pack8<SR>(w, nan, rw[2 * (g & 1)], rw[2 * (g & 1) + 1]);
+        }
+      }
+      __syncthreads();  // every thread has read its column pair
+      uint8_t* qt = tile;
+      uint8_t* qs = tile + kCT * kMx4QPitch;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        *reinterpret_cast<uint4*>(qt + (2 * cp + h) * kMx4QPitch + 16 * blk) = make_uint4(q[h][0], q[h][1], q[h][2], q[h][3]);
+        qs[(2 * cp + h) * 4 + blk] = static_cast<uint8_t>(code[h]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int c = (t >> 2) + 64 * k, chunk = t & 3;
+        const uint4 vv = *reinterpret_cast<const uint4*>(qt + c * kMx4QPitch + 16 * chunk);
+        *reinterpret_cast<uint4*>(out_col + (c0 + c) * (R / 2) + r0 / 2 + 16 * chunk) = vv;
+      }
+      if (t < kCT) *scale_dw(scale_col, c0 + t, R, r0) = *reinterpret_cast<const uint32_t*>(qs + 4 * t);
+    }
+  };
+  int64_t i = blockIdx.x;
+  if (i >= ntiles) return;
+  uint4 raw[NP];
+  int64_t r0, c0;
+  origin(i, r0, c0);
+#pragma unroll
+  for (int p = 0; p < NP; ++p) raw[p] = load1(p, r0, c0);
+  for (;;) {
+    const int64_t i1 = i + gridDim.x;
+    const bool has1 = i1 < ntiles;
+    int64_t r1 = 0, c1 = 0;
+    if (has1) origin(i1, r1, c1);
+    process(raw, r0, c0, has1, r1, c1);
+    if (!has1) break;
+    i = i1;
+    r0 = r1;
+    c0 = c1;
+  }
+}
+
+// 2D block scaling of weights: one E8M0 scale per 32 x 32 sub-tile, the MXFP4 rule on
+// the sub-tile's amax; the row copy repeats it for each row's block and the column copy
+// (the transpose) for each column's block, so both copies hold the same codes.  The tile
+// goes through LDS; thread t finds the amax of sub-tile t / 16 over two of its rows per
+// lane group (16 lanes, xor-reduced), then quantizes like k_mxfp4_recipe's row and
+// column paths with the sub-tile exponents.
+__global__ __launch_bounds__(kThreads) void k_mxfp4_2d(const uint16_t* __restrict__ x, int64_t R, int64_t C,
+                                                       uint8_t* __restrict__ out_row, uint8_t* __restrict__ scale_row,
+                                                       uint8_t* __restrict__ out_col, uint8_t* __restrict__ scale_col) {
+  auto scale_dw = [](uint8_t* base, int64_t r, int64_t cols, int64_t c0) {
+    return reinterpret_cast<uint32_t*>(base) + ((r >> 8) * (cols >> 7) + (c0 >> 7)) * 256 + (r & 255);
+  };
+  constexpr int NP = 8, RPP = 16;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kCT * kMxTPitch];
+  __shared__ int sub_e[16];
+  __shared__ uint32_t sub_m[16];
+  const int64_t ntc = C / kCT;
+  const int64_t ntiles = ntc * (R / kCT);
+  const int t = threadIdx.x, lane = t & 63;
+  const int prow = t >> 4, pcol = (t & 15) * 8;
+  for (int64_t i = blockIdx.x; i < ntiles; i += gridDim.x) {
+    const int64_t r0 = (i / ntc) * kCT, c0 = (i % ntc) * kCT;
+    uint4 raw[NP];
+    __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      raw[p] = *reinterpret_cast<const uint4*>(x + (r0 + p * RPP + prow) * C + c0 + pcol);
+      *reinterpret_cast<uint4*>(tile + (p * RPP + prow) * kMxTPitch + pcol * 2) = raw[p];
+    }
+    __syncthreads();
+    {  // sub-tile (st / 4, st % 4): lanes 16 st .. 16 st + 15, lane j reads rows 2j, 2j + 1
+      const int st = t >> 4, j = t & 15;
+      const int sr = (st >> 2) * 32 + 2 * j, sc = (st & 3) * 32;
+      uint32_t m = 0u;
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          m = absmax_bits<uint16_t>(m, *reinterpret_cast<const uint4*>(tile + (sr + rr) * kMxTPitch + (sc + 8 * q) * 2));
+      m = max(m & 0xffffu, m >> 16);
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off, 16)));
+      if (j == 0) {
+        sub_m[st] = m;
+        sub_e[st] = m > 0x7f80u ? 0 : mx4_exponent(m << 16);
+      }
+    }
+    __syncthreads();
+    // row copy: the lane's 8 elements of row lr, sub-tile (lr / 32, pcol / 32)
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int lr = p * RPP + prow;
+      const int st = (lr >> 5) * 4 + (pcol >> 5);
+      const bool nan = sub_m[st] > 0x7f80u;
+      const int e = sub_e[st];
+      float v[8];
+      unpack16<uint16_t>(raw[p], v);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) v[jj] = __builtin_ldexpf(v[jj], -e);
+      const int64_t r = r0 + lr;
+      *reinterpret_cast<uint32_t*>(out_row + r * (C / 2) + (c0 + pcol) / 2) = nan ? e2m1_pack8_slow(v) : e2m1_pack8(v);
+      if ((lane & 15) == 0) {
+        uint32_t dw = 0u;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int sb = (lr >> 5) * 4 + b;
+          dw |= (sub_m[sb] > 0x7f80u ? 255u : static_cast<uint32_t>(sub_e[sb] + 127)) << (8 * b);
+        }
+        *scale_dw(scale_row, r, C, c0) = dw;
+      }
+    }
+    // column copy: columns 2cp, 2cp + 1 over rows 32 blk .. + 31 (sub-tile (blk, cp / 16))
+    const int cp = t & 63, blk = t >> 6;
+    const int st = blk * 4 + (cp >> 4);
+    const bool nan = sub_m[st] > 0x7f80u;
+    const int e = sub_e[st];
+    const uint32_t code = nan ? 255u : static_cast<uint32_t>(e + 127);
+    uint32_t q[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float w[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const uint32_t d = *reinterpret_cast<const uint32_t*>(tile + (32 * blk + 8 * g + jj) * kMxTPitch + 4 * cp);
+          w[jj] = __builtin_ldexpf(__uint_as_float(h ? (d & 0xffff0000u) : (d << 16)), -e);
+        }
+        q[h][g] = nan ? e2m1_pack8_slow(w) : e2m1_pack8(w);
+      }
+    }
+    __syncthreads();  // every thread has read its column pair
+    uint8_t* qt = tile;
+    uint8_t* qs = tile + kCT * kMx4QPitch;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      *reinterpret_cast<uint4*>(qt + (2 * cp + h) * kMx4QPitch + 16 * blk) = make_uint4(q[h][0], q[h][1], q[h][2], q[h][3]);
+      qs[(2 * cp + h) * 4 + blk] = static_cast<uint8_t>(code);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int c = (t >> 2) + 64 * k, chunk = t & 3;
+      const uint4 vv = *reinterpret_cast<const uint4*>(qt + c * kMx4QPitch + 16 * chunk);
+      *reinterpret_cast<uint4*>(out_col + (c0 + c) * (R / 2) + r0 / 2 + 16 * chunk) = vv;
+    }
+    if (t < kCT) *scale_dw(scale_col, c0 + t, R, r0) = *reinterpret_cast<const uint32_t*>(qs + 4 * t);
+  }
+}
+
 // Blocks of `kernel` (kThreads threads) that fit at once on one compute unit, and the
 // compute units of the current device, asked of the runtime at every launch (the
 // library keeps no cache of them).
@@ -1475,6 +1836,43 @@ hipError_t launch_mx_quantize_panel(const void* x, int64_t rows, int64_t cols, i
   if (fp4) mx_panel_launch<false, true>(xx, rows, cols, out_row, scale_row, out_col, scale_col, s);
   else if (e5m2) mx_panel_launch<true, false>(xx, rows, cols, out_row, scale_row, out_col, scale_col, s);
   else mx_panel_launch<false, false>(xx, rows, cols, out_row, scale_row, out_col, scale_col, s);
+  return hipGetLastError();
+}
+
+template <bool ROW, bool COL, bool RHT, bool SR>
+void mx4_recipe_launch(const uint16_t* x, int64_t R, int64_t C, uint8_t* out_row, uint8_t* scale_row, uint8_t* out_col,
+                       uint8_t* scale_col, Mx4Recipe rc, hipStream_t st) {
+  const auto fn = k_mxfp4_recipe<ROW, COL, RHT, SR>;
+  const int g = persistent_grid(reinterpret_cast<const void*>(fn), (R / kCT) * (C / kCT), 1, COL ? kCapMxCol : kCapMxRow);
+  hipLaunchKernelGGL(fn, dim3(g), dim3(kThreads), 0, st, x, R, C, out_row, scale_row, out_col, scale_col, rc);
+}
+
+hipError_t launch_mxfp4_recipe(const void* x, int64_t rows, int64_t cols, int rht, int sr, int two_d,
+                               uint32_t sign_mask, uint64_t seed, uint8_t* out_row, uint8_t* scale_row,
+                               uint8_t* out_col, uint8_t* scale_col, hipStream_t s) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  const auto* xx = static_cast<const uint16_t*>(x);
+  if (two_d) {
+    const int g = persistent_grid(reinterpret_cast<const void*>(k_mxfp4_2d), (rows / kCT) * (cols / kCT), 1, kCapMxCol);
+    hipLaunchKernelGGL(k_mxfp4_2d, dim3(g), dim3(kThreads), 0, s, xx, rows, cols, out_row, scale_row, out_col, scale_col);
+    return hipGetLastError();
+  }
+  const Mx4Recipe rc{sign_mask, seed};
+  const bool row = out_row != nullptr, col = out_col != nullptr;
+  if (row && col) {
+    if (rht) sr ? mx4_recipe_launch<true, true, true, true>(xx, rows, cols, out_row, scale_row, out_col, scale_col, rc, s)
+             : mx4_recipe_launch<true, true, true, false>(xx, rows, cols, out_row, scale_row, out_col, scale_col, rc, s);
+    else sr ? mx4_recipe_launch<true, true, false, true>(xx, rows, cols, out_row, scale_row, out_col, scale_col, rc, s)
+            : mx4_recipe_launch<true, true, false, false>(xx, rows, cols, out_row, scale_row, out_col, scale_col, rc, s);
+  } else if (col) {
+    if (rht) sr ? mx4_recipe_launch<false, true, true, true>(xx, rows, cols, out_row, scale_row, out_col, scale_col, rc, s)
+             : mx4_recipe_launch<false, true, true, false>(xx, rows, cols, out_row, scale_row, out_col, scale_col, rc, s);
+    else sr ? mx4_recipe_launch<false, true, false, true>(xx, rows, cols, out_row, scale_row, out_col, scale_col, rc, s)
+            : mx4_recipe_launch<false, true, false, false>(xx, rows, cols, out_row, scale_row, out_col, scale_col, rc, s);
+  } else {
+    sr ? mx4_recipe_launch<true, false, false, true>(xx, rows, cols, out_row, scale_row, out_col, scale_col, rc, s)
+       : mx4_recipe_launch<true, false, false, false>(xx, rows, cols, out_row, scale_row, out_col, scale_col, rc, s);
+  }
   return hipGetLastError();
 }
 

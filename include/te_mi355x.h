@@ -459,6 +459,41 @@ te_status te_mxfp4_quantize_panel(const void* x, int x_dtype, int64_t rows, int6
                                   uint8_t* out_row, uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col,
                                   void* stream);
 
+/*
+ * te_mxfp4_quantize_recipe -- MXFP4 quantization with the FP4 recipe's steps around it.
+ *
+ * Defines: [LP-opt] "実モデルにおける結果の解釈" (diagnosis "GEMM の速度向上 >> トレー
+ * ニングの速度向上"): besides the FP4 GEMM, the recipe applies a random Hadamard
+ * transform to the Wgrad inputs, stochastic rounding to gradients and 2D block scaling
+ * to weights.  The scale rule is te_mxfp4_quantize's; scales go out in the panel layout
+ * (as te_mxfp4_quantize_panel).
+ *
+ *   flags      TE_MX4_RHT: the column-wise copy (the Wgrad operand, blocks along the
+ *                rows = tokens) is taken of y = (1/4) H16 diag(s) x, per 16 consecutive
+ *                rows: H16 the Sylvester Hadamard matrix, s_j = -1 where bit j of
+ *                rht_sign_mask is set (the same mask for both Wgrad operands of a step
+ *                keeps dY^T X unchanged); the sum is formed by the fast transform's
+ *                butterflies in fp64 and rounded once to fp32.
+ *              TE_MX4_SR: E2M1 elements rounded stochastically: between neighbouring
+ *                magnitudes lo <= a < hi (a the scaled magnitude, a >= 6 saturates),
+ *                up iff r < 65536 (a - lo) / (hi - lo); r of element i (row-major index
+ *                in the copy written) is 16-bit lane i % 16 of Philox4x64-10 with counter
+ *                (i / 16, copy, 0, 0), copy 0 row-wise / 1 column-wise, key (sr_seed, 0);
+ *                lane l = bits 16 (l % 4) .. of output word l / 4.
+ *              TE_MX4_2D: one scale per 32 x 32 tile (weights); both copies are written
+ *                and the column-wise copy is the transpose of the row-wise one (same
+ *                codes); excludes RHT and SR.
+ *   x          [rows, cols] TE_BF16, rows % 128 == 0 and cols % 128 == 0
+ *              (TE_ERR_UNSUPPORTED otherwise).
+ *   out_row / scale_row, out_col / scale_col  as te_mxfp4_quantize_panel; either pair
+ *              may be NULL (TE_MX4_RHT needs the column pair, TE_MX4_2D both).
+ */
+enum { TE_MX4_RHT = 1, TE_MX4_SR = 2, TE_MX4_2D = 4 };
+te_status te_mxfp4_quantize_recipe(const void* x, int x_dtype, int64_t rows, int64_t cols, int flags,
+                                   uint32_t rht_sign_mask, uint64_t sr_seed,
+                                   uint8_t* out_row, uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col,
+                                   void* stream);
+
 /* Bytes of E8M0 scales in the panel layout (see te_fp8_gemm) for a matrix of `rows`
  * rows and `cols` elements per row: ceil(rows / 256) * 256 * cols / 32.  Host only;
  * -1 if rows < 0 or cols is not a non-negative multiple of 128. */

@@ -115,18 +115,21 @@ def philox4x64_10(counters, key) -> np.ndarray:
     return np.stack([c0, c1, c2, c3], axis=1)
 
 
-def sr_bits16(rows: int, cols: int, copy: int, seed: int) -> np.ndarray:
-    """The 16-bit random integers of every element (r, c) of a [rows, cols] copy."""
+def sr_bits16(rows: int, cols: int, copy: int, seed: int, first_row: int = 0) -> np.ndarray:
+    """The 16-bit random integers of the elements (r, c) of rows first_row .. first_row +
+    rows - 1 of a copy with `cols` columns (element index i = r cols + c)."""
+    i0 = first_row * cols
     n = rows * cols
-    calls = -(-n // 16)
-    ctr = np.zeros((calls, 4), dtype=np.uint64)
-    ctr[:, 0] = np.arange(calls, dtype=np.uint64)
+    c_lo, c_hi = i0 // 16, -(-(i0 + n) // 16)
+    ctr = np.zeros((c_hi - c_lo, 4), dtype=np.uint64)
+    ctr[:, 0] = np.arange(c_lo, c_hi, dtype=np.uint64)
     ctr[:, 1] = np.uint64(copy)
     out = philox4x64_10(ctr, (seed, 0))                       # [calls, 4] uint64
-    lanes = np.empty((calls, 16), dtype=np.uint16)
+    lanes = np.empty((c_hi - c_lo, 16), dtype=np.uint16)
     for l in range(16):
         lanes[:, l] = ((out[:, l // 4] >> np.uint64(16 * (l % 4))) & np.uint64(0xFFFF)).astype(np.uint16)
-    return lanes.reshape(-1)[:n].reshape(rows, cols)
+    start = i0 - 16 * c_lo
+    return lanes.reshape(-1)[start:start + n].reshape(rows, cols)
 
 
 def e2m1_encode_sr(y, r16) -> np.ndarray:
@@ -147,15 +150,16 @@ def e2m1_encode_sr(y, r16) -> np.ndarray:
     return (code + sign).astype(np.uint8)
 
 
-def mxfp4_quantize_sr(x, seed: int, copy: int):
+def mxfp4_quantize_sr(x, seed: int, copy: int, first_row: int = 0):
     """MXFP4 of the rows of x with stochastic rounding of the elements: (packed [R, C/2],
-    e8m0 [R, C/32]); the random integers of element (r, c) as sr_bits16."""
+    e8m0 [R, C/32]); the rows of x are rows first_row .. of the copy, and the random
+    integers of element (r, c) are those of sr_bits16."""
     x32 = np.asarray(x, dtype=np.float32)
     R, C = x32.shape
     xb = x32.reshape(R, C // BLOCK, BLOCK).astype(np.float64)
     e, codes = block_exponent(xb)
     scaled = np.ldexp(xb, (-e)[:, :, None].astype(np.int32)).astype(np.float32)
-    q = e2m1_encode_sr(scaled.reshape(R, C), sr_bits16(R, C, copy, seed))
+    q = e2m1_encode_sr(scaled.reshape(R, C), sr_bits16(R, C, copy, seed, first_row))
     return pack(q), codes
 
 

@@ -86,6 +86,8 @@ def test_sr_bits_follow_the_linear_index_and_differ_by_copy_and_seed():
     a = O.sr_bits16(4, 48, 0, 99)
     np.testing.assert_array_equal(a.reshape(-1), O.sr_bits16(1, 192, 0, 99).reshape(-1))
     np.testing.assert_array_equal(a.reshape(-1)[:96], O.sr_bits16(6, 16, 0, 99).reshape(-1))
+    np.testing.assert_array_equal(O.sr_bits16(2, 48, 0, 99, first_row=1), a[1:3])   # rows of a copy
+    np.testing.assert_array_equal(O.sr_bits16(3, 40, 1, 5, first_row=2), O.sr_bits16(6, 40, 1, 5)[2:5])
     assert not np.array_equal(a, O.sr_bits16(4, 48, 1, 99))
     assert not np.array_equal(a, O.sr_bits16(4, 48, 0, 98))
     big = O.sr_bits16(256, 256, 0, 7).astype(np.int64)
