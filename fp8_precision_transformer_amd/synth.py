@@ -112,3 +112,68 @@ def to_bf16_bits(x32: np.ndarray) -> np.ndarray:
 def bf16_bits_as_f32(bits: np.ndarray) -> np.ndarray:
     """Widen bf16 bit patterns to fp32 (exact) for host-side consumers."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Device-side generators for the workloads too large to draw on the host every step
+# (the 24-layer CodonFM-5B drift sweep): torch's seeded generator on the GPU, the same
+# distributions as above, bf16 by round to nearest even.  The host side of a test copies
+# what it needs (amax, sampled rows) back; both sides see identical bytes.
+# ---------------------------------------------------------------------------
+
+def _torch_seed(*key: int) -> int:
+    return int(np.random.SeedSequence([int(k) for k in key]).generate_state(1, np.uint64)[0] & ((1 << 63) - 1))
+
+
+def gpu_generator(device, *key):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(_torch_seed(*key))
+    return g
+
+
+def gpu_normal(shape, std, device, *key):
+    """N(0, std) as bf16 on `device`."""
+    import torch
+
+    g = gpu_generator(device, *key)
+    return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * np.float32(std)).to(torch.bfloat16)
+
+
+def gpu_activations(shape, device, *key, outlier_frac=1e-3, outlier_mult=50.0):
+    """N(0, 1) with exactly round(outlier_frac * numel) positions (without replacement)
+    multiplied by outlier_mult, as bf16 on `device`."""
+    import torch
+
+    g = gpu_generator(device, *key)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    n = x.numel()
+    k = int(round(outlier_frac * n))
+    if k:
+        pos = torch.randperm(n, generator=g, device=device)[:k]
+        x.view(-1)[pos] *= np.float32(outlier_mult)
+    return x.to(torch.bfloat16)
+
+
+def gpu_grads(shape, device, *key, scale=1e-3):
+    """Student-t(3) times scale as bf16 on `device`: Z sqrt(3 / (Z1^2 + Z2^2 + Z3^2)), the
+    ratio of a normal and the root of a chi-square with three degrees of freedom."""
+    import torch
+
+    g = gpu_generator(device, *key)
+    z = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    chi = torch.zeros_like(z)
+    for _ in range(3):
+        u = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        chi.addcmul_(u, u)
+    chi.clamp_(min=1e-30)
+    return (z * torch.rsqrt(chi / 3.0) * np.float32(scale)).to(torch.bfloat16)
+
+
+def drift(x_bf16, step: int, rate: float = 1.05):
+    """x * rate^step: an fp32 multiply by fl32(rate^step), then bf16 rounding (host or device
+    tensor); the input scale of a training-like run that grows every step."""
+    import torch
+
+    return (x_bf16.float() * float(np.float32(rate ** step))).to(torch.bfloat16)
