@@ -333,11 +333,11 @@ def main():
         b = MX4B[w.name]
         if stage == "fprop":
             B.te_mxfp4_quantize_panel(X[w.name], b["x"], b["xs"])
-            B.te_mxfp4_quantize_recipe(W[w.name], B.TE_MX4_2D, b["w"], b["ws"], b["wT"], b["wTs"])
+            B.te_mxfp4_quantize_recipe(W[w.name], B.TE_MX4_2D, b["w"], b["ws"])
             return (b["x"], b["xs"], b["w"], b["ws"])
         if stage == "dgrad":
             B.te_mxfp4_quantize_recipe(DY[w.name], B.TE_MX4_SR, b["dy"], b["dys"], seed=SR_SEED + step)
-            B.te_mxfp4_quantize_recipe(W[w.name], B.TE_MX4_2D, b["w"], b["ws"], b["wT"], b["wTs"])
+            B.te_mxfp4_quantize_recipe(W[w.name], B.TE_MX4_2D, None, None, b["wT"], b["wTs"])
             return (b["dy"], b["dys"], b["wT"], b["wTs"])
         B.te_mxfp4_quantize_recipe(DY[w.name], B.TE_MX4_RHT | B.TE_MX4_SR, None, None, b["dyT"], b["dyTs"],
                                    sign_mask=RHT_MASK ^ step, seed=SR_SEED + step)

@@ -513,7 +513,6 @@ te_status te_mxfp4_quantize_recipe(const void* x, int x_dtype, int64_t rows, int
   if ((out_row == nullptr) != (scale_row == nullptr)) return fail(TE_ERR_NULL, "out_row and scale_row go together");
   if ((out_col == nullptr) != (scale_col == nullptr)) return fail(TE_ERR_NULL, "out_col and scale_col go together");
   if (two_d && (rht || sr)) return fail(TE_ERR_ARG, "%s: TE_MX4_2D (weights) takes neither RHT nor SR", name);
-  if (two_d && !(row && col)) return fail(TE_ERR_NULL, "%s: TE_MX4_2D writes both copies", name);
   if (rht && !col) return fail(TE_ERR_ARG, "%s: TE_MX4_RHT transforms the column copy, which is missing", name);
   if (rows % 128 != 0 || cols % 128 != 0)
     return fail(TE_ERR_UNSUPPORTED, "%s: rows and cols must be multiples of 128 (got %lld x %lld)", name,

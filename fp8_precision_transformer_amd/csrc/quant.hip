@@ -1187,6 +1187,19 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_tiles(const uint16_t* __rest
 // between neighbouring E2M1 magnitudes lo <= a < hi rounds up iff r < 65536 (a - lo) /
 // (hi - lo); every step of that test is exact in fp32.
 // ----------------------------------------------------------------------------
+// the 128-bit product m b as (hi, lo): four 32 x 32 -> 64 multiply-adds (v_mad_u64_u32),
+// each partial sum below 2^64, and one 64-bit add
+__device__ __forceinline__ void mulhilo64(uint64_t m, uint64_t b, uint64_t& lo, uint64_t& hi) {
+  const uint32_t m0 = static_cast<uint32_t>(m), m1 = static_cast<uint32_t>(m >> 32);
+  const uint32_t b0 = static_cast<uint32_t>(b), b1 = static_cast<uint32_t>(b >> 32);
+  const uint64_t p00 = static_cast<uint64_t>(m0) * b0;
+  const uint64_t p01 = static_cast<uint64_t>(m0) * b1 + (p00 >> 32);
+  const uint64_t p10 = static_cast<uint64_t>(m1) * b0 + static_cast<uint32_t>(p01);
+  const uint64_t p11 = static_cast<uint64_t>(m1) * b1 + (p01 >> 32);
+  lo = (p10 << 32) | static_cast<uint32_t>(p00);
+  hi = p11 + (p10 >> 32);
+}
+
 __device__ __forceinline__ void philox4x64_10(uint64_t& c0, uint64_t& c1, uint64_t& c2, uint64_t& c3, uint64_t k0,
                                               uint64_t k1) {
   constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
@@ -1197,8 +1210,9 @@ __device__ __forceinline__ void philox4x64_10(uint64_t& c0, uint64_t& c1, uint64
       k0 += W0;
       k1 += W1;
     }
-    const uint64_t lo0 = M0 * c0, hi0 = __umul64hi(M0, c0);
-    const uint64_t lo1 = M1 * c2, hi1 = __umul64hi(M1, c2);
+    uint64_t lo0, hi0, lo1, hi1;
+    mulhilo64(M0, c0, lo0, hi0);
+    mulhilo64(M1, c2, lo1, hi1);
     const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0;
     c1 = lo1;
@@ -1217,22 +1231,20 @@ __device__ __forceinline__ void sr_call(uint64_t call, uint32_t copy, uint64_t s
 }
 
 // E2M1 code of an already scaled value y, rounded stochastically with the 16-bit r16;
-// saturates at 6, keeps the sign, NaN -> +0
+// saturates at 6, keeps the sign, NaN -> +0.  Without branches: the magnitudes are
+// spaced w = 0.5 below 2, 1 in [2, 4) and 2 in [4, 6], so t = a / w (exact) has
+// floor(t) = the lower neighbour in units of w and t - floor(t) = (a - lo) / (hi - lo)
+// (exact); the code is floor(t) + up, plus 2 for each of the bounds 2 and 4 that a
+// passes (0.5 ... 2 are codes 1 ... 4; 3, 4 are codes 5, 6; 6 is code 7).
 __device__ __forceinline__ uint32_t e2m1_sr_code(float y, uint32_t r16) {
-  const float a = __builtin_fabsf(y);
-  if (!(a == a)) return 0u;
-  const uint32_t idx = static_cast<uint32_t>(a >= 0.5f) + static_cast<uint32_t>(a >= 1.0f) +
-                       static_cast<uint32_t>(a >= 1.5f) + static_cast<uint32_t>(a >= 2.0f) +
-                       static_cast<uint32_t>(a >= 3.0f) + static_cast<uint32_t>(a >= 4.0f) +
-                       static_cast<uint32_t>(a >= 6.0f);
-  uint32_t c = 7u;
-  if (idx < 7u) {
-    const float lo = idx <= 4u ? 0.5f * static_cast<float>(idx) : (idx == 5u ? 3.0f : 4.0f);
-    const float inv_w = idx < 4u ? 2.0f : (idx < 6u ? 1.0f : 0.5f);
-    const float p = __fmul_rn(__fsub_rn(a, lo), inv_w);  // exact
-    c = idx + static_cast<uint32_t>(static_cast<float>(r16) < __fmul_rn(p, 65536.0f));
-  }
-  return c | ((__float_as_uint(y) >> 31) << 3);
+  const float a = __builtin_fminf(__builtin_fabsf(y), 6.0f);
+  const bool ge2 = a >= 2.0f, ge4 = a >= 4.0f;
+  const float t = __fmul_rn(a, ge4 ? 0.5f : (ge2 ? 1.0f : 2.0f));
+  const float fl = __builtin_floorf(t);
+  const uint32_t up = static_cast<float>(r16) < __fmul_rn(__fsub_rn(t, fl), 65536.0f);
+  const uint32_t c = static_cast<uint32_t>(fl) + up + (ge2 ? 2u : 0u) + (ge4 ? 2u : 0u);
+  const uint32_t keep = 0u - static_cast<uint32_t>(y == y);  // all ones unless NaN
+  return (c | ((__float_as_uint(y) >> 31) << 3)) & keep;
 }
 
 // in place: v[0..15] <- fl32((1/4) H16 diag(s) v), fp64 butterflies
@@ -1253,6 +1265,13 @@ __device__ __forceinline__ void rht16(float* v, uint32_t sign_mask) {
   }
 #pragma unroll
   for (int j = 0; j < 16; ++j) v[j] = static_cast<float>(t[j] * 0.25);
+}
+
+// the value of the other lane of the pair (2k, 2k + 1)
+__device__ __forceinline__ uint64_t swap_lane_pairs64(uint64_t v) {
+  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(v)), 0xb1, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(static_cast<uint32_t>(v >> 32)), 0xb1, 0xf, 0xf, false);
+  return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
 }
 
 struct Mx4Recipe {
@@ -1305,6 +1324,8 @@ __global__ __launch_bounds__(kThreads) void k_mxfp4_recipe(const uint16_t* __res
   };
   auto process = [&](uint4 (&raw)[NP], int64_t r0, int64_t c0, bool has1, int64_t r1, int64_t c1) {
     if constexpr (COL) __syncthreads();
+    static_assert(NP % 2 == 0, "the stochastic-rounding row path pairs passes");
+    uint64_t nw0 = 0, nw1 = 0;  // stochastic rounding: this lane's words for the odd pass
 #pragma clang loop unroll(full)
     for (int p = 0; p < NP; ++p) {
       const int lr = p * RPP + prow;
@@ -1321,14 +1342,26 @@ __global__ __launch_bounds__(kThreads) void k_mxfp4_recipe(const uint16_t* __res
         unpack16<uint16_t>(raw[p], v);
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = __builtin_ldexpf(v[j], -e);
-        const int64_t i0 = r * C + c0 + pcol;  // row copy: element index of v[0]
         uint64_t w0 = 0, w1 = 0;
         if constexpr (SR) {
-          uint64_t a0 = static_cast<uint64_t>(i0 >> 4), a1 = 0, a2 = 0, a3 = 0;
-          philox4x64_10(a0, a1, a2, a3, rc.seed, 0);
-          const bool hi_half = (i0 & 15) != 0;  // lanes 8 .. 15 of the call: words 2, 3
-          w0 = hi_half ? a2 : a0;
-          w1 = hi_half ? a3 : a1;
+          // Lanes 2k and 2k + 1 hold the two halves (elements 0..7: words 0, 1; 8..15:
+          // words 2, 3) of one Philox call per pass, so each lane computes one call per
+          // two passes: the even lane the call of pass p, the odd lane that of pass p + 1,
+          // and each hands the other the two words it needs (a DPP swap of lane pairs).
+          if ((p & 1) == 0) {
+            const bool odd = lane & 1;
+            const int64_t rq = r0 + (p + (odd ? 1 : 0)) * RPP + prow;
+            uint64_t a0 = static_cast<uint64_t>((rq * C + c0 + pcol) >> 4), a1 = 0, a2 = 0, a3 = 0;
+            philox4x64_10(a0, a1, a2, a3, rc.seed, 0);
+            const uint64_t x0 = swap_lane_pairs64(odd ? a0 : a2), x1 = swap_lane_pairs64(odd ? a1 : a3);
+            w0 = odd ? x0 : a0;
+            w1 = odd ? x1 : a1;
+            nw0 = odd ? a2 : x0;
+            nw1 = odd ? a3 : x1;
+          } else {
+            w0 = nw0;
+            w1 = nw1;
+          }
         }
         *reinterpret_cast<uint32_t*>(out_row + r * (C / 2) + (c0 + pcol) / 2) = mx4_pack8<SR>(v, nan, w0, w1);
         const uint32_t code = nan ? 255u : static_cast<uint32_t>(e + 127);
@@ -1423,10 +1456,12 @@ __global__ __launch_bounds__(kThreads) void k_mxfp4_recipe(const uint16_t* __res
 
 // 2D block scaling of weights: one E8M0 scale per 32 x 32 sub-tile, the MXFP4 rule on
 // the sub-tile's amax; the row copy repeats it for each row's block and the column copy
-// (the transpose) for each column's block, so both copies hold the same codes.  The tile
+// (the transpose) for each column's block, so both copies hold the same codes.  ROW /
+// COL: which copies the launch writes.  The tile
 // goes through LDS; thread t finds the amax of sub-tile t / 16 over two of its rows per
 // lane group (16 lanes, xor-reduced), then quantizes like k_mxfp4_recipe's row and
 // column paths with the sub-tile exponents.
+template <bool ROW, bool COL>
 __global__ __launch_bounds__(kThreads) void k_mxfp4_2d(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                        uint8_t* __restrict__ out_row, uint8_t* __restrict__ scale_row,
                                                        uint8_t* __restrict__ out_col, uint8_t* __restrict__ scale_col) {
@@ -1471,7 +1506,7 @@ __global__ __launch_bounds__(kThreads) void k_mxfp4_2d(const uint16_t* __restric
     __syncthreads();
     // row copy: the lane's 8 elements of row lr, sub-tile (lr / 32, pcol / 32)
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
+    for (int p = 0; p < (ROW ? NP : 0); ++p) {
       const int lr = p * RPP + prow;
       const int st = (lr >> 5) * 4 + (pcol >> 5);
       const bool nan = sub_m[st] > 0x7f80u;
@@ -1492,6 +1527,7 @@ __global__ __launch_bounds__(kThreads) void k_mxfp4_2d(const uint16_t* __restric
         *scale_dw(scale_row, r, C, c0) = dw;
       }
     }
+    if constexpr (!COL) continue;
     // column copy: columns 2cp, 2cp + 1 over rows 32 blk .. + 31 (sub-tile (blk, cp / 16))
     const int cp = t & 63, blk = t >> 6;
     const int st = blk * 4 + (cp >> 4);
@@ -1853,8 +1889,9 @@ hipError_t launch_mxfp4_recipe(const void* x, int64_t rows, int64_t cols, int rh
   if (rows == 0 || cols == 0) return hipSuccess;
   const auto* xx = static_cast<const uint16_t*>(x);
   if (two_d) {
-    const int g = persistent_grid(reinterpret_cast<const void*>(k_mxfp4_2d), (rows / kCT) * (cols / kCT), 1, kCapMxCol);
-    hipLaunchKernelGGL(k_mxfp4_2d, dim3(g), dim3(kThreads), 0, s, xx, rows, cols, out_row, scale_row, out_col, scale_col);
+    const auto fn = out_row ? (out_col ? k_mxfp4_2d<true, true> : k_mxfp4_2d<true, false>) : k_mxfp4_2d<false, true>;
+    const int g = persistent_grid(reinterpret_cast<const void*>(fn), (rows / kCT) * (cols / kCT), 1, kCapMxCol);
+    hipLaunchKernelGGL(fn, dim3(g), dim3(kThreads), 0, s, xx, rows, cols, out_row, scale_row, out_col, scale_col);
     return hipGetLastError();
   }
   const Mx4Recipe rc{sign_mask, seed};

@@ -480,13 +480,14 @@ te_status te_mxfp4_quantize_panel(const void* x, int x_dtype, int64_t rows, int6
  *                in the copy written) is 16-bit lane i % 16 of Philox4x64-10 with counter
  *                (i / 16, copy, 0, 0), copy 0 row-wise / 1 column-wise, key (sr_seed, 0);
  *                lane l = bits 16 (l % 4) .. of output word l / 4.
- *              TE_MX4_2D: one scale per 32 x 32 tile (weights); both copies are written
- *                and the column-wise copy is the transpose of the row-wise one (same
- *                codes); excludes RHT and SR.
+ *              TE_MX4_2D: one scale per 32 x 32 tile (weights); the column-wise copy
+ *                is the transpose of the row-wise one (same codes), so a call that
+ *                writes one copy (Fprop: row-wise; Dgrad: column-wise) and a call
+ *                that writes the other agree; excludes RHT and SR.
  *   x          [rows, cols] TE_BF16, rows % 128 == 0 and cols % 128 == 0
  *              (TE_ERR_UNSUPPORTED otherwise).
  *   out_row / scale_row, out_col / scale_col  as te_mxfp4_quantize_panel; either pair
- *              may be NULL (TE_MX4_RHT needs the column pair, TE_MX4_2D both).
+ *              may be NULL, not both (TE_MX4_RHT needs the column pair).
  */
 enum { TE_MX4_RHT = 1, TE_MX4_SR = 2, TE_MX4_2D = 4 };
 te_status te_mxfp4_quantize_recipe(const void* x, int x_dtype, int64_t rows, int64_t cols, int flags,

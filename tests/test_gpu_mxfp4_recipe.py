@@ -117,6 +117,13 @@ def test_2d_weight_blocks_bit_exact(shape):
     np.testing.assert_array_equal(got["row"][0], qr)
     np.testing.assert_array_equal(got["col"][1], ec)
     np.testing.assert_array_equal(got["col"][0], qc)
+    # one copy per call (Fprop takes the row-wise copy, Dgrad the column-wise one)
+    row_only = _run(bits, TWO_D, col=False)
+    col_only = _run(bits, TWO_D, row=False)
+    np.testing.assert_array_equal(row_only["row"][0], qr)
+    np.testing.assert_array_equal(row_only["row"][1], er)
+    np.testing.assert_array_equal(col_only["col"][0], qc)
+    np.testing.assert_array_equal(col_only["col"][1], ec)
 
 
 def test_recipe_full_5b_gradient_sampled_columns():
@@ -181,15 +188,16 @@ def test_wgrad_of_transformed_operands():
     (dict(flags=TWO_D | SR), B.TE_ERR_ARG),
     (dict(flags=8), B.TE_ERR_ARG),
     (dict(flags=RHT, col=False), B.TE_ERR_ARG),
-    (dict(flags=TWO_D, col=False), B.TE_ERR_NULL),
+    (dict(flags=TWO_D, col=False, row=False), B.TE_ERR_NULL),
     (dict(flags=SR, shape=(128, 96)), B.TE_ERR_UNSUPPORTED),
 ])
 def test_recipe_rejections(kw, status):
     shape = kw.pop("shape", (128, 128))
     col = kw.pop("col", True)
+    row = kw.pop("row", True)
     R, C = shape
     x = torch.zeros(shape, dtype=torch.bfloat16, device=DEV)
-    orow, srow = _u8(R, C // 2), _u8(max(B.te_mx_scale_panel_bytes(R, C), 16))
+    orow, srow = (_u8(R, C // 2), _u8(max(B.te_mx_scale_panel_bytes(R, C), 16))) if row else (None, None)
     ocol, scol = (_u8(C, R // 2), _u8(max(B.te_mx_scale_panel_bytes(C, R), 16))) if col else (None, None)
     with pytest.raises(B.TEError) as ei:
         B.te_mxfp4_quantize_recipe(x, kw["flags"], orow, srow, ocol, scol)
