@@ -68,6 +68,7 @@ _SIGNATURES = {
                          _vp, _vp],
     "te_fp8_gemm_accumulate": [_vp, _i32, _vp, _vp, _i32, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp, _vp],
     "te_mxfp8_quantize": [_vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp],
+    "te_mxfp8_quantize_dbias": [_vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp],
     "te_mxfp4_quantize": [_vp, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
     "te_mxfp8_quantize_panel": [_vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp],
     "te_fp8_gemm_splitk": [_vp, _i32, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _vp, _i32, _vp, _i32, _i32, _vp, _i64,
@@ -100,6 +101,8 @@ def lib() -> ctypes.CDLL:
             L.te_gemm_variant.argtypes = []
             L.te_cast_transpose_dbias_workspace_bytes.restype = ctypes.c_int64
             L.te_cast_transpose_dbias_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
+            L.te_mxfp8_quantize_dbias_workspace_bytes.restype = ctypes.c_int64
+            L.te_mxfp8_quantize_dbias_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
             L.te_mx_scale_panel_bytes.restype = ctypes.c_int64
             L.te_mx_scale_panel_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
             L.te_fp8_gemm_splitk_workspace_bytes.restype = ctypes.c_int64
@@ -369,6 +372,29 @@ def te_mxfp8_quantize(x, elem_dtype, out_row=None, scale_row=None, out_col=None,
     rows, cols = _2d(x)
     _check(lib().te_mxfp8_quantize(_ptr(x), _hp_code(x), rows, cols, _fp8_code(elem_dtype), _ptr(out_row),
                                    _ptr(scale_row), _ptr(out_col), _ptr(scale_col), _stream(stream)))
+
+
+def te_mxfp8_quantize_dbias_workspace_bytes(rows, cols) -> int:
+    return int(lib().te_mxfp8_quantize_dbias_workspace_bytes(int(rows), int(cols)))
+
+
+def mx_dbias_workspace(rows, cols, device=None) -> torch.Tensor:
+    """A new workspace for te_mxfp8_quantize_dbias of [rows, cols] (no initial contents needed)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    return torch.empty(max(te_mxfp8_quantize_dbias_workspace_bytes(rows, cols), 16), dtype=torch.uint8, device=dev)
+
+
+def te_mxfp8_quantize_dbias(x, elem_dtype, dbias, workspace, out_row=None, scale_row=None, out_col=None,
+                            scale_col=None, stream=None):
+    """te_mxfp8_quantize plus dbias[c] = sum_r x[r, c] (fp32) from the same pass."""
+    for n, t in (("x", x), ("out_row", out_row), ("scale_row", scale_row), ("out_col", out_col),
+                 ("scale_col", scale_col), ("dbias", dbias), ("workspace", workspace)):
+        _need(t, n)
+    rows, cols = _2d(x)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().te_mxfp8_quantize_dbias(_ptr(x), _hp_code(x), rows, cols, _fp8_code(elem_dtype), _ptr(out_row),
+                                         _ptr(scale_row), _ptr(out_col), _ptr(scale_col), _ptr(dbias),
+                                         _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def te_mxfp4_quantize(x, out_row=None, scale_row=None, out_col=None, scale_col=None, stream=None):

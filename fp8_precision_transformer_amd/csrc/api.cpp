@@ -415,14 +415,15 @@ te_status te_fp8_gemm_accumulate(const void* a, int a_dtype, const void* a_scale
                    stream);
 }
 
-te_status te_mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int elem_dtype,
-                            uint8_t* out_row, uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col,
-                            void* stream) {
+namespace {
+te_status check_mxfp8_args(const void* x, int x_dtype, int64_t rows, int64_t cols, int elem_dtype,
+                           const uint8_t* out_row, const uint8_t* scale_row, const uint8_t* out_col,
+                           const uint8_t* scale_col) {
   if (rows < 0 || cols < 0) return fail(TE_ERR_SHAPE, "negative shape");
   if (!is_hp(x_dtype)) return fail(TE_ERR_DTYPE, "x_dtype must be TE_F32 or TE_BF16");
   if (!is_fp8(elem_dtype)) return fail(TE_ERR_DTYPE, "elem_dtype must be TE_E4M3 or TE_E5M2");
   const bool row = out_row || scale_row, col = out_col || scale_col;
-  if (!row && !col) return fail(TE_ERR_NULL, "both output pairs are NULL");
+  if (!row && !col && rows * cols > 0) return fail(TE_ERR_NULL, "both output pairs are NULL");
   if ((out_row == nullptr) != (scale_row == nullptr)) return fail(TE_ERR_NULL, "out_row and scale_row go together");
   if ((out_col == nullptr) != (scale_col == nullptr)) return fail(TE_ERR_NULL, "out_col and scale_col go together");
   if (row && cols % 32 != 0) return fail(TE_ERR_SHAPE, "row-wise MXFP8 needs cols %% 32 == 0");
@@ -431,13 +432,45 @@ te_status te_mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t co
   if ((x && !aligned16(x)) || (out_row && !aligned16(out_row)) || (out_col && !aligned16(out_col)))
     return fail(TE_ERR_ALIGN, "x and outputs must be 16-byte aligned");
   if ((rows + 127) / 128 > 65535) return fail(TE_ERR_SHAPE, "rows too large for the tile grid");
-  te_status st = check_device();
+  return TE_OK;
+}
+}  // namespace
+
+te_status te_mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int elem_dtype,
+                            uint8_t* out_row, uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col,
+                            void* stream) {
+  te_status st = check_mxfp8_args(x, x_dtype, rows, cols, elem_dtype, out_row, scale_row, out_col, scale_col);
   if (st != TE_OK) return st;
+  if ((st = check_device()) != TE_OK) return st;
+  const bool row = out_row != nullptr, col = out_col != nullptr;
   log_dispatch("te_mxfp8_quantize", row && col ? "tile128x64_row+col" : (row ? "tile128x64_row" : "tile128x64_col"),
                elem_dtype == TE_E5M2 ? "E5M2" : "E4M3");
   return hip_status(te::launch_mxfp8_quantize(x, x_dtype, rows, cols, elem_dtype == TE_E5M2, out_row, scale_row,
                                               out_col, scale_col, static_cast<hipStream_t>(stream)),
                     "te_mxfp8_quantize launch");
+}
+
+int64_t te_mxfp8_quantize_dbias_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return -1;
+  return (rows + 127) / 128 * cols * static_cast<int64_t>(sizeof(float));
+}
+
+te_status te_mxfp8_quantize_dbias(const void* x, int x_dtype, int64_t rows, int64_t cols, int elem_dtype,
+                                  uint8_t* out_row, uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col,
+                                  float* dbias, void* workspace, int64_t workspace_bytes, void* stream) {
+  te_status st = check_mxfp8_args(x, x_dtype, rows, cols, elem_dtype, out_row, scale_row, out_col, scale_col);
+  if (st != TE_OK) return st;
+  if (cols > 0 && !dbias) return fail(TE_ERR_NULL, "dbias is NULL");
+  const int64_t need = te_mxfp8_quantize_dbias_workspace_bytes(rows, cols);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(TE_ERR_ARG, "workspace of %lld bytes needed (got %lld)", (long long)need, (long long)workspace_bytes);
+  if (workspace && !aligned16(workspace)) return fail(TE_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if ((st = check_device()) != TE_OK) return st;
+  log_dispatch("te_mxfp8_quantize_dbias", "tile_colsum", elem_dtype == TE_E5M2 ? "E5M2" : "E4M3");
+  return hip_status(te::launch_mxfp8_quantize(x, x_dtype, rows, cols, elem_dtype == TE_E5M2, out_row, scale_row,
+                                              out_col, scale_col, static_cast<hipStream_t>(stream), dbias,
+                                              static_cast<float*>(workspace)),
+                    "te_mxfp8_quantize_dbias launch");
 }
 
 te_status te_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* out_row,

@@ -38,9 +38,12 @@ hipError_t launch_layernorm_fp8(const void* x, int x_dtype, int64_t rows, int64_
 hipError_t launch_scale_update(float* hist, float* scale, float* scale_inv, int n, int hist_len,
                                int e5m2, int most_recent, int margin, hipStream_t s);
 
+// dbias != nullptr: also the bias gradient dbias[c] = sum_r x[r, c] from the same pass,
+// through fp32 tile partials in part [ceil(rows / 128), cols]
 hipError_t launch_mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols,
                                  int e5m2, uint8_t* out_row, uint8_t* scale_row,
-                                 uint8_t* out_col, uint8_t* scale_col, hipStream_t s);
+                                 uint8_t* out_col, uint8_t* scale_col, hipStream_t s,
+                                 float* dbias = nullptr, float* part = nullptr);
 hipError_t launch_mx_quantize_panel(const void* x, int64_t rows, int64_t cols, int fp4, int e5m2,
                                     uint8_t* out_row, uint8_t* scale_row, uint8_t* out_col, uint8_t* scale_col,
                                     hipStream_t s);

@@ -719,12 +719,13 @@ __device__ __forceinline__ bool rows_vec_ok(int64_t cols) {
   return (cols % (16 / sizeof(T))) == 0;  // every row starts 16-byte aligned
 }
 
-template <typename T, bool E5M2>
+template <typename T, bool E5M2, bool DBIAS = false>
 __global__ __launch_bounds__(kThreads) void k_mxfp8(const T* __restrict__ x, int64_t R, int64_t C,
                                                     uint8_t* __restrict__ out_row,
                                                     uint8_t* __restrict__ scale_row,
                                                     uint8_t* __restrict__ out_col,
-                                                    uint8_t* __restrict__ scale_col) {
+                                                    uint8_t* __restrict__ scale_col,
+                                                    float* __restrict__ dbias_part) {
   __shared__ float tile[kTR * kMxPitch];
   const int64_t r0 = static_cast<int64_t>(blockIdx.y) * kTR;
   const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kTC;
@@ -755,10 +756,29 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8(const T* __restrict__ x, int
     o[1] = make_uint4(q[4], q[5], q[6], q[7]);
     scale_row[r * (C / 32) + (c0 + lc) / 32] = code;
   }
-  if (out_col != nullptr) {
+  if (out_col != nullptr || DBIAS) {
 #pragma unroll
     for (int j = 0; j < 32; ++j) tile[lr * kMxPitch + lc + j] = v[j];
     __syncthreads();
+  }
+  if constexpr (DBIAS) {
+    // the tile's column sums in the order of the cast-transpose pass over the same
+    // input type: rows g, g + G, ... summed for each g < G (G = its rows per pass),
+    // then the G group sums in order (rows past R read 0)
+    constexpr int G = CTMap<T>::RPP, NQ = CTMap<T>::NP;
+    static_assert(G * NQ == kTR, "a tile row group per pass");
+    if (t < kTC && c0 + t < C) {
+      float acc = 0.0f;
+      for (int g = 0; g < G; ++g) {
+        float sg = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) sg = __fadd_rn(sg, tile[(G * q + g) * kMxPitch + t]);
+        acc = __fadd_rn(acc, sg);
+      }
+      dbias_part[static_cast<int64_t>(blockIdx.y) * C + c0 + t] = acc;
+    }
+  }
+  if (out_col != nullptr) {
     const int oc = t & 63, seg = t >> 6;
     const int64_t c = c0 + oc;
     const int64_t rb = r0 + seg * 32;
@@ -979,12 +999,15 @@ __device__ __forceinline__ void mx_quant8_scaled(const uint4& raw, int e, uint32
 // PANEL: the E8M0 scales go out in the GEMM's panel layout: the dword of row r and
 // 128-element group g is dword ((r / 256) * G + g) * 256 + r % 256 (G = groups per row),
 // so a tile's 128 row dwords are 512 contiguous bytes instead of 128 scattered ones.
-template <bool E5M2, bool ROW, bool COL, bool FP4 = false, bool PANEL = false>
+// DBIAS: also the per-tile column sums of x (the bias gradient's partials, summed in the
+// cast-transpose pass's order) into dbias_part [R / 128, C].
+template <bool E5M2, bool ROW, bool COL, bool FP4 = false, bool PANEL = false, bool DBIAS = false>
 __global__ __launch_bounds__(kThreads) void k_mxfp8_tiles(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                                           uint8_t* __restrict__ out_row,
                                                           uint8_t* __restrict__ scale_row,
                                                           uint8_t* __restrict__ out_col,
-                                                          uint8_t* __restrict__ scale_col) {
+                                                          uint8_t* __restrict__ scale_col,
+                                                          float* __restrict__ dbias_part) {
   // the scale dword of (row r of a copy with `cols` elements per row, group of c0)
   auto scale_dw = [](uint8_t* base, int64_t r, int64_t cols, int64_t c0) {
     if constexpr (PANEL)
@@ -993,7 +1016,9 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_tiles(const uint16_t* __rest
       return reinterpret_cast<uint32_t*>(base + r * (cols / 32) + c0 / 32);
   };
   constexpr int NP = 8, RPP = 16;  // passes of 16 rows, 16 lanes x 8 elements per row
+  static_assert(NP == CTMap<uint16_t>::NP && RPP == CTMap<uint16_t>::RPP, "the cast-transpose pass's order");
   __shared__ __attribute__((aligned(16))) uint8_t tile[COL ? kCT * kMxTPitch : 16];
+  __shared__ float red[DBIAS ? RPP * kCT : 1];
   const int64_t ntc = C / kCT;
   const int64_t ntiles = ntc * (R / kCT);
   const int t = threadIdx.x, lane = t & 63;
@@ -1013,11 +1038,20 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_tiles(const uint16_t* __rest
   // pass by pass without the column copy, after all passes with it (the column work
   // then runs with the next tile's loads in flight).
   auto process = [&](uint4 (&raw)[NP], int64_t r0, int64_t c0, bool has1, int64_t r1, int64_t c1) {
-    if constexpr (COL) __syncthreads();  // the previous tile's LDS reads are done
+    if constexpr (COL || DBIAS) __syncthreads();  // the previous tile's LDS reads are done
+    float cs[8];  // DBIAS: this lane's column sums over its rows of the tile
+#pragma unroll
+    for (int j = 0; j < 8; ++j) cs[j] = 0.0f;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const int lr = p * RPP + prow;
       if constexpr (COL) *reinterpret_cast<uint4*>(tile + lr * kMxTPitch + pcol * 2) = raw[p];
+      if constexpr (DBIAS) {
+        float v[8];
+        unpack16<uint16_t>(raw[p], v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cs[j] = __fadd_rn(cs[j], v[j]);
+      }
       if constexpr (ROW) {
         uint32_t m = absmax_bits<uint16_t>(0u, raw[p]);
         m = max(m & 0xffffu, m >> 16);
@@ -1057,6 +1091,17 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_tiles(const uint16_t* __rest
       if (has1) {
 #pragma unroll
         for (int p = 0; p < NP; ++p) raw[p] = load1(p, r1, c1);
+      }
+    }
+    if constexpr (DBIAS) {  // one partial per (tile row, column): lane groups in order
+#pragma unroll
+      for (int j = 0; j < 8; ++j) red[prow * kCT + pcol + j] = cs[j];
+      __syncthreads();
+      if (t < kCT) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int g = 0; g < RPP; ++g) acc = __fadd_rn(acc, red[g * kCT + t]);
+        dbias_part[(r0 / kCT) * C + c0 + t] = acc;
       }
     }
     if constexpr (COL) {
@@ -1677,17 +1722,19 @@ hipError_t cast_transpose_t(const T* x, int64_t R, int64_t C, int mode, int marg
   return hipGetLastError();
 }
 
-template <bool E5M2, bool ROW, bool COL, bool FP4 = false, bool PANEL = false>
+template <bool E5M2, bool ROW, bool COL, bool FP4 = false, bool PANEL = false, bool DBIAS = false>
 void mx_tiles_launch(const uint16_t* x, int64_t R, int64_t C, uint8_t* out_row, uint8_t* scale_row,
-                     uint8_t* out_col, uint8_t* scale_col, hipStream_t st) {
-  const auto fn = k_mxfp8_tiles<E5M2, ROW, COL, FP4, PANEL>;
+                     uint8_t* out_col, uint8_t* scale_col, hipStream_t st, float* part = nullptr) {
+  const auto fn = k_mxfp8_tiles<E5M2, ROW, COL, FP4, PANEL, DBIAS>;
   const int g = persistent_grid(reinterpret_cast<const void*>(fn), (R / kCT) * (C / kCT), 1, COL ? kCapMxCol : kCapMxRow);
-  hipLaunchKernelGGL(fn, dim3(g), dim3(kThreads), 0, st, x, R, C, out_row, scale_row, out_col, scale_col);
+  hipLaunchKernelGGL(fn, dim3(g), dim3(kThreads), 0, st, x, R, C, out_row, scale_row, out_col, scale_col, part);
 }
 
+// part != nullptr: the bias gradient's per-tile column sums go to part [ceil(R / 128), C]
+// (the caller reduces them)
 template <typename T, bool E5M2>
 hipError_t mxfp8_t(const T* x, int64_t R, int64_t C, uint8_t* out_row, uint8_t* scale_row,
-                   uint8_t* out_col, uint8_t* scale_col, hipStream_t st) {
+                   uint8_t* out_col, uint8_t* scale_col, hipStream_t st, float* part = nullptr) {
   if (R == 0 || C == 0) return hipSuccess;
   // bf16 matrices of whole 128 x 128 tiles take the persistent tile kernel (32-bit
   // offsets inside a tile; the row-wise codes go out as dwords)
@@ -1696,15 +1743,25 @@ hipError_t mxfp8_t(const T* x, int64_t R, int64_t C, uint8_t* out_row, uint8_t* 
     if (R % kCT == 0 && C % kCT == 0 && C * kCT * 2 < (int64_t{1} << 31) && R * kCT < (int64_t{1} << 31) &&
         (!row || (reinterpret_cast<uintptr_t>(scale_row) & 3u) == 0) &&
         (!col || (reinterpret_cast<uintptr_t>(scale_col) & 3u) == 0)) {
-      if (row && col) mx_tiles_launch<E5M2, true, true>(x, R, C, out_row, scale_row, out_col, scale_col, st);
-      else if (row) mx_tiles_launch<E5M2, true, false>(x, R, C, out_row, scale_row, out_col, scale_col, st);
-      else mx_tiles_launch<E5M2, false, true>(x, R, C, out_row, scale_row, out_col, scale_col, st);
+      if (part) {
+        if (row && col) mx_tiles_launch<E5M2, true, true, false, false, true>(x, R, C, out_row, scale_row, out_col, scale_col, st, part);
+        else if (row) mx_tiles_launch<E5M2, true, false, false, false, true>(x, R, C, out_row, scale_row, out_col, scale_col, st, part);
+        else mx_tiles_launch<E5M2, false, true, false, false, true>(x, R, C, out_row, scale_row, out_col, scale_col, st, part);
+      } else {
+        if (row && col) mx_tiles_launch<E5M2, true, true>(x, R, C, out_row, scale_row, out_col, scale_col, st);
+        else if (row) mx_tiles_launch<E5M2, true, false>(x, R, C, out_row, scale_row, out_col, scale_col, st);
+        else mx_tiles_launch<E5M2, false, true>(x, R, C, out_row, scale_row, out_col, scale_col, st);
+      }
       return hipGetLastError();
     }
   }
   const dim3 grid(static_cast<unsigned>((C + kTC - 1) / kTC), static_cast<unsigned>((R + kTR - 1) / kTR));
-  hipLaunchKernelGGL((k_mxfp8<T, E5M2>), grid, dim3(kThreads), 0, st, x, R, C, out_row, scale_row,
-                     out_col, scale_col);
+  if (part)
+    hipLaunchKernelGGL((k_mxfp8<T, E5M2, true>), grid, dim3(kThreads), 0, st, x, R, C, out_row, scale_row, out_col,
+                       scale_col, part);
+  else
+    hipLaunchKernelGGL((k_mxfp8<T, E5M2>), grid, dim3(kThreads), 0, st, x, R, C, out_row, scale_row, out_col,
+                       scale_col, nullptr);
   return hipGetLastError();
 }
 
@@ -1821,12 +1878,19 @@ hipError_t launch_scale_update(float* hist, float* scale, float* scale_inv, int 
 
 hipError_t launch_mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int e5m2,
                                  uint8_t* out_row, uint8_t* scale_row, uint8_t* out_col,
-                                 uint8_t* scale_col, hipStream_t s) {
+                                 uint8_t* scale_col, hipStream_t s, float* dbias, float* part) {
+  hipError_t e;
   if (x_dtype == BF16)
-    return e5m2 ? mxfp8_t<uint16_t, true>(static_cast<const uint16_t*>(x), rows, cols, out_row, scale_row, out_col, scale_col, s)
-                : mxfp8_t<uint16_t, false>(static_cast<const uint16_t*>(x), rows, cols, out_row, scale_row, out_col, scale_col, s);
-  return e5m2 ? mxfp8_t<float, true>(static_cast<const float*>(x), rows, cols, out_row, scale_row, out_col, scale_col, s)
-              : mxfp8_t<float, false>(static_cast<const float*>(x), rows, cols, out_row, scale_row, out_col, scale_col, s);
+    e = e5m2 ? mxfp8_t<uint16_t, true>(static_cast<const uint16_t*>(x), rows, cols, out_row, scale_row, out_col, scale_col, s, part)
+             : mxfp8_t<uint16_t, false>(static_cast<const uint16_t*>(x), rows, cols, out_row, scale_row, out_col, scale_col, s, part);
+  else
+    e = e5m2 ? mxfp8_t<float, true>(static_cast<const float*>(x), rows, cols, out_row, scale_row, out_col, scale_col, s, part)
+             : mxfp8_t<float, false>(static_cast<const float*>(x), rows, cols, out_row, scale_row, out_col, scale_col, s, part);
+  if (e != hipSuccess || dbias == nullptr || cols == 0) return e;
+  // the bias gradient: the tile partials added over tile rows in order (an empty x: zeros)
+  hipLaunchKernelGGL(k_dbias_reduce, dim3(static_cast<unsigned>((cols + kDbCols - 1) / kDbCols)), dim3(256), 0, s,
+                     part, (rows + kCT - 1) / kCT, cols, dbias);
+  return hipGetLastError();
 }
 
 hipError_t launch_mxfp4_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* out_row,

@@ -213,9 +213,11 @@ class _FP8LinearFn(torch.autograd.Function):
             # M, the k of Wgrad)
             dyq, dys = _f8((M, N), dev), _f8((M, N // 32), dev)
             dyqT, dysT = _f8((N, M), dev), _f8((N, M // 32), dev)
-            if ctx.has_bias:
-                db = _column_sums(dy, dyq)  # its codes are overwritten just below
-            B.te_mxfp8_quantize(dy, bwd, dyq, dys, dyqT, dysT)
+            if ctx.has_bias:  # bias gradient from the same pass over dY
+                db = torch.empty(N, dtype=torch.float32, device=dev)
+                B.te_mxfp8_quantize_dbias(dy, bwd, db, B.mx_dbias_workspace(M, N, dev), dyq, dys, dyqT, dysT)
+            else:
+                B.te_mxfp8_quantize(dy, bwd, dyq, dys, dyqT, dysT)
             dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
             B.te_fp8_gemm(dyq, bwd, dys, wqT, fwd, wsT, dx, gran=B.TE_GRAN_MX_BLOCK32)      # Dgrad
             dw = torch.empty((N, K), dtype=torch.float32, device=dev)
@@ -239,20 +241,6 @@ class _FP8LinearFn(torch.autograd.Function):
         if isinstance(recipe, DelayedScaling):
             module._fp8[_recipe_key(recipe)]["pool"].bwd_pending = True
         return dx.to(ctx.x_dtype), dw.to(ctx.w_dtype), db, None, None, None
-
-
-def _column_sums(dy, codes):
-    """db[c] = sum_r dY[r, c] in fp32 by the library's dbias pass; the unit-scale E4M3
-    codes it also writes go to `codes` [M, N] and are not used (MXFP8 quantizes dY
-    itself)."""
-    M, N = dy.shape
-    dev = dy.device
-    one = torch.ones(1, dtype=torch.float32, device=dev)
-    si, am = torch.empty(1, dtype=torch.float32, device=dev), torch.empty(1, dtype=torch.float32, device=dev)
-    db = torch.empty(N, dtype=torch.float32, device=dev)
-    ws = B.dbias_workspace(M, N, dev)
-    B.te_cast_transpose_dbias(dy, "E4M3", B.TE_SCALE_DELAYED, 0, one, si, am, db, ws, codes, None)
-    return db
 
 
 def _recipe_key(recipe):

@@ -376,12 +376,40 @@ te_status te_fp8_gemm_accumulate(const void* a, int a_dtype, const void* a_scale
  *   out_col    [cols, rows] uint8 = MXFP8 of x^T (blocks along rows, an
  *              independent quantization, not a transpose of out_row);
  *              scale_col [cols, rows/32] E8M0.
- * Either pair may be NULL (not both).  Row pair needs cols % 32 == 0; col pair
- * needs rows % 32 == 0.
+ * Either pair may be NULL (not both, unless x is empty).  Row pair needs
+ * cols % 32 == 0; col pair needs rows % 32 == 0.
  */
 te_status te_mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols,
                             int elem_dtype, uint8_t* out_row, uint8_t* scale_row,
                             uint8_t* out_col, uint8_t* scale_col, void* stream);
+
+/*
+ * te_mxfp8_quantize_dbias -- te_mxfp8_quantize of dY that also returns its bias
+ * gradient, read in the same pass over dY (the MXFP8 recipe's backward of a linear
+ * layer with a bias).
+ *
+ * Defines: the backward of te.Linear(..., bias=True) ([FP8-intro] "Transformer
+ * Engine の使い方") under the MXFP8 recipe ([TE-summary] "主な機能"): db[c] =
+ * sum over rows r of x[r, c].
+ *
+ *   dbias      [cols] fp32, written: the sum in fp32 in the order of
+ *              te_cast_transpose_dbias over the same input type (within each
+ *              128-row tile, rows g, g + G, ... for each g < G, then the G group
+ *              sums; then over tiles in row order), so both calls give the same bits
+ *              and a run is reproducible.  NULL only if cols == 0.
+ *   workspace  te_mxfp8_quantize_dbias_workspace_bytes(rows, cols) bytes of device
+ *              memory, 16-byte aligned, owned by the caller: ceil(rows / 128) * cols
+ *              fp32 partial sums, overwritten by every call (no initial contents
+ *              needed).  Calls that may overlap need one workspace each.
+ *   workspace_bytes  its size; TE_ERR_ARG if smaller than needed.
+ * Every other argument, shape rule and error as te_mxfp8_quantize; rows == 0 gives
+ * dbias = 0.
+ */
+int64_t te_mxfp8_quantize_dbias_workspace_bytes(int64_t rows, int64_t cols);
+te_status te_mxfp8_quantize_dbias(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                                  int elem_dtype, uint8_t* out_row, uint8_t* scale_row,
+                                  uint8_t* out_col, uint8_t* scale_col, float* dbias,
+                                  void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * te_mxfp4_quantize -- MXFP4 block quantization (E2M1 elements, E8M0 per 32),

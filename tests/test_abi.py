@@ -186,6 +186,33 @@ def test_mxfp8_validation(kw, status):
 
 
 @needs_lib
+@pytest.mark.parametrize("kw,status", [
+    (dict(cols=48), B.TE_ERR_SHAPE),
+    (dict(scale_row=None), B.TE_ERR_NULL),
+    (dict(dbias=None), B.TE_ERR_NULL),
+    (dict(workspace=None), B.TE_ERR_ARG),
+    (dict(workspace_bytes=64 * 4 - 4), B.TE_ERR_ARG),
+    (dict(elem_dtype=B.TE_E8M0), B.TE_ERR_DTYPE),
+])
+def test_mxfp8_dbias_validation(kw, status):
+    """te_mxfp8_quantize_dbias checks te_mxfp8_quantize's rules, then the bias gradient
+    and its workspace (one fp32 partial per 128-row tile and column), on the host."""
+    args = dict(x=FAKE, x_dtype=B.TE_BF16, rows=64, cols=64, elem_dtype=B.TE_E4M3, out_row=FAKE,
+                scale_row=FAKE, out_col=FAKE, scale_col=FAKE, dbias=FAKE, workspace=FAKE, workspace_bytes=64 * 4,
+                stream=None)
+    args.update(kw)
+    assert B.lib().te_mxfp8_quantize_dbias(*args.values()) == status
+
+
+@needs_lib
+def test_mxfp8_dbias_workspace_bytes():
+    assert B.te_mxfp8_quantize_dbias_workspace_bytes(128, 16) == 16 * 4
+    assert B.te_mxfp8_quantize_dbias_workspace_bytes(129, 16) == 2 * 16 * 4
+    assert B.te_mxfp8_quantize_dbias_workspace_bytes(0, 16) == 0
+    assert B.te_mxfp8_quantize_dbias_workspace_bytes(-1, 16) == -1
+
+
+@needs_lib
 def test_noalloc_dbias_rejects_shapes_above_its_scratch_before_any_launch():
     """Validation on the host: a shape whose partial sums exceed the static scratch is
     TE_ERR_SHAPE before any device call."""

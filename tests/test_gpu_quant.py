@@ -451,6 +451,65 @@ def test_cast_transpose_dbias_rejects_small_workspace():
                                   empty_f32(128), ws, None, col)
 
 
+# te_mxfp8_quantize_dbias: the MXFP8 recipe's backward takes the bias gradient from the
+# pass that quantizes dY.  Whole 128 x 128 bf16 tiles (the tile kernel), a ragged shape
+# and fp32 input (the 128 x 64 kernel); E4M3 and E5M2; both copies or one.
+@pytest.mark.parametrize("shape,xdt", [((256, 384), "bf16"), ((384, 1024), "bf16"), ((224, 96), "bf16"),
+                                       ((288, 160), "f32"), ((256, 256), "f32")], ids=str)
+@pytest.mark.parametrize("fmt", ["E4M3", "E5M2"])
+@pytest.mark.parametrize("which", ["both", "row", "col"])
+def test_mxfp8_quantize_dbias(shape, xdt, fmt, which):
+    """Codes and scales exactly te_mxfp8_quantize's (and the oracle's); dbias within the
+    fp32 summation bound of the oracle's float64 sum and bit-identical to
+    te_cast_transpose_dbias's (the same summation order) on the same input."""
+    f = FMTS[fmt]
+    R, C = shape
+    x32 = synth.grads(shape, 9, R * 7 + C, 3, 0)
+    xd, xh = input_pair(x32, xdt)
+    row, col = which != "col", which != "row"
+    u8 = lambda *sh: torch.empty(sh, dtype=torch.uint8, device=DEV)  # noqa: E731
+    orow, srow = (u8(R, C), u8(R, C // 32)) if row else (None, None)
+    ocol, scol = (u8(C, R), u8(C, R // 32)) if col else (None, None)
+    assert B.te_mxfp8_quantize_dbias_workspace_bytes(R, C) == -(-R // 128) * C * 4
+    ws = torch.full((B.te_mxfp8_quantize_dbias_workspace_bytes(R, C) // 4,), float("nan"), dtype=torch.float32,
+                    device=DEV)  # no initial contents needed
+    db = empty_f32(C)
+    B.te_mxfp8_quantize_dbias(xd, fmt, db, ws, orow, srow, ocol, scol)
+    if row:
+        q, e = O.mxfp8_quantize(xh, f)
+        np.testing.assert_array_equal(host(orow), q)
+        np.testing.assert_array_equal(host(srow), e)
+    if col:
+        q, e = O.mxfp8_quantize(np.ascontiguousarray(xh.T), f)
+        np.testing.assert_array_equal(host(ocol), q)
+        np.testing.assert_array_equal(host(scol), e)
+    ref = O.bias_grad(xh)
+    bound = R * 2.0 ** -24 * np.abs(xh.astype(np.float64)).sum(axis=0)
+    got = host(db).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= bound), float(np.max(np.abs(got - ref) - bound))
+    db2 = empty_f32(C)
+    B.te_cast_transpose_dbias(xd, "E5M2", B.TE_SCALE_DELAYED, 0, scalar(1.0), empty_f32(), empty_f32(), db2,
+                              B.dbias_workspace(R, C, torch.device(DEV)), None, u8(C, R))
+    np.testing.assert_array_equal(host(db), host(db2))
+
+
+def test_mxfp8_quantize_dbias_empty_and_rejections():
+    ws = torch.empty(16, dtype=torch.uint8, device=DEV)
+    db = torch.full((64,), 7.0, dtype=torch.float32, device=DEV)
+    x0 = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    B.te_mxfp8_quantize_dbias(x0, "E4M3", db, ws)  # empty x: no outputs needed
+    assert np.all(host(db) == 0.0)  # the sum over no rows
+    x = torch.zeros((256, 128), dtype=torch.bfloat16, device=DEV)
+    o, sc = torch.empty((256, 128), dtype=torch.uint8, device=DEV), torch.empty((256, 4), dtype=torch.uint8, device=DEV)
+    small = torch.empty(B.te_mxfp8_quantize_dbias_workspace_bytes(256, 128) - 4, dtype=torch.uint8, device=DEV)
+    with pytest.raises(B.TEError) as ei:
+        B.te_mxfp8_quantize_dbias(x, "E4M3", empty_f32(128), small, o, sc)
+    assert ei.value.status == B.TE_ERR_ARG
+    with pytest.raises(B.TEError) as ei:
+        B.te_mxfp8_quantize_dbias(x, "E4M3", None, ws, o, sc)
+    assert ei.value.status == B.TE_ERR_NULL
+
+
 # Panel-layout scales: the same codes, and scale bytes that read back (through the
 # oracle's inverse of the panel layout) as the oracle's [rows, cols/32] scales; 384 rows
 # or columns leave a partial second panel
