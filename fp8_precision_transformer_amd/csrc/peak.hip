@@ -6,7 +6,11 @@
 //    HBM byte counters (FETCH_SIZE, WRITE_SIZE) are calibrated against, and the
 //    practical streaming rate (read + write) a memory-bound kernel can reach;
 //  - k_read: a read-only stream (xor-reduce of every 16-byte word), the practical
-//    read rate.
+//    read rate;
+//  - k_stream: the streaming ceiling study: copy (read 1 : write 1), cast-shaped
+//    (16 bytes read, 8 written per lane and chunk: the bf16 -> FP8 byte ratio),
+//    read-only and write-only streams, with U chunks per lane in flight, cached or
+//    nontemporal loads (NTL) and stores (NTS), over grid sizes chosen by the caller.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -87,4 +91,92 @@ extern "C" int te_read_launch(const void* src, void* out4, int64_t n16, int grid
   hipLaunchKernelGGL(k_read, dim3(static_cast<unsigned>(g)), dim3(256), 0, st, static_cast<const uint4*>(src),
                      static_cast<uint32_t*>(out4), n16);
   return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+// KIND 0: copy, 1: cast-shaped (8 output bytes per 16 input bytes), 2: read-only,
+// 3: write-only.  Lane chunk u of an iteration is 16-byte word base + u * stride, so
+// every load and store instruction covers a contiguous 4 KB per block.
+template <int KIND, int U, bool NTL, bool NTS>
+__global__ __launch_bounds__(256) void k_stream(const v4u* __restrict__ src, void* __restrict__ dst, int64_t n16) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  uint32_t acc = 0;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; base < n16; base += stride * U) {
+    v4u v[U];
+    if constexpr (KIND != 3) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = base + u * stride;
+        if (i < n16) v[u] = NTL ? __builtin_nontemporal_load(src + i) : src[i];
+        else v[u] = v4u{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * stride;
+      if (i >= n16) continue;
+      if constexpr (KIND == 0) {
+        if (NTS) __builtin_nontemporal_store(v[u], static_cast<v4u*>(dst) + i);
+        else static_cast<v4u*>(dst)[i] = v[u];
+      } else if constexpr (KIND == 1) {
+        const v2u o = {__builtin_amdgcn_perm(v[u].y, v[u].x, 0x07050301u),
+                       __builtin_amdgcn_perm(v[u].w, v[u].z, 0x07050301u)};
+        if (NTS) __builtin_nontemporal_store(o, static_cast<v2u*>(dst) + i);
+        else static_cast<v2u*>(dst)[i] = o;
+      } else if constexpr (KIND == 2) {
+        acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+      } else {
+        const v4u o = {static_cast<uint32_t>(i), 1u, 2u, 3u};
+        if (NTS) __builtin_nontemporal_store(o, static_cast<v4u*>(dst) + i);
+        else static_cast<v4u*>(dst)[i] = o;
+      }
+    }
+  }
+  if constexpr (KIND == 2) {
+    if (acc == 0x9e3779b9u) static_cast<uint32_t*>(dst)[0] = acc;
+  }
+}
+
+template <int KIND, int U>
+static void stream_launch(int nt, const void* src, void* dst, int64_t n16, int grid, hipStream_t st) {
+  const auto* s4 = static_cast<const v4u*>(src);
+  switch (nt & 3) {
+    case 0: hipLaunchKernelGGL((k_stream<KIND, U, false, false>), dim3(grid), dim3(256), 0, st, s4, dst, n16); break;
+    case 1: hipLaunchKernelGGL((k_stream<KIND, U, true, false>), dim3(grid), dim3(256), 0, st, s4, dst, n16); break;
+    case 2: hipLaunchKernelGGL((k_stream<KIND, U, false, true>), dim3(grid), dim3(256), 0, st, s4, dst, n16); break;
+    default: hipLaunchKernelGGL((k_stream<KIND, U, true, true>), dim3(grid), dim3(256), 0, st, s4, dst, n16); break;
+  }
+}
+
+template <int KIND>
+static int stream_u(int u, int nt, const void* src, void* dst, int64_t n16, int grid, hipStream_t st) {
+  switch (u) {
+    case 1: stream_launch<KIND, 1>(nt, src, dst, n16, grid, st); break;
+    case 2: stream_launch<KIND, 2>(nt, src, dst, n16, grid, st); break;
+    case 4: stream_launch<KIND, 4>(nt, src, dst, n16, grid, st); break;
+    case 8: stream_launch<KIND, 8>(nt, src, dst, n16, grid, st); break;
+    default: return 1;
+  }
+  return 0;
+}
+
+// kind 0..3 as k_stream; u in {1, 2, 4, 8}; nt: bit 0 nontemporal loads, bit 1
+// nontemporal stores; grid >= 1 blocks of 256 lanes.  dst holds
+// n16 16-byte words (copy, write-only), n16 8-byte words (cast-shaped) or 4 bytes
+// (read-only).
+extern "C" int te_stream_launch(int kind, int u, int nt, const void* src, void* dst, int64_t n16, int grid,
+                                void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (grid < 1) return 1;
+  int bad = 1;
+  switch (kind) {
+    case 0: bad = stream_u<0>(u, nt, src, dst, n16, grid, st); break;
+    case 1: bad = stream_u<1>(u, nt, src, dst, n16, grid, st); break;
+    case 2: bad = stream_u<2>(u, nt, src, dst, n16, grid, st); break;
+    case 3: bad = stream_u<3>(u, nt, src, dst, n16, grid, st); break;
+    default: return 1;
+  }
+  return bad || hipGetLastError() != hipSuccess ? 1 : 0;
 }

@@ -155,6 +155,23 @@ __device__ __forceinline__ float absmax_value(uint32_t m) {
   else return __uint_as_float(m);
 }
 
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+// Streaming input: read with nontemporal loads (the input is not read again after the
+// pass; the FP8 output, stored cached, is what the next GEMM reads from the last-level
+// cache).  A 16-byte word of input.
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+  const v4u v = __builtin_nontemporal_load(static_cast<const v4u*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Flat amax + cast: one 16-byte word per lane and load instruction (a wave covers 1 KB
+// contiguous), kFlatU words per lane in flight; the word's EW elements go out as EW
+// bytes.  The cast passes (MODE 0, 2) stream the input; the amax-only pass of current
+// scaling (MODE 1) reads it cached, so that the cast pass after it finds the end of the
+// input in the last-level cache (MODE 2 visits the words last to first).
+constexpr int kFlatU = 2;
 template <typename T, bool E5M2, int MODE>
 __global__ __launch_bounds__(kThreads) void k_amax_cast(const T* __restrict__ x, int64_t n,
                                                         float* __restrict__ scale,
@@ -164,6 +181,7 @@ __global__ __launch_bounds__(kThreads) void k_amax_cast(const T* __restrict__ x,
                                                         AmaxWork* __restrict__ work, int flags) {
   constexpr bool kAmax = MODE != 2;
   constexpr bool kCast = MODE != 1;
+  constexpr int U = kFlatU;
   float s = 1.0f;
   if constexpr (MODE == 0) s = *scale;
   if constexpr (MODE != 2) {
@@ -176,55 +194,44 @@ __global__ __launch_bounds__(kThreads) void k_amax_cast(const T* __restrict__ x,
       *scale_inv = 1.0f / s;
     }
   }
-  // a chunk is 16 elements = NW 16-byte words
-  constexpr int NW = 16 * static_cast<int>(sizeof(T)) / 16;
-  constexpr int EW = 16 / static_cast<int>(sizeof(T));
+  constexpr int EW = 16 / static_cast<int>(sizeof(T));  // elements per 16-byte word
   uint32_t m = 0u;  // running max of |x| as magnitude bits
-  auto load = [&](uint4* raw, int64_t c) {
-#pragma unroll
-    for (int k = 0; k < NW; ++k) raw[k] = reinterpret_cast<const uint4*>(x + c * 16)[k];
-  };
-  auto chunk = [&](const uint4* raw, int64_t c) {
-    if constexpr (kAmax) {
-#pragma unroll
-      for (int k = 0; k < NW; ++k) m = absmax_bits<T>(m, raw[k]);
-    }
-    if constexpr (kCast) {
-      float v[16];
-#pragma unroll
-      for (int k = 0; k < NW; ++k) unpack16<T>(raw[k], v + k * EW);
-      uint4 q;
-      q.x = quant4<E5M2>(v[0], v[1], v[2], v[3], s);
-      q.y = quant4<E5M2>(v[4], v[5], v[6], v[7], s);
-      q.z = quant4<E5M2>(v[8], v[9], v[10], v[11], s);
-      q.w = quant4<E5M2>(v[12], v[13], v[14], v[15], s);
-      *reinterpret_cast<uint4*>(out + c * 16) = q;
-    }
-  };
-  const int64_t nv = n >> 4;
+  const uint4* xw = reinterpret_cast<const uint4*>(x);
+  const int64_t nw = n / EW;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  auto at = [&](int64_t i) { return MODE == 2 ? nv - 1 - i : i; };
-  int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  for (; i + stride < nv; i += 2 * stride) {
-    const int64_t c0 = at(i), c1 = at(i + stride);
-    uint4 r0[NW], r1[NW];
-    load(r0, c0);
-    load(r1, c1);
-    chunk(r0, c0);
-    chunk(r1, c1);
-  }
-  if (i < nv) {
-    uint4 r0[NW];
-    load(r0, at(i));
-    chunk(r0, at(i));
-  }
-  if (blockIdx.x == 0) {  // tail of fewer than 16 elements
-    const int64_t t = nv * 16 + threadIdx.x;
-    if (t < n) {
-      const uint32_t b = raw_bits<T>(x + t);
-      if constexpr (kAmax) m = absmax_bits<T>(m, make_uint4(b, 0u, 0u, 0u));
+  auto at = [&](int64_t i) { return MODE == 2 ? nw - 1 - i : i; };
+  for (int64_t b = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; b < nw; b += stride * U) {
+    uint4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = b + u * stride;
+      if (i < nw) raw[u] = MODE == 1 ? xw[at(i)] : load_stream(xw + at(i));
+      else raw[u] = make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = b + u * stride;
+      if (i >= nw) break;
+      if constexpr (kAmax) m = absmax_bits<T>(m, raw[u]);
       if constexpr (kCast) {
-        const float v = sizeof(T) == 2 ? __uint_as_float(b << 16) : __uint_as_float(b);
+        float v[EW];
+        unpack16<T>(raw[u], v);
+        if constexpr (EW == 8) {
+          const v2u q = {quant4<E5M2>(v[0], v[1], v[2], v[3], s), quant4<E5M2>(v[4], v[5], v[6], v[7], s)};
+          *reinterpret_cast<v2u*>(out + at(i) * 8) = q;
+        } else {
+          *reinterpret_cast<uint32_t*>(out + at(i) * 4) = quant4<E5M2>(v[0], v[1], v[2], v[3], s);
+        }
+      }
+    }
+  }
+  if (blockIdx.x == 0) {  // tail of fewer than EW elements
+    const int64_t t = nw * EW + threadIdx.x;
+    if (t < n) {
+      const uint32_t bits = raw_bits<T>(x + t);
+      if constexpr (kAmax) m = absmax_bits<T>(m, make_uint4(bits, 0u, 0u, 0u));
+      if constexpr (kCast) {
+        const float v = sizeof(T) == 2 ? __uint_as_float(bits << 16) : __uint_as_float(bits);
         out[t] = static_cast<uint8_t>(quant4<E5M2>(v, 0.f, 0.f, 0.f, s) & 0xffu);
       }
     }
@@ -334,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void k_cast_transpose(
   auto load1 = [&](int p, int64_t r0, int64_t c0) {
     if constexpr (FAST) {
       const uint8_t* base = reinterpret_cast<const uint8_t*>(x + r0 * C + c0);
-      return *reinterpret_cast<const uint4*>(base + ld_off + p * ld_pass);
+      return load_stream(base + ld_off + p * ld_pass);
     } else {
       const int64_t r = r0 + p * RPP + prow;
       uint32_t w[4] = {0u, 0u, 0u, 0u};
@@ -1032,7 +1039,7 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_tiles(const uint16_t* __rest
   // one 16-byte load of pass p of the tile at (r0, c0)
   auto load1 = [&](int p, int64_t r0, int64_t c0) {
     const uint8_t* base = reinterpret_cast<const uint8_t*>(x + r0 * C + c0);
-    return *reinterpret_cast<const uint4*>(base + ld_off + p * ld_pass);
+    return load_stream(base + ld_off + p * ld_pass);
   };
   // The tile's registers are reloaded with the next tile as soon as they are consumed:
   // pass by pass without the column copy, after all passes with it (the column work
@@ -1365,7 +1372,7 @@ __global__ __launch_bounds__(kThreads) void k_mxfp4_recipe(const uint16_t* __res
   };
   auto load1 = [&](int p, int64_t r0, int64_t c0) {
     const uint8_t* base = reinterpret_cast<const uint8_t*>(x + r0 * C + c0);
-    return *reinterpret_cast<const uint4*>(base + ld_off + p * ld_pass);
+    return load_stream(base + ld_off + p * ld_pass);
   };
   auto process = [&](uint4 (&raw)[NP], int64_t r0, int64_t c0, bool has1, int64_t r1, int64_t c1) {
     if constexpr (COL) __syncthreads();
@@ -1527,7 +1534,7 @@ __global__ __launch_bounds__(kThreads) void k_mxfp4_2d(const uint16_t* __restric
     __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      raw[p] = *reinterpret_cast<const uint4*>(x + (r0 + p * RPP + prow) * C + c0 + pcol);
+      raw[p] = load_stream(x + (r0 + p * RPP + prow) * C + c0 + pcol);
       *reinterpret_cast<uint4*>(tile + (p * RPP + prow) * kMxTPitch + pcol * 2) = raw[p];
     }
     __syncthreads();
@@ -1640,7 +1647,7 @@ int persistent_grid(const void* kernel, int64_t units, int64_t per_block, int ma
 // 5B-layer tensors: two blocks (eight waves) per CU stream best for the flat cast,
 // the cast-transpose and the row-wise MX copy; the column-wise MX copy, which
 // spends more time per tile in LDS, prefers a full CU.
-constexpr int kCapFlat = 2;
+constexpr int kCapFlat = 4;
 constexpr int kCapCT = 2;
 constexpr int kCapMxRow = 2;
 constexpr int kCapMxCol = 8;
@@ -1650,7 +1657,7 @@ template <typename T, bool E5M2, int MODE>
 void launch_flat(const T* x, int64_t n, int margin, float* scale, float* scale_inv, float* amax,
                  uint8_t* out, AmaxWork* work, int flags, hipStream_t st) {
   const auto fn = k_amax_cast<T, E5M2, MODE>;
-  const int g = persistent_grid(reinterpret_cast<const void*>(fn), n >> 4, kThreads, kCapFlat);
+  const int g = persistent_grid(reinterpret_cast<const void*>(fn), (n / (16 / static_cast<int64_t>(sizeof(T)))) / kFlatU, kThreads, kCapFlat);
   hipLaunchKernelGGL(fn, dim3(g), dim3(kThreads), 0, st, x, n, scale, scale_inv, amax, out, margin, work, flags);
 }
 

@@ -159,7 +159,46 @@ def _peak_lib():
     L.te_peak_launch.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 3
     L.te_copy_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     L.te_read_launch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    L.te_stream_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     return L
+
+
+def stream(args):
+    """The streaming ceiling study (k_stream): copy, cast-shaped (read 2 : write 1, the
+    bf16 -> FP8 ratio), read-only and write-only streams of --mib MiB of input, with 1, 2,
+    4 or 8 chunks of 16 bytes per lane in flight, cached or nontemporal loads and
+    stores (nt bit 0: loads, bit 1: stores), over grid sizes of 1 to 16 blocks of 256
+    lanes per CU.  One JSON line per run, then the
+    best configuration of each kind."""
+    import ctypes
+    L = _peak_lib()
+    dev = "cuda:0"
+    n = args.mib * (1 << 20)
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ps, pd = ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr())
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    moved = {0: 2 * n, 1: n + n // 2, 2: n, 3: n}
+    names = {0: "copy", 1: "cast_shaped", 2: "read", 3: "write"}
+    best = {}
+    for kind in (0, 1, 2, 3):
+        for u in (1, 2, 4, 8):
+            for nt in ((0, 1, 2, 3) if kind < 2 else (0, 3)):
+                for per_cu in (1, 2, 4, 8, 16):
+                    grid = per_cu * cus
+
+                    def fn():
+                        if L.te_stream_launch(kind, u, nt, ps, pd, n // 16, grid, st):
+                            raise RuntimeError("te_stream_launch failed")
+                    ms = _time(fn, args.iters, args.warmup)
+                    rec = {"kernel": "k_stream", "kind": names[kind], "u": u, "nt": nt, "grid": grid,
+                           "bytes": moved[kind], "ms": round(ms, 5), "gbs": round(moved[kind] / ms / 1e6, 1)}
+                    print(json.dumps(rec), flush=True)
+                    if rec["gbs"] > best.get(names[kind], {"gbs": 0})["gbs"]:
+                        best[names[kind]] = rec
+    print(json.dumps({"best": best}), flush=True)
 
 
 def copy(args):
@@ -322,12 +361,16 @@ def main():
     cp.add_argument("--iters", type=int, default=10)
     cp.add_argument("--warmup", type=int, default=2)
     cp.add_argument("--sweep", action="store_true", help="also time copy and read-only streams over grid sizes")
+    sm = sub.add_parser("stream")
+    sm.add_argument("--mib", type=int, default=2048)
+    sm.add_argument("--iters", type=int, default=5)
+    sm.add_argument("--warmup", type=int, default=1)
     k = sub.add_parser("peak")
     k.add_argument("--iters", type=int, default=4096)
     k.add_argument("--waves-per-cu", type=int, default=1)
     args = p.parse_args()
     torch.cuda.set_device(0)
-    {"gemm": gemm, "cast": cast, "peak": peak, "layer": layer, "copy": copy, "lib": lib}[args.cmd](args)
+    {"gemm": gemm, "cast": cast, "peak": peak, "layer": layer, "copy": copy, "lib": lib, "stream": stream}[args.cmd](args)
 
 
 if __name__ == "__main__":
