@@ -520,7 +520,8 @@ def main():
     wall = time.perf_counter() - t0
     log(f"timed region {wall:.2f}s")
     # every mode's GEMMs must have run on the matrix-core path of its precision
-    want = {"bf16": "gemm4_bf16_", "mxfp8": "gemm4_mx_", "mxfp4": "gemm4_mxfp4_", "fp8": "gemm4_fp8_"}
+    want = {"bf16": ("gemm4_bf16_",), "mxfp8": ("gemm4_mx_", "gemm1w_mx_"), "mxfp4": ("gemm4_mxfp4_",),
+            "fp8": ("gemm4_fp8_", "gemm1w_fp8_")}
     for m, vs in variants.items():
         prefix = next(v for k, v in want.items() if m.startswith(k))
         bad = [v for v in vs if not v.startswith(prefix)]
@@ -576,9 +577,9 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MI355X_FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MI355X_FP8_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic("gemm_fp8"),
-                "kernel": "k_gemm4 FP8 (256x256 tiles, 8 waves in ping-pong, 128-byte k stages); "
-                          "12 launches per layer, achieved = layer FLOP / summed launch time; "
-                          "traffic = mean HBM bytes per launch",
+                "kernel": "k_gemm1w FP8 (256x256 tiles, one wave per SIMD with 128x128 each, 128-byte k stages, "
+                          "three stage slots for the operand with more rows); 12 launches per layer, achieved = "
+                          "layer FLOP / summed launch time; traffic = mean HBM bytes per launch",
                 "avg_launch_ms": round(t_ms / len(gemms), 4),
                 "flop_per_launch": int(flops / len(gemms))}
     # the same for the block-scaled GEMMs: MXFP8 against the FP8 peak, MXFP4 (the FP4
@@ -594,7 +595,7 @@ def main():
                 "avg_launch_ms": round(t_ms / len(gemms), 4), "flop_per_launch": int(flops / len(gemms))}
 
     roof8 = mx_roofline("mxfp8_prequant", MI355X_FP8_PEAK_TFLOPS, "gemm_mxfp8",
-                        "k_gemm4 MXFP8 (E4M3 x E4M3 scaled MFMA, E8M0 scales in the panel layout, 256x256 tiles, ping-pong); 12 launches per layer")
+                        "k_gemm1w MXFP8 (E4M3 x E4M3 scaled MFMA, E8M0 scales in the panel layout, 256x256 tiles, one wave per SIMD); 12 launches per layer")
     roof4 = mx_roofline("mxfp4_prequant", MI355X_FP4_PEAK_TFLOPS, "gemm_mxfp4",
                         "k_gemm4 MXFP4 (E2M1 x E2M1 scaled MFMA, E8M0 scales in the panel layout, 256x256 tiles, ping-pong); 12 launches per layer")
     roof16 = mx_roofline("bf16", MI355X_BF16_PEAK_TFLOPS, None,

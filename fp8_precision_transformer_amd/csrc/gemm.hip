@@ -1063,6 +1063,347 @@ const char* splitk_name(const char* name) {
   return it->second.c_str();
 }
 
+// ============================================================================
+// One wave per SIMD (per-tensor FP8 with k % 128 == 0; MX with panel-layout scales):
+// 4 waves (2 x 2), each a 128 x 128 block of the 256 x 256 tile (4 x 4 MFMA tiles of
+// 32 x 32), so a 64-byte k step reads 8 fragments for 16 MFMAs -- one LDS read per
+// MFMA, against 1.5 for the ping-pong's 128 x 64 waves, whose LDS command queue is
+// full a tenth of the time (rocprofv3 SQ_LDS_CMD_FIFO_FULL).  The 256 registers of
+// accumulators live in AGPRs beside 256 VGPRs, so both k steps of a stage and the MX
+// scales fit without the ping-pong's split of a stage into phases.
+//
+// One wave's stream is interleaved explicitly (scheduling groups): k step 0 of stage s
+// pairs each of its first 8 MFMAs with two fragment reads of k step 1 (the reads land
+// while the last 8 run); then the wave waits for stage s+1 and reaches the stage's one
+// barrier (every wave has read stage s, stage s+1 is visible); k step 1 pairs each MFMA
+// with a global->LDS load of a later stage into the slots of stage s, and the first 8
+// with two fragment reads of stage s+1.  Stage slots: the operand with more rows (the
+// one that does not stay in the last-level cache on the long-k shapes) gets three,
+// loaded two stages ahead, the other two (DEEP 1: A deep, 2: B deep).  Each slot is its
+// own LDS array, so the compiler can tell the loads into one slot from the reads of
+// another and interleave them.  Past the last stage the loads read zeros or the next
+// rows into slots that are never read again, so every iteration has the same shape.
+// Results are bit-identical to k_gemm4's: every output sums the same MFMAs in the same
+// k order.
+// ============================================================================
+template <int KIND, int AF, int BF, int DEEP>
+__global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
+  constexpr bool MX = KIND == KIND_MX;
+  // DEEP 1: A in three stage slots (loads two stages ahead), B in two; DEEP 2: the mirror
+  constexpr int NA = DEEP == 1 ? 3 : 2, NB = DEEP == 2 ? 3 : 2;
+  // one array per stage slot and operand, so that the compiler can tell the global->LDS
+  // loads into one slot from the fragment reads of another
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kPairOp];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA1[kPairOp];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA2[NA > 2 ? kPairOp : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[kPairOp];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB1[kPairOp];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB2[NB > 2 ? kPairOp : 16];
+  auto slotA = [&](int slot) { return slot == 0 ? sA0 : slot == 1 ? sA1 : sA2; };
+  auto slotB = [&](int slot) { return slot == 0 ? sB0 : slot == 1 ? sB1 : sB2; };
+  const int nb = p.nbm * p.nbn;
+  const int bid = static_cast<int>(blockIdx.x);
+  const int xcd = bid & 7, idx = bid >> 3;
+  const int per = nb >> 3, rem = nb & 7;
+  const int lin = xcd * per + (xcd < rem ? xcd : rem) + idx;
+  const int gspan = kGroupM * p.nbn;
+  const int group = lin / gspan;
+  const int first_m = group * kGroupM;
+  const int gsz = (p.nbm - first_m) < kGroupM ? (p.nbm - first_m) : kGroupM;
+  const int in_g = lin - group * gspan;
+  const int tm = first_m + in_g % gsz;
+  const int tn = in_g / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const int lr = lane & 31, lk = lane >> 5;
+  const int rows_a = (p.M - m0) < BM ? (p.M - m0) : BM;
+  const int rows_b = (p.N - n0) < BN ? (p.N - n0) : BN;
+  const v4i rsA = make_rsrc(p.a + static_cast<int64_t>(m0) * p.KB, static_cast<uint32_t>(rows_a) * p.KB);
+  const v4i rsB = make_rsrc(p.b + static_cast<int64_t>(n0) * p.KB, static_cast<uint32_t>(rows_b) * p.KB);
+  // global->LDS: wave w moves rows [64 w, 64 w + 64) of A and of B, 8 rows per
+  // instruction (the lane mapping and swizzle of k_gemm4)
+  const int c0 = (lane & 7) ^ (lane >> 3);
+  const uint32_t ld_base = static_cast<uint32_t>(wave * 64 + (lane >> 3)) * static_cast<uint32_t>(p.KB);
+  const int S = (p.KB + PK - 1) / PK;
+  // per instruction t: the lane's byte offset in stage 0; stage st adds 128 st.  With k a
+  // multiple of 128 every chunk of a real stage is inside its row; past the last stage
+  // the offsets run into the next rows or past the buffer (zeros), into a slot that is
+  // never read again.  A ragged k takes k_gemm4.
+  uint32_t voff[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+    voff[t] = ld_base + static_cast<uint32_t>(t * 8) * static_cast<uint32_t>(p.KB) +
+              static_cast<uint32_t>((c0 ^ (t & 3)) << 4);
+  auto issue_op = [&](const v4i& rs, uint8_t* dst, int st) {
+    const uint32_t kb = static_cast<uint32_t>(st) * PK;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int off = static_cast<int>(voff[t] + kb);
+      const int base = (wave * 64 + t * 8) * PK;
+      raw_buffer_load_lds(rs, (__attribute__((address_space(3))) uint32_t*)(dst + base), 16, off, 0, 0, 0);
+    }
+  };
+  // MX (panel-layout E8M0 scales): the dword of row r and stage g is dword
+  // ((r / 256) * S + g) * 256 + r % 256; lane l loads rows wm + l and wm + 64 + l of A
+  // (wn + l, wn + 64 + l of B) for a stage, together with the stage's operand loads;
+  // at the stage's start the half-waves swap row groups and each lane keeps the bytes
+  // of its k blocks (2h + lk), two row groups per register.
+  const uint32_t* scA = nullptr;
+  const uint32_t* scB = nullptr;
+  if constexpr (MX) {
+    scA = static_cast<const uint32_t*>(p.a_scale) + static_cast<int64_t>(m0 / BM) * S * 256 + wm + lane;
+    scB = static_cast<const uint32_t*>(p.b_scale) + static_cast<int64_t>(n0 / BN) * S * 256 + wn + lane;
+  }
+  uint32_t rA0[NA], rA1[NA], rB0[NB], rB1[NB];  // raw dwords per stage slot
+  auto load_scA = [&](int set, int st) {
+    if constexpr (MX) {
+      const int64_t o = static_cast<int64_t>(st < S ? st : S - 1) * 256;
+      rA0[set] = scA[o];
+      rA1[set] = scA[o + 64];
+    }
+  };
+  auto load_scB = [&](int set, int st) {
+    if constexpr (MX) {
+      const int64_t o = static_cast<int64_t>(st < S ? st : S - 1) * 256;
+      rB0[set] = scB[o];
+      rB1[set] = scB[o + 64];
+    }
+  };
+  uint32_t pA[2] = {0u, 0u}, pB[2] = {0u, 0u};
+  auto pack_sc = [&](int sa_set, int sb_set) {
+    if constexpr (MX) {
+      auto pick = [&](uint32_t w0, uint32_t w1) {
+        return ((w0 >> (8 * lk)) & 0x00ff00ffu) | (((w1 >> (8 * lk)) & 0x00ff00ffu) << 8);
+      };
+      const auto a0 = __builtin_amdgcn_permlane32_swap(rA0[sa_set], rA0[sa_set], false, false);
+      const auto a1 = __builtin_amdgcn_permlane32_swap(rA1[sa_set], rA1[sa_set], false, false);
+      const auto b0 = __builtin_amdgcn_permlane32_swap(rB0[sb_set], rB0[sb_set], false, false);
+      const auto b1 = __builtin_amdgcn_permlane32_swap(rB1[sb_set], rB1[sb_set], false, false);
+      pA[0] = pick(a0[0], a0[1]);
+      pA[1] = pick(a1[0], a1[1]);
+      pB[0] = pick(b0[0], b0[1]);
+      pB[1] = pick(b1[0], b1[1]);
+    }
+  };
+  const int fk = f8(lr);
+  const int ra0 = (wm + lr) * PK + ((lk ^ fk) << 4);
+  const int rb0 = (wn + lr) * PK + ((lk ^ fk) << 4);
+  v8i fa0[4], fb0[4], fa1[4], fb1[4];
+  auto read_ks = [&](int sla, int slb, int h, v8i (&fa)[4], v8i (&fb)[4]) {
+    const int alo = ra0 ^ (h << 6), ahi = alo ^ 32;
+    const int blo = rb0 ^ (h << 6), bhi = blo ^ 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int o = i * 32 * PK;
+      const v4u lo = *reinterpret_cast<const v4u*>(slotA(sla) + alo + o);
+      const v4u hi = *reinterpret_cast<const v4u*>(slotA(sla) + ahi + o);
+      fa[i] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int o = j * 32 * PK;
+      const v4u lo = *reinterpret_cast<const v4u*>(slotB(slb) + blo + o);
+      const v4u hi = *reinterpret_cast<const v4u*>(slotB(slb) + bhi + o);
+      fb[j] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{0};
+  auto mf = [&](auto H, auto I, auto J, const v8i (&fa)[4], const v8i (&fb)[4]) {
+    constexpr int h = decltype(H)::value, i = decltype(I)::value, j = decltype(J)::value;
+    if constexpr (MX)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AF, BF, 2 * h + (i & 1),
+                                                                 static_cast<int>(pA[i >> 1]), 2 * h + (j & 1),
+                                                                 static_cast<int>(pB[j >> 1]));
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AF, BF, 0, 0, 0, 0);
+  };
+  auto mfma_ks = [&](auto H, const v8i (&fa)[4], const v8i (&fb)[4]) {
+    auto row = [&](auto I) {
+      mf(H, I, ic<0>{}, fa, fb);
+      mf(H, I, ic<1>{}, fa, fb);
+      mf(H, I, ic<2>{}, fa, fb);
+      mf(H, I, ic<3>{}, fa, fb);
+    };
+    row(ic<0>{});
+    row(ic<1>{});
+    row(ic<2>{});
+    row(ic<3>{});
+  };
+
+  // Prologue: stages 0 and 1 of both operands and stage 2 of the deep one, the deep
+  // one's loads last, so that waiting for a stage of the shallow operand leaves the deep
+  // operand's latest stage in flight.  Loads per stage and operand: 8 (+ 2 scale dwords).
+  constexpr int LPO = 8 + (MX ? 2 : 0);
+  auto issue_A = [&](int slot, int st) { load_scA(slot, st); issue_op(rsA, slotA(slot), st); };
+  auto issue_B = [&](int slot, int st) { load_scB(slot, st); issue_op(rsB, slotB(slot), st); };
+  issue_A(0, 0);
+  issue_B(0, 0);
+  issue_A(1, 1);
+  issue_B(1, 1);
+  if constexpr (DEEP == 1) issue_A(2, 2);
+  if constexpr (DEEP == 2) issue_B(2, 2);
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((DEEP ? 3 : 2) * LPO));  // stage 0 landed
+  __builtin_amdgcn_s_barrier();
+  read_ks(0, 0, 0, fa0, fb0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  auto iter = [&](auto U, int s) {
+    constexpr int u = decltype(U)::value;
+    constexpr int sa = u % NA, sb = u % NB;
+    constexpr int sa1 = (u + 1) % NA, sb1 = (u + 1) % NB;
+    // k step 0: MFMAs on (fa0, fb0); fragments of k step 1 into (fa1, fb1)
+    pack_sc(sa, sb);
+    read_ks(sa, sb, 1, fa1, fb1);
+    mfma_ks(ic<0>{}, fa0, fb0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // stage s+1 landed (only the deep operand's stage s+2 may still be in flight); this
+    // wave's reads of stage s done
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(DEEP ? LPO : 0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // k step 1: MFMAs on (fa1, fb1); fragments of stage s+1, k step 0 into (fa0, fb0);
+    // loads of the shallow operand's stage s+2 and then the deep one's stage s+3 into
+    // the slots of stage s
+    read_ks(sa1, sb1, 0, fa0, fb0);
+    if constexpr (DEEP == 1) {
+      issue_B(sb, s + 2);
+      issue_A(sa, s + 3);
+    } else if constexpr (DEEP == 2) {
+      issue_A(sa, s + 2);
+      issue_B(sb, s + 3);
+    } else {
+      issue_A(sa, s + 2);
+      issue_B(sb, s + 2);
+    }
+    mfma_ks(ic<1>{}, fa1, fb1);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  constexpr int UNR = DEEP ? 6 : 2;
+  int s = 0;
+  for (; s + UNR <= S; s += UNR) {
+    iter(ic<0>{}, s);
+    iter(ic<1>{}, s + 1);
+    if constexpr (UNR == 6) {
+      iter(ic<2>{}, s + 2);
+      iter(ic<3>{}, s + 3);
+      iter(ic<4>{}, s + 4);
+      iter(ic<5>{}, s + 5);
+    }
+  }
+  if (s < S) iter(ic<0>{}, s);
+  if constexpr (UNR == 6) {
+    if (s + 1 < S) iter(ic<1>{}, s + 1);
+    if (s + 2 < S) iter(ic<2>{}, s + 2);
+    if (s + 3 < S) iter(ic<3>{}, s + 3);
+    if (s + 4 < S) iter(ic<4>{}, s + 4);
+  }
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));  // loads past the last stage still write LDS
+  __builtin_amdgcn_s_barrier();
+
+  // ---- epilogue: scale, bias, round; staged through LDS, 64 x 64 floats per pass ----
+  float sa = 1.0f, sb = 1.0f;
+  if constexpr (!MX) {
+    sa = *static_cast<const float*>(p.a_scale);
+    sb = *static_cast<const float*>(p.b_scale);
+  }
+  constexpr int kEpPitch = 256;
+  float* ep = reinterpret_cast<float*>((wave & 2 ? sA1 : sA0) + (wave & 1) * 64 * kEpPitch);
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    float bias_v[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + wn + hf * 64 + j * 32 + lr;
+      bias_v[j] = 0.0f;
+      if (p.bias != nullptr && col < p.N)
+        bias_v[j] = p.bias_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p.bias)[col]) << 16)
+                                : static_cast<const float*>(p.bias)[col];
+    }
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = pass * 2 + ii;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            float val = acc[i][2 * hf + j][v];
+            if constexpr (!MX) val = __fmul_rn(__fmul_rn(val, sa), sb);
+            if (p.bias != nullptr) val = __fadd_rn(val, bias_v[j]);
+            const int r = ii * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
+            ep[r * (kEpPitch / 4) + j * 32 + lr] = val;
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
+      __builtin_amdgcn_wave_barrier();
+      const int row0 = m0 + wm + pass * 64;
+      const int col0 = n0 + wn + hf * 64;
+      if (p.d_bf16) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int r = t * 8 + (lane >> 3);
+          const int c = (lane & 7) * 8;
+          const float4 lo = *reinterpret_cast<const float4*>(ep + r * (kEpPitch / 4) + c);
+          const float4 hi = *reinterpret_cast<const float4*>(ep + r * (kEpPitch / 4) + c + 4);
+          const int grow = row0 + r, gcol = col0 + c;
+          if (grow < p.M && gcol < p.N) {
+            const v4u o = {bf16x2_rne(lo.x, lo.y), bf16x2_rne(lo.z, lo.w), bf16x2_rne(hi.x, hi.y),
+                           bf16x2_rne(hi.z, hi.w)};
+            __builtin_nontemporal_store(
+                o, reinterpret_cast<v4u*>(static_cast<uint16_t*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int r = t * 4 + (lane >> 4);
+          const int c = (lane & 15) * 4;
+          v4f v4 = *reinterpret_cast<const v4f*>(ep + r * (kEpPitch / 4) + c);
+          const int grow = row0 + r, gcol = col0 + c;
+          if (grow < p.M && gcol < p.N) {
+            v4f* dst = reinterpret_cast<v4f*>(static_cast<float*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol);
+            if (p.accumulate) {
+              const v4f old = __builtin_nontemporal_load(dst);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v4[q] = __fadd_rn(old[q], v4[q]);
+            }
+            __builtin_nontemporal_store(v4, dst);
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
 template <int KIND, int AF, int BF, bool PANEL = false, bool FUSED = false>
 hipError_t run(Params p, hipStream_t s, const char* name) {
   g_last_variant = name;
@@ -1092,6 +1433,22 @@ hipError_t run(Params p, hipStream_t s, const char* name) {
     hipLaunchKernelGGL((k_gemm<KIND_MX, AF, BF>), dim3(nb), dim3(NT), 0, s, p);
   } else {
     hipLaunchKernelGGL((k_gemm4<KIND, AF, BF, PANEL, FUSED>), dim3(nb), dim3(NT8), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+// the one-wave kernel: per-tensor FP8 (k % 128 == 0) or MX with panel scales, one k
+// split, bf16 / fp32 output (with accumulation); the operand with more rows gets the
+// deeper stage ring
+template <int KIND, int AF, int BF>
+hipError_t run_1w(Params p, hipStream_t s, const char* name_a, const char* name_b) {
+  const int nb = p.nbm * p.nbn;
+  if (p.M >= p.N) {
+    g_last_variant = name_a;
+    hipLaunchKernelGGL((k_gemm1w<KIND, AF, BF, 1>), dim3(nb), dim3(256), 0, s, p);
+  } else {
+    g_last_variant = name_b;
+    hipLaunchKernelGGL((k_gemm1w<KIND, AF, BF, 2>), dim3(nb), dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }
@@ -1151,6 +1508,24 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
     return run<KIND_FP8, 1, 1, false, true>(p, s, "gemm4_fp8_e5m2_e5m2_256x256_pingpong_amax");
   }
   if (g.a_fmt == BF16) return run<KIND_BF16, 0, 0>(p, s, "gemm4_bf16_256x256_pingpong");
+  if (g.a_fmt != E2M1 && p.splits == 1 && ((g.mx && g.mx_panel) || (!g.mx && p.KB % PK == 0))) {
+    if (g.mx) {
+      if (af == 0 && bf == 0)
+        return run_1w<KIND_MX, 0, 0>(p, s, "gemm1w_mx_e4m3_e4m3_256x256_panel_deepA", "gemm1w_mx_e4m3_e4m3_256x256_panel_deepB");
+      if (af == 1 && bf == 0)
+        return run_1w<KIND_MX, 1, 0>(p, s, "gemm1w_mx_e5m2_e4m3_256x256_panel_deepA", "gemm1w_mx_e5m2_e4m3_256x256_panel_deepB");
+      if (af == 0 && bf == 1)
+        return run_1w<KIND_MX, 0, 1>(p, s, "gemm1w_mx_e4m3_e5m2_256x256_panel_deepA", "gemm1w_mx_e4m3_e5m2_256x256_panel_deepB");
+      return run_1w<KIND_MX, 1, 1>(p, s, "gemm1w_mx_e5m2_e5m2_256x256_panel_deepA", "gemm1w_mx_e5m2_e5m2_256x256_panel_deepB");
+    }
+    if (af == 0 && bf == 0)
+      return run_1w<KIND_FP8, 0, 0>(p, s, "gemm1w_fp8_e4m3_e4m3_256x256_deepA", "gemm1w_fp8_e4m3_e4m3_256x256_deepB");
+    if (af == 1 && bf == 0)
+      return run_1w<KIND_FP8, 1, 0>(p, s, "gemm1w_fp8_e5m2_e4m3_256x256_deepA", "gemm1w_fp8_e5m2_e4m3_256x256_deepB");
+    if (af == 0 && bf == 1)
+      return run_1w<KIND_FP8, 0, 1>(p, s, "gemm1w_fp8_e4m3_e5m2_256x256_deepA", "gemm1w_fp8_e4m3_e5m2_256x256_deepB");
+    return run_1w<KIND_FP8, 1, 1>(p, s, "gemm1w_fp8_e5m2_e5m2_256x256_deepA", "gemm1w_fp8_e5m2_e5m2_256x256_deepB");
+  }
   if (g.a_fmt == E2M1) {
     if (g.mx_panel) return run<KIND_MX4, 4, 4, true>(p, s, "gemm4_mxfp4_e2m1_e2m1_256x256_pingpong_panel");
     return run<KIND_MX4, 4, 4>(p, s, "gemm4_mxfp4_e2m1_e2m1_256x256_pingpong");
