@@ -1064,7 +1064,8 @@ const char* splitk_name(const char* name) {
 }
 
 // ============================================================================
-// One wave per SIMD (per-tensor FP8 with k % 128 == 0; MX with panel-layout scales):
+// One wave per SIMD (per-tensor FP8 with k % 128 == 0; MXFP8 and MXFP4 with panel-layout
+// scales):
 // 4 waves (2 x 2), each a 128 x 128 block of the 256 x 256 tile (4 x 4 MFMA tiles of
 // 32 x 32), so a 64-byte k step reads 8 fragments for 16 MFMAs -- one LDS read per
 // MFMA, against 1.5 for the ping-pong's 128 x 64 waves, whose LDS command queue is
@@ -1088,7 +1089,10 @@ const char* splitk_name(const char* name) {
 // ============================================================================
 template <int KIND, int AF, int BF, int DEEP>
 __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
-  constexpr bool MX = KIND == KIND_MX;
+  constexpr bool MX4 = KIND == KIND_MX4;
+  constexpr bool MX = KIND == KIND_MX || MX4;  // block-scaled (E8M0 panel scales)
+  constexpr int KSTEPS = MX4 ? 4 : 2;          // 64-element k steps per 128-byte stage
+  constexpr int SDW = MX4 ? 2 : 1;             // scale dwords per row and stage
   // DEEP 1: A in three stage slots (loads two stages ahead), B in two; DEEP 2: the mirror
   constexpr int NA = DEEP == 1 ? 3 : 2, NB = DEEP == 2 ? 3 : 2;
   // one array per stage slot and operand, so that the compiler can tell the global->LDS
@@ -1147,68 +1151,109 @@ __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
       raw_buffer_load_lds(rs, (__attribute__((address_space(3))) uint32_t*)(dst + base), 16, off, 0, 0, 0);
     }
   };
-  // MX (panel-layout E8M0 scales): the dword of row r and stage g is dword
-  // ((r / 256) * S + g) * 256 + r % 256; lane l loads rows wm + l and wm + 64 + l of A
-  // (wn + l, wn + 64 + l of B) for a stage, together with the stage's operand loads;
-  // at the stage's start the half-waves swap row groups and each lane keeps the bytes
-  // of its k blocks (2h + lk), two row groups per register.
+  // MX (panel-layout E8M0 scales): the dword of row r and 128-element group g is dword
+  // ((r / 256) * G + g) * 256 + r % 256 (G = k / 128; a stage holds one group of FP8,
+  // two of E2M1); lane l loads rows wm + l and wm + 64 + l of A (wn + l, wn + 64 + l of
+  // B) for a stage, together with the stage's operand loads; at the stage's start the
+  // half-waves swap row groups and each lane keeps the bytes of its k blocks.
   const uint32_t* scA = nullptr;
   const uint32_t* scB = nullptr;
+  const int G = S * SDW;
   if constexpr (MX) {
-    scA = static_cast<const uint32_t*>(p.a_scale) + static_cast<int64_t>(m0 / BM) * S * 256 + wm + lane;
-    scB = static_cast<const uint32_t*>(p.b_scale) + static_cast<int64_t>(n0 / BN) * S * 256 + wn + lane;
+    scA = static_cast<const uint32_t*>(p.a_scale) + static_cast<int64_t>(m0 / BM) * G * 256 + wm + lane;
+    scB = static_cast<const uint32_t*>(p.b_scale) + static_cast<int64_t>(n0 / BN) * G * 256 + wn + lane;
   }
-  uint32_t rA0[NA], rA1[NA], rB0[NB], rB1[NB];  // raw dwords per stage slot
+  uint32_t rA0[NA][SDW], rA1[NA][SDW], rB0[NB][SDW], rB1[NB][SDW];  // raw dwords per stage slot
   auto load_scA = [&](int set, int st) {
     if constexpr (MX) {
-      const int64_t o = static_cast<int64_t>(st < S ? st : S - 1) * 256;
-      rA0[set] = scA[o];
-      rA1[set] = scA[o + 64];
+#pragma unroll
+      for (int d = 0; d < SDW; ++d) {
+        const int64_t o = static_cast<int64_t>((st < S ? st : S - 1) * SDW + d) * 256;
+        rA0[set][d] = scA[o];
+        rA1[set][d] = scA[o + 64];
+      }
     }
   };
   auto load_scB = [&](int set, int st) {
     if constexpr (MX) {
-      const int64_t o = static_cast<int64_t>(st < S ? st : S - 1) * 256;
-      rB0[set] = scB[o];
-      rB1[set] = scB[o + 64];
+#pragma unroll
+      for (int d = 0; d < SDW; ++d) {
+        const int64_t o = static_cast<int64_t>((st < S ? st : S - 1) * SDW + d) * 256;
+        rB0[set][d] = scB[o];
+        rB1[set][d] = scB[o + 64];
+      }
     }
   };
-  uint32_t pA[2] = {0u, 0u}, pB[2] = {0u, 0u};
+  // packed scales: FP8 MX: byte 2h + (g & 1) of pA[g >> 1] is block 2h + lk of row group g
+  // (two row groups per dword); E2M1: byte sel(h) of pA[g] is block 2h + lk of row group g
+  uint32_t pA[4] = {0u, 0u, 0u, 0u}, pB[4] = {0u, 0u, 0u, 0u};
   auto pack_sc = [&](int sa_set, int sb_set) {
     if constexpr (MX) {
       auto pick = [&](uint32_t w0, uint32_t w1) {
         return ((w0 >> (8 * lk)) & 0x00ff00ffu) | (((w1 >> (8 * lk)) & 0x00ff00ffu) << 8);
       };
-      const auto a0 = __builtin_amdgcn_permlane32_swap(rA0[sa_set], rA0[sa_set], false, false);
-      const auto a1 = __builtin_amdgcn_permlane32_swap(rA1[sa_set], rA1[sa_set], false, false);
-      const auto b0 = __builtin_amdgcn_permlane32_swap(rB0[sb_set], rB0[sb_set], false, false);
-      const auto b1 = __builtin_amdgcn_permlane32_swap(rB1[sb_set], rB1[sb_set], false, false);
-      pA[0] = pick(a0[0], a0[1]);
-      pA[1] = pick(a1[0], a1[1]);
-      pB[0] = pick(b0[0], b0[1]);
-      pB[1] = pick(b1[0], b1[1]);
+      uint32_t ga[4][SDW], gb[4][SDW];  // dwords of row groups 0..3 for this lane
+#pragma unroll
+      for (int d = 0; d < SDW; ++d) {
+        const auto a0 = __builtin_amdgcn_permlane32_swap(rA0[sa_set][d], rA0[sa_set][d], false, false);
+        const auto a1 = __builtin_amdgcn_permlane32_swap(rA1[sa_set][d], rA1[sa_set][d], false, false);
+        const auto b0 = __builtin_amdgcn_permlane32_swap(rB0[sb_set][d], rB0[sb_set][d], false, false);
+        const auto b1 = __builtin_amdgcn_permlane32_swap(rB1[sb_set][d], rB1[sb_set][d], false, false);
+        ga[0][d] = a0[0];
+        ga[1][d] = a0[1];
+        ga[2][d] = a1[0];
+        ga[3][d] = a1[1];
+        gb[0][d] = b0[0];
+        gb[1][d] = b0[1];
+        gb[2][d] = b1[0];
+        gb[3][d] = b1[1];
+      }
+      if constexpr (MX4) {  // dword 0 of a row holds blocks 0-3 of the stage, dword 1 blocks 4-7
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          pA[g] = pick(ga[g][0], ga[g][1]);
+          pB[g] = pick(gb[g][0], gb[g][1]);
+        }
+      } else {
+        pA[0] = pick(ga[0][0], ga[1][0]);
+        pA[1] = pick(ga[2][0], ga[3][0]);
+        pB[0] = pick(gb[0][0], gb[1][0]);
+        pB[1] = pick(gb[2][0], gb[3][0]);
+      }
     }
   };
   const int fk = f8(lr);
   const int ra0 = (wm + lr) * PK + ((lk ^ fk) << 4);
   const int rb0 = (wn + lr) * PK + ((lk ^ fk) << 4);
-  v8i fa0[4], fb0[4], fa1[4], fb1[4];
-  auto read_ks = [&](int sla, int slb, int h, v8i (&fa)[4], v8i (&fb)[4]) {
-    const int alo = ra0 ^ (h << 6), ahi = alo ^ 32;
-    const int blo = rb0 ^ (h << 6), bhi = blo ^ 32;
+  // fragments: FP8 k step h of a row is logical chunks 4h + lk (low 16 bytes) and
+  // 4h + 2 + lk (high); E2M1 k step h (64 elements, 32 bytes) is logical chunk 2h + lk,
+  // one 16-byte read (the matrix core reads the low four registers of an E2M1 operand)
+  using Frag = std::conditional_t<MX4, v4u, v8i>;
+  Frag fa0[4], fb0[4], fa1[4], fb1[4];
+  auto read_ks = [&](int sla, int slb, int h, Frag (&fa)[4], Frag (&fb)[4]) {
+    if constexpr (MX4) {
+      const int ao = ra0 ^ (h << 5), bo = rb0 ^ (h << 5);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int o = i * 32 * PK;
-      const v4u lo = *reinterpret_cast<const v4u*>(slotA(sla) + alo + o);
-      const v4u hi = *reinterpret_cast<const v4u*>(slotA(sla) + ahi + o);
-      fa[i] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
+      for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const v4u*>(slotA(sla) + ao + i * 32 * PK);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int o = j * 32 * PK;
-      const v4u lo = *reinterpret_cast<const v4u*>(slotB(slb) + blo + o);
-      const v4u hi = *reinterpret_cast<const v4u*>(slotB(slb) + bhi + o);
-      fb[j] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const v4u*>(slotB(slb) + bo + j * 32 * PK);
+    } else {
+      const int alo = ra0 ^ (h << 6), ahi = alo ^ 32;
+      const int blo = rb0 ^ (h << 6), bhi = blo ^ 32;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = i * 32 * PK;
+        const v4u lo = *reinterpret_cast<const v4u*>(slotA(sla) + alo + o);
+        const v4u hi = *reinterpret_cast<const v4u*>(slotA(sla) + ahi + o);
+        fa[i] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int o = j * 32 * PK;
+        const v4u lo = *reinterpret_cast<const v4u*>(slotB(slb) + blo + o);
+        const v4u hi = *reinterpret_cast<const v4u*>(slotB(slb) + bhi + o);
+        fb[j] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
     }
   };
   v16f acc[4][4];
@@ -1216,16 +1261,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{0};
-  auto mf = [&](auto H, auto I, auto J, const v8i (&fa)[4], const v8i (&fb)[4]) {
+  auto mf = [&](auto H, auto I, auto J, const Frag (&fa)[4], const Frag (&fb)[4]) {
     constexpr int h = decltype(H)::value, i = decltype(I)::value, j = decltype(J)::value;
-    if constexpr (MX)
+    if constexpr (MX4) {
+      constexpr int sel = ((h & 1) << 1) | (h >> 1);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          __builtin_bit_cast(v8i, __builtin_shufflevector(fa[i], fa[i], 0, 1, 2, 3, 0, 1, 2, 3)),
+          __builtin_bit_cast(v8i, __builtin_shufflevector(fb[j], fb[j], 0, 1, 2, 3, 0, 1, 2, 3)), acc[i][j], 4, 4,
+          sel, static_cast<int>(pA[i]), sel, static_cast<int>(pB[j]));
+    } else if constexpr (MX) {
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AF, BF, 2 * h + (i & 1),
                                                                  static_cast<int>(pA[i >> 1]), 2 * h + (j & 1),
                                                                  static_cast<int>(pB[j >> 1]));
-    else
+    } else {
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AF, BF, 0, 0, 0, 0);
+    }
   };
-  auto mfma_ks = [&](auto H, const v8i (&fa)[4], const v8i (&fb)[4]) {
+  auto mfma_ks = [&](auto H, const Frag (&fa)[4], const Frag (&fb)[4]) {
     auto row = [&](auto I) {
       mf(H, I, ic<0>{}, fa, fb);
       mf(H, I, ic<1>{}, fa, fb);
@@ -1241,7 +1293,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
   // Prologue: stages 0 and 1 of both operands and stage 2 of the deep one, the deep
   // one's loads last, so that waiting for a stage of the shallow operand leaves the deep
   // operand's latest stage in flight.  Loads per stage and operand: 8 (+ 2 scale dwords).
-  constexpr int LPO = 8 + (MX ? 2 : 0);
+  constexpr int LPO = 8 + (MX ? 2 * SDW : 0);
   auto issue_A = [&](int slot, int st) { load_scA(slot, st); issue_op(rsA, slotA(slot), st); };
   auto issue_B = [&](int slot, int st) { load_scB(slot, st); issue_op(rsB, slotB(slot), st); };
   issue_A(0, 0);
@@ -1255,53 +1307,65 @@ __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
   read_ks(0, 0, 0, fa0, fb0);
   __builtin_amdgcn_sched_barrier(0);
 
+  // one stage: k steps 0 .. KSTEPS-1.  Every k step but the last pairs its first 8
+  // MFMAs with the fragment reads of the next k step; after the second-to-last, every
+  // read of this stage has been issued: wait for them and for stage s+1, then the
+  // stage's barrier; the last k step pairs its MFMAs with the loads of a later stage
+  // into this stage's slots and the first 8 with the reads of stage s+1's k step 0.
+  constexpr int RPM = MX4 ? 1 : 2;  // fragment reads per paired MFMA
   auto iter = [&](auto U, int s) {
     constexpr int u = decltype(U)::value;
     constexpr int sa = u % NA, sb = u % NB;
     constexpr int sa1 = (u + 1) % NA, sb1 = (u + 1) % NB;
-    // k step 0: MFMAs on (fa0, fb0); fragments of k step 1 into (fa1, fb1)
     pack_sc(sa, sb);
-    read_ks(sa, sb, 1, fa1, fb1);
-    mfma_ks(ic<0>{}, fa0, fb0);
+    auto kstep = [&](auto KS) {
+      constexpr int ks = decltype(KS)::value;
+      constexpr bool last = ks == KSTEPS - 1;
+      if constexpr (last) {
+        read_ks(sa1, sb1, 0, fa0, fb0);
+        if constexpr (DEEP == 1) {
+          issue_B(sb, s + 2);
+          issue_A(sa, s + 3);
+        } else if constexpr (DEEP == 2) {
+          issue_A(sa, s + 2);
+          issue_B(sb, s + 3);
+        } else {
+          issue_A(sa, s + 2);
+          issue_B(sb, s + 2);
+        }
+      } else if constexpr (ks & 1) {
+        read_ks(sa, sb, ks + 1, fa0, fb0);
+      } else {
+        read_ks(sa, sb, ks + 1, fa1, fb1);
+      }
+      if constexpr (ks & 1) mfma_ks(KS, fa1, fb1);
+      else mfma_ks(KS, fa0, fb0);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    // stage s+1 landed (only the deep operand's stage s+2 may still be in flight); this
-    // wave's reads of stage s done
-    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(DEEP ? LPO : 0));
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    // k step 1: MFMAs on (fa1, fb1); fragments of stage s+1, k step 0 into (fa0, fb0);
-    // loads of the shallow operand's stage s+2 and then the deep one's stage s+3 into
-    // the slots of stage s
-    read_ks(sa1, sb1, 0, fa0, fb0);
-    if constexpr (DEEP == 1) {
-      issue_B(sb, s + 2);
-      issue_A(sa, s + 3);
-    } else if constexpr (DEEP == 2) {
-      issue_A(sa, s + 2);
-      issue_B(sb, s + 3);
-    } else {
-      issue_A(sa, s + 2);
-      issue_B(sb, s + 2);
-    }
-    mfma_ks(ic<1>{}, fa1, fb1);
+      for (int q = 0; q < 8; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+        if constexpr (last) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      for (int q = 0; q < 8; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (last) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (ks == KSTEPS - 2) {
+        // stage s+1 landed (only the deep operand's stage s+2 may still be in flight);
+        // this wave's reads of stage s done
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(DEEP ? LPO : 0));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    kstep(ic<0>{});
+    kstep(ic<1>{});
+    if constexpr (KSTEPS == 4) {
+      kstep(ic<2>{});
+      kstep(ic<3>{});
     }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
   };
   constexpr int UNR = DEEP ? 6 : 2;
   int s = 0;
@@ -1527,7 +1591,9 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
     return run_1w<KIND_FP8, 1, 1>(p, s, "gemm1w_fp8_e5m2_e5m2_256x256_deepA", "gemm1w_fp8_e5m2_e5m2_256x256_deepB");
   }
   if (g.a_fmt == E2M1) {
-    if (g.mx_panel) return run<KIND_MX4, 4, 4, true>(p, s, "gemm4_mxfp4_e2m1_e2m1_256x256_pingpong_panel");
+    if (g.mx_panel)
+      return run_1w<KIND_MX4, 4, 4>(p, s, "gemm1w_mxfp4_e2m1_e2m1_256x256_panel_deepA",
+                                    "gemm1w_mxfp4_e2m1_e2m1_256x256_panel_deepB");
     return run<KIND_MX4, 4, 4>(p, s, "gemm4_mxfp4_e2m1_e2m1_256x256_pingpong");
   }
   if (g.mx && g.mx_panel) {

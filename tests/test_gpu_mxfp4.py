@@ -222,7 +222,8 @@ def test_mxfp4_gemm_full_5b_shape_sampled(stage):
                    F.dequantize(qb[cols], eb[cols]), 1.0, "bf16")
 
 
-# the panel layout of the same scales: bit-identical to the row-major MXFP4 GEMM
+# the panel layout of the same scales (the one-wave kernel): bit-identical to the
+# row-major MXFP4 GEMM (the ping-pong kernel)
 @pytest.mark.parametrize("mnk", [(32, 32, 256), (300, 272, 512), (520, 400, 1280), (1, 16, 256),
                                  (256, 256, 4096)], ids=str)
 def test_mxfp4_gemm_panel_scales_bit_identical(mnk):
@@ -236,7 +237,8 @@ def test_mxfp4_gemm_panel_scales_bit_identical(mnk):
                       gran=B.TE_GRAN_MX_BLOCK32)
         B.te_fp8_gemm(dev_u8(qa), "E2M1", dev_u8(pa), dev_u8(qb), "E2M1", dev_u8(pb), d2,
                       gran=B.TE_GRAN_MX_BLOCK32_PANEL)
-        assert B.te_gemm_variant() == "gemm4_mxfp4_e2m1_e2m1_256x256_pingpong_panel"
+        deep = "deepA" if m >= n else "deepB"  # the operand with more rows gets three stage slots
+        assert B.te_gemm_variant() == f"gemm1w_mxfp4_e2m1_e2m1_256x256_panel_{deep}"
         assert torch.equal(d1, d2), (mnk, odt)
 
 
