@@ -1648,7 +1648,7 @@ int persistent_grid(const void* kernel, int64_t units, int64_t per_block, int ma
 // the cast-transpose and the row-wise MX copy; the column-wise MX copy, which
 // spends more time per tile in LDS, prefers a full CU.
 constexpr int kCapFlat = 4;
-constexpr int kCapCT = 2;
+constexpr int kCapCT = 4;
 constexpr int kCapMxRow = 2;
 constexpr int kCapMxCol = 8;
 constexpr int kCapLn = 8;  // LayerNorm: four rows per block, one per wave
