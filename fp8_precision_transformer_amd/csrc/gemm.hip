@@ -1154,8 +1154,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
   // MX (panel-layout E8M0 scales): the dword of row r and 128-element group g is dword
   // ((r / 256) * G + g) * 256 + r % 256 (G = k / 128; a stage holds one group of FP8,
   // two of E2M1); lane l loads rows wm + l and wm + 64 + l of A (wn + l, wn + 64 + l of
-  // B) for a stage, together with the stage's operand loads; at the stage's start the
-  // half-waves swap row groups and each lane keeps the bytes of its k blocks.
+  // B) for a stage, in k step 0 of the stage that issues the stage's operand loads (the
+  // last k step's scheduling slots are taken by those); once the stage before it has
+  // passed its barrier, the half-waves swap row groups and each lane keeps the bytes of
+  // its k blocks, into the second of two sets of packed scales, so that the exchange
+  // runs beside that stage's last MFMAs rather than ahead of the stage's first.
   const uint32_t* scA = nullptr;
   const uint32_t* scB = nullptr;
   const int G = S * SDW;
@@ -1186,12 +1189,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
   };
   // packed scales: FP8 MX: byte 2h + (g & 1) of pA[g >> 1] is block 2h + lk of row group g
   // (two row groups per dword); E2M1: byte sel(h) of pA[g] is block 2h + lk of row group g
-  uint32_t pA[4] = {0u, 0u, 0u, 0u}, pB[4] = {0u, 0u, 0u, 0u};
-  auto pack_sc = [&](int sa_set, int sb_set) {
+  // (two sets: the stage's, and the next stage's being packed)
+  uint32_t pA2[2][4] = {}, pB2[2][4] = {};
+  // v_perm_b32 selector over {w1, w0}: bytes lk and 2 + lk of w0 and of w1, interleaved
+  const uint32_t psel = 0x06020400u + 0x01010101u * static_cast<uint32_t>(lk);
+  auto pack_sc = [&](int sa_set, int sb_set, int buf) {
+    uint32_t (&pA)[4] = pA2[buf];
+    uint32_t (&pB)[4] = pB2[buf];
     if constexpr (MX) {
-      auto pick = [&](uint32_t w0, uint32_t w1) {
-        return ((w0 >> (8 * lk)) & 0x00ff00ffu) | (((w1 >> (8 * lk)) & 0x00ff00ffu) << 8);
-      };
+      auto pick = [&](uint32_t w0, uint32_t w1) { return __builtin_amdgcn_perm(w1, w0, psel); };
       uint32_t ga[4][SDW], gb[4][SDW];  // dwords of row groups 0..3 for this lane
 #pragma unroll
       for (int d = 0; d < SDW; ++d) {
@@ -1261,8 +1267,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{0};
-  auto mf = [&](auto H, auto I, auto J, const Frag (&fa)[4], const Frag (&fb)[4]) {
+  auto mf = [&](auto PB, auto H, auto I, auto J, const Frag (&fa)[4], const Frag (&fb)[4]) {
     constexpr int h = decltype(H)::value, i = decltype(I)::value, j = decltype(J)::value;
+    const uint32_t (&pA)[4] = pA2[decltype(PB)::value];
+    const uint32_t (&pB)[4] = pB2[decltype(PB)::value];
     if constexpr (MX4) {
       constexpr int sel = ((h & 1) << 1) | (h >> 1);
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
@@ -1277,12 +1285,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AF, BF, 0, 0, 0, 0);
     }
   };
-  auto mfma_ks = [&](auto H, const Frag (&fa)[4], const Frag (&fb)[4]) {
+  auto mfma_ks = [&](auto PB, auto H, const Frag (&fa)[4], const Frag (&fb)[4]) {
     auto row = [&](auto I) {
-      mf(H, I, ic<0>{}, fa, fb);
-      mf(H, I, ic<1>{}, fa, fb);
-      mf(H, I, ic<2>{}, fa, fb);
-      mf(H, I, ic<3>{}, fa, fb);
+      mf(PB, H, I, ic<0>{}, fa, fb);
+      mf(PB, H, I, ic<1>{}, fa, fb);
+      mf(PB, H, I, ic<2>{}, fa, fb);
+      mf(PB, H, I, ic<3>{}, fa, fb);
     };
     row(ic<0>{});
     row(ic<1>{});
@@ -1305,41 +1313,57 @@ __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((DEEP ? 3 : 2) * LPO));  // stage 0 landed
   __builtin_amdgcn_s_barrier();
   read_ks(0, 0, 0, fa0, fb0);
+  pack_sc(0, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
 
   // one stage: k steps 0 .. KSTEPS-1.  Every k step but the last pairs its first 8
-  // MFMAs with the fragment reads of the next k step; after the second-to-last, every
-  // read of this stage has been issued: wait for them and for stage s+1, then the
+  // MFMAs with the fragment reads of the next k step (MX: k step 0 pairs its last MFMAs
+  // with the scale loads of the stages the last k step loads); after the second-to-last,
+  // every read of this stage has been issued: wait for them and for stage s+1, then the
   // stage's barrier; the last k step pairs its MFMAs with the loads of a later stage
-  // into this stage's slots and the first 8 with the reads of stage s+1's k step 0.
+  // into this stage's slots and the first 8 with the reads of stage s+1's k step 0, and
+  // packs stage s+1's scales.
   constexpr int RPM = MX4 ? 1 : 2;  // fragment reads per paired MFMA
   auto iter = [&](auto U, int s) {
     constexpr int u = decltype(U)::value;
     constexpr int sa = u % NA, sb = u % NB;
     constexpr int sa1 = (u + 1) % NA, sb1 = (u + 1) % NB;
-    pack_sc(sa, sb);
+    constexpr int pb = u & 1;
     auto kstep = [&](auto KS) {
       constexpr int ks = decltype(KS)::value;
       constexpr bool last = ks == KSTEPS - 1;
+      if constexpr (ks == 0 && MX) {
+        if constexpr (DEEP == 1) {
+          load_scB(sb, s + 2);
+          load_scA(sa, s + 3);
+        } else if constexpr (DEEP == 2) {
+          load_scA(sa, s + 2);
+          load_scB(sb, s + 3);
+        } else {
+          load_scA(sa, s + 2);
+          load_scB(sb, s + 2);
+        }
+      }
       if constexpr (last) {
         read_ks(sa1, sb1, 0, fa0, fb0);
+        pack_sc(sa1, sb1, pb ^ 1);  // stage s+1 landed at the last wait
         if constexpr (DEEP == 1) {
-          issue_B(sb, s + 2);
-          issue_A(sa, s + 3);
+          issue_op(rsB, slotB(sb), s + 2);
+          issue_op(rsA, slotA(sa), s + 3);
         } else if constexpr (DEEP == 2) {
-          issue_A(sa, s + 2);
-          issue_B(sb, s + 3);
+          issue_op(rsA, slotA(sa), s + 2);
+          issue_op(rsB, slotB(sb), s + 3);
         } else {
-          issue_A(sa, s + 2);
-          issue_B(sb, s + 2);
+          issue_op(rsA, slotA(sa), s + 2);
+          issue_op(rsB, slotB(sb), s + 2);
         }
       } else if constexpr (ks & 1) {
         read_ks(sa, sb, ks + 1, fa0, fb0);
       } else {
         read_ks(sa, sb, ks + 1, fa1, fb1);
       }
-      if constexpr (ks & 1) mfma_ks(KS, fa1, fb1);
-      else mfma_ks(KS, fa0, fb0);
+      if constexpr (ks & 1) mfma_ks(ic<pb>{}, KS, fa1, fb1);
+      else mfma_ks(ic<pb>{}, KS, fa0, fb0);
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -1349,13 +1373,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if constexpr (last) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        if (last || (ks == 0 && MX && q < 4 * SDW)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (ks == KSTEPS - 2) {
-        // stage s+1 landed (only the deep operand's stage s+2 may still be in flight);
-        // this wave's reads of stage s done
-        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(DEEP ? LPO : 0));
+        // stage s+1 landed (only the deep operand's stage s+2 and the scales issued in
+        // k step 0 may still be in flight); this wave's reads of stage s done
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((DEEP ? 8 : 0) + (MX ? 4 * SDW : 0)));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
       }

@@ -1,7 +1,8 @@
 // Measurement probes, built into libte_peak.so and driven by microbench.py:
 //  - k_peak: MFMA-only throughput with register operands, no memory traffic in the
-//    loop: the sustained FP8 (32x32x64 f8f6f4) and BF16 (32x32x16) matrix-core rate
-//    under the clocks the device actually runs, as a ceiling beside the published peak;
+//    loop: the sustained FP8 (32x32x64 f8f6f4), BF16 (32x32x16), MXFP8 and MXFP4
+//    (block-scaled 32x32x64 with the scales in registers) matrix-core rates under the
+//    clocks the device actually runs, as a ceiling beside the published peak;
 //  - k_copy: a plain 16-byte-per-lane device copy of known size, the reference that
 //    HBM byte counters (FETCH_SIZE, WRITE_SIZE) are calibrated against, and the
 //    practical streaming rate (read + write) a memory-bound kernel can reach;
@@ -18,14 +19,19 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-template <bool BF16>
+// KIND 0: FP8 (the scaled instruction with constant zero scales, which the compiler emits
+// as the plain v_mfma_f32_32x32x64_f8f6f4), 1: BF16, 2: MXFP8 (v_mfma_scale with E8M0
+// scales in registers), 3: MXFP4 (E2M1 operands, scales in registers)
+template <int KIND>
 __global__ __launch_bounds__(256, 1) void k_peak(const int* seed, float* out, int iters) {
+  constexpr bool BF16 = KIND == 1;
   const int t = threadIdx.x + seed[0];
   v8i a, b;
   for (int i = 0; i < 8; ++i) {
     a[i] = (t * 131 + i * 7) & 0x3f3f3f3f;
     b[i] = (t * 17 + i * 3) & 0x3f3f3f3f;
   }
+  const int sc = 0x7f7f7f7f ^ (seed[0] & 1);  // E8M0 unit scales, not known at compile time
   v16f acc[16];
   for (int i = 0; i < 16; ++i) acc[i] = v16f{0};
   for (int it = 0; it < iters; ++it) {
@@ -35,6 +41,10 @@ __global__ __launch_bounds__(256, 1) void k_peak(const int* seed, float* out, in
         const v8bf av = __builtin_bit_cast(v8bf, __builtin_shufflevector(a, a, 0, 1, 2, 3));
         const v8bf bv = __builtin_bit_cast(v8bf, __builtin_shufflevector(b, b, 0, 1, 2, 3));
         acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i], 0, 0, 0);
+      } else if constexpr (KIND == 2) {
+        acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i], 0, 0, 0, sc, 1, sc);
+      } else if constexpr (KIND == 3) {
+        acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i], 4, 4, 0, sc, 1, sc);
       } else {
         acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i], 0, 0, 0, 0, 0, 0);
       }
@@ -46,12 +56,16 @@ __global__ __launch_bounds__(256, 1) void k_peak(const int* seed, float* out, in
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
-extern "C" int te_peak_launch(int bf16, int blocks, int iters, const int* seed, float* out, void* stream) {
+// kind: 0 FP8, 1 BF16, 2 MXFP8, 3 MXFP4 (see k_peak)
+extern "C" int te_peak_launch(int kind, int blocks, int iters, const int* seed, float* out, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (bf16)
-    hipLaunchKernelGGL((k_peak<true>), dim3(blocks), dim3(256), 0, st, seed, out, iters);
-  else
-    hipLaunchKernelGGL((k_peak<false>), dim3(blocks), dim3(256), 0, st, seed, out, iters);
+  switch (kind) {
+    case 0: hipLaunchKernelGGL((k_peak<0>), dim3(blocks), dim3(256), 0, st, seed, out, iters); break;
+    case 1: hipLaunchKernelGGL((k_peak<1>), dim3(blocks), dim3(256), 0, st, seed, out, iters); break;
+    case 2: hipLaunchKernelGGL((k_peak<2>), dim3(blocks), dim3(256), 0, st, seed, out, iters); break;
+    case 3: hipLaunchKernelGGL((k_peak<3>), dim3(blocks), dim3(256), 0, st, seed, out, iters); break;
+    default: return 1;
+  }
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

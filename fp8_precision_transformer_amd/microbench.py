@@ -314,9 +314,10 @@ def peak(args):
     blocks = 256 * args.waves_per_cu  # one 4-wave block per CU per wave slot
     out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    for kind in ("fp8", "bf16"):
-        bf = 1 if kind == "bf16" else 0
-        fn = lambda: L.te_peak_launch(bf, blocks, args.iters, ctypes.c_void_p(seed.data_ptr()),  # noqa: E731
+    kinds = ((0, "fp8"), (1, "bf16"), (2, "mxfp8"), (3, "mxfp4"))
+    for code, kind in kinds * args.repeat:  # later passes run at the clocks the first settled
+        bf = code == 1
+        fn = lambda: L.te_peak_launch(code, blocks, args.iters, ctypes.c_void_p(seed.data_ptr()),  # noqa: E731
                                       ctypes.c_void_p(out.data_ptr()), st)
         ms = _time(fn, 5, 2)
         flop_per_mfma = 2 * 32 * 32 * (16 if bf else 64)
@@ -368,6 +369,7 @@ def main():
     k = sub.add_parser("peak")
     k.add_argument("--iters", type=int, default=4096)
     k.add_argument("--waves-per-cu", type=int, default=1)
+    k.add_argument("--repeat", type=int, default=2)
     args = p.parse_args()
     torch.cuda.set_device(0)
     {"gemm": gemm, "cast": cast, "peak": peak, "layer": layer, "copy": copy, "lib": lib, "stream": stream}[args.cmd](args)
