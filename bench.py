@@ -66,21 +66,21 @@ MI355X_HBM_GBS = 8000.0           # HBM3E (published)
 MEASURED_TRAFFIC = {
     # FP8 GEMM: mean over the layer's 12 GEMM launches (microbench layer --kind fp8)
     "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                 "sha256": "c2cfe8aa6371ccf95f4a540c11ba262cc27fa751dd3109eb3dc06fe550753f1d",
-                 "bytes_per_launch": 1668072618},
+                 "sha256": "0cb9e0976af0c83ab16158d969375fda2177e7c208a43fcbb999787c4cb2191e",
+                 "bytes_per_launch": 1650924075},
     # delayed-scaling quantizers of one layer in autocast mode (24 casts and cast-transposes),
     # summed over the layer's launches (bench.py --modes fp8_delayed_autocast under --pmc)
     "quant_delayed_layer": {"source": "fp8_precision_transformer_amd/csrc/quant.hip",
-                            "sha256": "f877c26bcbfaa78d0d35383ce0865f410e6dd6a856f6c21125e061b096d2d5b5",
-                            "bytes_per_launch": 7452565263},
+                            "sha256": "00d6d3c167b470c62680a963531bd63d00fd7f15c0db436362cc38a3c87cfa55",
+                            "bytes_per_launch": 7452996527},
     # MXFP8 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mxp)
     "gemm_mxfp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "c2cfe8aa6371ccf95f4a540c11ba262cc27fa751dd3109eb3dc06fe550753f1d",
-                   "bytes_per_launch": 1877983316},
+                   "sha256": "0cb9e0976af0c83ab16158d969375fda2177e7c208a43fcbb999787c4cb2191e",
+                   "bytes_per_launch": 1717656536},
     # MXFP4 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mx4p)
     "gemm_mxfp4": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "c2cfe8aa6371ccf95f4a540c11ba262cc27fa751dd3109eb3dc06fe550753f1d",
-                   "bytes_per_launch": 881414668},
+                   "sha256": "0cb9e0976af0c83ab16158d969375fda2177e7c208a43fcbb999787c4cb2191e",
+                   "bytes_per_launch": 928328214},
 }
 
 
