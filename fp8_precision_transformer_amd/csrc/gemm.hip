@@ -1082,8 +1082,9 @@ const char* splitk_name(const char* name) {
 // one that does not stay in the last-level cache on the long-k shapes) gets three,
 // loaded two stages ahead, the other two (DEEP 1: A deep, 2: B deep).  Each slot is its
 // own LDS array, so the compiler can tell the loads into one slot from the reads of
-// another and interleave them.  Past the last stage the loads read zeros or the next
-// rows into slots that are never read again, so every iteration has the same shape.
+// another and interleave them.  Past the last stage the loads are sent out of range:
+// they fetch nothing and fill slots that are never read again, so every iteration has
+// the same shape.
 // Results are bit-identical to k_gemm4's: every output sums the same MFMAs in the same
 // k order.
 // ============================================================================
@@ -1118,6 +1119,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
   const int tm = first_m + in_g % gsz;
   const int tn = in_g / gsz;
   const int m0 = tm * BM, n0 = tn * BN;
+  // per-tensor scale_inv values, read once at the start (scalar loads; the kernel never
+  // writes them)
+  float sa = 1.0f, sb = 1.0f;
+  if constexpr (!MX) {
+    sa = *(const __attribute__((address_space(4))) float*)(reinterpret_cast<uintptr_t>(p.a_scale));
+    sb = *(const __attribute__((address_space(4))) float*)(reinterpret_cast<uintptr_t>(p.b_scale));
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1134,16 +1142,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
   const uint32_t ld_base = static_cast<uint32_t>(wave * 64 + (lane >> 3)) * static_cast<uint32_t>(p.KB);
   const int S = (p.KB + PK - 1) / PK;
   // per instruction t: the lane's byte offset in stage 0; stage st adds 128 st.  With k a
-  // multiple of 128 every chunk of a real stage is inside its row; past the last stage
-  // the offsets run into the next rows or past the buffer (zeros), into a slot that is
-  // never read again.  A ragged k takes k_gemm4.
+  // multiple of 128 every chunk of a real stage is inside its row; the loads past the
+  // last stage are sent out of range.  A ragged k takes k_gemm4.
   uint32_t voff[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t)
     voff[t] = ld_base + static_cast<uint32_t>(t * 8) * static_cast<uint32_t>(p.KB) +
               static_cast<uint32_t>((c0 ^ (t & 3)) << 4);
   auto issue_op = [&](const v4i& rs, uint8_t* dst, int st) {
-    const uint32_t kb = static_cast<uint32_t>(st) * PK;
+    // past the last stage: an offset beyond the buffer's range, so the load fetches
+    // nothing (it writes zeros into a slot that is never read again)
+    const uint32_t kb = st < S ? static_cast<uint32_t>(st) * PK : 0x40000000u;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int off = static_cast<int>(voff[t] + kb);
@@ -1414,24 +1423,32 @@ __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
   __builtin_amdgcn_s_barrier();
 
   // ---- epilogue: scale, bias, round; staged through LDS, 64 x 64 floats per pass ----
-  float sa = 1.0f, sb = 1.0f;
-  if constexpr (!MX) {
-    sa = *static_cast<const float*>(p.a_scale);
-    sb = *static_cast<const float*>(p.b_scale);
-  }
   constexpr int kEpPitch = 256;
   float* ep = reinterpret_cast<float*>((wave & 2 ? sA1 : sA0) + (wave & 1) * 64 * kEpPitch);
+  // the bias of this lane's four columns, fetched together (one memory latency)
+  float bias4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (p.bias != nullptr) {
+    // columns past n read column n - 1 (every load issued unconditionally) and take 0
+    uint32_t raw[4];
+    if (p.bias_bf16) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = min(n0 + wn + q * 32 + lr, p.N - 1);
+        raw[q] = static_cast<uint32_t>(static_cast<const uint16_t*>(p.bias)[col]) << 16;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = min(n0 + wn + q * 32 + lr, p.N - 1);
+        raw[q] = static_cast<const uint32_t*>(p.bias)[col];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bias4[q] = n0 + wn + q * 32 + lr < p.N ? __uint_as_float(raw[q]) : 0.0f;
+  }
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
-    float bias_v[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn + hf * 64 + j * 32 + lr;
-      bias_v[j] = 0.0f;
-      if (p.bias != nullptr && col < p.N)
-        bias_v[j] = p.bias_bf16 ? __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p.bias)[col]) << 16)
-                                : static_cast<const float*>(p.bias)[col];
-    }
+    const float bias_v[2] = {bias4[2 * hf], bias4[2 * hf + 1]};
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
