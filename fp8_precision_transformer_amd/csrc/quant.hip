@@ -503,15 +503,39 @@ __global__ __launch_bounds__(256) void k_dbias_reduce(const float* __restrict__ 
 //   y = ((x - mu) * rsigma) * gamma + beta,  q = satRNE(fl32(y * scale)),
 // every operation a separately rounded fp32 operation.  One wave per row (a block
 // holds four rows, persistent over row groups): lane l takes the 16-byte chunks
-// l, l + 64, ... of the row; up to kLnReg chunks per lane (4096 bf16 / 2048 fp32
-// columns) stay in registers, wider rows are re-read from cache for the second and
-// third pass.  Sums run per lane in chunk order, then over the wave by an xor
-// butterfly (every lane ends with the same bits), so a run is reproducible and no
-// block barrier is needed.  MODE 0: delayed scaling (amax of y + cast in one
-// launch); MODE 1: current scaling's first pass (statistics, amax of y); MODE 2: its
-// cast pass with the scale from *amax.
+// l, l + 64, ... of the row.  Rows of up to NREG chunks per lane (two for rows of up
+// to 128 chunks, else kLnReg: 4096 bf16 / 2048 fp32 columns) stay in registers, and
+// the wave loads its next row while it works on the current one; gamma and beta then
+// sit in LDS, staged once per block (register use allows two blocks per CU).
+// Wider rows are re-read from cache for the second and third pass.  Sums run per
+// lane over four partial sums in chunk order (one per element slot j mod 4), then
+// over the wave by an xor butterfly (every lane ends with the same bits), so a run is
+// reproducible and no block barrier is needed in the row loop.  MODE 0: delayed
+// scaling (amax of y + cast in one launch); MODE 1: current scaling's first pass
+// (statistics, amax of y); MODE 2: its cast pass with the scale from *amax.
 // ----------------------------------------------------------------------------
 constexpr int kLnReg = 8;
+constexpr int kLnParamBytes = 16384;  // gamma or beta staged in LDS (4096 fp32 values)
+
+// Raw buffer access for the rows of the register path: offsets at or past num_records
+// load zeros and drop stores, so a lane's chunks past the row end, the rows past the
+// last one and the lanes that do not write a row statistic need no branch (the
+// compiler then counts the loads in flight exactly and keeps the next row's loads
+// outstanding while the current row is worked on).
+typedef int ln_v4i __attribute__((ext_vector_type(4)));
+typedef int ln_v2i __attribute__((ext_vector_type(2)));
+__device__ ln_v4i ln_buffer_load4(ln_v4i rsrc, int voffset, int soffset, int aux) __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+__device__ void ln_buffer_store2(ln_v2i data, ln_v4i rsrc, int voffset, int soffset, int aux) __asm("llvm.amdgcn.raw.buffer.store.v2i32");
+__device__ void ln_buffer_store1(int data, ln_v4i rsrc, int voffset, int soffset, int aux) __asm("llvm.amdgcn.raw.buffer.store.i32");
+__device__ __forceinline__ ln_v4i ln_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  ln_v4i r;
+  r[0] = static_cast<int>(a & 0xffffffffu);
+  r[1] = static_cast<int>(a >> 32);  // stride 0: raw byte-addressed buffer
+  r[2] = static_cast<int>(bytes);
+  r[3] = 0x00020000;
+  return r;
+}
 
 // EV consecutive gamma or beta values from column c (16-byte aligned vectors)
 template <typename P, int EV>
@@ -548,7 +572,7 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-template <typename T, typename P, bool E5M2, int MODE>
+template <typename T, typename P, bool E5M2, int MODE, int NREG>
 __global__ __launch_bounds__(kThreads) void k_layernorm(const T* __restrict__ x, int64_t R, int64_t C,
                                                         const P* __restrict__ gamma, const P* __restrict__ beta,
                                                         float eps, float* __restrict__ scale,
@@ -558,7 +582,9 @@ __global__ __launch_bounds__(kThreads) void k_layernorm(const T* __restrict__ x,
                                                         AmaxWork* __restrict__ work, int flags) {
   constexpr int EV = 16 / static_cast<int>(sizeof(T));  // elements per 16-byte chunk
   constexpr int kWaves = kThreads / 64;
-  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  // gamma at [0, kLnParamBytes), beta at [kLnParamBytes, 2 kLnParamBytes)
+  __shared__ uint4 prm[2 * kLnParamBytes / 16];
+  const int t = threadIdx.x, lane = t & 63, wid = __builtin_amdgcn_readfirstlane(t >> 6);
   float s = 1.0f;
   if constexpr (MODE == 0) {
     s = *scale;
@@ -572,90 +598,192 @@ __global__ __launch_bounds__(kThreads) void k_layernorm(const T* __restrict__ x,
     }
   }
   const int64_t nch = C / EV;
-  const bool in_regs = nch <= 64 * kLnReg;
+  const int64_t pbytes = C * static_cast<int64_t>(sizeof(P));
+  const bool fast = nch <= 64 * NREG && pbytes <= kLnParamBytes;
   const float inv_c = 1.0f / static_cast<float>(C);
   uint32_t m = 0u;  // running max of |y| as magnitude bits
-  for (int64_t row = static_cast<int64_t>(blockIdx.x) * kWaves + wid; row < R;
-       row += static_cast<int64_t>(gridDim.x) * kWaves) {
-    const T* xr = x + row * C;
-    auto load = [&](int64_t ch) { return *reinterpret_cast<const uint4*>(xr + ch * EV); };
-    uint4 reg[kLnReg];
-    float acc = 0.0f;
-    if (in_regs) {
+  const uint8_t* gl = reinterpret_cast<const uint8_t*>(prm);
+  const uint8_t* bl = gl + kLnParamBytes;
+
+  // y and its code for one chunk: g, b the chunk's gamma and beta
+  auto out_vals = [&](const float (&v)[EV], const float (&g)[EV], const float (&b)[EV], float mean, float rs,
+                      int64_t row, int64_t ch) {
+    float y[EV];
 #pragma unroll
-      for (int k = 0; k < kLnReg; ++k) {
-        const int64_t ch = lane + 64 * k;
-        if (ch < nch) reg[k] = load(ch);
-      }
-#pragma unroll
-      for (int k = 0; k < kLnReg; ++k) {
-        if (lane + 64 * k < nch) {
-          float v[EV];
-          unpack16<T>(reg[k], v);
-#pragma unroll
-          for (int j = 0; j < EV; ++j) acc = __fadd_rn(acc, v[j]);
-        }
-      }
-    } else {
-      for (int64_t ch = lane; ch < nch; ch += 64) {
-        float v[EV];
-        unpack16<T>(load(ch), v);
-#pragma unroll
-        for (int j = 0; j < EV; ++j) acc = __fadd_rn(acc, v[j]);
-      }
+    for (int j = 0; j < EV; ++j) {
+      y[j] = __fadd_rn(__fmul_rn(__fmul_rn(__fsub_rn(v[j], mean), rs), g[j]), b[j]);
+      if constexpr (MODE != 2) m = max(m, __float_as_uint(y[j]) & 0x7fffffffu);
     }
-    const float mean = __fmul_rn(wave_sum(acc), inv_c);
-    // squared deviations, then the output, chunk by chunk (from registers or cache)
-    auto sq_chunk = [&](const uint4& raw) {
-      float v[EV];
-      unpack16<T>(raw, v);
-#pragma unroll
-      for (int j = 0; j < EV; ++j) {
-        const float d = __fsub_rn(v[j], mean);
-        acc = __fadd_rn(acc, __fmul_rn(d, d));
-      }
-    };
-    acc = 0.0f;
-    if (in_regs) {
-#pragma unroll
-      for (int k = 0; k < kLnReg; ++k)
-        if (lane + 64 * k < nch) sq_chunk(reg[k]);
-    } else {
-      for (int64_t ch = lane; ch < nch; ch += 64) sq_chunk(load(ch));
+    if constexpr (MODE != 1) {
+      uint8_t* o = out + row * C + ch * EV;
+      if constexpr (EV == 8)
+        *reinterpret_cast<uint2*>(o) = make_uint2(quant4<E5M2>(y[0], y[1], y[2], y[3], s),
+                                                  quant4<E5M2>(y[4], y[5], y[6], y[7], s));
+      else
+        *reinterpret_cast<uint32_t*>(o) = quant4<E5M2>(y[0], y[1], y[2], y[3], s);
     }
-    const float var = __fmul_rn(wave_sum(acc), inv_c);
-    const float rs = 1.0f / __fsqrt_rn(__fadd_rn(var, eps));
+  };
+  auto stats_out = [&](int64_t row, float mean, float rs) {
     if (MODE != 2 && lane == 0) {
       if (mu_out != nullptr) mu_out[row] = mean;
       if (rs_out != nullptr) rs_out[row] = rs;
     }
-    auto out_chunk = [&](const uint4& raw, int64_t ch) {
-      float v[EV], y[EV], g[EV], b[EV];
-      unpack16<T>(raw, v);
-      load_params<P, EV>(gamma, ch * EV, g);
-      load_params<P, EV>(beta, ch * EV, b);
+  };
+
+  if (fast) {
+    const int n16 = static_cast<int>(pbytes / 16);
+    for (int i = t; i < n16; i += kThreads) {
+      prm[i] = reinterpret_cast<const uint4*>(gamma)[i];
+      prm[kLnParamBytes / 16 + i] = reinterpret_cast<const uint4*>(beta)[i];
+    }
+    __syncthreads();
+    // EV parameters of chunk ch from LDS
+    auto lds_params = [&](const uint8_t* base, int64_t ch, float (&o)[EV]) {
+      constexpr int PB = EV * static_cast<int>(sizeof(P));  // 8, 16 or 32 bytes
+      const uint8_t* p = base + ch * PB;
+      if constexpr (sizeof(P) == 4) {
 #pragma unroll
-      for (int j = 0; j < EV; ++j) {
-        y[j] = __fadd_rn(__fmul_rn(__fmul_rn(__fsub_rn(v[j], mean), rs), g[j]), b[j]);
-        if constexpr (MODE != 2) m = max(m, __float_as_uint(y[j]) & 0x7fffffffu);
-      }
-      if constexpr (MODE != 1) {
-        uint8_t* o = out + row * C + ch * EV;
-        if constexpr (EV == 8)
-          *reinterpret_cast<uint2*>(o) = make_uint2(quant4<E5M2>(y[0], y[1], y[2], y[3], s),
-                                                    quant4<E5M2>(y[4], y[5], y[6], y[7], s));
-        else
-          *reinterpret_cast<uint32_t*>(o) = quant4<E5M2>(y[0], y[1], y[2], y[3], s);
+        for (int k = 0; k < EV / 4; ++k) {
+          const uint4 u = reinterpret_cast<const uint4*>(p)[k];
+          o[4 * k] = __uint_as_float(u.x);
+          o[4 * k + 1] = __uint_as_float(u.y);
+          o[4 * k + 2] = __uint_as_float(u.z);
+          o[4 * k + 3] = __uint_as_float(u.w);
+        }
+      } else if constexpr (EV == 8) {
+        const uint4 u = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[2 * i] = bf16_lo(w[i]);
+          o[2 * i + 1] = bf16_hi(w[i]);
+        }
+      } else {
+        const uint2 u = *reinterpret_cast<const uint2*>(p);
+        o[0] = bf16_lo(u.x);
+        o[1] = bf16_hi(u.x);
+        o[2] = bf16_lo(u.y);
+        o[3] = bf16_hi(u.y);
       }
     };
-    if (in_regs) {
+    const uint32_t xrow_bytes = static_cast<uint32_t>(C * static_cast<int64_t>(sizeof(T)));
+    // a row past the last one: an empty buffer (every load reads zeros, nothing fetched)
+    auto load_row = [&](int64_t row, uint4 (&reg)[NREG]) {
+      const bool ok = row < R;
+      const ln_v4i rs = ln_rsrc(x + (ok ? row : 0) * C, ok ? xrow_bytes : 0u);
 #pragma unroll
-      for (int k = 0; k < kLnReg; ++k) {
-        const int64_t ch = lane + 64 * k;
-        if (ch < nch) out_chunk(reg[k], ch);
+      for (int k = 0; k < NREG; ++k) {
+        const ln_v4i v = ln_buffer_load4(rs, (lane + 64 * k) * 16, 0, MODE == 1 ? 0 : 2);
+        reg[k] = make_uint4(static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1]), static_cast<uint32_t>(v[2]),
+                            static_cast<uint32_t>(v[3]));
       }
-    } else {
-      for (int64_t ch = lane; ch < nch; ch += 64) out_chunk(load(ch), ch);
+    };
+    const ln_v4i rs_mu = ln_rsrc(mu_out, mu_out != nullptr && MODE != 2 ? static_cast<uint32_t>(R * 4) : 0u);
+    const ln_v4i rs_rs = ln_rsrc(rs_out, rs_out != nullptr && MODE != 2 ? static_cast<uint32_t>(R * 4) : 0u);
+    auto process = [&](int64_t row, const uint4 (&reg)[NREG]) {
+      // chunks past the row end hold zeros: they add +0 to the sums (no branch)
+      float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int k = 0; k < NREG; ++k) {
+        float v[EV];
+        unpack16<T>(reg[k], v);
+#pragma unroll
+        for (int j = 0; j < EV; ++j) a4[j & 3] = __fadd_rn(a4[j & 3], v[j]);
+      }
+      const float mean = __fmul_rn(wave_sum(__fadd_rn(__fadd_rn(a4[0], a4[1]), __fadd_rn(a4[2], a4[3]))), inv_c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a4[q] = 0.0f;
+#pragma unroll
+      for (int k = 0; k < NREG; ++k) {
+        const bool in_row = lane + 64 * k < nch;
+        float v[EV];
+        unpack16<T>(reg[k], v);
+#pragma unroll
+        for (int j = 0; j < EV; ++j) {
+          const float d = __fsub_rn(v[j], mean);
+          a4[j & 3] = __fadd_rn(a4[j & 3], in_row ? __fmul_rn(d, d) : 0.0f);
+        }
+      }
+      const float var = __fmul_rn(wave_sum(__fadd_rn(__fadd_rn(a4[0], a4[1]), __fadd_rn(a4[2], a4[3]))), inv_c);
+      const float rs = 1.0f / __fsqrt_rn(__fadd_rn(var, eps));
+      // lane 0 writes the row statistics; the other lanes' offsets are out of range
+      const int soff = lane == 0 ? static_cast<int>(row * 4) : static_cast<int>(0x80000000u);
+      ln_buffer_store1(__float_as_int(mean), rs_mu, soff, 0, 0);
+      ln_buffer_store1(__float_as_int(rs), rs_rs, soff, 0, 0);
+      const ln_v4i rs_out_row = ln_rsrc(out + row * C, MODE != 1 ? static_cast<uint32_t>(C) : 0u);
+#pragma unroll
+      for (int k = 0; k < NREG; ++k) {
+        const int64_t ch = lane + 64 * k;
+        const bool in_row = ch < nch;  // lanes past the row end: parameters of chunk 0, store dropped
+        float v[EV], g[EV], b[EV], y[EV];
+        unpack16<T>(reg[k], v);
+        lds_params(gl, in_row ? ch : 0, g);
+        lds_params(bl, in_row ? ch : 0, b);
+#pragma unroll
+        for (int j = 0; j < EV; ++j) {
+          y[j] = __fadd_rn(__fmul_rn(__fmul_rn(__fsub_rn(v[j], mean), rs), g[j]), b[j]);
+          if constexpr (MODE != 2) m = in_row ? max(m, __float_as_uint(y[j]) & 0x7fffffffu) : m;
+        }
+        const int off = static_cast<int>(ch * EV);  // >= C past the row end: dropped
+        if constexpr (EV == 8) {
+          const ln_v2i q = {static_cast<int>(quant4<E5M2>(y[0], y[1], y[2], y[3], s)),
+                            static_cast<int>(quant4<E5M2>(y[4], y[5], y[6], y[7], s))};
+          ln_buffer_store2(q, rs_out_row, off, 0, 0);
+        } else {
+          ln_buffer_store1(static_cast<int>(quant4<E5M2>(y[0], y[1], y[2], y[3], s)), rs_out_row, off, 0, 0);
+        }
+      }
+    };
+    // two register sets: the next row is in flight while the current one is worked on
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
+    int64_t row = static_cast<int64_t>(blockIdx.x) * kWaves + wid;
+    uint4 ra[NREG], rb[NREG];
+    load_row(row, ra);
+    while (row < R) {
+      int64_t nx = row + stride;
+      load_row(nx, rb);
+      process(row, ra);
+      row = nx;
+      if (row >= R) break;
+      nx = row + stride;
+      load_row(nx, ra);
+      process(row, rb);
+      row = nx;
+    }
+  } else {
+    for (int64_t row = static_cast<int64_t>(blockIdx.x) * kWaves + wid; row < R;
+         row += static_cast<int64_t>(gridDim.x) * kWaves) {
+      const T* xr = x + row * C;
+      auto load = [&](int64_t ch) { return *reinterpret_cast<const uint4*>(xr + ch * EV); };
+      float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int64_t ch = lane; ch < nch; ch += 64) {
+        float v[EV];
+        unpack16<T>(load(ch), v);
+#pragma unroll
+        for (int j = 0; j < EV; ++j) a4[j & 3] = __fadd_rn(a4[j & 3], v[j]);
+      }
+      const float mean = __fmul_rn(wave_sum(__fadd_rn(__fadd_rn(a4[0], a4[1]), __fadd_rn(a4[2], a4[3]))), inv_c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a4[q] = 0.0f;
+      for (int64_t ch = lane; ch < nch; ch += 64) {
+        float v[EV];
+        unpack16<T>(load(ch), v);
+#pragma unroll
+        for (int j = 0; j < EV; ++j) {
+          const float d = __fsub_rn(v[j], mean);
+          a4[j & 3] = __fadd_rn(a4[j & 3], __fmul_rn(d, d));
+        }
+      }
+      const float var = __fmul_rn(wave_sum(__fadd_rn(__fadd_rn(a4[0], a4[1]), __fadd_rn(a4[2], a4[3]))), inv_c);
+      const float rs = 1.0f / __fsqrt_rn(__fadd_rn(var, eps));
+      stats_out(row, mean, rs);
+      for (int64_t ch = lane; ch < nch; ch += 64) {
+        float v[EV], g[EV], b[EV];
+        unpack16<T>(load(ch), v);
+        load_params<P, EV>(gamma, ch * EV, g);
+        load_params<P, EV>(beta, ch * EV, b);
+        out_vals(v, g, b, mean, rs, row, ch);
+      }
     }
   }
   if constexpr (MODE != 2) grid_amax_q(__uint_as_float(m), amax, work, (flags & kAccAmax) != 0);
@@ -1644,14 +1772,16 @@ int persistent_grid(const void* kernel, int64_t units, int64_t per_block, int ma
 }
 
 // Resident blocks per compute unit for each persistent kernel, measured on the
-// 5B-layer tensors: two blocks (eight waves) per CU stream best for the flat cast,
-// the cast-transpose and the row-wise MX copy; the column-wise MX copy, which
-// spends more time per tile in LDS, prefers a full CU.
+// 5B-layer tensors: four blocks per CU stream best for the flat cast and the
+// cast-transpose (their input read with nontemporal loads), two for the row-wise MX
+// copy; the column-wise MX copy, which spends more time per tile in LDS, prefers a
+// full CU.  LayerNorm: up to four blocks of four rows (one per wave, each with its next
+// row in flight); its registers allow two.
 constexpr int kCapFlat = 4;
 constexpr int kCapCT = 4;
 constexpr int kCapMxRow = 2;
 constexpr int kCapMxCol = 8;
-constexpr int kCapLn = 8;  // LayerNorm: four rows per block, one per wave
+constexpr int kCapLn = 4;
 
 template <typename T, bool E5M2, int MODE>
 void launch_flat(const T* x, int64_t n, int margin, float* scale, float* scale_inv, float* amax,
@@ -1776,7 +1906,9 @@ template <typename T, typename P, bool E5M2, int MODE>
 void ln_launch(const T* x, int64_t R, int64_t C, const P* g, const P* b, float eps, int margin, float* scale,
                float* sinv, float* amax, uint8_t* out, float* mu, float* rs, AmaxWork* w, int flags,
                hipStream_t st) {
-  const auto fn = k_layernorm<T, P, E5M2, MODE>;
+  // registers per lane for a row: two 16-byte chunks for rows of up to 128 chunks, else eight
+  const bool narrow = C / (16 / static_cast<int64_t>(sizeof(T))) <= 128;
+  const auto fn = narrow ? k_layernorm<T, P, E5M2, MODE, 2> : k_layernorm<T, P, E5M2, MODE, kLnReg>;
   const int grid = persistent_grid(reinterpret_cast<const void*>(fn), R, kThreads / 64, kCapLn);
   hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), 0, st, x, R, C, g, b, eps, scale, sinv, amax, out, mu, rs,
                      margin, w, flags);
