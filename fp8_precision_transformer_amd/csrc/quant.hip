@@ -166,6 +166,26 @@ __device__ __forceinline__ uint4 load_stream(const void* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Raw buffer access: offsets at or past num_records load zeros and drop stores, so
+// optional outputs, lanes past a row end and rows past the last one need no branch.
+// Branch-free loads and stores let the compiler count the memory operations in flight
+// exactly; behind a branch it falls back to waiting for all of them.
+typedef int bv4i __attribute__((ext_vector_type(4)));
+typedef int bv2i __attribute__((ext_vector_type(2)));
+__device__ bv4i buffer_load4(bv4i rsrc, int voffset, int soffset, int aux) __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+__device__ void buffer_store2(bv2i data, bv4i rsrc, int voffset, int soffset, int aux) __asm("llvm.amdgcn.raw.buffer.store.v2i32");
+__device__ void buffer_store1(int data, bv4i rsrc, int voffset, int soffset, int aux) __asm("llvm.amdgcn.raw.buffer.store.i32");
+__device__ void buffer_store4(bv4i data, bv4i rsrc, int voffset, int soffset, int aux) __asm("llvm.amdgcn.raw.buffer.store.v4i32");
+__device__ __forceinline__ bv4i buf_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  bv4i r;
+  r[0] = static_cast<int>(a & 0xffffffffu);
+  r[1] = static_cast<int>(a >> 32);  // stride 0: raw byte-addressed buffer
+  r[2] = static_cast<int>(bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
 // Flat amax + cast: one 16-byte word per lane and load instruction (a wave covers 1 KB
 // contiguous), kFlatU words per lane in flight; the word's EW elements go out as EW
 // bytes.  The cast passes (MODE 0, 2) stream the input; the amax-only pass of current
@@ -250,8 +270,12 @@ __global__ __launch_bounds__(kThreads) void k_amax_cast(const T* __restrict__ x,
 // FP8 bytes go through LDS (pitch 132 bytes); for the transposed output each
 // lane reads a 16 x 4 byte block as 16 dwords, transposes it with byte permutes
 // and writes four 16-byte column runs; 8 consecutive lanes complete one
-// 128-byte line of out_col.  The next tile's loads are issued before the
-// current tile is converted, so each block keeps a tile in flight.
+// 128-byte line of out_col.  The next tile's loads, into the second of two register
+// sets, are issued before the current tile's transposed stores, so each block keeps a
+// tile in flight.  Whole tiles load and store through buffer descriptors with no
+// branch (an absent next tile or output copy is an empty buffer), so the compiler
+// counts the operations in flight exactly instead of waiting for all of them.  A
+// request for the row-wise copy alone (no dbias) is the flat cast.
 // ----------------------------------------------------------------------------
 constexpr int kCT = 128;             // tile edge
 constexpr int kCTPitch = kCT + 4;    // LDS bytes per tile row
@@ -338,10 +362,14 @@ __global__ __launch_bounds__(kThreads) void k_cast_transpose(
   };
   // FAST: one 16-byte load per pass; otherwise element loads with bounds checks
   // (outside the matrix reads as 0), packed into the same raw words.
-  auto load1 = [&](int p, int64_t r0, int64_t c0) {
-    if constexpr (FAST) {
-      const uint8_t* base = reinterpret_cast<const uint8_t*>(x + r0 * C + c0);
-      return load_stream(base + ld_off + p * ld_pass);
+  // the tile's bytes of x from its first element ((kCT - 1) C + kCT elements)
+  const uint32_t tile_x_bytes = static_cast<uint32_t>(((kCT - 1) * C + kCT) * static_cast<int64_t>(sizeof(T)));
+  auto load1 = [&](int p, int64_t r0, int64_t c0, bool valid = true) {
+    if constexpr (FAST) {  // an absent tile (valid false): an empty buffer, zeros, nothing fetched
+      const bv4i rs = buf_rsrc(x + (valid ? r0 * C + c0 : 0), valid ? tile_x_bytes : 0u);
+      const bv4i v = buffer_load4(rs, static_cast<int>(ld_off + p * ld_pass), 0, 2);
+      return make_uint4(static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1]), static_cast<uint32_t>(v[2]),
+                        static_cast<uint32_t>(v[3]));
     } else {
       const int64_t r = r0 + p * RPP + prow;
       uint32_t w[4] = {0u, 0u, 0u, 0u};
@@ -357,9 +385,14 @@ __global__ __launch_bounds__(kThreads) void k_cast_transpose(
   // The tile's registers are reloaded with the next tile as soon as they are consumed:
   // pass by pass without the transposed copy, after all passes with it (the transposed
   // stores then run with the next tile's loads in flight).
-  auto process = [&](uint4 (&raw)[NP], int64_t r0, int64_t c0, bool has1, int64_t r1, int64_t c1) {
+  // raw: this tile's registers; nxt: the next tile's (two sets, alternating, so the loads
+  // of the next tile land in registers the current tile does not use)
+  auto process = [&](uint4 (&raw)[NP], uint4 (&nxt)[NP], int64_t r0, int64_t c0, bool has1, int64_t r1,
+                     int64_t c1) {
     __syncthreads();  // the previous tile's LDS reads are done
-    uint8_t* orow = out_row + r0 * C + c0;
+    // the tile's rows of the row copy ((kCT - 1) C + kCT bytes from its first byte)
+    const bv4i rs_row = buf_rsrc(out_row != nullptr ? out_row + r0 * C + c0 : nullptr,
+                                 out_row != nullptr ? static_cast<uint32_t>((kCT - 1) * C + kCT) : 0u);
     float cs[E];  // DBIAS: this lane's column sums over its rows of the tile (rows past R read 0)
 #pragma unroll
     for (int j = 0; j < E; ++j) cs[j] = 0.0f;
@@ -379,19 +412,21 @@ __global__ __launch_bounds__(kThreads) void k_cast_transpose(
         q[j] = quant4<E5M2>(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3], s);
         lds[(lr * kCTPitch + pcol) / 4 + j] = q[j];
       }
-      if (out_row != nullptr) {
-        if constexpr (FAST) {
-          uint8_t* o = orow + ro_off + p * ro_pass;
-          if constexpr (E == 8) *reinterpret_cast<uint2*>(o) = make_uint2(q[0], q[1]);
-          else *reinterpret_cast<uint32_t*>(o) = q[0];
-        } else if (r0 + lr < R) {
+      if constexpr (FAST) {  // no row copy: an empty buffer, the stores are dropped
+        if constexpr (E == 8) {
+          const bv2i qq = {static_cast<int>(q[0]), static_cast<int>(q[1])};
+          buffer_store2(qq, rs_row, static_cast<int>(ro_off + p * ro_pass), 0, 0);
+        } else {
+          buffer_store1(static_cast<int>(q[0]), rs_row, static_cast<int>(ro_off + p * ro_pass), 0, 0);
+        }
+      } else if (out_row != nullptr) {
+        if (r0 + lr < R) {
           uint8_t* o = out_row + (r0 + lr) * C + c0 + pcol;
 #pragma unroll
           for (int j = 0; j < E; ++j)
             if (c0 + pcol + j < C) o[j] = static_cast<uint8_t>(q[j >> 2] >> (8 * (j & 3)));
         }
       }
-      if (has1 && out_col == nullptr) raw[p] = load1(p, r1, c1);
     }
     if constexpr (DBIAS) {
       // tile column sums, rows in a fixed order (lane passes, then lane groups), so the
@@ -406,10 +441,18 @@ __global__ __launch_bounds__(kThreads) void k_cast_transpose(
         dbias_part[(r0 / kCT) * C + c0 + t] = acc;
       }
     }
-    if (out_col == nullptr) return;
-    if (has1) {
+    // the next tile's loads, in flight during the transposed stores.  FAST: loads and
+    // stores without branches (an absent next tile or output is an empty buffer), so the
+    // compiler counts the operations in flight exactly
+    if constexpr (FAST) {
 #pragma unroll
-      for (int p = 0; p < NP; ++p) raw[p] = load1(p, r1, c1);
+      for (int p = 0; p < NP; ++p) nxt[p] = load1(p, r1, c1, has1);
+    } else {
+      if (has1) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) nxt[p] = load1(p, r1, c1);
+      }
+      if (out_col == nullptr) return;
     }
     __syncthreads();
     uint32_t d[16];
@@ -429,11 +472,15 @@ __global__ __launch_bounds__(kThreads) void k_cast_transpose(
       w[2][j] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
       w[3][j] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
     }
-    if constexpr (FAST) {
-      uint8_t* ocol = out_col + c0 * R + r0;
+    if constexpr (FAST) {  // the tile's columns of the column copy ((kCT - 1) R + kCT bytes)
+      const bv4i rs_col = buf_rsrc(out_col != nullptr ? out_col + c0 * R + r0 : nullptr,
+                                   out_col != nullptr ? static_cast<uint32_t>((kCT - 1) * R + kCT) : 0u);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint4*>(ocol + co_off + i * co_col) = make_uint4(w[i][0], w[i][1], w[i][2], w[i][3]);
+      for (int i = 0; i < 4; ++i) {
+        const bv4i ww = {static_cast<int>(w[i][0]), static_cast<int>(w[i][1]), static_cast<int>(w[i][2]),
+                         static_cast<int>(w[i][3])};
+        buffer_store4(ww, rs_col, static_cast<int>(co_off + i * co_col), 0, 0);
+      }
     } else {
       const int64_t rb = r0 + 16 * rg;
 #pragma unroll
@@ -451,21 +498,31 @@ __global__ __launch_bounds__(kThreads) void k_cast_transpose(
 
   int64_t i = blockIdx.x;
   if (i < ntiles) {
-    uint4 raw[NP];
+    uint4 ra[NP], rb[NP];
     int64_t r0, c0;
     origin(i, r0, c0);
 #pragma unroll
-    for (int p = 0; p < NP; ++p) raw[p] = load1(p, r0, c0);
-    for (;;) {
+    for (int p = 0; p < NP; ++p) ra[p] = load1(p, r0, c0);
+    if constexpr (FAST) {
+      // four dropped stores: every later tile's loads are followed by the four transposed
+      // stores, so the loop is entered with the same operations in flight either way
+      const bv4i none = buf_rsrc(nullptr, 0u);
+      const bv4i zero = {0, 0, 0, 0};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) buffer_store4(zero, none, 16 * k, 0, 0);
+    }
+    auto step = [&](uint4 (&cur)[NP], uint4 (&nxt)[NP]) {  // false after the last tile
       const int64_t i1 = i + gridDim.x;
       const bool has1 = i1 < ntiles;
       int64_t r1 = 0, c1 = 0;
       if (has1) origin(i1, r1, c1);
-      process(raw, r0, c0, has1, r1, c1);
-      if (!has1) break;
+      process(cur, nxt, r0, c0, has1, r1, c1);
       i = i1;
       r0 = r1;
       c0 = c1;
+      return has1;
+    };
+    while (step(ra, rb) && step(rb, ra)) {
     }
   }
   if constexpr (MODE == 0) grid_amax_q(absmax_value<T>(m), amax, work, (flags & kAccAmax) != 0);
@@ -517,27 +574,6 @@ __global__ __launch_bounds__(256) void k_dbias_reduce(const float* __restrict__ 
 constexpr int kLnReg = 8;
 constexpr int kLnParamBytes = 16384;  // gamma or beta staged in LDS (4096 fp32 values)
 
-// Raw buffer access for the rows of the register path: offsets at or past num_records
-// load zeros and drop stores, so a lane's chunks past the row end, the rows past the
-// last one and the lanes that do not write a row statistic need no branch (the
-// compiler then counts the loads in flight exactly and keeps the next row's loads
-// outstanding while the current row is worked on).
-typedef int ln_v4i __attribute__((ext_vector_type(4)));
-typedef int ln_v2i __attribute__((ext_vector_type(2)));
-__device__ ln_v4i ln_buffer_load4(ln_v4i rsrc, int voffset, int soffset, int aux) __asm("llvm.amdgcn.raw.buffer.load.v4i32");
-__device__ void ln_buffer_store2(ln_v2i data, ln_v4i rsrc, int voffset, int soffset, int aux) __asm("llvm.amdgcn.raw.buffer.store.v2i32");
-__device__ void ln_buffer_store1(int data, ln_v4i rsrc, int voffset, int soffset, int aux) __asm("llvm.amdgcn.raw.buffer.store.i32");
-__device__ __forceinline__ ln_v4i ln_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  ln_v4i r;
-  r[0] = static_cast<int>(a & 0xffffffffu);
-  r[1] = static_cast<int>(a >> 32);  // stride 0: raw byte-addressed buffer
-  r[2] = static_cast<int>(bytes);
-  r[3] = 0x00020000;
-  return r;
-}
-
-// EV consecutive gamma or beta values from column c (16-byte aligned vectors)
 template <typename P, int EV>
 __device__ __forceinline__ void load_params(const P* p, int64_t c, float* out) {
   if constexpr (sizeof(P) == 4) {
@@ -670,16 +706,16 @@ __global__ __launch_bounds__(kThreads) void k_layernorm(const T* __restrict__ x,
     // a row past the last one: an empty buffer (every load reads zeros, nothing fetched)
     auto load_row = [&](int64_t row, uint4 (&reg)[NREG]) {
       const bool ok = row < R;
-      const ln_v4i rs = ln_rsrc(x + (ok ? row : 0) * C, ok ? xrow_bytes : 0u);
+      const bv4i rs = buf_rsrc(x + (ok ? row : 0) * C, ok ? xrow_bytes : 0u);
 #pragma unroll
       for (int k = 0; k < NREG; ++k) {
-        const ln_v4i v = ln_buffer_load4(rs, (lane + 64 * k) * 16, 0, MODE == 1 ? 0 : 2);
+        const bv4i v = buffer_load4(rs, (lane + 64 * k) * 16, 0, MODE == 1 ? 0 : 2);
         reg[k] = make_uint4(static_cast<uint32_t>(v[0]), static_cast<uint32_t>(v[1]), static_cast<uint32_t>(v[2]),
                             static_cast<uint32_t>(v[3]));
       }
     };
-    const ln_v4i rs_mu = ln_rsrc(mu_out, mu_out != nullptr && MODE != 2 ? static_cast<uint32_t>(R * 4) : 0u);
-    const ln_v4i rs_rs = ln_rsrc(rs_out, rs_out != nullptr && MODE != 2 ? static_cast<uint32_t>(R * 4) : 0u);
+    const bv4i rs_mu = buf_rsrc(mu_out, mu_out != nullptr && MODE != 2 ? static_cast<uint32_t>(R * 4) : 0u);
+    const bv4i rs_rs = buf_rsrc(rs_out, rs_out != nullptr && MODE != 2 ? static_cast<uint32_t>(R * 4) : 0u);
     auto process = [&](int64_t row, const uint4 (&reg)[NREG]) {
       // chunks past the row end hold zeros: they add +0 to the sums (no branch)
       float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -708,9 +744,9 @@ __global__ __launch_bounds__(kThreads) void k_layernorm(const T* __restrict__ x,
       const float rs = 1.0f / __fsqrt_rn(__fadd_rn(var, eps));
       // lane 0 writes the row statistics; the other lanes' offsets are out of range
       const int soff = lane == 0 ? static_cast<int>(row * 4) : static_cast<int>(0x80000000u);
-      ln_buffer_store1(__float_as_int(mean), rs_mu, soff, 0, 0);
-      ln_buffer_store1(__float_as_int(rs), rs_rs, soff, 0, 0);
-      const ln_v4i rs_out_row = ln_rsrc(out + row * C, MODE != 1 ? static_cast<uint32_t>(C) : 0u);
+      buffer_store1(__float_as_int(mean), rs_mu, soff, 0, 0);
+      buffer_store1(__float_as_int(rs), rs_rs, soff, 0, 0);
+      const bv4i rs_out_row = buf_rsrc(out + row * C, MODE != 1 ? static_cast<uint32_t>(C) : 0u);
 #pragma unroll
       for (int k = 0; k < NREG; ++k) {
         const int64_t ch = lane + 64 * k;
@@ -726,11 +762,11 @@ __global__ __launch_bounds__(kThreads) void k_layernorm(const T* __restrict__ x,
         }
         const int off = static_cast<int>(ch * EV);  // >= C past the row end: dropped
         if constexpr (EV == 8) {
-          const ln_v2i q = {static_cast<int>(quant4<E5M2>(y[0], y[1], y[2], y[3], s)),
+          const bv2i q = {static_cast<int>(quant4<E5M2>(y[0], y[1], y[2], y[3], s)),
                             static_cast<int>(quant4<E5M2>(y[4], y[5], y[6], y[7], s))};
-          ln_buffer_store2(q, rs_out_row, off, 0, 0);
+          buffer_store2(q, rs_out_row, off, 0, 0);
         } else {
-          ln_buffer_store1(static_cast<int>(quant4<E5M2>(y[0], y[1], y[2], y[3], s)), rs_out_row, off, 0, 0);
+          buffer_store1(static_cast<int>(quant4<E5M2>(y[0], y[1], y[2], y[3], s)), rs_out_row, off, 0, 0);
         }
       }
     };
@@ -1846,6 +1882,8 @@ hipError_t cast_transpose_t(const T* x, int64_t R, int64_t C, int mode, int marg
                          part, int64_t{0}, C, dbias);
     return hipGetLastError();
   }
+  // the row-wise copy alone is the flat cast of x
+  if (out_col == nullptr && dbias == nullptr) return amax_cast_t<T, E5M2>(x, R * C, mode, margin, scale, scale_inv, amax, out_row, w, st);
   if (mode == 1) launch_flat<T, E5M2, 1>(x, R * C, margin, scale, scale_inv, amax, nullptr, w, 0, st);
   if (dbias != nullptr) {
     if (current) ct_launch<T, E5M2, 2, true>(x, R, C, margin, scale, scale_inv, amax, out_row, out_col, w, 0, part, st);
