@@ -66,21 +66,21 @@ MI355X_HBM_GBS = 8000.0           # HBM3E (published)
 MEASURED_TRAFFIC = {
     # FP8 GEMM: mean over the layer's 12 GEMM launches (microbench layer --kind fp8)
     "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                 "sha256": "0cb9e0976af0c83ab16158d969375fda2177e7c208a43fcbb999787c4cb2191e",
-                 "bytes_per_launch": 1650924075},
+                 "sha256": "32667088d056ddee50fbc524686cdb61223e000f9ecf6d746900a3a20a6e9774",
+                 "bytes_per_launch": 1704659062},
     # delayed-scaling quantizers of one layer in autocast mode (24 casts and cast-transposes),
     # summed over the layer's launches (bench.py --modes fp8_delayed_autocast under --pmc)
     "quant_delayed_layer": {"source": "fp8_precision_transformer_amd/csrc/quant.hip",
-                            "sha256": "00d6d3c167b470c62680a963531bd63d00fd7f15c0db436362cc38a3c87cfa55",
-                            "bytes_per_launch": 7452996527},
+                            "sha256": "4941dbac0176cdf5a483cc2851be6064b12b075020ed69e8ea321ed72c9545de",
+                            "bytes_per_launch": 7453803153},
     # MXFP8 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mxp)
     "gemm_mxfp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "0cb9e0976af0c83ab16158d969375fda2177e7c208a43fcbb999787c4cb2191e",
-                   "bytes_per_launch": 1717656536},
+                   "sha256": "32667088d056ddee50fbc524686cdb61223e000f9ecf6d746900a3a20a6e9774",
+                   "bytes_per_launch": 1757392320},
     # MXFP4 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mx4p)
     "gemm_mxfp4": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "0cb9e0976af0c83ab16158d969375fda2177e7c208a43fcbb999787c4cb2191e",
-                   "bytes_per_launch": 928328214},
+                   "sha256": "32667088d056ddee50fbc524686cdb61223e000f9ecf6d746900a3a20a6e9774",
+                   "bytes_per_launch": 919346764},
 }
 
 
