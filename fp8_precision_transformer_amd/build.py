@@ -1,8 +1,10 @@
 """Build libte_mi355x.so (gfx950 only) in-tree with hipcc.
 
 Flags that matter for bit-exactness: correctly rounded fp32 division (the scale
-fp8_max / amax and 1 / scale), no fast-math, no denormal flushing.  Packed fp32
-instructions are disabled (-packed-fp32-ops) so plain float code is emitted.
+fp8_max / amax and 1 / scale), no fast-math, no denormal flushing, and no contraction
+of a multiply and an add into one fused operation (-ffp-contract=off), so every
+operation the kernels write is rounded on its own, as the documented formulas state.
+Packed fp32 instructions are disabled (-packed-fp32-ops) so plain float code is emitted.
 Code object v5 keeps the library loadable by the HIP runtime PyTorch ships.
 """
 
@@ -30,6 +32,7 @@ HIP_FLAGS = [
     "-mcode-object-version=5",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-fast-math",
+    "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
     "-Wno-unused-function",
