@@ -71,8 +71,8 @@ MEASURED_TRAFFIC = {
     # delayed-scaling quantizers of one layer in autocast mode (24 casts and cast-transposes),
     # summed over the layer's launches (bench.py --modes fp8_delayed_autocast under --pmc)
     "quant_delayed_layer": {"source": "fp8_precision_transformer_amd/csrc/quant.hip",
-                            "sha256": "4941dbac0176cdf5a483cc2851be6064b12b075020ed69e8ea321ed72c9545de",
-                            "bytes_per_launch": 7453803153},
+                            "sha256": "69668d0fb473dfbdbd4c2f5a64a809fdc5b2c87029c59cf24abc5d7252cb3e29",
+                            "bytes_per_launch": 7453825274},
     # MXFP8 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mxp)
     "gemm_mxfp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
                    "sha256": "32667088d056ddee50fbc524686cdb61223e000f9ecf6d746900a3a20a6e9774",

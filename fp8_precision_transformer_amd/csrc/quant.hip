@@ -635,7 +635,9 @@ __global__ __launch_bounds__(kThreads) void k_layernorm(const T* __restrict__ x,
   }
   const int64_t nch = C / EV;
   const int64_t pbytes = C * static_cast<int64_t>(sizeof(P));
-  const bool fast = nch <= 64 * NREG && pbytes <= kLnParamBytes;
+  // register path: the row fits NREG chunks per lane, gamma and beta fit LDS, and the
+  // statistics' byte offsets (4 row) fit the buffer offsets (below 2^31)
+  const bool fast = nch <= 64 * NREG && pbytes <= kLnParamBytes && R < (int64_t{1} << 29);
   const float inv_c = 1.0f / static_cast<float>(C);
   uint32_t m = 0u;  // running max of |y| as magnitude bits
   const uint8_t* gl = reinterpret_cast<const uint8_t*>(prm);
