@@ -66,8 +66,8 @@ MI355X_HBM_GBS = 8000.0           # HBM3E (published)
 MEASURED_TRAFFIC = {
     # FP8 GEMM: mean over the layer's 12 GEMM launches (microbench layer --kind fp8)
     "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                 "sha256": "32667088d056ddee50fbc524686cdb61223e000f9ecf6d746900a3a20a6e9774",
-                 "bytes_per_launch": 1704659062},
+                 "sha256": "e468f437d7cc8ebe13a26fd9af8f275f6022eb47a404359142cf139ae07e54eb",
+                 "bytes_per_launch": 1621920753},
     # delayed-scaling quantizers of one layer in autocast mode (24 casts and cast-transposes),
     # summed over the layer's launches (bench.py --modes fp8_delayed_autocast under --pmc)
     "quant_delayed_layer": {"source": "fp8_precision_transformer_amd/csrc/quant.hip",
@@ -75,12 +75,12 @@ MEASURED_TRAFFIC = {
                             "bytes_per_launch": 7453825274},
     # MXFP8 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mxp)
     "gemm_mxfp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "32667088d056ddee50fbc524686cdb61223e000f9ecf6d746900a3a20a6e9774",
-                   "bytes_per_launch": 1757392320},
+                   "sha256": "e468f437d7cc8ebe13a26fd9af8f275f6022eb47a404359142cf139ae07e54eb",
+                   "bytes_per_launch": 1678071885},
     # MXFP4 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mx4p)
     "gemm_mxfp4": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "32667088d056ddee50fbc524686cdb61223e000f9ecf6d746900a3a20a6e9774",
-                   "bytes_per_launch": 919346764},
+                   "sha256": "e468f437d7cc8ebe13a26fd9af8f275f6022eb47a404359142cf139ae07e54eb",
+                   "bytes_per_launch": 913881316},
 }
 
 

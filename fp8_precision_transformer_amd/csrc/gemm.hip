@@ -1446,67 +1446,72 @@ __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) bias4[q] = n0 + wn + q * 32 + lr < p.N ? __uint_as_float(raw[q]) : 0.0f;
   }
+  // the bias add is decided once per launch, not per element
+  auto epilogue = [&](auto HB) {
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const float bias_v[2] = {bias4[2 * hf], bias4[2 * hf + 1]};
+    for (int hf = 0; hf < 2; ++hf) {
+      const float bias_v[2] = {bias4[2 * hf], bias4[2 * hf + 1]};
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
+      for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const int i = pass * 2 + ii;
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = pass * 2 + ii;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+          for (int j = 0; j < 2; ++j) {
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            float val = acc[i][2 * hf + j][v];
-            if constexpr (!MX) val = __fmul_rn(__fmul_rn(val, sa), sb);
-            if (p.bias != nullptr) val = __fadd_rn(val, bias_v[j]);
-            const int r = ii * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
-            ep[r * (kEpPitch / 4) + j * 32 + lr] = val;
-          }
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
-      __builtin_amdgcn_wave_barrier();
-      const int row0 = m0 + wm + pass * 64;
-      const int col0 = n0 + wn + hf * 64;
-      if (p.d_bf16) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int r = t * 8 + (lane >> 3);
-          const int c = (lane & 7) * 8;
-          const float4 lo = *reinterpret_cast<const float4*>(ep + r * (kEpPitch / 4) + c);
-          const float4 hi = *reinterpret_cast<const float4*>(ep + r * (kEpPitch / 4) + c + 4);
-          const int grow = row0 + r, gcol = col0 + c;
-          if (grow < p.M && gcol < p.N) {
-            const v4u o = {bf16x2_rne(lo.x, lo.y), bf16x2_rne(lo.z, lo.w), bf16x2_rne(hi.x, hi.y),
-                           bf16x2_rne(hi.z, hi.w)};
-            __builtin_nontemporal_store(
-                o, reinterpret_cast<v4u*>(static_cast<uint16_t*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol));
-          }
-        }
-      } else {
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int r = t * 4 + (lane >> 4);
-          const int c = (lane & 15) * 4;
-          v4f v4 = *reinterpret_cast<const v4f*>(ep + r * (kEpPitch / 4) + c);
-          const int grow = row0 + r, gcol = col0 + c;
-          if (grow < p.M && gcol < p.N) {
-            v4f* dst = reinterpret_cast<v4f*>(static_cast<float*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol);
-            if (p.accumulate) {
-              const v4f old = __builtin_nontemporal_load(dst);
-#pragma unroll
-              for (int q = 0; q < 4; ++q) v4[q] = __fadd_rn(old[q], v4[q]);
+            for (int v = 0; v < 16; ++v) {
+              float val = acc[i][2 * hf + j][v];
+              if constexpr (!MX) val = __fmul_rn(__fmul_rn(val, sa), sb);
+              if constexpr (decltype(HB)::value != 0) val = __fadd_rn(val, bias_v[j]);
+              const int r = ii * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
+              ep[r * (kEpPitch / 4) + j * 32 + lr] = val;
             }
-            __builtin_nontemporal_store(v4, dst);
           }
         }
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
+        __builtin_amdgcn_wave_barrier();
+        const int row0 = m0 + wm + pass * 64;
+        const int col0 = n0 + wn + hf * 64;
+        if (p.d_bf16) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int r = t * 8 + (lane >> 3);
+            const int c = (lane & 7) * 8;
+            const float4 lo = *reinterpret_cast<const float4*>(ep + r * (kEpPitch / 4) + c);
+            const float4 hi = *reinterpret_cast<const float4*>(ep + r * (kEpPitch / 4) + c + 4);
+            const int grow = row0 + r, gcol = col0 + c;
+            if (grow < p.M && gcol < p.N) {
+              const v4u o = {bf16x2_rne(lo.x, lo.y), bf16x2_rne(lo.z, lo.w), bf16x2_rne(hi.x, hi.y),
+                             bf16x2_rne(hi.z, hi.w)};
+              __builtin_nontemporal_store(
+                  o, reinterpret_cast<v4u*>(static_cast<uint16_t*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol));
+            }
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            const int r = t * 4 + (lane >> 4);
+            const int c = (lane & 15) * 4;
+            v4f v4 = *reinterpret_cast<const v4f*>(ep + r * (kEpPitch / 4) + c);
+            const int grow = row0 + r, gcol = col0 + c;
+            if (grow < p.M && gcol < p.N) {
+              v4f* dst = reinterpret_cast<v4f*>(static_cast<float*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol);
+              if (p.accumulate) {
+                const v4f old = __builtin_nontemporal_load(dst);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v4[q] = __fadd_rn(old[q], v4[q]);
+              }
+              __builtin_nontemporal_store(v4, dst);
+            }
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
+        __builtin_amdgcn_wave_barrier();
       }
-      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
-      __builtin_amdgcn_wave_barrier();
     }
-  }
+  };
+  if (p.bias != nullptr) epilogue(ic<1>{});
+  else epilogue(ic<0>{});
 }
 
 template <int KIND, int AF, int BF, bool PANEL = false, bool FUSED = false>
