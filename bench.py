@@ -100,6 +100,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--breakdown-steps", type=int, default=3,
+                   help="steps of the pass with events around each GEMM and its casts, after the timed steps")
     p.add_argument("--modes", default="all")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-latency", action="store_true", help="skip the small, launch-bound configurations")
@@ -413,26 +415,35 @@ def main():
 
     Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
+    class _NoEv:  # stands in for the per-GEMM events when a layer is timed as a whole
+        def record(self):
+            pass
+
+    NOEV = _NoEv()
+
     step_ctr = [0]
 
     def run_mode(mode, rec):
-        """Enqueue one layer of `mode`; rec collects (key, ev_start, ev_mid, ev_end)."""
+        """Enqueue one layer of `mode`; rec collects (key, ev_start, ev_mid, ev_end) per GEMM,
+        or is None: then no event is recorded inside the layer."""
+        mk = Ev if rec is not None else (lambda: NOEV)
         if mode == "fp8_current_fused":
             for wname, stage in FUSED_ORDER:
                 qf, gf = fused_operands(wname, stage)
-                e0, e1, e2 = Ev(), Ev(), Ev()
+                e0, e1, e2 = mk(), mk(), mk()
                 e0.record()
                 qf()
                 e1.record()
                 gf()
                 e2.record()
                 variants.setdefault(mode, set()).add(B.te_gemm_variant())
-                rec.append((mode, wname, stage, e0, e1, e2))
+                if rec is not None:
+                    rec.append((mode, wname, stage, e0, e1, e2))
             return
         for li, w in enumerate(weights):
             for stage in ("fprop", "dgrad", "wgrad"):
                 out = OUT[w.name][stage]
-                e0, e1, e2 = Ev(), Ev(), Ev()
+                e0, e1, e2 = mk(), mk(), mk()
                 e0.record()
                 if mode == "bf16":
                     e1.record()
@@ -476,15 +487,17 @@ def main():
                     gemm_mx4(ops, out)
                 e2.record()
                 variants.setdefault(mode, set()).add(B.te_gemm_variant())
-                rec.append((mode, w.name, stage, e0, e1, e2))
+                if rec is not None:
+                    rec.append((mode, w.name, stage, e0, e1, e2))
         if mode in DSTATE:
             hist4, s4, si4, hist5, s5, si5 = DSTATE[mode]
-            e0, e2 = Ev(), Ev()
+            e0, e2 = mk(), mk()
             e0.record()
             B.te_scale_update(hist4, s4, si4, E4, B.TE_AMAX_MAX, 0)
             B.te_scale_update(hist5, s5, si5, E5, B.TE_AMAX_MAX, 0)
             e2.record()
-            rec.append((mode, "scale_update", "-", e0, e0, e2))
+            if rec is not None:
+                rec.append((mode, "scale_update", "-", e0, e0, e2))
 
     log("preparing pre-quantized operands")
     prepare_prequant()
@@ -502,23 +515,41 @@ def main():
     torch.cuda.synchronize()
 
     log(f"timing {args.steps} steps")
-    recs = []
+    # Each mode's layer is timed as a whole (one event pair around its casts, GEMMs and
+    # scale updates): an event recorded between two kernels costs several microseconds of
+    # device time, so per-GEMM events inside the timed layers would inflate them.
+    layer_evs = []
     step_ms = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         es, ee = Ev(), Ev()
         es.record()
-        rec = []
+        lay = []
         for mode in modes:
-            run_mode(mode, rec)
+            a, b = Ev(), Ev()
+            a.record()
+            run_mode(mode, None)
+            b.record()
+            lay.append((mode, a, b))
         ee.record()
         step_ctr[0] += 1
-        recs.append(rec)
+        layer_evs.append(lay)
         step_ms.append((es, ee))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log(f"timed region {wall:.2f}s")
+    # the split into quantization and GEMM time, per GEMM: a separate pass after the timed
+    # steps with an event pair around each GEMM's casts and one around the GEMM
+    log(f"breakdown pass, {args.breakdown_steps} steps")
+    recs = []
+    for s in range(args.breakdown_steps):
+        rec = []
+        for mode in modes:
+            run_mode(mode, rec)
+        step_ctr[0] += 1
+        recs.append(rec)
+    torch.cuda.synchronize()
     # every mode's GEMMs must have run on the matrix-core path of its precision
     want = {"bf16": ("gemm4_bf16_",), "mxfp8": ("gemm4_mx_", "gemm1w_mx_"), "mxfp4": ("gemm4_mxfp4_", "gemm1w_mxfp4_"),
             "fp8": ("gemm4_fp8_", "gemm1w_fp8_")}
@@ -531,23 +562,23 @@ def main():
 
     # ---------------- reduce timings ----------------
     per_layer = {m: [] for m in modes}
+    for lay in layer_evs:
+        for mode, a, b in lay:
+            per_layer[mode].append(a.elapsed_time(b))
     quant_ms = {m: [] for m in modes}
     gemm_ms = {m: [] for m in modes}
     per_gemm = {m: {} for m in modes}
     for rec in recs:
-        acc = {m: 0.0 for m in modes}
         accq = {m: 0.0 for m in modes}
         accg = {m: 0.0 for m in modes}
         for mode, wname, stage, e0, e1, e2 in rec:
             tot = e0.elapsed_time(e2)
             g = e1.elapsed_time(e2) if wname != "scale_update" else 0.0
-            acc[mode] += tot
             accg[mode] += g
             accq[mode] += tot - g
             if wname != "scale_update":
                 per_gemm[mode].setdefault(f"{wname}.{stage}", []).append(g)
         for m in modes:
-            per_layer[m].append(acc[m])
             quant_ms[m].append(accq[m])
             gemm_ms[m].append(accg[m])
     med = lambda v: float(np.median(v))  # noqa: E731
@@ -567,19 +598,20 @@ def main():
     headline = "fp8_delayed_autocast" if "fp8_delayed_autocast" in modes else modes[0]
     value = LAYER_FLOPS / (ms_layer[headline] * 1e-3) / 1e12
 
-    # roofline of the dominant kernel: the FP8 GEMM (kernel-only launches of the pre-quantize mode)
+    # roofline of the dominant kernel: the FP8 GEMM. The pre-quantize mode's layer is its 12
+    # GEMM launches back to back, so the layer's event pair over 12 gives the average launch.
     roof = None
     gm = "fp8_current_prequant" if "fp8_current_prequant" in modes else None
     if gm:
         flops = sum(g.flops for g in gemms)
-        t_ms = sum(med(per_gemm[gm][f"{g.weight}.{g.stage}"]) for g in gemms)
+        t_ms = ms_layer[gm]
         achieved = flops / (t_ms * 1e-3) / 1e12 / 1.0
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MI355X_FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MI355X_FP8_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic("gemm_fp8"),
                 "kernel": "k_gemm1w FP8 (256x256 tiles, one wave per SIMD with 128x128 each, 128-byte k stages, "
                           "three stage slots for the operand with more rows); 12 launches per layer, achieved = "
-                          "layer FLOP / summed launch time; traffic = mean HBM bytes per launch",
+                          "layer FLOP / time of the 12 launches back to back; traffic = mean HBM bytes per launch",
                 "avg_launch_ms": round(t_ms / len(gemms), 4),
                 "flop_per_launch": int(flops / len(gemms))}
     # the same for the block-scaled GEMMs: MXFP8 against the FP8 peak, MXFP4 (the FP4
@@ -588,7 +620,7 @@ def main():
         if mode not in modes:
             return None
         flops = sum(g.flops for g in gemms)
-        t_ms = sum(med(per_gemm[mode][f"{g.weight}.{g.stage}"]) for g in gemms)
+        t_ms = ms_layer[mode]  # 12 GEMM launches back to back
         achieved = flops / (t_ms * 1e-3) / 1e12
         return {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": measured_traffic(key), "kernel": kernel,
@@ -609,7 +641,9 @@ def main():
                   "unit": "GB/s", "frac": round(qbytes / (qms * 1e-3) / 1e9 / MI355X_HBM_GBS, 4),
                   "traffic": measured_traffic("quant_delayed_layer"), "traffic_per": "layer",
                   "algorithmic_bytes_per_layer": qbytes,
-                  "kernel": "delayed amax+cast / cast-transpose (24 launches + 2 scale updates per layer)"}
+                  "kernel": "delayed amax+cast / cast-transpose (24 launches + 2 scale updates per layer)",
+                  "time": "breakdown pass: an event pair around each GEMM's two casts (the closing event's "
+                          "own device time included)"}
 
     shared = None
     if "fp8_delayed_shared" in modes:
@@ -694,6 +728,10 @@ def main():
         "modes": result_modes,
         "qkv_asymmetry": asym,
         "per_gemm_ms": per_gemm_out,
+        "timing": {"ms_per_layer": "median over the timed steps of one event pair around each mode's whole layer",
+                   "gemm_ms, quant_ms, per_gemm_ms": f"breakdown pass ({args.breakdown_steps} steps after the timed "
+                                                     "ones): event pairs around each GEMM and around its casts; every "
+                                                     "pair includes its closing event's device time"},
         "roofline": roof,
         "roofline_quant": roof_q,
         "roofline_mxfp8": roof8,
