@@ -66,8 +66,8 @@ MI355X_HBM_GBS = 8000.0           # HBM3E (published)
 MEASURED_TRAFFIC = {
     # FP8 GEMM: mean over the layer's 12 GEMM launches (microbench layer --kind fp8)
     "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                 "sha256": "e468f437d7cc8ebe13a26fd9af8f275f6022eb47a404359142cf139ae07e54eb",
-                 "bytes_per_launch": 1621920753},
+                 "sha256": "5adc5f21c2b14c5eb4c43657433bf236974701189c9c343ae8f6454b33b66271",
+                 "bytes_per_launch": 1529221186},
     # delayed-scaling quantizers of one layer in autocast mode (24 casts and cast-transposes),
     # summed over the layer's launches (bench.py --modes fp8_delayed_autocast under --pmc)
     "quant_delayed_layer": {"source": "fp8_precision_transformer_amd/csrc/quant.hip",
@@ -75,12 +75,12 @@ MEASURED_TRAFFIC = {
                             "bytes_per_launch": 7453825274},
     # MXFP8 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mxp)
     "gemm_mxfp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "e468f437d7cc8ebe13a26fd9af8f275f6022eb47a404359142cf139ae07e54eb",
-                   "bytes_per_launch": 1678071885},
+                   "sha256": "5adc5f21c2b14c5eb4c43657433bf236974701189c9c343ae8f6454b33b66271",
+                   "bytes_per_launch": 1697995895},
     # MXFP4 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mx4p)
     "gemm_mxfp4": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "e468f437d7cc8ebe13a26fd9af8f275f6022eb47a404359142cf139ae07e54eb",
-                   "bytes_per_launch": 913881316},
+                   "sha256": "5adc5f21c2b14c5eb4c43657433bf236974701189c9c343ae8f6454b33b66271",
+                   "bytes_per_launch": 916893021},
 }
 
 
@@ -609,8 +609,9 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MI355X_FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MI355X_FP8_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic("gemm_fp8"),
-                "kernel": "k_gemm1w FP8 (256x256 tiles, one wave per SIMD with 128x128 each, 128-byte k stages, "
-                          "three stage slots for the operand with more rows); 12 launches per layer, achieved = "
+                "kernel": "k_gemm1x FP8 (256x256 tiles, one wave per SIMD with 128x128 each in 16x16x128 MFMAs, "
+                          "128-byte k stages, three stage slots for the operand with more rows); 12 launches per "
+                          "layer, achieved = "
                           "layer FLOP / time of the 12 launches back to back; traffic = mean HBM bytes per launch",
                 "avg_launch_ms": round(t_ms / len(gemms), 4),
                 "flop_per_launch": int(flops / len(gemms))}

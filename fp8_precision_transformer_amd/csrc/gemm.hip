@@ -1514,6 +1514,347 @@ __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
   else epilogue(ic<0>{});
 }
 
+// ============================================================================
+// One wave per SIMD with 16 x 16 x 128 MFMAs (per-tensor FP8, k % 128 == 0).
+// With operands that change from one instruction to the next, as in a GEMM, the
+// 16 x 16 x 128 FP8 instruction sustains about a tenth more FLOP/s than the 32 x 32 x 64
+// one: both run below the published rate at the clocks the device holds under that
+// load, the larger one further below (k_peak_rand in peak.hip: 4290 against 3900
+// TFLOP/s with register operands only).  The outputs are bit-identical to the 32 x 32 x 64
+// kernels': the products of each aligned group of 8 k are summed the same way.
+// A wave's 128 x 128 block is 8 x 8 MFMA tiles of 16 x 16, and one instruction takes a
+// whole 128-byte stage of k, so a stage is 64 MFMAs over 8 + 8 fragments.  The operand
+// with more rows (R) is read whole into registers during the stage before the one that
+// uses it (two register sets); the other (T) is read one 16-row group ahead of the 8
+// MFMAs that use the group.
+// Stage slots: R three -- its slot of stage s is free once stage s has been read into
+// registers, so R loads run two stages ahead; T two -- T's slot of stage s is read all
+// through stage s, so it is refilled in two parts: groups 0-2 of each wave's 128 rows
+// (read before the stage's barrier) with stage s + 2 at that barrier, groups 3-7 (read
+// after it) with stage s + 1 at the next one.  One barrier per stage, after its first
+// two groups of MFMAs: before it every wave has read T's groups 0-2 of stage s, and R
+// and T groups 0-2 of stage s + 1 and T groups 3-7 of stage s have landed; after it
+// the wave reads R of stage s + 1 and the rest of T, and issues the loads of T groups
+// 3-7 of s + 1, T groups 0-2 of s + 2 and R of s + 3, in that order, so that only R's
+// are still in flight at the next barrier.
+// ============================================================================
+template <int AF, int BF, int DEEP>
+__global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
+  constexpr bool RA = DEEP == 1;  // R is A (A has at least as many rows as B)
+  __shared__ __attribute__((aligned(1024))) uint8_t sR0[kPairOp];
+  __shared__ __attribute__((aligned(1024))) uint8_t sR1[kPairOp];
+  __shared__ __attribute__((aligned(1024))) uint8_t sR2[kPairOp];
+  // T slots in two arrays each: the rows of groups 0-2 of both 128-row halves (96 rows)
+  // and of groups 3-7 (160 rows), so that the compiler can tell the loads into one part
+  // from the reads of the other
+  constexpr int kTa = 96 * PK, kTb = 160 * PK;
+  __shared__ __attribute__((aligned(1024))) uint8_t sT0a[kTa];
+  __shared__ __attribute__((aligned(1024))) uint8_t sT1a[kTa];
+  __shared__ __attribute__((aligned(1024))) uint8_t sT0b[kTb];
+  __shared__ __attribute__((aligned(1024))) uint8_t sT1b[kTb];
+  auto slotR = [&](int slot) { return slot == 0 ? sR0 : slot == 1 ? sR1 : sR2; };
+  auto slotTa = [&](int slot) { return slot == 0 ? sT0a : sT1a; };
+  auto slotTb = [&](int slot) { return slot == 0 ? sT0b : sT1b; };
+  const int nb = p.nbm * p.nbn;
+  const int bid = static_cast<int>(blockIdx.x);
+  const int xcd = bid & 7, idx = bid >> 3;
+  const int per = nb >> 3, rem = nb & 7;
+  const int lin = xcd * per + (xcd < rem ? xcd : rem) + idx;
+  const int gspan = kGroupM * p.nbn;
+  const int group = lin / gspan;
+  const int first_m = group * kGroupM;
+  const int gsz = (p.nbm - first_m) < kGroupM ? (p.nbm - first_m) : kGroupM;
+  const int in_g = lin - group * gspan;
+  const int tm = first_m + in_g % gsz;
+  const int tn = in_g / gsz;
+  const int m0 = tm * BM, n0 = tn * BN;
+  // per-tensor scale_inv values, read once at the start (scalar loads; the kernel never
+  // writes them)
+  const float sa = *(const __attribute__((address_space(4))) float*)(reinterpret_cast<uintptr_t>(p.a_scale));
+  const float sb = *(const __attribute__((address_space(4))) float*)(reinterpret_cast<uintptr_t>(p.b_scale));
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int rows_a = (p.M - m0) < BM ? (p.M - m0) : BM;
+  const int rows_b = (p.N - n0) < BN ? (p.N - n0) : BN;
+  const v4i rsA = make_rsrc(p.a + static_cast<int64_t>(m0) * p.KB, static_cast<uint32_t>(rows_a) * p.KB);
+  const v4i rsB = make_rsrc(p.b + static_cast<int64_t>(n0) * p.KB, static_cast<uint32_t>(rows_b) * p.KB);
+  const v4i rsR = RA ? rsA : rsB;
+  const v4i rsT = RA ? rsB : rsA;
+  const int S = (p.KB + PK - 1) / PK;
+  // global->LDS: one instruction moves 8 rows (1 KB) from row rb; lane l lands at row
+  // rb + (l >> 3), physical chunk l & 7, and fetches the logical chunk stored there
+  const int c0 = (lane & 7) ^ (lane >> 3);
+  auto voff_of = [&](int gb, int lb) {  // global row base, LDS row base (multiples of 8)
+    return static_cast<uint32_t>(gb + (lane >> 3)) * static_cast<uint32_t>(p.KB) +
+           static_cast<uint32_t>((c0 ^ ((lb >> 3) & 3)) << 4);
+  };
+  // R: wave w moves rows [64 w, 64 w + 64).  T: the 8-row units of groups 0-2 of both
+  // 128-row halves (part 1: 12 units, 3 per wave; LDS rows 48 h + 16 g + ...) and of
+  // groups 3-7 (part 2: 20 units, 5 per wave; LDS rows 80 h + 16 (g - 3) + ...); the
+  // global row of an LDS row is 128 h + 16 g + ...
+  uint32_t voR[8], voT1[3], voT2[5];
+  int rbT1[3], rbT2[5];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) voR[t] = voff_of(wave * 64 + t * 8, wave * 64 + t * 8);
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    const int q = wave * 3 + t, h = q / 6, r = q % 6;
+    rbT1[t] = 48 * h + 16 * (r >> 1) + 8 * (r & 1);
+    voT1[t] = voff_of(128 * h + 16 * (r >> 1) + 8 * (r & 1), rbT1[t]);
+  }
+#pragma unroll
+  for (int t = 0; t < 5; ++t) {
+    const int q = wave * 5 + t, h = q / 10, r = q % 10;
+    rbT2[t] = 80 * h + 16 * (r >> 1) + 8 * (r & 1);
+    voT2[t] = voff_of(128 * h + 16 * (3 + (r >> 1)) + 8 * (r & 1), rbT2[t]);
+  }
+  auto ld = [&](const v4i& rs, uint8_t* slot, int rb, uint32_t vo, int st) {
+    // past the last stage: an offset beyond the buffer's range, so the load fetches
+    // nothing (it writes zeros into a slot that is never read again)
+    const uint32_t kb = __builtin_amdgcn_readfirstlane(st < S ? static_cast<uint32_t>(st) * PK : 0x40000000u);
+    raw_buffer_load_lds(rs, (__attribute__((address_space(3))) uint32_t*)(slot + rb * PK), 16,
+                        static_cast<int>(vo + kb), 0, 0, 0);
+  };
+  // load k (0 .. 15) of the set issued after stage s's barrier: T part 2 of stage s + 1,
+  // T part 1 of stage s + 2, R of stage s + 3
+  auto load_k = [&](int k, int ts, int rs, int s) {
+    if (k < 5) ld(rsT, slotTb(ts ^ 1), rbT2[k], voT2[k], s + 1);
+    else if (k < 8) ld(rsT, slotTa(ts), rbT1[k - 5], voT1[k - 5], s + 2);
+    else ld(rsR, slotR(rs), wave * 64 + (k - 8) * 8, voR[k - 8], s + 3);
+  };
+  // fragments: lane l reads row 16 g + (l & 15) of the wave's 128, logical chunks l >> 4
+  // (low 16 bytes) and 4 + (l >> 4) (high); the offsets of even and odd groups differ in
+  // the chunk swizzle only, the group adds 16 g rows
+  // (T: group g < 3 is LDS row 48 h + 16 g + (l & 15) of part 1, group g >= 3 row
+  // 80 h + 16 (g - 3) + (l & 15) of part 2, h the wave's half of T's rows)
+  const int th = (RA ? wn : wm) >> 7;
+  int oR[2][2], oTa[2][2], oTb[2][2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int swR = (l16 & 7) ^ ((2 * par + (l16 >> 3)) & 3);
+      oR[par][hh] = ((RA ? wm : wn) + l16) * PK + (((4 * hh + lq) ^ swR) << 4);
+      const int swA = (l16 & 7) ^ ((6 * th + 2 * par + (l16 >> 3)) & 3);
+      oTa[par][hh] = (48 * th + l16) * PK + (((4 * hh + lq) ^ swA) << 4);
+      const int swB = (l16 & 7) ^ ((10 * th + 2 * par + (l16 >> 3)) & 3);
+      oTb[par][hh] = (80 * th + l16) * PK + (((4 * hh + lq) ^ swB) << 4);
+    }
+  auto rd = [&](const uint8_t* slot, const int (&o)[2][2], int g) {
+    const v4u lo = *reinterpret_cast<const v4u*>(slot + o[g & 1][0] + g * 16 * PK);
+    const v4u hi = *reinterpret_cast<const v4u*>(slot + o[g & 1][1] + g * 16 * PK);
+    return __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // T group g of T slot ts
+  auto rdT = [&](int ts, int g) { return g < 3 ? rd(slotTa(ts), oTa, g) : rd(slotTb(ts), oTb, g - 3); };
+  v4f acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  v8i Rf[2][8], Tf[2];
+
+  // prologue: T of stage 0 (both parts), R of stage 0, T part 1 of stage 1, R of stages
+  // 1 and 2; then stage 0's R and first T group into registers
+#pragma unroll
+  for (int t = 0; t < 3; ++t) ld(rsT, sT0a, rbT1[t], voT1[t], 0);
+#pragma unroll
+  for (int t = 0; t < 5; ++t) ld(rsT, sT0b, rbT2[t], voT2[t], 0);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) ld(rsR, sR0, wave * 64 + t * 8, voR[t], 0);
+#pragma unroll
+  for (int t = 0; t < 3; ++t) ld(rsT, sT1a, rbT1[t], voT1[t], 1);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) ld(rsR, sR1, wave * 64 + t * 8, voR[t], 1);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) ld(rsR, sR2, wave * 64 + t * 8, voR[t], 2);
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(3 + 8 + 8));  // stage 0 landed
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int g = 0; g < 8; ++g) Rf[0][g] = rd(sR0, oR, g);
+  Tf[0] = rdT(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // one group of 8 MFMAs (T group t against R's 8), each followed by its share of the
+  // fragment reads and global->LDS loads; the order is pinned (scheduling barriers).  The
+  // MFMAs are written as instructions with the accumulator bound to AGPRs: through the
+  // builtin, the register allocator spread the 64 four-register accumulators over both
+  // register files and moved them back and forth (hundreds of spills and copies per
+  // stage).  The compiler still counts the LDS waits for the operands it reads.
+  auto mfma16 = [&](v4f& c, const v8i& a, const v8i& b) {
+    if constexpr (AF == 0 && BF == 0)
+      asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    else if constexpr (AF == 1 && BF == 0)
+      asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 cbsz:1" : "+a"(c) : "v"(a), "v"(b));
+    else if constexpr (AF == 0 && BF == 1)
+      asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 blgp:1" : "+a"(c) : "v"(a), "v"(b));
+    else
+      asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 cbsz:1 blgp:1" : "+a"(c) : "v"(a), "v"(b));
+  };
+  auto group8 = [&](auto U, auto TT, int s) {
+    constexpr int u = decltype(U)::value, t = decltype(TT)::value;
+    constexpr int pr = u & 1;                     // R register set of stage s
+    constexpr int ts = u & 1;                     // T slot of stage s
+    constexpr int rs = u % 3, rs1 = (u + 1) % 3;  // R slots of stages s, s + 1
+    constexpr int k0 = t < 2 ? 0 : t < 6 ? 3 * (t - 2) : 12 + 2 * (t - 6);
+    constexpr int nld = t < 2 ? 0 : t < 6 ? 3 : 2;
+    auto mf = [&](int r) {
+      if constexpr (RA) mfma16(acc[r][t], Rf[pr][r], Tf[t & 1]);
+      else mfma16(acc[t][r], Tf[t & 1], Rf[pr][r]);
+    };
+    // MFMA 0, the next T fragment; MFMAs 1-4 with R of stage s + 1 (groups 2-5); the
+    // loads after MFMAs 1 .. nld
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      mf(r);
+      if (r == 0) {
+        if constexpr (t < 7) Tf[(t + 1) & 1] = rdT(ts, t + 1);
+        else Tf[0] = rdT(ts ^ 1, 0);
+      }
+      if constexpr (t >= 2 && t <= 5) {
+        if (r == 1 || r == 2) Rf[pr ^ 1][2 * (t - 2) + r - 1] = rd(slotR(rs1), oR, 2 * (t - 2) + r - 1);
+      }
+      if (r >= 3 && r - 3 < nld) load_k(k0 + r - 3, ts, rs, s);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (t == 1) {
+      // T groups 0-2 of stage s read by this wave; stage s + 1's R and T groups 0-2 and
+      // stage s's T groups 3-7 landed (only the R loads of the last barrier in flight)
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(8));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto iter = [&](auto U, int s) {
+    group8(U, ic<0>{}, s);
+    group8(U, ic<1>{}, s);
+    group8(U, ic<2>{}, s);
+    group8(U, ic<3>{}, s);
+    group8(U, ic<4>{}, s);
+    group8(U, ic<5>{}, s);
+    group8(U, ic<6>{}, s);
+    group8(U, ic<7>{}, s);
+  };
+  int s = 0;
+  for (; s + 6 <= S; s += 6) {
+    iter(ic<0>{}, s);
+    iter(ic<1>{}, s + 1);
+    iter(ic<2>{}, s + 2);
+    iter(ic<3>{}, s + 3);
+    iter(ic<4>{}, s + 4);
+    iter(ic<5>{}, s + 5);
+  }
+  if (s < S) iter(ic<0>{}, s);
+  if (s + 1 < S) iter(ic<1>{}, s + 1);
+  if (s + 2 < S) iter(ic<2>{}, s + 2);
+  if (s + 3 < S) iter(ic<3>{}, s + 3);
+  if (s + 4 < S) iter(ic<4>{}, s + 4);
+  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));  // loads past the last stage still write LDS
+  __builtin_amdgcn_s_barrier();
+  // the MFMAs are written as instructions, so the compiler does not count the wait states
+  // between the last one and the first read of its accumulators: 32 here, more than the
+  // instruction needs
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7");
+  asm volatile("s_nop 7");
+  asm volatile("s_nop 7");
+  asm volatile("s_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- epilogue: scale, bias, round; staged through LDS, 64 x 64 floats per pass ----
+  // a 16 x 16 tile's lane holds column l & 15 and rows 4 (l >> 4) .. + 3; staged rows
+  // are 68 floats apart, so the four lane groups' rows land on different banks
+  constexpr int kEp = 68;
+  float* ep = reinterpret_cast<float*>(wave == 0 ? sR0 : wave == 1 ? sR1 : wave == 2 ? sR2 : sT0b);
+  // the bias of this lane's eight columns, fetched together (one memory latency)
+  float bias8[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  if (p.bias != nullptr) {
+    // columns past n read column n - 1 (every load issued unconditionally) and take 0
+    uint32_t raw[8];
+    if (p.bias_bf16) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int col = min(n0 + wn + q * 16 + l16, p.N - 1);
+        raw[q] = static_cast<uint32_t>(static_cast<const uint16_t*>(p.bias)[col]) << 16;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int col = min(n0 + wn + q * 16 + l16, p.N - 1);
+        raw[q] = static_cast<const uint32_t*>(p.bias)[col];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) bias8[q] = n0 + wn + q * 16 + l16 < p.N ? __uint_as_float(raw[q]) : 0.0f;
+  }
+  // the bias add is decided once per launch, not per element
+  auto epilogue = [&](auto HB) {
+#pragma unroll
+    for (int pc = 0; pc < 2; ++pc) {
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              float val = __fmul_rn(__fmul_rn(acc[4 * pr + ii][4 * pc + jj][v], sa), sb);
+              if constexpr (decltype(HB)::value != 0) val = __fadd_rn(val, bias8[4 * pc + jj]);
+              ep[(16 * ii + 4 * lq + v) * kEp + 16 * jj + l16] = val;
+            }
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
+        __builtin_amdgcn_wave_barrier();
+        const int row0 = m0 + wm + pr * 64;
+        const int col0 = n0 + wn + pc * 64;
+        if (p.d_bf16) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int r = t * 8 + (lane >> 3);
+            const int c = (lane & 7) * 8;
+            const float4 lo = *reinterpret_cast<const float4*>(ep + r * kEp + c);
+            const float4 hi = *reinterpret_cast<const float4*>(ep + r * kEp + c + 4);
+            const int grow = row0 + r, gcol = col0 + c;
+            if (grow < p.M && gcol < p.N) {
+              const v4u o = {bf16x2_rne(lo.x, lo.y), bf16x2_rne(lo.z, lo.w), bf16x2_rne(hi.x, hi.y),
+                             bf16x2_rne(hi.z, hi.w)};
+              __builtin_nontemporal_store(
+                  o, reinterpret_cast<v4u*>(static_cast<uint16_t*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol));
+            }
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            const int r = t * 4 + (lane >> 4);
+            const int c = (lane & 15) * 4;
+            v4f v4 = *reinterpret_cast<const v4f*>(ep + r * kEp + c);
+            const int grow = row0 + r, gcol = col0 + c;
+            if (grow < p.M && gcol < p.N) {
+              v4f* dst = reinterpret_cast<v4f*>(static_cast<float*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol);
+              if (p.accumulate) {
+                const v4f old = __builtin_nontemporal_load(dst);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v4[q] = __fadd_rn(old[q], v4[q]);
+              }
+              __builtin_nontemporal_store(v4, dst);
+            }
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+  };
+  if (p.bias != nullptr) epilogue(ic<1>{});
+  else epilogue(ic<0>{});
+}
+
 template <int KIND, int AF, int BF, bool PANEL = false, bool FUSED = false>
 hipError_t run(Params p, hipStream_t s, const char* name) {
   g_last_variant = name;
@@ -1553,6 +1894,16 @@ hipError_t run(Params p, hipStream_t s, const char* name) {
 template <int KIND, int AF, int BF>
 hipError_t run_1w(Params p, hipStream_t s, const char* name_a, const char* name_b) {
   const int nb = p.nbm * p.nbn;
+  if constexpr (KIND == KIND_FP8) {  // per-tensor FP8: the 16 x 16 x 128 kernel
+    if (p.M >= p.N) {
+      g_last_variant = name_a;
+      hipLaunchKernelGGL((k_gemm1x<AF, BF, 1>), dim3(nb), dim3(256), 0, s, p);
+    } else {
+      g_last_variant = name_b;
+      hipLaunchKernelGGL((k_gemm1x<AF, BF, 2>), dim3(nb), dim3(256), 0, s, p);
+    }
+    return hipGetLastError();
+  }
   if (p.M >= p.N) {
     g_last_variant = name_a;
     hipLaunchKernelGGL((k_gemm1w<KIND, AF, BF, 1>), dim3(nb), dim3(256), 0, s, p);
@@ -1629,12 +1980,16 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
       return run_1w<KIND_MX, 1, 1>(p, s, "gemm1w_mx_e5m2_e5m2_256x256_panel_deepA", "gemm1w_mx_e5m2_e5m2_256x256_panel_deepB");
     }
     if (af == 0 && bf == 0)
-      return run_1w<KIND_FP8, 0, 0>(p, s, "gemm1w_fp8_e4m3_e4m3_256x256_deepA", "gemm1w_fp8_e4m3_e4m3_256x256_deepB");
+      return run_1w<KIND_FP8, 0, 0>(p, s, "gemm1w_fp8_e4m3_e4m3_256x256_mfma16_deepA",
+                                       "gemm1w_fp8_e4m3_e4m3_256x256_mfma16_deepB");
     if (af == 1 && bf == 0)
-      return run_1w<KIND_FP8, 1, 0>(p, s, "gemm1w_fp8_e5m2_e4m3_256x256_deepA", "gemm1w_fp8_e5m2_e4m3_256x256_deepB");
+      return run_1w<KIND_FP8, 1, 0>(p, s, "gemm1w_fp8_e5m2_e4m3_256x256_mfma16_deepA",
+                                       "gemm1w_fp8_e5m2_e4m3_256x256_mfma16_deepB");
     if (af == 0 && bf == 1)
-      return run_1w<KIND_FP8, 0, 1>(p, s, "gemm1w_fp8_e4m3_e5m2_256x256_deepA", "gemm1w_fp8_e4m3_e5m2_256x256_deepB");
-    return run_1w<KIND_FP8, 1, 1>(p, s, "gemm1w_fp8_e5m2_e5m2_256x256_deepA", "gemm1w_fp8_e5m2_e5m2_256x256_deepB");
+      return run_1w<KIND_FP8, 0, 1>(p, s, "gemm1w_fp8_e4m3_e5m2_256x256_mfma16_deepA",
+                                       "gemm1w_fp8_e4m3_e5m2_256x256_mfma16_deepB");
+    return run_1w<KIND_FP8, 1, 1>(p, s, "gemm1w_fp8_e5m2_e5m2_256x256_mfma16_deepA",
+                                       "gemm1w_fp8_e5m2_e5m2_256x256_mfma16_deepB");
   }
   if (g.a_fmt == E2M1) {
     if (g.mx_panel)

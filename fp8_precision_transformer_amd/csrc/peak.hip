@@ -3,6 +3,10 @@
 //    loop: the sustained FP8 (32x32x64 f8f6f4), BF16 (32x32x16), MXFP8 and MXFP4
 //    (block-scaled 32x32x64 with the scales in registers) matrix-core rates under the
 //    clocks the device actually runs, as a ceiling beside the published peak;
+//  - k_peak_rand: the FP8 rate when the operands change from one instruction to the
+//    next, as in a GEMM (eight register sets of random E4M3 codes), for the 32x32x64 and
+//    the 16x16x128 instruction: the chip holds lower clocks under that load, and the two
+//    shapes do not slow down alike;
 //  - k_copy: a plain 16-byte-per-lane device copy of known size, the reference that
 //    HBM byte counters (FETCH_SIZE, WRITE_SIZE) are calibrated against, and the
 //    practical streaming rate (read + write) a memory-bound kernel can reach;
@@ -56,7 +60,70 @@ __global__ __launch_bounds__(256, 1) void k_peak(const int* seed, float* out, in
   out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
-// kind: 0 FP8, 1 BF16, 2 MXFP8, 3 MXFP4 (see k_peak)
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ inline uint32_t mix32(uint32_t x) {  // an integer hash, for operand codes only
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+// SHAPE 0: 32x32x64 (16 accumulators of 16), 1: 16x16x128 (64 accumulators of 4); one
+// wave per SIMD, 256 accumulator registers either way; every instruction takes one of 8
+// random A sets against a B set that rotates with it; codes without NaN (bit 3 clear)
+template <int SHAPE>
+__global__ __launch_bounds__(256, 1) void k_peak_rand(const int* seed, float* out, int iters) {
+  const uint32_t t = threadIdx.x + 256u * blockIdx.x + static_cast<uint32_t>(seed[0]);
+  v8i A[8], B[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      A[s][j] = static_cast<int>(mix32(t * 64u + s * 8u + j + 1u) & 0xF7F7F7F7u);
+      B[s][j] = static_cast<int>(mix32(t * 64u + s * 8u + j + 0x9e3779b9u) & 0xF7F7F7F7u);
+    }
+  float r = 0.0f;
+  if constexpr (SHAPE == 0) {
+    v16f acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = v16f{0};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A[s], B[(s + i) & 7], acc[i], 0, 0, 0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) r += acc[i][j];
+  } else {
+    v4f acc[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+          acc[(s & 1) * 32 + i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              A[s], B[(s + i) & 7], acc[(s & 1) * 32 + i], 0, 0, 0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 64; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r += acc[i][j];
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = r;
+}
+
+// kind: 0 FP8, 1 BF16, 2 MXFP8, 3 MXFP4 (see k_peak); 4 FP8 32x32x64 and 5 FP8 16x16x128
+// with changing random operands (k_peak_rand; 8 x 16 and 8 x 32 instructions per
+// iteration, the same FLOP)
 extern "C" int te_peak_launch(int kind, int blocks, int iters, const int* seed, float* out, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (kind) {
@@ -64,6 +131,8 @@ extern "C" int te_peak_launch(int kind, int blocks, int iters, const int* seed, 
     case 1: hipLaunchKernelGGL((k_peak<1>), dim3(blocks), dim3(256), 0, st, seed, out, iters); break;
     case 2: hipLaunchKernelGGL((k_peak<2>), dim3(blocks), dim3(256), 0, st, seed, out, iters); break;
     case 3: hipLaunchKernelGGL((k_peak<3>), dim3(blocks), dim3(256), 0, st, seed, out, iters); break;
+    case 4: hipLaunchKernelGGL((k_peak_rand<0>), dim3(blocks), dim3(256), 0, st, seed, out, iters); break;
+    case 5: hipLaunchKernelGGL((k_peak_rand<1>), dim3(blocks), dim3(256), 0, st, seed, out, iters); break;
     default: return 1;
   }
   return hipGetLastError() == hipSuccess ? 0 : 1;

@@ -314,14 +314,17 @@ def peak(args):
     blocks = 256 * args.waves_per_cu  # one 4-wave block per CU per wave slot
     out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    kinds = ((0, "fp8"), (1, "bf16"), (2, "mxfp8"), (3, "mxfp4"))
+    kinds = ((0, "fp8"), (1, "bf16"), (2, "mxfp8"), (3, "mxfp4"), (4, "fp8_32x32x64_changing_operands"),
+             (5, "fp8_16x16x128_changing_operands"))
     for code, kind in kinds * args.repeat:  # later passes run at the clocks the first settled
         bf = code == 1
         fn = lambda: L.te_peak_launch(code, blocks, args.iters, ctypes.c_void_p(seed.data_ptr()),  # noqa: E731
                                       ctypes.c_void_p(out.data_ptr()), st)
         ms = _time(fn, 5, 2)
         flop_per_mfma = 2 * 32 * 32 * (16 if bf else 64)
-        fl = float(blocks) * 4 * args.iters * 16 * flop_per_mfma
+        # k_peak: 16 instructions per iteration; k_peak_rand: 8 x 16 of 32x32x64 or the same
+        # FLOP in 8 x 32 of 16x16x128
+        fl = float(blocks) * 4 * args.iters * (128 if code >= 4 else 16) * flop_per_mfma
         print(json.dumps({"kernel": f"mfma_peak_{kind}", "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1)}),
               flush=True)
 

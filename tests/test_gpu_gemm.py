@@ -257,7 +257,7 @@ def test_dispatched_variant_is_the_requested_matrix_core_path():
         d = _out(m, n, "f32")
         for fa, fb in (("E4M3", "E4M3"), ("E5M2", "E4M3")):
             B.te_fp8_gemm(a, fa, scalar(1.0), b, fb, scalar(1.0), d)
-            want = (f"gemm1w_fp8_{fa.lower()}_{fb.lower()}_256x256_deepA" if k % 128 == 0
+            want = (f"gemm1w_fp8_{fa.lower()}_{fb.lower()}_256x256_mfma16_deepA" if k % 128 == 0
                     else f"gemm4_fp8_{fa.lower()}_{fb.lower()}_256x256_pingpong")
             assert B.te_gemm_variant() == want
             B.te_fp8_gemm(a, fa, ea, b, fb, eb, d, gran=B.TE_GRAN_MX_BLOCK32)
