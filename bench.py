@@ -67,20 +67,20 @@ MEASURED_TRAFFIC = {
     # FP8 GEMM: mean over the layer's 12 GEMM launches (microbench layer --kind fp8)
     "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
                  "sha256": "5adc5f21c2b14c5eb4c43657433bf236974701189c9c343ae8f6454b33b66271",
-                 "bytes_per_launch": 1529221186},
+                 "bytes_per_launch": 1571042182},
     # delayed-scaling quantizers of one layer in autocast mode (24 casts and cast-transposes),
     # summed over the layer's launches (bench.py --modes fp8_delayed_autocast under --pmc)
     "quant_delayed_layer": {"source": "fp8_precision_transformer_amd/csrc/quant.hip",
                             "sha256": "69668d0fb473dfbdbd4c2f5a64a809fdc5b2c87029c59cf24abc5d7252cb3e29",
-                            "bytes_per_launch": 7453825274},
+                            "bytes_per_launch": 7453824386},
     # MXFP8 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mxp)
     "gemm_mxfp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
                    "sha256": "5adc5f21c2b14c5eb4c43657433bf236974701189c9c343ae8f6454b33b66271",
-                   "bytes_per_launch": 1697995895},
+                   "bytes_per_launch": 1776470979},
     # MXFP4 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mx4p)
     "gemm_mxfp4": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
                    "sha256": "5adc5f21c2b14c5eb4c43657433bf236974701189c9c343ae8f6454b33b66271",
-                   "bytes_per_launch": 916893021},
+                   "bytes_per_launch": 921644787},
 }
 
 
