@@ -66,21 +66,21 @@ MI355X_HBM_GBS = 8000.0           # HBM3E (published)
 MEASURED_TRAFFIC = {
     # FP8 GEMM: mean over the layer's 12 GEMM launches (microbench layer --kind fp8)
     "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                 "sha256": "5adc5f21c2b14c5eb4c43657433bf236974701189c9c343ae8f6454b33b66271",
-                 "bytes_per_launch": 1571042182},
+                 "sha256": "85698f8aec34db7bfcdb179279931a2238e944be4cb9c06395203997bef8cd79",
+                 "bytes_per_launch": 1527166465},
     # delayed-scaling quantizers of one layer in autocast mode (24 casts and cast-transposes),
     # summed over the layer's launches (bench.py --modes fp8_delayed_autocast under --pmc)
     "quant_delayed_layer": {"source": "fp8_precision_transformer_amd/csrc/quant.hip",
                             "sha256": "69668d0fb473dfbdbd4c2f5a64a809fdc5b2c87029c59cf24abc5d7252cb3e29",
-                            "bytes_per_launch": 7453824386},
+                            "bytes_per_launch": 7453822016},
     # MXFP8 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mxp)
     "gemm_mxfp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "5adc5f21c2b14c5eb4c43657433bf236974701189c9c343ae8f6454b33b66271",
-                   "bytes_per_launch": 1776470979},
+                   "sha256": "85698f8aec34db7bfcdb179279931a2238e944be4cb9c06395203997bef8cd79",
+                   "bytes_per_launch": 1651419070},
     # MXFP4 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mx4p)
     "gemm_mxfp4": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "5adc5f21c2b14c5eb4c43657433bf236974701189c9c343ae8f6454b33b66271",
-                   "bytes_per_launch": 921644787},
+                   "sha256": "85698f8aec34db7bfcdb179279931a2238e944be4cb9c06395203997bef8cd79",
+                   "bytes_per_launch": 908555377},
 }
 
 

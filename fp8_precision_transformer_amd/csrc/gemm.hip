@@ -1520,8 +1520,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
 // 16 x 16 x 128 FP8 instruction sustains about a tenth more FLOP/s than the 32 x 32 x 64
 // one: both run below the published rate at the clocks the device holds under that
 // load, the larger one further below (k_peak_rand in peak.hip: 4290 against 3900
-// TFLOP/s with register operands only).  The outputs are bit-identical to the 32 x 32 x 64
-// kernels': the products of each aligned group of 8 k are summed the same way.
+// TFLOP/s with register operands only).  The matrix core sums aligned groups of 8 k as
+// the 32 x 32 x 64 instruction does; the group sums are added in another order, so the
+// outputs round differently from the other FP8 kernels' (split-K, fused amax, ragged k),
+// within the same bound.
 // A wave's 128 x 128 block is 8 x 8 MFMA tiles of 16 x 16, and one instruction takes a
 // whole 128-byte stage of k, so a stage is 64 MFMAs over 8 + 8 fragments.  The operand
 // with more rows (R) is read whole into registers during the stage before the one that
@@ -1626,8 +1628,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
     else if (k < 8) ld(rsT, slotTa(ts), rbT1[k - 5], voT1[k - 5], s + 2);
     else ld(rsR, slotR(rs), wave * 64 + (k - 8) * 8, voR[k - 8], s + 3);
   };
-  // fragments: lane l reads row 16 g + (l & 15) of the wave's 128, logical chunks l >> 4
-  // (low 16 bytes) and 4 + (l >> 4) (high); the offsets of even and odd groups differ in
+  // fragments: lane l reads row 16 g + (l & 15) of the wave's 128, logical chunks 2 (l >> 4)
+  // (low 16 bytes) and 2 (l >> 4) + 1 (high): each lane group holds 32 consecutive bytes of
+  // k.  The instruction needs A and B in the same k order only; with chunks l >> 4 and
+  // 4 + (l >> 4) instead, 16 rows x 4 chunks per read, the reads took 1.7x as long (LDS
+  // bank conflicts on half the LDS cycles).  The offsets of even and odd groups differ in
   // the chunk swizzle only, the group adds 16 g rows
   // (T: group g < 3 is LDS row 48 h + 16 g + (l & 15) of part 1, group g >= 3 row
   // 80 h + 16 (g - 3) + (l & 15) of part 2, h the wave's half of T's rows)
@@ -1638,11 +1643,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int swR = (l16 & 7) ^ ((2 * par + (l16 >> 3)) & 3);
-      oR[par][hh] = ((RA ? wm : wn) + l16) * PK + (((4 * hh + lq) ^ swR) << 4);
+      oR[par][hh] = ((RA ? wm : wn) + l16) * PK + (((2 * lq + hh) ^ swR) << 4);
       const int swA = (l16 & 7) ^ ((6 * th + 2 * par + (l16 >> 3)) & 3);
-      oTa[par][hh] = (48 * th + l16) * PK + (((4 * hh + lq) ^ swA) << 4);
+      oTa[par][hh] = (48 * th + l16) * PK + (((2 * lq + hh) ^ swA) << 4);
       const int swB = (l16 & 7) ^ ((10 * th + 2 * par + (l16 >> 3)) & 3);
-      oTb[par][hh] = (80 * th + l16) * PK + (((4 * hh + lq) ^ swB) << 4);
+      oTb[par][hh] = (80 * th + l16) * PK + (((2 * lq + hh) ^ swB) << 4);
     }
   auto rd = [&](const uint8_t* slot, const int (&o)[2][2], int g) {
     const v4u lo = *reinterpret_cast<const v4u*>(slot + o[g & 1][0] + g * 16 * PK);
