@@ -66,8 +66,8 @@ MI355X_HBM_GBS = 8000.0           # HBM3E (published)
 MEASURED_TRAFFIC = {
     # FP8 GEMM: mean over the layer's 12 GEMM launches (microbench layer --kind fp8)
     "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                 "sha256": "85698f8aec34db7bfcdb179279931a2238e944be4cb9c06395203997bef8cd79",
-                 "bytes_per_launch": 1527166465},
+                 "sha256": "202ab60058f87a7e83c7dcf462f1c5f6d8ffa19be4567128ea15b2b2e6bddd19",
+                 "bytes_per_launch": 1526788487},
     # delayed-scaling quantizers of one layer in autocast mode (24 casts and cast-transposes),
     # summed over the layer's launches (bench.py --modes fp8_delayed_autocast under --pmc)
     "quant_delayed_layer": {"source": "fp8_precision_transformer_amd/csrc/quant.hip",
@@ -75,12 +75,12 @@ MEASURED_TRAFFIC = {
                             "bytes_per_launch": 7453822016},
     # MXFP8 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mxp)
     "gemm_mxfp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "85698f8aec34db7bfcdb179279931a2238e944be4cb9c06395203997bef8cd79",
-                   "bytes_per_launch": 1651419070},
+                   "sha256": "202ab60058f87a7e83c7dcf462f1c5f6d8ffa19be4567128ea15b2b2e6bddd19",
+                   "bytes_per_launch": 1686121085},
     # MXFP4 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mx4p)
     "gemm_mxfp4": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "85698f8aec34db7bfcdb179279931a2238e944be4cb9c06395203997bef8cd79",
-                   "bytes_per_launch": 908555377},
+                   "sha256": "202ab60058f87a7e83c7dcf462f1c5f6d8ffa19be4567128ea15b2b2e6bddd19",
+                   "bytes_per_launch": 909399072},
 }
 
 

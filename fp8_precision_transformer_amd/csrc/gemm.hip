@@ -1520,10 +1520,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
 // 16 x 16 x 128 FP8 instruction sustains about a tenth more FLOP/s than the 32 x 32 x 64
 // one: both run below the published rate at the clocks the device holds under that
 // load, the larger one further below (k_peak_rand in peak.hip: 4290 against 3900
-// TFLOP/s with register operands only).  The matrix core sums aligned groups of 8 k as
-// the 32 x 32 x 64 instruction does; the group sums are added in another order, so the
-// outputs round differently from the other FP8 kernels' (split-K, fused amax, ragged k),
-// within the same bound.
+// TFLOP/s with register operands only).  The outputs are bit-identical to the 32 x 32 x 64
+// kernels'.
 // A wave's 128 x 128 block is 8 x 8 MFMA tiles of 16 x 16, and one instruction takes a
 // whole 128-byte stage of k, so a stage is 64 MFMAs over 8 + 8 fragments.  The operand
 // with more rows (R) is read whole into registers during the stage before the one that
@@ -1588,11 +1586,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
   const v4i rsT = RA ? rsB : rsA;
   const int S = (p.KB + PK - 1) / PK;
   // global->LDS: one instruction moves 8 rows (1 KB) from row rb; lane l lands at row
-  // rb + (l >> 3), physical chunk l & 7, and fetches the logical chunk stored there
-  const int c0 = (lane & 7) ^ (lane >> 3);
+  // rb + (l >> 3), physical chunk l & 7, and fetches the logical chunk stored there.  In
+  // this kernel's slots logical chunk c of row r sits at c ^ ((r >> 1) & 7): the two rows
+  // of a 256-byte LDS line share the swizzle, which keeps a fragment read (16 rows x 4
+  // chunks) free of bank conflicts; the swizzle of the other kernels (c ^ (r & 7) ^
+  // ((r >> 3) & 3)) spent half of the LDS cycles here in conflicts
   auto voff_of = [&](int gb, int lb) {  // global row base, LDS row base (multiples of 8)
     return static_cast<uint32_t>(gb + (lane >> 3)) * static_cast<uint32_t>(p.KB) +
-           static_cast<uint32_t>((c0 ^ ((lb >> 3) & 3)) << 4);
+           static_cast<uint32_t>(((lane & 7) ^ (((lb + (lane >> 3)) >> 1) & 7)) << 4);
   };
   // R: wave w moves rows [64 w, 64 w + 64).  T: the 8-row units of groups 0-2 of both
   // 128-row halves (part 1: 12 units, 3 per wave; LDS rows 48 h + 16 g + ...) and of
@@ -1628,26 +1629,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
     else if (k < 8) ld(rsT, slotTa(ts), rbT1[k - 5], voT1[k - 5], s + 2);
     else ld(rsR, slotR(rs), wave * 64 + (k - 8) * 8, voR[k - 8], s + 3);
   };
-  // fragments: lane l reads row 16 g + (l & 15) of the wave's 128, logical chunks 2 (l >> 4)
-  // (low 16 bytes) and 2 (l >> 4) + 1 (high): each lane group holds 32 consecutive bytes of
-  // k.  The instruction needs A and B in the same k order only; with chunks l >> 4 and
-  // 4 + (l >> 4) instead, 16 rows x 4 chunks per read, the reads took 1.7x as long (LDS
-  // bank conflicts on half the LDS cycles).  The offsets of even and odd groups differ in
-  // the chunk swizzle only, the group adds 16 g rows
-  // (T: group g < 3 is LDS row 48 h + 16 g + (l & 15) of part 1, group g >= 3 row
-  // 80 h + 16 (g - 3) + (l & 15) of part 2, h the wave's half of T's rows)
+  // fragments: lane l reads row 16 g + (l & 15) of the wave's 128, logical chunks l >> 4
+  // (low 16 bytes) and 4 + (l >> 4) (high): the k order of the matrix instruction, so the
+  // products are grouped and summed exactly as by the 32 x 32 x 64 instruction (outputs
+  // bit-identical to the other FP8 kernels').  The offsets of even and odd groups are
+  // computed alike (16 rows move the swizzle by 8), the group adds 16 g rows.  (T: group
+  // g < 3 is LDS row 48 h + 16 g + (l & 15) of part 1, group g >= 3 row 80 h + 16 (g - 3)
+  // + (l & 15) of part 2, h the wave's half of T's rows)
   const int th = (RA ? wn : wm) >> 7;
   int oR[2][2], oTa[2][2], oTb[2][2];
 #pragma unroll
   for (int par = 0; par < 2; ++par)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const int swR = (l16 & 7) ^ ((2 * par + (l16 >> 3)) & 3);
-      oR[par][hh] = ((RA ? wm : wn) + l16) * PK + (((2 * lq + hh) ^ swR) << 4);
-      const int swA = (l16 & 7) ^ ((6 * th + 2 * par + (l16 >> 3)) & 3);
-      oTa[par][hh] = (48 * th + l16) * PK + (((2 * lq + hh) ^ swA) << 4);
-      const int swB = (l16 & 7) ^ ((10 * th + 2 * par + (l16 >> 3)) & 3);
-      oTb[par][hh] = (80 * th + l16) * PK + (((2 * lq + hh) ^ swB) << 4);
+      const int rR = (RA ? wm : wn) + 16 * par + l16, rA = 48 * th + 16 * par + l16, rB = 80 * th + 16 * par + l16;
+      oR[par][hh] = ((RA ? wm : wn) + l16) * PK + (((4 * hh + lq) ^ ((rR >> 1) & 7)) << 4);
+      oTa[par][hh] = (48 * th + l16) * PK + (((4 * hh + lq) ^ ((rA >> 1) & 7)) << 4);
+      oTb[par][hh] = (80 * th + l16) * PK + (((4 * hh + lq) ^ ((rB >> 1) & 7)) << 4);
     }
   auto rd = [&](const uint8_t* slot, const int (&o)[2][2], int g) {
     const v4u lo = *reinterpret_cast<const v4u*>(slot + o[g & 1][0] + g * 16 * PK);
