@@ -66,8 +66,8 @@ MI355X_HBM_GBS = 8000.0           # HBM3E (published)
 MEASURED_TRAFFIC = {
     # FP8 GEMM: mean over the layer's 12 GEMM launches (microbench layer --kind fp8)
     "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                 "sha256": "202ab60058f87a7e83c7dcf462f1c5f6d8ffa19be4567128ea15b2b2e6bddd19",
-                 "bytes_per_launch": 1526788487},
+                 "sha256": "8d8c4814d98b58a8d122a5585ec817324354ecef6aad3ecd2383b9c2c6282fb9",
+                 "bytes_per_launch": 1537208205},
     # delayed-scaling quantizers of one layer in autocast mode (24 casts and cast-transposes),
     # summed over the layer's launches (bench.py --modes fp8_delayed_autocast under --pmc)
     "quant_delayed_layer": {"source": "fp8_precision_transformer_amd/csrc/quant.hip",
@@ -75,12 +75,12 @@ MEASURED_TRAFFIC = {
                             "bytes_per_launch": 7453822016},
     # MXFP8 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mxp)
     "gemm_mxfp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "202ab60058f87a7e83c7dcf462f1c5f6d8ffa19be4567128ea15b2b2e6bddd19",
-                   "bytes_per_launch": 1686121085},
+                   "sha256": "8d8c4814d98b58a8d122a5585ec817324354ecef6aad3ecd2383b9c2c6282fb9",
+                   "bytes_per_launch": 1554718322},
     # MXFP4 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mx4p)
     "gemm_mxfp4": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "202ab60058f87a7e83c7dcf462f1c5f6d8ffa19be4567128ea15b2b2e6bddd19",
-                   "bytes_per_launch": 909399072},
+                   "sha256": "8d8c4814d98b58a8d122a5585ec817324354ecef6aad3ecd2383b9c2c6282fb9",
+                   "bytes_per_launch": 912476227},
 }
 
 
@@ -628,7 +628,7 @@ def main():
                 "avg_launch_ms": round(t_ms / len(gemms), 4), "flop_per_launch": int(flops / len(gemms))}
 
     roof8 = mx_roofline("mxfp8_prequant", MI355X_FP8_PEAK_TFLOPS, "gemm_mxfp8",
-                        "k_gemm1w MXFP8 (E4M3 x E4M3 scaled MFMA, E8M0 scales in the panel layout, 256x256 tiles, one wave per SIMD); 12 launches per layer")
+                        "k_gemm1x MXFP8 (E4M3 x E4M3 scaled 16x16x128 MFMA, E8M0 scales in the panel layout, 256x256 tiles, one wave per SIMD); 12 launches per layer")
     roof4 = mx_roofline("mxfp4_prequant", MI355X_FP4_PEAK_TFLOPS, "gemm_mxfp4",
                         "k_gemm1w MXFP4 (E2M1 x E2M1 scaled MFMA, E8M0 scales in the panel layout, 256x256 tiles, one wave per SIMD); 12 launches per layer")
     roof16 = mx_roofline("bf16", MI355X_BF16_PEAK_TFLOPS, None,

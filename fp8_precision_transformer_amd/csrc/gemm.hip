@@ -329,6 +329,8 @@ __device__ void raw_buffer_load_lds(v4i rsrc, __attribute__((address_space(3))) 
                                     int size, int voffset, int soffset, int offset,
                                     int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
+__device__ int buffer_load_u32(v4i rsrc, int voffset, int soffset, int aux) __asm("llvm.amdgcn.raw.buffer.load.i32");
+
 __device__ __forceinline__ v4i make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   v4i r;
@@ -1515,7 +1517,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
 }
 
 // ============================================================================
-// One wave per SIMD with 16 x 16 x 128 MFMAs (per-tensor FP8, k % 128 == 0).
+// One wave per SIMD with 16 x 16 x 128 MFMAs (per-tensor FP8, k % 128 == 0; MXFP8 with
+// panel-layout scales).
 // With operands that change from one instruction to the next, as in a GEMM, the
 // 16 x 16 x 128 FP8 instruction sustains about a tenth more FLOP/s than the 32 x 32 x 64
 // one: both run below the published rate at the clocks the device holds under that
@@ -1538,9 +1541,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
 // 3-7 of s + 1, T groups 0-2 of s + 2 and R of s + 3, in that order, so that only R's
 // are still in flight at the next barrier.
 // ============================================================================
-template <int AF, int BF, int DEEP>
+template <int KIND, int AF, int BF, int DEEP>
 __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
-  constexpr bool RA = DEEP == 1;  // R is A (A has at least as many rows as B)
+  constexpr bool MX = KIND == KIND_MX;  // E8M0 block scales, panel layout
+  constexpr bool RA = DEEP == 1;        // R is A (A has at least as many rows as B)
   __shared__ __attribute__((aligned(1024))) uint8_t sR0[kPairOp];
   __shared__ __attribute__((aligned(1024))) uint8_t sR1[kPairOp];
   __shared__ __attribute__((aligned(1024))) uint8_t sR2[kPairOp];
@@ -1570,8 +1574,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
   const int m0 = tm * BM, n0 = tn * BN;
   // per-tensor scale_inv values, read once at the start (scalar loads; the kernel never
   // writes them)
-  const float sa = *(const __attribute__((address_space(4))) float*)(reinterpret_cast<uintptr_t>(p.a_scale));
-  const float sb = *(const __attribute__((address_space(4))) float*)(reinterpret_cast<uintptr_t>(p.b_scale));
+  float sa = 1.0f, sb = 1.0f;
+  if constexpr (!MX) {
+    sa = *(const __attribute__((address_space(4))) float*)(reinterpret_cast<uintptr_t>(p.a_scale));
+    sb = *(const __attribute__((address_space(4))) float*)(reinterpret_cast<uintptr_t>(p.b_scale));
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1654,6 +1661,56 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
   };
   // T group g of T slot ts
   auto rdT = [&](int ts, int g) { return g < 3 ? rd(slotTa(ts), oTa, g) : rd(slotTb(ts), oTb, g - 3); };
+  // MX: a lane's fragment data is 32-element block l >> 4 of its row's stage, so its scale
+  // is byte l >> 4 of the row's dword in the panel layout (dword ((r / 256) G + g) 256 +
+  // r % 256 for row r and 128-element group g; G = k / 128, one group per stage).  Per
+  // operand and stage a lane loads the dwords of rows 16 (2 (l >> 4) + h) + (l & 15),
+  // h = 0, 1, of the wave's 128 (two loads: the wave reads its 128 rows once), two stages
+  // ahead; the bytes reach the lanes that need them through a transpose over the lane
+  // groups (below), the stage before they are used.  (16 byte loads per stage instead
+  // kept the address unit busy, 7% slower; a fetch through ds_bpermute, 11%.)  Buffers
+  // over the tile's panel: stages past the last read 0.
+  const v4i rsSR = make_rsrc(MX ? static_cast<const uint8_t*>(RA ? p.a_scale : p.b_scale) +
+                                      static_cast<int64_t>((RA ? m0 : n0) / 256) * S * 1024
+                                : nullptr,
+                             MX ? static_cast<uint32_t>(S) * 1024u : 0u);
+  const v4i rsST = make_rsrc(MX ? static_cast<const uint8_t*>(RA ? p.b_scale : p.a_scale) +
+                                      static_cast<int64_t>((RA ? n0 : m0) / 256) * S * 1024
+                                : nullptr,
+                             MX ? static_cast<uint32_t>(S) * 1024u : 0u);
+  const int scR = 4 * ((RA ? wm : wn) + 32 * lq + l16), scT = 4 * ((RA ? wn : wm) + 32 * lq + l16);
+  // The lanes of group q hold the dwords of groups 2q and 2q + 1 (rows 16 (2q + h) + (l &
+  // 15)); byte d of each is the scale lane group d needs: a 4 x 4 transpose of 2-byte items
+  // over the lane groups, done with the two half-wave swaps (no LDS traffic)
+  const bool odd = (lq & 1) != 0;
+  const uint32_t selK = odd ? 0x07060302u : 0x05040100u;  // keep this group's items
+  const uint32_t selS = odd ? 0x05040100u : 0x07060302u;  // send the partner's
+  const uint32_t sel0 = odd ? 0x01000504u : 0x05040100u;  // groups 0-3 in source order
+  const uint32_t sel1 = odd ? 0x03020706u : 0x07060302u;  // groups 4-7
+  // packed scales: byte g & 3 of dword g >> 2 is the scale of group g
+  uint32_t rawR[2][2], rawT[2][2], Rsc[2][2], Tsc[2][2];  // raw: two stages in flight
+  auto load_raw = [&](uint32_t (&dst)[2], const v4i& rs, int off, int st) {
+    const int so = __builtin_amdgcn_readfirstlane(st * 1024);
+    dst[0] = static_cast<uint32_t>(buffer_load_u32(rs, off, so, 0));
+    dst[1] = static_cast<uint32_t>(buffer_load_u32(rs, off + 64, so, 0));
+  };
+  auto xpose = [&](uint32_t (&dst)[2], const uint32_t (&raw)[2]) {
+    // items for destinations 0, 1 (A) and 2, 3 (B): (group 2q, group 2q + 1) byte pairs
+    const uint32_t A = __builtin_amdgcn_perm(raw[1], raw[0], 0x05010400u);
+    const uint32_t B = __builtin_amdgcn_perm(raw[1], raw[0], 0x07030602u);
+    // half-waves: lanes 0-31 end with the items for destinations 0, 1, lanes 32-63 with
+    // those for 2, 3 (P: source q or q - 2, Q: source q + 2 or q)
+    const auto pq = __builtin_amdgcn_permlane32_swap(A, B, false, false);
+    const uint32_t P = pq[0], Q = pq[1];
+    // rows of 16 lanes in pairs: the even row keeps the lower destination's items and
+    // sends the upper's, the odd row the other way round
+    const uint32_t K = __builtin_amdgcn_perm(Q, P, selK);
+    const uint32_t S2 = __builtin_amdgcn_perm(Q, P, selS);
+    const auto xy = __builtin_amdgcn_permlane16_swap(S2, S2, false, false);
+    const uint32_t R = odd ? xy[0] : xy[1];
+    dst[0] = __builtin_amdgcn_perm(R, K, sel0);
+    dst[1] = __builtin_amdgcn_perm(R, K, sel1);
+  };
   v4f acc[8][8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -1680,6 +1737,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
 #pragma unroll
   for (int g = 0; g < 8; ++g) Rf[0][g] = rd(sR0, oR, g);
   Tf[0] = rdT(0, 0);
+  if constexpr (MX) {
+    load_raw(rawR[0], rsSR, scR, 0);
+    load_raw(rawT[0], rsST, scT, 0);
+    load_raw(rawR[1], rsSR, scR, 1);
+    load_raw(rawT[1], rsST, scT, 1);
+    xpose(Rsc[0], rawR[0]);
+    xpose(Tsc[0], rawT[0]);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // one group of 8 MFMAs (T group t against R's 8), each followed by its share of the
@@ -1688,6 +1753,39 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
   // builtin, the register allocator spread the 64 four-register accumulators over both
   // register files and moved them back and forth (hundreds of spills and copies per
   // stage).  The compiler still counts the LDS waits for the operands it reads.
+  // scaled: the scale of A is byte IA of sca, of B byte IB of scb (op_sel bit 0 and
+  // op_sel_hi bit 0 give A's byte, bit 1 of each B's)
+  auto mfma16s = [&](auto IA, auto IB, v4f& c, const v8i& a, const v8i& b, uint32_t sca, uint32_t scb) {
+    constexpr int ia = decltype(IA)::value, ib = decltype(IB)::value;
+#define TE_MFS(A0, B0, A1, B1, FMT)                                                                       \
+  asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[" #A0 "," #B0         \
+               ",0] op_sel_hi:[" #A1 "," #B1 ",0]" FMT                                                  \
+               : "+a"(c)                                                                                \
+               : "v"(a), "v"(b), "v"(sca), "v"(scb))
+#define TE_MFS_F(A0, B0, A1, B1)                                   \
+  if constexpr (AF == 0 && BF == 0) TE_MFS(A0, B0, A1, B1, "");    \
+  else if constexpr (AF == 1 && BF == 0) TE_MFS(A0, B0, A1, B1, " cbsz:1"); \
+  else if constexpr (AF == 0 && BF == 1) TE_MFS(A0, B0, A1, B1, " blgp:1"); \
+  else TE_MFS(A0, B0, A1, B1, " cbsz:1 blgp:1");
+    if constexpr (ia == 0 && ib == 0) { TE_MFS_F(0, 0, 0, 0) }
+    else if constexpr (ia == 1 && ib == 0) { TE_MFS_F(1, 0, 0, 0) }
+    else if constexpr (ia == 2 && ib == 0) { TE_MFS_F(0, 0, 1, 0) }
+    else if constexpr (ia == 3 && ib == 0) { TE_MFS_F(1, 0, 1, 0) }
+    else if constexpr (ia == 0 && ib == 1) { TE_MFS_F(0, 1, 0, 0) }
+    else if constexpr (ia == 1 && ib == 1) { TE_MFS_F(1, 1, 0, 0) }
+    else if constexpr (ia == 2 && ib == 1) { TE_MFS_F(0, 1, 1, 0) }
+    else if constexpr (ia == 3 && ib == 1) { TE_MFS_F(1, 1, 1, 0) }
+    else if constexpr (ia == 0 && ib == 2) { TE_MFS_F(0, 0, 0, 1) }
+    else if constexpr (ia == 1 && ib == 2) { TE_MFS_F(1, 0, 0, 1) }
+    else if constexpr (ia == 2 && ib == 2) { TE_MFS_F(0, 0, 1, 1) }
+    else if constexpr (ia == 3 && ib == 2) { TE_MFS_F(1, 0, 1, 1) }
+    else if constexpr (ia == 0 && ib == 3) { TE_MFS_F(0, 1, 0, 1) }
+    else if constexpr (ia == 1 && ib == 3) { TE_MFS_F(1, 1, 0, 1) }
+    else if constexpr (ia == 2 && ib == 3) { TE_MFS_F(0, 1, 1, 1) }
+    else { TE_MFS_F(1, 1, 1, 1) }
+#undef TE_MFS_F
+#undef TE_MFS
+  };
   auto mfma16 = [&](v4f& c, const v8i& a, const v8i& b) {
     if constexpr (AF == 0 && BF == 0)
       asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
@@ -1705,15 +1803,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
     constexpr int rs = u % 3, rs1 = (u + 1) % 3;  // R slots of stages s, s + 1
     constexpr int k0 = t < 2 ? 0 : t < 6 ? 3 * (t - 2) : 12 + 2 * (t - 6);
     constexpr int nld = t < 2 ? 0 : t < 6 ? 3 : 2;
-    auto mf = [&](int r) {
-      if constexpr (RA) mfma16(acc[r][t], Rf[pr][r], Tf[t & 1]);
-      else mfma16(acc[t][r], Tf[t & 1], Rf[pr][r]);
+    auto mf = [&](auto RR) {
+      constexpr int r = decltype(RR)::value;
+      if constexpr (MX) {
+        if constexpr (RA)
+          mfma16s(ic<r & 3>{}, ic<t & 3>{}, acc[r][t], Rf[pr][r], Tf[t & 1], Rsc[pr][r >> 2], Tsc[u & 1][t >> 2]);
+        else
+          mfma16s(ic<t & 3>{}, ic<r & 3>{}, acc[t][r], Tf[t & 1], Rf[pr][r], Tsc[u & 1][t >> 2], Rsc[pr][r >> 2]);
+      } else {
+        if constexpr (RA) mfma16(acc[r][t], Rf[pr][r], Tf[t & 1]);
+        else mfma16(acc[t][r], Tf[t & 1], Rf[pr][r]);
+      }
     };
     // MFMA 0, the next T fragment; MFMAs 1-4 with R of stage s + 1 (groups 2-5); the
     // loads after MFMAs 1 .. nld
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      mf(r);
+    auto step = [&](auto RR) {
+      constexpr int r = decltype(RR)::value;
+      mf(RR);
       if (r == 0) {
         if constexpr (t < 7) Tf[(t + 1) & 1] = rdT(ts, t + 1);
         else Tf[0] = rdT(ts ^ 1, 0);
@@ -1722,12 +1828,37 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
         if (r == 1 || r == 2) Rf[pr ^ 1][2 * (t - 2) + r - 1] = rd(slotR(rs1), oR, 2 * (t - 2) + r - 1);
       }
       if (r >= 3 && r - 3 < nld) load_k(k0 + r - 3, ts, rs, s);
+      if constexpr (MX) {
+        // scales: raw dwords of stage s + 2 in groups 0 (R) and 1 (T), those of stage s + 1
+        // transposed into the packed set in groups 6 and 7
+        if constexpr (t == 0) {
+          if (r == 2) load_raw(rawR[u & 1], rsSR, scR, s + 2);
+        }
+        if constexpr (t == 1) {
+          if (r == 2) load_raw(rawT[u & 1], rsST, scT, s + 2);
+        }
+        if constexpr (t == 6) {
+          if (r == 6) xpose(Rsc[pr ^ 1], rawR[(u + 1) & 1]);
+        }
+        if constexpr (t == 7) {
+          if (r == 6) xpose(Tsc[(u + 1) & 1], rawT[(u + 1) & 1]);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    step(ic<0>{});
+    step(ic<1>{});
+    step(ic<2>{});
+    step(ic<3>{});
+    step(ic<4>{});
+    step(ic<5>{});
+    step(ic<6>{});
+    step(ic<7>{});
     if constexpr (t == 1) {
       // T groups 0-2 of stage s read by this wave; stage s + 1's R and T groups 0-2 and
-      // stage s's T groups 3-7 landed (only the R loads of the last barrier in flight)
-      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(8));
+      // stage s's T groups 3-7 landed (only the R loads of the last barrier in flight, and
+      // MX: the four scale loads of this stage's first two groups, issued after them)
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(MX ? 12 : 8));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1806,7 +1937,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
           for (int jj = 0; jj < 4; ++jj) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-              float val = __fmul_rn(__fmul_rn(acc[4 * pr + ii][4 * pc + jj][v], sa), sb);
+              float val = acc[4 * pr + ii][4 * pc + jj][v];
+              if constexpr (!MX) val = __fmul_rn(__fmul_rn(val, sa), sb);
               if constexpr (decltype(HB)::value != 0) val = __fadd_rn(val, bias8[4 * pc + jj]);
               ep[(16 * ii + 4 * lq + v) * kEp + 16 * jj + l16] = val;
             }
@@ -1897,13 +2029,13 @@ hipError_t run(Params p, hipStream_t s, const char* name) {
 template <int KIND, int AF, int BF>
 hipError_t run_1w(Params p, hipStream_t s, const char* name_a, const char* name_b) {
   const int nb = p.nbm * p.nbn;
-  if constexpr (KIND == KIND_FP8) {  // per-tensor FP8: the 16 x 16 x 128 kernel
+  if constexpr (KIND == KIND_FP8 || KIND == KIND_MX) {  // the 16 x 16 x 128 kernel
     if (p.M >= p.N) {
       g_last_variant = name_a;
-      hipLaunchKernelGGL((k_gemm1x<AF, BF, 1>), dim3(nb), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((k_gemm1x<KIND, AF, BF, 1>), dim3(nb), dim3(256), 0, s, p);
     } else {
       g_last_variant = name_b;
-      hipLaunchKernelGGL((k_gemm1x<AF, BF, 2>), dim3(nb), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((k_gemm1x<KIND, AF, BF, 2>), dim3(nb), dim3(256), 0, s, p);
     }
     return hipGetLastError();
   }
@@ -1975,12 +2107,16 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.a_fmt != E2M1 && p.splits == 1 && ((g.mx && g.mx_panel) || (!g.mx && p.KB % PK == 0))) {
     if (g.mx) {
       if (af == 0 && bf == 0)
-        return run_1w<KIND_MX, 0, 0>(p, s, "gemm1w_mx_e4m3_e4m3_256x256_panel_deepA", "gemm1w_mx_e4m3_e4m3_256x256_panel_deepB");
+        return run_1w<KIND_MX, 0, 0>(p, s, "gemm1w_mx_e4m3_e4m3_256x256_panel_mfma16_deepA",
+                                      "gemm1w_mx_e4m3_e4m3_256x256_panel_mfma16_deepB");
       if (af == 1 && bf == 0)
-        return run_1w<KIND_MX, 1, 0>(p, s, "gemm1w_mx_e5m2_e4m3_256x256_panel_deepA", "gemm1w_mx_e5m2_e4m3_256x256_panel_deepB");
+        return run_1w<KIND_MX, 1, 0>(p, s, "gemm1w_mx_e5m2_e4m3_256x256_panel_mfma16_deepA",
+                                      "gemm1w_mx_e5m2_e4m3_256x256_panel_mfma16_deepB");
       if (af == 0 && bf == 1)
-        return run_1w<KIND_MX, 0, 1>(p, s, "gemm1w_mx_e4m3_e5m2_256x256_panel_deepA", "gemm1w_mx_e4m3_e5m2_256x256_panel_deepB");
-      return run_1w<KIND_MX, 1, 1>(p, s, "gemm1w_mx_e5m2_e5m2_256x256_panel_deepA", "gemm1w_mx_e5m2_e5m2_256x256_panel_deepB");
+        return run_1w<KIND_MX, 0, 1>(p, s, "gemm1w_mx_e4m3_e5m2_256x256_panel_mfma16_deepA",
+                                      "gemm1w_mx_e4m3_e5m2_256x256_panel_mfma16_deepB");
+      return run_1w<KIND_MX, 1, 1>(p, s, "gemm1w_mx_e5m2_e5m2_256x256_panel_mfma16_deepA",
+                                      "gemm1w_mx_e5m2_e5m2_256x256_panel_mfma16_deepB");
     }
     if (af == 0 && bf == 0)
       return run_1w<KIND_FP8, 0, 0>(p, s, "gemm1w_fp8_e4m3_e4m3_256x256_mfma16_deepA",
