@@ -630,7 +630,7 @@ def main():
     roof8 = mx_roofline("mxfp8_prequant", MI355X_FP8_PEAK_TFLOPS, "gemm_mxfp8",
                         "k_gemm1x MXFP8 (E4M3 x E4M3 scaled 16x16x128 MFMA, E8M0 scales in the panel layout, 256x256 tiles, one wave per SIMD); 12 launches per layer")
     roof4 = mx_roofline("mxfp4_prequant", MI355X_FP4_PEAK_TFLOPS, "gemm_mxfp4",
-                        "k_gemm1w MXFP4 (E2M1 x E2M1 scaled MFMA, E8M0 scales in the panel layout, 256x256 tiles, one wave per SIMD); 12 launches per layer")
+                        "k_gemm1x MXFP4 (E2M1 x E2M1 scaled 16x16x128 MFMA, E8M0 scales in the panel layout, 256x256 tiles, one wave per SIMD); 12 launches per layer")
     roof16 = mx_roofline("bf16", MI355X_BF16_PEAK_TFLOPS, None,
                          "k_gemm4 BF16 (v_mfma_f32_32x32x16_bf16, 256x256 tiles, ping-pong); 12 launches per layer")
     roof_q = None

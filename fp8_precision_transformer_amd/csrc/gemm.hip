@@ -9,19 +9,22 @@
 // [TE-summary] "主な機能": MXFP8 block scaling.
 //
 // Operand kinds:
-//   FP8  per-tensor scaled E4M3/E5M2 (any mix), v_mfma_f32_32x32x64_f8f6f4;
+//   FP8  per-tensor scaled E4M3/E5M2 (any mix), v_mfma_f32_{16x16x128,32x32x64}_f8f6f4;
 //        epilogue d = fl32(fl32(acc * sa_inv) * sb_inv) + bias;
 //   MX   E4M3/E5M2 elements with one E8M0 exponent per 32 elements along k,
-//        v_mfma_scale_f32_32x32x64_f8f6f4 (the matrix core applies the scales);
+//        v_mfma_scale_f32_{16x16x128,32x32x64}_f8f6f4 (the matrix core applies the scales);
 //   MX4  E2M1 elements (two per byte) with one E8M0 exponent per 32, the same
 //        scaled instruction with the FP4 operand format (MXFP4);
 //   BF16 comparison GEMM, v_mfma_f32_32x32x16_bf16.
 //
-// Two kernels, both with a 256 x 256 output tile per workgroup and an
-// XCD-aware tile order (each of the 8 XCDs, with its own L2, runs a
-// contiguous, row-grouped range of tiles):
-//   k_gemm4  8 waves in two ping-pong groups (see its header): every FP8 and
-//            BF16 GEMM, and MX GEMMs with k a multiple of 128;
+// Three kernels, all with a 256 x 256 output tile per workgroup and an XCD-aware
+// tile order (each of the 8 XCDs, with its own L2, runs a contiguous, row-grouped
+// range of tiles):
+//   k_gemm1x one wave per SIMD on 16 x 16 x 128 MFMAs (see its header): per-tensor
+//            FP8 with k a multiple of 128, and MXFP8 / MXFP4 with panel-layout scales;
+//   k_gemm4  8 waves in two ping-pong groups on 32 x 32 MFMAs (see its header): BF16,
+//            FP8 with the fused amax epilogue, split-K or ragged k, and MX GEMMs with
+//            row-major scales and k a multiple of 128;
 //   k_gemm   4 waves of 128 x 128, two-stage LDS pipeline with register
 //            staging: MX GEMMs whose k is not a multiple of 128.
 
@@ -1066,470 +1069,21 @@ const char* splitk_name(const char* name) {
 }
 
 // ============================================================================
-// One wave per SIMD (per-tensor FP8 with k % 128 == 0; MXFP8 and MXFP4 with panel-layout
-// scales):
-// 4 waves (2 x 2), each a 128 x 128 block of the 256 x 256 tile (4 x 4 MFMA tiles of
-// 32 x 32), so a 64-byte k step reads 8 fragments for 16 MFMAs -- one LDS read per
-// MFMA, against 1.5 for the ping-pong's 128 x 64 waves, whose LDS command queue is
-// full a tenth of the time (rocprofv3 SQ_LDS_CMD_FIFO_FULL).  The 256 registers of
-// accumulators live in AGPRs beside 256 VGPRs, so both k steps of a stage and the MX
-// scales fit without the ping-pong's split of a stage into phases.
-//
-// One wave's stream is interleaved explicitly (scheduling groups): k step 0 of stage s
-// pairs each of its first 8 MFMAs with two fragment reads of k step 1 (the reads land
-// while the last 8 run); then the wave waits for stage s+1 and reaches the stage's one
-// barrier (every wave has read stage s, stage s+1 is visible); k step 1 pairs each MFMA
-// with a global->LDS load of a later stage into the slots of stage s, and the first 8
-// with two fragment reads of stage s+1.  Stage slots: the operand with more rows (the
-// one that does not stay in the last-level cache on the long-k shapes) gets three,
-// loaded two stages ahead, the other two (DEEP 1: A deep, 2: B deep).  Each slot is its
-// own LDS array, so the compiler can tell the loads into one slot from the reads of
-// another and interleave them.  Past the last stage the loads are sent out of range:
-// they fetch nothing and fill slots that are never read again, so every iteration has
-// the same shape.
-// Results are bit-identical to k_gemm4's: every output sums the same MFMAs in the same
-// k order.
-// ============================================================================
-template <int KIND, int AF, int BF, int DEEP>
-__global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
-  constexpr bool MX4 = KIND == KIND_MX4;
-  constexpr bool MX = KIND == KIND_MX || MX4;  // block-scaled (E8M0 panel scales)
-  constexpr int KSTEPS = MX4 ? 4 : 2;          // 64-element k steps per 128-byte stage
-  constexpr int SDW = MX4 ? 2 : 1;             // scale dwords per row and stage
-  // DEEP 1: A in three stage slots (loads two stages ahead), B in two; DEEP 2: the mirror
-  constexpr int NA = DEEP == 1 ? 3 : 2, NB = DEEP == 2 ? 3 : 2;
-  // one array per stage slot and operand, so that the compiler can tell the global->LDS
-  // loads into one slot from the fragment reads of another
-  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kPairOp];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA1[kPairOp];
-  __shared__ __attribute__((aligned(1024))) uint8_t sA2[NA > 2 ? kPairOp : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB0[kPairOp];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB1[kPairOp];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB2[NB > 2 ? kPairOp : 16];
-  auto slotA = [&](int slot) { return slot == 0 ? sA0 : slot == 1 ? sA1 : sA2; };
-  auto slotB = [&](int slot) { return slot == 0 ? sB0 : slot == 1 ? sB1 : sB2; };
-  const int nb = p.nbm * p.nbn;
-  const int bid = static_cast<int>(blockIdx.x);
-  const int xcd = bid & 7, idx = bid >> 3;
-  const int per = nb >> 3, rem = nb & 7;
-  const int lin = xcd * per + (xcd < rem ? xcd : rem) + idx;
-  const int gspan = kGroupM * p.nbn;
-  const int group = lin / gspan;
-  const int first_m = group * kGroupM;
-  const int gsz = (p.nbm - first_m) < kGroupM ? (p.nbm - first_m) : kGroupM;
-  const int in_g = lin - group * gspan;
-  const int tm = first_m + in_g % gsz;
-  const int tn = in_g / gsz;
-  const int m0 = tm * BM, n0 = tn * BN;
-  // per-tensor scale_inv values, read once at the start (scalar loads; the kernel never
-  // writes them)
-  float sa = 1.0f, sb = 1.0f;
-  if constexpr (!MX) {
-    sa = *(const __attribute__((address_space(4))) float*)(reinterpret_cast<uintptr_t>(p.a_scale));
-    sb = *(const __attribute__((address_space(4))) float*)(reinterpret_cast<uintptr_t>(p.b_scale));
-  }
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
-  const int lr = lane & 31, lk = lane >> 5;
-  const int rows_a = (p.M - m0) < BM ? (p.M - m0) : BM;
-  const int rows_b = (p.N - n0) < BN ? (p.N - n0) : BN;
-  const v4i rsA = make_rsrc(p.a + static_cast<int64_t>(m0) * p.KB, static_cast<uint32_t>(rows_a) * p.KB);
-  const v4i rsB = make_rsrc(p.b + static_cast<int64_t>(n0) * p.KB, static_cast<uint32_t>(rows_b) * p.KB);
-  // global->LDS: wave w moves rows [64 w, 64 w + 64) of A and of B, 8 rows per
-  // instruction (the lane mapping and swizzle of k_gemm4)
-  const int c0 = (lane & 7) ^ (lane >> 3);
-  const uint32_t ld_base = static_cast<uint32_t>(wave * 64 + (lane >> 3)) * static_cast<uint32_t>(p.KB);
-  const int S = (p.KB + PK - 1) / PK;
-  // per instruction t: the lane's byte offset in stage 0; stage st adds 128 st.  With k a
-  // multiple of 128 every chunk of a real stage is inside its row; the loads past the
-  // last stage are sent out of range.  A ragged k takes k_gemm4.
-  uint32_t voff[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t)
-    voff[t] = ld_base + static_cast<uint32_t>(t * 8) * static_cast<uint32_t>(p.KB) +
-              static_cast<uint32_t>((c0 ^ (t & 3)) << 4);
-  auto issue_op = [&](const v4i& rs, uint8_t* dst, int st) {
-    // past the last stage: an offset beyond the buffer's range, so the load fetches
-    // nothing (it writes zeros into a slot that is never read again)
-    const uint32_t kb = st < S ? static_cast<uint32_t>(st) * PK : 0x40000000u;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int off = static_cast<int>(voff[t] + kb);
-      const int base = (wave * 64 + t * 8) * PK;
-      raw_buffer_load_lds(rs, (__attribute__((address_space(3))) uint32_t*)(dst + base), 16, off, 0, 0, 0);
-    }
-  };
-  // MX (panel-layout E8M0 scales): the dword of row r and 128-element group g is dword
-  // ((r / 256) * G + g) * 256 + r % 256 (G = k / 128; a stage holds one group of FP8,
-  // two of E2M1); lane l loads rows wm + l and wm + 64 + l of A (wn + l, wn + 64 + l of
-  // B) for a stage, in k step 0 of the stage that issues the stage's operand loads (the
-  // last k step's scheduling slots are taken by those); once the stage before it has
-  // passed its barrier, the half-waves swap row groups and each lane keeps the bytes of
-  // its k blocks, into the second of two sets of packed scales, so that the exchange
-  // runs beside that stage's last MFMAs rather than ahead of the stage's first.
-  const uint32_t* scA = nullptr;
-  const uint32_t* scB = nullptr;
-  const int G = S * SDW;
-  if constexpr (MX) {
-    scA = static_cast<const uint32_t*>(p.a_scale) + static_cast<int64_t>(m0 / BM) * G * 256 + wm + lane;
-    scB = static_cast<const uint32_t*>(p.b_scale) + static_cast<int64_t>(n0 / BN) * G * 256 + wn + lane;
-  }
-  uint32_t rA0[NA][SDW], rA1[NA][SDW], rB0[NB][SDW], rB1[NB][SDW];  // raw dwords per stage slot
-  auto load_scA = [&](int set, int st) {
-    if constexpr (MX) {
-#pragma unroll
-      for (int d = 0; d < SDW; ++d) {
-        const int64_t o = static_cast<int64_t>((st < S ? st : S - 1) * SDW + d) * 256;
-        rA0[set][d] = scA[o];
-        rA1[set][d] = scA[o + 64];
-      }
-    }
-  };
-  auto load_scB = [&](int set, int st) {
-    if constexpr (MX) {
-#pragma unroll
-      for (int d = 0; d < SDW; ++d) {
-        const int64_t o = static_cast<int64_t>((st < S ? st : S - 1) * SDW + d) * 256;
-        rB0[set][d] = scB[o];
-        rB1[set][d] = scB[o + 64];
-      }
-    }
-  };
-  // packed scales: FP8 MX: byte 2h + (g & 1) of pA[g >> 1] is block 2h + lk of row group g
-  // (two row groups per dword); E2M1: byte sel(h) of pA[g] is block 2h + lk of row group g
-  // (two sets: the stage's, and the next stage's being packed)
-  uint32_t pA2[2][4] = {}, pB2[2][4] = {};
-  // v_perm_b32 selector over {w1, w0}: bytes lk and 2 + lk of w0 and of w1, interleaved
-  const uint32_t psel = 0x06020400u + 0x01010101u * static_cast<uint32_t>(lk);
-  auto pack_sc = [&](int sa_set, int sb_set, int buf) {
-    uint32_t (&pA)[4] = pA2[buf];
-    uint32_t (&pB)[4] = pB2[buf];
-    if constexpr (MX) {
-      auto pick = [&](uint32_t w0, uint32_t w1) { return __builtin_amdgcn_perm(w1, w0, psel); };
-      uint32_t ga[4][SDW], gb[4][SDW];  // dwords of row groups 0..3 for this lane
-#pragma unroll
-      for (int d = 0; d < SDW; ++d) {
-        const auto a0 = __builtin_amdgcn_permlane32_swap(rA0[sa_set][d], rA0[sa_set][d], false, false);
-        const auto a1 = __builtin_amdgcn_permlane32_swap(rA1[sa_set][d], rA1[sa_set][d], false, false);
-        const auto b0 = __builtin_amdgcn_permlane32_swap(rB0[sb_set][d], rB0[sb_set][d], false, false);
-        const auto b1 = __builtin_amdgcn_permlane32_swap(rB1[sb_set][d], rB1[sb_set][d], false, false);
-        ga[0][d] = a0[0];
-        ga[1][d] = a0[1];
-        ga[2][d] = a1[0];
-        ga[3][d] = a1[1];
-        gb[0][d] = b0[0];
-        gb[1][d] = b0[1];
-        gb[2][d] = b1[0];
-        gb[3][d] = b1[1];
-      }
-      if constexpr (MX4) {  // dword 0 of a row holds blocks 0-3 of the stage, dword 1 blocks 4-7
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          pA[g] = pick(ga[g][0], ga[g][1]);
-          pB[g] = pick(gb[g][0], gb[g][1]);
-        }
-      } else {
-        pA[0] = pick(ga[0][0], ga[1][0]);
-        pA[1] = pick(ga[2][0], ga[3][0]);
-        pB[0] = pick(gb[0][0], gb[1][0]);
-        pB[1] = pick(gb[2][0], gb[3][0]);
-      }
-    }
-  };
-  const int fk = f8(lr);
-  const int ra0 = (wm + lr) * PK + ((lk ^ fk) << 4);
-  const int rb0 = (wn + lr) * PK + ((lk ^ fk) << 4);
-  // fragments: FP8 k step h of a row is logical chunks 4h + lk (low 16 bytes) and
-  // 4h + 2 + lk (high); E2M1 k step h (64 elements, 32 bytes) is logical chunk 2h + lk,
-  // one 16-byte read (the matrix core reads the low four registers of an E2M1 operand)
-  using Frag = std::conditional_t<MX4, v4u, v8i>;
-  Frag fa0[4], fb0[4], fa1[4], fb1[4];
-  auto read_ks = [&](int sla, int slb, int h, Frag (&fa)[4], Frag (&fb)[4]) {
-    if constexpr (MX4) {
-      const int ao = ra0 ^ (h << 5), bo = rb0 ^ (h << 5);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const v4u*>(slotA(sla) + ao + i * 32 * PK);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const v4u*>(slotB(slb) + bo + j * 32 * PK);
-    } else {
-      const int alo = ra0 ^ (h << 6), ahi = alo ^ 32;
-      const int blo = rb0 ^ (h << 6), bhi = blo ^ 32;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int o = i * 32 * PK;
-        const v4u lo = *reinterpret_cast<const v4u*>(slotA(sla) + alo + o);
-        const v4u hi = *reinterpret_cast<const v4u*>(slotA(sla) + ahi + o);
-        fa[i] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int o = j * 32 * PK;
-        const v4u lo = *reinterpret_cast<const v4u*>(slotB(slb) + blo + o);
-        const v4u hi = *reinterpret_cast<const v4u*>(slotB(slb) + bhi + o);
-        fb[j] = __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-    }
-  };
-  v16f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{0};
-  auto mf = [&](auto PB, auto H, auto I, auto J, const Frag (&fa)[4], const Frag (&fb)[4]) {
-    constexpr int h = decltype(H)::value, i = decltype(I)::value, j = decltype(J)::value;
-    const uint32_t (&pA)[4] = pA2[decltype(PB)::value];
-    const uint32_t (&pB)[4] = pB2[decltype(PB)::value];
-    if constexpr (MX4) {
-      constexpr int sel = ((h & 1) << 1) | (h >> 1);
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          __builtin_bit_cast(v8i, __builtin_shufflevector(fa[i], fa[i], 0, 1, 2, 3, 0, 1, 2, 3)),
-          __builtin_bit_cast(v8i, __builtin_shufflevector(fb[j], fb[j], 0, 1, 2, 3, 0, 1, 2, 3)), acc[i][j], 4, 4,
-          sel, static_cast<int>(pA[i]), sel, static_cast<int>(pB[j]));
-    } else if constexpr (MX) {
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AF, BF, 2 * h + (i & 1),
-                                                                 static_cast<int>(pA[i >> 1]), 2 * h + (j & 1),
-                                                                 static_cast<int>(pB[j >> 1]));
-    } else {
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], AF, BF, 0, 0, 0, 0);
-    }
-  };
-  auto mfma_ks = [&](auto PB, auto H, const Frag (&fa)[4], const Frag (&fb)[4]) {
-    auto row = [&](auto I) {
-      mf(PB, H, I, ic<0>{}, fa, fb);
-      mf(PB, H, I, ic<1>{}, fa, fb);
-      mf(PB, H, I, ic<2>{}, fa, fb);
-      mf(PB, H, I, ic<3>{}, fa, fb);
-    };
-    row(ic<0>{});
-    row(ic<1>{});
-    row(ic<2>{});
-    row(ic<3>{});
-  };
-
-  // Prologue: stages 0 and 1 of both operands and stage 2 of the deep one, the deep
-  // one's loads last, so that waiting for a stage of the shallow operand leaves the deep
-  // operand's latest stage in flight.  Loads per stage and operand: 8 (+ 2 scale dwords).
-  constexpr int LPO = 8 + (MX ? 2 * SDW : 0);
-  auto issue_A = [&](int slot, int st) { load_scA(slot, st); issue_op(rsA, slotA(slot), st); };
-  auto issue_B = [&](int slot, int st) { load_scB(slot, st); issue_op(rsB, slotB(slot), st); };
-  issue_A(0, 0);
-  issue_B(0, 0);
-  issue_A(1, 1);
-  issue_B(1, 1);
-  if constexpr (DEEP == 1) issue_A(2, 2);
-  if constexpr (DEEP == 2) issue_B(2, 2);
-  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((DEEP ? 3 : 2) * LPO));  // stage 0 landed
-  __builtin_amdgcn_s_barrier();
-  read_ks(0, 0, 0, fa0, fb0);
-  pack_sc(0, 0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // one stage: k steps 0 .. KSTEPS-1.  Every k step but the last pairs its first 8
-  // MFMAs with the fragment reads of the next k step (MX: k step 0 pairs its last MFMAs
-  // with the scale loads of the stages the last k step loads); after the second-to-last,
-  // every read of this stage has been issued: wait for them and for stage s+1, then the
-  // stage's barrier; the last k step pairs its MFMAs with the loads of a later stage
-  // into this stage's slots and the first 8 with the reads of stage s+1's k step 0, and
-  // packs stage s+1's scales.
-  constexpr int RPM = MX4 ? 1 : 2;  // fragment reads per paired MFMA
-  auto iter = [&](auto U, int s) {
-    constexpr int u = decltype(U)::value;
-    constexpr int sa = u % NA, sb = u % NB;
-    constexpr int sa1 = (u + 1) % NA, sb1 = (u + 1) % NB;
-    constexpr int pb = u & 1;
-    auto kstep = [&](auto KS) {
-      constexpr int ks = decltype(KS)::value;
-      constexpr bool last = ks == KSTEPS - 1;
-      if constexpr (ks == 0 && MX) {
-        if constexpr (DEEP == 1) {
-          load_scB(sb, s + 2);
-          load_scA(sa, s + 3);
-        } else if constexpr (DEEP == 2) {
-          load_scA(sa, s + 2);
-          load_scB(sb, s + 3);
-        } else {
-          load_scA(sa, s + 2);
-          load_scB(sb, s + 2);
-        }
-      }
-      if constexpr (last) {
-        read_ks(sa1, sb1, 0, fa0, fb0);
-        pack_sc(sa1, sb1, pb ^ 1);  // stage s+1 landed at the last wait
-        if constexpr (DEEP == 1) {
-          issue_op(rsB, slotB(sb), s + 2);
-          issue_op(rsA, slotA(sa), s + 3);
-        } else if constexpr (DEEP == 2) {
-          issue_op(rsA, slotA(sa), s + 2);
-          issue_op(rsB, slotB(sb), s + 3);
-        } else {
-          issue_op(rsA, slotA(sa), s + 2);
-          issue_op(rsB, slotB(sb), s + 2);
-        }
-      } else if constexpr (ks & 1) {
-        read_ks(sa, sb, ks + 1, fa0, fb0);
-      } else {
-        read_ks(sa, sb, ks + 1, fa1, fb1);
-      }
-      if constexpr (ks & 1) mfma_ks(ic<pb>{}, KS, fa1, fb1);
-      else mfma_ks(ic<pb>{}, KS, fa0, fb0);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
-        if constexpr (last) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (last || (ks == 0 && MX && q < 4 * SDW)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (ks == KSTEPS - 2) {
-        // stage s+1 landed (only the deep operand's stage s+2 and the scales issued in
-        // k step 0 may still be in flight); this wave's reads of stage s done
-        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((DEEP ? 8 : 0) + (MX ? 4 * SDW : 0)));
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    kstep(ic<0>{});
-    kstep(ic<1>{});
-    if constexpr (KSTEPS == 4) {
-      kstep(ic<2>{});
-      kstep(ic<3>{});
-    }
-  };
-  constexpr int UNR = DEEP ? 6 : 2;
-  int s = 0;
-  for (; s + UNR <= S; s += UNR) {
-    iter(ic<0>{}, s);
-    iter(ic<1>{}, s + 1);
-    if constexpr (UNR == 6) {
-      iter(ic<2>{}, s + 2);
-      iter(ic<3>{}, s + 3);
-      iter(ic<4>{}, s + 4);
-      iter(ic<5>{}, s + 5);
-    }
-  }
-  if (s < S) iter(ic<0>{}, s);
-  if constexpr (UNR == 6) {
-    if (s + 1 < S) iter(ic<1>{}, s + 1);
-    if (s + 2 < S) iter(ic<2>{}, s + 2);
-    if (s + 3 < S) iter(ic<3>{}, s + 3);
-    if (s + 4 < S) iter(ic<4>{}, s + 4);
-  }
-  __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));  // loads past the last stage still write LDS
-  __builtin_amdgcn_s_barrier();
-
-  // ---- epilogue: scale, bias, round; staged through LDS, 64 x 64 floats per pass ----
-  constexpr int kEpPitch = 256;
-  float* ep = reinterpret_cast<float*>((wave & 2 ? sA1 : sA0) + (wave & 1) * 64 * kEpPitch);
-  // the bias of this lane's four columns, fetched together (one memory latency)
-  float bias4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (p.bias != nullptr) {
-    // columns past n read column n - 1 (every load issued unconditionally) and take 0
-    uint32_t raw[4];
-    if (p.bias_bf16) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = min(n0 + wn + q * 32 + lr, p.N - 1);
-        raw[q] = static_cast<uint32_t>(static_cast<const uint16_t*>(p.bias)[col]) << 16;
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = min(n0 + wn + q * 32 + lr, p.N - 1);
-        raw[q] = static_cast<const uint32_t*>(p.bias)[col];
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) bias4[q] = n0 + wn + q * 32 + lr < p.N ? __uint_as_float(raw[q]) : 0.0f;
-  }
-  // the bias add is decided once per launch, not per element
-  auto epilogue = [&](auto HB) {
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const float bias_v[2] = {bias4[2 * hf], bias4[2 * hf + 1]};
-#pragma unroll
-      for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-          const int i = pass * 2 + ii;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              float val = acc[i][2 * hf + j][v];
-              if constexpr (!MX) val = __fmul_rn(__fmul_rn(val, sa), sb);
-              if constexpr (decltype(HB)::value != 0) val = __fadd_rn(val, bias_v[j]);
-              const int r = ii * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
-              ep[r * (kEpPitch / 4) + j * 32 + lr] = val;
-            }
-          }
-        }
-        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
-        __builtin_amdgcn_wave_barrier();
-        const int row0 = m0 + wm + pass * 64;
-        const int col0 = n0 + wn + hf * 64;
-        if (p.d_bf16) {
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const int r = t * 8 + (lane >> 3);
-            const int c = (lane & 7) * 8;
-            const float4 lo = *reinterpret_cast<const float4*>(ep + r * (kEpPitch / 4) + c);
-            const float4 hi = *reinterpret_cast<const float4*>(ep + r * (kEpPitch / 4) + c + 4);
-            const int grow = row0 + r, gcol = col0 + c;
-            if (grow < p.M && gcol < p.N) {
-              const v4u o = {bf16x2_rne(lo.x, lo.y), bf16x2_rne(lo.z, lo.w), bf16x2_rne(hi.x, hi.y),
-                             bf16x2_rne(hi.z, hi.w)};
-              __builtin_nontemporal_store(
-                  o, reinterpret_cast<v4u*>(static_cast<uint16_t*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol));
-            }
-          }
-        } else {
-#pragma unroll
-          for (int t = 0; t < 16; ++t) {
-            const int r = t * 4 + (lane >> 4);
-            const int c = (lane & 15) * 4;
-            v4f v4 = *reinterpret_cast<const v4f*>(ep + r * (kEpPitch / 4) + c);
-            const int grow = row0 + r, gcol = col0 + c;
-            if (grow < p.M && gcol < p.N) {
-              v4f* dst = reinterpret_cast<v4f*>(static_cast<float*>(p.d) + static_cast<int64_t>(grow) * p.N + gcol);
-              if (p.accumulate) {
-                const v4f old = __builtin_nontemporal_load(dst);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) v4[q] = __fadd_rn(old[q], v4[q]);
-              }
-              __builtin_nontemporal_store(v4, dst);
-            }
-          }
-        }
-        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
-        __builtin_amdgcn_wave_barrier();
-      }
-    }
-  };
-  if (p.bias != nullptr) epilogue(ic<1>{});
-  else epilogue(ic<0>{});
-}
-
-// ============================================================================
-// One wave per SIMD with 16 x 16 x 128 MFMAs (per-tensor FP8, k % 128 == 0; MXFP8 with
-// panel-layout scales).
+// One wave per SIMD with 16 x 16 x 128 MFMAs (per-tensor FP8 with k % 128 == 0; MXFP8
+// and MXFP4 with panel-layout scales).
 // With operands that change from one instruction to the next, as in a GEMM, the
 // 16 x 16 x 128 FP8 instruction sustains about a tenth more FLOP/s than the 32 x 32 x 64
 // one: both run below the published rate at the clocks the device holds under that
 // load, the larger one further below (k_peak_rand in peak.hip: 4290 against 3900
-// TFLOP/s with register operands only).  The outputs are bit-identical to the 32 x 32 x 64
-// kernels'.
-// A wave's 128 x 128 block is 8 x 8 MFMA tiles of 16 x 16, and one instruction takes a
-// whole 128-byte stage of k, so a stage is 64 MFMAs over 8 + 8 fragments.  The operand
-// with more rows (R) is read whole into registers during the stage before the one that
-// uses it (two register sets); the other (T) is read one 16-row group ahead of the 8
-// MFMAs that use the group.
+// TFLOP/s with register operands only).  The outputs are bit-identical to k_gemm4's:
+// every output sums the same products in the same k order.
+// Four waves (2 x 2) each own a 128 x 128 block of the 256 x 256 tile, 8 x 8 MFMA
+// tiles of 16 x 16, whose 64 accumulators (256 registers) live in AGPRs beside 256
+// VGPRs.  One instruction takes a whole 128-byte stage of k for FP8 (64 MFMAs per stage
+// over 8 + 8 fragments); an E2M1 stage holds 256 elements, two k steps of 128.  The
+// operand with more rows (R) is read whole into registers during the stage before the
+// one that uses it (two register sets); the other (T) is read one 16-row group ahead of
+// the 8 MFMAs that use the group.
 // Stage slots: R three -- its slot of stage s is free once stage s has been read into
 // registers, so R loads run two stages ahead; T two -- T's slot of stage s is read all
 // through stage s, so it is refilled in two parts: groups 0-2 of each wave's 128 rows
@@ -1539,11 +1093,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm1w(Params p) {
 // and T groups 0-2 of stage s + 1 and T groups 3-7 of stage s have landed; after it
 // the wave reads R of stage s + 1 and the rest of T, and issues the loads of T groups
 // 3-7 of s + 1, T groups 0-2 of s + 2 and R of s + 3, in that order, so that only R's
-// are still in flight at the next barrier.
+// are still in flight at the next barrier.  Each slot part is its own LDS array, so the
+// compiler can tell the loads into one from the reads of another and adds no wait.
+// Past the last stage the loads are sent out of range: they fetch nothing and fill
+// slots that are never read again, so every iteration has the same shape.
 // ============================================================================
 template <int KIND, int AF, int BF, int DEEP>
 __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
-  constexpr bool MX = KIND == KIND_MX;  // E8M0 block scales, panel layout
+  constexpr bool MX4 = KIND == KIND_MX4;           // E2M1 elements: two 128-element k steps per stage
+  constexpr bool MX = KIND == KIND_MX || MX4;      // E8M0 block scales, panel layout
+  constexpr int KS = MX4 ? 2 : 1;                  // MFMA k steps per 128-byte stage
   constexpr bool RA = DEEP == 1;        // R is A (A has at least as many rows as B)
   __shared__ __attribute__((aligned(1024))) uint8_t sR0[kPairOp];
   __shared__ __attribute__((aligned(1024))) uint8_t sR1[kPairOp];
@@ -1654,13 +1213,22 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
       oTa[par][hh] = (48 * th + l16) * PK + (((4 * hh + lq) ^ ((rA >> 1) & 7)) << 4);
       oTb[par][hh] = (80 * th + l16) * PK + (((4 * hh + lq) ^ ((rB >> 1) & 7)) << 4);
     }
+  // E2M1 k step h of a group: logical chunk 4 h + (l >> 4), one 16-byte read (the
+  // instruction reads four registers of an E2M1 operand: the lane group's 32-element block)
+  using Frag = std::conditional_t<MX4, v4u, v8i>;
   auto rd = [&](const uint8_t* slot, const int (&o)[2][2], int g) {
     const v4u lo = *reinterpret_cast<const v4u*>(slot + o[g & 1][0] + g * 16 * PK);
     const v4u hi = *reinterpret_cast<const v4u*>(slot + o[g & 1][1] + g * 16 * PK);
     return __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  // T group g of T slot ts
-  auto rdT = [&](int ts, int g) { return g < 3 ? rd(slotTa(ts), oTa, g) : rd(slotTb(ts), oTb, g - 3); };
+  auto rdF = [&](const uint8_t* slot, const int (&o)[2][2], int g, int h) -> Frag {
+    if constexpr (MX4) return *reinterpret_cast<const v4u*>(slot + o[g & 1][h] + g * 16 * PK);
+    else return rd(slot, o, g);
+  };
+  // T group g (k step h) of T slot ts
+  auto rdT = [&](int ts, int g, int h) {
+    return g < 3 ? rdF(slotTa(ts), oTa, g, h) : rdF(slotTb(ts), oTb, g - 3, h);
+  };
   // MX: a lane's fragment data is 32-element block l >> 4 of its row's stage, so its scale
   // is byte l >> 4 of the row's dword in the panel layout (dword ((r / 256) G + g) 256 +
   // r % 256 for row r and 128-element group g; G = k / 128, one group per stage).  Per
@@ -1671,13 +1239,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
   // kept the address unit busy, 7% slower; a fetch through ds_bpermute, 11%.)  Buffers
   // over the tile's panel: stages past the last read 0.
   const v4i rsSR = make_rsrc(MX ? static_cast<const uint8_t*>(RA ? p.a_scale : p.b_scale) +
-                                      static_cast<int64_t>((RA ? m0 : n0) / 256) * S * 1024
+                                      static_cast<int64_t>((RA ? m0 : n0) / 256) * S * KS * 1024
                                 : nullptr,
-                             MX ? static_cast<uint32_t>(S) * 1024u : 0u);
+                             MX ? static_cast<uint32_t>(S * KS) * 1024u : 0u);
   const v4i rsST = make_rsrc(MX ? static_cast<const uint8_t*>(RA ? p.b_scale : p.a_scale) +
-                                      static_cast<int64_t>((RA ? n0 : m0) / 256) * S * 1024
+                                      static_cast<int64_t>((RA ? n0 : m0) / 256) * S * KS * 1024
                                 : nullptr,
-                             MX ? static_cast<uint32_t>(S) * 1024u : 0u);
+                             MX ? static_cast<uint32_t>(S * KS) * 1024u : 0u);
   const int scR = 4 * ((RA ? wm : wn) + 32 * lq + l16), scT = 4 * ((RA ? wn : wm) + 32 * lq + l16);
   // The lanes of group q hold the dwords of groups 2q and 2q + 1 (rows 16 (2q + h) + (l &
   // 15)); byte d of each is the scale lane group d needs: a 4 x 4 transpose of 2-byte items
@@ -1688,13 +1256,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
   const uint32_t sel0 = odd ? 0x01000504u : 0x05040100u;  // groups 0-3 in source order
   const uint32_t sel1 = odd ? 0x03020706u : 0x07060302u;  // groups 4-7
   // packed scales: byte g & 3 of dword g >> 2 is the scale of group g
-  uint32_t rawR[2][2], rawT[2][2], Rsc[2][2], Tsc[2][2];  // raw: two stages in flight
-  auto load_raw = [&](uint32_t (&dst)[2], const v4i& rs, int off, int st) {
-    const int so = __builtin_amdgcn_readfirstlane(st * 1024);
-    dst[0] = static_cast<uint32_t>(buffer_load_u32(rs, off, so, 0));
-    dst[1] = static_cast<uint32_t>(buffer_load_u32(rs, off + 64, so, 0));
+  // (E2M1: a stage holds two 128-element groups, k step h reads group 2 st + h)
+  uint32_t rawR[2][KS][2], rawT[2][KS][2], Rsc[2][KS][2], Tsc[2][KS][2];  // raw: two stages in flight
+  auto load_raw = [&](uint32_t (&dst)[KS][2], const v4i& rs, int off, int st) {
+#pragma unroll
+    for (int h = 0; h < KS; ++h) {
+      const int so = __builtin_amdgcn_readfirstlane((st * KS + h) * 1024);
+      dst[h][0] = static_cast<uint32_t>(buffer_load_u32(rs, off, so, 0));
+      dst[h][1] = static_cast<uint32_t>(buffer_load_u32(rs, off + 64, so, 0));
+    }
   };
-  auto xpose = [&](uint32_t (&dst)[2], const uint32_t (&raw)[2]) {
+  auto xpose1 = [&](uint32_t (&dst)[2], const uint32_t (&raw)[2]) {
     // items for destinations 0, 1 (A) and 2, 3 (B): (group 2q, group 2q + 1) byte pairs
     const uint32_t A = __builtin_amdgcn_perm(raw[1], raw[0], 0x05010400u);
     const uint32_t B = __builtin_amdgcn_perm(raw[1], raw[0], 0x07030602u);
@@ -1711,12 +1283,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
     dst[0] = __builtin_amdgcn_perm(R, K, sel0);
     dst[1] = __builtin_amdgcn_perm(R, K, sel1);
   };
+  auto xpose = [&](uint32_t (&dst)[KS][2], const uint32_t (&raw)[KS][2]) {
+#pragma unroll
+    for (int h = 0; h < KS; ++h) xpose1(dst[h], raw[h]);
+  };
   v4f acc[8][8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  v8i Rf[2][8], Tf[2];
+  Frag Rf[2][8][KS], Tf[2][KS];
 
   // prologue: T of stage 0 (both parts), R of stage 0, T part 1 of stage 1, R of stages
   // 1 and 2; then stage 0's R and first T group into registers
@@ -1735,8 +1311,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
   __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(3 + 8 + 8));  // stage 0 landed
   __builtin_amdgcn_s_barrier();
 #pragma unroll
-  for (int g = 0; g < 8; ++g) Rf[0][g] = rd(sR0, oR, g);
-  Tf[0] = rdT(0, 0);
+  for (int g = 0; g < 8; ++g)
+#pragma unroll
+    for (int h = 0; h < KS; ++h) Rf[0][g][h] = rdF(sR0, oR, g, h);
+#pragma unroll
+  for (int h = 0; h < KS; ++h) Tf[0][h] = rdT(0, 0, h);
   if constexpr (MX) {
     load_raw(rawR[0], rsSR, scR, 0);
     load_raw(rawT[0], rsST, scT, 0);
@@ -1755,15 +1334,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
   // stage).  The compiler still counts the LDS waits for the operands it reads.
   // scaled: the scale of A is byte IA of sca, of B byte IB of scb (op_sel bit 0 and
   // op_sel_hi bit 0 give A's byte, bit 1 of each B's)
-  auto mfma16s = [&](auto IA, auto IB, v4f& c, const v8i& a, const v8i& b, uint32_t sca, uint32_t scb) {
+  auto mfma16s = [&](auto IA, auto IB, v4f& c, const Frag& a, const Frag& b, uint32_t sca, uint32_t scb) {
     constexpr int ia = decltype(IA)::value, ib = decltype(IB)::value;
+#if defined(__HIP_DEVICE_COMPILE__)  // device pass only: the host pass cannot type the AGPR operands
 #define TE_MFS(A0, B0, A1, B1, FMT)                                                                       \
   asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[" #A0 "," #B0         \
                ",0] op_sel_hi:[" #A1 "," #B1 ",0]" FMT                                                  \
                : "+a"(c)                                                                                \
                : "v"(a), "v"(b), "v"(sca), "v"(scb))
 #define TE_MFS_F(A0, B0, A1, B1)                                   \
-  if constexpr (AF == 0 && BF == 0) TE_MFS(A0, B0, A1, B1, "");    \
+  if constexpr (MX4) TE_MFS(A0, B0, A1, B1, " cbsz:4 blgp:4");     \
+  else if constexpr (AF == 0 && BF == 0) TE_MFS(A0, B0, A1, B1, ""); \
   else if constexpr (AF == 1 && BF == 0) TE_MFS(A0, B0, A1, B1, " cbsz:1"); \
   else if constexpr (AF == 0 && BF == 1) TE_MFS(A0, B0, A1, B1, " blgp:1"); \
   else TE_MFS(A0, B0, A1, B1, " cbsz:1 blgp:1");
@@ -1785,8 +1366,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
     else { TE_MFS_F(1, 1, 1, 1) }
 #undef TE_MFS_F
 #undef TE_MFS
+#endif
   };
-  auto mfma16 = [&](v4f& c, const v8i& a, const v8i& b) {
+  auto mfma16 = [&](v4f& c, const Frag& a, const Frag& b) {
+#if defined(__HIP_DEVICE_COMPILE__)  // device pass only: the host pass cannot type the AGPR operands
     if constexpr (AF == 0 && BF == 0)
       asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
     else if constexpr (AF == 1 && BF == 0)
@@ -1795,6 +1378,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
       asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 blgp:1" : "+a"(c) : "v"(a), "v"(b));
     else
       asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 cbsz:1 blgp:1" : "+a"(c) : "v"(a), "v"(b));
+#endif
   };
   auto group8 = [&](auto U, auto TT, int s) {
     constexpr int u = decltype(U)::value, t = decltype(TT)::value;
@@ -1803,45 +1387,51 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
     constexpr int rs = u % 3, rs1 = (u + 1) % 3;  // R slots of stages s, s + 1
     constexpr int k0 = t < 2 ? 0 : t < 6 ? 3 * (t - 2) : 12 + 2 * (t - 6);
     constexpr int nld = t < 2 ? 0 : t < 6 ? 3 : 2;
-    auto mf = [&](auto RR) {
-      constexpr int r = decltype(RR)::value;
+    auto mf = [&](auto QQ) {
+      constexpr int q = decltype(QQ)::value, r = q & 7, h = q >> 3;
       if constexpr (MX) {
         if constexpr (RA)
-          mfma16s(ic<r & 3>{}, ic<t & 3>{}, acc[r][t], Rf[pr][r], Tf[t & 1], Rsc[pr][r >> 2], Tsc[u & 1][t >> 2]);
+          mfma16s(ic<r & 3>{}, ic<t & 3>{}, acc[r][t], Rf[pr][r][h], Tf[t & 1][h], Rsc[pr][h][r >> 2],
+                  Tsc[u & 1][h][t >> 2]);
         else
-          mfma16s(ic<t & 3>{}, ic<r & 3>{}, acc[t][r], Tf[t & 1], Rf[pr][r], Tsc[u & 1][t >> 2], Rsc[pr][r >> 2]);
+          mfma16s(ic<t & 3>{}, ic<r & 3>{}, acc[t][r], Tf[t & 1][h], Rf[pr][r][h], Tsc[u & 1][h][t >> 2],
+                  Rsc[pr][h][r >> 2]);
       } else {
-        if constexpr (RA) mfma16(acc[r][t], Rf[pr][r], Tf[t & 1]);
-        else mfma16(acc[t][r], Tf[t & 1], Rf[pr][r]);
+        if constexpr (RA) mfma16(acc[r][t], Rf[pr][r][0], Tf[t & 1][0]);
+        else mfma16(acc[t][r], Tf[t & 1][0], Rf[pr][r][0]);
       }
     };
-    // MFMA 0, the next T fragment; MFMAs 1-4 with R of stage s + 1 (groups 2-5); the
-    // loads after MFMAs 1 .. nld
-    auto step = [&](auto RR) {
-      constexpr int r = decltype(RR)::value;
-      mf(RR);
-      if (r == 0) {
-        if constexpr (t < 7) Tf[(t + 1) & 1] = rdT(ts, t + 1);
-        else Tf[0] = rdT(ts ^ 1, 0);
+    // MFMA 0 (and 1: E2M1) with the next T fragment; MFMAs 1-2 (2-5: E2M1) with R of
+    // stage s + 1 (groups 2-5); the loads after MFMAs 3 .. (6 ..: E2M1)
+    constexpr int q_ld = MX4 ? 6 : 3;
+    auto step = [&](auto QQ) {
+      constexpr int q = decltype(QQ)::value;
+      mf(QQ);
+      if constexpr (q < KS) {
+        if constexpr (t < 7) Tf[(t + 1) & 1][q] = rdT(ts, t + 1, q);
+        else Tf[0][q] = rdT(ts ^ 1, 0, q);
       }
       if constexpr (t >= 2 && t <= 5) {
-        if (r == 1 || r == 2) Rf[pr ^ 1][2 * (t - 2) + r - 1] = rd(slotR(rs1), oR, 2 * (t - 2) + r - 1);
+        if constexpr (q >= 1 && q < 1 + 2 * KS) {
+          constexpr int i = q - 1, g = 2 * (t - 2) + i / KS, h = i % KS;
+          Rf[pr ^ 1][g][h] = rdF(slotR(rs1), oR, g, h);
+        }
       }
-      if (r >= 3 && r - 3 < nld) load_k(k0 + r - 3, ts, rs, s);
+      if (q >= q_ld && q - q_ld < nld) load_k(k0 + q - q_ld, ts, rs, s);
       if constexpr (MX) {
         // scales: raw dwords of stage s + 2 in groups 0 (R) and 1 (T), those of stage s + 1
         // transposed into the packed set in groups 6 and 7
         if constexpr (t == 0) {
-          if (r == 2) load_raw(rawR[u & 1], rsSR, scR, s + 2);
+          if (q == 2) load_raw(rawR[u & 1], rsSR, scR, s + 2);
         }
         if constexpr (t == 1) {
-          if (r == 2) load_raw(rawT[u & 1], rsST, scT, s + 2);
+          if (q == 2) load_raw(rawT[u & 1], rsST, scT, s + 2);
         }
         if constexpr (t == 6) {
-          if (r == 6) xpose(Rsc[pr ^ 1], rawR[(u + 1) & 1]);
+          if (q == 6) xpose(Rsc[pr ^ 1], rawR[(u + 1) & 1]);
         }
         if constexpr (t == 7) {
-          if (r == 6) xpose(Tsc[(u + 1) & 1], rawT[(u + 1) & 1]);
+          if (q == 6) xpose(Tsc[(u + 1) & 1], rawT[(u + 1) & 1]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -1854,11 +1444,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm1x(Params p) {
     step(ic<5>{});
     step(ic<6>{});
     step(ic<7>{});
+    if constexpr (KS == 2) {
+      step(ic<8>{});
+      step(ic<9>{});
+      step(ic<10>{});
+      step(ic<11>{});
+      step(ic<12>{});
+      step(ic<13>{});
+      step(ic<14>{});
+      step(ic<15>{});
+    }
     if constexpr (t == 1) {
       // T groups 0-2 of stage s read by this wave; stage s + 1's R and T groups 0-2 and
       // stage s's T groups 3-7 landed (only the R loads of the last barrier in flight, and
       // MX: the four scale loads of this stage's first two groups, issued after them)
-      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(MX ? 12 : 8));
+      __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(MX ? 8 + 4 * KS : 8));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -2023,28 +1623,19 @@ hipError_t run(Params p, hipStream_t s, const char* name) {
   return hipGetLastError();
 }
 
-// the one-wave kernel: per-tensor FP8 (k % 128 == 0) or MX with panel scales, one k
-// split, bf16 / fp32 output (with accumulation); the operand with more rows gets the
-// deeper stage ring
+// the one-wave kernel: per-tensor FP8 (k % 128 == 0) or MXFP8 / MXFP4 with panel
+// scales, one k split, bf16 / fp32 output (with accumulation); the operand with more
+// rows gets the deeper stage ring
 template <int KIND, int AF, int BF>
 hipError_t run_1w(Params p, hipStream_t s, const char* name_a, const char* name_b) {
+  static_assert(KIND == KIND_FP8 || KIND == KIND_MX || KIND == KIND_MX4, "FP8, MXFP8 or MXFP4");
   const int nb = p.nbm * p.nbn;
-  if constexpr (KIND == KIND_FP8 || KIND == KIND_MX) {  // the 16 x 16 x 128 kernel
-    if (p.M >= p.N) {
-      g_last_variant = name_a;
-      hipLaunchKernelGGL((k_gemm1x<KIND, AF, BF, 1>), dim3(nb), dim3(256), 0, s, p);
-    } else {
-      g_last_variant = name_b;
-      hipLaunchKernelGGL((k_gemm1x<KIND, AF, BF, 2>), dim3(nb), dim3(256), 0, s, p);
-    }
-    return hipGetLastError();
-  }
   if (p.M >= p.N) {
     g_last_variant = name_a;
-    hipLaunchKernelGGL((k_gemm1w<KIND, AF, BF, 1>), dim3(nb), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_gemm1x<KIND, AF, BF, 1>), dim3(nb), dim3(256), 0, s, p);
   } else {
     g_last_variant = name_b;
-    hipLaunchKernelGGL((k_gemm1w<KIND, AF, BF, 2>), dim3(nb), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((k_gemm1x<KIND, AF, BF, 2>), dim3(nb), dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }
@@ -2132,8 +1723,8 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   }
   if (g.a_fmt == E2M1) {
     if (g.mx_panel)
-      return run_1w<KIND_MX4, 4, 4>(p, s, "gemm1w_mxfp4_e2m1_e2m1_256x256_panel_deepA",
-                                    "gemm1w_mxfp4_e2m1_e2m1_256x256_panel_deepB");
+      return run_1w<KIND_MX4, 4, 4>(p, s, "gemm1w_mxfp4_e2m1_e2m1_256x256_panel_mfma16_deepA",
+                                    "gemm1w_mxfp4_e2m1_e2m1_256x256_panel_mfma16_deepB");
     return run<KIND_MX4, 4, 4>(p, s, "gemm4_mxfp4_e2m1_e2m1_256x256_pingpong");
   }
   if (g.mx && g.mx_panel) {

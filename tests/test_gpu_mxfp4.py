@@ -238,7 +238,7 @@ def test_mxfp4_gemm_panel_scales_bit_identical(mnk):
         B.te_fp8_gemm(dev_u8(qa), "E2M1", dev_u8(pa), dev_u8(qb), "E2M1", dev_u8(pb), d2,
                       gran=B.TE_GRAN_MX_BLOCK32_PANEL)
         deep = "deepA" if m >= n else "deepB"  # the operand with more rows gets three stage slots
-        assert B.te_gemm_variant() == f"gemm1w_mxfp4_e2m1_e2m1_256x256_panel_{deep}"
+        assert B.te_gemm_variant() == f"gemm1w_mxfp4_e2m1_e2m1_256x256_panel_mfma16_{deep}"
         assert torch.equal(d1, d2), (mnk, odt)
 
 
