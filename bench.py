@@ -66,21 +66,21 @@ MI355X_HBM_GBS = 8000.0           # HBM3E (published)
 MEASURED_TRAFFIC = {
     # FP8 GEMM: mean over the layer's 12 GEMM launches (microbench layer --kind fp8)
     "gemm_fp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                 "sha256": "8d8c4814d98b58a8d122a5585ec817324354ecef6aad3ecd2383b9c2c6282fb9",
-                 "bytes_per_launch": 1519236981},
+                 "sha256": "6aad5b4ed9b0481ed38fce191204469a13f243814d1a7d6bb1a295e06736ad65",
+                 "bytes_per_launch": 1516276876},
     # delayed-scaling quantizers of one layer in autocast mode (24 casts and cast-transposes),
     # summed over the layer's launches (bench.py --modes fp8_delayed_autocast under --pmc)
     "quant_delayed_layer": {"source": "fp8_precision_transformer_amd/csrc/quant.hip",
                             "sha256": "69668d0fb473dfbdbd4c2f5a64a809fdc5b2c87029c59cf24abc5d7252cb3e29",
-                            "bytes_per_launch": 7453812835},
+                            "bytes_per_launch": 7453824682},
     # MXFP8 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mxp)
     "gemm_mxfp8": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "8d8c4814d98b58a8d122a5585ec817324354ecef6aad3ecd2383b9c2c6282fb9",
-                   "bytes_per_launch": 1550434854},
+                   "sha256": "6aad5b4ed9b0481ed38fce191204469a13f243814d1a7d6bb1a295e06736ad65",
+                   "bytes_per_launch": 1562112206},
     # MXFP4 GEMM, panel-layout scales: the same 12 shapes (microbench layer --kind mx4p)
     "gemm_mxfp4": {"source": "fp8_precision_transformer_amd/csrc/gemm.hip",
-                   "sha256": "8d8c4814d98b58a8d122a5585ec817324354ecef6aad3ecd2383b9c2c6282fb9",
-                   "bytes_per_launch": 918969121},
+                   "sha256": "6aad5b4ed9b0481ed38fce191204469a13f243814d1a7d6bb1a295e06736ad65",
+                   "bytes_per_launch": 882233785},
 }
 
 
