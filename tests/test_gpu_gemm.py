@@ -241,6 +241,32 @@ def test_fp8_gemm_full_5b_shape_sampled(stage, weight):
                    (1 / 64) ** 2, "bf16")
 
 
+@pytest.mark.parametrize("stage", ["fprop", "wgrad"])
+def test_mx_gemm_panel_full_5b_shape_sampled(stage):
+    """MXFP8 with panel-layout scales (the one-wave kernel the benchmark times) at a full
+    5B-layer shape; the oracle checks 96 sampled rows x 384 sampled columns."""
+    g = {(x.weight, x.stage): x for x in layer_gemms(CODONFM_5B)}[("qkv", stage)]
+    fa = "E4M3" if stage == "fprop" else "E5M2"
+    rng = np.random.default_rng(_seed("mxp", stage))
+    def codes(shape):
+        mag = rng.integers(0x18, 0x48, shape, dtype=np.uint8)
+        return mag | (rng.integers(0, 2, shape, dtype=np.uint8) << 7)
+    a, b = codes((g.m, g.k)), codes((g.n, g.k))
+    ea = rng.integers(120, 134, (g.m, g.k // 32), dtype=np.uint8)
+    eb = rng.integers(120, 134, (g.n, g.k // 32), dtype=np.uint8)
+    d = _out(g.m, g.n, "bf16")
+    B.te_fp8_gemm(dev_u8(a), fa, dev_u8(O.mx_scales_panel(ea)), dev_u8(b), "E4M3", dev_u8(O.mx_scales_panel(eb)), d,
+                  gran=B.TE_GRAN_MX_BLOCK32_PANEL)
+    assert "panel_mfma16" in B.te_gemm_variant()
+    rows = np.sort(rng.choice(g.m, 96, replace=False))
+    cols = np.sort(rng.choice(g.n, 384, replace=False))
+    rows[-1], cols[-1] = g.m - 1, g.n - 1
+    ref = O.gemm_mx(a[rows], ea[rows], FMTS[fa], b[cols], eb[cols], O.E4M3, out="bf16")
+    av = O.decode_table(FMTS[fa])[a[rows]] * np.repeat(O.e8m0_to_float(ea[rows]), 32, axis=1)
+    bv = O.decode_table(O.E4M3)[b[cols]] * np.repeat(O.e8m0_to_float(eb[cols]), 32, axis=1)
+    check_fp8_gemm(host(d)[np.ix_(rows, cols)], ref, av, bv, 1.0, "bf16")
+
+
 def test_dispatched_variant_is_the_requested_matrix_core_path():
     """te_gemm_variant names the kernel that ran: the FP8, MX and BF16 requests each take
     their own matrix-core path (no silent fallback to another precision); per-tensor FP8

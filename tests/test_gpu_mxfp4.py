@@ -201,9 +201,12 @@ def test_mxfp4_gemm_rejects():
         B.te_fp8_gemm(a, "E2M1", e, _u8(256, 256), "E4M3", e, d, gran=B.TE_GRAN_MX_BLOCK32)
 
 
+@pytest.mark.parametrize("layout", ["rowmajor", "panel"])
 @pytest.mark.parametrize("stage", ["fprop", "wgrad"])
-def test_mxfp4_gemm_full_5b_shape_sampled(stage):
-    """A 5B-layer GEMM shape at full size; the oracle checks 64 rows x 256 columns."""
+def test_mxfp4_gemm_full_5b_shape_sampled(stage, layout):
+    """A 5B-layer GEMM shape at full size, with row-major scales (the ping-pong kernel)
+    and with panel-layout scales (the one-wave kernel the layer runs); the oracle checks
+    64 rows x 256 columns."""
     g = {(x.weight, x.stage): x for x in layer_gemms(CODONFM_5B)}[("mlp_up", stage)]
     if g.k % 256:
         pytest.skip("k not a multiple of 256")
@@ -213,7 +216,12 @@ def test_mxfp4_gemm_full_5b_shape_sampled(stage):
     ea = rng.integers(120, 134, (g.m, g.k // 32), dtype=np.uint8)
     eb = rng.integers(120, 134, (g.n, g.k // 32), dtype=np.uint8)
     d = _out(g.m, g.n, "bf16")
-    B.te_fp8_gemm(dev_u8(qa), "E2M1", dev_u8(ea), dev_u8(qb), "E2M1", dev_u8(eb), d, gran=B.TE_GRAN_MX_BLOCK32)
+    if layout == "panel":
+        B.te_fp8_gemm(dev_u8(qa), "E2M1", dev_u8(O.mx_scales_panel(ea)), dev_u8(qb), "E2M1",
+                      dev_u8(O.mx_scales_panel(eb)), d, gran=B.TE_GRAN_MX_BLOCK32_PANEL)
+        assert "panel_mfma16" in B.te_gemm_variant()
+    else:
+        B.te_fp8_gemm(dev_u8(qa), "E2M1", dev_u8(ea), dev_u8(qb), "E2M1", dev_u8(eb), d, gran=B.TE_GRAN_MX_BLOCK32)
     rows = np.sort(rng.choice(g.m, 64, replace=False))
     cols = np.sort(rng.choice(g.n, 256, replace=False))
     rows[-1], cols[-1] = g.m - 1, g.n - 1
